@@ -1,0 +1,360 @@
+"""Pins of the CPU oracle against facts fixed outside it: hand-derived
+fixtures of the pages' layouts (tests/golden/), closed forms, invariants, and
+special cases that reduce to numpy library routines.  CPU only."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from weight_streaming_gemv_qgemv_amd import synth
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+F32, I8, I4, I2 = 0, 1, 2, 3
+
+
+def _load(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- unpack order
+@pytest.mark.parametrize("case", _load("qgemv_unpack_order.json")["cases"], ids=lambda c: c["name"])
+def test_golden_qgemv(orc, case):
+    if "rows_f32" in case:
+        W = np.array(case["rows_f32"], np.float32).view(np.uint8)
+    else:
+        W = np.stack([np.frombuffer(bytes.fromhex(h), np.uint8) for h in case["rows_hex"]])
+    x = np.array(case["x"], np.float32)
+    y, _ = orc.qgemv(case["fmt"], W, np.array(case["scale"], np.float32), x, O=case["O"])
+    assert np.array_equal(y, np.array(case["y"], np.float64))
+
+
+def test_f32_scale_optional(orc):
+    W = np.array([[1.5, -2.0]], np.float32).view(np.uint8)
+    y, _ = orc.qgemv(F32, W, None, np.array([[2.0, 3.0]], np.float32))
+    assert y[0, 0] == -3.0
+
+
+def _int4_bytes_from_values(v):
+    """Pack integer values in [-8,7] with the pages' int4 layout, written
+    independently of the oracle: low nibble = even element, stored as v+8,
+    pad nibble 8."""
+    O, I = v.shape
+    n = (v + 8).astype(np.uint8)
+    if I % 2:
+        n = np.concatenate([n, np.full((O, 1), 8, np.uint8)], axis=1)
+    return (n[:, 0::2] | (n[:, 1::2] << 4)).astype(np.uint8)
+
+
+def _int2_bytes_from_values(v):
+    O, I = v.shape
+    c = (v + 2).astype(np.uint8)
+    pad = (-I) % 4
+    if pad:
+        c = np.concatenate([c, np.zeros((O, pad), np.uint8)], axis=1)
+    return (c[:, 0::4] | (c[:, 1::4] << 2) | (c[:, 2::4] << 4) | (c[:, 3::4] << 6)).astype(np.uint8)
+
+
+@pytest.mark.parametrize("fmt", [I8, I4, I2])
+def test_exhaustive_byte_unpack_onehot(orc, fmt):
+    """Every byte value, read through one-hot x, gives back the element its
+    position defines (each byte value is its own row)."""
+    per = {I8: 1, I4: 2, I2: 4}[fmt]
+    W = np.arange(256, dtype=np.uint8).reshape(256, 1)
+    for j in range(per):
+        x = np.zeros((1, per), np.float32)
+        x[0, j] = 1.0
+        y, _ = orc.qgemv(fmt, W, np.ones(256, np.float32), x)
+        b = np.arange(256)
+        if fmt == I8:
+            want = np.where(b > 127, b - 256, b)
+        elif fmt == I4:
+            want = ((b >> (4 * j)) & 15) - 8
+        else:
+            want = ((b >> (2 * j)) & 3) - 2
+        assert np.array_equal(y[0], want.astype(np.float64)), j
+
+
+@pytest.mark.parametrize("I", [1, 2, 7, 8, 33])
+def test_exact_integer_qgemv_vs_integer_matmul(orc, I):
+    """Integers packed by an independent numpy packer; with integer x and
+    power-of-two scales the product is exact, so the oracle must equal the
+    int64 library matmul exactly."""
+    g = synth.rng(11, I)
+    O, S = 9, 3
+    for fmt, lo, hi, pack in ((I4, -8, 7, _int4_bytes_from_values),
+                              (I2, -2, 1, _int2_bytes_from_values)):
+        v = g.integers(lo, hi + 1, size=(O, I))
+        W = pack(v)
+        x = synth.exact_activations(g, S, I)
+        sc = synth.exact_scales(g, O)
+        y, mag = orc.qgemv(fmt, W, sc, x)
+        want = (x.astype(np.int64) @ v.T).astype(np.float64) * sc.astype(np.float64)[None, :]
+        assert np.array_equal(y, want)
+        wmag = (np.abs(x).astype(np.int64) @ np.abs(v).T).astype(np.float64) * np.abs(sc)[None, :]
+        assert np.array_equal(mag, wmag)
+    v8 = g.integers(-128, 128, size=(O, I)).astype(np.int8)
+    x = synth.exact_activations(g, S, I)
+    sc = synth.exact_scales(g, O)
+    y, _ = orc.qgemv(I8, v8.view(np.uint8), sc, x)
+    assert np.array_equal(y, (x.astype(np.int64) @ v8.astype(np.int64).T) * sc.astype(np.float64))
+
+
+def test_closed_form_rows(orc):
+    """All-zero nibbles give -8*scale*sum(x) (the spec pin); nibble 8
+    gives 0; int2 crumb 0 gives -2*scale*sum(x), crumb 2 gives 0; a constant
+    int8 row c gives c*scale*sum(x)."""
+    g = synth.rng(5)
+    for I in (1, 6, 1023, 6144):
+        x = synth.activations(g, 2, I)
+        sx = x.astype(np.float64).sum(axis=1)
+        sc = np.array([0.0125], np.float32)
+        s = float(sc[0])
+        rb4, rb2 = (I + 1) // 2, (I + 3) // 4
+        cases = [
+            (I4, np.zeros((1, rb4), np.uint8), -8 * s * sx),
+            (I4, np.full((1, rb4), 0x88, np.uint8), 0 * sx),
+            (I2, np.zeros((1, rb2), np.uint8), -2 * s * sx),
+            (I2, np.full((1, rb2), 0xAA, np.uint8), 0 * sx),
+            (I8, np.full((1, I), 5, np.uint8), 5 * s * sx),
+            (I8, np.full((1, I), 0xFD, np.uint8), -3 * s * sx),
+        ]
+        for fmt, W, want in cases:
+            y, _ = orc.qgemv(fmt, W, sc, x)
+            np.testing.assert_allclose(y[:, 0], want, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("fmt", [F32, I8, I4, I2])
+def test_linear_in_x_library_matmul(orc, fmt):
+    """The product equals a dense fp64 matmul by the matrix read back column
+    by column through one-hot x (linearity + library matmul)."""
+    g = synth.rng(7, fmt)
+    O, I, S = 13, 37, 4
+    W = synth.weight_bytes(g, fmt, O, I)
+    sc = synth.scales(g, O)
+    cols, _ = orc.qgemv(fmt, W, sc, np.eye(I, dtype=np.float32))   # [I, O]
+    x = synth.activations(g, S, I)
+    y, mag = orc.qgemv(fmt, W, sc, x)
+    np.testing.assert_allclose(y, x.astype(np.float64) @ cols, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(mag, np.abs(x.astype(np.float64)) @ np.abs(cols), rtol=1e-12)
+
+
+# ---------------------------------------------------------------- pack / quantise
+@pytest.mark.parametrize("I", [1, 2, 9, 64, 65])
+def test_pack_int4_roundtrip(orc, I):
+    """quantise->pack->unpack gives clamp(rint(w/s), -8, 7) computed by numpy,
+    with s = max(amax/7, 1e-8); odd rows carry pad nibble 8."""
+    g = synth.rng(3, I)
+    w = g.standard_normal((6, I)).astype(np.float32)
+    w[0] = 0.0
+    q4, s = orc.pack_int4(w)
+    amax = np.abs(w).max(axis=1)
+    np.testing.assert_array_equal(s, np.maximum(amax / np.float32(7), np.float32(1e-8)))
+    want = np.clip(np.rint(w / s[:, None]), -8, 7)
+    back, _ = orc.qgemv(I4, q4, np.ones(6, np.float32), np.eye(I, dtype=np.float32))
+    np.testing.assert_array_equal(back.T, want)
+    if I % 2:
+        assert np.all((q4[:, -1] >> 4) == 8)
+    # byte level: with amax = 7 the scale is 1 and the stored bytes must be
+    # the ones the independent numpy packer makes
+    ints = np.array([[a for a in range(-7, 8)] + [7]], np.float32)  # amax 7 -> s = 1
+    qq, ss = orc.pack_int4(ints)
+    assert ss[0] == 1.0
+    np.testing.assert_array_equal(qq, _int4_bytes_from_values(ints.astype(np.int64)))
+
+
+@pytest.mark.parametrize("I", [1, 3, 4, 5, 17])
+def test_pack_int2_roundtrip(orc, I):
+    g = synth.rng(4, I)
+    w = g.standard_normal((5, I)).astype(np.float32)
+    q2, s = orc.pack_int2(w)
+    want = np.clip(np.rint(w / s[:, None]), -2, 1)
+    back, _ = orc.qgemv(I2, q2, np.ones(5, np.float32), np.eye(I, dtype=np.float32))
+    np.testing.assert_array_equal(back.T, want)
+    ints = np.array([[-1, 0, 1, 1, 0, -1, 1][: max(I, 1)] + [1] * max(0, I - 7)], np.float32)
+    qq, ss = orc.pack_int2(ints)
+    assert ss[0] == 1.0
+    np.testing.assert_array_equal(qq, _int2_bytes_from_values(ints.astype(np.int64)))
+
+
+def test_quantize_rows_int8(orc):
+    g = synth.rng(9)
+    w = g.standard_normal((4, 50)).astype(np.float32)
+    q, s = orc.quantize_rows(w, 8)
+    np.testing.assert_array_equal(s, np.maximum(np.abs(w).max(axis=1) / np.float32(127), np.float32(1e-8)))
+    np.testing.assert_array_equal(q, np.clip(np.rint(w / s[:, None]), -128, 127).astype(np.int8))
+
+
+# ---------------------------------------------------------------- router
+@pytest.mark.parametrize("case", _load("router_ties.json")["cases"], ids=lambda c: c["name"])
+def test_golden_router(orc, case):
+    E, D = case["E"], case["D"]
+    Wr = np.zeros((E, D), np.float32)
+    r = orc.router(Wr, np.array(case["bias"], np.float32), np.array(case["x"], np.float32),
+                   case["K"], case["norm_topk"], case["routed_scale"])
+    assert np.array_equal(r["idx"], np.array(case["idx"], np.int32))
+    np.testing.assert_allclose(r["w"], np.array(case["w"]), rtol=1e-15)
+
+
+def test_router_sigmoid_closed_form(orc):
+    """D=1, x=1: logits are the router weights; scores are the logistic
+    function of them (closed form), weights their normalised top-K share."""
+    Wr = np.array([[0.0], [2.0], [-2.0], [1.0], [0.0], [3.0]], np.float32)
+    r = orc.router(Wr, np.zeros(6, np.float32), np.ones((1, 1), np.float32), 2, 1, 2.5)
+    sig = [1.0 / (1.0 + math.exp(-v)) for v in (0.0, 2.0, -2.0, 1.0, 0.0, 3.0)]
+    np.testing.assert_array_equal(r["sig"][0], np.array(sig, np.float32))
+    assert list(r["idx"][0]) == [5, 1]
+    s5, s1 = float(np.float32(sig[5])), float(np.float32(sig[1]))
+    np.testing.assert_allclose(r["w"][0], [2.5 * s5 / (s5 + s1), 2.5 * s1 / (s5 + s1)], rtol=1e-15)
+
+
+@pytest.mark.parametrize("E", [24, 168, 256])
+def test_router_invariants(orc, E):
+    g = synth.rng(21, E)
+    D, S, K = 64, 40, min(8, E)
+    Wr, b = synth.router_weights(g, E, D)
+    x = synth.activations(g, S, D)
+    r = orc.router(Wr, b, x, K, 1, 2.5)
+    # logits equal the library matmul in fp64
+    np.testing.assert_allclose(r["logit"], x.astype(np.float64) @ Wr.astype(np.float64).T,
+                               rtol=1e-12, atol=1e-12)
+    # weights renormalise then scale by routed_scale
+    sel = np.take_along_axis(r["sig"].astype(np.float64), r["idx"], axis=1)
+    np.testing.assert_allclose(r["w"].sum(axis=1), 2.5 * sel.sum(1) / (sel.sum(1) + 1e-20), rtol=1e-14)
+    np.testing.assert_allclose(r["w"], 2.5 * sel / sel.sum(1, keepdims=True), rtol=1e-14)
+    # greedy selection == sort by (-choice, index), first K
+    c = r["sig"] + b[None, :]
+    for s in range(S):
+        order = np.lexsort((np.arange(E), -c[s].astype(np.float64)))[:K]
+        assert list(r["idx"][s]) == list(order)
+    # zero bias: top-K of the logits (sigmoid is monotone), via library argsort
+    r0 = orc.router(Wr, np.zeros(E, np.float32), x, K, 1, 2.5)
+    lg = x.astype(np.float64) @ Wr.astype(np.float64).T
+    for s in range(S):
+        assert set(r0["idx"][s]) == set(np.argsort(-lg[s], kind="stable")[:K])
+    # a +10 bias on a chosen set forces exactly that set, ordered by choice
+    forced = g.choice(E, K, replace=False)
+    bb = b.copy()
+    bb[forced] += np.float32(10.0)
+    rf = orc.router(Wr, bb, x, K, 1, 2.5)
+    cf = rf["sig"] + bb[None, :]
+    for s in range(S):
+        assert set(rf["idx"][s]) == set(forced)
+        assert all(cf[s, rf["idx"][s][i]] >= cf[s, rf["idx"][s][i + 1]] for i in range(K - 1))
+    # identical router rows: equal choices, lowest index first
+    Wt = Wr.copy()
+    Wt[:] = Wr[0]
+    rt = orc.router(Wt, np.zeros(E, np.float32), x, K, 1, 2.5)
+    assert np.all(rt["idx"] == np.arange(K)[None, :])
+
+
+def test_router_topp_truncation(orc):
+    """topp keeps the shortest descending-weight prefix reaching topp of the
+    total; topp outside (0,1) keeps all K."""
+    g = synth.rng(33)
+    E, D, S, K = 32, 16, 20, 8
+    Wr, b = synth.router_weights(g, E, D)
+    Wr *= 20  # spread the scores
+    x = synth.activations(g, S, D)
+    full = orc.router(Wr, b, x, K, 1, 2.5, topp=0.0)
+    assert np.all(full["keff"] == K)
+    for p in (0.3, 0.6, 0.85):
+        r = orc.router(Wr, b, x, K, 1, 2.5, topp=p)
+        for s in range(S):
+            picks = full["idx"][s]
+            sig = full["sig"][s, picks].astype(np.float64)
+            order = np.argsort(-sig, kind="stable")
+            ke = r["keff"][s]
+            assert 1 <= ke <= K
+            assert list(r["idx"][s][:ke]) == list(picks[order][:ke])
+            assert np.all(r["idx"][s][ke:] == -1) and np.all(r["w"][s][ke:] == 0)
+            cs = np.cumsum(sig[order])
+            tot = sig.sum()
+            assert cs[ke - 1] >= p * tot * (1 - 1e-6)
+            if ke > 1:
+                assert cs[ke - 2] < p * tot * (1 + 1e-6)
+            kept = sig[order][:ke]
+            np.testing.assert_allclose(r["w"][s][:ke], 2.5 * kept / kept.sum(), rtol=1e-13)
+
+
+# ---------------------------------------------------------------- MoE
+def _dequant(orc, fmt, W, sc, I):
+    cols, _ = orc.qgemv(fmt, W, sc, np.eye(I, dtype=np.float32))
+    return cols.T  # [O, I] dense fp64, scales folded in
+
+
+def _silu(z):
+    return z / (1.0 + np.exp(-z))
+
+
+def _small_moe(seed, fmt=I4, E=6, D=40, F=24, shared=True):
+    ex = synth.expert_bank(seed, fmt, E, D, F)
+    sh = synth.shared_mlp(seed, fmt, D, F) if shared else None
+    return ex, sh
+
+
+def test_moe_k1_is_textbook_swiglu(orc):
+    """K=1, weight 1, no shared expert: the output is the SwiGLU MLP
+    down(silu(gate x) * up x) of the chosen expert, in library fp64."""
+    E, D, F, S = 6, 40, 24, 5
+    ex, _ = _small_moe(41, E=E, D=D, F=F, shared=False)
+    g = synth.rng(41, 99)
+    x = synth.activations(g, S, D)
+    idx = np.array([[3], [0], [5], [3], [1]], np.int32)
+    w = np.ones((S, 1), np.float32)
+    r = orc.moe(ex, None, x, idx, w, intermediates=True)
+    for s in range(S):
+        e = idx[s, 0]
+        Gd = _dequant(orc, I4, ex["wg"][e], ex["sg"][e], D)
+        Ud = _dequant(orc, I4, ex["wu"][e], ex["su"][e], D)
+        Dd = _dequant(orc, I4, ex["wd"][e], ex["sd"][e], F)
+        xs = x[s].astype(np.float64)
+        h = _silu(Gd @ xs) * (Ud @ xs)
+        np.testing.assert_allclose(r["out"][s], Dd @ h, rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(r["h"][s], h, rtol=1e-11, atol=1e-13)
+        np.testing.assert_allclose(r["mag"][s], np.abs(Dd) @ np.abs(h), rtol=1e-11)
+
+
+def test_moe_invariants(orc):
+    E, D, F, S, K = 6, 40, 24, 7, 3
+    ex, sh = _small_moe(42, E=E, D=D, F=F)
+    g = synth.rng(42, 7)
+    x = synth.activations(g, S, D)
+    idx, w = synth.routing_uniform(g, S, K, E)
+    base = orc.moe(ex, sh, x, idx, w)
+    # shared expert alone when all routed weights are zero == textbook MLP
+    zero = orc.moe(ex, sh, x, idx, np.zeros_like(w))
+    Gd = _dequant(orc, I4, sh["wg"], sh["sg"], D)
+    Ud = _dequant(orc, I4, sh["wu"], sh["su"], D)
+    Dd = _dequant(orc, I4, sh["wd"], sh["sd"], F)
+    xd = x.astype(np.float64)
+    shared_ref = (_silu(xd @ Gd.T) * (xd @ Ud.T)) @ Dd.T
+    np.testing.assert_allclose(zero["out"], shared_ref, rtol=1e-11, atol=1e-12)
+    # linear in the routing weights
+    w2 = g.uniform(0, 1, size=w.shape).astype(np.float32)
+    a = orc.moe(ex, sh, x, idx, w2)
+    both = orc.moe(ex, sh, x, idx, w.astype(np.float64) + w2.astype(np.float64))
+    np.testing.assert_allclose(both["out"] - zero["out"],
+                               (base["out"] - zero["out"]) + (a["out"] - zero["out"]),
+                               rtol=1e-9, atol=1e-11)
+    # routed part == sum of K=1 runs weighted
+    acc = zero["out"].copy()
+    for k in range(K):
+        one = orc.moe(ex, None, x, idx[:, k:k + 1], w[:, k:k + 1])
+        acc += one["out"]
+    np.testing.assert_allclose(base["out"], acc, rtol=1e-11, atol=1e-12)
+    # token permutation permutes rows
+    perm = g.permutation(S)
+    p = orc.moe(ex, sh, x[perm], idx[perm], w[perm])
+    np.testing.assert_array_equal(p["out"], base["out"][perm])
+    # zero input -> zero output (silu(0)*0 = 0 through every expert)
+    z = orc.moe(ex, sh, np.zeros_like(x), idx, w)
+    assert np.all(z["out"] == 0.0)
+    # skipped slots (idx < 0) contribute nothing
+    idx2 = idx.copy()
+    idx2[:, -1] = -1
+    sk = orc.moe(ex, sh, x, idx2, w)
+    ref = orc.moe(ex, sh, x, idx[:, :-1], w[:, :-1])
+    np.testing.assert_array_equal(sk["out"], ref["out"])
