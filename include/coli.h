@@ -1,0 +1,252 @@
+/*
+ * coli.h -- C ABI of libcoli: dequant-on-use quantized GEMV and the batched
+ * MoE block (router, expert-grouped SwiGLU experts, shared expert) on AMD
+ * MI355X (gfx950).
+ *
+ * Conventions shared by every entry point
+ *   - Every array argument is a DEVICE pointer (memory the caller allocated
+ *     on the current HIP device, e.g. a torch tensor's data_ptr()), unless the
+ *     argument says "host".  The library never allocates, frees or keeps any
+ *     caller memory and holds no state between calls.
+ *   - Arrays are dense, row-major (C-contiguous).  A packed weight matrix
+ *     [O, I] is stored as O rows of coli_row_bytes(fmt, I) bytes each.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls only enqueue work on it and return; nothing synchronises except
+ *     coli_check_device_flags().
+ *   - Outputs are overwritten, never accumulated into.
+ *   - Return value: COLI_OK (0) or a negative coli_status.  All argument
+ *     checks run on the host before anything is enqueued; on an error nothing
+ *     is launched and no output is touched.  The library never aborts or exits.
+ *   - Sizes of 0 are allowed where stated (an empty batch enqueues nothing).
+ *
+ * Sources (page title -- section):
+ *   glm.c@98759bf  colibri-strix c/glm.c, commit 98759bf
+ *   glm.c@97c756a  colibri-strix c/glm.c, commit 97c756a
+ *   metal@93cde63  colibri c/backend_metal.mm, commit 93cde63
+ *   docs-quickstart  colibri compare main...docs-quickstart (qt_resolve_fmt)
+ */
+#ifndef COLI_H
+#define COLI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Weight row formats: the QT tensor's fmt codes [glm.c@98759bf -- typedef QT].
+ *   COLI_F32 : fp32 values, 4*I bytes per row.
+ *   COLI_I8  : signed int8 values, I bytes per row   [glm.c@98759bf -- matmul_q]
+ *   COLI_I4  : two values per byte, (I+1)/2 bytes per row; element 2k is the
+ *              low nibble of byte k, 2k+1 the high nibble; value = nibble - 8
+ *              [glm.c@98759bf -- matmul_i4, pack_int4]
+ *   COLI_I2  : four values per byte, (I+3)/4 bytes per row; element i is bits
+ *              2*(i%4)..2*(i%4)+1 of byte i/4; value = crumb - 2
+ *              [glm.c@98759bf -- matmul_i2, pack_int2]
+ * Padding nibbles / crumbs past I in a row's last byte are never read. */
+enum coli_fmt { COLI_F32 = 0, COLI_I8 = 1, COLI_I4 = 2, COLI_I2 = 3 };
+
+enum coli_status {
+    COLI_OK = 0,
+    COLI_EINVAL = -1,     /* a required pointer is NULL, or a flag is out of its range */
+    COLI_ESHAPE = -2,     /* a size is negative, or a byte count overflows int64 */
+    COLI_EFMT = -3,       /* unknown weight format, or one this call does not take */
+    COLI_EALIGN = -4,     /* a pointer is not aligned as the call requires */
+    COLI_ERANGE = -5,     /* K, E or another count outside its supported range */
+    COLI_EWORKSPACE = -6, /* workspace NULL or smaller than the size query says */
+    COLI_EDEVICE = -7,    /* the HIP runtime reported an error */
+    COLI_EIDX = -8        /* coli_check_device_flags: bad routing ids were seen */
+};
+
+/* Precision of the MoE expert products.
+ *   COLI_PREC_FP32: fp32 activations, fp32 accumulation; every float output
+ *     meets |y - y_ref| <= 1e-4 * (scale * sum |v * x|) + 1e-6.
+ *   COLI_PREC_BF16: activations rounded to bf16 and int weights converted
+ *     exactly to bf16 for the matrix cores, fp32 accumulation, scale applied
+ *     in fp32 after the sum; bound 2e-2 of the same magnitude.  Meant for
+ *     prefill-sized batches. */
+enum coli_prec { COLI_PREC_FP32 = 0, COLI_PREC_BF16 = 1 };
+
+/* Bytes in one packed row of I elements, or -1 for an unknown fmt / I < 0
+ * [glm.c@98759bf -- qt_bytes].  Host only; no device work. */
+int64_t coli_row_bytes(int fmt, int64_t I);
+
+/* Quantized matrix-vector product, dequantised on use
+ *     y[s, o] = scale[o] * sum_{i<I} v(o, i) * x[s, i]
+ * [glm.c@98759bf -- matmul_q, matmul_i4, matmul_i2, matmul_qt;
+ *  metal@93cde63 -- mm_gemv].  The per-row scale multiplies the finished sum.
+ *   fmt    COLI_F32 / I8 / I4 / I2.
+ *   W      [O, coli_row_bytes(fmt, I)] bytes, 4-byte aligned.
+ *   scale  [O] fp32.  May be NULL only for COLI_F32 (then 1), since glm.c's
+ *          f32 rows carry no scale while the Metal kernel applies one.
+ *   x      [S, I] fp32, 4-byte aligned.
+ *   y      [S, O] fp32, overwritten.
+ *   S, I, O >= 0.  S == 0 or O == 0 enqueues nothing; I == 0 writes zeros.
+ * Errors: COLI_EFMT, COLI_EINVAL (NULL array), COLI_ESHAPE, COLI_EALIGN,
+ * COLI_EDEVICE. */
+int coli_qgemv(int fmt, const void *W, const float *scale, const float *x,
+               float *y, int S, int I, int O, void *stream);
+
+/* Router: sigmoid scores and noaux_tc top-K with one group
+ * [glm.c@98759bf -- moe, phase A; metal@93cde63 -- r_router, r_top8,
+ *  r_top8_par].  For each token s:
+ *     logit[e] = sum_d Wr[e, d] * x[s, d]      (accumulated in fp64)
+ *     sig[s,e] = fp32(1 / (1 + exp(-logit[e])))  (fp64, rounded once)
+ *     choice[e] = sig[s,e] + bias[e]           (fp32 add)
+ *     K picks: the largest choice among experts not yet taken; equal
+ *              choices go to the lower expert index.
+ *     w[kk] = sig[s, idx[kk]]  (the score, not the choice)
+ *     topp in (0,1): reorder the picks by descending weight (stable) and keep
+ *              the shortest prefix whose running fp32 sum reaches
+ *              topp * (1e-20 + total); keff[s] = its length; else keff[s] = K.
+ *     norm_topk != 0: w[kk] /= (sum_{kk<keff} w + 1e-20), in fp32.
+ *     w[kk] *= routed_scale.
+ *   Wr    [E, D] fp32.   bias [E] fp32.   x [S, D] fp32.
+ *   idx   [S, K] int32 out; slots kk >= keff[s] hold -1.
+ *   w     [S, K] fp32 out; slots kk >= keff[s] hold 0.
+ *   keff  [S] int32 out, or NULL.
+ *   sig   [S, E] fp32 out (the sigmoid scores); required.
+ *   ws    device scratch of ws_bytes >= coli_router_workspace_bytes(S, E, D)
+ *         bytes, 8-byte aligned (partial fp64 logits).
+ *   1 <= K <= min(E, 64), 1 <= E <= 1024, D >= 1, S >= 0.
+ * Errors: COLI_EINVAL, COLI_ESHAPE, COLI_ERANGE, COLI_EALIGN, COLI_EWORKSPACE,
+ * COLI_EDEVICE. */
+int coli_router(const float *Wr, const float *bias, const float *x, int S,
+                int E, int D, int K, int norm_topk, float routed_scale,
+                float topp, int32_t *idx, float *w, int32_t *keff, float *sig,
+                void *ws, size_t ws_bytes, void *stream);
+
+/* Scratch bytes coli_router needs for S tokens, E experts, width D (0 for
+ * invalid arguments).  Host only. */
+size_t coli_router_workspace_bytes(int S, int E, int D);
+
+/* Routed experts stacked in one allocation per tensor
+ * [glm.c@98759bf -- typedef ESlot; metal@93cde63 -- moe_submit]:
+ *   w_gate, w_up  [E, F, coli_row_bytes(fmt, D)] bytes,
+ *   w_down        [E, D, coli_row_bytes(fmt, F)] bytes,
+ *   s_gate, s_up  [E, F] fp32,   s_down [E, D] fp32.
+ * fmt is one of COLI_I8 / I4 / I2 (all three tensors share it). */
+typedef struct {
+    int fmt;
+    int E, D, F;
+    const void *w_gate, *w_up, *w_down;
+    const float *s_gate, *s_up, *s_down;
+} coli_experts;
+
+/* One SwiGLU MLP applied with weight 1 to every token: the shared expert
+ * [glm.c@98759bf -- moe, phase E; dense_mlp]:  down(silu(gate x) * up x).
+ *   w_gate, w_up [F, coli_row_bytes(fmt, D)], w_down [D, coli_row_bytes(fmt, F)],
+ *   s_gate, s_up [F], s_down [D].  D is the experts' D. */
+typedef struct {
+    int fmt;
+    int F;
+    const void *w_gate, *w_up, *w_down;
+    const float *s_gate, *s_up, *s_down;
+} coli_mlp;
+
+/* Router parameters for coli_moe_layer (see coli_router).  E and D are the
+ * experts'. */
+typedef struct {
+    const float *w;     /* [E, D] fp32 */
+    const float *bias;  /* [E] fp32 (e_score_correction_bias) */
+    int K;
+    int norm_topk;
+    float routed_scale;
+    float topp;         /* <= 0 or >= 1: off */
+} coli_router_params;
+
+/* Device workspace size (bytes) needed by coli_moe_gemv / coli_moe_layer for
+ * S tokens, K slots per token, E experts of width D x F, a shared expert of
+ * width F_shared (0 = none), at precision prec.  Returns 0 for invalid
+ * arguments.  Host only.  The workspace needs 256-byte alignment. */
+size_t coli_moe_workspace_bytes(int S, int K, int E, int D, int F,
+                                int F_shared, int prec);
+
+/* Byte offsets of the documented regions inside the workspace, for callers
+ * that want the intermediates (all relative to the workspace base; a region
+ * absent for the given arguments has offset -1):
+ *   flags      uint32: bit 0 = an expert id outside [-1, E) was skipped,
+ *                      bit 1 = a token listed one expert twice.
+ *   sig        [S, E] fp32 router scores (coli_moe_layer running the router).
+ *   idx, w     [S, K] routing used (copy of the inputs or the router's).
+ *   offsets    [E + 1] int32: rows of expert e are offsets[e]..offsets[e+1]-1
+ *              in the grouped order.
+ *   row_pair   [S*K] int32: grouped row r holds pair p = s*K + kk.
+ *   pair_row   [S*K] int32: inverse map (-1 for a skipped slot).
+ *   counts     [E] int32: rows per expert.
+ *   h          [S*K + S, Fmax] fp32: SwiGLU output per grouped row; the
+ *              shared expert's row for token s is S*K + s.
+ *   y          [S*K + S, D] fp32: expert output per grouped row (same
+ *              numbering), before the routing weight.
+ *   router_part  fp64 partial router logits (scratch). */
+typedef struct {
+    int64_t flags, sig, idx, w, offsets, counts, row_pair, pair_row, h, y, router_part;
+    int64_t h_ld;   /* row stride of h in floats (max of F and F_shared) */
+    int64_t total;  /* == coli_moe_workspace_bytes(...) */
+} coli_ws_layout;
+
+int coli_moe_workspace_layout(int S, int K, int E, int D, int F, int F_shared,
+                              int prec, coli_ws_layout *out /* host */);
+
+/* Routed experts for S tokens with given routing (the batch-union MoE, phases
+ * B and D) [glm.c@98759bf -- moe, phases B and D; metal@93cde63 -- moe_gemv,
+ * moe_silu, moe_finish; glm.c@97c756a -- matmul_i4_pair, expert_gate_up]:
+ *     out[s] = sum_{kk : idx[s,kk] >= 0} w[s,kk] * down_e(silu(gate_e x_s) * up_e x_s),
+ *     e = idx[s,kk].
+ * Slots are grouped by expert on the device (stable in s*K + kk order) so each
+ * active expert's weights stream from memory once per call; gate and up are
+ * computed in one pass over x and SwiGLU is applied before h is stored; the
+ * weighted sum runs in slot order kk = 0..K-1, so results are deterministic.
+ *   ex     routed experts (device pointers inside; the struct itself is host).
+ *   x      [S, D] fp32.   idx [S, K] int32: an expert id, or -1 = empty slot.
+ *   w      [S, K] fp32.   out [S, D] fp32, overwritten.
+ *   prec   COLI_PREC_FP32 or COLI_PREC_BF16.
+ *   ws     device workspace of ws_bytes >= coli_moe_workspace_bytes(S,K,E,D,F,0,prec).
+ * An id < -1 or >= E is skipped and a listed-twice expert is computed twice;
+ * both set a flag that coli_check_device_flags() reports.
+ * 1 <= K <= 64, 1 <= E <= 1024, S >= 0, D, F >= 1.
+ * Errors: COLI_EINVAL, COLI_EFMT, COLI_ESHAPE, COLI_ERANGE, COLI_EALIGN,
+ * COLI_EWORKSPACE, COLI_EDEVICE. */
+int coli_moe_gemv(const coli_experts *ex, const float *x, int S, int K,
+                  const int32_t *idx, const float *w, float *out, int prec,
+                  void *ws, size_t ws_bytes, void *stream);
+
+/* Full MoE block for S tokens (ragged decode rows or a prefill batch):
+ * router (unless routing is given), routed experts, shared expert, combine
+ * [glm.c@98759bf -- moe, phases A, B, D, E; metal@93cde63 --
+ *  coli_metal_layer_decode, coli_metal_moe_block]:
+ *     out[s] = sum_kk w[s,kk] * expert_{idx[s,kk]}(x_s)  +  shared(x_s).
+ *   r          router parameters; used when pre_idx == NULL.
+ *   ex         routed experts.   shared: the shared expert, or NULL.
+ *   x          [S, D] fp32.
+ *   pre_idx, pre_w  [S, K] given routing (both or neither), the analogue of
+ *              routing computed elsewhere and handed to moe(); when given the
+ *              router does not run.
+ *   out        [S, D] fp32, overwritten.
+ *   idx_out, w_out  [S, K] routing actually used, or NULL.
+ *   ws, ws_bytes    as coli_moe_gemv, sized with F_shared = shared ? shared->F : 0.
+ * Errors: as coli_moe_gemv. */
+int coli_moe_layer(const coli_router_params *r, const coli_experts *ex,
+                   const coli_mlp *shared, const float *x, int S,
+                   const int32_t *pre_idx, const float *pre_w, float *out,
+                   int32_t *idx_out, float *w_out, int prec, void *ws,
+                   size_t ws_bytes, void *stream);
+
+/* Waits for `stream`, then reads the workspace flags the last MoE call on it
+ * left.  *flags_out (host, may be NULL) receives the raw bits.  Returns
+ * COLI_OK when none is set, COLI_EIDX when a routing id was skipped or
+ * duplicated, COLI_EDEVICE on a runtime error. */
+int coli_check_device_flags(const void *ws, void *stream, uint32_t *flags_out);
+
+/* Static text for a status code. */
+const char *coli_strerror(int status);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int coli_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* COLI_H */

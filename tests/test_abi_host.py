@@ -1,0 +1,145 @@
+"""Host-only checks of the C ABI: the library loads, exports every function
+include/coli.h declares, and rejects bad arguments before touching a device
+(no compute call is made, so these run without a GPU)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "coli.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from weight_streaming_gemv_qgemv_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from weight_streaming_gemv_qgemv_amd import build
+        build.build()
+    return binding.lib()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(coli_[a-z0-9_]+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_header_declares_entry_points():
+    names = _declared()
+    for n in ("coli_qgemv", "coli_moe_gemv", "coli_moe_layer", "coli_router",
+              "coli_check_device_flags", "coli_strerror", "coli_moe_workspace_bytes"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    for n in _declared():
+        assert hasattr(L, n), n
+
+
+def test_binding_covers_exports():
+    from weight_streaming_gemv_qgemv_amd import binding
+    assert set(binding.EXPORTS) == set(_declared())
+
+
+def test_row_bytes_and_strerror(L):
+    from weight_streaming_gemv_qgemv_amd import binding as b
+    assert [b.row_bytes(f, 7) for f in (0, 1, 2, 3)] == [28, 7, 4, 2]
+    assert b.row_bytes(2, 6144) == 3072 and b.row_bytes(3, 6144) == 1536
+    assert b.row_bytes(9, 4) == -1 and b.row_bytes(2, -1) == -1
+    for s in range(-8, 1):
+        assert b.strerror(s)
+    assert L.coli_version() >= 10000
+
+
+FAKE = 0x10000  # a 16-byte aligned non-null pointer value; never dereferenced
+
+
+def test_qgemv_rejects_before_launch(L):
+    from weight_streaming_gemv_qgemv_amd import binding as b
+    q = b.qgemv_raw
+    assert q(4, FAKE, FAKE, FAKE, FAKE, 1, 8, 8) == b.EFMT
+    assert q(-1, FAKE, FAKE, FAKE, FAKE, 1, 8, 8) == b.EFMT
+    assert q(2, FAKE, FAKE, FAKE, FAKE, -1, 8, 8) == b.ESHAPE
+    assert q(2, FAKE, FAKE, FAKE, FAKE, 1, -8, 8) == b.ESHAPE
+    assert q(2, FAKE, FAKE, FAKE, None, 1, 8, 8) == b.EINVAL
+    assert q(2, None, FAKE, FAKE, FAKE, 1, 8, 8) == b.EINVAL
+    assert q(2, FAKE, None, FAKE, FAKE, 1, 8, 8) == b.EINVAL      # int formats need scales
+    assert q(2, FAKE + 1, FAKE, FAKE, FAKE, 1, 8, 8) == b.EALIGN
+    assert q(2, FAKE, FAKE, FAKE + 2, FAKE, 1, 8, 8) == b.EALIGN
+    # empty batches are valid no-ops (nothing is launched)
+    assert q(2, FAKE, FAKE, FAKE, FAKE, 0, 8, 8) == b.OK
+    assert q(2, FAKE, FAKE, FAKE, FAKE, 3, 8, 0) == b.OK
+    # overflow of S*O*4
+    assert q(0, FAKE, FAKE, FAKE, FAKE, 2**31 - 1, 2**31 - 1, 2**31 - 1) == b.ESHAPE
+
+
+def test_router_rejects_before_launch(L):
+    from weight_streaming_gemv_qgemv_amd import binding as b
+    r = L.coli_router
+    ws = b.router_workspace_bytes(4, 16, 64)
+    assert ws > 0
+    args = dict(Wr=FAKE, bias=FAKE, x=FAKE, S=4, E=16, D=64, K=4, norm=1, rs=2.5, topp=0.0,
+                idx=FAKE, w=FAKE, keff=None, sig=FAKE, ws=FAKE, wsb=ws)
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        return r(a["Wr"], a["bias"], a["x"], a["S"], a["E"], a["D"], a["K"], a["norm"], a["rs"],
+                 a["topp"], a["idx"], a["w"], a["keff"], a["sig"], a["ws"], a["wsb"], None)
+
+    assert call(K=17) == b.ERANGE
+    assert call(K=0) == b.ERANGE
+    assert call(E=2000, K=4) == b.ERANGE
+    assert call(K=65, E=100) == b.ERANGE
+    assert call(sig=None) == b.EINVAL
+    assert call(norm=2) == b.EINVAL
+    assert call(ws=None) == b.EWORKSPACE
+    assert call(wsb=ws - 8) == b.EWORKSPACE
+    assert call(x=FAKE + 2) == b.EALIGN
+    assert call(S=0) == b.OK
+
+
+def test_moe_rejects_before_launch(L):
+    from weight_streaming_gemv_qgemv_amd import binding as b
+    E, D, F, S, K = 8, 64, 32, 4, 2
+    ex = b.Experts(2, E, D, F, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    need = b.moe_workspace_bytes(S, K, E, D, F, 0, 0)
+    assert need > 0
+
+    def call(ex=ex, x=FAKE, S=S, K=K, idx=FAKE, w=FAKE, out=FAKE, prec=0, ws=FAKE, wsb=need):
+        return L.coli_moe_gemv(C.byref(ex), x, S, K, idx, w, out, prec, ws, wsb, None)
+
+    assert call(wsb=need - 1) == b.EWORKSPACE
+    assert call(ws=None) == b.EWORKSPACE
+    assert call(ws=FAKE + 16) == b.EALIGN
+    assert call(K=65) == b.ERANGE
+    assert call(prec=7) == b.EINVAL
+    assert call(idx=None) == b.EINVAL
+    assert call(S=0) == b.OK
+    bad = b.Experts(0, E, D, F, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)   # f32 experts unsupported
+    assert call(ex=bad) == b.EFMT
+    big = b.Experts(2, 2048, D, F, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert call(ex=big) == b.ERANGE
+    nul = b.Experts(2, E, D, F, FAKE, None, FAKE, FAKE, FAKE, FAKE)
+    assert call(ex=nul) == b.EINVAL
+    # layer: routing given as only one of the pair
+    rp = b.RouterParams(FAKE, FAKE, K, 1, 2.5, 0.0)
+    assert L.coli_moe_layer(C.byref(rp), C.byref(ex), None, FAKE, S, FAKE, None, FAKE, None, None,
+                            0, FAKE, need, None) == b.EINVAL
+
+
+def test_workspace_layout_is_consistent(L):
+    from weight_streaming_gemv_qgemv_amd import binding as b
+    for (S, K, E, D, F, Fs) in [(1, 1, 1, 1, 1, 0), (64, 8, 256, 6144, 2048, 2048),
+                                (2048, 8, 256, 6144, 2048, 2048), (5, 3, 24, 40, 24, 16)]:
+        lay = b.moe_workspace_layout(S, K, E, D, F, Fs)
+        assert lay["total"] == b.moe_workspace_bytes(S, K, E, D, F, Fs)
+        regions = sorted((v, k) for k, v in lay.items() if k not in ("total", "h_ld"))
+        assert all(v % 256 == 0 for v, _ in regions)
+        assert lay["h_ld"] == max(F, Fs)
+        rows = S * K + (S if Fs else 0)
+        assert lay["y"] + rows * D * 4 <= lay["total"]
+        assert lay["h"] + rows * max(F, Fs) * 4 <= lay["y"]

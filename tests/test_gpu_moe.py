@@ -1,0 +1,262 @@
+"""GPU parity of coli_moe_gemv / coli_moe_layer against the oracle.
+
+Bars (COLI_PREC_FP32):
+  out:  |out - ref| <= 1e-4 * M_out + 1e-6, M_out = sum_k |w_k| |sd[o]| sum_j
+        |vd(o,j) h_j| (+ the shared expert's term): the per-product bound of
+        the last contraction, weighted as it is combined;
+  h:    the SwiGLU output per grouped row, against the oracle's h with the
+        first-order propagation of the gate/up bounds:
+        1e-4 * (1.1 * Mg |u| + |silu(g)| Mu) + 1e-6;
+  y:    each expert's down output per grouped row, against the oracle's down
+        product of the DEVICE's own h (a plain per-product bound).
+Expert ids and grouping are integers: checked exactly."""
+import numpy as np
+import pytest
+
+from gpu_helpers import announce, assert_within, need_gpu, to_dev
+from weight_streaming_gemv_qgemv_amd import synth
+
+pytestmark = pytest.mark.gpu
+REL = 1e-4
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return need_gpu()
+
+
+def dev_bank(bank, dev):
+    out = dict(bank)
+    for k in ("wg", "wu", "wd", "sg", "su", "sd"):
+        out[k] = to_dev(bank[k], dev)
+    return out
+
+
+def silu(z):
+    return z / (1.0 + np.exp(-z))
+
+
+def read_ws(ws, lay, S, K, D, Fld, rows):
+    raw = ws.cpu().numpy()
+
+    def arr(off, n, dt):
+        return np.frombuffer(raw[off:off + n * np.dtype(dt).itemsize].tobytes(), dtype=dt)
+
+    P = S * K
+    return dict(
+        flags=int(arr(lay["flags"], 1, np.uint32)[0]),
+        pair_row=arr(lay["pair_row"], P, np.int32),
+        row_pair=arr(lay["row_pair"], P, np.int32),
+        h=arr(lay["h"], rows * Fld, np.float32).reshape(rows, Fld),
+        y=arr(lay["y"], rows * D, np.float32).reshape(rows, D),
+    )
+
+
+def check_moe(orc, bank, shared, x, idx, w, out, ws, lay, what, rel=REL):
+    S, K = idx.shape
+    D, F = bank["D"], bank["F"]
+    ref = orc.moe(bank, shared, x, idx, w.astype(np.float64), intermediates=True)
+    assert_within(out, ref["out"], ref["mag"], rel, what=what + " out")
+    rows = S * K + (S if shared is not None else 0)
+    wsd = read_ws(ws, lay, S, K, D, lay["h_ld"], rows)
+    # grouping: pair_row is a bijection onto the kept slots, ordered by expert
+    # then slot
+    valid = (idx.reshape(-1) >= 0) & (idx.reshape(-1) < bank["E"])
+    pr = wsd["pair_row"]
+    assert np.all(pr[~valid] == -1)
+    kept = np.nonzero(valid)[0]
+    order = kept[np.lexsort((kept, idx.reshape(-1)[kept]))]
+    np.testing.assert_array_equal(pr[order], np.arange(len(order)))
+    np.testing.assert_array_equal(wsd["row_pair"][:len(order)], order)
+    # h per kept slot
+    for p in kept[:: max(1, len(kept) // 64)]:
+        r = pr[p]
+        hg = wsd["h"][r, :F]
+        g, u = ref["g"][p], ref["u"][p]
+        bound_mag = 1.1 * ref["gmag"][p] * np.abs(u) + np.abs(silu(g)) * ref["umag"][p]
+        assert_within(hg, ref["h"][p], bound_mag, rel, what=f"{what} h slot {p}")
+        e = idx.reshape(-1)[p]
+        yref, ymag = orc.qgemv(bank["fmt"], bank["wd"][e], bank["sd"][e],
+                               hg.astype(np.float64)[None, :])
+        assert_within(wsd["y"][r], yref[0], ymag[0], rel, what=f"{what} y slot {p}")
+    if shared is not None:
+        for s in range(0, S, max(1, S // 8)):
+            r = S * K + s
+            hs = wsd["h"][r, :shared["F"]]
+            yref, ymag = orc.qgemv(shared["fmt"], shared["wd"], shared["sd"],
+                                   hs.astype(np.float64)[None, :])
+            assert_within(wsd["y"][r], yref[0], ymag[0], rel, what=f"{what} shared y {s}")
+    return wsd
+
+
+def run_gemv(dev, bank_d, x, idx, w, prec=0):
+    import torch
+    from weight_streaming_gemv_qgemv_amd import binding as b
+    out, ws = b.moe_gemv(bank_d, to_dev(x, dev), to_dev(idx, dev), to_dev(w, dev), prec=prec)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), ws
+
+
+@pytest.mark.parametrize("fmt", [1, 2, 3])
+def test_moe_gemv_tiny_unaligned(dev, orc, fmt):
+    from weight_streaming_gemv_qgemv_amd import binding as b
+    E, D, F, S, K = 6, 40, 24, 5, 3
+    bank = synth.expert_bank(10 + fmt, fmt, E, D, F)
+    g = synth.rng(11, fmt)
+    x = synth.activations(g, S, D)
+    idx, w = synth.routing_uniform(g, S, K, E)
+    announce("moe tiny", fmt)
+    out, ws = run_gemv(dev, dev_bank(bank, dev), x, idx, w)
+    lay = b.moe_workspace_layout(S, K, E, D, F)
+    wsd = check_moe(orc, bank, None, x, idx, w, out, ws, lay, f"tiny fmt{fmt}")
+    assert wsd["flags"] == 0
+
+
+@pytest.mark.parametrize("fmt", [1, 2, 3])
+def test_moe_gemv_tiles_aligned(dev, orc, fmt):
+    from weight_streaming_gemv_qgemv_amd import binding as b
+    E, D, F, S, K = 16, 512, 256, 21, 4
+    bank = synth.expert_bank(20 + fmt, fmt, E, D, F)
+    g = synth.rng(21, fmt)
+    x = synth.activations(g, S, D)
+    idx, w = synth.routing_uniform(g, S, K, E)
+    idx[0, :] = [3, 4, 5, 6]
+    idx[1:12, 0] = 3          # one expert with many rows (several token passes)
+    for s in range(1, 12):
+        row = [3] + [e for e in g.permutation(E) if e != 3][:K - 1]
+        idx[s] = row
+    announce("moe tiles", fmt)
+    out, ws = run_gemv(dev, dev_bank(bank, dev), x, idx, w)
+    lay = b.moe_workspace_layout(S, K, E, D, F)
+    check_moe(orc, bank, None, x, idx, w, out, ws, lay, f"tiles fmt{fmt}")
+
+
+def test_moe_gemv_skipped_and_bad_slots(dev, orc):
+    from weight_streaming_gemv_qgemv_amd import binding as b
+    E, D, F, S, K = 8, 256, 128, 6, 3
+    bank = synth.expert_bank(30, 2, E, D, F)
+    g = synth.rng(31)
+    x = synth.activations(g, S, D)
+    idx, w = synth.routing_uniform(g, S, K, E)
+    idx[0, 2] = -1                 # empty slot: skipped, no flag
+    announce("moe skipped slot")
+    out, ws = run_gemv(dev, dev_bank(bank, dev), x, idx, w)
+    lay = b.moe_workspace_layout(S, K, E, D, F)
+    check_moe(orc, bank, None, x, idx, w, out, ws, lay, "skipped")
+    assert b.check_device_flags(ws) == (b.OK, 0)
+    bad = idx.copy()
+    bad[1, 0] = E + 3              # out of range: skipped and flagged
+    bad[2, 1] = -7
+    announce("moe bad ids")
+    out, ws = run_gemv(dev, dev_bank(bank, dev), x, bad, w)
+    rc, flags = b.check_device_flags(ws)
+    assert rc == b.EIDX and flags & 1
+    masked = bad.copy()
+    masked[(masked < 0) | (masked >= E)] = -1
+    ref = orc.moe(bank, None, x, masked, w.astype(np.float64))
+    assert_within(out, ref["out"], ref["mag"], REL, what="bad ids")
+    dup = idx.copy()
+    dup[3, 1] = dup[3, 0]          # listed twice: computed twice and flagged
+    announce("moe duplicate id")
+    out, ws = run_gemv(dev, dev_bank(bank, dev), x, dup, w)
+    rc, flags = b.check_device_flags(ws)
+    assert rc == b.EIDX and flags & 2
+    ref = orc.moe(bank, None, x, dup, w.astype(np.float64))
+    assert_within(out, ref["out"], ref["mag"], REL, what="dup")
+
+
+def test_moe_layer_small_with_router_and_shared(dev, orc):
+    import torch
+    from weight_streaming_gemv_qgemv_amd import binding as b
+    E, D, F, S, K = 24, 512, 256, 13, 4
+    bank = synth.expert_bank(40, 2, E, D, F)
+    shared = synth.shared_mlp(40, 2, D, F)
+    g = synth.rng(41)
+    Wr, bias = synth.router_weights(g, E, D)
+    x = synth.activations(g, S, D)
+    announce("moe layer small")
+    bd = dev_bank(bank, dev)
+    sd = dev_bank(shared, dev)
+    rp = dict(w=to_dev(Wr, dev), bias=to_dev(bias, dev), K=K, norm_topk=1, routed_scale=2.5)
+    idx_o = torch.empty((S, K), dtype=torch.int32, device=dev)
+    w_o = torch.empty((S, K), dtype=torch.float32, device=dev)
+    out, ws = b.moe_layer(rp, bd, sd, to_dev(x, dev), idx_out=idx_o, w_out=w_o)
+    torch.cuda.synchronize()
+    r = orc.router(Wr, bias, x, K, 1, 2.5)
+    np.testing.assert_array_equal(idx_o.cpu().numpy(), r["idx"])
+    wg = w_o.cpu().numpy()
+    np.testing.assert_allclose(wg, r["w"], rtol=1e-6)
+    lay = b.moe_workspace_layout(S, K, E, D, F, F)
+    check_moe(orc, bank, shared, x, r["idx"], wg, out.cpu().numpy(), ws, lay, "layer small")
+    # shared only: all routed weights zero
+    announce("moe layer shared only")
+    z = np.zeros((S, K), np.float32)
+    out2, _ = b.moe_layer(None, bd, sd, to_dev(x, dev), pre_idx=to_dev(r["idx"], dev),
+                          pre_w=to_dev(z, dev))
+    torch.cuda.synchronize()
+    ref = orc.moe(bank, shared, x, r["idx"], z.astype(np.float64))
+    assert_within(out2.cpu().numpy(), ref["out"], ref["mag"], REL, what="shared only")
+
+
+def test_moe_layer_empty_batch(dev):
+    import torch
+    from weight_streaming_gemv_qgemv_amd import binding as b
+    announce("moe empty")
+    E, D, F = 8, 64, 32
+    bd = dev_bank(synth.expert_bank(50, 2, E, D, F), dev)
+    x = torch.zeros((0, D), device=dev)
+    out = torch.zeros((0, D), device=dev)
+    idx = torch.zeros((0, 2), dtype=torch.int32, device=dev)
+    w = torch.zeros((0, 2), device=dev)
+    o, _ = b.moe_gemv(bd, x, idx, w, out=out)
+    assert o.shape == (0, D)
+
+
+# ---------------------------------------------------------------- full size
+@pytest.fixture(scope="module")
+def glm_bank():
+    """256 experts of width 6144 x 2048, int4 (4.8 GB host), plus the shared
+    expert."""
+    bank = synth.expert_bank(3000, 2, 256, 6144, 2048)
+    shared = synth.shared_mlp(3000, 2, 6144, 2048)
+    return bank, shared
+
+
+def test_expert_decode_16_tokens(dev, orc, glm_bank):
+    """256 int4 experts, 16 tokens, given top-8 routing: full oracle check."""
+    from weight_streaming_gemv_qgemv_amd import binding as b
+    bank, _ = glm_bank
+    g = synth.rng(3001)
+    S, K = 16, 8
+    x = synth.activations(g, S, 6144)
+    idx, w = synth.routing_uniform(g, S, K, 256)
+    announce("moe decode 16 tokens")
+    out, ws = run_gemv(dev, dev_bank(bank, dev), x, idx, w)
+    lay = b.moe_workspace_layout(S, K, 256, 6144, 2048)
+    check_moe(orc, bank, None, x, idx, w, out, ws, lay, "decode16")
+
+
+def test_layer_decode_64_tokens(dev, orc, glm_bank):
+    """Full layer, 64 ragged decode rows: router + 256 int4 experts + shared;
+    ids exact on all 64 tokens, outputs checked on 16 sampled tokens."""
+    import torch
+    from weight_streaming_gemv_qgemv_amd import binding as b
+    bank, shared = glm_bank
+    g = synth.rng(3002)
+    S, K, E, D = 64, 8, 256, 6144
+    Wr, bias = synth.router_weights(g, E, D)
+    x = synth.activations(g, S, D)
+    announce("moe layer 64 tokens")
+    rp = dict(w=to_dev(Wr, dev), bias=to_dev(bias, dev), K=K, norm_topk=1, routed_scale=2.5)
+    idx_o = torch.empty((S, K), dtype=torch.int32, device=dev)
+    w_o = torch.empty((S, K), dtype=torch.float32, device=dev)
+    out, ws = b.moe_layer(rp, dev_bank(bank, dev), dev_bank(shared, dev), to_dev(x, dev),
+                          idx_out=idx_o, w_out=w_o)
+    torch.cuda.synchronize()
+    r = orc.router(Wr, bias, x, K, 1, 2.5)
+    np.testing.assert_array_equal(idx_o.cpu().numpy(), r["idx"])
+    wg = w_o.cpu().numpy()
+    np.testing.assert_allclose(wg, r["w"], rtol=1e-6)
+    toks = np.sort(g.choice(S, 16, replace=False))
+    ref = orc.moe(bank, shared, x[toks], r["idx"][toks], wg[toks].astype(np.float64))
+    assert_within(out.cpu().numpy()[toks], ref["out"], ref["mag"], REL, what="layer64")

@@ -1,0 +1,153 @@
+"""GPU parity of coli_qgemv against the fp64 oracle (through the C ABI).
+
+Bar: |y - y_ref| <= 1e-4 * scale[o] * sum_i |v(o,i) x[s,i]| + 1e-6 for random
+inputs; bit-exact when inputs are small integers and scales powers of two
+(every partial sum is then an exact fp32 value)."""
+import numpy as np
+import pytest
+
+from gpu_helpers import announce, assert_within, need_gpu, to_dev
+from weight_streaming_gemv_qgemv_amd import synth
+
+pytestmark = pytest.mark.gpu
+REL = 1e-4
+FMTS = {"f32": 0, "i8": 1, "i4": 2, "i2": 3}
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return need_gpu()
+
+
+def run_gpu(dev, fmt, W, sc, x, O):
+    import torch
+    from weight_streaming_gemv_qgemv_amd import binding as b
+    y = torch.full((x.shape[0], O), float("nan"), dtype=torch.float32, device=dev)
+    b.qgemv(fmt, to_dev(W, dev), None if sc is None else to_dev(sc, dev), to_dev(x, dev), y, O=O)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
+def test_tiny_shapes_brute_force(dev, orc, fmt):
+    """Every (O, I) in a small grid, ragged I (unaligned rows), S up to 3."""
+    g = synth.rng(100, fmt)
+    for O in (1, 2, 5, 17, 40):
+        for I in (1, 2, 3, 7, 8, 15, 16, 31, 33, 40):
+            S = 1 + (O + I) % 3
+            announce("qgemv tiny", fmt, O, I, S)
+            W = synth.weight_bytes(g, fmt, O, I)
+            sc = synth.scales(g, O)
+            x = synth.activations(g, S, I)
+            ref, mag = orc.qgemv(fmt, W, sc, x)
+            got = run_gpu(dev, fmt, W, sc, x, O)
+            assert_within(got, ref, mag, REL, what=f"fmt{fmt} O{O} I{I} S{S}")
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
+@pytest.mark.parametrize("O,I", [(37, 40), (300, 1000), (257, 4096), (64, 8192 + 64)])
+def test_exact_integer_bitwise(dev, orc, fmt, O, I):
+    """Integer x in [-4, 4] and scales 2^-k: the device result must equal the
+    oracle bit for bit, whatever its summation order."""
+    g = synth.rng(200, fmt, O, I)
+    for S in (1, 3, 8, 9):
+        announce("qgemv exact", fmt, O, I, S)
+        if fmt == 0:
+            W = g.integers(-8, 8, size=(O, I)).astype(np.float32).view(np.uint8)
+        else:
+            W = synth.weight_bytes(g, fmt, O, I)
+        sc = synth.exact_scales(g, O)
+        x = synth.exact_activations(g, S, I)
+        ref, _ = orc.qgemv(fmt, W, sc, x)
+        got = run_gpu(dev, fmt, W, sc, x, O)
+        assert np.array_equal(got.astype(np.float64), ref), f"fmt{fmt} S{S}"
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
+@pytest.mark.parametrize("S", [1, 2, 4, 5, 8, 11])
+def test_several_tiles_ragged(dev, orc, fmt, S):
+    g = synth.rng(300, fmt, S)
+    for O, I in ((129, 2048), (77, 3000), (300, 1024)):
+        announce("qgemv tiles", fmt, O, I, S)
+        W = synth.weight_bytes(g, fmt, O, I)
+        sc = synth.scales(g, O)
+        x = synth.activations(g, S, I)
+        ref, mag = orc.qgemv(fmt, W, sc, x)
+        got = run_gpu(dev, fmt, W, sc, x, O)
+        assert_within(got, ref, mag, REL, what=f"fmt{fmt} O{O} I{I} S{S}")
+
+
+def test_single_int4_qgemv_512x1024(dev, orc):
+    """The small single-matrix workload: int4, O=512, I=1024, S=1 (full check)."""
+    g = synth.rng(1000)
+    W = synth.weight_bytes(g, 2, 512, 1024)
+    sc = synth.scales(g, 512)
+    x = synth.activations(g, 1, 1024)
+    announce("qgemv 512x1024 i4")
+    ref, mag = orc.qgemv(2, W, sc, x)
+    got = run_gpu(dev, 2, W, sc, x, 512)
+    assert_within(got, ref, mag, REL, what="512x1024")
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
+def test_dense_sweep_12288x6144(dev, orc, fmt):
+    """The dense sweep at full size: O=12288, I=6144, S in {1,4,8}; the oracle
+    checks 1536 sampled output rows of every S (rows are independent)."""
+    import torch
+    from weight_streaming_gemv_qgemv_amd import binding as b
+    O, I = 12288, 6144
+    g = synth.rng(2000 + fmt)
+    W = synth.weight_bytes(g, fmt, O, I)
+    sc = synth.scales(g, O)
+    Wd, scd = to_dev(W, dev), to_dev(sc, dev)
+    rows = np.sort(g.choice(O, 1536, replace=False))
+    rows[0], rows[-1] = 0, O - 1
+    for S in (1, 4, 8):
+        announce("qgemv 12288x6144", fmt, S)
+        x = synth.activations(g, S, I)
+        y = torch.empty((S, O), dtype=torch.float32, device=dev)
+        b.qgemv(fmt, Wd, None if fmt == 0 and S == 4 else scd, to_dev(x, dev), y)
+        torch.cuda.synchronize()
+        got = y.cpu().numpy()[:, rows]
+        scs = None if fmt == 0 and S == 4 else sc[rows]
+        ref, mag = orc.qgemv(fmt, W[rows], scs, x)
+        assert_within(got, ref, mag, REL, what=f"fmt{fmt} S{S}")
+
+
+def test_edges_empty_and_zero_width(dev):
+    import torch
+    from weight_streaming_gemv_qgemv_amd import binding as b
+    announce("qgemv edges")
+    y = torch.full((3, 5), 7.0, device=dev)
+    W = torch.zeros((5, 16), dtype=torch.uint8, device=dev)
+    sc = torch.ones(5, device=dev)
+    x = torch.zeros((3, 0), device=dev)
+    # I == 0: the empty sum is 0
+    assert b.lib().coli_qgemv(2, W.data_ptr(), sc.data_ptr(), x.data_ptr(), y.data_ptr(),
+                              3, 0, 5, None) == 0
+    torch.cuda.synchronize()
+    assert torch.all(y == 0)
+    # S == 0 and O == 0 write nothing
+    y.fill_(7.0)
+    assert b.lib().coli_qgemv(2, W.data_ptr(), sc.data_ptr(), x.data_ptr(), y.data_ptr(),
+                              0, 16, 5, None) == 0
+    assert b.lib().coli_qgemv(2, W.data_ptr(), sc.data_ptr(), x.data_ptr(), y.data_ptr(),
+                              3, 16, 0, None) == 0
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0)
+
+
+def test_closed_form_rows_on_device(dev):
+    """All-zero nibble rows give -8 * scale * sum(x) on the device too."""
+    import torch
+    from weight_streaming_gemv_qgemv_amd import binding as b
+    announce("qgemv closed form")
+    g = synth.rng(4000)
+    I, O = 6144, 64
+    x = synth.exact_activations(g, 2, I)
+    W = np.zeros((O, I // 2), np.uint8)
+    sc = synth.exact_scales(g, O)
+    y = b.qgemv(2, to_dev(W, dev), to_dev(sc, dev), to_dev(x, dev))
+    torch.cuda.synchronize()
+    want = -8.0 * sc[None, :].astype(np.float64) * x.astype(np.float64).sum(1)[:, None]
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), want)

@@ -1,0 +1,238 @@
+"""ctypes binding of libcoli.so (include/coli.h).
+
+Argument marshalling only: tensors become device pointers, the current torch
+stream becomes the hipStream_t, and every step of the computation runs in the
+library's HIP kernels.  There is no fallback: if libcoli.so is missing or a
+call fails, this module raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libcoli.so")
+
+F32, I8, I4, I2 = 0, 1, 2, 3
+PREC_FP32, PREC_BF16 = 0, 1
+OK, EINVAL, ESHAPE, EFMT, EALIGN, ERANGE, EWORKSPACE, EDEVICE, EIDX = 0, -1, -2, -3, -4, -5, -6, -7, -8
+
+
+class ColiError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {strerror(status)} (status {status})")
+        self.status = status
+
+
+class Experts(C.Structure):
+    _fields_ = [("fmt", C.c_int), ("E", C.c_int), ("D", C.c_int), ("F", C.c_int),
+                ("w_gate", C.c_void_p), ("w_up", C.c_void_p), ("w_down", C.c_void_p),
+                ("s_gate", C.c_void_p), ("s_up", C.c_void_p), ("s_down", C.c_void_p)]
+
+
+class Mlp(C.Structure):
+    _fields_ = [("fmt", C.c_int), ("F", C.c_int),
+                ("w_gate", C.c_void_p), ("w_up", C.c_void_p), ("w_down", C.c_void_p),
+                ("s_gate", C.c_void_p), ("s_up", C.c_void_p), ("s_down", C.c_void_p)]
+
+
+class RouterParams(C.Structure):
+    _fields_ = [("w", C.c_void_p), ("bias", C.c_void_p), ("K", C.c_int),
+                ("norm_topk", C.c_int), ("routed_scale", C.c_float), ("topp", C.c_float)]
+
+
+class WsLayout(C.Structure):
+    _fields_ = [(n, C.c_int64) for n in ("flags", "sig", "idx", "w", "offsets", "counts",
+                                          "row_pair", "pair_row", "h", "y", "router_part",
+                                          "h_ld", "total")]
+
+
+EXPORTS = ["coli_row_bytes", "coli_qgemv", "coli_router", "coli_router_workspace_bytes",
+           "coli_moe_workspace_bytes", "coli_moe_workspace_layout", "coli_moe_gemv",
+           "coli_moe_layer", "coli_check_device_flags", "coli_strerror", "coli_version"]
+
+_lib = None
+
+
+def lib():
+    """Load libcoli.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m weight_streaming_gemv_qgemv_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        vp, i32, i64, f32, sz = C.c_void_p, C.c_int, C.c_int64, C.c_float, C.c_size_t
+        L.coli_row_bytes.restype = i64
+        L.coli_row_bytes.argtypes = [i32, i64]
+        L.coli_qgemv.restype = i32
+        L.coli_qgemv.argtypes = [i32, vp, vp, vp, vp, i32, i32, i32, vp]
+        L.coli_router.restype = i32
+        L.coli_router.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, f32, f32, vp, vp, vp, vp,
+                                  vp, sz, vp]
+        L.coli_router_workspace_bytes.restype = sz
+        L.coli_router_workspace_bytes.argtypes = [i32, i32, i32]
+        L.coli_moe_workspace_bytes.restype = sz
+        L.coli_moe_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+        L.coli_moe_workspace_layout.restype = i32
+        L.coli_moe_workspace_layout.argtypes = [i32, i32, i32, i32, i32, i32, i32, C.POINTER(WsLayout)]
+        L.coli_moe_gemv.restype = i32
+        L.coli_moe_gemv.argtypes = [C.POINTER(Experts), vp, i32, i32, vp, vp, vp, i32, vp, sz, vp]
+        L.coli_moe_layer.restype = i32
+        L.coli_moe_layer.argtypes = [C.POINTER(RouterParams), C.POINTER(Experts), C.POINTER(Mlp),
+                                     vp, i32, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+        L.coli_check_device_flags.restype = i32
+        L.coli_check_device_flags.argtypes = [vp, vp, C.POINTER(C.c_uint32)]
+        L.coli_strerror.restype = C.c_char_p
+        L.coli_strerror.argtypes = [i32]
+        L.coli_version.restype = i32
+        L.coli_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return lib().coli_strerror(status).decode()
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _check(rc: int, what: str):
+    if rc != OK:
+        raise ColiError(rc, what)
+
+
+def row_bytes(fmt: int, I: int) -> int:
+    return int(lib().coli_row_bytes(fmt, I))
+
+
+# ------------------------------------------------------------------ qgemv
+def qgemv(fmt: int, W: torch.Tensor, scale, x: torch.Tensor, y: torch.Tensor | None = None,
+          O: int | None = None, stream=None) -> torch.Tensor:
+    """y[s,o] = scale[o] * sum_i v(o,i) x[s,i]; W [O, row_bytes] uint8 (or f32 [O, I])."""
+    S, I = x.shape
+    if O is None:
+        O = W.shape[0]
+    if y is None:
+        y = torch.empty((S, O), dtype=torch.float32, device=x.device)
+    rc = lib().coli_qgemv(fmt, _ptr(W), _ptr(scale), _ptr(x), _ptr(y), S, I, O, _stream(stream))
+    _check(rc, "coli_qgemv")
+    return y
+
+
+def qgemv_raw(fmt, W, scale, x, y, S, I, O, stream=0) -> int:
+    """Direct call with raw pointers / sizes; returns the status code."""
+    return int(lib().coli_qgemv(fmt, W, scale, x, y, S, I, O, stream))
+
+
+# ------------------------------------------------------------------ router
+def router_workspace_bytes(S: int, E: int, D: int) -> int:
+    return int(lib().coli_router_workspace_bytes(S, E, D))
+
+
+def router(Wr, bias, x, K: int, norm_topk: int = 1, routed_scale: float = 2.5, topp: float = 0.0,
+           ws: torch.Tensor | None = None, stream=None):
+    S, D = x.shape
+    E = Wr.shape[0]
+    dev = x.device
+    idx = torch.empty((S, K), dtype=torch.int32, device=dev)
+    w = torch.empty((S, K), dtype=torch.float32, device=dev)
+    keff = torch.empty((S,), dtype=torch.int32, device=dev)
+    sig = torch.empty((S, E), dtype=torch.float32, device=dev)
+    nb = router_workspace_bytes(S, E, D)
+    if ws is None:
+        ws = torch.empty((max(nb, 256),), dtype=torch.uint8, device=dev)
+    rc = lib().coli_router(_ptr(Wr), _ptr(bias), _ptr(x), S, E, D, K, norm_topk, routed_scale,
+                           topp, _ptr(idx), _ptr(w), _ptr(keff), _ptr(sig), _ptr(ws),
+                           ws.numel(), _stream(stream))
+    _check(rc, "coli_router")
+    return dict(idx=idx, w=w, keff=keff, sig=sig)
+
+
+# ------------------------------------------------------------------ MoE
+def experts_struct(ex: dict) -> Experts:
+    return Experts(ex["fmt"], ex["E"], ex["D"], ex["F"], _ptr(ex["wg"]), _ptr(ex["wu"]),
+                   _ptr(ex["wd"]), _ptr(ex["sg"]), _ptr(ex["su"]), _ptr(ex["sd"]))
+
+
+def mlp_struct(sh: dict) -> Mlp:
+    return Mlp(sh["fmt"], sh["F"], _ptr(sh["wg"]), _ptr(sh["wu"]), _ptr(sh["wd"]),
+               _ptr(sh["sg"]), _ptr(sh["su"]), _ptr(sh["sd"]))
+
+
+def moe_workspace_bytes(S, K, E, D, F, F_shared=0, prec=PREC_FP32) -> int:
+    return int(lib().coli_moe_workspace_bytes(S, K, E, D, F, F_shared, prec))
+
+
+def moe_workspace_layout(S, K, E, D, F, F_shared=0, prec=PREC_FP32) -> dict:
+    L = WsLayout()
+    rc = lib().coli_moe_workspace_layout(S, K, E, D, F, F_shared, prec, C.byref(L))
+    _check(rc, "coli_moe_workspace_layout")
+    return {n: getattr(L, n) for n, _ in WsLayout._fields_}
+
+
+def alloc_workspace(nbytes: int, device) -> torch.Tensor:
+    # torch's caching allocator returns 512-byte aligned blocks
+    t = torch.empty((max(nbytes, 256),), dtype=torch.uint8, device=device)
+    assert t.data_ptr() % 256 == 0
+    return t
+
+
+def moe_gemv(ex: dict, x, idx, w, out=None, prec=PREC_FP32, ws=None, stream=None):
+    S, D = x.shape
+    K = idx.shape[1]
+    if out is None:
+        out = torch.empty((S, D), dtype=torch.float32, device=x.device)
+    nb = moe_workspace_bytes(S, K, ex["E"], D, ex["F"], 0, prec)
+    if ws is None:
+        ws = alloc_workspace(nb, x.device)
+    es = experts_struct(ex)
+    rc = lib().coli_moe_gemv(C.byref(es), _ptr(x), S, K, _ptr(idx), _ptr(w), _ptr(out), prec,
+                             _ptr(ws), ws.numel(), _stream(stream))
+    _check(rc, "coli_moe_gemv")
+    return out, ws
+
+
+def moe_layer(router_p: dict | None, ex: dict, shared: dict | None, x, pre_idx=None, pre_w=None,
+              out=None, idx_out=None, w_out=None, prec=PREC_FP32, ws=None, K=None, stream=None):
+    S, D = x.shape
+    if K is None:
+        K = router_p["K"] if router_p else pre_idx.shape[1]
+    if out is None:
+        out = torch.empty((S, D), dtype=torch.float32, device=x.device)
+    Fs = shared["F"] if shared is not None else 0
+    nb = moe_workspace_bytes(S, K, ex["E"], D, ex["F"], Fs, prec)
+    if ws is None:
+        ws = alloc_workspace(nb, x.device)
+    rp = RouterParams(_ptr(router_p["w"]) if router_p else None,
+                      _ptr(router_p["bias"]) if router_p else None, K,
+                      int(router_p.get("norm_topk", 1)) if router_p else 1,
+                      float(router_p.get("routed_scale", 2.5)) if router_p else 1.0,
+                      float(router_p.get("topp", 0.0)) if router_p else 0.0)
+    es = experts_struct(ex)
+    sp = C.byref(mlp_struct(shared)) if shared is not None else None
+    rc = lib().coli_moe_layer(C.byref(rp), C.byref(es), sp, _ptr(x), S, _ptr(pre_idx),
+                              _ptr(pre_w), _ptr(out), _ptr(idx_out), _ptr(w_out), prec,
+                              _ptr(ws), ws.numel(), _stream(stream))
+    _check(rc, "coli_moe_layer")
+    return out, ws
+
+
+def check_device_flags(ws, stream=None) -> tuple[int, int]:
+    f = C.c_uint32(0)
+    rc = lib().coli_check_device_flags(_ptr(ws), _stream(stream), C.byref(f))
+    return rc, f.value

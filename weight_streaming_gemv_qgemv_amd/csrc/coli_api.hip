@@ -1,0 +1,430 @@
+// coli_api.hip -- libcoli entry points, expert grouping and the combine.
+//
+// Expert grouping is the pages' batch-union [glm.c@98759bf -- moe, phase B
+// and the per-expert row lists of phase D; metal@93cde63 -- moe_submit's
+// erow table]: every routed slot (s, kk) of an expert becomes one row of that
+// expert's group, groups are laid out expert by expert, and inside a group
+// rows keep slot order s*K + kk, so each active expert streams its weights
+// once per call and the whole result is independent of thread timing.  Here
+// the grouping runs on the device (no host round trip).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "coli.h"
+#include "coli_device.h"
+#include "coli_gemv.h"
+#include "coli_internal.h"
+#include "coli_router.h"
+
+namespace coli {
+
+namespace {
+
+constexpr int kGroupWaves = 16;          // experts per block in the grouping kernels
+constexpr int kWin = 8192;               // slots staged in LDS at a time (32 KB)
+
+// Flags written by the grouping kernel (plain stores from block 0).
+constexpr uint32_t kFlagBadId = 1u;
+constexpr uint32_t kFlagDup = 2u;
+
+// Count the slots of each expert; block 0 also validates every slot.
+__global__ __launch_bounds__(1024) void k_group_count(const int32_t *__restrict__ idx, int P,
+                                                      int K, int E, int32_t *__restrict__ counts,
+                                                      uint32_t *__restrict__ flags)
+{
+    __shared__ int32_t sidx[kWin];
+    __shared__ uint32_t sflag;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int e = blockIdx.x * kGroupWaves + wave;
+    if (threadIdx.x == 0) sflag = 0u;
+    int count = 0;
+    for (int base = 0; base < P; base += kWin) {
+        const int n = min(kWin, P - base);
+        __syncthreads();
+        for (int i = threadIdx.x; i < n; i += blockDim.x) sidx[i] = idx[base + i];
+        __syncthreads();
+        if (e < E) {
+            for (int c = 0; c < n; c += 64) {
+                const int i = c + lane;
+                const bool hit = i < n && sidx[i] == e;
+                count += __popcll(__ballot(hit));
+            }
+        }
+        if (blockIdx.x == 0) {
+            uint32_t f = 0u;
+            for (int i = threadIdx.x; i < n; i += blockDim.x) {
+                const int p = base + i;
+                const int v = sidx[i];
+                if (v < -1 || v >= E) f |= kFlagBadId;
+                if (v >= 0) {
+                    const int s0 = (p / K) * K;
+                    for (int q = s0; q < p; ++q)
+                        if (idx[q] == v) { f |= kFlagDup; break; }
+                }
+            }
+            if (f) atomicOr(&sflag, f);
+        }
+    }
+    if (e < E && lane == 0) counts[e] = count;
+    if (blockIdx.x == 0) {
+        __syncthreads();
+        if (threadIdx.x == 0) flags[0] = sflag;
+    }
+}
+
+// Exclusive prefix of the counts per expert, then a stable scatter of every
+// slot of the expert into its group.
+__global__ __launch_bounds__(1024) void k_group_scatter(const int32_t *__restrict__ idx, int P,
+                                                        int E, const int32_t *__restrict__ counts,
+                                                        int32_t *__restrict__ offsets,
+                                                        int32_t *__restrict__ row_pair,
+                                                        int32_t *__restrict__ pair_row)
+{
+    __shared__ int32_t sidx[kWin];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int e = blockIdx.x * kGroupWaves + wave;
+    int off = 0;
+    if (e < E) {
+        int part = 0;
+        for (int j = lane; j < e; j += 64) part += counts[j];
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o, kWave);
+        off = part;
+        if (lane == 0) {
+            offsets[e] = off;
+            if (e == E - 1) offsets[E] = off + counts[e];
+        }
+    }
+    int run = 0;
+    for (int base = 0; base < P; base += kWin) {
+        const int n = min(kWin, P - base);
+        __syncthreads();
+        for (int i = threadIdx.x; i < n; i += blockDim.x) sidx[i] = idx[base + i];
+        __syncthreads();
+        if (e < E) {
+            for (int c = 0; c < n; c += 64) {
+                const int i = c + lane;
+                const bool hit = i < n && sidx[i] == e;
+                const uint64_t m = __ballot(hit);
+                if (hit) {
+                    const uint64_t below = lane ? (m & ((~0ull) >> (64 - lane))) : 0ull;
+                    const int pos = off + run + __popcll(below);
+                    row_pair[pos] = base + i;
+                    pair_row[base + i] = pos;
+                }
+                run += __popcll(m);
+            }
+        }
+        if (blockIdx.x == 0) {
+            for (int i = threadIdx.x; i < n; i += blockDim.x) {
+                const int v = sidx[i];
+                if (v < 0 || v >= E) pair_row[base + i] = -1;
+            }
+        }
+    }
+}
+
+// out[s, :] = sum_{kk: slot kept} w[s,kk] * y[row(s,kk), :]  (+ y[shared row]),
+// slots in order kk = 0..K-1, then the shared expert: a fixed order.
+__global__ __launch_bounds__(256) void k_combine(const float *__restrict__ y, int D, int K,
+                                                 const int32_t *__restrict__ pair_row,
+                                                 const float *__restrict__ w, int has_shared,
+                                                 int64_t shared_row0, float *__restrict__ out,
+                                                 int vec4)
+{
+    const int s = blockIdx.x;
+    const int32_t *pr = pair_row + (int64_t)s * K;
+    const float *ws = w + (int64_t)s * K;
+    if (vec4) {
+        for (int d = threadIdx.x * 4; d < D; d += blockDim.x * 4) {
+            float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int kk = 0; kk < K; ++kk) {
+                const int r = pr[kk];
+                if (r < 0) continue;
+                const float wk = ws[kk];
+                const float4 v = *reinterpret_cast<const float4 *>(y + (int64_t)r * D + d);
+                acc.x = fmaf(wk, v.x, acc.x);
+                acc.y = fmaf(wk, v.y, acc.y);
+                acc.z = fmaf(wk, v.z, acc.z);
+                acc.w = fmaf(wk, v.w, acc.w);
+            }
+            if (has_shared) {
+                const float4 v =
+                    *reinterpret_cast<const float4 *>(y + (shared_row0 + s) * (int64_t)D + d);
+                acc.x += v.x;
+                acc.y += v.y;
+                acc.z += v.z;
+                acc.w += v.w;
+            }
+            *reinterpret_cast<float4 *>(out + (int64_t)s * D + d) = acc;
+        }
+    } else {
+        for (int d = threadIdx.x; d < D; d += blockDim.x) {
+            float acc = 0.f;
+            for (int kk = 0; kk < K; ++kk) {
+                const int r = pr[kk];
+                if (r < 0) continue;
+                acc = fmaf(ws[kk], y[(int64_t)r * D + d], acc);
+            }
+            if (has_shared) acc += y[(shared_row0 + s) * (int64_t)D + d];
+            out[(int64_t)s * D + d] = acc;
+        }
+    }
+}
+
+inline bool al16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int to_status(hipError_t e) { return e == hipSuccess ? COLI_OK : COLI_EDEVICE; }
+
+// Grouped expert products: routed experts (+ shared) -> h -> y -> out.
+int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int S, int K,
+                const int32_t *idx, const float *w, float *out, uint8_t *ws,
+                const coli_ws_layout &L, hipStream_t st)
+{
+    const int E = ex->E, D = ex->D, F = ex->F;
+    const int P = S * K;
+    uint32_t *flags = reinterpret_cast<uint32_t *>(ws + L.flags);
+    int32_t *counts = reinterpret_cast<int32_t *>(ws + L.counts);
+    int32_t *offsets = reinterpret_cast<int32_t *>(ws + L.offsets);
+    int32_t *row_pair = reinterpret_cast<int32_t *>(ws + L.row_pair);
+    int32_t *pair_row = reinterpret_cast<int32_t *>(ws + L.pair_row);
+    float *h = reinterpret_cast<float *>(ws + L.h);
+    float *y = reinterpret_cast<float *>(ws + L.y);
+    const int gblocks = (E + kGroupWaves - 1) / kGroupWaves;
+    hipLaunchKernelGGL(k_group_count, dim3(gblocks), dim3(1024), 0, st, idx, P, K, E, counts,
+                       flags);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return COLI_EDEVICE;
+    hipLaunchKernelGGL(k_group_scatter, dim3(gblocks), dim3(1024), 0, st, idx, P, E, counts,
+                       offsets, row_pair, pair_row);
+    err = hipGetLastError();
+    if (err != hipSuccess) return COLI_EDEVICE;
+
+    const int64_t rbD = coli_row_bytes(ex->fmt, D), rbF = coli_row_bytes(ex->fmt, F);
+    const int64_t shared_row0 = (int64_t)P;
+    const int hint = 8;
+    const bool sh_same_up = sh && sh->fmt == ex->fmt;
+    const bool sh_same_down = sh && sh->fmt == ex->fmt && sh->F == F;
+
+    // ---- gate/up + SwiGLU -> h
+    GemvArgs a = {};
+    a.w[0] = (const uint8_t *)ex->w_gate;
+    a.w[1] = (const uint8_t *)ex->w_up;
+    a.s[0] = ex->s_gate;
+    a.s[1] = ex->s_up;
+    a.w_gstride = (int64_t)F * rbD;
+    a.s_gstride = F;
+    a.ngroups = E;
+    a.O = F;
+    a.I = D;
+    a.rb = rbD;
+    a.offsets = offsets;
+    a.row_pair = row_pair;
+    a.K = K;
+    a.xrow_token = 1;
+    a.x = x;
+    a.ldx = D;
+    a.x_vec4 = al16(x) && (D % 4 == 0);
+    a.out = h;
+    a.ldo = L.h_ld;
+    a.aligned = (rbD % 16 == 0) && al16(ex->w_gate) && al16(ex->w_up);
+    if (sh_same_up) {
+        a.has_extra = 1;
+        a.xw[0] = (const uint8_t *)sh->w_gate;
+        a.xw[1] = (const uint8_t *)sh->w_up;
+        a.xs[0] = sh->s_gate;
+        a.xs[1] = sh->s_up;
+        a.xO = sh->F;
+        a.x_rows = S;
+        a.x_row0 = (int)shared_row0;
+        a.aligned = a.aligned && al16(sh->w_gate) && al16(sh->w_up);
+    }
+    err = gemv_launch(a, ex->fmt, 2, hint, st);
+    if (err != hipSuccess) return COLI_EDEVICE;
+    if (sh && !sh_same_up) {
+        GemvArgs b = a;
+        const int64_t rbs = coli_row_bytes(sh->fmt, D);
+        b.ngroups = 0;
+        b.has_extra = 1;
+        b.xw[0] = (const uint8_t *)sh->w_gate;
+        b.xw[1] = (const uint8_t *)sh->w_up;
+        b.xs[0] = sh->s_gate;
+        b.xs[1] = sh->s_up;
+        b.xO = sh->F;
+        b.O = sh->F;
+        b.x_rows = S;
+        b.x_row0 = (int)shared_row0;
+        b.rb = rbs;
+        b.aligned = (rbs % 16 == 0) && al16(sh->w_gate) && al16(sh->w_up);
+        err = gemv_launch(b, sh->fmt, 2, hint, st);
+        if (err != hipSuccess) return COLI_EDEVICE;
+    }
+
+    // ---- down -> y
+    GemvArgs d = {};
+    d.w[0] = (const uint8_t *)ex->w_down;
+    d.s[0] = ex->s_down;
+    d.w_gstride = (int64_t)D * rbF;
+    d.s_gstride = D;
+    d.ngroups = E;
+    d.O = D;
+    d.I = F;
+    d.rb = rbF;
+    d.offsets = offsets;
+    d.row_pair = row_pair;
+    d.K = K;
+    d.xrow_token = 0;
+    d.x = h;
+    d.ldx = L.h_ld;
+    d.x_vec4 = (L.h_ld % 4 == 0);
+    d.out = y;
+    d.ldo = D;
+    d.aligned = (rbF % 16 == 0) && al16(ex->w_down);
+    if (sh_same_down) {
+        d.has_extra = 1;
+        d.xw[0] = (const uint8_t *)sh->w_down;
+        d.xs[0] = sh->s_down;
+        d.xO = D;
+        d.x_rows = S;
+        d.x_row0 = (int)shared_row0;
+        d.aligned = d.aligned && al16(sh->w_down);
+    }
+    err = gemv_launch(d, ex->fmt, 1, hint, st);
+    if (err != hipSuccess) return COLI_EDEVICE;
+    if (sh && !sh_same_down) {
+        GemvArgs b = d;
+        const int64_t rbs = coli_row_bytes(sh->fmt, sh->F);
+        b.ngroups = 0;
+        b.has_extra = 1;
+        b.xw[0] = (const uint8_t *)sh->w_down;
+        b.xs[0] = sh->s_down;
+        b.xO = D;
+        b.x_rows = S;
+        b.x_row0 = (int)shared_row0;
+        b.I = sh->F;
+        b.rb = rbs;
+        b.aligned = (rbs % 16 == 0) && al16(sh->w_down);
+        err = gemv_launch(b, sh->fmt, 1, hint, st);
+        if (err != hipSuccess) return COLI_EDEVICE;
+    }
+
+    // ---- weighted combine, fixed order
+    hipLaunchKernelGGL(k_combine, dim3(S), dim3(256), 0, st, y, D, K, pair_row, w, sh ? 1 : 0,
+                       shared_row0, out, (int)(al16(out) && al16(y) && D % 4 == 0));
+    return to_status(hipGetLastError());
+}
+
+}  // namespace
+}  // namespace coli
+
+using namespace coli;
+
+extern "C" int coli_qgemv(int fmt, const void *W, const float *scale, const float *x, float *y,
+                          int S, int I, int O, void *stream)
+{
+    int rc = coli__check_qgemv(fmt, W, scale, x, y, S, I, O);
+    if (rc != COLI_OK) return rc;
+    if (S == 0 || O == 0) return COLI_OK;
+    const int64_t rb = coli_row_bytes(fmt, I);
+    GemvArgs a = {};
+    a.w[0] = (const uint8_t *)W;
+    a.s[0] = scale;
+    a.ngroups = 1;
+    a.O = O;
+    a.x_rows = S;
+    a.I = I;
+    a.rb = rb;
+    a.K = 1;
+    a.x = x;
+    a.ldx = I;
+    a.x_vec4 = al16(x) && (I % 4 == 0);
+    a.out = y;
+    a.ldo = O;
+    a.aligned = (rb % 16 == 0) && al16(W);
+    return to_status(gemv_launch(a, fmt, 1, S, (hipStream_t)stream));
+}
+
+extern "C" int coli_router(const float *Wr, const float *bias, const float *x, int S, int E,
+                           int D, int K, int norm_topk, float routed_scale, float topp,
+                           int32_t *idx, float *w, int32_t *keff, float *sig, void *ws,
+                           size_t ws_bytes, void *stream)
+{
+    int rc = coli__check_router(Wr, bias, x, S, E, D, K, norm_topk, idx, w, sig, ws, ws_bytes);
+    if (rc != COLI_OK) return rc;
+    if (S == 0) return COLI_OK;
+    return to_status(router_launch(Wr, bias, x, S, E, D, K, norm_topk, routed_scale, topp, idx,
+                                   w, keff, sig, (double *)ws, (hipStream_t)stream));
+}
+
+extern "C" int coli_moe_gemv(const coli_experts *ex, const float *x, int S, int K,
+                             const int32_t *idx, const float *w, float *out, int prec, void *ws,
+                             size_t ws_bytes, void *stream)
+{
+    int rc = coli__check_moe(ex, nullptr, x, S, K, idx, w, out, prec, ws, ws_bytes, 1);
+    if (rc != COLI_OK) return rc;
+    if (S == 0) return COLI_OK;
+    coli_ws_layout L;
+    rc = coli_moe_workspace_layout(S, K, ex->E, ex->D, ex->F, 0, prec, &L);
+    if (rc != COLI_OK) return rc;
+    return run_experts(ex, nullptr, x, S, K, idx, w, out, (uint8_t *)ws, L, (hipStream_t)stream);
+}
+
+extern "C" int coli_moe_layer(const coli_router_params *r, const coli_experts *ex,
+                              const coli_mlp *shared, const float *x, int S,
+                              const int32_t *pre_idx, const float *pre_w, float *out,
+                              int32_t *idx_out, float *w_out, int prec, void *ws,
+                              size_t ws_bytes, void *stream)
+{
+    if (!r) return COLI_EINVAL;
+    if ((pre_idx == nullptr) != (pre_w == nullptr)) return COLI_EINVAL;
+    const int K = r->K;
+    int rc = coli__check_moe(ex, shared, x, S, K, pre_idx, pre_w, out, prec, ws, ws_bytes, 0);
+    if (rc != COLI_OK) return rc;
+    if ((idx_out && ((uintptr_t)idx_out & 3)) || (w_out && ((uintptr_t)w_out & 3)))
+        return COLI_EALIGN;
+    const bool run_router = pre_idx == nullptr;
+    if (run_router) {
+        if (!r->w || !r->bias) return COLI_EINVAL;
+        if (K > ex->E) return COLI_ERANGE;
+        if (r->norm_topk != 0 && r->norm_topk != 1) return COLI_EINVAL;
+        if (((uintptr_t)r->w & 3) || ((uintptr_t)r->bias & 3)) return COLI_EALIGN;
+    }
+    if (S == 0) return COLI_OK;
+    coli_ws_layout L;
+    rc = coli_moe_workspace_layout(S, K, ex->E, ex->D, ex->F, shared ? shared->F : 0, prec, &L);
+    if (rc != COLI_OK) return rc;
+    uint8_t *wsb = (uint8_t *)ws;
+    hipStream_t st = (hipStream_t)stream;
+    const int32_t *idx = pre_idx;
+    const float *w = pre_w;
+    if (run_router) {
+        int32_t *ri = idx_out ? idx_out : reinterpret_cast<int32_t *>(wsb + L.idx);
+        float *rw = w_out ? w_out : reinterpret_cast<float *>(wsb + L.w);
+        hipError_t e = router_launch(r->w, r->bias, x, S, ex->E, ex->D, K, r->norm_topk,
+                                     r->routed_scale, r->topp, ri, rw, nullptr,
+                                     reinterpret_cast<float *>(wsb + L.sig),
+                                     reinterpret_cast<double *>(wsb + L.router_part), st);
+        if (e != hipSuccess) return COLI_EDEVICE;
+        idx = ri;
+        w = rw;
+    } else {
+        const size_t n = (size_t)S * K;
+        if (idx_out && hipMemcpyAsync(idx_out, pre_idx, n * 4, hipMemcpyDeviceToDevice, st) != hipSuccess)
+            return COLI_EDEVICE;
+        if (w_out && hipMemcpyAsync(w_out, pre_w, n * 4, hipMemcpyDeviceToDevice, st) != hipSuccess)
+            return COLI_EDEVICE;
+    }
+    return run_experts(ex, shared, x, S, K, idx, w, out, wsb, L, st);
+}
+
+extern "C" int coli_check_device_flags(const void *ws, void *stream, uint32_t *flags_out)
+{
+    if (!ws) return COLI_EINVAL;
+    hipStream_t st = (hipStream_t)stream;
+    uint32_t f = 0;
+    if (hipMemcpyAsync(&f, ws, sizeof f, hipMemcpyDeviceToHost, st) != hipSuccess)
+        return COLI_EDEVICE;
+    if (hipStreamSynchronize(st) != hipSuccess) return COLI_EDEVICE;
+    if (flags_out) *flags_out = f;
+    return f ? COLI_EIDX : COLI_OK;
+}

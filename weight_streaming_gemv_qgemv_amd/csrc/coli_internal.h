@@ -1,0 +1,40 @@
+/* coli_internal.h -- declarations shared by libcoli's own translation units
+ * (host checks in coli_validate.c, launches in the .hip files).  Not part of
+ * the public ABI. */
+#ifndef COLI_INTERNAL_H
+#define COLI_INTERNAL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "coli.h"
+
+#define COLI_MAX_E 1024 /* 16 scores per lane of a 64-wide wave */
+#define COLI_MAX_K 64
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+int coli__check_qgemv(int fmt, const void *W, const float *scale,
+                      const float *x, const float *y, int S, int I, int O);
+int coli__check_router(const float *Wr, const float *bias, const float *x,
+                       int S, int E, int D, int K, int norm_topk,
+                       const int32_t *idx, const float *w, const float *sig,
+                       const void *ws, size_t ws_bytes);
+/* Router logits are summed over d in `splits` slices of `*slice` elements
+ * (a multiple of 16), chosen so the fp64 matrix-core grid fills the chip;
+ * the partial sums need coli__router_partial_bytes() of scratch. */
+int coli__router_splits(int S, int E, int D, int *slice);
+int64_t coli__router_partial_bytes(int S, int E, int D);
+
+int coli__check_moe(const coli_experts *ex, const coli_mlp *sh, const float *x,
+                    int S, int K, const int32_t *idx, const float *w,
+                    const float *out, int prec, const void *ws, size_t ws_bytes,
+                    int need_routing);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

@@ -1,0 +1,222 @@
+// coli_router.hip -- sigmoid noaux_tc router (one group) on gfx950.
+//
+// [glm.c@98759bf -- moe, phase A; metal@93cde63 -- r_router, r_top8,
+//  r_top8_par]
+//
+//   logit[s,e] = sum_d Wr[e,d] x[s,d]   fp64 products and sums (exact widening
+//                                        of the fp32 inputs), on the fp64
+//                                        matrix cores, split over d into
+//                                        slices that are summed in a fixed
+//                                        order afterwards
+//   sig[s,e]   = fp32(1 / (1 + exp(-logit)))   (fp64, rounded once)
+//   choice     = sig + bias                    (fp32 add)
+//   K picks by largest choice, lower index on ties; w = sig[pick]; optional
+//   top-p truncation; optional normalisation; times routed_scale (fp32, in
+//   the pages' order).
+//
+// Taking the logit in fp64 makes the rounded fp32 score independent of the
+// summation order (up to a rounding-boundary case of probability ~1e-8 per
+// score), so the picks match a sequential fp64 reference bit for bit.
+#include "coli_device.h"
+#include "coli_router.h"
+
+namespace coli {
+
+namespace {
+
+typedef double double4_t __attribute__((ext_vector_type(4)));
+
+// Partial logits over one d-slice for a tile of 16 tokens x 64 experts
+// (4 waves, 16 experts each).  v_mfma_f64_16x16x4f64 operand layout:
+//   A (16 x 4):  lane l holds A[l % 16][l / 16]
+//   B (4 x 16):  lane l holds B[l / 16][l % 16]
+//   D (16 x 16): lane l, element r holds D[4 * (l / 16) + r][l % 16]
+// A = router rows (experts), B = x rows (tokens) transposed.  Each lane
+// reads 4 consecutive d of its expert row and of its token row, and feeds
+// them to 4 consecutive MFMAs, so MFMA k-slot l/16 at step j is
+// d = d0 + 4 * (l / 16) + j: every product Wr[e,d] * x[s,d] is formed once.
+__global__ __launch_bounds__(256) void k_router_partial(const float *__restrict__ Wr,
+                                                        const float *__restrict__ x, int S,
+                                                        int E, int D, int slice,
+                                                        double *__restrict__ part)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t0 = blockIdx.x * 16;
+    const int e0 = blockIdx.y * 64 + wave * 16;
+    const int split = blockIdx.z;
+    const int dbeg = split * slice;
+    const int dend = min(D, dbeg + slice);
+    const int row = lane & 15, kg = lane >> 4;
+    const int e = e0 + row, t = t0 + row;
+    const float *wp = (e < E) ? Wr + (int64_t)e * D : nullptr;
+    const float *xp = (t < S) ? x + (int64_t)t * D : nullptr;
+    double4_t acc = {0.0, 0.0, 0.0, 0.0};
+    for (int d0 = dbeg; d0 < dend; d0 += 16) {
+        const int d = d0 + 4 * kg;
+        float wa[4], xb[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const bool in = d + j < dend;
+            wa[j] = (wp && in) ? wp[d + j] : 0.f;
+            xb[j] = (xp && in) ? xp[d + j] : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)wa[j], (double)xb[j], acc, 0, 0, 0);
+    }
+    // D[i][j]: i = expert row 4*kg + r, j = token column `row`
+    const int tt = t0 + row;
+    if (tt < S) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int ee = e0 + 4 * kg + r;
+            if (ee < E) part[((int64_t)split * S + tt) * E + ee] = acc[r];
+        }
+    }
+}
+
+// Sum the slices in slice order, then the sigmoid in fp64, rounded once.
+__global__ void k_router_sigmoid(const double *__restrict__ part, int splits, int S, int E,
+                                 float *__restrict__ sig)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t n = (int64_t)S * E;
+    if (i >= n) return;
+    double l = 0.0;
+    for (int k = 0; k < splits; ++k) l += part[(int64_t)k * n + i];
+    sig[i] = (float)(1.0 / (1.0 + exp(-l)));
+}
+
+// One wave per token: greedy top-K over choice = sig + bias.
+//  - lane l owns experts e = l + 64 j (j < ceil(E/64) <= 16), so e rises
+//    with j; a lane's candidate is its first maximal untaken choice
+//    (strict '>' while j rises);
+//  - the wave reduces (value, index) pairs with "larger value, else lower
+//    index", a total order on finite values, so every lane agrees on the
+//    pick, which equals the sequential scan's first maximum;
+//  - the pick's owner marks it taken; lane 0 then runs the pages' tail
+//    (top-p, normalisation, routed_scale) sequentially in fp32.
+__global__ __launch_bounds__(256) void k_router_topk(const float *__restrict__ sig,
+                                                     const float *__restrict__ bias, int S,
+                                                     int E, int K, int norm_topk,
+                                                     float routed_scale, float topp,
+                                                     int32_t *__restrict__ idx,
+                                                     float *__restrict__ w,
+                                                     int32_t *__restrict__ keff)
+{
+    __shared__ int pick_s[4][64];
+    __shared__ float pw_s[4][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int s = blockIdx.x * 4 + wave;
+    if (s >= S) return;   // whole wave leaves together; no block barrier below
+    const float *sg = sig + (int64_t)s * E;
+    const int per = (E + 63) / 64;
+    float ch[16], sv[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int e = lane + 64 * j;
+        const bool ok = j < per && e < E;
+        sv[j] = ok ? sg[e] : 0.f;
+        ch[j] = ok ? sv[j] + bias[e] : 0.f;
+    }
+    uint32_t live = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+        if (j < per && lane + 64 * j < E) live |= 1u << j;
+    int *pick = pick_s[wave];
+    float *pw = pw_s[wave];
+    for (int kk = 0; kk < K; ++kk) {
+        float bv = 0.f;
+        int bi = 0x7FFFFFFF;
+        bool have = false;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            if (live & (1u << j)) {
+                if (!have || ch[j] > bv) { bv = ch[j]; bi = lane + 64 * j; have = true; }
+            }
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            const float ov = __shfl_xor(bv, off, kWave);
+            const int oi = __shfl_xor(bi, off, kWave);
+            const bool take = (oi != 0x7FFFFFFF) &&
+                              (bi == 0x7FFFFFFF || ov > bv || (ov == bv && oi < bi));
+            if (take) { bv = ov; bi = oi; }
+        }
+        bi = __shfl(bi, 0, kWave);
+        float sbest = 0.f;
+        if (bi >= 0 && bi < E && (bi & 63) == lane) {
+            const int j = bi >> 6;
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj)
+                if (jj == j) sbest = sv[jj];
+            live &= ~(1u << j);
+        }
+        sbest = __shfl(sbest, bi & 63, kWave);
+        if (lane == 0) {
+            pick[kk] = bi;
+            pw[kk] = sbest;
+        }
+    }
+    if (lane != 0) return;
+    int ke = K;
+    if (topp > 0.f && topp < 1.f) {
+        for (int a2 = 1; a2 < K; ++a2) {
+            const int ii = pick[a2];
+            const float wv = pw[a2];
+            int b = a2 - 1;
+            while (b >= 0 && pw[b] < wv) {
+                pw[b + 1] = pw[b];
+                pick[b + 1] = pick[b];
+                --b;
+            }
+            pw[b + 1] = wv;
+            pick[b + 1] = ii;
+        }
+        float tot = 1e-20f;
+        for (int kk = 0; kk < K; ++kk) tot += pw[kk];
+        float cum = 0.f;
+        for (int kk = 0; kk < K; ++kk) {
+            cum += pw[kk];
+            if (cum >= topp * tot) { ke = kk + 1; break; }
+        }
+    }
+    if (norm_topk) {
+        float sm = 0.f;
+        for (int kk = 0; kk < ke; ++kk) sm += pw[kk];
+        sm += 1e-20f;
+        for (int kk = 0; kk < ke; ++kk) pw[kk] /= sm;
+    }
+    for (int kk = 0; kk < K; ++kk) {
+        const bool in = kk < ke;
+        idx[(int64_t)s * K + kk] = in ? pick[kk] : -1;
+        w[(int64_t)s * K + kk] = in ? pw[kk] * routed_scale : 0.f;
+    }
+    if (keff) keff[s] = ke;
+}
+
+}  // namespace
+
+hipError_t router_launch(const float *Wr, const float *bias, const float *x, int S, int E,
+                         int D, int K, int norm_topk, float routed_scale, float topp,
+                         int32_t *idx, float *w, int32_t *keff, float *sig, double *part,
+                         hipStream_t st)
+{
+    if (S <= 0) return hipSuccess;
+    int slice = 0;
+    const int splits = coli__router_splits(S, E, D, &slice);
+    dim3 grid((S + 15) / 16, (E + 63) / 64, splits);
+    hipLaunchKernelGGL(k_router_partial, grid, dim3(256), 0, st, Wr, x, S, E, D, slice, part);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int64_t n = (int64_t)S * E;
+    hipLaunchKernelGGL(k_router_sigmoid, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                       part, splits, S, E, sig);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(k_router_topk, dim3((S + 3) / 4), dim3(256), 0, st, sig, bias, S, E, K,
+                       norm_topk, routed_scale, topp, idx, w, keff);
+    return hipGetLastError();
+}
+
+}  // namespace coli

@@ -1,0 +1,221 @@
+/*
+ * coli_validate.c -- host-side argument checks, size queries and workspace
+ * layout of libcoli.  Plain C, no HIP: it is linked into libcoli.so and also
+ * built alone so the checks can be exercised on a machine without a GPU.
+ *
+ * The refusal of mismatched sizes follows the pages' hardening of weight
+ * format resolution: a byte count that fits no known layout is an error,
+ * never a guess [docs-quickstart -- qt_resolve_fmt].
+ */
+#include <stdint.h>
+#include <stddef.h>
+
+#include "coli.h"
+#include "coli_internal.h"
+
+#define ALIGN_WS 256
+
+int64_t coli_row_bytes(int fmt, int64_t I)
+{
+    if (I < 0) return -1;
+    switch (fmt) {
+    case COLI_F32: return I > INT64_MAX / 4 ? -1 : 4 * I;
+    case COLI_I8:  return I;
+    case COLI_I4:  return (I + 1) / 2;
+    case COLI_I2:  return (I + 3) / 4;
+    default:       return -1;
+    }
+}
+
+const char *coli_strerror(int status)
+{
+    switch (status) {
+    case COLI_OK:         return "ok";
+    case COLI_EINVAL:     return "invalid argument (NULL pointer or flag out of range)";
+    case COLI_ESHAPE:     return "invalid size (negative, or byte count overflow)";
+    case COLI_EFMT:       return "unsupported weight format";
+    case COLI_EALIGN:     return "misaligned pointer";
+    case COLI_ERANGE:     return "count out of supported range (K, E)";
+    case COLI_EWORKSPACE: return "workspace missing or too small";
+    case COLI_EDEVICE:    return "HIP runtime error";
+    case COLI_EIDX:       return "routing ids out of range or duplicated (device flag)";
+    default:              return "unknown status";
+    }
+}
+
+int coli_version(void) { return 1 * 10000 + 0 * 100 + 0; }
+
+/* a*b with overflow check into *out; returns 0 on overflow */
+static int mul_ok(int64_t a, int64_t b, int64_t *out)
+{
+    if (a < 0 || b < 0) return 0;
+    if (a != 0 && b > INT64_MAX / a) return 0;
+    *out = a * b;
+    return 1;
+}
+
+static int aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+int coli__check_qgemv(int fmt, const void *W, const float *scale,
+                      const float *x, const float *y, int S, int I, int O)
+{
+    if (fmt < COLI_F32 || fmt > COLI_I2) return COLI_EFMT;
+    if (S < 0 || I < 0 || O < 0) return COLI_ESHAPE;
+    int64_t rb = coli_row_bytes(fmt, I), t;
+    if (rb < 0 || !mul_ok(rb, O, &t) || !mul_ok((int64_t)S, I, &t) ||
+        !mul_ok((int64_t)S, O, &t) || !mul_ok(t, 4, &t))
+        return COLI_ESHAPE;
+    if (S == 0 || O == 0) return COLI_OK;
+    if (!y) return COLI_EINVAL;
+    if (I > 0 && (!W || !x)) return COLI_EINVAL;
+    if (!scale && fmt != COLI_F32) return COLI_EINVAL;
+    if ((W && !aligned(W, 4)) || (x && !aligned(x, 4)) || !aligned(y, 4) ||
+        (scale && !aligned(scale, 4)))
+        return COLI_EALIGN;
+    return COLI_OK;
+}
+
+int coli__check_router(const float *Wr, const float *bias, const float *x,
+                       int S, int E, int D, int K, int norm_topk,
+                       const int32_t *idx, const float *w, const float *sig,
+                       const void *ws, size_t ws_bytes)
+{
+    if (S < 0 || E < 0 || D < 0 || K < 0) return COLI_ESHAPE;
+    if (E < 1 || E > COLI_MAX_E || K < 1 || K > COLI_MAX_K || K > E) return COLI_ERANGE;
+    if (D < 1) return COLI_ESHAPE;
+    if (norm_topk != 0 && norm_topk != 1) return COLI_EINVAL;
+    int64_t t;
+    if (!mul_ok((int64_t)S, D, &t) || !mul_ok((int64_t)E, D, &t) ||
+        !mul_ok((int64_t)S, E, &t) || !mul_ok(t, 8, &t))
+        return COLI_ESHAPE;
+    if (S == 0) return COLI_OK;
+    if (!Wr || !bias || !x || !idx || !w || !sig) return COLI_EINVAL;
+    if (!aligned(Wr, 4) || !aligned(bias, 4) || !aligned(x, 4) || !aligned(idx, 4) ||
+        !aligned(w, 4) || !aligned(sig, 4))
+        return COLI_EALIGN;
+    if (!ws || ws_bytes < (size_t)coli__router_partial_bytes(S, E, D)) return COLI_EWORKSPACE;
+    if (!aligned(ws, 8)) return COLI_EALIGN;
+    return COLI_OK;
+}
+
+static int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+int coli__router_splits(int S, int E, int D, int *slice)
+{
+    int64_t tiles = (int64_t)((S + 15) / 16) * ((E + 63) / 64);
+    int64_t want = tiles > 0 ? (512 + tiles - 1) / tiles : 1;
+    int64_t maxs = D / 64 > 0 ? D / 64 : 1;
+    if (want > maxs) want = maxs;
+    if (want < 1) want = 1;
+    int64_t sl = round_up((D + want - 1) / want, 16);
+    if (sl < 16) sl = 16;
+    if (slice) *slice = (int)sl;
+    return (int)((D + sl - 1) / sl);
+}
+
+int64_t coli__router_partial_bytes(int S, int E, int D)
+{
+    if (S <= 0 || E <= 0 || D <= 0) return 0;
+    int splits = coli__router_splits(S, E, D, 0);
+    return (int64_t)splits * S * E * 8;
+}
+
+size_t coli_router_workspace_bytes(int S, int E, int D)
+{
+    if (S < 0 || E < 1 || E > COLI_MAX_E || D < 1) return 0;
+    int64_t b = coli__router_partial_bytes(S, E, D);
+    return (size_t)(b > 0 ? b : 256);
+}
+
+/* Workspace layout: one 256-byte aligned region after the other. */
+int coli_moe_workspace_layout(int S, int K, int E, int D, int F, int F_shared,
+                              int prec, coli_ws_layout *out)
+{
+    if (!out) return COLI_EINVAL;
+    if (S < 0 || K < 1 || E < 1 || D < 1 || F < 1 || F_shared < 0) return COLI_ESHAPE;
+    if (prec != COLI_PREC_FP32 && prec != COLI_PREC_BF16) return COLI_EINVAL;
+    int64_t P, rows, Fmax = F > F_shared ? F : F_shared, t, off = 0;
+    if (!mul_ok((int64_t)S, K, &P)) return COLI_ESHAPE;
+    rows = P + (F_shared > 0 ? S : 0);
+#define REGION(field, bytes)                                   \
+    do {                                                       \
+        int64_t b_ = (bytes);                                  \
+        if (b_ < 0 || off > INT64_MAX - b_ - ALIGN_WS) return COLI_ESHAPE; \
+        out->field = off;                                      \
+        off = round_up(off + b_, ALIGN_WS);                    \
+    } while (0)
+    REGION(flags, 64);
+    if (!mul_ok((int64_t)S, E, &t) || !mul_ok(t, 4, &t)) return COLI_ESHAPE;
+    REGION(sig, t);
+    REGION(idx, P * 4);
+    REGION(w, P * 4);
+    REGION(offsets, ((int64_t)E + 2) * 4);
+    REGION(counts, ((int64_t)E + 2) * 4);
+    REGION(row_pair, P * 4);
+    REGION(pair_row, P * 4);
+    if (!mul_ok(rows, Fmax, &t) || !mul_ok(t, 4, &t)) return COLI_ESHAPE;
+    REGION(h, t);
+    if (!mul_ok(rows, D, &t) || !mul_ok(t, 4, &t)) return COLI_ESHAPE;
+    REGION(y, t);
+    REGION(router_part, coli__router_partial_bytes(S, E, D));
+#undef REGION
+    out->h_ld = Fmax;
+    out->total = off;
+    return COLI_OK;
+}
+
+size_t coli_moe_workspace_bytes(int S, int K, int E, int D, int F, int F_shared, int prec)
+{
+    coli_ws_layout L;
+    if (coli_moe_workspace_layout(S, K, E, D, F, F_shared, prec, &L) != COLI_OK) return 0;
+    return (size_t)L.total;
+}
+
+static int check_mlp_tensors(int fmt, int D, int F, const void *wg, const void *wu,
+                             const void *wd, const float *sg, const float *su,
+                             const float *sd, int64_t count)
+{
+    if (fmt != COLI_I8 && fmt != COLI_I4 && fmt != COLI_I2) return COLI_EFMT;
+    if (F < 1 || D < 1) return COLI_ESHAPE;
+    int64_t a, b;
+    if (!mul_ok(coli_row_bytes(fmt, D), F, &a) || !mul_ok(a, count, &a) ||
+        !mul_ok(coli_row_bytes(fmt, F), D, &b) || !mul_ok(b, count, &b))
+        return COLI_ESHAPE;
+    if (!wg || !wu || !wd || !sg || !su || !sd) return COLI_EINVAL;
+    if (!aligned(wg, 4) || !aligned(wu, 4) || !aligned(wd, 4) || !aligned(sg, 4) ||
+        !aligned(su, 4) || !aligned(sd, 4))
+        return COLI_EALIGN;
+    return COLI_OK;
+}
+
+int coli__check_moe(const coli_experts *ex, const coli_mlp *sh, const float *x,
+                    int S, int K, const int32_t *idx, const float *w,
+                    const float *out, int prec, const void *ws, size_t ws_bytes,
+                    int need_routing)
+{
+    if (!ex) return COLI_EINVAL;
+    if (prec != COLI_PREC_FP32 && prec != COLI_PREC_BF16) return COLI_EINVAL;
+    if (S < 0 || K < 0 || ex->E < 0 || ex->D < 0 || ex->F < 0) return COLI_ESHAPE;
+    if (ex->E < 1 || ex->E > COLI_MAX_E || K < 1 || K > COLI_MAX_K) return COLI_ERANGE;
+    int rc = check_mlp_tensors(ex->fmt, ex->D, ex->F, ex->w_gate, ex->w_up, ex->w_down,
+                               ex->s_gate, ex->s_up, ex->s_down, ex->E);
+    if (rc) return rc;
+    if (sh) {
+        if (sh->F < 1) return COLI_ESHAPE;
+        rc = check_mlp_tensors(sh->fmt, ex->D, sh->F, sh->w_gate, sh->w_up, sh->w_down,
+                               sh->s_gate, sh->s_up, sh->s_down, 1);
+        if (rc) return rc;
+    }
+    int64_t t;
+    if (!mul_ok((int64_t)S, ex->D, &t) || !mul_ok(t, 4, &t)) return COLI_ESHAPE;
+    size_t need = coli_moe_workspace_bytes(S, K, ex->E, ex->D, ex->F, sh ? sh->F : 0, prec);
+    if (need == 0) return COLI_ESHAPE;
+    if (S == 0) return COLI_OK;
+    if (!x || !out) return COLI_EINVAL;
+    if (need_routing && (!idx || !w)) return COLI_EINVAL;
+    if (!aligned(x, 4) || !aligned(out, 4) || (idx && !aligned(idx, 4)) || (w && !aligned(w, 4)))
+        return COLI_EALIGN;
+    if (!ws || ws_bytes < need) return COLI_EWORKSPACE;
+    if (!aligned(ws, ALIGN_WS)) return COLI_EALIGN;
+    return COLI_OK;
+}
