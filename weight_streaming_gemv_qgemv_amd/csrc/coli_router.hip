@@ -30,7 +30,8 @@ typedef double double4_t __attribute__((ext_vector_type(4)));
 // (4 waves, 16 experts each).  v_mfma_f64_16x16x4f64 operand layout:
 //   A (16 x 4):  lane l holds A[l % 16][l / 16]
 //   B (4 x 16):  lane l holds B[l / 16][l % 16]
-//   D (16 x 16): lane l, element r holds D[4 * (l / 16) + r][l % 16]
+//   D (16 x 16): lane l, element r holds D[4 * r + l / 16][l % 16]
+//                (the fp64 variant interleaves rows across the lane groups)
 // A = router rows (experts), B = x rows (tokens) transposed.  Each lane
 // reads 4 consecutive d of its expert row and of its token row, and feeds
 // them to 4 consecutive MFMAs, so MFMA k-slot l/16 at step j is
@@ -64,12 +65,12 @@ __global__ __launch_bounds__(256) void k_router_partial(const float *__restrict_
         for (int j = 0; j < 4; ++j)
             acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)wa[j], (double)xb[j], acc, 0, 0, 0);
     }
-    // D[i][j]: i = expert row 4*kg + r, j = token column `row`
+    // D[i][j]: i = expert row 4*r + kg, j = token column `row`
     const int tt = t0 + row;
     if (tt < S) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int ee = e0 + 4 * kg + r;
+            const int ee = e0 + 4 * r + kg;
             if (ee < E) part[((int64_t)split * S + tt) * E + ee] = acc[r];
         }
     }
