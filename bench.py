@@ -1,0 +1,292 @@
+#!/usr/bin/env python3
+"""Benchmark of the dequant-on-use MoE path on one MI355X.
+
+Default workload ("layer64"): one full MoE block decoding 64 ragged tokens
+(the GLM-5.2 MoE block: hidden 6144, 256 int4 experts of intermediate 2048,
+top-8 sigmoid noaux_tc router with routed_scaling_factor 2.5, one int4 shared
+expert).  A step is one coli_moe_layer call: router, device-side expert
+grouping, fused gate/up + SwiGLU, down, shared expert and the weighted
+combine.  Two copies of the expert bank live in HBM and steps alternate
+between them, so no step finds its weights in the 256 MB last-level cache.
+
+Other workloads: "decode16" (coli_moe_gemv, 16 tokens, given top-8 routing),
+"qgemv" (int4 12288 x 6144, S = 1, over a rotation of weight copies).
+
+Prints ONE JSON line.  `value` is the step's algorithmic bytes (weights of
+the experts actually used, scales, router, activations, outputs) divided by
+the step time, in GB/s; tokens/s and the share of the 8 TB/s HBM peak are
+reported beside it.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "int4 expert-GEMV HBM GB/s (% of peak) + MoE-layer decode tokens/s"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def expert_bytes(fmt, D, F):
+    from weight_streaming_gemv_qgemv_amd import synth
+    rbD, rbF = synth.packed_row_bytes(fmt, D), synth.packed_row_bytes(fmt, F)
+    gate_up = 2 * F * rbD + 2 * F * 4
+    down = D * rbF + D * 4
+    return gate_up, down
+
+
+def to_dev(a, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def bank_to_dev(bank, dev):
+    out = dict(bank)
+    for k in ("wg", "wu", "wd", "sg", "su", "sd"):
+        out[k] = to_dev(bank[k], dev)
+    return out
+
+
+def clone_bank(bd):
+    out = dict(bd)
+    for k in ("wg", "wu", "wd", "sg", "su", "sd"):
+        out[k] = bd[k].clone()
+    return out
+
+
+def time_steps(step, steps, warmup):
+    import torch
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    from weight_streaming_gemv_qgemv_amd import binding as b
+    b.stage_times(reset=True)
+    b.stage_timing(True)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(steps):
+        step(warmup + i)
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    b.stage_timing(False)
+    stages = b.stage_times(reset=True)
+    return t0.elapsed_time(t1) / steps, wall, stages
+
+
+def cpu_baseline_layer(bank, shared, Wr, bias, x, K, ntok):
+    """The oracle as it stands, on the first `ntok` tokens of the same input."""
+    from oracle import oracle
+    xs = x[:ntok]
+    t0 = time.perf_counter()
+    r = oracle.router(Wr, bias, xs, K, 1, 2.5)
+    oracle.moe(bank, shared, xs, r["idx"], r["w"])
+    dt = time.perf_counter() - t0
+    return dt, r["idx"]
+
+
+def run_layer64(args, dev):
+    import torch
+    from weight_streaming_gemv_qgemv_amd import binding as b
+    from weight_streaming_gemv_qgemv_amd import synth
+    S, K, E, D, F, fmt = 64, 8, 256, 6144, 2048, 2
+    log("generating 256 int4 experts + shared expert (host)")
+    bank = synth.expert_bank(4000, fmt, E, D, F)
+    shared = synth.shared_mlp(4000, fmt, D, F)
+    g = synth.rng(4001)
+    Wr, bias = synth.router_weights(g, E, D)
+    x = synth.activations(g, S, D)
+    log("uploading")
+    banks = [bank_to_dev(bank, dev)]
+    banks.append(clone_bank(banks[0]))
+    sd = [bank_to_dev(shared, dev)]
+    sd.append(clone_bank(sd[0]))
+    rp = dict(w=to_dev(Wr, dev), bias=to_dev(bias, dev), K=K, norm_topk=1, routed_scale=2.5)
+    xd = to_dev(x, dev)
+    out = torch.empty((S, D), dtype=torch.float32, device=dev)
+    idx_o = torch.empty((S, K), dtype=torch.int32, device=dev)
+    w_o = torch.empty((S, K), dtype=torch.float32, device=dev)
+    ws = b.alloc_workspace(b.moe_workspace_bytes(S, K, E, D, F, F), dev)
+
+    def step(i):
+        j = i & 1
+        b.moe_layer(rp, banks[j], sd[j], xd, out=out, idx_out=idx_o, w_out=w_o, ws=ws)
+
+    step(0)
+    torch.cuda.synchronize()
+    uniq = int(np.unique(idx_o.cpu().numpy()).size)
+    gu, dn = expert_bytes(fmt, D, F)
+    step_bytes = (E * D * 4 + E * 4) + S * D * 4 + uniq * (gu + dn) + (gu + dn) + S * D * 4 + S * K * 8
+    log(f"unique experts {uniq}; algorithmic bytes/step {step_bytes / 1e9:.4f} GB")
+    ms, wall, stages = time_steps(step, args.steps, args.warmup)
+    # dominant kernel: gate/up + SwiGLU (2/3 of the expert bytes), one launch per step
+    gu_ms, gu_n = stages["gate_up"]
+    gu_bytes = (uniq + 1) * gu + S * D * 4 + (S * K + S) * F * 4
+    res = dict(workload="moe_layer_decode_64", ms=ms, wall=wall, step_bytes=step_bytes,
+               tokens=S, stages=stages, uniq=uniq,
+               dominant=dict(kernel="k_gemv<I4,M=2> (expert gate/up + SwiGLU)",
+                             bytes_per_launch=gu_bytes, ms_per_launch=gu_ms / max(gu_n, 1),
+                             launches=gu_n))
+    if not args.no_cpu_baseline:
+        ntok = args.cpu_tokens
+        log(f"cpu baseline: oracle on {ntok} tokens")
+        dt, sidx = cpu_baseline_layer(bank, shared, Wr, bias, x, K, ntok)
+        su = int(np.unique(sidx).size)
+        sb = (E * D * 4 + E * 4) + ntok * D * 4 + su * (gu + dn) + (gu + dn) + ntok * D * 4
+        from oracle import oracle
+        res["cpu"] = dict(value=sb / dt / 1e9, unit="GB/s", cores=oracle.num_threads(),
+                          kind="oracle",
+                          sample=f"router + MoE layer on the first {ntok} of the 64 tokens "
+                                 f"({su} unique experts), {dt:.2f} s",
+                          tokens_per_s=ntok / dt, seconds=dt)
+    return res
+
+
+def run_decode16(args, dev):
+    import torch
+    from weight_streaming_gemv_qgemv_amd import binding as b
+    from weight_streaming_gemv_qgemv_amd import synth
+    S, K, E, D, F, fmt = 16, 8, 256, 6144, 2048, 2
+    bank = synth.expert_bank(4100, fmt, E, D, F)
+    g = synth.rng(4101)
+    x = synth.activations(g, S, D)
+    idx, w = synth.routing_uniform(g, S, K, E)
+    banks = [bank_to_dev(bank, dev)]
+    banks.append(clone_bank(banks[0]))
+    xd, idd, wd = to_dev(x, dev), to_dev(idx, dev), to_dev(w, dev)
+    out = torch.empty((S, D), dtype=torch.float32, device=dev)
+    ws = b.alloc_workspace(b.moe_workspace_bytes(S, K, E, D, F), dev)
+
+    def step(i):
+        b.moe_gemv(banks[i & 1], xd, idd, wd, out=out, ws=ws)
+
+    uniq = int(np.unique(idx).size)
+    gu, dn = expert_bytes(fmt, D, F)
+    step_bytes = S * D * 4 + uniq * (gu + dn) + S * D * 4 + S * K * 8
+    ms, wall, stages = time_steps(step, args.steps, args.warmup)
+    gu_ms, gu_n = stages["gate_up"]
+    res = dict(workload="moe_expert_decode_16", ms=ms, wall=wall, step_bytes=step_bytes,
+               tokens=S, stages=stages, uniq=uniq,
+               dominant=dict(kernel="k_gemv<I4,M=2> (expert gate/up + SwiGLU)",
+                             bytes_per_launch=uniq * gu + S * D * 4 + S * K * F * 4,
+                             ms_per_launch=gu_ms / max(gu_n, 1), launches=gu_n))
+    if not args.no_cpu_baseline:
+        from oracle import oracle
+        n = args.cpu_tokens
+        t0 = time.perf_counter()
+        oracle.moe(bank, None, x[:n], idx[:n], w[:n].astype(np.float64))
+        dt = time.perf_counter() - t0
+        su = int(np.unique(idx[:n]).size)
+        res["cpu"] = dict(value=(n * D * 8 + su * (gu + dn)) / dt / 1e9, unit="GB/s",
+                          cores=oracle.num_threads(), kind="oracle",
+                          sample=f"routed experts for the first {n} of 16 tokens ({su} unique "
+                                 f"experts), {dt:.2f} s", tokens_per_s=n / dt, seconds=dt)
+    return res
+
+
+def run_qgemv(args, dev):
+    import torch
+    from weight_streaming_gemv_qgemv_amd import binding as b
+    from weight_streaming_gemv_qgemv_amd import synth
+    O, I, S, fmt = 12288, 6144, 1, 2
+    g = synth.rng(4200)
+    W = synth.weight_bytes(g, fmt, O, I)
+    sc = synth.scales(g, O)
+    x = synth.activations(g, S, I)
+    Wd0 = to_dev(W, dev)
+    copies = [Wd0] + [Wd0.clone() for _ in range(31)]      # 32 x 37.7 MB > 1 GiB rotation
+    scd, xd = to_dev(sc, dev), to_dev(x, dev)
+    y = torch.empty((S, O), dtype=torch.float32, device=dev)
+
+    def step(i):
+        b.qgemv(fmt, copies[i % len(copies)], scd, xd, y)
+
+    step_bytes = O * W.shape[1] + O * 4 + S * I * 4 + S * O * 4
+    ms, wall, stages = time_steps(step, args.steps, args.warmup)
+    q_ms, q_n = stages["qgemv"]
+    return dict(workload="qgemv_i4_12288x6144_s1", ms=ms, wall=wall, step_bytes=step_bytes,
+                tokens=S, stages=stages, uniq=None,
+                dominant=dict(kernel="k_gemv<I4,M=1>", bytes_per_launch=step_bytes,
+                              ms_per_launch=q_ms / max(q_n, 1), launches=q_n))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="layer64", choices=["layer64", "decode16", "qgemv"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=64)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build measures the per-GPU share of the "
+              f"MoE block; --gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    from weight_streaming_gemv_qgemv_amd import binding as b
+    b.lib()
+    run = {"layer64": run_layer64, "decode16": run_decode16, "qgemv": run_qgemv}[args.workload]
+    r = run(args, dev)
+    ms = r["ms"]
+    gbs = r["step_bytes"] / (ms * 1e-3) / 1e9
+    dom = r["dominant"]
+    ach = dom["bytes_per_launch"] / (dom["ms_per_launch"] * 1e-3) / 1e9 if dom["ms_per_launch"] else None
+    line = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32 (int4 weights)",
+        "data": "synthetic",
+        "config": {"workload": r["workload"], "tokens_per_step": r["tokens"],
+                   "experts": 256 if r["uniq"] is not None else None,
+                   "unique_experts_per_step": r["uniq"], "hidden": 6144,
+                   "moe_inter": 2048, "top_k": 8 if r["uniq"] is not None else None,
+                   "weight_format": "int4 per-row scale",
+                   "algorithmic_bytes_per_step": r["step_bytes"]},
+        "tokens_per_s": round(r["tokens"] / (ms * 1e-3), 1),
+        "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "stage_ms_per_step": {k: round(v[0] / max(v[1], 1), 5) for k, v in r["stages"].items() if v[1]},
+        "roofline": {"bound": "hbm", "achieved": round(ach, 2) if ach else None,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBS, 4) if ach else None,
+                     "traffic": None, "kernel": dom["kernel"],
+                     "algorithmic_bytes_per_launch": dom["bytes_per_launch"],
+                     "ms_per_launch": round(dom["ms_per_launch"], 5)},
+        "context": {"pages_metal_moe_gemv_GBps": "358-389 (Apple-Silicon GPU, unified memory)"},
+    }
+    if "cpu" in r:
+        c = r["cpu"]
+        line["cpu_baseline"] = {"value": round(c["value"], 4), "unit": c["unit"], "cores": c["cores"],
+                                "kind": c["kind"], "sample": c["sample"],
+                                "tokens_per_s": round(c["tokens_per_s"], 3)}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

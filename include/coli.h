@@ -239,6 +239,20 @@ int coli_moe_layer(const coli_router_params *r, const coli_experts *ex,
  * duplicated, COLI_EDEVICE on a runtime error. */
 int coli_check_device_flags(const void *ws, void *stream, uint32_t *flags_out);
 
+/* Stage timing, for benchmarks and profiling.  Off by default; while on,
+ * every call records a hipEvent pair on its stream around each stage it runs
+ * (the only state the library keeps between calls).  coli_stage_times waits
+ * for the recorded events and writes, per stage, the total milliseconds and
+ * the number of timed launches since the last reset (host arrays of
+ * COLI_NSTAGES entries; either may be NULL).  Stages: 0 router, 1 grouping,
+ * 2 gate/up + SwiGLU, 3 down, 4 combine, 5 qgemv.  The pages time the same
+ * phases of their MoE block [metal@93cde63 -- moe_finish timers;
+ * glm.c@98759bf -- profile counters]. */
+#define COLI_NSTAGES 6
+int coli_stage_timing(int enable);
+int coli_stage_times(double *ms, int64_t *calls, int reset);
+const char *coli_stage_name(int stage);
+
 /* Static text for a status code. */
 const char *coli_strerror(int status);
 

@@ -51,7 +51,9 @@ class WsLayout(C.Structure):
 
 EXPORTS = ["coli_row_bytes", "coli_qgemv", "coli_router", "coli_router_workspace_bytes",
            "coli_moe_workspace_bytes", "coli_moe_workspace_layout", "coli_moe_gemv",
-           "coli_moe_layer", "coli_check_device_flags", "coli_strerror", "coli_version"]
+           "coli_moe_layer", "coli_check_device_flags", "coli_strerror", "coli_version",
+           "coli_stage_timing", "coli_stage_times", "coli_stage_name"]
+NSTAGES = 6
 
 _lib = None
 
@@ -89,6 +91,12 @@ def lib():
         L.coli_strerror.argtypes = [i32]
         L.coli_version.restype = i32
         L.coli_version.argtypes = []
+        L.coli_stage_timing.restype = i32
+        L.coli_stage_timing.argtypes = [i32]
+        L.coli_stage_times.restype = i32
+        L.coli_stage_times.argtypes = [vp, vp, i32]
+        L.coli_stage_name.restype = C.c_char_p
+        L.coli_stage_name.argtypes = [i32]
         _lib = L
     return _lib
 
@@ -230,6 +238,19 @@ def moe_layer(router_p: dict | None, ex: dict, shared: dict | None, x, pre_idx=N
                               _ptr(ws), ws.numel(), _stream(stream))
     _check(rc, "coli_moe_layer")
     return out, ws
+
+
+def stage_timing(enable: bool) -> None:
+    _check(lib().coli_stage_timing(1 if enable else 0), "coli_stage_timing")
+
+
+def stage_times(reset: bool = True) -> dict:
+    """{stage name: (total ms, launches)} since the last reset (waits for the
+    recorded events)."""
+    ms = (C.c_double * NSTAGES)()
+    calls = (C.c_int64 * NSTAGES)()
+    _check(lib().coli_stage_times(ms, calls, 1 if reset else 0), "coli_stage_times")
+    return {lib().coli_stage_name(i).decode(): (ms[i], calls[i]) for i in range(NSTAGES)}
 
 
 def check_device_flags(ws, stream=None) -> tuple[int, int]:

@@ -15,6 +15,7 @@
 #include "coli_gemv.h"
 #include "coli_internal.h"
 #include "coli_router.h"
+#include "coli_stages.h"
 
 namespace coli {
 
@@ -191,14 +192,18 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
     float *h = reinterpret_cast<float *>(ws + L.h);
     float *y = reinterpret_cast<float *>(ws + L.y);
     const int gblocks = (E + kGroupWaves - 1) / kGroupWaves;
+    hipError_t err;
+    {
+    StageTimer tg(kStGroup, st);
     hipLaunchKernelGGL(k_group_count, dim3(gblocks), dim3(1024), 0, st, idx, P, K, E, counts,
                        flags);
-    hipError_t err = hipGetLastError();
+    err = hipGetLastError();
     if (err != hipSuccess) return COLI_EDEVICE;
     hipLaunchKernelGGL(k_group_scatter, dim3(gblocks), dim3(1024), 0, st, idx, P, E, counts,
                        offsets, row_pair, pair_row);
     err = hipGetLastError();
     if (err != hipSuccess) return COLI_EDEVICE;
+    }
 
     const int64_t rbD = coli_row_bytes(ex->fmt, D), rbF = coli_row_bytes(ex->fmt, F);
     const int64_t shared_row0 = (int64_t)P;
@@ -207,6 +212,8 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
     const bool sh_same_down = sh && sh->fmt == ex->fmt && sh->F == F;
 
     // ---- gate/up + SwiGLU -> h
+    {
+    StageTimer tgu(kStGateUp, st);
     GemvArgs a = {};
     a.w[0] = (const uint8_t *)ex->w_gate;
     a.w[1] = (const uint8_t *)ex->w_up;
@@ -259,8 +266,11 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
         err = gemv_launch(b, sh->fmt, 2, hint, st);
         if (err != hipSuccess) return COLI_EDEVICE;
     }
+    }
 
     // ---- down -> y
+    {
+    StageTimer tdn(kStDown, st);
     GemvArgs d = {};
     d.w[0] = (const uint8_t *)ex->w_down;
     d.s[0] = ex->s_down;
@@ -307,8 +317,10 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
         err = gemv_launch(b, sh->fmt, 1, hint, st);
         if (err != hipSuccess) return COLI_EDEVICE;
     }
+    }
 
     // ---- weighted combine, fixed order
+    StageTimer tcb(kStCombine, st);
     hipLaunchKernelGGL(k_combine, dim3(S), dim3(256), 0, st, y, D, K, pair_row, w, sh ? 1 : 0,
                        shared_row0, out, (int)(al16(out) && al16(y) && D % 4 == 0));
     return to_status(hipGetLastError());
@@ -341,6 +353,7 @@ extern "C" int coli_qgemv(int fmt, const void *W, const float *scale, const floa
     a.out = y;
     a.ldo = O;
     a.aligned = (rb % 16 == 0) && al16(W);
+    StageTimer t(kStQgemv, (hipStream_t)stream);
     return to_status(gemv_launch(a, fmt, 1, S, (hipStream_t)stream));
 }
 
@@ -352,6 +365,7 @@ extern "C" int coli_router(const float *Wr, const float *bias, const float *x, i
     int rc = coli__check_router(Wr, bias, x, S, E, D, K, norm_topk, idx, w, sig, ws, ws_bytes);
     if (rc != COLI_OK) return rc;
     if (S == 0) return COLI_OK;
+    StageTimer t(kStRouter, (hipStream_t)stream);
     return to_status(router_launch(Wr, bias, x, S, E, D, K, norm_topk, routed_scale, topp, idx,
                                    w, keff, sig, (double *)ws, (hipStream_t)stream));
 }
@@ -400,6 +414,7 @@ extern "C" int coli_moe_layer(const coli_router_params *r, const coli_experts *e
     if (run_router) {
         int32_t *ri = idx_out ? idx_out : reinterpret_cast<int32_t *>(wsb + L.idx);
         float *rw = w_out ? w_out : reinterpret_cast<float *>(wsb + L.w);
+        StageTimer tr(kStRouter, st);
         hipError_t e = router_launch(r->w, r->bias, x, S, ex->E, ex->D, K, r->norm_topk,
                                      r->routed_scale, r->topp, ri, rw, nullptr,
                                      reinterpret_cast<float *>(wsb + L.sig),
