@@ -46,7 +46,8 @@ class RouterParams(C.Structure):
 class WsLayout(C.Structure):
     _fields_ = [(n, C.c_int64) for n in ("flags", "sig", "idx", "w", "offsets", "counts",
                                           "row_pair", "pair_row", "h", "y", "router_part",
-                                          "h_ld", "total")]
+                                          "xq", "xsum", "hq", "hsum_part", "work", "n_work",
+                                          "xq_ld", "hq_ld", "h_ld", "total")]
 
 
 EXPORTS = ["coli_row_bytes", "coli_qgemv", "coli_router", "coli_router_workspace_bytes",

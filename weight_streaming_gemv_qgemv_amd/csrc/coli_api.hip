@@ -13,6 +13,7 @@
 #include "coli.h"
 #include "coli_device.h"
 #include "coli_gemv.h"
+#include "coli_mfma.h"
 #include "coli_internal.h"
 #include "coli_router.h"
 #include "coli_stages.h"
@@ -177,6 +178,57 @@ inline bool al16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 int to_status(hipError_t e) { return e == hipSuccess ? COLI_OK : COLI_EDEVICE; }
 
+// The shared expert alone on the vector ALUs (used when its format or width
+// differs from the routed experts'): h rows and y rows start at shared_row0.
+int run_shared_valu(const coli_mlp *sh, const float *x, int S, int D, float *h, int64_t h_ld,
+                    float *y, int64_t shared_row0, int hint, hipStream_t st)
+{
+    const int64_t rbs = coli_row_bytes(sh->fmt, D), rbf = coli_row_bytes(sh->fmt, sh->F);
+    GemvArgs b = {};
+    b.ngroups = 0;
+    b.has_extra = 1;
+    b.xw[0] = (const uint8_t *)sh->w_gate;
+    b.xw[1] = (const uint8_t *)sh->w_up;
+    b.xs[0] = sh->s_gate;
+    b.xs[1] = sh->s_up;
+    b.xO = sh->F;
+    b.O = sh->F;
+    b.x_rows = S;
+    b.x_row0 = (int)shared_row0;
+    b.I = D;
+    b.rb = rbs;
+    b.K = 1;
+    b.xrow_token = 1;
+    b.x = x;
+    b.ldx = D;
+    b.x_vec4 = al16(x) && (D % 4 == 0);
+    b.out = h;
+    b.ldo = h_ld;
+    b.aligned = (rbs % 16 == 0) && al16(sh->w_gate) && al16(sh->w_up);
+    if (gemv_launch(b, sh->fmt, 2, hint, st) != hipSuccess) return COLI_EDEVICE;
+    GemvArgs d = {};
+    d.ngroups = 0;
+    d.has_extra = 1;
+    d.xw[0] = (const uint8_t *)sh->w_down;
+    d.xs[0] = sh->s_down;
+    d.xO = D;
+    d.O = D;
+    d.x_rows = S;
+    d.x_row0 = (int)shared_row0;
+    d.I = sh->F;
+    d.rb = rbf;
+    d.K = 1;
+    d.xrow_token = 0;
+    d.x = h;
+    d.ldx = h_ld;
+    d.x_vec4 = (h_ld % 4 == 0);
+    d.out = y;
+    d.ldo = D;
+    d.aligned = (rbf % 16 == 0) && al16(sh->w_down);
+    if (gemv_launch(d, sh->fmt, 1, hint, st) != hipSuccess) return COLI_EDEVICE;
+    return COLI_OK;
+}
+
 // Grouped expert products: routed experts (+ shared) -> h -> y -> out.
 int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int S, int K,
                 const int32_t *idx, const float *w, float *out, uint8_t *ws,
@@ -208,6 +260,110 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
     const int64_t rbD = coli_row_bytes(ex->fmt, D), rbF = coli_row_bytes(ex->fmt, F);
     const int64_t shared_row0 = (int64_t)P;
     const int hint = 8;
+    // matrix-core path: whole 16-byte row segments, 16-byte aligned tensors
+    const bool mm = rbD % 16 == 0 && rbF % 16 == 0 && al16(ex->w_gate) && al16(ex->w_up) &&
+                    al16(ex->w_down) && (ex->fmt == COLI_I8 || ex->fmt == COLI_I4 || ex->fmt == COLI_I2);
+    const bool sh_mm = mm && sh && sh->fmt == ex->fmt && sh->F == F && al16(sh->w_gate) &&
+                       al16(sh->w_up) && al16(sh->w_down);
+    if (mm) {
+        const int64_t rows = (int64_t)P + (sh ? S : 0);
+        int32_t *work = reinterpret_cast<int32_t *>(ws + L.work);
+        int32_t *n_work = reinterpret_cast<int32_t *>(ws + L.n_work);
+        uint16_t *xq = reinterpret_cast<uint16_t *>(ws + L.xq);
+        float *xsum = reinterpret_cast<float *>(ws + L.xsum);
+        uint16_t *hq = reinterpret_cast<uint16_t *>(ws + L.hq);
+        float *hsum = reinterpret_cast<float *>(ws + L.hsum_part);
+        const int64_t max_gp = (rows + 7) / 8 + E + 1;
+        {
+            StageTimer tgu(kStGateUp, st);
+            if (build_work_launch(offsets, E, sh_mm ? S : 0, work, n_work, st) != hipSuccess)
+                return COLI_EDEVICE;
+            if (xprep_launch(ex->fmt, x, D, S, D, (int)L.xq_ld, xq, xsum, st) != hipSuccess)
+                return COLI_EDEVICE;
+            MmArgs a = {};
+            a.w[0] = (const uint8_t *)ex->w_gate;
+            a.w[1] = (const uint8_t *)ex->w_up;
+            a.s[0] = ex->s_gate;
+            a.s[1] = ex->s_up;
+            a.w_gstride = (int64_t)F * rbD;
+            a.s_gstride = F;
+            a.ngroups = E;
+            a.O = F;
+            if (sh_mm) {
+                a.has_extra = 1;
+                a.xw[0] = (const uint8_t *)sh->w_gate;
+                a.xw[1] = (const uint8_t *)sh->w_up;
+                a.xs[0] = sh->s_gate;
+                a.xs[1] = sh->s_up;
+                a.xO = F;
+                a.x_rows = S;
+                a.x_row0 = (int)shared_row0;
+            }
+            a.I = D;
+            a.rb = rbD;
+            a.offsets = offsets;
+            a.row_pair = row_pair;
+            a.K = K;
+            a.xrow_token = 1;
+            a.xq = xq;
+            a.xld = L.xq_ld;
+            a.xsum = xsum;
+            a.xsum_parts = 1;
+            a.work = work;
+            a.n_work = n_work;
+            a.out = h;
+            a.ldo = L.h_ld;
+            a.hq = hq;
+            a.hq_ld = L.hq_ld;
+            a.hq_rows = (int)L.hq_ld;
+            a.hq_fmt = ex->fmt;
+            a.hsum_part = hsum;
+            a.hsum_stride = rows;
+            if (mm_launch(a, ex->fmt, 2, max_gp, st) != hipSuccess) return COLI_EDEVICE;
+        }
+        {
+            StageTimer tdn(kStDown, st);
+            MmArgs d = {};
+            d.w[0] = (const uint8_t *)ex->w_down;
+            d.s[0] = ex->s_down;
+            d.w_gstride = (int64_t)D * rbF;
+            d.s_gstride = D;
+            d.ngroups = E;
+            d.O = D;
+            if (sh_mm) {
+                d.has_extra = 1;
+                d.xw[0] = (const uint8_t *)sh->w_down;
+                d.xs[0] = sh->s_down;
+                d.xO = D;
+                d.x_rows = S;
+                d.x_row0 = (int)shared_row0;
+            }
+            d.I = F;
+            d.rb = rbF;
+            d.offsets = offsets;
+            d.row_pair = row_pair;
+            d.K = K;
+            d.xrow_token = 0;
+            d.xq = hq;
+            d.xld = L.hq_ld;
+            d.xsum = hsum;
+            d.xsum_parts = (int)(L.hq_ld / mm_rows_per_block());
+            d.xsum_stride = rows;
+            d.work = work;
+            d.n_work = n_work;
+            d.out = y;
+            d.ldo = D;
+            if (mm_launch(d, ex->fmt, 1, max_gp, st) != hipSuccess) return COLI_EDEVICE;
+        }
+        if (sh && !sh_mm) {
+            int rc = run_shared_valu(sh, x, S, D, h, L.h_ld, y, shared_row0, hint, st);
+            if (rc != COLI_OK) return rc;
+        }
+        StageTimer tcb(kStCombine, st);
+        hipLaunchKernelGGL(k_combine, dim3(S), dim3(256), 0, st, y, D, K, pair_row, w, sh ? 1 : 0,
+                           shared_row0, out, (int)(al16(out) && al16(y) && D % 4 == 0));
+        return to_status(hipGetLastError());
+    }
     const bool sh_same_up = sh && sh->fmt == ex->fmt;
     const bool sh_same_down = sh && sh->fmt == ex->fmt && sh->F == F;
 

@@ -158,7 +158,20 @@ int coli_moe_workspace_layout(int S, int K, int E, int D, int F, int F_shared,
     if (!mul_ok(rows, D, &t) || !mul_ok(t, 4, &t)) return COLI_ESHAPE;
     REGION(y, t);
     REGION(router_part, coli__router_partial_bytes(S, E, D));
+    /* matrix-core path: activations as bf16 hi/lo planes padded to 256 */
+    int64_t Dld = round_up(D, 256), Fld = round_up(Fmax, 256), tilesF = Fld / 128;
+    if (!mul_ok((int64_t)S, 4 * Dld, &t)) return COLI_ESHAPE;
+    REGION(xq, t);
+    REGION(xsum, (int64_t)S * 4);
+    if (!mul_ok(rows, 4 * Fld, &t)) return COLI_ESHAPE;
+    REGION(hq, t);
+    if (!mul_ok(rows, 4 * tilesF, &t)) return COLI_ESHAPE;
+    REGION(hsum_part, t);
+    REGION(work, ((rows + 7) / 8 + (int64_t)E + 2) * 4);
+    REGION(n_work, 64);
 #undef REGION
+    out->xq_ld = Dld;
+    out->hq_ld = Fld;
     out->h_ld = Fmax;
     out->total = off;
     return COLI_OK;
