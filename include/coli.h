@@ -180,13 +180,15 @@ size_t coli_moe_workspace_bytes(int S, int K, int E, int D, int F,
  *   y          [S*K + S, D] fp32: expert output per grouped row (same
  *              numbering), before the routing weight.
  *   router_part  fp64 partial router logits (scratch).
- *   xq, xsum, hq, hsum_part, work, n_work   matrix-core scratch: bf16 hi/lo
- *              activation planes ([S][2][xq_ld], [S*K + S][2][hq_ld]), their
- *              sums, and the device-built list of (expert, token pass) items. */
+ *   xf, xsum, hf, hsum, work, n_work   matrix-core scratch: per (expert,
+ *              16-token pass) the activations and the SwiGLU output as bf16
+ *              hi/lo fragments (xf_stride / hf_stride elements per pass),
+ *              their sums, and the device-built list of passes. */
 typedef struct {
     int64_t flags, sig, idx, w, offsets, counts, row_pair, pair_row, h, y, router_part;
-    int64_t xq, xsum, hq, hsum_part, work, n_work;
-    int64_t xq_ld, hq_ld;  /* plane strides in elements (D, max(F, F_shared) rounded up to 256) */
+    int64_t xf, xsum, hf, hsum, work, n_work;
+    int64_t n_pass_max;            /* passes the scratch is sized for */
+    int64_t xf_stride, hf_stride;  /* bf16 elements per pass */
     int64_t h_ld;   /* row stride of h in floats (max of F and F_shared) */
     int64_t total;  /* == coli_moe_workspace_bytes(...) */
 } coli_ws_layout;

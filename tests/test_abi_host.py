@@ -137,7 +137,8 @@ def test_workspace_layout_is_consistent(L):
                                 (2048, 8, 256, 6144, 2048, 2048), (5, 3, 24, 40, 24, 16)]:
         lay = b.moe_workspace_layout(S, K, E, D, F, Fs)
         assert lay["total"] == b.moe_workspace_bytes(S, K, E, D, F, Fs)
-        regions = sorted((v, k) for k, v in lay.items() if not k.endswith("_ld") and k != "total")
+        regions = sorted((v, k) for k, v in lay.items()
+                         if not k.endswith(("_ld", "_stride", "_max")) and k != "total")
         assert all(v % 256 == 0 for v, _ in regions)
         assert lay["h_ld"] == max(F, Fs)
         rows = S * K + (S if Fs else 0)

@@ -46,8 +46,8 @@ class RouterParams(C.Structure):
 class WsLayout(C.Structure):
     _fields_ = [(n, C.c_int64) for n in ("flags", "sig", "idx", "w", "offsets", "counts",
                                           "row_pair", "pair_row", "h", "y", "router_part",
-                                          "xq", "xsum", "hq", "hsum_part", "work", "n_work",
-                                          "xq_ld", "hq_ld", "h_ld", "total")]
+                                          "xf", "xsum", "hf", "hsum", "work", "n_work",
+                                          "n_pass_max", "xf_stride", "hf_stride", "h_ld", "total")]
 
 
 EXPORTS = ["coli_row_bytes", "coli_qgemv", "coli_router", "coli_router_workspace_bytes",

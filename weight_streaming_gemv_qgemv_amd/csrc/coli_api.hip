@@ -269,16 +269,15 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
         const int64_t rows = (int64_t)P + (sh ? S : 0);
         int32_t *work = reinterpret_cast<int32_t *>(ws + L.work);
         int32_t *n_work = reinterpret_cast<int32_t *>(ws + L.n_work);
-        uint16_t *xq = reinterpret_cast<uint16_t *>(ws + L.xq);
+        uint16_t *xf = reinterpret_cast<uint16_t *>(ws + L.xf);
         float *xsum = reinterpret_cast<float *>(ws + L.xsum);
-        uint16_t *hq = reinterpret_cast<uint16_t *>(ws + L.hq);
-        float *hsum = reinterpret_cast<float *>(ws + L.hsum_part);
-        const int64_t max_gp = (rows + 7) / 8 + E + 1;
+        uint16_t *hf = reinterpret_cast<uint16_t *>(ws + L.hf);
+        float *hsum = reinterpret_cast<float *>(ws + L.hsum);
+        const int64_t max_gp = L.n_pass_max;
+        const int64_t kpD = mm_kpad(D), kpF = mm_kpad(F);
         {
             StageTimer tgu(kStGateUp, st);
             if (build_work_launch(offsets, E, sh_mm ? S : 0, work, n_work, st) != hipSuccess)
-                return COLI_EDEVICE;
-            if (xprep_launch(ex->fmt, x, D, S, D, (int)L.xq_ld, xq, xsum, st) != hipSuccess)
                 return COLI_EDEVICE;
             MmArgs a = {};
             a.w[0] = (const uint8_t *)ex->w_gate;
@@ -300,25 +299,28 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
                 a.x_row0 = (int)shared_row0;
             }
             a.I = D;
+            a.kpad = (int)kpD;
             a.rb = rbD;
             a.offsets = offsets;
             a.row_pair = row_pair;
             a.K = K;
             a.xrow_token = 1;
-            a.xq = xq;
-            a.xld = L.xq_ld;
+            a.xf = xf;
+            a.xf_stride = L.xf_stride;
             a.xsum = xsum;
             a.xsum_parts = 1;
+            a.xsum_stride = 0;
             a.work = work;
             a.n_work = n_work;
             a.out = h;
             a.ldo = L.h_ld;
-            a.hq = hq;
-            a.hq_ld = L.hq_ld;
-            a.hq_rows = (int)L.hq_ld;
-            a.hq_fmt = ex->fmt;
-            a.hsum_part = hsum;
-            a.hsum_stride = rows;
+            a.hf = hf;
+            a.hf_stride = L.hf_stride;
+            a.hf_rows = (int)kpF;
+            a.hf_fmt = ex->fmt;
+            a.hsum = hsum;
+            a.hsum_stride = max_gp * 16;
+            if (xprep_launch(ex->fmt, a, x, D, max_gp, st) != hipSuccess) return COLI_EDEVICE;
             if (mm_launch(a, ex->fmt, 2, max_gp, st) != hipSuccess) return COLI_EDEVICE;
         }
         {
@@ -339,16 +341,17 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
                 d.x_row0 = (int)shared_row0;
             }
             d.I = F;
+            d.kpad = (int)kpF;
             d.rb = rbF;
             d.offsets = offsets;
             d.row_pair = row_pair;
             d.K = K;
             d.xrow_token = 0;
-            d.xq = hq;
-            d.xld = L.hq_ld;
+            d.xf = hf;
+            d.xf_stride = L.hf_stride;
             d.xsum = hsum;
-            d.xsum_parts = (int)(L.hq_ld / mm_rows_per_block());
-            d.xsum_stride = rows;
+            d.xsum_parts = (int)(kpF / mm_rows_per_block());
+            d.xsum_stride = max_gp * 16;
             d.work = work;
             d.n_work = n_work;
             d.out = y;

@@ -7,9 +7,11 @@
 
 namespace coli {
 
-// Groups as in GemvArgs (coli_gemv.h); activations come prepared: hi/lo bf16
-// planes xq[row][2][xld] in the weights' slot order, and sum(hi + lo) per row
-// as the sum of xsum_parts partial arrays (stride xsum_stride).
+// Groups as in GemvArgs (coli_gemv.h).  Work is a list of (group, 16-token
+// pass) entries; every pass has its activations prepared fragment-major in
+// xf (xf_stride elements per pass, kpad = input width rounded up to 512) and
+// the sum of their bf16 hi + lo parts per token in xsum (the sum of
+// xsum_parts arrays of xsum_stride floats, indexed pass * 16 + token).
 struct MmArgs {
     const uint8_t *w[2];
     const float *s[2];
@@ -18,34 +20,35 @@ struct MmArgs {
     const uint8_t *xw[2];
     const float *xs[2];
     int has_extra, xO, x_rows, x_row0;
-    int I;
+    int I, kpad;
     int64_t rb;
     const int *offsets;
     const int *row_pair;
     int K, xrow_token;
-    const uint16_t *xq;
-    int64_t xld;
-    const float *xsum;
+    uint16_t *xf;
+    int64_t xf_stride;
+    float *xsum;
     int xsum_parts;
     int64_t xsum_stride;
     const int *work;     // (g | pass << 11) per group-pass, NULL = one group
     const int *n_work;
     float *out;
     int64_t ldo;
-    // M == 2 only: the result also as hi/lo planes for the next product
-    uint16_t *hq;
-    int64_t hq_ld;
-    int hq_rows;         // rows of hq written per output row (zeros past O)
-    int hq_fmt;          // slot order of the next product's weights
-    float *hsum_part;    // [tiles][hsum_stride] partial sums of hi + lo
+    // M == 2 only: the result also prepared as the next product's activations
+    uint16_t *hf;
+    int64_t hf_stride;
+    int hf_rows;         // outputs written per token (zeros past O), = next kpad
+    int hf_fmt;          // weight format of the next product
+    float *hsum;         // [tiles][hsum_stride] partial sums per pass * 16 + token
     int64_t hsum_stride;
     int tiles;           // set by mm_launch
 };
 
-int mm_kblock(int fmt);
 int mm_rows_per_block();
-hipError_t xprep_launch(int fmt, const float *x, int64_t ldx, int rows, int I, int ld,
-                        uint16_t *xq, float *xsum, hipStream_t st);
+int64_t mm_kpad(int64_t I);
+// One block per possible group-pass (blocks past the device count exit).
+hipError_t xprep_launch(int fmt, const MmArgs &a, const float *x, int64_t ldx,
+                        int64_t max_group_passes, hipStream_t st);
 hipError_t mm_launch(MmArgs a, int fmt, int M, int64_t max_group_passes, hipStream_t st);
 hipError_t build_work_launch(const int32_t *offsets, int E, int extra_rows, int32_t *work,
                              int32_t *n_work, hipStream_t st);

@@ -158,20 +158,24 @@ int coli_moe_workspace_layout(int S, int K, int E, int D, int F, int F_shared,
     if (!mul_ok(rows, D, &t) || !mul_ok(t, 4, &t)) return COLI_ESHAPE;
     REGION(y, t);
     REGION(router_part, coli__router_partial_bytes(S, E, D));
-    /* matrix-core path: activations as bf16 hi/lo planes padded to 256 */
-    int64_t Dld = round_up(D, 256), Fld = round_up(Fmax, 256), tilesF = Fld / 128;
-    if (!mul_ok((int64_t)S, 4 * Dld, &t)) return COLI_ESHAPE;
-    REGION(xq, t);
-    REGION(xsum, (int64_t)S * 4);
-    if (!mul_ok(rows, 4 * Fld, &t)) return COLI_ESHAPE;
-    REGION(hq, t);
-    if (!mul_ok(rows, 4 * tilesF, &t)) return COLI_ESHAPE;
-    REGION(hsum_part, t);
-    REGION(work, ((rows + 7) / 8 + (int64_t)E + 2) * 4);
+    /* matrix-core path: per (expert, 8-token pass) the activations as bf16
+     * hi/lo fragments (16 columns x input width rounded up to 512), their
+     * sums, the SwiGLU output prepared the same way, and the work list */
+    int64_t ngp = (rows + 15) / 16 + (int64_t)E + 1;   /* passes of 16 rows */
+    int64_t KpD = round_up(D, 512), KpF = round_up(Fmax, 512), tilesF = KpF / 128;
+    if (!mul_ok(ngp, 64 * KpD, &t)) return COLI_ESHAPE;
+    REGION(xf, t);
+    REGION(xsum, ngp * 16 * 4);
+    if (!mul_ok(ngp, 64 * KpF, &t)) return COLI_ESHAPE;
+    REGION(hf, t);
+    if (!mul_ok(tilesF * ngp, 16 * 4, &t)) return COLI_ESHAPE;
+    REGION(hsum, t);
+    REGION(work, (ngp + 1) * 4);
     REGION(n_work, 64);
 #undef REGION
-    out->xq_ld = Dld;
-    out->hq_ld = Fld;
+    out->n_pass_max = ngp;
+    out->xf_stride = 32 * KpD;
+    out->hf_stride = 32 * KpF;
     out->h_ld = Fmax;
     out->total = off;
     return COLI_OK;
