@@ -10,7 +10,8 @@ combine.  Two copies of the expert bank live in HBM and steps alternate
 between them, so no step finds its weights in the 256 MB last-level cache.
 
 Other workloads: "decode16" (coli_moe_gemv, 16 tokens, given top-8 routing),
-"qgemv" (int4 12288 x 6144, S = 1, over a rotation of weight copies).
+"qgemv" (int4 12288 x 6144, S = 1, over a rotation of weight copies), "copy"
+(a plain 1 GiB device copy, the yardstick for the HBM byte counters).
 
 Prints ONE JSON line.  `value` is the step's algorithmic bytes (weights of
 the experts actually used, scales, router, activations, outputs) divided by
@@ -66,16 +67,17 @@ def clone_bank(bd):
 
 
 def time_steps(step, steps, warmup):
+    """Warm up, then time exactly `steps` steps between two synchronisations
+    (stage events off).  A second pass of `steps` steps records a HIP event
+    pair around every stage on the stream the kernels run on; it gives the
+    per-kernel durations used for the roofline and the stage breakdown."""
     import torch
+    from weight_streaming_gemv_qgemv_amd import binding as b
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    from weight_streaming_gemv_qgemv_amd import binding as b
-    b.stage_times(reset=True)
-    b.stage_timing(True)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record()
     for i in range(steps):
@@ -83,9 +85,20 @@ def time_steps(step, steps, warmup):
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    ms = t0.elapsed_time(t1) / steps
+    b.stage_times(reset=True)
+    b.stage_timing(True)
+    s0 = torch.cuda.Event(enable_timing=True)
+    s1 = torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for i in range(steps):
+        step(warmup + steps + i)
+    s1.record()
+    torch.cuda.synchronize()
     b.stage_timing(False)
     stages = b.stage_times(reset=True)
-    return t0.elapsed_time(t1) / steps, wall, stages
+    stages["_step_ms_with_stage_events"] = (s0.elapsed_time(s1), steps)
+    return ms, wall, stages
 
 
 def cpu_baseline_layer(bank, shared, Wr, bias, x, K, ntok):
@@ -138,7 +151,7 @@ def run_layer64(args, dev):
     gu_bytes = (uniq + 1) * gu + S * D * 4 + (S * K + S) * F * 4
     res = dict(workload="moe_layer_decode_64", ms=ms, wall=wall, step_bytes=step_bytes,
                tokens=S, stages=stages, uniq=uniq,
-               dominant=dict(kernel="k_gemv<I4,M=2> (expert gate/up + SwiGLU)",
+               dominant=dict(kernel="k_mm<I4,2> (grouped expert gate/up + SwiGLU, matrix cores)",
                              bytes_per_launch=gu_bytes, ms_per_launch=gu_ms / max(gu_n, 1),
                              launches=gu_n))
     if not args.no_cpu_baseline:
@@ -181,7 +194,7 @@ def run_decode16(args, dev):
     gu_ms, gu_n = stages["gate_up"]
     res = dict(workload="moe_expert_decode_16", ms=ms, wall=wall, step_bytes=step_bytes,
                tokens=S, stages=stages, uniq=uniq,
-               dominant=dict(kernel="k_gemv<I4,M=2> (expert gate/up + SwiGLU)",
+               dominant=dict(kernel="k_mm<I4,2> (grouped expert gate/up + SwiGLU, matrix cores)",
                              bytes_per_launch=uniq * gu + S * D * 4 + S * K * F * 4,
                              ms_per_launch=gu_ms / max(gu_n, 1), launches=gu_n))
     if not args.no_cpu_baseline:
@@ -224,12 +237,27 @@ def run_qgemv(args, dev):
                               ms_per_launch=q_ms / max(q_n, 1), launches=q_n))
 
 
+def run_copy(args, dev):
+    """A plain 1 GiB device-to-device copy of known size: the yardstick that
+    converts the FETCH_SIZE / WRITE_SIZE counters into bytes."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    c = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        c.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"workload": "copy_1GiB", "bytes_read_per_copy": n,
+                      "bytes_written_per_copy": n, "copies": args.steps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="layer64", choices=["layer64", "decode16", "qgemv"])
+    ap.add_argument("--workload", default="layer64", choices=["layer64", "decode16", "qgemv", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=64)
     args = ap.parse_args()
@@ -244,6 +272,9 @@ def main():
     dev = torch.device("cuda:0")
     from weight_streaming_gemv_qgemv_amd import binding as b
     b.lib()
+    if args.workload == "copy":
+        run_copy(args, dev)
+        return
     run = {"layer64": run_layer64, "decode16": run_decode16, "qgemv": run_qgemv}[args.workload]
     r = run(args, dev)
     ms = r["ms"]

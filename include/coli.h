@@ -252,10 +252,11 @@ int coli_check_device_flags(const void *ws, void *stream, uint32_t *flags_out);
  * for the recorded events and writes, per stage, the total milliseconds and
  * the number of timed launches since the last reset (host arrays of
  * COLI_NSTAGES entries; either may be NULL).  Stages: 0 router, 1 grouping,
- * 2 gate/up + SwiGLU, 3 down, 4 combine, 5 qgemv.  The pages time the same
+ * 2 gate/up + SwiGLU, 3 down, 4 combine, 5 qgemv, 6 matrix-core preparation
+ * (work list and activation fragments ahead of gate/up).  The pages time the same
  * phases of their MoE block [metal@93cde63 -- moe_finish timers;
  * glm.c@98759bf -- profile counters]. */
-#define COLI_NSTAGES 6
+#define COLI_NSTAGES 7
 int coli_stage_timing(int enable);
 int coli_stage_times(double *ms, int64_t *calls, int reset);
 const char *coli_stage_name(int stage);

@@ -42,7 +42,7 @@ def check(got, ref, K, what, sig_ulps_allowed=2):
 
 
 @pytest.mark.parametrize("E", [24, 168, 256])
-@pytest.mark.parametrize("D", [64, 1000, 6144])
+@pytest.mark.parametrize("D", [64, 1000, 1001, 6144])   # 1001: unaligned rows, scalar loads
 def test_router_random(dev, orc, E, D):
     g = synth.rng(500, E, D)
     for S in (1, 7, 64):

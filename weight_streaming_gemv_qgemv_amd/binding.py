@@ -54,7 +54,7 @@ EXPORTS = ["coli_row_bytes", "coli_qgemv", "coli_router", "coli_router_workspace
            "coli_moe_workspace_bytes", "coli_moe_workspace_layout", "coli_moe_gemv",
            "coli_moe_layer", "coli_check_device_flags", "coli_strerror", "coli_version",
            "coli_stage_timing", "coli_stage_times", "coli_stage_name"]
-NSTAGES = 6
+NSTAGES = 7
 
 _lib = None
 

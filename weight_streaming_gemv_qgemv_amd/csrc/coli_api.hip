@@ -75,26 +75,49 @@ __global__ __launch_bounds__(1024) void k_group_count(const int32_t *__restrict_
 }
 
 // Exclusive prefix of the counts per expert, then a stable scatter of every
-// slot of the expert into its group.
+// slot of the expert into its group.  When `work` is given, each expert's
+// wave also writes the matrix-core work list entries of its group (passes of
+// `tpp` rows, entry g | pass << 11, in group order), and the wave of the last
+// expert adds those of the extra group g = E (extra_rows rows) and the count.
 __global__ __launch_bounds__(1024) void k_group_scatter(const int32_t *__restrict__ idx, int P,
                                                         int E, const int32_t *__restrict__ counts,
                                                         int32_t *__restrict__ offsets,
                                                         int32_t *__restrict__ row_pair,
-                                                        int32_t *__restrict__ pair_row)
+                                                        int32_t *__restrict__ pair_row,
+                                                        int extra_rows, int tpp,
+                                                        int32_t *__restrict__ work,
+                                                        int32_t *__restrict__ n_work)
 {
     __shared__ int32_t sidx[kWin];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int e = blockIdx.x * kGroupWaves + wave;
     int off = 0;
     if (e < E) {
-        int part = 0;
-        for (int j = lane; j < e; j += 64) part += counts[j];
+        int part = 0, ppart = 0;
+        for (int j = lane; j < e; j += 64) {
+            const int c = counts[j];
+            part += c;
+            ppart += (c + tpp - 1) / tpp;
+        }
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o, kWave);
+        for (int o = 32; o > 0; o >>= 1) {
+            part += __shfl_xor(part, o, kWave);
+            ppart += __shfl_xor(ppart, o, kWave);
+        }
         off = part;
+        const int ce = counts[e];
         if (lane == 0) {
             offsets[e] = off;
-            if (e == E - 1) offsets[E] = off + counts[e];
+            if (e == E - 1) offsets[E] = off + ce;
+        }
+        if (work) {
+            const int np = (ce + tpp - 1) / tpp;
+            for (int p = lane; p < np; p += 64) work[ppart + p] = e | (p << 11);
+            if (e == E - 1) {
+                const int nx = (extra_rows + tpp - 1) / tpp;
+                for (int p = lane; p < nx; p += 64) work[ppart + np + p] = E | (p << 11);
+                if (lane == 0) *n_work = ppart + np + nx;
+            }
         }
     }
     int run = 0;
@@ -128,7 +151,10 @@ __global__ __launch_bounds__(1024) void k_group_scatter(const int32_t *__restric
 
 // out[s, :] = sum_{kk: slot kept} w[s,kk] * y[row(s,kk), :]  (+ y[shared row]),
 // slots in order kk = 0..K-1, then the shared expert: a fixed order.
-__global__ __launch_bounds__(256) void k_combine(const float *__restrict__ y, int D, int K,
+// Block (s, c) covers columns [c * kCombineCols, +kCombineCols) of token s:
+// one float4 (vec4) or one float per thread, all K rows read together.
+constexpr int kCombineThreads = 256;
+__global__ __launch_bounds__(kCombineThreads) void k_combine(const float *__restrict__ y, int D, int K,
                                                  const int32_t *__restrict__ pair_row,
                                                  const float *__restrict__ w, int has_shared,
                                                  int64_t shared_row0, float *__restrict__ out,
@@ -138,40 +164,50 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ y, in
     const int32_t *pr = pair_row + (int64_t)s * K;
     const float *ws = w + (int64_t)s * K;
     if (vec4) {
-        for (int d = threadIdx.x * 4; d < D; d += blockDim.x * 4) {
-            float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-            for (int kk = 0; kk < K; ++kk) {
-                const int r = pr[kk];
-                if (r < 0) continue;
-                const float wk = ws[kk];
-                const float4 v = *reinterpret_cast<const float4 *>(y + (int64_t)r * D + d);
-                acc.x = fmaf(wk, v.x, acc.x);
-                acc.y = fmaf(wk, v.y, acc.y);
-                acc.z = fmaf(wk, v.z, acc.z);
-                acc.w = fmaf(wk, v.w, acc.w);
-            }
-            if (has_shared) {
-                const float4 v =
-                    *reinterpret_cast<const float4 *>(y + (shared_row0 + s) * (int64_t)D + d);
-                acc.x += v.x;
-                acc.y += v.y;
-                acc.z += v.z;
-                acc.w += v.w;
-            }
-            *reinterpret_cast<float4 *>(out + (int64_t)s * D + d) = acc;
+        const int d = (blockIdx.y * kCombineThreads + threadIdx.x) * 4;
+        if (d >= D) return;
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int kk = 0; kk < K; ++kk) {
+            const int r = pr[kk];
+            if (r < 0) continue;
+            const float wk = ws[kk];
+            const float4 v = *reinterpret_cast<const float4 *>(y + (int64_t)r * D + d);
+            acc.x = fmaf(wk, v.x, acc.x);
+            acc.y = fmaf(wk, v.y, acc.y);
+            acc.z = fmaf(wk, v.z, acc.z);
+            acc.w = fmaf(wk, v.w, acc.w);
         }
+        if (has_shared) {
+            const float4 v = *reinterpret_cast<const float4 *>(y + (shared_row0 + s) * (int64_t)D + d);
+            acc.x += v.x;
+            acc.y += v.y;
+            acc.z += v.z;
+            acc.w += v.w;
+        }
+        *reinterpret_cast<float4 *>(out + (int64_t)s * D + d) = acc;
     } else {
-        for (int d = threadIdx.x; d < D; d += blockDim.x) {
-            float acc = 0.f;
-            for (int kk = 0; kk < K; ++kk) {
-                const int r = pr[kk];
-                if (r < 0) continue;
-                acc = fmaf(ws[kk], y[(int64_t)r * D + d], acc);
-            }
-            if (has_shared) acc += y[(shared_row0 + s) * (int64_t)D + d];
-            out[(int64_t)s * D + d] = acc;
+        const int d = blockIdx.y * kCombineThreads + threadIdx.x;
+        if (d >= D) return;
+        float acc = 0.f;
+        for (int kk = 0; kk < K; ++kk) {
+            const int r = pr[kk];
+            if (r < 0) continue;
+            acc = fmaf(ws[kk], y[(int64_t)r * D + d], acc);
         }
+        if (has_shared) acc += y[(shared_row0 + s) * (int64_t)D + d];
+        out[(int64_t)s * D + d] = acc;
     }
+}
+
+hipError_t combine_launch(const float *y, int S, int D, int K, const int32_t *pair_row,
+                          const float *w, int has_shared, int64_t shared_row0, float *out,
+                          int vec4, hipStream_t st)
+{
+    const int per = vec4 ? 4 * kCombineThreads : kCombineThreads;
+    const dim3 grid((unsigned)S, (unsigned)((D + per - 1) / per));
+    hipLaunchKernelGGL(k_combine, grid, dim3(kCombineThreads), 0, st, y, D, K, pair_row, w,
+                       has_shared, shared_row0, out, vec4);
+    return hipGetLastError();
 }
 
 inline bool al16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
@@ -245,18 +281,6 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
     float *y = reinterpret_cast<float *>(ws + L.y);
     const int gblocks = (E + kGroupWaves - 1) / kGroupWaves;
     hipError_t err;
-    {
-    StageTimer tg(kStGroup, st);
-    hipLaunchKernelGGL(k_group_count, dim3(gblocks), dim3(1024), 0, st, idx, P, K, E, counts,
-                       flags);
-    err = hipGetLastError();
-    if (err != hipSuccess) return COLI_EDEVICE;
-    hipLaunchKernelGGL(k_group_scatter, dim3(gblocks), dim3(1024), 0, st, idx, P, E, counts,
-                       offsets, row_pair, pair_row);
-    err = hipGetLastError();
-    if (err != hipSuccess) return COLI_EDEVICE;
-    }
-
     const int64_t rbD = coli_row_bytes(ex->fmt, D), rbF = coli_row_bytes(ex->fmt, F);
     const int64_t shared_row0 = (int64_t)P;
     const int hint = 8;
@@ -265,10 +289,22 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
                     al16(ex->w_down) && (ex->fmt == COLI_I8 || ex->fmt == COLI_I4 || ex->fmt == COLI_I2);
     const bool sh_mm = mm && sh && sh->fmt == ex->fmt && sh->F == F && al16(sh->w_gate) &&
                        al16(sh->w_up) && al16(sh->w_down);
+    int32_t *work = reinterpret_cast<int32_t *>(ws + L.work);
+    int32_t *n_work = reinterpret_cast<int32_t *>(ws + L.n_work);
+    {
+    StageTimer tg(kStGroup, st);
+    hipLaunchKernelGGL(k_group_count, dim3(gblocks), dim3(1024), 0, st, idx, P, K, E, counts,
+                       flags);
+    err = hipGetLastError();
+    if (err != hipSuccess) return COLI_EDEVICE;
+    hipLaunchKernelGGL(k_group_scatter, dim3(gblocks), dim3(1024), 0, st, idx, P, E, counts,
+                       offsets, row_pair, pair_row, sh_mm ? S : 0, mm_tokens_per_pass(),
+                       mm ? work : nullptr, n_work);
+    err = hipGetLastError();
+    if (err != hipSuccess) return COLI_EDEVICE;
+    }
+
     if (mm) {
-        const int64_t rows = (int64_t)P + (sh ? S : 0);
-        int32_t *work = reinterpret_cast<int32_t *>(ws + L.work);
-        int32_t *n_work = reinterpret_cast<int32_t *>(ws + L.n_work);
         uint16_t *xf = reinterpret_cast<uint16_t *>(ws + L.xf);
         float *xsum = reinterpret_cast<float *>(ws + L.xsum);
         uint16_t *hf = reinterpret_cast<uint16_t *>(ws + L.hf);
@@ -276,9 +312,6 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
         const int64_t max_gp = L.n_pass_max;
         const int64_t kpD = mm_kpad(D), kpF = mm_kpad(F);
         {
-            StageTimer tgu(kStGateUp, st);
-            if (build_work_launch(offsets, E, sh_mm ? S : 0, work, n_work, st) != hipSuccess)
-                return COLI_EDEVICE;
             MmArgs a = {};
             a.w[0] = (const uint8_t *)ex->w_gate;
             a.w[1] = (const uint8_t *)ex->w_up;
@@ -308,8 +341,6 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
             a.xf = xf;
             a.xf_stride = L.xf_stride;
             a.xsum = xsum;
-            a.xsum_parts = 1;
-            a.xsum_stride = 0;
             a.work = work;
             a.n_work = n_work;
             a.out = h;
@@ -319,8 +350,12 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
             a.hf_rows = (int)kpF;
             a.hf_fmt = ex->fmt;
             a.hsum = hsum;
-            a.hsum_stride = max_gp * 16;
-            if (xprep_launch(ex->fmt, a, x, D, max_gp, st) != hipSuccess) return COLI_EDEVICE;
+            a.hsum_stride = max_gp * mm_tokens_per_pass();
+            {
+                StageTimer tp(kStPrep, st);
+                if (xprep_launch(ex->fmt, a, x, D, max_gp, st) != hipSuccess) return COLI_EDEVICE;
+            }
+            StageTimer tgu(kStGateUp, st);
             if (mm_launch(a, ex->fmt, 2, max_gp, st) != hipSuccess) return COLI_EDEVICE;
         }
         {
@@ -349,9 +384,12 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
             d.xrow_token = 0;
             d.xf = hf;
             d.xf_stride = L.hf_stride;
-            d.xsum = hsum;
-            d.xsum_parts = (int)(kpF / mm_rows_per_block());
-            d.xsum_stride = max_gp * 16;
+            // the activations' sums: the gate/up tiles' partial sums, added up
+            // (into xsum, free once gate/up has run)
+            if (sum_parts_launch(hsum, (int)(kpF / mm_rows_per_block()), max_gp * mm_tokens_per_pass(), max_gp, xsum,
+                                 st) != hipSuccess)
+                return COLI_EDEVICE;
+            d.xsum = xsum;
             d.work = work;
             d.n_work = n_work;
             d.out = y;
@@ -363,9 +401,8 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
             if (rc != COLI_OK) return rc;
         }
         StageTimer tcb(kStCombine, st);
-        hipLaunchKernelGGL(k_combine, dim3(S), dim3(256), 0, st, y, D, K, pair_row, w, sh ? 1 : 0,
-                           shared_row0, out, (int)(al16(out) && al16(y) && D % 4 == 0));
-        return to_status(hipGetLastError());
+        return to_status(combine_launch(y, S, D, K, pair_row, w, sh ? 1 : 0, shared_row0, out,
+                                        (int)(al16(out) && al16(y) && D % 4 == 0), st));
     }
     const bool sh_same_up = sh && sh->fmt == ex->fmt;
     const bool sh_same_down = sh && sh->fmt == ex->fmt && sh->F == F;
@@ -480,9 +517,8 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
 
     // ---- weighted combine, fixed order
     StageTimer tcb(kStCombine, st);
-    hipLaunchKernelGGL(k_combine, dim3(S), dim3(256), 0, st, y, D, K, pair_row, w, sh ? 1 : 0,
-                       shared_row0, out, (int)(al16(out) && al16(y) && D % 4 == 0));
-    return to_status(hipGetLastError());
+    return to_status(combine_launch(y, S, D, K, pair_row, w, sh ? 1 : 0, shared_row0, out,
+                                    (int)(al16(out) && al16(y) && D % 4 == 0), st));
 }
 
 }  // namespace

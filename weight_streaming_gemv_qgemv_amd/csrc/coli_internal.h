@@ -11,6 +11,9 @@
 
 #define COLI_MAX_E 1024 /* 16 scores per lane of a 64-wide wave */
 #define COLI_MAX_K 64
+/* rows ("tokens") per pass of the matrix-core expert kernels: each pass
+ * feeds 2 * COLI_MM_TPP columns (bf16 hi and lo per token) of one MFMA tile */
+#define COLI_MM_TPP 8
 
 #ifdef __cplusplus
 extern "C" {

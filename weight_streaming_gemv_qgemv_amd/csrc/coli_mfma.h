@@ -27,9 +27,7 @@ struct MmArgs {
     int K, xrow_token;
     uint16_t *xf;
     int64_t xf_stride;
-    float *xsum;
-    int xsum_parts;
-    int64_t xsum_stride;
+    float *xsum;         // [group-pass * 16 + token] sum(hi + lo) of the activations
     const int *work;     // (g | pass << 11) per group-pass, NULL = one group
     const int *n_work;
     float *out;
@@ -45,13 +43,16 @@ struct MmArgs {
 };
 
 int mm_rows_per_block();
+int mm_tokens_per_pass();
 int64_t mm_kpad(int64_t I);
 // One block per possible group-pass (blocks past the device count exit).
 hipError_t xprep_launch(int fmt, const MmArgs &a, const float *x, int64_t ldx,
                         int64_t max_group_passes, hipStream_t st);
 hipError_t mm_launch(MmArgs a, int fmt, int M, int64_t max_group_passes, hipStream_t st);
-hipError_t build_work_launch(const int32_t *offsets, int E, int extra_rows, int32_t *work,
-                             int32_t *n_work, hipStream_t st);
+// out[i] = sum_p parts[p * stride + i] in p order, i < max_group_passes * 16.
+hipError_t sum_parts_launch(const float *parts, int nparts, int64_t stride, int64_t max_group_passes,
+                           float *out, hipStream_t st);
+
 
 }  // namespace coli
 

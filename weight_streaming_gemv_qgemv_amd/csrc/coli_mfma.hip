@@ -22,6 +22,7 @@
 //     their XCD, and all tiles of one group-pass run on the same XCD so its
 //     activation rows are fetched into one L2.
 #include "coli_device.h"
+#include "coli_internal.h"
 #include "coli_mfma.h"
 
 namespace coli {
@@ -50,6 +51,21 @@ __device__ __forceinline__ uint32_t wsel(const uint4 &v, int d)
     return d == 0 ? v.x : d == 1 ? v.y : d == 2 ? v.z : v.w;
 }
 
+// Constants hidden from constant folding (an empty asm statement emits no
+// instruction): with the mask in a scalar register and the exponent pattern
+// in a vector register, (a & m) | o becomes one v_and_or_b32 -- with literal
+// operands it would be an AND and an OR.
+__device__ __forceinline__ uint32_t opaque_s(uint32_t v)
+{
+    asm("" : "+s"(v));
+    return v;
+}
+__device__ __forceinline__ uint32_t opaque_v(uint32_t v)
+{
+    asm("" : "+v"(v));
+    return v;
+}
+
 // bf16 codes for MFMA step s (8 elements) of a 16-byte segment.
 template <int FMT> __device__ __forceinline__ uint4 codes(const uint4 &w, int s);
 
@@ -59,7 +75,7 @@ template <int FMT> __device__ __forceinline__ uint4 codes(const uint4 &w, int s)
 template <> __device__ __forceinline__ uint4 codes<kI4>(const uint4 &w, int s)
 {
     const uint32_t u = wsel(w, s);
-    const uint32_t m = 0x000F000Fu, e = 0x43004300u;
+    const uint32_t m = opaque_s(0x000F000Fu), e = opaque_v(0x43004300u);
     return make_uint4((u & m) | e, ((u >> 4) & m) | e, ((u >> 8) & m) | e, ((u >> 12) & m) | e);
 }
 
@@ -70,7 +86,7 @@ template <> __device__ __forceinline__ uint4 codes<kI2>(const uint4 &w, int s)
 {
     const uint32_t u = wsel(w, s >> 1);
     const int k0 = 4 * (s & 1);
-    const uint32_t m = 0x00030003u, e = 0x43004300u;
+    const uint32_t m = opaque_s(0x00030003u), e = opaque_v(0x43004300u);
     return make_uint4(((u >> (2 * k0)) & m) | e, ((u >> (2 * k0 + 2)) & m) | e,
                       ((u >> (2 * k0 + 4)) & m) | e, ((u >> (2 * k0 + 6)) & m) | e);
 }
@@ -118,16 +134,18 @@ __device__ __forceinline__ floatx4 mfma(const uint4 &a, const uint4 &b, floatx4 
 }
 
 // ---------------------------------------------------------------- layout
-// Work is cut into passes of up to kTPP = 16 activation rows ("tokens") of
-// one group.  A pass's activations are stored "fragment-major": for k-block
+// Work is cut into passes of up to kTPP activation rows ("tokens") of one
+// group.  A pass's activations are stored "fragment-major": for k-block
 // kbi, MFMA step s and lane group q, chunk c = (kbi*STEPS + s)*4 + q holds,
-// for each of the kCols = 32 columns (token t: column 2t = hi, 2t+1 = lo;
-// N-tile n = columns 16n..16n+15), the 8 bf16 values of the slots that lane
-// (col, q) feeds to that step.  A k-block's activations are one contiguous
+// for each of the kCols = 2 kTPP columns (token t: column 2t = hi, 2t+1 =
+// lo; N-tile n = columns 16n..16n+15), the 8 bf16 values of the slots that
+// lane (col, q) feeds to that step.  A k-block's activations are one contiguous
 // STEPS*2 KB run, and the live tokens' columns are a prefix of every chunk.
 // Element e of the product's input sits in chunk c, slot j = pos_of(e).
-constexpr int kTPP = 16;
+constexpr int kTPP = COLI_MM_TPP;
 constexpr int kCols = 2 * kTPP;
+constexpr int kNT = kCols / 16;   // MFMA N-tiles per pass
+static_assert(kCols % 16 == 0 && kNT >= 1 && kNT <= 2, "a pass is one or two N-tiles");
 
 template <int FMT> __device__ __forceinline__ int elem_of(int kbi, int s, int q, int j)
 {
@@ -169,7 +187,15 @@ __device__ __forceinline__ void pos_any(int fmt, int e, int &c, int &j)
     else pos_of<kI8>(e, c, j);
 }
 
-// Group-pass decode shared by the prep and the product kernels.
+// Work-list and group-offset reads: written by an earlier kernel and never
+// written here, so they are read through the constant address space (scalar
+// loads) when the index is uniform.
+__device__ __forceinline__ int cload(const int *p)
+{
+    return *(__attribute__((address_space(4))) const int *)p;
+}
+
+// Group-pass decode shared by the prep and the product kernels (gp uniform).
 struct GP {
     int g, pass, r0, cnt, t0, nt;
     bool extra;
@@ -178,7 +204,7 @@ __device__ __forceinline__ GP decode_gp(const MmArgs &a, int gp)
 {
     GP d;
     if (a.work) {
-        const int wv = a.work[gp];
+        const int wv = cload(a.work + gp);
         d.g = wv & 0x7FF;
         d.pass = wv >> 11;
     } else {
@@ -190,8 +216,8 @@ __device__ __forceinline__ GP decode_gp(const MmArgs &a, int gp)
         d.r0 = a.x_row0;
         d.cnt = a.x_rows;
     } else if (a.offsets) {
-        d.r0 = a.offsets[d.g];
-        d.cnt = a.offsets[d.g + 1] - d.r0;
+        d.r0 = cload(a.offsets + d.g);
+        d.cnt = cload(a.offsets + d.g + 1) - d.r0;
     } else {
         d.r0 = 0;
         d.cnt = a.x_rows;
@@ -203,250 +229,304 @@ __device__ __forceinline__ GP decode_gp(const MmArgs &a, int gp)
 
 __device__ __forceinline__ int n_group_passes(const MmArgs &a)
 {
-    return a.work ? *a.n_work : (a.x_rows + kTPP - 1) / kTPP;
+    return a.work ? cload(a.n_work) : (a.x_rows + kTPP - 1) / kTPP;
 }
 
 // ---------------------------------------------------------------- x prep
-// One block per group-pass: gathers the pass's activation rows (dead ones
-// as zeros), splits them into bf16 hi/lo and stores them fragment-major;
-// also sum(hi + lo) per token, in a fixed order.
+// Block (group-pass, token): the block reads the token's activation row in
+// coalesced runs of RUN consecutive elements (all of a thread's loads are
+// issued before any is used), splits each value into bf16 hi/lo and stores
+// the run as the 16-byte units of the chunk(s) it feeds.  A run of 8 (int8,
+// int4) is exactly one chunk; a run of 16 (int2) is the two chunks of an
+// even/odd step pair.  Only live columns are written: the product kernel
+// reads nothing else.  Also sum(hi + lo) per token, in a fixed order.
+constexpr int kPrepThreads = 256;
+constexpr int kPrepRuns = 4;   // runs per thread per round
 template <int FMT>
-__global__ __launch_bounds__(256) void k_xprep(MmArgs a, const float *__restrict__ x, int64_t ldx)
+__global__ __launch_bounds__(kPrepThreads) void k_xprep(MmArgs a, const float *__restrict__ x,
+                                                        int64_t ldx, int vec)
 {
-    using T = MF<FMT>;
-    __shared__ float red[4][kTPP];
-    const int gp = blockIdx.x;
+    constexpr int RUN = FMT == kI2 ? 16 : 8;
+    __shared__ float red[kPrepThreads / kWave];
+    const int gp = blockIdx.x, t = blockIdx.y;
     if (gp >= n_group_passes(a)) return;
     const GP d = decode_gp(a, gp);
-    const int tid = threadIdx.x, t = tid % kTPP;
-    int row = -1;
-    if (t < d.nt) {
-        const int tok = d.t0 + t;
-        if (!a.xrow_token) row = d.r0 + tok;
-        else if (d.extra) row = tok;
-        else row = a.row_pair[d.r0 + tok] / a.K;
-    }
-    const float *xr = row >= 0 ? x + (int64_t)row * ldx : nullptr;
+    if (t >= d.nt) return;   // uniform over the block
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tok = d.t0 + t;
+    int row;
+    if (!a.xrow_token) row = d.r0 + tok;
+    else if (d.extra) row = tok;
+    else row = a.row_pair[d.r0 + tok] / a.K;
+    const float *xr = x + (int64_t)row * ldx;
     uint16_t *dst = a.xf + (int64_t)gp * a.xf_stride;
-    const int nchunks = a.kpad / 8;
+    const int nruns = a.kpad / RUN;
     float sum = 0.f;
-    for (int item = tid; item < nchunks * kTPP; item += 256) {
-        const int c = item / kTPP;
-        const int kbi = c / (T::STEPS * 4), s = (c >> 2) % T::STEPS, q = c & 3;
-        uint32_t hw[4], lw[4];
+    for (int r0 = 0; r0 < nruns; r0 += kPrepThreads * kPrepRuns) {
+        float v[kPrepRuns][RUN];
 #pragma unroll
-        for (int j2 = 0; j2 < 4; ++j2) {
-            uint32_t hp = 0, lp = 0;
+        for (int k = 0; k < kPrepRuns; ++k) {
+            const int e0 = (r0 + k * kPrepThreads + tid) * RUN;
+            if (vec && e0 + RUN <= a.I) {
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int e = elem_of<FMT>(kbi, s, q, 2 * j2 + h);
-                const float v = (xr && e < a.I) ? xr[e] : 0.f;
-                const uint16_t hv = bf16_rne(v);
-                const uint16_t lv = bf16_rne(v - bf16_f(hv));
-                sum += bf16_f(hv) + bf16_f(lv);
-                hp |= (uint32_t)hv << (16 * h);
-                lp |= (uint32_t)lv << (16 * h);
+                for (int i = 0; i < RUN / 4; ++i) {
+                    const float4 f = *reinterpret_cast<const float4 *>(xr + e0 + 4 * i);
+                    v[k][4 * i] = f.x;
+                    v[k][4 * i + 1] = f.y;
+                    v[k][4 * i + 2] = f.z;
+                    v[k][4 * i + 3] = f.w;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < RUN; ++i) v[k][i] = e0 + i < a.I ? xr[e0 + i] : 0.f;
             }
-            hw[j2] = hp;
-            lw[j2] = lp;
         }
-        *reinterpret_cast<uint4 *>(dst + ((int64_t)c * kCols + 2 * t) * 8) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-        *reinterpret_cast<uint4 *>(dst + ((int64_t)c * kCols + 2 * t + 1) * 8) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+#pragma unroll
+        for (int k = 0; k < kPrepRuns; ++k) {
+            const int r = r0 + k * kPrepThreads + tid;
+            if (r >= nruns) break;
+            uint16_t hv[RUN], lv[RUN];
+#pragma unroll
+            for (int i = 0; i < RUN; ++i) {
+                hv[i] = bf16_rne(v[k][i]);
+                lv[i] = bf16_rne(v[k][i] - bf16_f(hv[i]));
+                sum += bf16_f(hv[i]) + bf16_f(lv[i]);
+            }
+            // slot pairs (2m, 2m+1) of each chunk, as the unpacking orders them
+            int c, j;
+            pos_of<FMT>(r * RUN, c, j);
+            uint32_t hw[RUN / 2], lw[RUN / 2];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                int k0, k1;
+                if constexpr (FMT == kI8) { k0 = 2 * m; k1 = 2 * m + 1; }
+                else if constexpr (FMT == kI4) { k0 = m; k1 = m + 4; }
+                else { k0 = m; k1 = m + 8; }
+                hw[m] = (uint32_t)hv[k0] | ((uint32_t)hv[k1] << 16);
+                lw[m] = (uint32_t)lv[k0] | ((uint32_t)lv[k1] << 16);
+                if constexpr (FMT == kI2) {
+                    hw[4 + m] = (uint32_t)hv[m + 4] | ((uint32_t)hv[m + 12] << 16);
+                    lw[4 + m] = (uint32_t)lv[m + 4] | ((uint32_t)lv[m + 12] << 16);
+                }
+            }
+#pragma unroll
+            for (int h = 0; h < RUN / 8; ++h) {
+                uint16_t *u = dst + ((int64_t)(c + 4 * h) * kCols + 2 * t) * 8;
+                *reinterpret_cast<uint4 *>(u) = make_uint4(hw[4 * h], hw[4 * h + 1], hw[4 * h + 2], hw[4 * h + 3]);
+                *reinterpret_cast<uint4 *>(u + 8) = make_uint4(lw[4 * h], lw[4 * h + 1], lw[4 * h + 2], lw[4 * h + 3]);
+            }
+        }
     }
-    // lanes with the same t (= lane % 16): xor over the higher lane bits
-    sum += __shfl_xor(sum, 16, kWave);
-    sum += __shfl_xor(sum, 32, kWave);
-    if ((tid & 63) < kTPP) red[tid >> 6][t] = sum;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, kWave);
+    if (lane == 0) red[wave] = sum;
     __syncthreads();
-    if (tid < kTPP)
-        a.xsum[(int64_t)gp * kTPP + tid] = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
+    if (tid == 0) {
+        float tot = 0.f;
+        for (int w = 0; w < kPrepThreads / kWave; ++w) tot += red[w];
+        a.xsum[(int64_t)gp * kTPP + t] = tot;
+    }
 }
 
 // ---------------------------------------------------------------- main kernel
-// NTL = N-tiles (of 16 columns = 8 tokens) processed per pass: 1 when the
-// pass has at most 8 live tokens, else 2.
+// One MFMA k-block step of a wave: weights (row-contiguous registers) moved
+// into the operand layout in place with ds_bpermute -- lane (q, col) gets
+// row col, chunk q, from lane 4 col + q -- then STEPS x M x 2 x NTL products
+// against the activations staged in LDS (bs).  NTL = live N-tiles of 16
+// columns (8 tokens each).
 template <int FMT, int M, int NTL>
-__device__ __forceinline__ void mm_kloop(const MmArgs &a, const uint8_t *const (&wr)[M][2],
-                                         int64_t last_seg, int src_lane, const uint4 *bglob,
-                                         int live_units, int nkb, int tid, int lane,
-                                         uint4 (*bsh)[MF<FMT>::STEPS * 4 * kCols],
-                                         floatx4 (&acc)[M][2][2])
+__device__ __forceinline__ void mm_step(uint4 (&wl)[M][2][MF<FMT>::SEGS], const uint4 *bs,
+                                        int src4, int q, int col, floatx4 (&acc)[M][2][kNT])
 {
     using T = MF<FMT>;
-    constexpr int SEGS = T::SEGS, SPS = T::SPS, STEPS = T::STEPS, KB = T::KB, BITS = T::BITS;
-    constexpr int CH = STEPS * 4;                 // chunks per k-block
+    constexpr int SEGS = T::SEGS, SPS = T::SPS, STEPS = T::STEPS;
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int sg = 0; sg < SEGS; ++sg) {
+                const uint4 v = wl[m][mt][sg];
+                wl[m][mt][sg] = make_uint4((uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)v.x),
+                                           (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)v.y),
+                                           (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)v.z),
+                                           (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)v.w));
+            }
+#pragma unroll
+    for (int s2 = 0; s2 < STEPS; ++s2) {
+        uint4 xb[NTL];
+#pragma unroll
+        for (int n = 0; n < NTL; ++n) xb[n] = bs[(s2 * 4 + q) * kCols + 16 * n + col];
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                const uint4 cw = codes<FMT>(wl[m][mt][s2 / SPS], s2 % SPS);
+#pragma unroll
+                for (int n = 0; n < NTL; ++n) acc[m][mt][n] = mfma(cw, xb[n], acc[m][mt][n]);
+            }
+    }
+}
+
+// Everything about one item -- (group-pass gp, 128-row tile) -- that its
+// loads, its activation staging and its epilogue need.
+template <int M, int UMAX>
+struct Item {
+    int gp, tile, nt, row0, Og;
+    const uint8_t *wb[M];      // the group's matrices (uniform)
+    uint32_t roff[2];          // this lane's row (clamped) * rb + its 16-byte chunk, per row tile
+    const float *sc[M];
+    const uint4 *bglob;        // the group-pass's activation fragments (uniform)
+    int boff[UMAX];            // this thread's activation units in a k-block (-1: dead)
+};
+
+// Persistent blocks walk the items of their XCD (block b of XCD x takes
+// items b, b + blocks-per-XCD, ...; all tiles of one group-pass run on the
+// same XCD, so its activations are fetched into one L2) as ONE pipeline of
+// k-block steps that runs across item boundaries:
+//   * weights are loaded two steps ahead into a ring of three register
+//     buffers, activations three steps ahead into another ring of three
+//     (the loop body is three steps, so every buffer has a fixed name); at
+//     the end of each step the next step's activations go to a ring of
+//     three LDS buffers;
+//   * loads complete in issue order, so per step they are issued as: the
+//     epilogue's scales and token sums (second-to-last step of an item),
+//     the activations three steps ahead, the weights two steps ahead.  The
+//     staging wait (activations issued two steps earlier) then never covers
+//     the weights in flight, the products wait only for their own k-block,
+//     and the epilogue never waits for the next item's k-blocks; two
+//     k-blocks of weights per wave stay in flight all the time.
+//   * kpad is a multiple of 1024, so an item has at least 4 k-blocks and
+//     three steps ahead is at most the next item.
+template <int FMT, int M>
+__global__ __launch_bounds__(256) void k_mm(MmArgs a)
+{
+    using T = MF<FMT>;
+    constexpr int STEPS = T::STEPS, KB = T::KB, SEGS = T::SEGS, BITS = T::BITS;
+    constexpr int CH = STEPS * 4;                 // activation chunks per k-block
     constexpr int UMAX = (CH * kCols + 255) / 256;
-    const int q = lane >> 4, col = lane & 15;
-    // k-block kbi: segment sg of each row at byte kbi*KB*BITS/8 + 64 sg + 16
-    // chunk.  Its activations are loaded once per block -- only the live
-    // columns, live_units = CH * 2nt 16-byte units, spread over the block --
-    // and shared through LDS, so the weights are nearly the only global
-    // loads (every 16-byte-per-lane load costs the texture path about the
-    // same, whatever it reads).
-    const int lc = live_units / CH;               // live columns per chunk
-    auto load = [&](int kbi, uint4 (&wv)[M][2][SEGS], uint4 (&bv)[UMAX]) {
-        const int64_t b0 = (int64_t)kbi * KB * BITS / 8;
+    constexpr float OFF = T::OFF;
+    __shared__ float red[4][kTPP];
+    __shared__ uint4 bsh[3][CH * kCols];
+    __shared__ uint4 btrash[256];   // dead staging lanes write here: every load and store is unconditional
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 15, q = lane >> 4;
+    const int lrow = lane >> 2, lchunk = lane & 3;
+    const int src4 = 4 * (4 * col + q);
+    const int xcd = blockIdx.x % kXcds, lb = blockIdx.x / kXcds;
+    const int bpx = gridDim.x / kXcds;                 // blocks per XCD (grid is a multiple of 8)
+    const int n_gp = n_group_passes(a);
+    const int gp_per_xcd = (n_gp + kXcds - 1 - xcd) / kXcds;   // group-passes gp = xcd + 8 i
+    const int n_items = gp_per_xcd * a.tiles;
+    const int nkb = a.kpad / KB;                       // >= 4: kpad is a multiple of 1024
+    if (lb >= n_items) return;                         // whole block, before any barrier
+    const int64_t kbytes = (int64_t)KB * BITS / 8;
+    // segments past the row end are clamped to its last segment (they meet
+    // zero activations)
+    const uint32_t last_seg = (uint32_t)(a.rb - 16 - 16 * lchunk);
+
+    using It = Item<M, UMAX>;
+    auto make = [&](It &c, int it) {
+        // uniform: the work-list and offset lookups below are scalar loads
+        c.gp = __builtin_amdgcn_readfirstlane(xcd + kXcds * (it / a.tiles));
+        c.tile = __builtin_amdgcn_readfirstlane(it % a.tiles);
+        const GP d = decode_gp(a, c.gp);
+        c.nt = d.nt;
+        c.row0 = d.r0 + d.t0;
+        const uint8_t *W[M];
+        if (d.extra) {
+            c.Og = a.xO;
+#pragma unroll
+            for (int m = 0; m < M; ++m) { W[m] = a.xw[m]; c.sc[m] = a.xs[m]; }
+        } else {
+            c.Og = a.O;
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                W[m] = a.w[m] + (int64_t)d.g * a.w_gstride;
+                c.sc[m] = a.s[m] + (int64_t)d.g * a.s_gstride;
+            }
+        }
+        // lane L loads row L/4, chunk L%4 (a quarter-wave reads 4 rows x 64
+        // contiguous bytes); rows past Og are clamped and never written
+        const int obase = c.tile * kRowsPerBlock + wave * kRowsPerWave;
+#pragma unroll
+        for (int m = 0; m < M; ++m) c.wb[m] = W[m];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+            c.roff[mt] = (uint32_t)(min(obase + 16 * mt + lrow, c.Og - 1) * a.rb) + 16 * lchunk;
+        c.bglob = reinterpret_cast<const uint4 *>(a.xf + (int64_t)c.gp * a.xf_stride);
+        // live activation units of a k-block: CH chunks x 2 nt columns
+        const int lc = 2 * d.nt, live = CH * lc;
+#pragma unroll
+        for (int i = 0; i < UMAX; ++i) {
+            const int u = tid + 256 * i;
+            const int ch = u / lc;
+            c.boff[i] = u < live ? ch * kCols + (u - ch * lc) : -1;
+        }
+    };
+    // weights: uniform matrix base + 32-bit lane offset (scalar-base loads);
+    // past the row end (only when the row is shorter than kpad) each lane's
+    // segment is clamped to the row's last one
+    auto loadW = [&](const It &c, int kbi, uint4 (&w)[M][2][SEGS]) {
+        const uint32_t b0 = (uint32_t)kbi * (uint32_t)kbytes;
 #pragma unroll
         for (int m = 0; m < M; ++m)
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
                 for (int sg = 0; sg < SEGS; ++sg)
-                    wv[m][mt][sg] = gload16(wr[m][mt] + min(b0 + 64 * sg, last_seg));
+                    w[m][mt][sg] = gload16(c.wb[m] + (c.roff[mt] + min(b0 + 64 * sg, last_seg)));
+    };
+    // activations: dead units re-read unit 0 and are written to the trash
+    // slot, so every load and store is unconditional
+    auto loadB = [&](const It &c, int kbi, uint4 (&bv)[UMAX]) {
+        const uint4 *src = c.bglob + (int64_t)kbi * CH * kCols;
+#pragma unroll
+        for (int i = 0; i < UMAX; ++i) bv[i] = gload16(src + (uint32_t)max(c.boff[i], 0));
+    };
+    auto stage = [&](const It &c, int buf, const uint4 (&bv)[UMAX]) {
 #pragma unroll
         for (int i = 0; i < UMAX; ++i) {
-            const int u = tid + 256 * i;
-            if (u < live_units) {
-                const int ch = u / lc, cu = u - ch * lc;
-                bv[i] = gload16(bglob + ((int64_t)kbi * CH + ch) * kCols + cu);
-            }
+            uint4 *dst = c.boff[i] >= 0 ? &bsh[buf][c.boff[i]] : &btrash[tid];
+            *dst = bv[i];
         }
     };
-    auto stage = [&](int buf, const uint4 (&bv)[UMAX]) {
-#pragma unroll
-        for (int i = 0; i < UMAX; ++i) {
-            const int u = tid + 256 * i;
-            if (u < live_units) {
-                const int ch = u / lc, cu = u - ch * lc;
-                bsh[buf][ch * kCols + cu] = bv[i];
-            }
-        }
-    };
-    auto compute = [&](const uint4 (&wl)[M][2][SEGS], int buf) {
-        uint4 wv[M][2][SEGS];
+    // epilogue inputs: the scales of the lane's 4 rows per (matrix, row tile)
+    // and the sums of its tokens (clamped indexes, unconditional loads; rows
+    // and tokens out of range are never written)
+    float sreg[M][2][4], xsr[kNT];
+    auto load_epi = [&](const It &c) {
+        const int obase = c.tile * kRowsPerBlock + wave * kRowsPerWave;
 #pragma unroll
         for (int m = 0; m < M; ++m)
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                for (int sg = 0; sg < SEGS; ++sg) {
-                    const uint4 v = wl[m][mt][sg];
-                    wv[m][mt][sg] = make_uint4(
-                        (uint32_t)__builtin_amdgcn_ds_bpermute(4 * src_lane, (int)v.x),
-                        (uint32_t)__builtin_amdgcn_ds_bpermute(4 * src_lane, (int)v.y),
-                        (uint32_t)__builtin_amdgcn_ds_bpermute(4 * src_lane, (int)v.z),
-                        (uint32_t)__builtin_amdgcn_ds_bpermute(4 * src_lane, (int)v.w));
-                }
+                for (int r = 0; r < 4; ++r)
+                    sreg[m][mt][r] = gloadf(c.sc[m] + min(obase + 16 * mt + 4 * q + r, c.Og - 1));
 #pragma unroll
-        for (int s2 = 0; s2 < STEPS; ++s2) {
-            uint4 xb[NTL];
-#pragma unroll
-            for (int n = 0; n < NTL; ++n) xb[n] = bsh[buf][(s2 * 4 + q) * kCols + 16 * n + col];
-#pragma unroll
-            for (int m = 0; m < M; ++m)
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt) {
-                    const uint4 cw = codes<FMT>(wv[m][mt][s2 / SPS], s2 % SPS);
-#pragma unroll
-                    for (int n = 0; n < NTL; ++n) acc[m][mt][n] = mfma(cw, xb[n], acc[m][mt][n]);
-                }
-        }
+        for (int n = 0; n < kNT; ++n)
+            xsr[n] = gloadf(a.xsum + (int64_t)c.gp * kTPP + min(8 * n + (col >> 1), c.nt - 1));
     };
-    // Weights double-buffered in registers, activations in LDS, one k-block
-    // ahead; straight-line body (the last prefetch re-reads a valid k-block
-    // and is not used).  sched_barrier keeps the scheduler from sinking a
-    // prefetch below the products.
-    uint4 wa[M][2][SEGS], wb[M][2][SEGS], ba[UMAX], bb[UMAX];
-    __syncthreads();   // bsh of the previous item is no longer read
-    load(0, wa, ba);
-    stage(0, ba);
-    __syncthreads();
-    for (int kbi = 0; kbi < nkb; kbi += 2) {
-        load(kbi + 1, wb, bb);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(wa, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        stage(1, bb);
-        __syncthreads();
-        load(min(kbi + 2, nkb - 1), wa, ba);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(wb, 1);
-        __builtin_amdgcn_sched_barrier(0);
-        // every wave finished reading buffer 0 before the barrier that
-        // published buffer 1
-        stage(0, ba);
-        __syncthreads();
-    }
-}
 
-template <int FMT, int M>
-__global__ __launch_bounds__(256) void k_mm(MmArgs a)
-{
-    using T = MF<FMT>;
-    constexpr int STEPS = T::STEPS, KB = T::KB;
-    constexpr float OFF = T::OFF;
-    __shared__ float red[4][kTPP];
-    __shared__ uint4 bsh[2][STEPS * 4 * kCols];   // activations of one k-block, double-buffered
+    floatx4 acc[M][2][kNT];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int n = 0; n < kNT; ++n) acc[m][mt][n] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int col = lane & 15, q = lane >> 4;
-    const int xcd = blockIdx.x % kXcds, lb = blockIdx.x / kXcds;
-    const int bpx = gridDim.x / kXcds;                 // blocks per XCD (grid is a multiple of 8)
-    const int n_gp = n_group_passes(a);
-    const int gp_per_xcd = (n_gp + kXcds - 1 - xcd) / kXcds;   // group-passes gp = xcd + 8 i
-    const int n_items = gp_per_xcd * a.tiles;
-    const int nkb = a.kpad / KB;                       // even: kpad is a multiple of 512
-
-    for (int it = lb; it < n_items; it += bpx) {
-        const int gp = xcd + kXcds * (it / a.tiles);
-        const int tile = it % a.tiles;
-        const GP d = decode_gp(a, gp);
-        const uint8_t *W[M];
-        const float *SC[M];
-        int Og;
-        if (d.extra) {
-            Og = a.xO;
+    // ---- epilogue: D[4q + r][16n + col]; add the lo column to the hi column
+    auto epilogue = [&](const It &c) {
+        const int obase = c.tile * kRowsPerBlock + wave * kRowsPerWave;
+        float hpart[kNT] = {};   // per N-tile: this lane's hi + lo outputs (M == 2)
 #pragma unroll
-            for (int m = 0; m < M; ++m) { W[m] = a.xw[m]; SC[m] = a.xs[m]; }
-        } else {
-            Og = a.O;
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-                W[m] = a.w[m] + (int64_t)d.g * a.w_gstride;
-                SC[m] = a.s[m] + (int64_t)d.g * a.s_gstride;
-            }
-        }
-        const int obase = tile * kRowsPerBlock + wave * kRowsPerWave;
-        // Weights are loaded row-contiguously -- lane L reads row L/4, chunk
-        // L%4, so a quarter-wave touches 4 rows x 64 bytes -- and moved into
-        // the MFMA operand layout (lane (q, col) holds row col, chunk q) with
-        // ds_bpermute, which runs on the LDS crossbar instead of the texture
-        // path.  Rows past Og are clamped (never written); segments past the
-        // row end are clamped to its last segment and meet zero activations.
-        const int lrow = lane >> 2, lchunk = lane & 3;
-        const uint8_t *wr[M][2];
-#pragma unroll
-        for (int m = 0; m < M; ++m)
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-                wr[m][mt] = W[m] + (int64_t)min(obase + 16 * mt + lrow, Og - 1) * a.rb + 16 * lchunk;
-        const int64_t last_seg = a.rb - 16 - 16 * lchunk;
-        const uint4 *bglob = reinterpret_cast<const uint4 *>(a.xf + (int64_t)gp * a.xf_stride);
-        const int live_units = STEPS * 4 * 2 * d.nt;
-        floatx4 acc[M][2][2];
-#pragma unroll
-        for (int m = 0; m < M; ++m)
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                for (int n = 0; n < 2; ++n) acc[m][mt][n] = floatx4{0.f, 0.f, 0.f, 0.f};
-        if (nkb > 0) {
-            if (d.nt > 8)
-                mm_kloop<FMT, M, 2>(a, wr, last_seg, 4 * col + q, bglob, live_units, nkb, tid, lane, bsh, acc);
-            else
-                mm_kloop<FMT, M, 1>(a, wr, last_seg, 4 * col + q, bglob, live_units, nkb, tid, lane, bsh, acc);
-        }
-        // ---- epilogue: D[4q + r][16n + col]; add the lo column to the hi column
-        float hpart[2] = {0.f, 0.f};   // per N-tile: this lane's hi + lo outputs (M == 2)
-#pragma unroll
-        for (int n = 0; n < 2; ++n) {
+        for (int n = 0; n < kNT; ++n) {
+            if (n == 1 && c.nt <= 8) break;            // uniform
             const int tok = 8 * n + (col >> 1);
-            if (n == 1 && d.nt <= 8) break;            // uniform
-            const bool live = tok < d.nt;
-            float xs_t = 0.f;
-            if (live)
-                for (int p = 0; p < a.xsum_parts; ++p)
-                    xs_t += gloadf(a.xsum + (int64_t)p * a.xsum_stride + (int64_t)gp * kTPP + tok);
+            const bool live = tok < c.nt;
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
                 float v[M][4];
@@ -460,35 +540,34 @@ __global__ __launch_bounds__(256) void k_mm(MmArgs a)
                 float res[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int o = ob + r;
                     float y = 0.f;
-                    if (o < Og) {
-                        y = gloadf(SC[0] + o) * (v[0][r] - OFF * xs_t);
+                    if (ob + r < c.Og) {
+                        y = sreg[0][mt][r] * (v[0][r] - OFF * xsr[n]);
                         if constexpr (M == 2) {
-                            const float u = gloadf(SC[1] + o) * (v[1][r] - OFF * xs_t);
+                            const float u = sreg[1][mt][r] * (v[1][r] - OFF * xsr[n]);
                             y = silu_f(y) * u;
                         }
                     }
                     res[r] = y;
                 }
                 if (writer) {
-                    float *op = a.out + (int64_t)(d.r0 + d.t0 + tok) * a.ldo;
+                    float *op = a.out + (int64_t)(c.row0 + tok) * a.ldo;
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        if (ob + r < Og) op[ob + r] = res[r];
+                        if (ob + r < c.Og) op[ob + r] = res[r];
                     if constexpr (M == 2) {
                         if (a.hf) {
-                            uint16_t *hb = a.hf + (int64_t)gp * a.hf_stride + 2 * tok * 8;
+                            uint16_t *hb = a.hf + (int64_t)c.gp * a.hf_stride + 2 * tok * 8;
 #pragma unroll
                             for (int r = 0; r < 4; ++r) {
                                 const int o = ob + r;
                                 if (o < a.hf_rows) {
                                     const uint16_t hv = bf16_rne(res[r]);
                                     const uint16_t lv = bf16_rne(res[r] - bf16_f(hv));
-                                    int c, j;
-                                    pos_any(a.hf_fmt, o, c, j);
-                                    hb[(int64_t)c * kCols * 8 + j] = hv;
-                                    hb[(int64_t)c * kCols * 8 + 8 + j] = lv;
+                                    int cc, j;
+                                    pos_any(a.hf_fmt, o, cc, j);
+                                    hb[(int64_t)cc * kCols * 8 + j] = hv;
+                                    hb[(int64_t)cc * kCols * 8 + 8 + j] = lv;
                                     hpart[n] += bf16_f(hv) + bf16_f(lv);
                                 }
                             }
@@ -500,21 +579,106 @@ __global__ __launch_bounds__(256) void k_mm(MmArgs a)
         if constexpr (M == 2) {
             if (a.hsum) {
                 // sum over the 4 lane groups (rows), then over the 4 waves, per token
-                __syncthreads();   // red[] of the previous item is consumed
 #pragma unroll
-                for (int n = 0; n < 2; ++n) {
+                for (int n = 0; n < kNT; ++n) {
                     float hp = hpart[n];
                     hp += __shfl_xor(hp, 16, kWave);
                     hp += __shfl_xor(hp, 32, kWave);
                     if (q == 0 && (col & 1) == 0) red[wave][8 * n + (col >> 1)] = hp;
                 }
                 __syncthreads();
-                if (tid < d.nt)
-                    a.hsum[(int64_t)tile * a.hsum_stride + (int64_t)gp * kTPP + tid] =
+                if (tid < c.nt)
+                    a.hsum[(int64_t)c.tile * a.hsum_stride + (int64_t)c.gp * kTPP + tid] =
                         (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
+                __syncthreads();   // red[] is free again
             }
         }
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int n = 0; n < kNT; ++n) acc[m][mt][n] = floatx4{0.f, 0.f, 0.f, 0.f};
+    };
+
+    // nxt is the block's next item, or a copy of cur after the last one (its
+    // loads then re-read valid data that nothing uses)
+    It cur, nxt;
+    make(cur, lb);
+    int jn = lb + bpx;
+    bool has_nxt = jn < n_items;
+    if (has_nxt) make(nxt, jn);
+    else nxt = cur;
+
+    uint4 w0[M][2][SEGS], w1[M][2][SEGS], w2[M][2][SEGS];
+    uint4 b0[UMAX], b1[UMAX], b2[UMAX];
+    int k = 0, buf = 0;
+    // prologue, as the steady state would have issued it: B(0), B(1), W(0),
+    // B(2), W(1); then B(0) goes to LDS
+    loadB(cur, 0, b0);
+    loadB(cur, 1, b1);
+    loadW(cur, 0, w0);
+    loadB(cur, 2, b2);
+    loadW(cur, 1, w1);
+    stage(cur, 0, b0);
+    __syncthreads();
+
+    // one k-block step s = (cur, k): returns true after the block's last item
+    //   wc = W(s), wl <- W(s+2); bst = B(s+1) (to LDS), bld <- B(s+3)
+    auto step = [&](uint4 (&wc)[M][2][SEGS], uint4 (&wl)[M][2][SEGS], const uint4 (&bst)[UMAX],
+                    uint4 (&bld)[UMAX]) -> bool {
+        if (k == nkb - 2) load_epi(cur);
+        // the sources are selected, not branched on: the same loads are
+        // issued on every path, so the waits count them exactly
+        It src = cur;
+        if (k + 3 >= nkb) src = nxt;
+        loadB(src, k + 3 < nkb ? k + 3 : k + 3 - nkb, bld);
+        src = cur;
+        if (k + 2 >= nkb) src = nxt;
+        loadW(src, k + 2 < nkb ? k + 2 : k + 2 - nkb, wl);
+        __builtin_amdgcn_sched_barrier(0);
+        if (kNT == 2 && cur.nt > 8) mm_step<FMT, M, kNT>(wc, bsh[buf], src4, q, col, acc);
+        else mm_step<FMT, M, 1>(wc, bsh[buf], src4, q, col, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        const int nb = buf == 2 ? 0 : buf + 1;
+        // every wave finished reading buffer nb (two steps ago) before the
+        // barrier at the end of the previous step
+        src = cur;
+        if (k + 1 >= nkb) src = nxt;
+        stage(src, nb, bst);
+        __syncthreads();
+        buf = nb;
+        if (k != nkb - 1) {
+            ++k;
+            return false;
+        }
+        epilogue(cur);
+        if (!has_nxt) return true;
+        cur = nxt;
+        k = 0;
+        jn += bpx;
+        has_nxt = jn < n_items;
+        if (has_nxt) make(nxt, jn);
+        else nxt = cur;
+        return false;
+    };
+    for (;;) {
+        if (step(w0, w2, b1, b0)) break;
+        if (step(w1, w0, b2, b1)) break;
+        if (step(w2, w1, b0, b2)) break;
     }
+}
+
+// xsum of the down product's passes: the gate/up epilogue leaves one partial
+// sum per 128-row tile; add them in tile order (one thread per pass token).
+__global__ void k_sum_parts(const float *__restrict__ parts, int nparts, int64_t stride, int n,
+                            float *__restrict__ out)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    float s = 0.f;
+    for (int p = 0; p < nparts; ++p) s += parts[(int64_t)p * stride + i];
+    out[i] = s;
 }
 
 // Resident blocks of one kernel on the whole device (occupancy x CUs),
@@ -556,20 +720,33 @@ hipError_t launch_fmt(const MmArgs &a, int M, int64_t items, hipStream_t st)
 }  // namespace
 
 int mm_rows_per_block() { return kRowsPerBlock; }
-int64_t mm_kpad(int64_t I) { return (I + 511) / 512 * 512; }
+int mm_tokens_per_pass() { return kTPP; }
+int64_t mm_kpad(int64_t I) { return (I + 1023) / 1024 * 1024; }
 
 hipError_t xprep_launch(int fmt, const MmArgs &a, const float *x, int64_t ldx, int64_t max_group_passes,
                         hipStream_t st)
 {
     if (max_group_passes <= 0) return hipSuccess;
     if (max_group_passes > 0x7FFFFFFF) return hipErrorInvalidValue;
-    const dim3 g((unsigned)max_group_passes), b(256);
+    const dim3 g((unsigned)max_group_passes, kTPP), b(kPrepThreads);
+    const int vec = ldx % 4 == 0 && ((uintptr_t)x & 15u) == 0;
     switch (fmt) {
-    case kI8: hipLaunchKernelGGL(k_xprep<kI8>, g, b, 0, st, a, x, ldx); break;
-    case kI4: hipLaunchKernelGGL(k_xprep<kI4>, g, b, 0, st, a, x, ldx); break;
-    case kI2: hipLaunchKernelGGL(k_xprep<kI2>, g, b, 0, st, a, x, ldx); break;
+    case kI8: hipLaunchKernelGGL(k_xprep<kI8>, g, b, 0, st, a, x, ldx, vec); break;
+    case kI4: hipLaunchKernelGGL(k_xprep<kI4>, g, b, 0, st, a, x, ldx, vec); break;
+    case kI2: hipLaunchKernelGGL(k_xprep<kI2>, g, b, 0, st, a, x, ldx, vec); break;
     default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+hipError_t sum_parts_launch(const float *parts, int nparts, int64_t stride, int64_t max_group_passes,
+                           float *out, hipStream_t st)
+{
+    const int64_t n = max_group_passes * kTPP;
+    if (n <= 0) return hipSuccess;
+    if (n > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_sum_parts, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, parts,
+                       nparts, stride, (int)n, out);
     return hipGetLastError();
 }
 
@@ -585,49 +762,6 @@ hipError_t mm_launch(MmArgs a, int fmt, int M, int64_t max_group_passes, hipStre
     case kI2: return launch_fmt<kI2>(a, M, items, st);
     default: return hipErrorInvalidValue;
     }
-}
-
-// ---------------------------------------------------------------- work list
-// One block: passes of kTPP rows per group (the extra group has x_rows rows),
-// exclusive scan, then (g | pass << 11) entries in group order.
-__global__ __launch_bounds__(1024) void k_build_work(const int32_t *__restrict__ offsets, int E,
-                                                     int extra_rows, int32_t *__restrict__ work,
-                                                     int32_t *__restrict__ n_work)
-{
-    __shared__ int32_t scan[1024];
-    __shared__ int32_t carry;
-    const int G = E + (extra_rows > 0 ? 1 : 0);
-    if (threadIdx.x == 0) carry = 0;
-    __syncthreads();
-    for (int base = 0; base < G; base += 1024) {
-        const int g = base + threadIdx.x;
-        int np = 0;
-        if (g < G) {
-            const int cnt = g < E ? offsets[g + 1] - offsets[g] : extra_rows;
-            np = (cnt + kTPP - 1) / kTPP;
-        }
-        scan[threadIdx.x] = np;
-        __syncthreads();
-        for (int off = 1; off < 1024; off <<= 1) {
-            const int v = threadIdx.x >= off ? scan[threadIdx.x - off] : 0;
-            __syncthreads();
-            scan[threadIdx.x] += v;
-            __syncthreads();
-        }
-        const int start = carry + scan[threadIdx.x] - np;
-        for (int p = 0; p < np; ++p) work[start + p] = g | (p << 11);
-        __syncthreads();
-        if (threadIdx.x == 1023) carry += scan[1023];
-        __syncthreads();
-    }
-    if (threadIdx.x == 0) *n_work = carry;
-}
-
-hipError_t build_work_launch(const int32_t *offsets, int E, int extra_rows, int32_t *work,
-                             int32_t *n_work, hipStream_t st)
-{
-    hipLaunchKernelGGL(k_build_work, dim3(1), dim3(1024), 0, st, offsets, E, extra_rows, work, n_work);
-    return hipGetLastError();
 }
 
 }  // namespace coli

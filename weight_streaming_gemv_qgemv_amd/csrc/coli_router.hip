@@ -26,6 +26,8 @@ namespace {
 
 typedef double double4_t __attribute__((ext_vector_type(4)));
 
+constexpr int kRouterMaxE = 1024;   // the experts a wave holds: 16 per lane
+
 // Partial logits over one d-slice for a tile of 16 tokens x 64 experts
 // (4 waves, 16 experts each).  v_mfma_f64_16x16x4f64 operand layout:
 //   A (16 x 4):  lane l holds A[l % 16][l / 16]
@@ -36,11 +38,16 @@ typedef double double4_t __attribute__((ext_vector_type(4)));
 // reads 4 consecutive d of its expert row and of its token row, and feeds
 // them to 4 consecutive MFMAs, so MFMA k-slot l/16 at step j is
 // d = d0 + 4 * (l / 16) + j: every product Wr[e,d] * x[s,d] is formed once.
+// VEC: rows are 16-byte aligned and D % 4 == 0, so the 4 values are one
+// 16-byte load; the loads of 6 steps (96 d) are issued together and the
+// next 6 steps are in flight while the current ones are multiplied.
+template <bool VEC>
 __global__ __launch_bounds__(256) void k_router_partial(const float *__restrict__ Wr,
                                                         const float *__restrict__ x, int S,
                                                         int E, int D, int slice,
                                                         double *__restrict__ part)
 {
+    constexpr int kSteps = 6;   // 16-d steps per chunk
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int t0 = blockIdx.x * 16;
     const int e0 = blockIdx.y * 64 + wave * 16;
@@ -52,18 +59,49 @@ __global__ __launch_bounds__(256) void k_router_partial(const float *__restrict_
     const float *wp = (e < E) ? Wr + (int64_t)e * D : nullptr;
     const float *xp = (t < S) ? x + (int64_t)t * D : nullptr;
     double4_t acc = {0.0, 0.0, 0.0, 0.0};
-    for (int d0 = dbeg; d0 < dend; d0 += 16) {
-        const int d = d0 + 4 * kg;
-        float wa[4], xb[4];
+    auto load = [&](int d0, float4 (&wa)[kSteps], float4 (&xb)[kSteps]) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const bool in = d + j < dend;
-            wa[j] = (wp && in) ? wp[d + j] : 0.f;
-            xb[j] = (xp && in) ? xp[d + j] : 0.f;
+        for (int st = 0; st < kSteps; ++st) {
+            const int d = d0 + 16 * st + 4 * kg;
+            float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+            if (VEC) {
+                // d and dend are multiples of 4: the 4 values are all in or all out
+                if (d < dend) {
+                    if (wp) a = *reinterpret_cast<const float4 *>(wp + d);
+                    if (xp) b = *reinterpret_cast<const float4 *>(xp + d);
+                }
+            } else {
+                float av[4], bv[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const bool in = d + j < dend;
+                    av[j] = (wp && in) ? wp[d + j] : 0.f;
+                    bv[j] = (xp && in) ? xp[d + j] : 0.f;
+                }
+                a = make_float4(av[0], av[1], av[2], av[3]);
+                b = make_float4(bv[0], bv[1], bv[2], bv[3]);
+            }
+            wa[st] = a;
+            xb[st] = b;
         }
+    };
+    auto product = [&](const float4 (&wa)[kSteps], const float4 (&xb)[kSteps]) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)wa[j], (double)xb[j], acc, 0, 0, 0);
+        for (int st = 0; st < kSteps; ++st) {
+            acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)wa[st].x, (double)xb[st].x, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)wa[st].y, (double)xb[st].y, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)wa[st].z, (double)xb[st].z, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)wa[st].w, (double)xb[st].w, acc, 0, 0, 0);
+        }
+    };
+    float4 wa0[kSteps], xb0[kSteps], wa1[kSteps], xb1[kSteps];
+    load(dbeg, wa0, xb0);
+    for (int d0 = dbeg; d0 < dend; d0 += 32 * kSteps) {
+        load(d0 + 16 * kSteps, wa1, xb1);   // past dend: all zeros, no access
+        product(wa0, xb0);
+        if (d0 + 16 * kSteps >= dend) break;
+        load(d0 + 32 * kSteps, wa0, xb0);
+        product(wa1, xb1);
     }
     // D[i][j]: i = expert row 4*r + kg, j = token column `row`
     const int tt = t0 + row;
@@ -76,19 +114,10 @@ __global__ __launch_bounds__(256) void k_router_partial(const float *__restrict_
     }
 }
 
-// Sum the slices in slice order, then the sigmoid in fp64, rounded once.
-__global__ void k_router_sigmoid(const double *__restrict__ part, int splits, int S, int E,
-                                 float *__restrict__ sig)
-{
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t n = (int64_t)S * E;
-    if (i >= n) return;
-    double l = 0.0;
-    for (int k = 0; k < splits; ++k) l += part[(int64_t)k * n + i];
-    sig[i] = (float)(1.0 / (1.0 + exp(-l)));
-}
-
-// One wave per token: greedy top-K over choice = sig + bias.
+// One token per block.  First the block sums each score's slices in slice
+// order and takes the sigmoid in fp64, rounded once (scores go to `sig` and
+// to LDS).  Then the first wave runs the greedy top-K over
+// choice = sig + bias:
 //  - lane l owns experts e = l + 64 j (j < ceil(E/64) <= 16), so e rises
 //    with j; a lane's candidate is its first maximal untaken choice
 //    (strict '>' while j rises);
@@ -97,20 +126,46 @@ __global__ void k_router_sigmoid(const double *__restrict__ part, int splits, in
 //    pick, which equals the sequential scan's first maximum;
 //  - the pick's owner marks it taken; lane 0 then runs the pages' tail
 //    (top-p, normalisation, routed_scale) sequentially in fp32.
-__global__ __launch_bounds__(256) void k_router_topk(const float *__restrict__ sig,
+__global__ __launch_bounds__(256) void k_router_topk(const double *__restrict__ part, int splits,
                                                      const float *__restrict__ bias, int S,
                                                      int E, int K, int norm_topk,
                                                      float routed_scale, float topp,
+                                                     float *__restrict__ sig,
                                                      int32_t *__restrict__ idx,
                                                      float *__restrict__ w,
                                                      int32_t *__restrict__ keff)
 {
-    __shared__ int pick_s[4][64];
-    __shared__ float pw_s[4][64];
+    __shared__ int pick_s[64];
+    __shared__ float pw_s[64];
+    __shared__ float sig_s[kRouterMaxE];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int s = blockIdx.x * 4 + wave;
-    if (s >= S) return;   // whole wave leaves together; no block barrier below
-    const float *sg = sig + (int64_t)s * E;
+    const int s0 = blockIdx.x;
+    const int nt = 1;
+    {
+        const int64_t n = (int64_t)S * E;
+        for (int i = threadIdx.x; i < nt * E; i += 256) {
+            const int64_t g = (int64_t)s0 * E + i;
+            // the loads of up to 32 slices are issued before the first add
+            constexpr int kChunk = 32;
+            double l = 0.0;
+            for (int k0 = 0; k0 < splits; k0 += kChunk) {
+                double pv[kChunk];
+#pragma unroll
+                for (int k = 0; k < kChunk; ++k)
+                    pv[k] = k0 + k < splits ? part[(int64_t)(k0 + k) * n + g] : 0.0;
+#pragma unroll
+                for (int k = 0; k < kChunk; ++k)
+                    if (k0 + k < splits) l += pv[k];
+            }
+            const float sv = (float)(1.0 / (1.0 + exp(-l)));
+            sig[g] = sv;
+            sig_s[i] = sv;
+        }
+    }
+    __syncthreads();
+    const int s = s0;
+    if (wave != 0) return;   // whole waves leave; no block barrier below
+    const float *sg = sig_s;
     const int per = (E + 63) / 64;
     float ch[16], sv[16];
 #pragma unroll
@@ -124,8 +179,8 @@ __global__ __launch_bounds__(256) void k_router_topk(const float *__restrict__ s
 #pragma unroll
     for (int j = 0; j < 16; ++j)
         if (j < per && lane + 64 * j < E) live |= 1u << j;
-    int *pick = pick_s[wave];
-    float *pw = pw_s[wave];
+    int *pick = pick_s;
+    float *pw = pw_s;
     for (int kk = 0; kk < K; ++kk) {
         float bv = 0.f;
         int bi = 0x7FFFFFFF;
@@ -207,16 +262,16 @@ hipError_t router_launch(const float *Wr, const float *bias, const float *x, int
     int slice = 0;
     const int splits = coli__router_splits(S, E, D, &slice);
     dim3 grid((S + 15) / 16, (E + 63) / 64, splits);
-    hipLaunchKernelGGL(k_router_partial, grid, dim3(256), 0, st, Wr, x, S, E, D, slice, part);
+    const bool vec = D % 4 == 0 && ((uintptr_t)Wr & 15u) == 0 && ((uintptr_t)x & 15u) == 0;
+    if (vec)
+        hipLaunchKernelGGL(k_router_partial<true>, grid, dim3(256), 0, st, Wr, x, S, E, D, slice, part);
+    else
+        hipLaunchKernelGGL(k_router_partial<false>, grid, dim3(256), 0, st, Wr, x, S, E, D, slice, part);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const int64_t n = (int64_t)S * E;
-    hipLaunchKernelGGL(k_router_sigmoid, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                       part, splits, S, E, sig);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(k_router_topk, dim3((S + 3) / 4), dim3(256), 0, st, sig, bias, S, E, K,
-                       norm_topk, routed_scale, topp, idx, w, keff);
+    if (E > kRouterMaxE) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_router_topk, dim3(S), dim3(256), 0, st, part, splits, bias, S,
+                       E, K, norm_topk, routed_scale, topp, sig, idx, w, keff);
     return hipGetLastError();
 }
 

@@ -6,7 +6,8 @@
 
 namespace coli {
 
-enum Stage { kStRouter = 0, kStGroup = 1, kStGateUp = 2, kStDown = 3, kStCombine = 4, kStQgemv = 5 };
+enum Stage { kStRouter = 0, kStGroup = 1, kStGateUp = 2, kStDown = 3, kStCombine = 4, kStQgemv = 5,
+             kStPrep = 6 };
 
 // Records a start event on construction and an end event on destruction
 // when stage timing is enabled; does nothing otherwise.

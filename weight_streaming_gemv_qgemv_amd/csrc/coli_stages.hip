@@ -1,8 +1,8 @@
 // coli_stages.hip -- optional per-stage GPU timing of the MoE calls.
 //
 // Off by default.  When enabled, each MoE call records a hipEvent on its
-// stream before and after every stage (router, grouping, gate/up, down,
-// combine, qgemv); coli_stage_times() waits for the recorded events and adds
+// stream before and after every stage (router, grouping, matrix-core
+// preparation, gate/up, down, combine, qgemv); coli_stage_times() waits for the recorded events and adds
 // up the elapsed times.  This is the only state the library keeps between
 // calls, and it exists for measurement: the pages time the same phases of
 // their MoE block (expert-matmul, setup, kernel and scatter time).
@@ -42,7 +42,7 @@ hipEvent_t take_event()
     return e;
 }
 
-const char *const kNames[COLI_NSTAGES] = {"router", "group", "gate_up", "down", "combine", "qgemv"};
+const char *const kNames[COLI_NSTAGES] = {"router", "group", "gate_up", "down", "combine", "qgemv", "prep"};
 
 }  // namespace
 
@@ -52,14 +52,14 @@ StageTimer::StageTimer(int stage, hipStream_t st) : stage_(stage), st_(st)
     if (!g_on) return;
     a_ = take_event();
     b_ = take_event();
-    if (a_ && b_) hipEventRecord((hipEvent_t)a_, st_);
+    if (a_ && b_) (void)hipEventRecord((hipEvent_t)a_, st_);
 }
 
 StageTimer::~StageTimer()
 {
     std::lock_guard<std::mutex> g(g_mu);
     if (!a_ || !b_) return;
-    hipEventRecord((hipEvent_t)b_, st_);
+    (void)hipEventRecord((hipEvent_t)b_, st_);
     g_pending.push_back(Rec{stage_, (hipEvent_t)a_, (hipEvent_t)b_});
 }
 

@@ -158,24 +158,26 @@ int coli_moe_workspace_layout(int S, int K, int E, int D, int F, int F_shared,
     if (!mul_ok(rows, D, &t) || !mul_ok(t, 4, &t)) return COLI_ESHAPE;
     REGION(y, t);
     REGION(router_part, coli__router_partial_bytes(S, E, D));
-    /* matrix-core path: per (expert, 8-token pass) the activations as bf16
-     * hi/lo fragments (16 columns x input width rounded up to 512), their
-     * sums, the SwiGLU output prepared the same way, and the work list */
-    int64_t ngp = (rows + 15) / 16 + (int64_t)E + 1;   /* passes of 16 rows */
-    int64_t KpD = round_up(D, 512), KpF = round_up(Fmax, 512), tilesF = KpF / 128;
-    if (!mul_ok(ngp, 64 * KpD, &t)) return COLI_ESHAPE;
+    /* matrix-core path: per (expert, COLI_MM_TPP-row pass) the activations as
+     * bf16 hi/lo fragments (2 COLI_MM_TPP columns x input width rounded up to
+     * 1024), their sums, the SwiGLU output prepared the same way, its partial
+     * sums per 128-row tile, and the work list */
+    const int64_t tpp = COLI_MM_TPP;
+    int64_t ngp = (rows + tpp - 1) / tpp + (int64_t)E + 1;   /* passes */
+    int64_t KpD = round_up(D, 1024), KpF = round_up(Fmax, 1024), tilesF = KpF / 128;
+    if (!mul_ok(ngp, 4 * tpp * KpD, &t)) return COLI_ESHAPE;
     REGION(xf, t);
-    REGION(xsum, ngp * 16 * 4);
-    if (!mul_ok(ngp, 64 * KpF, &t)) return COLI_ESHAPE;
+    REGION(xsum, ngp * tpp * 4);
+    if (!mul_ok(ngp, 4 * tpp * KpF, &t)) return COLI_ESHAPE;
     REGION(hf, t);
-    if (!mul_ok(tilesF * ngp, 16 * 4, &t)) return COLI_ESHAPE;
+    if (!mul_ok(tilesF * ngp, tpp * 4, &t)) return COLI_ESHAPE;
     REGION(hsum, t);
     REGION(work, (ngp + 1) * 4);
     REGION(n_work, 64);
 #undef REGION
     out->n_pass_max = ngp;
-    out->xf_stride = 32 * KpD;
-    out->hf_stride = 32 * KpF;
+    out->xf_stride = 2 * tpp * KpD;
+    out->hf_stride = 2 * tpp * KpF;
     out->h_ld = Fmax;
     out->total = off;
     return COLI_OK;
