@@ -66,6 +66,26 @@ def clone_bank(bd):
     return out
 
 
+def recorded_traffic(workload, kernel_key):
+    """HBM bytes per launch of one kernel from the committed rocprofv3
+    counter summary (FETCH_SIZE + WRITE_SIZE, calibrated against a plain
+    copy), or None when there is none for this workload or the kernel source
+    has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                        "moe_layer_decode64_traffic.md")
+    try:
+        line = next(l for l in open(path) if l.startswith("traffic-json: "))
+        rec = json.loads(line[len("traffic-json: "):])
+        src = open(os.path.join(os.path.dirname(os.path.abspath(__file__)), rec["source"]), "rb").read()
+    except (OSError, StopIteration, ValueError, KeyError):
+        return None
+    if rec.get("workload") != workload or hashlib.sha256(src).hexdigest() != rec.get("sha256"):
+        return None
+    k = rec.get("per_launch", {}).get(kernel_key)
+    return None if k is None else int(k["fetch_bytes"] + k["write_bytes"])
+
+
 def time_steps(step, steps, warmup):
     """Warm up, then time exactly `steps` steps between two synchronisations
     (stage events off).  A second pass of `steps` steps records a HIP event
@@ -153,7 +173,8 @@ def run_layer64(args, dev):
                tokens=S, stages=stages, uniq=uniq,
                dominant=dict(kernel="k_mm<I4,2> (grouped expert gate/up + SwiGLU, matrix cores)",
                              bytes_per_launch=gu_bytes, ms_per_launch=gu_ms / max(gu_n, 1),
-                             launches=gu_n))
+                             launches=gu_n,
+                             traffic=recorded_traffic("moe_layer_decode_64", "k_mm<2, 2>")))
     if not args.no_cpu_baseline:
         ntok = args.cpu_tokens
         log(f"cpu baseline: oracle on {ntok} tokens")
@@ -306,7 +327,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(ach, 2) if ach else None,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(ach / HBM_PEAK_GBS, 4) if ach else None,
-                     "traffic": None, "kernel": dom["kernel"],
+                     "traffic": dom.get("traffic"), "kernel": dom["kernel"],
                      "algorithmic_bytes_per_launch": dom["bytes_per_launch"],
                      "ms_per_launch": round(dom["ms_per_launch"], 5)},
         "context": {"pages_metal_moe_gemv_GBps": "358-389 (Apple-Silicon GPU, unified memory)"},

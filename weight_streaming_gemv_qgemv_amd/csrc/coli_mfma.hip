@@ -611,29 +611,25 @@ __global__ __launch_bounds__(256) void k_mm(MmArgs a)
     else nxt = cur;
 
     uint4 w0[M][2][SEGS], w1[M][2][SEGS], w2[M][2][SEGS];
-    uint4 b0[UMAX], b1[UMAX], b2[UMAX];
+    uint4 breg[UMAX];
     int k = 0, buf = 0;
-    // prologue, as the steady state would have issued it: B(0), B(1), W(0),
-    // B(2), W(1); then B(0) goes to LDS
-    loadB(cur, 0, b0);
-    loadB(cur, 1, b1);
+    // prologue: W(0), W(1), B(0) -> LDS
     loadW(cur, 0, w0);
-    loadB(cur, 2, b2);
     loadW(cur, 1, w1);
-    stage(cur, 0, b0);
+    loadB(cur, 0, breg);
+    stage(cur, 0, breg);
     __syncthreads();
 
     // one k-block step s = (cur, k): returns true after the block's last item
-    //   wc = W(s), wl <- W(s+2); bst = B(s+1) (to LDS), bld <- B(s+3)
-    auto step = [&](uint4 (&wc)[M][2][SEGS], uint4 (&wl)[M][2][SEGS], const uint4 (&bst)[UMAX],
-                    uint4 (&bld)[UMAX]) -> bool {
+    //   wc = W(s), wl <- W(s+2); B(s+1) loaded and staged to LDS
+    auto step = [&](uint4 (&wc)[M][2][SEGS], uint4 (&wl)[M][2][SEGS]) -> bool {
         if (k == nkb - 2) load_epi(cur);
         // the sources are selected, not branched on: the same loads are
         // issued on every path, so the waits count them exactly
+        It bsrc = cur;
+        if (k + 1 >= nkb) bsrc = nxt;
+        loadB(bsrc, k + 1 < nkb ? k + 1 : 0, breg);
         It src = cur;
-        if (k + 3 >= nkb) src = nxt;
-        loadB(src, k + 3 < nkb ? k + 3 : k + 3 - nkb, bld);
-        src = cur;
         if (k + 2 >= nkb) src = nxt;
         loadW(src, k + 2 < nkb ? k + 2 : k + 2 - nkb, wl);
         __builtin_amdgcn_sched_barrier(0);
@@ -643,9 +639,7 @@ __global__ __launch_bounds__(256) void k_mm(MmArgs a)
         const int nb = buf == 2 ? 0 : buf + 1;
         // every wave finished reading buffer nb (two steps ago) before the
         // barrier at the end of the previous step
-        src = cur;
-        if (k + 1 >= nkb) src = nxt;
-        stage(src, nb, bst);
+        stage(bsrc, nb, breg);
         __syncthreads();
         buf = nb;
         if (k != nkb - 1) {
@@ -663,9 +657,9 @@ __global__ __launch_bounds__(256) void k_mm(MmArgs a)
         return false;
     };
     for (;;) {
-        if (step(w0, w2, b1, b0)) break;
-        if (step(w1, w0, b2, b1)) break;
-        if (step(w2, w1, b0, b2)) break;
+        if (step(w0, w2)) break;
+        if (step(w1, w0)) break;
+        if (step(w2, w1)) break;
     }
 }
 
