@@ -10,7 +10,8 @@ combine.  Two copies of the expert bank live in HBM and steps alternate
 between them, so no step finds its weights in the 256 MB last-level cache.
 
 Other workloads: "decode16" (coli_moe_gemv, 16 tokens, given top-8 routing),
-"qgemv" (int4 12288 x 6144, S = 1, over a rotation of weight copies), "copy"
+"qgemv" (int4 12288 x 6144, S = 1, over a rotation of weight copies),
+"prefill2048" (2048 tokens, Zipf routing, bf16 matrix cores, router timed), "copy"
 (a plain 1 GiB device copy, the yardstick for the HBM byte counters).
 
 Prints ONE JSON line.  `value` is the step's algorithmic bytes (weights of
@@ -32,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 matrix peak
 METRIC = "int4 expert-GEMV HBM GB/s (% of peak) + MoE-layer decode tokens/s"
 
 
@@ -190,6 +192,48 @@ def run_layer64(args, dev):
     return res
 
 
+def run_prefill2048(args, dev):
+    """2048 tokens through the layer in bf16 precision: the router runs and
+    is timed (coli_router), the experts take a fixed Zipf(1.1)-skewed
+    routing through pre_idx / pre_w."""
+    import torch
+    from weight_streaming_gemv_qgemv_amd import binding as b
+    from weight_streaming_gemv_qgemv_amd import synth
+    S, K, E, D, F, fmt = 2048, 8, 256, 6144, 2048, 2
+    log("generating 256 int4 experts + shared expert (host)")
+    bank = synth.expert_bank(4000, fmt, E, D, F)
+    shared = synth.shared_mlp(4000, fmt, D, F)
+    g = synth.rng(4500)
+    Wr, bias = synth.router_weights(g, E, D)
+    x = synth.activations(g, S, D)
+    idx, w = synth.routing_zipf(g, S, K, E)
+    bd, sd = bank_to_dev(bank, dev), bank_to_dev(shared, dev)
+    xd, idd, wd = to_dev(x, dev), to_dev(idx, dev), to_dev(w, dev)
+    Wrd, bd_bias = to_dev(Wr, dev), to_dev(bias, dev)
+    out = torch.empty((S, D), dtype=torch.float32, device=dev)
+    rws = b.alloc_workspace(b.router_workspace_bytes(S, E, D), dev)
+    ws = b.alloc_workspace(b.moe_workspace_bytes(S, K, E, D, F, F, 1), dev)
+
+    def step(i):
+        b.router(Wrd, bd_bias, xd, K, 1, 2.5, 0.0, ws=rws)
+        b.moe_layer(None, bd, sd, xd, pre_idx=idd, pre_w=wd, out=out, prec=1, ws=ws)
+
+    uniq = int(np.unique(idx).size)
+    gu, dn = expert_bytes(fmt, D, F)
+    step_bytes = (E * D * 4 + E * 4) + S * D * 4 + uniq * (gu + dn) + (gu + dn) + S * D * 4 + S * K * 8
+    rows = S * K + S
+    flops = 2 * rows * 3 * D * F            # gate, up, down on every routed and shared row
+    ms, wall, stages = time_steps(step, args.steps, args.warmup)
+    gu_ms, gu_n = stages["gate_up"]
+    gu_flops = 2 * rows * 2 * D * F
+    return dict(workload="moe_layer_prefill_2048_bf16", ms=ms, wall=wall, step_bytes=step_bytes,
+                tokens=S, stages=stages, uniq=uniq, flops=flops,
+                dominant=dict(kernel="k_mm<I4,2> (grouped expert gate/up + SwiGLU, bf16 matrix cores)",
+                              bytes_per_launch=(uniq + 1) * gu + S * D * 4 + rows * F * 4,
+                              flops_per_launch=gu_flops, ms_per_launch=gu_ms / max(gu_n, 1),
+                              launches=gu_n))
+
+
 def run_decode16(args, dev):
     import torch
     from weight_streaming_gemv_qgemv_amd import binding as b
@@ -278,7 +322,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="layer64", choices=["layer64", "decode16", "qgemv", "copy"])
+    ap.add_argument("--workload", default="layer64",
+                    choices=["layer64", "decode16", "qgemv", "prefill2048", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=64)
     args = ap.parse_args()
@@ -296,7 +341,7 @@ def main():
     if args.workload == "copy":
         run_copy(args, dev)
         return
-    run = {"layer64": run_layer64, "decode16": run_decode16, "qgemv": run_qgemv}[args.workload]
+    run = {"prefill2048": run_prefill2048, "layer64": run_layer64, "decode16": run_decode16, "qgemv": run_qgemv}[args.workload]
     r = run(args, dev)
     ms = r["ms"]
     gbs = r["step_bytes"] / (ms * 1e-3) / 1e9
@@ -332,6 +377,16 @@ def main():
                      "ms_per_launch": round(dom["ms_per_launch"], 5)},
         "context": {"pages_metal_moe_gemv_GBps": "358-389 (Apple-Silicon GPU, unified memory)"},
     }
+    if "flops" in r:
+        # prefill: the matrix cores bound the dominant kernel
+        tf = dom["flops_per_launch"] / (dom["ms_per_launch"] * 1e-3) / 1e12 if dom["ms_per_launch"] else None
+        line["dtype"] = "bf16 (int4 weights, fp32 accumulate)"
+        line["roofline"] = {"bound": "mfma", "achieved": round(tf, 2) if tf else None,
+                            "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                            "frac": round(tf / BF16_PEAK_TFLOPS, 4) if tf else None, "traffic": None,
+                            "kernel": dom["kernel"], "flops_per_launch": dom["flops_per_launch"],
+                            "ms_per_launch": round(dom["ms_per_launch"], 5)}
+        line["layer_mfma_utilisation"] = round(r["flops"] / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
     if "cpu" in r:
         c = r["cpu"]
         line["cpu_baseline"] = {"value": round(c["value"], 4), "unit": c["unit"], "cores": c["cores"],

@@ -62,10 +62,13 @@ enum coli_status {
 /* Precision of the MoE expert products.
  *   COLI_PREC_FP32: fp32 activations, fp32 accumulation; every float output
  *     meets |y - y_ref| <= 1e-4 * (scale * sum |v * x|) + 1e-6.
- *   COLI_PREC_BF16: activations rounded to bf16 and int weights converted
- *     exactly to bf16 for the matrix cores, fp32 accumulation, scale applied
- *     in fp32 after the sum; bound 2e-2 of the same magnitude.  Meant for
- *     prefill-sized batches. */
+ *     (The matrix cores take x as bf16 hi + lo, 8 rows per pass.)
+ *   COLI_PREC_BF16: activations -- x, and h for the down product -- rounded
+ *     once to bf16, int weights converted exactly to bf16 for the matrix
+ *     cores, fp32 accumulation, scale applied in fp32 after the sum, 16 rows
+ *     per pass; bound 2e-2 of the same magnitude.  Meant for prefill-sized
+ *     batches.  Shapes that take the vector-ALU kernels (rows that are not
+ *     whole 16-byte segments) compute in fp32 under either value. */
 enum coli_prec { COLI_PREC_FP32 = 0, COLI_PREC_BF16 = 1 };
 
 /* Bytes in one packed row of I elements, or -1 for an unknown fmt / I < 0

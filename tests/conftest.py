@@ -18,3 +18,13 @@ def orc():
     from oracle import oracle
     oracle.lib()
     return oracle
+
+
+@pytest.fixture(scope="session")
+def glm_bank():
+    """256 experts of width 6144 x 2048, int4 (4.8 GB host), plus the shared
+    expert: the decode, layer and prefill workloads' expert bank."""
+    from weight_streaming_gemv_qgemv_amd import synth
+    bank = synth.expert_bank(3000, 2, 256, 6144, 2048)
+    shared = synth.shared_mlp(3000, 2, 6144, 2048)
+    return bank, shared

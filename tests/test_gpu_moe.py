@@ -213,15 +213,8 @@ def test_moe_layer_empty_batch(dev):
 
 
 # ---------------------------------------------------------------- full size
-@pytest.fixture(scope="module")
-def glm_bank():
-    """256 experts of width 6144 x 2048, int4 (4.8 GB host), plus the shared
-    expert."""
-    bank = synth.expert_bank(3000, 2, 256, 6144, 2048)
-    shared = synth.shared_mlp(3000, 2, 6144, 2048)
-    return bank, shared
-
-
+# (the glm_bank fixture -- 256 int4 experts of 6144 x 2048 plus the shared
+# expert -- lives in conftest.py, shared with the prefill tests)
 def test_expert_decode_16_tokens(dev, orc, glm_bank):
     """256 int4 experts, 16 tokens, given top-8 routing: full oracle check."""
     from weight_streaming_gemv_qgemv_amd import binding as b

@@ -267,7 +267,7 @@ int run_shared_valu(const coli_mlp *sh, const float *x, int S, int D, float *h, 
 
 // Grouped expert products: routed experts (+ shared) -> h -> y -> out.
 int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int S, int K,
-                const int32_t *idx, const float *w, float *out, uint8_t *ws,
+                const int32_t *idx, const float *w, float *out, int prec, uint8_t *ws,
                 const coli_ws_layout &L, hipStream_t st)
 {
     const int E = ex->E, D = ex->D, F = ex->F;
@@ -289,6 +289,10 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
                     al16(ex->w_down) && (ex->fmt == COLI_I8 || ex->fmt == COLI_I4 || ex->fmt == COLI_I2);
     const bool sh_mm = mm && sh && sh->fmt == ex->fmt && sh->F == F && al16(sh->w_gate) &&
                        al16(sh->w_up) && al16(sh->w_down);
+    // matrix-core passes: 8 rows as bf16 hi/lo column pairs (fp32-level
+    // accuracy) or 16 rows rounded once to bf16
+    const int bf16 = prec == COLI_PREC_BF16 ? 1 : 0;
+    const int tpp = bf16 ? 2 * COLI_MM_TPP : COLI_MM_TPP;
     int32_t *work = reinterpret_cast<int32_t *>(ws + L.work);
     int32_t *n_work = reinterpret_cast<int32_t *>(ws + L.n_work);
     {
@@ -298,7 +302,7 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
     err = hipGetLastError();
     if (err != hipSuccess) return COLI_EDEVICE;
     hipLaunchKernelGGL(k_group_scatter, dim3(gblocks), dim3(1024), 0, st, idx, P, E, counts,
-                       offsets, row_pair, pair_row, sh_mm ? S : 0, mm_tokens_per_pass(),
+                       offsets, row_pair, pair_row, sh_mm ? S : 0, tpp,
                        mm ? work : nullptr, n_work);
     err = hipGetLastError();
     if (err != hipSuccess) return COLI_EDEVICE;
@@ -313,6 +317,8 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
         const int64_t kpD = mm_kpad(D), kpF = mm_kpad(F);
         {
             MmArgs a = {};
+            a.tpp = tpp;
+            a.bf16 = bf16;
             a.w[0] = (const uint8_t *)ex->w_gate;
             a.w[1] = (const uint8_t *)ex->w_up;
             a.s[0] = ex->s_gate;
@@ -350,7 +356,7 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
             a.hf_rows = (int)kpF;
             a.hf_fmt = ex->fmt;
             a.hsum = hsum;
-            a.hsum_stride = max_gp * mm_tokens_per_pass();
+            a.hsum_stride = max_gp * mm_pass_slots();
             {
                 StageTimer tp(kStPrep, st);
                 if (xprep_launch(ex->fmt, a, x, D, max_gp, st) != hipSuccess) return COLI_EDEVICE;
@@ -361,6 +367,8 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
         {
             StageTimer tdn(kStDown, st);
             MmArgs d = {};
+            d.tpp = tpp;
+            d.bf16 = bf16;
             d.w[0] = (const uint8_t *)ex->w_down;
             d.s[0] = ex->s_down;
             d.w_gstride = (int64_t)D * rbF;
@@ -386,7 +394,7 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
             d.xf_stride = L.hf_stride;
             // the activations' sums: the gate/up tiles' partial sums, added up
             // (into xsum, free once gate/up has run)
-            if (sum_parts_launch(hsum, (int)(kpF / mm_rows_per_block()), max_gp * mm_tokens_per_pass(), max_gp, xsum,
+            if (sum_parts_launch(hsum, (int)(kpF / mm_rows_per_block()), max_gp * mm_pass_slots(), max_gp, xsum,
                                  st) != hipSuccess)
                 return COLI_EDEVICE;
             d.xsum = xsum;
@@ -575,7 +583,7 @@ extern "C" int coli_moe_gemv(const coli_experts *ex, const float *x, int S, int 
     coli_ws_layout L;
     rc = coli_moe_workspace_layout(S, K, ex->E, ex->D, ex->F, 0, prec, &L);
     if (rc != COLI_OK) return rc;
-    return run_experts(ex, nullptr, x, S, K, idx, w, out, (uint8_t *)ws, L, (hipStream_t)stream);
+    return run_experts(ex, nullptr, x, S, K, idx, w, out, prec, (uint8_t *)ws, L, (hipStream_t)stream);
 }
 
 extern "C" int coli_moe_layer(const coli_router_params *r, const coli_experts *ex,
@@ -624,7 +632,7 @@ extern "C" int coli_moe_layer(const coli_router_params *r, const coli_experts *e
         if (w_out && hipMemcpyAsync(w_out, pre_w, n * 4, hipMemcpyDeviceToDevice, st) != hipSuccess)
             return COLI_EDEVICE;
     }
-    return run_experts(ex, shared, x, S, K, idx, w, out, wsb, L, st);
+    return run_experts(ex, shared, x, S, K, idx, w, out, prec, wsb, L, st);
 }
 
 extern "C" int coli_check_device_flags(const void *ws, void *stream, uint32_t *flags_out)

@@ -7,11 +7,12 @@
 
 namespace coli {
 
-// Groups as in GemvArgs (coli_gemv.h).  Work is a list of (group, 16-token
-// pass) entries; every pass has its activations prepared fragment-major in
-// xf (xf_stride elements per pass, kpad = input width rounded up to 512) and
-// the sum of their bf16 hi + lo parts per token in xsum (the sum of
-// xsum_parts arrays of xsum_stride floats, indexed pass * 16 + token).
+// Groups as in GemvArgs (coli_gemv.h).  Work is a list of (group, pass)
+// entries, a pass being up to `tpp` rows of one group: 8 in fp32 precision
+// (bf16 hi/lo column pairs), 16 in bf16 precision (one column each).  Every
+// pass has its activations prepared fragment-major in xf (xf_stride elements
+// per pass, kpad = input width rounded up to 1024) and the sum of the stored
+// values per token in xsum (indexed pass * 16 + token).
 struct MmArgs {
     const uint8_t *w[2];
     const float *s[2];
@@ -28,6 +29,8 @@ struct MmArgs {
     uint16_t *xf;
     int64_t xf_stride;
     float *xsum;         // [group-pass * 16 + token] sum(hi + lo) of the activations
+    int tpp;             // rows per pass: 8 (fp32, hi/lo) or 16 (bf16)
+    int bf16;            // activations rounded once to bf16 (no lo part)
     const int *work;     // (g | pass << 11) per group-pass, NULL = one group
     const int *n_work;
     float *out;
@@ -43,7 +46,8 @@ struct MmArgs {
 };
 
 int mm_rows_per_block();
-int mm_tokens_per_pass();
+// Token slots per pass (the stride of xsum/hsum per group-pass).
+int mm_pass_slots();
 int64_t mm_kpad(int64_t I);
 // One block per possible group-pass (blocks past the device count exit).
 hipError_t xprep_launch(int fmt, const MmArgs &a, const float *x, int64_t ldx,

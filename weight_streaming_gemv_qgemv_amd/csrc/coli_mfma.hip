@@ -134,18 +134,18 @@ __device__ __forceinline__ floatx4 mfma(const uint4 &a, const uint4 &b, floatx4 
 }
 
 // ---------------------------------------------------------------- layout
-// Work is cut into passes of up to kTPP activation rows ("tokens") of one
-// group.  A pass's activations are stored "fragment-major": for k-block
-// kbi, MFMA step s and lane group q, chunk c = (kbi*STEPS + s)*4 + q holds,
-// for each of the kCols = 2 kTPP columns (token t: column 2t = hi, 2t+1 =
-// lo; N-tile n = columns 16n..16n+15), the 8 bf16 values of the slots that
-// lane (col, q) feeds to that step.  A k-block's activations are one contiguous
+// Work is cut into passes of activation rows ("tokens") of one group, one
+// MFMA tile of kCols = 16 columns each.  fp32 precision: up to 8 tokens,
+// token t in columns 2t (bf16 hi) and 2t+1 (bf16 lo).  bf16 precision: up to
+// 16 tokens, token t in column t (x rounded once).  A pass's activations are
+// stored "fragment-major": for k-block kbi, MFMA step s and lane group q,
+// chunk c = (kbi*STEPS + s)*4 + q holds, for each column, the 8 bf16 values
+// of the slots that lane (col, q) feeds to that step.  A k-block's activations are one contiguous
 // STEPS*2 KB run, and the live tokens' columns are a prefix of every chunk.
 // Element e of the product's input sits in chunk c, slot j = pos_of(e).
-constexpr int kTPP = COLI_MM_TPP;
-constexpr int kCols = 2 * kTPP;
-constexpr int kNT = kCols / 16;   // MFMA N-tiles per pass
-static_assert(kCols % 16 == 0 && kNT >= 1 && kNT <= 2, "a pass is one or two N-tiles");
+constexpr int kCols = 16;             // MFMA columns per pass (one N-tile)
+constexpr int kMaxTok = kCols;        // tokens per pass at most (bf16)
+static_assert(2 * COLI_MM_TPP == kCols, "fp32 passes hold COLI_MM_TPP tokens as hi/lo column pairs");
 
 template <int FMT> __device__ __forceinline__ int elem_of(int kbi, int s, int q, int j)
 {
@@ -222,14 +222,14 @@ __device__ __forceinline__ GP decode_gp(const MmArgs &a, int gp)
         d.r0 = 0;
         d.cnt = a.x_rows;
     }
-    d.t0 = d.pass * kTPP;
-    d.nt = min(kTPP, d.cnt - d.t0);
+    d.t0 = d.pass * a.tpp;
+    d.nt = min(a.tpp, d.cnt - d.t0);
     return d;
 }
 
 __device__ __forceinline__ int n_group_passes(const MmArgs &a)
 {
-    return a.work ? cload(a.n_work) : (a.x_rows + kTPP - 1) / kTPP;
+    return a.work ? cload(a.n_work) : (a.x_rows + a.tpp - 1) / a.tpp;
 }
 
 // ---------------------------------------------------------------- x prep
@@ -239,7 +239,8 @@ __device__ __forceinline__ int n_group_passes(const MmArgs &a)
 // the run as the 16-byte units of the chunk(s) it feeds.  A run of 8 (int8,
 // int4) is exactly one chunk; a run of 16 (int2) is the two chunks of an
 // even/odd step pair.  Only live columns are written: the product kernel
-// reads nothing else.  Also sum(hi + lo) per token, in a fixed order.
+// reads nothing else.  Also the sum of the stored values (hi + lo, or hi
+// alone in bf16 precision) per token, in a fixed order.
 constexpr int kPrepThreads = 256;
 constexpr int kPrepRuns = 4;   // runs per thread per round
 template <int FMT>
@@ -290,7 +291,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_xprep(MmArgs a, const float *_
             for (int i = 0; i < RUN; ++i) {
                 hv[i] = bf16_rne(v[k][i]);
                 lv[i] = bf16_rne(v[k][i] - bf16_f(hv[i]));
-                sum += bf16_f(hv[i]) + bf16_f(lv[i]);
+                sum += a.bf16 ? bf16_f(hv[i]) : bf16_f(hv[i]) + bf16_f(lv[i]);
             }
             // slot pairs (2m, 2m+1) of each chunk, as the unpacking orders them
             int c, j;
@@ -311,9 +312,10 @@ __global__ __launch_bounds__(kPrepThreads) void k_xprep(MmArgs a, const float *_
             }
 #pragma unroll
             for (int h = 0; h < RUN / 8; ++h) {
-                uint16_t *u = dst + ((int64_t)(c + 4 * h) * kCols + 2 * t) * 8;
+                uint16_t *u = dst + ((int64_t)(c + 4 * h) * kCols + (a.bf16 ? t : 2 * t)) * 8;
                 *reinterpret_cast<uint4 *>(u) = make_uint4(hw[4 * h], hw[4 * h + 1], hw[4 * h + 2], hw[4 * h + 3]);
-                *reinterpret_cast<uint4 *>(u + 8) = make_uint4(lw[4 * h], lw[4 * h + 1], lw[4 * h + 2], lw[4 * h + 3]);
+                if (!a.bf16)
+                    *reinterpret_cast<uint4 *>(u + 8) = make_uint4(lw[4 * h], lw[4 * h + 1], lw[4 * h + 2], lw[4 * h + 3]);
             }
         }
     }
@@ -324,7 +326,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_xprep(MmArgs a, const float *_
     if (tid == 0) {
         float tot = 0.f;
         for (int w = 0; w < kPrepThreads / kWave; ++w) tot += red[w];
-        a.xsum[(int64_t)gp * kTPP + t] = tot;
+        a.xsum[(int64_t)gp * kMaxTok + t] = tot;
     }
 }
 
@@ -332,11 +334,10 @@ __global__ __launch_bounds__(kPrepThreads) void k_xprep(MmArgs a, const float *_
 // One MFMA k-block step of a wave: weights (row-contiguous registers) moved
 // into the operand layout in place with ds_bpermute -- lane (q, col) gets
 // row col, chunk q, from lane 4 col + q -- then STEPS x M x 2 x NTL products
-// against the activations staged in LDS (bs).  NTL = live N-tiles of 16
-// columns (8 tokens each).
-template <int FMT, int M, int NTL>
+// against the activations staged in LDS (bs): one N-tile of 16 columns.
+template <int FMT, int M>
 __device__ __forceinline__ void mm_step(uint4 (&wl)[M][2][MF<FMT>::SEGS], const uint4 *bs,
-                                        int src4, int q, int col, floatx4 (&acc)[M][2][kNT])
+                                        int src4, int q, int col, floatx4 (&acc)[M][2])
 {
     using T = MF<FMT>;
     constexpr int SEGS = T::SEGS, SPS = T::SPS, STEPS = T::STEPS;
@@ -354,17 +355,12 @@ __device__ __forceinline__ void mm_step(uint4 (&wl)[M][2][MF<FMT>::SEGS], const 
             }
 #pragma unroll
     for (int s2 = 0; s2 < STEPS; ++s2) {
-        uint4 xb[NTL];
-#pragma unroll
-        for (int n = 0; n < NTL; ++n) xb[n] = bs[(s2 * 4 + q) * kCols + 16 * n + col];
+        const uint4 xb = bs[(s2 * 4 + q) * kCols + col];
 #pragma unroll
         for (int m = 0; m < M; ++m)
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                const uint4 cw = codes<FMT>(wl[m][mt][s2 / SPS], s2 % SPS);
-#pragma unroll
-                for (int n = 0; n < NTL; ++n) acc[m][mt][n] = mfma(cw, xb[n], acc[m][mt][n]);
-            }
+            for (int mt = 0; mt < 2; ++mt)
+                acc[m][mt] = mfma(codes<FMT>(wl[m][mt][s2 / SPS], s2 % SPS), xb, acc[m][mt]);
     }
 }
 
@@ -406,7 +402,7 @@ __global__ __launch_bounds__(256) void k_mm(MmArgs a)
     constexpr int CH = STEPS * 4;                 // activation chunks per k-block
     constexpr int UMAX = (CH * kCols + 255) / 256;
     constexpr float OFF = T::OFF;
-    __shared__ float red[4][kTPP];
+    __shared__ float red[4][kMaxTok];
     __shared__ uint4 bsh[3][CH * kCols];
     __shared__ uint4 btrash[256];   // dead staging lanes write here: every load and store is unconditional
 
@@ -456,8 +452,8 @@ __global__ __launch_bounds__(256) void k_mm(MmArgs a)
         for (int mt = 0; mt < 2; ++mt)
             c.roff[mt] = (uint32_t)(min(obase + 16 * mt + lrow, c.Og - 1) * a.rb) + 16 * lchunk;
         c.bglob = reinterpret_cast<const uint4 *>(a.xf + (int64_t)c.gp * a.xf_stride);
-        // live activation units of a k-block: CH chunks x 2 nt columns
-        const int lc = 2 * d.nt, live = CH * lc;
+        // live activation units of a k-block: CH chunks x (2 nt or nt) columns
+        const int lc = a.bf16 ? d.nt : 2 * d.nt, live = CH * lc;
 #pragma unroll
         for (int i = 0; i < UMAX; ++i) {
             const int u = tid + 256 * i;
@@ -495,7 +491,9 @@ __global__ __launch_bounds__(256) void k_mm(MmArgs a)
     // epilogue inputs: the scales of the lane's 4 rows per (matrix, row tile)
     // and the sums of its tokens (clamped indexes, unconditional loads; rows
     // and tokens out of range are never written)
-    float sreg[M][2][4], xsr[kNT];
+    // this lane's token: column col (bf16) or col / 2 (hi/lo pairs)
+    const int ltok = a.bf16 ? col : (col >> 1);
+    float sreg[M][2][4], xsr;
     auto load_epi = [&](const It &c) {
         const int obase = c.tile * kRowsPerBlock + wave * kRowsPerWave;
 #pragma unroll
@@ -505,70 +503,68 @@ __global__ __launch_bounds__(256) void k_mm(MmArgs a)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     sreg[m][mt][r] = gloadf(c.sc[m] + min(obase + 16 * mt + 4 * q + r, c.Og - 1));
-#pragma unroll
-        for (int n = 0; n < kNT; ++n)
-            xsr[n] = gloadf(a.xsum + (int64_t)c.gp * kTPP + min(8 * n + (col >> 1), c.nt - 1));
+        xsr = gloadf(a.xsum + (int64_t)c.gp * kMaxTok + min(ltok, c.nt - 1));
     };
 
-    floatx4 acc[M][2][kNT];
+    floatx4 acc[M][2];
 #pragma unroll
     for (int m = 0; m < M; ++m)
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int n = 0; n < kNT; ++n) acc[m][mt][n] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int mt = 0; mt < 2; ++mt) acc[m][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    // ---- epilogue: D[4q + r][16n + col]; add the lo column to the hi column
+    // ---- epilogue: D[4q + r][col]; in hi/lo precision the lo column is
+    // added to the hi column
     auto epilogue = [&](const It &c) {
         const int obase = c.tile * kRowsPerBlock + wave * kRowsPerWave;
-        float hpart[kNT] = {};   // per N-tile: this lane's hi + lo outputs (M == 2)
+        const bool live = ltok < c.nt;
+        const bool writer = live && (a.bf16 || (col & 1) == 0);
+        float hpart = 0.f;   // this lane's stored h values (M == 2)
 #pragma unroll
-        for (int n = 0; n < kNT; ++n) {
-            if (n == 1 && c.nt <= 8) break;            // uniform
-            const int tok = 8 * n + (col >> 1);
-            const bool live = tok < c.nt;
+        for (int mt = 0; mt < 2; ++mt) {
+            float v[M][4];
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                float v[M][4];
-#pragma unroll
-                for (int m = 0; m < M; ++m)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        v[m][r] = acc[m][mt][n][r] + __shfl_xor(acc[m][mt][n][r], 1, kWave);
-                const bool writer = (col & 1) == 0 && live;
-                const int ob = obase + 16 * mt + 4 * q;
-                float res[4];
+            for (int m = 0; m < M; ++m)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    float y = 0.f;
-                    if (ob + r < c.Og) {
-                        y = sreg[0][mt][r] * (v[0][r] - OFF * xsr[n]);
-                        if constexpr (M == 2) {
-                            const float u = sreg[1][mt][r] * (v[1][r] - OFF * xsr[n]);
-                            y = silu_f(y) * u;
-                        }
-                    }
-                    res[r] = y;
+                    const float other = __shfl_xor(acc[m][mt][r], 1, kWave);
+                    v[m][r] = a.bf16 ? acc[m][mt][r] : acc[m][mt][r] + other;
                 }
-                if (writer) {
-                    float *op = a.out + (int64_t)(c.row0 + tok) * a.ldo;
+            const int ob = obase + 16 * mt + 4 * q;
+            float res[4];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (ob + r < c.Og) op[ob + r] = res[r];
+            for (int r = 0; r < 4; ++r) {
+                float y = 0.f;
+                if (ob + r < c.Og) {
+                    y = sreg[0][mt][r] * (v[0][r] - OFF * xsr);
                     if constexpr (M == 2) {
-                        if (a.hf) {
-                            uint16_t *hb = a.hf + (int64_t)c.gp * a.hf_stride + 2 * tok * 8;
+                        const float u = sreg[1][mt][r] * (v[1][r] - OFF * xsr);
+                        y = silu_f(y) * u;
+                    }
+                }
+                res[r] = y;
+            }
+            if (writer) {
+                float *op = a.out + (int64_t)(c.row0 + ltok) * a.ldo;
 #pragma unroll
-                            for (int r = 0; r < 4; ++r) {
-                                const int o = ob + r;
-                                if (o < a.hf_rows) {
-                                    const uint16_t hv = bf16_rne(res[r]);
+                for (int r = 0; r < 4; ++r)
+                    if (ob + r < c.Og) op[ob + r] = res[r];
+                if constexpr (M == 2) {
+                    if (a.hf) {
+                        uint16_t *hb = a.hf + (int64_t)c.gp * a.hf_stride + (a.bf16 ? ltok : 2 * ltok) * 8;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int o = ob + r;
+                            if (o < a.hf_rows) {
+                                const uint16_t hv = bf16_rne(res[r]);
+                                int cc, j;
+                                pos_any(a.hf_fmt, o, cc, j);
+                                hb[(int64_t)cc * kCols * 8 + j] = hv;
+                                if (a.bf16) {
+                                    hpart += bf16_f(hv);
+                                } else {
                                     const uint16_t lv = bf16_rne(res[r] - bf16_f(hv));
-                                    int cc, j;
-                                    pos_any(a.hf_fmt, o, cc, j);
-                                    hb[(int64_t)cc * kCols * 8 + j] = hv;
                                     hb[(int64_t)cc * kCols * 8 + 8 + j] = lv;
-                                    hpart[n] += bf16_f(hv) + bf16_f(lv);
+                                    hpart += bf16_f(hv) + bf16_f(lv);
                                 }
                             }
                         }
@@ -579,16 +575,12 @@ __global__ __launch_bounds__(256) void k_mm(MmArgs a)
         if constexpr (M == 2) {
             if (a.hsum) {
                 // sum over the 4 lane groups (rows), then over the 4 waves, per token
-#pragma unroll
-                for (int n = 0; n < kNT; ++n) {
-                    float hp = hpart[n];
-                    hp += __shfl_xor(hp, 16, kWave);
-                    hp += __shfl_xor(hp, 32, kWave);
-                    if (q == 0 && (col & 1) == 0) red[wave][8 * n + (col >> 1)] = hp;
-                }
+                hpart += __shfl_xor(hpart, 16, kWave);
+                hpart += __shfl_xor(hpart, 32, kWave);
+                if (q == 0 && writer) red[wave][ltok] = hpart;
                 __syncthreads();
                 if (tid < c.nt)
-                    a.hsum[(int64_t)c.tile * a.hsum_stride + (int64_t)c.gp * kTPP + tid] =
+                    a.hsum[(int64_t)c.tile * a.hsum_stride + (int64_t)c.gp * kMaxTok + tid] =
                         (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
                 __syncthreads();   // red[] is free again
             }
@@ -596,9 +588,7 @@ __global__ __launch_bounds__(256) void k_mm(MmArgs a)
 #pragma unroll
         for (int m = 0; m < M; ++m)
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                for (int n = 0; n < kNT; ++n) acc[m][mt][n] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int mt = 0; mt < 2; ++mt) acc[m][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
     };
 
     // nxt is the block's next item, or a copy of cur after the last one (its
@@ -633,8 +623,7 @@ __global__ __launch_bounds__(256) void k_mm(MmArgs a)
         if (k + 2 >= nkb) src = nxt;
         loadW(src, k + 2 < nkb ? k + 2 : k + 2 - nkb, wl);
         __builtin_amdgcn_sched_barrier(0);
-        if (kNT == 2 && cur.nt > 8) mm_step<FMT, M, kNT>(wc, bsh[buf], src4, q, col, acc);
-        else mm_step<FMT, M, 1>(wc, bsh[buf], src4, q, col, acc);
+        mm_step<FMT, M>(wc, bsh[buf], src4, q, col, acc);
         __builtin_amdgcn_sched_barrier(0);
         const int nb = buf == 2 ? 0 : buf + 1;
         // every wave finished reading buffer nb (two steps ago) before the
@@ -714,7 +703,7 @@ hipError_t launch_fmt(const MmArgs &a, int M, int64_t items, hipStream_t st)
 }  // namespace
 
 int mm_rows_per_block() { return kRowsPerBlock; }
-int mm_tokens_per_pass() { return kTPP; }
+int mm_pass_slots() { return kMaxTok; }
 int64_t mm_kpad(int64_t I) { return (I + 1023) / 1024 * 1024; }
 
 hipError_t xprep_launch(int fmt, const MmArgs &a, const float *x, int64_t ldx, int64_t max_group_passes,
@@ -722,7 +711,7 @@ hipError_t xprep_launch(int fmt, const MmArgs &a, const float *x, int64_t ldx, i
 {
     if (max_group_passes <= 0) return hipSuccess;
     if (max_group_passes > 0x7FFFFFFF) return hipErrorInvalidValue;
-    const dim3 g((unsigned)max_group_passes, kTPP), b(kPrepThreads);
+    const dim3 g((unsigned)max_group_passes, kMaxTok), b(kPrepThreads);
     const int vec = ldx % 4 == 0 && ((uintptr_t)x & 15u) == 0;
     switch (fmt) {
     case kI8: hipLaunchKernelGGL(k_xprep<kI8>, g, b, 0, st, a, x, ldx, vec); break;
@@ -736,7 +725,7 @@ hipError_t xprep_launch(int fmt, const MmArgs &a, const float *x, int64_t ldx, i
 hipError_t sum_parts_launch(const float *parts, int nparts, int64_t stride, int64_t max_group_passes,
                            float *out, hipStream_t st)
 {
-    const int64_t n = max_group_passes * kTPP;
+    const int64_t n = max_group_passes * kMaxTok;
     if (n <= 0) return hipSuccess;
     if (n > 0x7FFFFFFF) return hipErrorInvalidValue;
     hipLaunchKernelGGL(k_sum_parts, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, parts,

@@ -167,10 +167,10 @@ int coli_moe_workspace_layout(int S, int K, int E, int D, int F, int F_shared,
     int64_t KpD = round_up(D, 1024), KpF = round_up(Fmax, 1024), tilesF = KpF / 128;
     if (!mul_ok(ngp, 4 * tpp * KpD, &t)) return COLI_ESHAPE;
     REGION(xf, t);
-    REGION(xsum, ngp * tpp * 4);
+    REGION(xsum, ngp * 2 * tpp * 4);     /* 2 tpp token slots: bf16 passes */
     if (!mul_ok(ngp, 4 * tpp * KpF, &t)) return COLI_ESHAPE;
     REGION(hf, t);
-    if (!mul_ok(tilesF * ngp, tpp * 4, &t)) return COLI_ESHAPE;
+    if (!mul_ok(tilesF * ngp, 2 * tpp * 4, &t)) return COLI_ESHAPE;
     REGION(hsum, t);
     REGION(work, (ngp + 1) * 4);
     REGION(n_work, 64);
