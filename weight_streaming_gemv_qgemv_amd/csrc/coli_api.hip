@@ -292,7 +292,7 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
     // matrix-core passes: 8 rows as bf16 hi/lo column pairs (fp32-level
     // accuracy) or 16 rows rounded once to bf16
     const int bf16 = prec == COLI_PREC_BF16 ? 1 : 0;
-    const int tpp = bf16 ? 2 * COLI_MM_TPP : COLI_MM_TPP;
+    const int tpp = bf16 ? COLI_MM_TPP_BF16 : COLI_MM_TPP_FP32;
     int32_t *work = reinterpret_cast<int32_t *>(ws + L.work);
     int32_t *n_work = reinterpret_cast<int32_t *>(ws + L.n_work);
     {
@@ -356,7 +356,7 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
             a.hf_rows = (int)kpF;
             a.hf_fmt = ex->fmt;
             a.hsum = hsum;
-            a.hsum_stride = max_gp * mm_pass_slots();
+            a.hsum_stride = max_gp * mm_pass_slots(bf16);
             {
                 StageTimer tp(kStPrep, st);
                 if (xprep_launch(ex->fmt, a, x, D, max_gp, st) != hipSuccess) return COLI_EDEVICE;
@@ -394,7 +394,8 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
             d.xf_stride = L.hf_stride;
             // the activations' sums: the gate/up tiles' partial sums, added up
             // (into xsum, free once gate/up has run)
-            if (sum_parts_launch(hsum, (int)(kpF / mm_rows_per_block()), max_gp * mm_pass_slots(), max_gp, xsum,
+            if (sum_parts_launch(hsum, (int)(kpF / mm_rows_per_block(2, bf16)), max_gp * mm_pass_slots(bf16),
+                                 max_gp * mm_pass_slots(bf16), xsum,
                                  st) != hipSuccess)
                 return COLI_EDEVICE;
             d.xsum = xsum;

@@ -11,9 +11,11 @@
 
 #define COLI_MAX_E 1024 /* 16 scores per lane of a 64-wide wave */
 #define COLI_MAX_K 64
-/* rows ("tokens") per pass of the matrix-core expert kernels: each pass
- * feeds 2 * COLI_MM_TPP columns (bf16 hi and lo per token) of one MFMA tile */
-#define COLI_MM_TPP 8
+/* rows ("tokens") per pass of the matrix-core expert kernels: in fp32
+ * precision 8, as bf16 hi/lo column pairs of one 16-column MFMA tile; in
+ * bf16 precision 32, one column each over two tiles */
+#define COLI_MM_TPP_FP32 8
+#define COLI_MM_TPP_BF16 32
 
 #ifdef __cplusplus
 extern "C" {

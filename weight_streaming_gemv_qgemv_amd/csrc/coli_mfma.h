@@ -45,17 +45,18 @@ struct MmArgs {
     int tiles;           // set by mm_launch
 };
 
-int mm_rows_per_block();
-// Token slots per pass (the stride of xsum/hsum per group-pass).
-int mm_pass_slots();
+// Output rows per item of the paired (M = 2) or single (M = 1) product.
+int mm_rows_per_block(int M, int bf16);
+// Columns (token slots) per pass: the stride of xsum/hsum per group-pass.
+int mm_pass_slots(int bf16);
 int64_t mm_kpad(int64_t I);
 // One block per possible group-pass (blocks past the device count exit).
 hipError_t xprep_launch(int fmt, const MmArgs &a, const float *x, int64_t ldx,
                         int64_t max_group_passes, hipStream_t st);
 hipError_t mm_launch(MmArgs a, int fmt, int M, int64_t max_group_passes, hipStream_t st);
-// out[i] = sum_p parts[p * stride + i] in p order, i < max_group_passes * 16.
-hipError_t sum_parts_launch(const float *parts, int nparts, int64_t stride, int64_t max_group_passes,
-                           float *out, hipStream_t st);
+// out[i] = sum_p parts[p * stride + i] in p order, i < n.
+hipError_t sum_parts_launch(const float *parts, int nparts, int64_t stride, int64_t n, float *out,
+                           hipStream_t st);
 
 
 }  // namespace coli

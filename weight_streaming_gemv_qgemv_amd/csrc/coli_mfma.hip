@@ -32,8 +32,10 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int kRowsPerWave = 32;   // two 16-row MFMA tiles
-constexpr int kRowsPerBlock = 128; // four waves
+constexpr int kWavesPerBlock = 4;
+// Row tiles of 16 per wave: 2, except for the paired gate/up product with
+// two-N-tile passes, where 1 keeps the register footprint of the others.
+template <int M, int NT> struct RowTiles { static constexpr int MT = (M == 2 && NT == 2) ? 1 : 2; };
 constexpr int kXcds = 8;
 
 template <int FMT> struct MF;
@@ -134,18 +136,19 @@ __device__ __forceinline__ floatx4 mfma(const uint4 &a, const uint4 &b, floatx4 
 }
 
 // ---------------------------------------------------------------- layout
-// Work is cut into passes of activation rows ("tokens") of one group, one
-// MFMA tile of kCols = 16 columns each.  fp32 precision: up to 8 tokens,
-// token t in columns 2t (bf16 hi) and 2t+1 (bf16 lo).  bf16 precision: up to
-// 16 tokens, token t in column t (x rounded once).  A pass's activations are
-// stored "fragment-major": for k-block kbi, MFMA step s and lane group q,
-// chunk c = (kbi*STEPS + s)*4 + q holds, for each column, the 8 bf16 values
-// of the slots that lane (col, q) feeds to that step.  A k-block's activations are one contiguous
+// Work is cut into passes of activation rows ("tokens") of one group, of
+// 16 NT columns (NT MFMA N-tiles of 16).  fp32 precision: NT = 1, up to 8
+// tokens, token t in columns 2t (bf16 hi) and 2t+1 (bf16 lo).  bf16
+// precision: NT = 2, up to 32 tokens, token t in column t (x rounded once).
+// A pass's activations are stored "fragment-major": for k-block kbi, MFMA
+// step s and lane group q, chunk c = (kbi*STEPS + s)*4 + q holds, for each
+// column, the 8 bf16 values of the slots that lane (col, q) feeds to that
+// step; the live columns are a prefix of every chunk, and a pass whose live
+// columns fit one N-tile runs the products of that tile only.  A k-block's activations are one contiguous
 // STEPS*2 KB run, and the live tokens' columns are a prefix of every chunk.
 // Element e of the product's input sits in chunk c, slot j = pos_of(e).
-constexpr int kCols = 16;             // MFMA columns per pass (one N-tile)
-constexpr int kMaxTok = kCols;        // tokens per pass at most (bf16)
-static_assert(2 * COLI_MM_TPP == kCols, "fp32 passes hold COLI_MM_TPP tokens as hi/lo column pairs");
+static_assert(2 * COLI_MM_TPP_FP32 == 16 && COLI_MM_TPP_BF16 == 32, "pass widths: 1 and 2 N-tiles");
+constexpr int nt_of(int bf16) { return bf16 ? 2 : 1; }
 
 template <int FMT> __device__ __forceinline__ int elem_of(int kbi, int s, int q, int j)
 {
@@ -243,11 +246,12 @@ __device__ __forceinline__ int n_group_passes(const MmArgs &a)
 // alone in bf16 precision) per token, in a fixed order.
 constexpr int kPrepThreads = 256;
 constexpr int kPrepRuns = 4;   // runs per thread per round
-template <int FMT>
+template <int FMT, int NT>
 __global__ __launch_bounds__(kPrepThreads) void k_xprep(MmArgs a, const float *__restrict__ x,
                                                         int64_t ldx, int vec)
 {
     constexpr int RUN = FMT == kI2 ? 16 : 8;
+    constexpr int kCols = 16 * NT;
     __shared__ float red[kPrepThreads / kWave];
     const int gp = blockIdx.x, t = blockIdx.y;
     if (gp >= n_group_passes(a)) return;
@@ -326,7 +330,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_xprep(MmArgs a, const float *_
     if (tid == 0) {
         float tot = 0.f;
         for (int w = 0; w < kPrepThreads / kWave; ++w) tot += red[w];
-        a.xsum[(int64_t)gp * kMaxTok + t] = tot;
+        a.xsum[(int64_t)gp * kCols + t] = tot;
     }
 }
 
@@ -334,17 +338,17 @@ __global__ __launch_bounds__(kPrepThreads) void k_xprep(MmArgs a, const float *_
 // One MFMA k-block step of a wave: weights (row-contiguous registers) moved
 // into the operand layout in place with ds_bpermute -- lane (q, col) gets
 // row col, chunk q, from lane 4 col + q -- then STEPS x M x 2 x NTL products
-// against the activations staged in LDS (bs): one N-tile of 16 columns.
-template <int FMT, int M>
-__device__ __forceinline__ void mm_step(uint4 (&wl)[M][2][MF<FMT>::SEGS], const uint4 *bs,
-                                        int src4, int q, int col, floatx4 (&acc)[M][2])
+// against the activations staged in LDS (bs), for the first NTL N-tiles.
+template <int FMT, int M, int MT, int NT, int NTL>
+__device__ __forceinline__ void mm_step(uint4 (&wl)[M][MT][MF<FMT>::SEGS], const uint4 *bs,
+                                        int src4, int q, int col, floatx4 (&acc)[M][MT][NT])
 {
     using T = MF<FMT>;
     constexpr int SEGS = T::SEGS, SPS = T::SPS, STEPS = T::STEPS;
 #pragma unroll
     for (int m = 0; m < M; ++m)
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int sg = 0; sg < SEGS; ++sg) {
                 const uint4 v = wl[m][mt][sg];
@@ -355,22 +359,27 @@ __device__ __forceinline__ void mm_step(uint4 (&wl)[M][2][MF<FMT>::SEGS], const 
             }
 #pragma unroll
     for (int s2 = 0; s2 < STEPS; ++s2) {
-        const uint4 xb = bs[(s2 * 4 + q) * kCols + col];
+        uint4 xb[NTL];
+#pragma unroll
+        for (int n = 0; n < NTL; ++n) xb[n] = bs[(s2 * 4 + q) * (16 * NT) + 16 * n + col];
 #pragma unroll
         for (int m = 0; m < M; ++m)
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-                acc[m][mt] = mfma(codes<FMT>(wl[m][mt][s2 / SPS], s2 % SPS), xb, acc[m][mt]);
+            for (int mt = 0; mt < MT; ++mt) {
+                const uint4 cw = codes<FMT>(wl[m][mt][s2 / SPS], s2 % SPS);
+#pragma unroll
+                for (int n = 0; n < NTL; ++n) acc[m][mt][n] = mfma(cw, xb[n], acc[m][mt][n]);
+            }
     }
 }
 
 // Everything about one item -- (group-pass gp, 128-row tile) -- that its
 // loads, its activation staging and its epilogue need.
-template <int M, int UMAX>
+template <int M, int MT, int UMAX>
 struct Item {
     int gp, tile, nt, row0, Og;
     const uint8_t *wb[M];      // the group's matrices (uniform)
-    uint32_t roff[2];          // this lane's row (clamped) * rb + its 16-byte chunk, per row tile
+    uint32_t roff[MT];         // this lane's row (clamped) * rb + its 16-byte chunk, per row tile
     const float *sc[M];
     const uint4 *bglob;        // the group-pass's activation fragments (uniform)
     int boff[UMAX];            // this thread's activation units in a k-block (-1: dead)
@@ -394,11 +403,14 @@ struct Item {
 //     k-blocks of weights per wave stay in flight all the time.
 //   * kpad is a multiple of 1024, so an item has at least 4 k-blocks and
 //     three steps ahead is at most the next item.
-template <int FMT, int M>
+template <int FMT, int M, int NT>
 __global__ __launch_bounds__(256) void k_mm(MmArgs a)
 {
     using T = MF<FMT>;
     constexpr int STEPS = T::STEPS, KB = T::KB, SEGS = T::SEGS, BITS = T::BITS;
+    constexpr int MT = RowTiles<M, NT>::MT;
+    constexpr int kNT = NT, kCols = 16 * NT, kMaxTok = kCols;
+    constexpr int kRowsPerWave = 16 * MT, kRowsPerBlock = kWavesPerBlock * kRowsPerWave;
     constexpr int CH = STEPS * 4;                 // activation chunks per k-block
     constexpr int UMAX = (CH * kCols + 255) / 256;
     constexpr float OFF = T::OFF;
@@ -422,7 +434,7 @@ __global__ __launch_bounds__(256) void k_mm(MmArgs a)
     // zero activations)
     const uint32_t last_seg = (uint32_t)(a.rb - 16 - 16 * lchunk);
 
-    using It = Item<M, UMAX>;
+    using It = Item<M, MT, UMAX>;
     auto make = [&](It &c, int it) {
         // uniform: the work-list and offset lookups below are scalar loads
         c.gp = __builtin_amdgcn_readfirstlane(xcd + kXcds * (it / a.tiles));
@@ -449,7 +461,7 @@ __global__ __launch_bounds__(256) void k_mm(MmArgs a)
 #pragma unroll
         for (int m = 0; m < M; ++m) c.wb[m] = W[m];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
             c.roff[mt] = (uint32_t)(min(obase + 16 * mt + lrow, c.Og - 1) * a.rb) + 16 * lchunk;
         c.bglob = reinterpret_cast<const uint4 *>(a.xf + (int64_t)c.gp * a.xf_stride);
         // live activation units of a k-block: CH chunks x (2 nt or nt) columns
@@ -464,12 +476,12 @@ __global__ __launch_bounds__(256) void k_mm(MmArgs a)
     // weights: uniform matrix base + 32-bit lane offset (scalar-base loads);
     // past the row end (only when the row is shorter than kpad) each lane's
     // segment is clamped to the row's last one
-    auto loadW = [&](const It &c, int kbi, uint4 (&w)[M][2][SEGS]) {
+    auto loadW = [&](const It &c, int kbi, uint4 (&w)[M][MT][SEGS]) {
         const uint32_t b0 = (uint32_t)kbi * (uint32_t)kbytes;
 #pragma unroll
         for (int m = 0; m < M; ++m)
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
+            for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                 for (int sg = 0; sg < SEGS; ++sg)
                     w[m][mt][sg] = gload16(c.wb[m] + (c.roff[mt] + min(b0 + 64 * sg, last_seg)));
@@ -491,80 +503,90 @@ __global__ __launch_bounds__(256) void k_mm(MmArgs a)
     // epilogue inputs: the scales of the lane's 4 rows per (matrix, row tile)
     // and the sums of its tokens (clamped indexes, unconditional loads; rows
     // and tokens out of range are never written)
-    // this lane's token: column col (bf16) or col / 2 (hi/lo pairs)
-    const int ltok = a.bf16 ? col : (col >> 1);
-    float sreg[M][2][4], xsr;
+    // this lane's token in N-tile n: column 16 n + col (bf16) or half of it
+    // (hi/lo pairs)
+    auto ltok = [&](int n) { return a.bf16 ? 16 * n + col : 8 * n + (col >> 1); };
+    float sreg[M][MT][4], xsr[kNT];
     auto load_epi = [&](const It &c) {
         const int obase = c.tile * kRowsPerBlock + wave * kRowsPerWave;
 #pragma unroll
         for (int m = 0; m < M; ++m)
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
+            for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     sreg[m][mt][r] = gloadf(c.sc[m] + min(obase + 16 * mt + 4 * q + r, c.Og - 1));
-        xsr = gloadf(a.xsum + (int64_t)c.gp * kMaxTok + min(ltok, c.nt - 1));
+#pragma unroll
+        for (int n = 0; n < kNT; ++n)
+            xsr[n] = gloadf(a.xsum + (int64_t)c.gp * kMaxTok + min(ltok(n), c.nt - 1));
     };
 
-    floatx4 acc[M][2];
+    floatx4 acc[M][MT][kNT];
 #pragma unroll
     for (int m = 0; m < M; ++m)
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) acc[m][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int n = 0; n < kNT; ++n) acc[m][mt][n] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    // ---- epilogue: D[4q + r][col]; in hi/lo precision the lo column is
-    // added to the hi column
+    // ---- epilogue: D[4q + r][16 n + col]; in hi/lo precision the lo
+    // column is added to the hi column
     auto epilogue = [&](const It &c) {
         const int obase = c.tile * kRowsPerBlock + wave * kRowsPerWave;
-        const bool live = ltok < c.nt;
-        const bool writer = live && (a.bf16 || (col & 1) == 0);
-        float hpart = 0.f;   // this lane's stored h values (M == 2)
+        const int ncols = a.bf16 ? c.nt : 2 * c.nt;
+        float hpart[kNT] = {};   // this lane's stored h values per N-tile (M == 2)
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            float v[M][4];
+        for (int n = 0; n < kNT; ++n) {
+            if (16 * n >= ncols) break;                  // uniform: tile not live
+            const int tok = ltok(n);
+            const bool writer = tok < c.nt && (a.bf16 || (col & 1) == 0);
 #pragma unroll
-            for (int m = 0; m < M; ++m)
+            for (int mt = 0; mt < MT; ++mt) {
+                float v[M][4];
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float other = __shfl_xor(acc[m][mt][n][r], 1, kWave);
+                        v[m][r] = a.bf16 ? acc[m][mt][n][r] : acc[m][mt][n][r] + other;
+                    }
+                const int ob = obase + 16 * mt + 4 * q;
+                float res[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float other = __shfl_xor(acc[m][mt][r], 1, kWave);
-                    v[m][r] = a.bf16 ? acc[m][mt][r] : acc[m][mt][r] + other;
-                }
-            const int ob = obase + 16 * mt + 4 * q;
-            float res[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float y = 0.f;
-                if (ob + r < c.Og) {
-                    y = sreg[0][mt][r] * (v[0][r] - OFF * xsr);
-                    if constexpr (M == 2) {
-                        const float u = sreg[1][mt][r] * (v[1][r] - OFF * xsr);
-                        y = silu_f(y) * u;
+                    float y = 0.f;
+                    if (ob + r < c.Og) {
+                        y = sreg[0][mt][r] * (v[0][r] - OFF * xsr[n]);
+                        if constexpr (M == 2) {
+                            const float u = sreg[1][mt][r] * (v[1][r] - OFF * xsr[n]);
+                            y = silu_f(y) * u;
+                        }
                     }
+                    res[r] = y;
                 }
-                res[r] = y;
-            }
-            if (writer) {
-                float *op = a.out + (int64_t)(c.row0 + ltok) * a.ldo;
+                if (writer) {
+                    float *op = a.out + (int64_t)(c.row0 + tok) * a.ldo;
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (ob + r < c.Og) op[ob + r] = res[r];
-                if constexpr (M == 2) {
-                    if (a.hf) {
-                        uint16_t *hb = a.hf + (int64_t)c.gp * a.hf_stride + (a.bf16 ? ltok : 2 * ltok) * 8;
+                    for (int r = 0; r < 4; ++r)
+                        if (ob + r < c.Og) op[ob + r] = res[r];
+                    if constexpr (M == 2) {
+                        if (a.hf) {
+                            uint16_t *hb = a.hf + (int64_t)c.gp * a.hf_stride + (a.bf16 ? tok : 2 * tok) * 8;
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int o = ob + r;
-                            if (o < a.hf_rows) {
-                                const uint16_t hv = bf16_rne(res[r]);
-                                int cc, j;
-                                pos_any(a.hf_fmt, o, cc, j);
-                                hb[(int64_t)cc * kCols * 8 + j] = hv;
-                                if (a.bf16) {
-                                    hpart += bf16_f(hv);
-                                } else {
-                                    const uint16_t lv = bf16_rne(res[r] - bf16_f(hv));
-                                    hb[(int64_t)cc * kCols * 8 + 8 + j] = lv;
-                                    hpart += bf16_f(hv) + bf16_f(lv);
+                            for (int r = 0; r < 4; ++r) {
+                                const int o = ob + r;
+                                if (o < a.hf_rows) {
+                                    const uint16_t hv = bf16_rne(res[r]);
+                                    int cc, j;
+                                    pos_any(a.hf_fmt, o, cc, j);
+                                    hb[(int64_t)cc * kCols * 8 + j] = hv;
+                                    if (a.bf16) {
+                                        hpart[n] += bf16_f(hv);
+                                    } else {
+                                        const uint16_t lv = bf16_rne(res[r] - bf16_f(hv));
+                                        hb[(int64_t)cc * kCols * 8 + 8 + j] = lv;
+                                        hpart[n] += bf16_f(hv) + bf16_f(lv);
+                                    }
                                 }
                             }
                         }
@@ -575,9 +597,14 @@ __global__ __launch_bounds__(256) void k_mm(MmArgs a)
         if constexpr (M == 2) {
             if (a.hsum) {
                 // sum over the 4 lane groups (rows), then over the 4 waves, per token
-                hpart += __shfl_xor(hpart, 16, kWave);
-                hpart += __shfl_xor(hpart, 32, kWave);
-                if (q == 0 && writer) red[wave][ltok] = hpart;
+#pragma unroll
+                for (int n = 0; n < kNT; ++n) {
+                    float hp = hpart[n];
+                    hp += __shfl_xor(hp, 16, kWave);
+                    hp += __shfl_xor(hp, 32, kWave);
+                    const int tok = ltok(n);
+                    if (q == 0 && tok < c.nt && (a.bf16 || (col & 1) == 0)) red[wave][tok] = hp;
+                }
                 __syncthreads();
                 if (tid < c.nt)
                     a.hsum[(int64_t)c.tile * a.hsum_stride + (int64_t)c.gp * kMaxTok + tid] =
@@ -588,7 +615,9 @@ __global__ __launch_bounds__(256) void k_mm(MmArgs a)
 #pragma unroll
         for (int m = 0; m < M; ++m)
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) acc[m][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int n = 0; n < kNT; ++n) acc[m][mt][n] = floatx4{0.f, 0.f, 0.f, 0.f};
     };
 
     // nxt is the block's next item, or a copy of cur after the last one (its
@@ -600,7 +629,7 @@ __global__ __launch_bounds__(256) void k_mm(MmArgs a)
     if (has_nxt) make(nxt, jn);
     else nxt = cur;
 
-    uint4 w0[M][2][SEGS], w1[M][2][SEGS], w2[M][2][SEGS];
+    uint4 w0[M][MT][SEGS], w1[M][MT][SEGS], w2[M][MT][SEGS];
     uint4 breg[UMAX];
     int k = 0, buf = 0;
     // prologue: W(0), W(1), B(0) -> LDS
@@ -612,7 +641,7 @@ __global__ __launch_bounds__(256) void k_mm(MmArgs a)
 
     // one k-block step s = (cur, k): returns true after the block's last item
     //   wc = W(s), wl <- W(s+2); B(s+1) loaded and staged to LDS
-    auto step = [&](uint4 (&wc)[M][2][SEGS], uint4 (&wl)[M][2][SEGS]) -> bool {
+    auto step = [&](uint4 (&wc)[M][MT][SEGS], uint4 (&wl)[M][MT][SEGS]) -> bool {
         if (k == nkb - 2) load_epi(cur);
         // the sources are selected, not branched on: the same loads are
         // issued on every path, so the waits count them exactly
@@ -623,7 +652,10 @@ __global__ __launch_bounds__(256) void k_mm(MmArgs a)
         if (k + 2 >= nkb) src = nxt;
         loadW(src, k + 2 < nkb ? k + 2 : k + 2 - nkb, wl);
         __builtin_amdgcn_sched_barrier(0);
-        mm_step<FMT, M>(wc, bsh[buf], src4, q, col, acc);
+        if (NT == 2 && (a.bf16 ? cur.nt : 2 * cur.nt) > 16)
+            mm_step<FMT, M, MT, NT, NT>(wc, bsh[buf], src4, q, col, acc);
+        else
+            mm_step<FMT, M, MT, NT, 1>(wc, bsh[buf], src4, q, col, acc);
         __builtin_amdgcn_sched_barrier(0);
         const int nb = buf == 2 ? 0 : buf + 1;
         // every wave finished reading buffer nb (two steps ago) before the
@@ -680,30 +712,36 @@ int resident_blocks(const void *kern, int *cache)
     return cache[dev];
 }
 
-template <int FMT, int M>
+template <int FMT, int M, int NT>
 hipError_t launch_fm(const MmArgs &a, int64_t items, hipStream_t st)
 {
     static int cache[64] = {0};
-    const void *kern = (const void *)k_mm<FMT, M>;
+    const void *kern = (const void *)k_mm<FMT, M, NT>;
     int64_t cap = resident_blocks(kern, cache) / kXcds * kXcds;
     if (cap < kXcds) cap = kXcds;
     int64_t grid = (items + kXcds - 1) / kXcds * kXcds;
     if (grid > cap) grid = cap;
     if (grid < kXcds) grid = kXcds;
-    hipLaunchKernelGGL((k_mm<FMT, M>), dim3((unsigned)grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_mm<FMT, M, NT>), dim3((unsigned)grid), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
 template <int FMT>
 hipError_t launch_fmt(const MmArgs &a, int M, int64_t items, hipStream_t st)
 {
-    return M == 2 ? launch_fm<FMT, 2>(a, items, st) : launch_fm<FMT, 1>(a, items, st);
+    if (a.bf16) return M == 2 ? launch_fm<FMT, 2, 2>(a, items, st) : launch_fm<FMT, 1, 2>(a, items, st);
+    return M == 2 ? launch_fm<FMT, 2, 1>(a, items, st) : launch_fm<FMT, 1, 1>(a, items, st);
 }
 
 }  // namespace
 
-int mm_rows_per_block() { return kRowsPerBlock; }
-int mm_pass_slots() { return kMaxTok; }
+int mm_rows_per_block(int M, int bf16)
+{
+    const int mt = bf16 ? (M == 2 ? RowTiles<2, 2>::MT : RowTiles<1, 2>::MT)
+                        : (M == 2 ? RowTiles<2, 1>::MT : RowTiles<1, 1>::MT);
+    return kWavesPerBlock * 16 * mt;
+}
+int mm_pass_slots(int bf16) { return 16 * nt_of(bf16); }
 int64_t mm_kpad(int64_t I) { return (I + 1023) / 1024 * 1024; }
 
 hipError_t xprep_launch(int fmt, const MmArgs &a, const float *x, int64_t ldx, int64_t max_group_passes,
@@ -711,21 +749,29 @@ hipError_t xprep_launch(int fmt, const MmArgs &a, const float *x, int64_t ldx, i
 {
     if (max_group_passes <= 0) return hipSuccess;
     if (max_group_passes > 0x7FFFFFFF) return hipErrorInvalidValue;
-    const dim3 g((unsigned)max_group_passes, kMaxTok), b(kPrepThreads);
+    const dim3 g((unsigned)max_group_passes, 16 * nt_of(a.bf16)), b(kPrepThreads);
     const int vec = ldx % 4 == 0 && ((uintptr_t)x & 15u) == 0;
     switch (fmt) {
-    case kI8: hipLaunchKernelGGL(k_xprep<kI8>, g, b, 0, st, a, x, ldx, vec); break;
-    case kI4: hipLaunchKernelGGL(k_xprep<kI4>, g, b, 0, st, a, x, ldx, vec); break;
-    case kI2: hipLaunchKernelGGL(k_xprep<kI2>, g, b, 0, st, a, x, ldx, vec); break;
+    case kI8:
+        if (a.bf16) hipLaunchKernelGGL((k_xprep<kI8, 2>), g, b, 0, st, a, x, ldx, vec);
+        else hipLaunchKernelGGL((k_xprep<kI8, 1>), g, b, 0, st, a, x, ldx, vec);
+        break;
+    case kI4:
+        if (a.bf16) hipLaunchKernelGGL((k_xprep<kI4, 2>), g, b, 0, st, a, x, ldx, vec);
+        else hipLaunchKernelGGL((k_xprep<kI4, 1>), g, b, 0, st, a, x, ldx, vec);
+        break;
+    case kI2:
+        if (a.bf16) hipLaunchKernelGGL((k_xprep<kI2, 2>), g, b, 0, st, a, x, ldx, vec);
+        else hipLaunchKernelGGL((k_xprep<kI2, 1>), g, b, 0, st, a, x, ldx, vec);
+        break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-hipError_t sum_parts_launch(const float *parts, int nparts, int64_t stride, int64_t max_group_passes,
-                           float *out, hipStream_t st)
+hipError_t sum_parts_launch(const float *parts, int nparts, int64_t stride, int64_t n, float *out,
+                           hipStream_t st)
 {
-    const int64_t n = max_group_passes * kMaxTok;
     if (n <= 0) return hipSuccess;
     if (n > 0x7FFFFFFF) return hipErrorInvalidValue;
     hipLaunchKernelGGL(k_sum_parts, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, parts,
@@ -737,7 +783,8 @@ hipError_t mm_launch(MmArgs a, int fmt, int M, int64_t max_group_passes, hipStre
 {
     const int Ocover = a.hf && a.hf_rows > a.O ? a.hf_rows : a.O;
     const int Omax = a.has_extra && a.xO > Ocover ? a.xO : Ocover;
-    a.tiles = (Omax + kRowsPerBlock - 1) / kRowsPerBlock;
+    const int rpb = mm_rows_per_block(M, a.bf16);
+    a.tiles = (Omax + rpb - 1) / rpb;
     const int64_t items = max_group_passes * a.tiles;
     switch (fmt) {
     case kI8: return launch_fmt<kI8>(a, M, items, st);

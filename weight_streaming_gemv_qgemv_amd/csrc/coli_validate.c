@@ -158,26 +158,29 @@ int coli_moe_workspace_layout(int S, int K, int E, int D, int F, int F_shared,
     if (!mul_ok(rows, D, &t) || !mul_ok(t, 4, &t)) return COLI_ESHAPE;
     REGION(y, t);
     REGION(router_part, coli__router_partial_bytes(S, E, D));
-    /* matrix-core path: per (expert, COLI_MM_TPP-row pass) the activations as
-     * bf16 hi/lo fragments (2 COLI_MM_TPP columns x input width rounded up to
-     * 1024), their sums, the SwiGLU output prepared the same way, its partial
-     * sums per 128-row tile, and the work list */
-    const int64_t tpp = COLI_MM_TPP;
+    /* matrix-core path, per (group, pass): the activations fragment-major
+     * (cols bf16 columns x input width rounded up to 1024), their sums, the
+     * SwiGLU output prepared the same way, its partial sums per gate/up item
+     * (128 rows in fp32 precision, 64 in bf16), and the work list.  fp32
+     * passes hold COLI_MM_TPP_FP32 rows as hi/lo column pairs (16 columns),
+     * bf16 passes COLI_MM_TPP_BF16 rows (32 columns). */
+    const int bf16 = prec == COLI_PREC_BF16;
+    const int64_t tpp = bf16 ? COLI_MM_TPP_BF16 : COLI_MM_TPP_FP32, cols = bf16 ? 32 : 16;
     int64_t ngp = (rows + tpp - 1) / tpp + (int64_t)E + 1;   /* passes */
-    int64_t KpD = round_up(D, 1024), KpF = round_up(Fmax, 1024), tilesF = KpF / 128;
-    if (!mul_ok(ngp, 4 * tpp * KpD, &t)) return COLI_ESHAPE;
+    int64_t KpD = round_up(D, 1024), KpF = round_up(Fmax, 1024), tilesF = KpF / (bf16 ? 64 : 128);
+    if (!mul_ok(ngp, 2 * cols * KpD, &t)) return COLI_ESHAPE;
     REGION(xf, t);
-    REGION(xsum, ngp * 2 * tpp * 4);     /* 2 tpp token slots: bf16 passes */
-    if (!mul_ok(ngp, 4 * tpp * KpF, &t)) return COLI_ESHAPE;
+    REGION(xsum, ngp * cols * 4);
+    if (!mul_ok(ngp, 2 * cols * KpF, &t)) return COLI_ESHAPE;
     REGION(hf, t);
-    if (!mul_ok(tilesF * ngp, 2 * tpp * 4, &t)) return COLI_ESHAPE;
+    if (!mul_ok(tilesF * ngp, cols * 4, &t)) return COLI_ESHAPE;
     REGION(hsum, t);
     REGION(work, (ngp + 1) * 4);
     REGION(n_work, 64);
 #undef REGION
     out->n_pass_max = ngp;
-    out->xf_stride = 2 * tpp * KpD;
-    out->hf_stride = 2 * tpp * KpF;
+    out->xf_stride = cols * KpD;
+    out->hf_stride = cols * KpF;
     out->h_ld = Fmax;
     out->total = off;
     return COLI_OK;
