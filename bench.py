@@ -280,13 +280,15 @@ def run_qgemv(args, dev):
     import torch
     from weight_streaming_gemv_qgemv_amd import binding as b
     from weight_streaming_gemv_qgemv_amd import synth
-    O, I, S, fmt = 12288, 6144, 1, 2
-    g = synth.rng(4200)
+    fmt = {"f32": 0, "i8": 1, "i4": 2, "i2": 3}[args.fmt]
+    O, I, S = 12288, 6144, args.tokens
+    g = synth.rng(4200, fmt)
     W = synth.weight_bytes(g, fmt, O, I)
     sc = synth.scales(g, O)
     x = synth.activations(g, S, I)
     Wd0 = to_dev(W, dev)
-    copies = [Wd0] + [Wd0.clone() for _ in range(31)]      # 32 x 37.7 MB > 1 GiB rotation
+    ncopy = max(2, -(-(1 << 30) // W.nbytes))                  # a rotation of >= 1 GiB
+    copies = [Wd0] + [Wd0.clone() for _ in range(ncopy - 1)]
     scd, xd = to_dev(sc, dev), to_dev(x, dev)
     y = torch.empty((S, O), dtype=torch.float32, device=dev)
 
@@ -296,9 +298,9 @@ def run_qgemv(args, dev):
     step_bytes = O * W.shape[1] + O * 4 + S * I * 4 + S * O * 4
     ms, wall, stages = time_steps(step, args.steps, args.warmup)
     q_ms, q_n = stages["qgemv"]
-    return dict(workload="qgemv_i4_12288x6144_s1", ms=ms, wall=wall, step_bytes=step_bytes,
+    return dict(workload=f"qgemv_{args.fmt}_12288x6144_s{S}", ms=ms, wall=wall, step_bytes=step_bytes,
                 tokens=S, stages=stages, uniq=None,
-                dominant=dict(kernel="k_gemv<I4,M=1>", bytes_per_launch=step_bytes,
+                dominant=dict(kernel=f"qgemv {args.fmt} (coli_qgemv)", bytes_per_launch=step_bytes,
                               ms_per_launch=q_ms / max(q_n, 1), launches=q_n))
 
 
@@ -325,6 +327,8 @@ def main():
     ap.add_argument("--workload", default="layer64",
                     choices=["layer64", "decode16", "qgemv", "prefill2048", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fmt", default="i4", choices=["f32", "i8", "i4", "i2"], help="qgemv workload")
+    ap.add_argument("--tokens", type=int, default=1, help="qgemv workload: S")
     ap.add_argument("--cpu-tokens", type=int, default=64)
     args = ap.parse_args()
     if args.gpus != 1:
