@@ -173,10 +173,10 @@ def run_layer64(args, dev):
     gu_bytes = (uniq + 1) * gu + S * D * 4 + (S * K + S) * F * 4
     res = dict(workload="moe_layer_decode_64", ms=ms, wall=wall, step_bytes=step_bytes,
                tokens=S, stages=stages, uniq=uniq,
-               dominant=dict(kernel="k_mm<I4,2> (grouped expert gate/up + SwiGLU, matrix cores)",
+               dominant=dict(kernel="k_dec<I4,2> (grouped expert gate/up + SwiGLU, matrix cores)",
                              bytes_per_launch=gu_bytes, ms_per_launch=gu_ms / max(gu_n, 1),
                              launches=gu_n,
-                             traffic=recorded_traffic("moe_layer_decode_64", "k_mm<2, 2>")))
+                             traffic=recorded_traffic("moe_layer_decode_64", "k_dec<2, 2>")))
     if not args.no_cpu_baseline:
         ntok = args.cpu_tokens
         log(f"cpu baseline: oracle on {ntok} tokens")
@@ -259,7 +259,7 @@ def run_decode16(args, dev):
     gu_ms, gu_n = stages["gate_up"]
     res = dict(workload="moe_expert_decode_16", ms=ms, wall=wall, step_bytes=step_bytes,
                tokens=S, stages=stages, uniq=uniq,
-               dominant=dict(kernel="k_mm<I4,2> (grouped expert gate/up + SwiGLU, matrix cores)",
+               dominant=dict(kernel="k_dec<I4,2> (grouped expert gate/up + SwiGLU, matrix cores)",
                              bytes_per_launch=uniq * gu + S * D * 4 + S * K * F * 4,
                              ms_per_launch=gu_ms / max(gu_n, 1), launches=gu_n))
     if not args.no_cpu_baseline:

@@ -183,15 +183,19 @@ size_t coli_moe_workspace_bytes(int S, int K, int E, int D, int F,
  *   y          [S*K + S, D] fp32: expert output per grouped row (same
  *              numbering), before the routing weight.
  *   router_part  fp64 partial router logits (scratch).
- *   xf, xsum, hf, hsum, work, n_work   matrix-core scratch: per (expert,
- *              16-token pass) the activations and the SwiGLU output as bf16
- *              hi/lo fragments (xf_stride / hf_stride elements per pass),
- *              their sums, and the device-built list of passes. */
+ *   xf, xsum, hf, hsum, work, n_work   matrix-core scratch and the
+ *              device-built list of passes.  COLI_PREC_FP32: xf holds one row
+ *              per token and hf one row per grouped row, each the row's
+ *              activations (x, resp. the SwiGLU output) as bf16 hi/lo pairs
+ *              in the kernels' fragment order (xf_stride / hf_stride bf16
+ *              per row); xsum and hsum are empty.  COLI_PREC_BF16: xf and hf
+ *              hold the activations per (expert, 32-row pass), xsum and hsum
+ *              their sums (xf_stride / hf_stride bf16 per pass). */
 typedef struct {
     int64_t flags, sig, idx, w, offsets, counts, row_pair, pair_row, h, y, router_part;
     int64_t xf, xsum, hf, hsum, work, n_work;
     int64_t n_pass_max;            /* passes the scratch is sized for */
-    int64_t xf_stride, hf_stride;  /* bf16 elements per pass */
+    int64_t xf_stride, hf_stride;  /* bf16 elements per row (fp32) or pass (bf16) */
     int64_t h_ld;   /* row stride of h in floats (max of F and F_shared) */
     int64_t total;  /* == coli_moe_workspace_bytes(...) */
 } coli_ws_layout;

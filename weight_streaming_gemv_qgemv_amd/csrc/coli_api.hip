@@ -11,6 +11,7 @@
 #include <stdint.h>
 
 #include "coli.h"
+#include "coli_dec.h"
 #include "coli_device.h"
 #include "coli_gemv.h"
 #include "coli_mfma.h"
@@ -308,6 +309,95 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
     if (err != hipSuccess) return COLI_EDEVICE;
     }
 
+    if (mm && !bf16) {
+        // fp32 precision: x as one row table per token, the SwiGLU output as
+        // one per grouped row
+        uint16_t *xt = reinterpret_cast<uint16_t *>(ws + L.xf);
+        uint16_t *ht = reinterpret_cast<uint16_t *>(ws + L.hf);
+        const int64_t max_gp = L.n_pass_max;
+        const int kpD = (int)mm_kpad(D), kpF = (int)mm_kpad(F);
+        {
+            StageTimer tp(kStPrep, st);
+            if (xrows_launch(ex->fmt, x, D, S, D, kpD, xt, st) != hipSuccess) return COLI_EDEVICE;
+        }
+        {
+            StageTimer tgu(kStGateUp, st);
+            DecArgs a = {};
+            a.w[0] = (const uint8_t *)ex->w_gate;
+            a.w[1] = (const uint8_t *)ex->w_up;
+            a.s[0] = ex->s_gate;
+            a.s[1] = ex->s_up;
+            a.w_gstride = (int64_t)F * rbD;
+            a.s_gstride = F;
+            a.ngroups = E;
+            a.O = F;
+            if (sh_mm) {
+                a.has_extra = 1;
+                a.xw[0] = (const uint8_t *)sh->w_gate;
+                a.xw[1] = (const uint8_t *)sh->w_up;
+                a.xs[0] = sh->s_gate;
+                a.xs[1] = sh->s_up;
+                a.xO = F;
+                a.x_rows = S;
+                a.x_row0 = (int)shared_row0;
+            }
+            a.I = D;
+            a.kpad = kpD;
+            a.rb = rbD;
+            a.offsets = offsets;
+            a.row_pair = row_pair;
+            a.K = K;
+            a.act_by_token = 1;
+            a.act = xt;
+            a.work = work;
+            a.n_work = n_work;
+            a.out = h;
+            a.ldo = L.h_ld;
+            a.out_vec4 = L.h_ld % 4 == 0 && al16(h);
+            a.hf = ht;
+            a.hf_kpad = kpF;
+            if (dec_launch(a, ex->fmt, 2, max_gp, st) != hipSuccess) return COLI_EDEVICE;
+        }
+        {
+            StageTimer tdn(kStDown, st);
+            DecArgs d = {};
+            d.w[0] = (const uint8_t *)ex->w_down;
+            d.s[0] = ex->s_down;
+            d.w_gstride = (int64_t)D * rbF;
+            d.s_gstride = D;
+            d.ngroups = E;
+            d.O = D;
+            if (sh_mm) {
+                d.has_extra = 1;
+                d.xw[0] = (const uint8_t *)sh->w_down;
+                d.xs[0] = sh->s_down;
+                d.xO = D;
+                d.x_rows = S;
+                d.x_row0 = (int)shared_row0;
+            }
+            d.I = F;
+            d.kpad = kpF;
+            d.rb = rbF;
+            d.offsets = offsets;
+            d.row_pair = row_pair;
+            d.K = K;
+            d.act_by_token = 0;
+            d.act = ht;
+            d.work = work;
+            d.n_work = n_work;
+            d.out = y;
+            d.ldo = D;
+            d.out_vec4 = D % 4 == 0 && al16(y);
+            if (dec_launch(d, ex->fmt, 1, max_gp, st) != hipSuccess) return COLI_EDEVICE;
+        }
+        if (sh && !sh_mm) {
+            int rc = run_shared_valu(sh, x, S, D, h, L.h_ld, y, shared_row0, hint, st);
+            if (rc != COLI_OK) return rc;
+        }
+        StageTimer tcb(kStCombine, st);
+        return to_status(combine_launch(y, S, D, K, pair_row, w, sh ? 1 : 0, shared_row0, out,
+                                        (int)(al16(out) && al16(y) && D % 4 == 0), st));
+    }
     if (mm) {
         uint16_t *xf = reinterpret_cast<uint16_t *>(ws + L.xf);
         float *xsum = reinterpret_cast<float *>(ws + L.xsum);
@@ -351,10 +441,10 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
             a.n_work = n_work;
             a.out = h;
             a.ldo = L.h_ld;
+            a.out_vec4 = L.h_ld % 4 == 0 && al16(h);
             a.hf = hf;
             a.hf_stride = L.hf_stride;
             a.hf_rows = (int)kpF;
-            a.hf_fmt = ex->fmt;
             a.hsum = hsum;
             a.hsum_stride = max_gp * mm_pass_slots(bf16);
             {
@@ -403,6 +493,7 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
             d.n_work = n_work;
             d.out = y;
             d.ldo = D;
+            d.out_vec4 = D % 4 == 0 && al16(y);
             if (mm_launch(d, ex->fmt, 1, max_gp, st) != hipSuccess) return COLI_EDEVICE;
         }
         if (sh && !sh_mm) {

@@ -1,0 +1,57 @@
+// coli_dec.h -- host interface of the decode expert kernels (coli_dec.hip).
+#ifndef COLI_DEC_H
+#define COLI_DEC_H
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace coli {
+
+// Activation "row tables": one row per activation row, kpad elements (the
+// input width rounded up to 1024, zeros past it) stored as bf16 hi/lo pairs
+// in fragment order -- chunk c (8 elements) is the 32-byte run of its hi unit
+// and its lo unit, so a row is 4 * kpad bytes.
+inline int64_t dec_row_bytes(int64_t kpad) { return 4 * kpad; }
+
+// Groups, passes and work list as for the matrix-core kernels (coli_mfma.h):
+// the work list holds one entry g | pass << 11 per group-pass, a pass being up
+// to 8 rows of one group.
+struct DecArgs {
+    const uint8_t *w[2];
+    const float *s[2];
+    int64_t w_gstride, s_gstride;
+    int ngroups, O;
+    const uint8_t *xw[2];   // the extra (shared) group's matrices
+    const float *xs[2];
+    int has_extra, xO, x_rows, x_row0;
+    int I, kpad;
+    int64_t rb;
+    const int *offsets;
+    const int *row_pair;
+    int K;
+    // activation row of grouped row r: its token (row_pair[r] / K; the extra
+    // group's rows are tokens 0..x_rows-1) when act_by_token, else r itself
+    int act_by_token;
+    const uint16_t *act;     // row table of the activations
+    const int *work;
+    const int *n_work;
+    float *out;              // fp32 result rows (grouped row r at out + r * ldo)
+    int64_t ldo;
+    int out_vec4;            // out rows may be written with 16-byte stores
+    // M == 2 only: the result also written as the next product's row table
+    // (rows = grouped rows, kpad = hf_kpad, same weight format)
+    uint16_t *hf;
+    int hf_kpad;
+    int tiles;               // set by dec_launch
+};
+
+// x [rows, ldx] fp32 -> row table (rows x 4 kpad bytes) for weight format fmt.
+hipError_t xrows_launch(int fmt, const float *x, int64_t ldx, int rows, int I, int kpad,
+                        uint16_t *table, hipStream_t st);
+// M = 2: h = silu(gate . x) * (up . x); M = 1: y = down . h.
+hipError_t dec_launch(DecArgs a, int fmt, int M, int64_t max_group_passes, hipStream_t st);
+int dec_rows_per_block(int M);
+
+}  // namespace coli
+
+#endif

@@ -1,0 +1,442 @@
+// coli_dec.hip -- grouped expert products for decode batches on the bf16
+// matrix cores, fp32-level accuracy.
+//
+// The products of the pages' MoE block [glm.c@98759bf -- moe, phase D;
+// glm.c@97c756a -- expert_gate_up, matmul_i4_pair; metal@93cde63 --
+// moe_gemv, moe_silu]: for every expert (group) and the rows routed to it,
+//   gate/up:  h = silu(sg * (Vg x)) * (su * (Vu x))
+//   down:     y = sd * (Vd h)
+// with Vg, Vu, Vd the dequantised int8 / int4 / int2 weights.
+//
+// Layout of the work:
+//   * a pass is up to 8 rows of one group; row t of the pass takes MFMA
+//     columns 2t (bf16 hi of its activations) and 2t+1 (bf16 lo), so the
+//     16-column tile carries fp32-accurate activations (|x - hi - lo| <=
+//     2^-16 |x|);
+//   * activations come from "row tables" (coli_dec.h): one row per
+//     activation row, in fragment order; a lane reads the 16-byte unit of its
+//     own column straight from global memory (L2), so the waves of a block
+//     never synchronise;
+//   * sum(x) per column, needed to remove OFF * sum(x) from the code
+//     products, is one more MFMA per step against a tile of ones, over the
+//     very bf16 values the products use;
+//   * an item is (group-pass, 128-row tile) for gate/up (32 rows per wave),
+//     (group-pass, 256-row tile) for down (64 rows per wave); the items of
+//     a contiguous run of group-passes go to one XCD (passes of one group
+//     run there together, so later passes find the weights in its L2),
+//     persistent blocks walk them in order, and each wave loads the next
+//     k-block's weights while it multiplies the current one, and the next
+//     item's first k-block during the current item's last.
+#include "coli_device.h"
+#include "coli_frag.h"
+#include "coli_dec.h"
+
+namespace coli {
+
+namespace {
+
+constexpr int kDecWaves = 4;
+constexpr int kDecXcds = 8;
+constexpr int kDecTpp = 8;   // rows per pass
+template <int M> struct DecTiles { static constexpr int MT = M == 2 ? 2 : 4; };
+
+// ---------------------------------------------------------------- row tables
+// Block (row, part): runs of RUN consecutive elements (8: one chunk; int2
+// 16: the chunks of an even/odd step pair) split into bf16 hi/lo and stored
+// as the chunk's two 16-byte units.  Elements past I are zeros.
+template <int FMT>
+__global__ __launch_bounds__(256) void k_xrows(const float *__restrict__ x, int64_t ldx, int I,
+                                               int kpad, uint16_t *__restrict__ table, int vec)
+{
+    constexpr int RUN = FMT == kI2 ? 16 : 8;
+    const int row = blockIdx.x;
+    const float *xr = x + (int64_t)row * ldx;
+    uint16_t *dst = table + (int64_t)row * 2 * kpad;
+    const int nruns = kpad / RUN;
+    for (int r = blockIdx.y * 256 + threadIdx.x; r < nruns; r += gridDim.y * 256) {
+        const int e0 = r * RUN;
+        float v[RUN];
+        if (vec && e0 + RUN <= I) {
+#pragma unroll
+            for (int i = 0; i < RUN / 4; ++i) {
+                const float4 f = *reinterpret_cast<const float4 *>(xr + e0 + 4 * i);
+                v[4 * i] = f.x;
+                v[4 * i + 1] = f.y;
+                v[4 * i + 2] = f.z;
+                v[4 * i + 3] = f.w;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < RUN; ++i) v[i] = e0 + i < I ? xr[e0 + i] : 0.f;
+        }
+        uint16_t hv[RUN], lv[RUN];
+#pragma unroll
+        for (int i = 0; i < RUN; ++i) {
+            hv[i] = bf16_rne(v[i]);
+            lv[i] = bf16_rne(v[i] - bf16_f(hv[i]));
+        }
+        // slot pairs (2m, 2m+1) of each chunk, in the order the unpacking
+        // produces the weight codes
+        int c, j;
+        pos_of<FMT>(e0, c, j);
+        uint32_t hw[RUN / 2], lw[RUN / 2];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            int k0, k1;
+            if constexpr (FMT == kI8) { k0 = 2 * m; k1 = 2 * m + 1; }
+            else if constexpr (FMT == kI4) { k0 = m; k1 = m + 4; }
+            else { k0 = m; k1 = m + 8; }
+            hw[m] = (uint32_t)hv[k0] | ((uint32_t)hv[k1] << 16);
+            lw[m] = (uint32_t)lv[k0] | ((uint32_t)lv[k1] << 16);
+            if constexpr (FMT == kI2) {
+                hw[4 + m] = (uint32_t)hv[m + 4] | ((uint32_t)hv[m + 12] << 16);
+                lw[4 + m] = (uint32_t)lv[m + 4] | ((uint32_t)lv[m + 12] << 16);
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < RUN / 8; ++h) {
+            uint16_t *u = dst + (int64_t)(c + 4 * h) * 16;   // chunk c + 4h: next MFMA step
+            *reinterpret_cast<uint4 *>(u) = make_uint4(hw[4 * h], hw[4 * h + 1], hw[4 * h + 2], hw[4 * h + 3]);
+            *reinterpret_cast<uint4 *>(u + 8) = make_uint4(lw[4 * h], lw[4 * h + 1], lw[4 * h + 2], lw[4 * h + 3]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- products
+template <int FMT, int M>
+__global__ __launch_bounds__(256) void k_dec(DecArgs a)
+{
+    using T = MF<FMT>;
+    constexpr int STEPS = T::STEPS, KB = T::KB, SEGS = T::SEGS, BITS = T::BITS, SPS = T::SPS;
+    constexpr int MT = DecTiles<M>::MT, RPW = 16 * MT, RPB = kDecWaves * RPW;
+    constexpr float OFF = T::OFF;
+    constexpr uint32_t kChunkStep = 4 * 32;   // bytes between one step's chunks and the next's
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 15, q = lane >> 4, lrow = lane >> 2, lchunk = lane & 3;
+    const int src4 = 4 * (4 * col + q);
+    const int xcd = blockIdx.x % kDecXcds, lb = blockIdx.x / kDecXcds;
+    const int bpx = gridDim.x / kDecXcds;               // grid is a multiple of 8
+    const int n_gp = cload(a.n_work);
+    const int gp_lo = (int)((int64_t)n_gp * xcd / kDecXcds);
+    const int gp_cnt = (int)((int64_t)n_gp * (xcd + 1) / kDecXcds) - gp_lo;
+    const int n_items = gp_cnt * a.tiles;
+    if (lb >= n_items) return;
+    const int nkb = a.kpad / KB;                        // even and >= 4 (kpad: multiple of 1024)
+    constexpr uint32_t kbytes = KB * BITS / 8;
+    // a lane's 16-byte segment past the row end is clamped to the row's last
+    // one (it meets zero activations)
+    const uint32_t last_seg = (uint32_t)(a.rb - 16 - 16 * lchunk);
+    const uint8_t *actb = reinterpret_cast<const uint8_t *>(a.act);
+    const uint32_t arow = (uint32_t)(4 * a.kpad);       // bytes per row-table row
+
+    struct It {
+        int gp, tile, nt, r0t, Og;
+        const uint8_t *wb[M];
+        const float *sc[M];
+        uint32_t roff[MT];   // this lane's row (clamped) * rb + its 16-byte chunk
+        uint32_t boff;       // this lane's unit in its activation row (bytes)
+    };
+    auto make = [&](It &c, int it) {
+        c.gp = __builtin_amdgcn_readfirstlane(gp_lo + it / a.tiles);
+        c.tile = __builtin_amdgcn_readfirstlane(it % a.tiles);
+        const int wv = cload(a.work + c.gp);
+        const int g = wv & 0x7FF, pass = wv >> 11;
+        const bool extra = a.has_extra && g == a.ngroups;
+        int r0, cnt;
+        if (extra) {
+            r0 = a.x_row0;
+            cnt = a.x_rows;
+        } else {
+            r0 = cload(a.offsets + g);
+            cnt = cload(a.offsets + g + 1) - r0;
+        }
+        c.nt = min(kDecTpp, cnt - pass * kDecTpp);
+        c.r0t = r0 + pass * kDecTpp;
+        if (extra) {
+            c.Og = a.xO;
+#pragma unroll
+            for (int m = 0; m < M; ++m) { c.wb[m] = a.xw[m]; c.sc[m] = a.xs[m]; }
+        } else {
+            c.Og = a.O;
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                c.wb[m] = a.w[m] + (int64_t)g * a.w_gstride;
+                c.sc[m] = a.s[m] + (int64_t)g * a.s_gstride;
+            }
+        }
+        const int obase = c.tile * RPB + wave * RPW;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            c.roff[mt] = (uint32_t)(min(obase + 16 * mt + lrow, c.Og - 1) * a.rb) + 16 * lchunk;
+        // activation row of each pass row, from scalar loads (dead columns
+        // repeat the last live row; their results are never stored)
+        const int t = col >> 1;
+        int ar = 0;
+#pragma unroll
+        for (int u = 0; u < kDecTpp; ++u) {
+            const int gr = c.r0t + min(u, c.nt - 1);
+            int au;
+            if (!a.act_by_token) au = gr;
+            else if (extra) au = gr - a.x_row0;
+            else au = cload(a.row_pair + gr) / a.K;
+            ar = t == u ? au : ar;
+        }
+        c.boff = (uint32_t)ar * arow + 32 * q + 16 * (col & 1);
+    };
+    auto loadW = [&](const It &c, int kbi, uint4 (&w)[M][MT][SEGS]) {
+        const uint32_t b0 = (uint32_t)kbi * kbytes;
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int sg = 0; sg < SEGS; ++sg)
+                    w[m][mt][sg] = gload16(c.wb[m] + (c.roff[mt] + min(b0 + 64 * sg, last_seg)));
+    };
+    auto loadB = [&](const It &c, int kbi, uint4 (&b)[STEPS]) {
+        const uint32_t o = c.boff + (uint32_t)kbi * (STEPS * kChunkStep);
+#pragma unroll
+        for (int s = 0; s < STEPS; ++s) b[s] = gload16(actb + (o + s * kChunkStep));
+    };
+
+    floatx4 acc[M][MT], accs;
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[m][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    accs = floatx4{0.f, 0.f, 0.f, 0.f};
+    const uint32_t one2 = opaque_v(0x3F803F80u);       // bf16 (1, 1)
+    const uint4 ones = make_uint4(one2, one2, one2, one2);
+
+    // one k-block: weights moved into the operand layout in place (lane
+    // (q, col) gets row col, chunk q, from lane 4 col + q), then per MFMA
+    // step the M x MT code products and the column sums
+    auto compute = [&](uint4 (&w)[M][MT][SEGS], const uint4 (&b)[STEPS]) {
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int sg = 0; sg < SEGS; ++sg) {
+                    const uint4 v = w[m][mt][sg];
+                    w[m][mt][sg] = make_uint4((uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)v.x),
+                                              (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)v.y),
+                                              (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)v.z),
+                                              (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)v.w));
+                }
+#pragma unroll
+        for (int s2 = 0; s2 < STEPS; ++s2) {
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    acc[m][mt] = mfma(codes<FMT>(w[m][mt][s2 / SPS], s2 % SPS), b[s2], acc[m][mt]);
+            accs = mfma(ones, b[s2], accs);
+        }
+    };
+
+    float sreg[M][MT][4];
+    auto load_epi = [&](const It &c) {
+        const int obase = c.tile * RPB + wave * RPW;
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    sreg[m][mt][r] = gloadf(c.sc[m] + min(obase + 16 * mt + 4 * q + r, c.Og - 1));
+    };
+    // D[4q + r][col] of tile (m, mt); the lo column is added to the hi one
+    auto epilogue = [&](const It &c) {
+        const int obase = c.tile * RPB + wave * RPW;
+        const int tok = col >> 1;
+        const bool live = tok < c.nt;
+        const float xs = accs[0] + __shfl_xor(accs[0], 1, kWave);   // sum of hi + lo over k
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            float v[M][4];
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[m][r] = acc[m][mt][r] + __shfl_xor(acc[m][mt][r], 1, kWave);
+            const int ob = obase + 16 * mt + 4 * q;
+            float res[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float y = sreg[0][mt][r] * (v[0][r] - OFF * xs);
+                if constexpr (M == 2) {
+                    const float u = sreg[1][mt][r] * (v[1][r] - OFF * xs);
+                    y = silu_f(y) * u;
+                }
+                res[r] = ob + r < c.Og ? y : 0.f;
+            }
+            if (live && (col & 1) == 0) {
+                float *op = a.out + (int64_t)(c.r0t + tok) * a.ldo;
+                if (a.out_vec4 && ob + 3 < c.Og) {
+                    *reinterpret_cast<float4 *>(op + ob) = make_float4(res[0], res[1], res[2], res[3]);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (ob + r < c.Og) op[ob + r] = res[r];
+                }
+            }
+            if constexpr (M == 2) {
+                if (a.hf) {
+                    // h as the down product's row table: this lane's 4
+                    // outputs are half of one unit (8 slots of a chunk), the
+                    // partner lane (q ^ 1, int2: q ^ 2) holds the other half,
+                    // and the lower lane of the pair stores the unit; even
+                    // columns store hi units, odd columns lo units
+                    constexpr int PX = FMT == kI2 ? 32 : 16;
+                    const bool lowq = FMT == kI2 ? q < 2 : (q & 1) == 0;
+                    uint32_t hv[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const uint16_t h16 = bf16_rne(res[r]);
+                        hv[r] = (col & 1) ? bf16_rne(res[r] - bf16_f(h16)) : h16;
+                    }
+                    uint32_t pv[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) pv[r] = (uint32_t)__shfl_xor((int)hv[r], PX, kWave);
+                    if (lowq && live && ob < a.hf_kpad) {
+                        int cc, j;
+                        pos_of<FMT>(ob, cc, j);
+                        uint4 u;
+                        if constexpr (FMT == kI8)
+                            u = make_uint4(hv[0] | hv[1] << 16, hv[2] | hv[3] << 16,
+                                           pv[0] | pv[1] << 16, pv[2] | pv[3] << 16);
+                        else
+                            u = make_uint4(hv[0] | pv[0] << 16, hv[1] | pv[1] << 16,
+                                           hv[2] | pv[2] << 16, hv[3] | pv[3] << 16);
+                        *reinterpret_cast<uint4 *>(a.hf + (int64_t)(c.r0t + tok) * 2 * a.hf_kpad +
+                                                   (int64_t)(2 * cc + (col & 1)) * 8) = u;
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[m][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        accs = floatx4{0.f, 0.f, 0.f, 0.f};
+    };
+
+    // Every load below is issued unconditionally (selected sources), so the
+    // compiler's waits count them exactly: each product waits only for its
+    // own k-block, with the next k-block's weights in flight.
+    It cur;
+    make(cur, lb);
+    int jn = lb + bpx;
+    uint4 wA[M][MT][SEGS], wB[M][MT][SEGS], bb[STEPS];
+    loadW(cur, 0, wA);
+    for (;;) {
+        for (int k = 0; k < nkb - 2; k += 2) {
+            loadB(cur, k, bb);
+            loadW(cur, k + 1, wB);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(wA, bb);
+            __builtin_amdgcn_sched_barrier(0);
+            loadB(cur, k + 1, bb);
+            loadW(cur, k + 2, wA);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(wB, bb);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // last two k-blocks: the epilogue's scales, then the next item's
+        // first k-block (a copy of this item's when there is none)
+        const bool has_nxt = jn < n_items;
+        It nxt = cur;
+        if (has_nxt) make(nxt, jn);
+        load_epi(cur);
+        loadB(cur, nkb - 2, bb);
+        loadW(cur, nkb - 1, wB);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(wA, bb);
+        __builtin_amdgcn_sched_barrier(0);
+        loadB(cur, nkb - 1, bb);
+        loadW(nxt, 0, wA);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(wB, bb);
+        __builtin_amdgcn_sched_barrier(0);
+        epilogue(cur);
+        if (!has_nxt) break;
+        cur = nxt;
+        jn += bpx;
+    }
+}
+
+int dec_resident_blocks(const void *kern, int *cache)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] > 0) return cache[dev];
+    int cus = 0, per = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kern, 256, 0) != hipSuccess || per <= 0)
+        per = 1;
+    cache[dev] = cus * per;
+    return cache[dev];
+}
+
+template <int FMT, int M>
+hipError_t launch_dec(const DecArgs &a, int64_t items, hipStream_t st)
+{
+    static int cache[64] = {0};
+    const void *kern = (const void *)k_dec<FMT, M>;
+    int64_t cap = dec_resident_blocks(kern, cache) / kDecXcds * kDecXcds;
+    if (cap < kDecXcds) cap = kDecXcds;
+    int64_t grid = (items + kDecXcds - 1) / kDecXcds * kDecXcds;
+    if (grid > cap) grid = cap;
+    if (grid < kDecXcds) grid = kDecXcds;
+    hipLaunchKernelGGL((k_dec<FMT, M>), dim3((unsigned)grid), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int dec_rows_per_block(int M) { return kDecWaves * 16 * (M == 2 ? DecTiles<2>::MT : DecTiles<1>::MT); }
+
+hipError_t xrows_launch(int fmt, const float *x, int64_t ldx, int rows, int I, int kpad,
+                        uint16_t *table, hipStream_t st)
+{
+    if (rows <= 0) return hipSuccess;
+    const int run = fmt == kI2 ? 16 : 8;
+    const int parts = (kpad / run + 255) / 256;
+    const dim3 g((unsigned)rows, (unsigned)parts);
+    const int vec = ldx % 4 == 0 && ((uintptr_t)x & 15u) == 0;
+    switch (fmt) {
+    case kI8: hipLaunchKernelGGL(k_xrows<kI8>, g, dim3(256), 0, st, x, ldx, I, kpad, table, vec); break;
+    case kI4: hipLaunchKernelGGL(k_xrows<kI4>, g, dim3(256), 0, st, x, ldx, I, kpad, table, vec); break;
+    case kI2: hipLaunchKernelGGL(k_xrows<kI2>, g, dim3(256), 0, st, x, ldx, I, kpad, table, vec); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t dec_launch(DecArgs a, int fmt, int M, int64_t max_group_passes, hipStream_t st)
+{
+    int Ocover = a.O;
+    if (M == 2 && a.hf && a.hf_kpad > Ocover) Ocover = a.hf_kpad;
+    if (a.has_extra && a.xO > Ocover) Ocover = a.xO;
+    const int rpb = dec_rows_per_block(M);
+    a.tiles = (Ocover + rpb - 1) / rpb;
+    const int64_t items = max_group_passes * a.tiles;
+    if (M == 2) {
+        switch (fmt) {
+        case kI8: return launch_dec<kI8, 2>(a, items, st);
+        case kI4: return launch_dec<kI4, 2>(a, items, st);
+        case kI2: return launch_dec<kI2, 2>(a, items, st);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    switch (fmt) {
+    case kI8: return launch_dec<kI8, 1>(a, items, st);
+    case kI4: return launch_dec<kI4, 1>(a, items, st);
+    case kI2: return launch_dec<kI2, 1>(a, items, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace coli

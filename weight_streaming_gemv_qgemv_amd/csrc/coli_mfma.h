@@ -29,17 +29,18 @@ struct MmArgs {
     uint16_t *xf;
     int64_t xf_stride;
     float *xsum;         // [group-pass * 16 + token] sum(hi + lo) of the activations
-    int tpp;             // rows per pass: 8 (fp32, hi/lo) or 16 (bf16)
+    int tpp;             // rows per pass: 8 (fp32, hi/lo) or 32 (bf16)
     int bf16;            // activations rounded once to bf16 (no lo part)
     const int *work;     // (g | pass << 11) per group-pass, NULL = one group
     const int *n_work;
     float *out;
     int64_t ldo;
+    int out_vec4;        // out rows may be written with 16-byte stores
     // M == 2 only: the result also prepared as the next product's activations
     uint16_t *hf;
     int64_t hf_stride;
-    int hf_rows;         // outputs written per token (zeros past O), = next kpad
-    int hf_fmt;          // weight format of the next product
+    int hf_rows;         // outputs written per token (zeros past O), = next kpad;
+                         // laid out for a product of the same weight format
     float *hsum;         // [tiles][hsum_stride] partial sums per pass * 16 + token
     int64_t hsum_stride;
     int tiles;           // set by mm_launch

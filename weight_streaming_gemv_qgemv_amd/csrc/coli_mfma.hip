@@ -23,117 +23,18 @@
 //     activation rows are fetched into one L2.
 #include "coli_device.h"
 #include "coli_internal.h"
+#include "coli_frag.h"
 #include "coli_mfma.h"
 
 namespace coli {
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-
 constexpr int kWavesPerBlock = 4;
 // Row tiles of 16 per wave: 2, except for the paired gate/up product with
 // two-N-tile passes, where 1 keeps the register footprint of the others.
 template <int M, int NT> struct RowTiles { static constexpr int MT = (M == 2 && NT == 2) ? 1 : 2; };
 constexpr int kXcds = 8;
-
-template <int FMT> struct MF;
-// A k-block of one weight row is SEGS x 64 bytes: lane group q (= lane / 16)
-// reads 16-byte segment sg at byte 64 sg + 16 q, so one load instruction
-// covers 64 contiguous bytes of each of its 16 rows and the SEGS = 2 loads of
-// a k-block consume whole 128-byte lines.  SPS: 8-element MFMA steps per
-// segment; STEPS = SEGS * SPS; KB: elements per k-block; OFF: code - value.
-template <> struct MF<kI8> { static constexpr int BITS = 8, SEGS = 2, SPS = 2, STEPS = 4, KB = 128; static constexpr float OFF = 128.f; };
-template <> struct MF<kI4> { static constexpr int BITS = 4, SEGS = 2, SPS = 4, STEPS = 8, KB = 256; static constexpr float OFF = 136.f; };
-template <> struct MF<kI2> { static constexpr int BITS = 2, SEGS = 1, SPS = 8, STEPS = 8, KB = 256; static constexpr float OFF = 130.f; };
-
-__device__ __forceinline__ uint32_t wsel(const uint4 &v, int d)
-{
-    return d == 0 ? v.x : d == 1 ? v.y : d == 2 ? v.z : v.w;
-}
-
-// Constants hidden from constant folding (an empty asm statement emits no
-// instruction): with the mask in a scalar register and the exponent pattern
-// in a vector register, (a & m) | o becomes one v_and_or_b32 -- with literal
-// operands it would be an AND and an OR.
-__device__ __forceinline__ uint32_t opaque_s(uint32_t v)
-{
-    asm("" : "+s"(v));
-    return v;
-}
-__device__ __forceinline__ uint32_t opaque_v(uint32_t v)
-{
-    asm("" : "+v"(v));
-    return v;
-}
-
-// bf16 codes for MFMA step s (8 elements) of a 16-byte segment.
-template <int FMT> __device__ __forceinline__ uint4 codes(const uint4 &w, int s);
-
-// int4: word s holds nibbles n0..n7; the pairs (n_i, n_i+4) sit at bits
-// 4i and 4i+16, so (word >> 4i) & 0x000F000F | 0x43004300 is the bf16 pair
-// (128 + n_i, 128 + n_i+4).  Slot order [0,4,1,5,2,6,3,7].
-template <> __device__ __forceinline__ uint4 codes<kI4>(const uint4 &w, int s)
-{
-    const uint32_t u = wsel(w, s);
-    const uint32_t m = opaque_s(0x000F000Fu), e = opaque_v(0x43004300u);
-    return make_uint4((u & m) | e, ((u >> 4) & m) | e, ((u >> 8) & m) | e, ((u >> 12) & m) | e);
-}
-
-// int2: word s/2 holds crumbs c0..c15; (word >> 2k) & 0x00030003 | 0x43004300
-// is the pair (128 + c_k, 128 + c_k+8).  Step s covers k = 4(s&1) .. +3.
-// Slot order [0,8,1,9,2,10,3,11 | 4,12,5,13,6,14,7,15].
-template <> __device__ __forceinline__ uint4 codes<kI2>(const uint4 &w, int s)
-{
-    const uint32_t u = wsel(w, s >> 1);
-    const int k0 = 4 * (s & 1);
-    const uint32_t m = opaque_s(0x00030003u), e = opaque_v(0x43004300u);
-    return make_uint4(((u >> (2 * k0)) & m) | e, ((u >> (2 * k0 + 2)) & m) | e,
-                      ((u >> (2 * k0 + 4)) & m) | e, ((u >> (2 * k0 + 6)) & m) | e);
-}
-
-// int8: bytes 8s..8s+7, sign bit flipped (code = v + 128 in 0..255, exact
-// in bf16: the fp32 value's low half is zero), natural order.
-__device__ __forceinline__ uint32_t bf_pair_of_bytes(uint32_t b, int k)
-{
-    const uint32_t f0 = __float_as_uint((float)((b >> (8 * k)) & 0xFFu));
-    const uint32_t f1 = __float_as_uint((float)((b >> (8 * k + 8)) & 0xFFu));
-    return __builtin_amdgcn_perm(f1, f0, 0x07060302u);
-}
-template <> __device__ __forceinline__ uint4 codes<kI8>(const uint4 &w, int s)
-{
-    const uint32_t b0 = wsel(w, 2 * s) ^ 0x80808080u, b1 = wsel(w, 2 * s + 1) ^ 0x80808080u;
-    return make_uint4(bf_pair_of_bytes(b0, 0), bf_pair_of_bytes(b0, 2), bf_pair_of_bytes(b1, 0),
-                      bf_pair_of_bytes(b1, 2));
-}
-
-__device__ __forceinline__ uint16_t bf16_rne(float f)
-{
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
-__device__ __forceinline__ float bf16_f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
-
-// Loads through the global address space: a flat load counts on both the
-// vector-memory and the LDS counters and may return out of order, which makes
-// the compiler wait for every outstanding load before the first use.
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(1))) const u32x4 g_u32x4;
-typedef __attribute__((address_space(1))) const float g_float;
-__device__ __forceinline__ uint4 gload16(const void *p)
-{
-    const u32x4 v = *(g_u32x4 *)p;
-    return make_uint4(v.x, v.y, v.z, v.w);
-}
-__device__ __forceinline__ float gloadf(const float *p) { return *(g_float *)p; }
-
-__device__ __forceinline__ floatx4 mfma(const uint4 &a, const uint4 &b, floatx4 c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
 
 // ---------------------------------------------------------------- layout
 // Work is cut into passes of activation rows ("tokens") of one group, of
@@ -149,54 +50,6 @@ __device__ __forceinline__ floatx4 mfma(const uint4 &a, const uint4 &b, floatx4 
 // Element e of the product's input sits in chunk c, slot j = pos_of(e).
 static_assert(2 * COLI_MM_TPP_FP32 == 16 && COLI_MM_TPP_BF16 == 32, "pass widths: 1 and 2 N-tiles");
 constexpr int nt_of(int bf16) { return bf16 ? 2 : 1; }
-
-template <int FMT> __device__ __forceinline__ int elem_of(int kbi, int s, int q, int j)
-{
-    using T = MF<FMT>;
-    const int sg = s / T::SPS, sub = s % T::SPS;
-    const int first = kbi * T::KB + (64 * sg + 16 * q) * 8 / T::BITS;
-    if constexpr (FMT == kI4) return first + 8 * sub + (j >> 1) + 4 * (j & 1);
-    if constexpr (FMT == kI8) return first + 8 * sub + j;
-    return first + 16 * (sub >> 1) + 4 * (sub & 1) + (j >> 1) + 8 * (j & 1);
-}
-
-template <int FMT> __device__ __forceinline__ void pos_of(int e, int &c, int &j)
-{
-    using T = MF<FMT>;
-    const int kbi = e / T::KB, r = e % T::KB;
-    const int byte = r * T::BITS / 8;
-    const int sg = byte / 64, q = (byte % 64) / 16;
-    const int u = r - (64 * sg + 16 * q) * 8 / T::BITS;   // element inside the 16-byte segment
-    int sub;
-    if constexpr (FMT == kI4) {
-        sub = u >> 3;
-        const int v = u & 7;
-        j = 2 * (v & 3) + (v >> 2);
-    } else if constexpr (FMT == kI8) {
-        sub = u >> 3;
-        j = u & 7;
-    } else {
-        const int uu = u & 15, k = uu & 7;
-        sub = 2 * (u >> 4) + (k >> 2);
-        j = 2 * (k & 3) + (uu >> 3);
-    }
-    c = (kbi * T::STEPS + sg * T::SPS + sub) * 4 + q;
-}
-
-__device__ __forceinline__ void pos_any(int fmt, int e, int &c, int &j)
-{
-    if (fmt == kI4) pos_of<kI4>(e, c, j);
-    else if (fmt == kI2) pos_of<kI2>(e, c, j);
-    else pos_of<kI8>(e, c, j);
-}
-
-// Work-list and group-offset reads: written by an earlier kernel and never
-// written here, so they are read through the constant address space (scalar
-// loads) when the index is uniform.
-__device__ __forceinline__ int cload(const int *p)
-{
-    return *(__attribute__((address_space(4))) const int *)p;
-}
 
 // Group-pass decode shared by the prep and the product kernels (gp uniform).
 struct GP {
@@ -425,7 +278,11 @@ __global__ __launch_bounds__(256) void k_mm(MmArgs a)
     const int xcd = blockIdx.x % kXcds, lb = blockIdx.x / kXcds;
     const int bpx = gridDim.x / kXcds;                 // blocks per XCD (grid is a multiple of 8)
     const int n_gp = n_group_passes(a);
-    const int gp_per_xcd = (n_gp + kXcds - 1 - xcd) / kXcds;   // group-passes gp = xcd + 8 i
+    // XCD x takes the contiguous run of group-passes [gp_lo, gp_hi): the
+    // passes of one group are adjacent, so they run on the same XCD at about
+    // the same time and the later passes find the weights in its L2
+    const int gp_lo = (int)((int64_t)n_gp * xcd / kXcds);
+    const int gp_per_xcd = (int)((int64_t)n_gp * (xcd + 1) / kXcds) - gp_lo;
     const int n_items = gp_per_xcd * a.tiles;
     const int nkb = a.kpad / KB;                       // >= 4: kpad is a multiple of 1024
     if (lb >= n_items) return;                         // whole block, before any barrier
@@ -437,7 +294,7 @@ __global__ __launch_bounds__(256) void k_mm(MmArgs a)
     using It = Item<M, MT, UMAX>;
     auto make = [&](It &c, int it) {
         // uniform: the work-list and offset lookups below are scalar loads
-        c.gp = __builtin_amdgcn_readfirstlane(xcd + kXcds * (it / a.tiles));
+        c.gp = __builtin_amdgcn_readfirstlane(gp_lo + it / a.tiles);
         c.tile = __builtin_amdgcn_readfirstlane(it % a.tiles);
         const GP d = decode_gp(a, c.gp);
         c.nt = d.nt;
@@ -566,29 +423,49 @@ __global__ __launch_bounds__(256) void k_mm(MmArgs a)
                 }
                 if (writer) {
                     float *op = a.out + (int64_t)(c.row0 + tok) * a.ldo;
+                    if (a.out_vec4 && ob + 3 < c.Og) {
+                        *reinterpret_cast<float4 *>(op + ob) = make_float4(res[0], res[1], res[2], res[3]);
+                    } else {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (ob + r < c.Og) op[ob + r] = res[r];
-                    if constexpr (M == 2) {
-                        if (a.hf) {
-                            uint16_t *hb = a.hf + (int64_t)c.gp * a.hf_stride + (a.bf16 ? tok : 2 * tok) * 8;
+                        for (int r = 0; r < 4; ++r)
+                            if (ob + r < c.Og) op[ob + r] = res[r];
+                    }
+                }
+                if constexpr (M == 2) {
+                    if (a.hf) {
+                        // h as the down product's activations: this lane's 4
+                        // outputs are half of one 16-byte unit (8 slots of one
+                        // chunk and column), the partner lane (q ^ 1, or q ^ 2
+                        // for int2) holds the other half; the lower lane of
+                        // the pair stores the whole unit.  Column 16 n + col:
+                        // bf16 hi (even col) or lo (odd col) in fp32 precision.
+                        constexpr int PX = FMT == kI2 ? 32 : 16;
+                        const bool lowq = FMT == kI2 ? q < 2 : (q & 1) == 0;
+                        const bool lo_col = !a.bf16 && (col & 1);
+                        uint32_t hv[4];
 #pragma unroll
-                            for (int r = 0; r < 4; ++r) {
-                                const int o = ob + r;
-                                if (o < a.hf_rows) {
-                                    const uint16_t hv = bf16_rne(res[r]);
-                                    int cc, j;
-                                    pos_any(a.hf_fmt, o, cc, j);
-                                    hb[(int64_t)cc * kCols * 8 + j] = hv;
-                                    if (a.bf16) {
-                                        hpart[n] += bf16_f(hv);
-                                    } else {
-                                        const uint16_t lv = bf16_rne(res[r] - bf16_f(hv));
-                                        hb[(int64_t)cc * kCols * 8 + 8 + j] = lv;
-                                        hpart[n] += bf16_f(hv) + bf16_f(lv);
-                                    }
-                                }
-                            }
+                        for (int r = 0; r < 4; ++r) {
+                            const uint16_t h16 = bf16_rne(res[r]);
+                            const uint16_t l16 = bf16_rne(res[r] - bf16_f(h16));
+                            if (writer && ob + r < a.hf_rows)
+                                hpart[n] += a.bf16 ? bf16_f(h16) : bf16_f(h16) + bf16_f(l16);
+                            hv[r] = lo_col ? l16 : h16;
+                        }
+                        uint32_t pv[4];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) pv[r] = (uint32_t)__shfl_xor((int)hv[r], PX, kWave);
+                        if (lowq && tok < c.nt && ob < a.hf_rows) {
+                            int cc, j;
+                            pos_of<FMT>(ob, cc, j);
+                            uint4 u;
+                            if constexpr (FMT == kI8)
+                                u = make_uint4(hv[0] | hv[1] << 16, hv[2] | hv[3] << 16,
+                                               pv[0] | pv[1] << 16, pv[2] | pv[3] << 16);
+                            else
+                                u = make_uint4(hv[0] | pv[0] << 16, hv[1] | pv[1] << 16,
+                                               hv[2] | pv[2] << 16, hv[3] | pv[3] << 16);
+                            *reinterpret_cast<uint4 *>(a.hf + (int64_t)c.gp * a.hf_stride +
+                                                       ((int64_t)cc * kCols + 16 * n + col) * 8) = u;
                         }
                     }
                 }

@@ -167,20 +167,33 @@ int coli_moe_workspace_layout(int S, int K, int E, int D, int F, int F_shared,
     const int bf16 = prec == COLI_PREC_BF16;
     const int64_t tpp = bf16 ? COLI_MM_TPP_BF16 : COLI_MM_TPP_FP32, cols = bf16 ? 32 : 16;
     int64_t ngp = (rows + tpp - 1) / tpp + (int64_t)E + 1;   /* passes */
-    int64_t KpD = round_up(D, 1024), KpF = round_up(Fmax, 1024), tilesF = KpF / (bf16 ? 64 : 128);
-    if (!mul_ok(ngp, 2 * cols * KpD, &t)) return COLI_ESHAPE;
-    REGION(xf, t);
-    REGION(xsum, ngp * cols * 4);
-    if (!mul_ok(ngp, 2 * cols * KpF, &t)) return COLI_ESHAPE;
-    REGION(hf, t);
-    if (!mul_ok(tilesF * ngp, cols * 4, &t)) return COLI_ESHAPE;
-    REGION(hsum, t);
+    int64_t KpD = round_up(D, 1024), KpF = round_up(Fmax, 1024), tilesF = KpF / 64;
+    if (bf16) {
+        /* bf16 precision: per pass, its rows' activations fragment-major
+         * (32 columns), the same for the SwiGLU output, and their sums */
+        if (!mul_ok(ngp, 2 * cols * KpD, &t)) return COLI_ESHAPE;
+        REGION(xf, t);
+        REGION(xsum, ngp * cols * 4);
+        if (!mul_ok(ngp, 2 * cols * KpF, &t)) return COLI_ESHAPE;
+        REGION(hf, t);
+        if (!mul_ok(tilesF * ngp, cols * 4, &t)) return COLI_ESHAPE;
+        REGION(hsum, t);
+    } else {
+        /* fp32 precision: one row table per token (x) and per grouped row
+         * (the SwiGLU output), bf16 hi/lo pairs in fragment order */
+        if (!mul_ok((int64_t)S, 4 * KpD, &t)) return COLI_ESHAPE;
+        REGION(xf, t);
+        REGION(xsum, 0);
+        if (!mul_ok(rows, 4 * KpF, &t)) return COLI_ESHAPE;
+        REGION(hf, t);
+        REGION(hsum, 0);
+    }
     REGION(work, (ngp + 1) * 4);
     REGION(n_work, 64);
 #undef REGION
     out->n_pass_max = ngp;
-    out->xf_stride = cols * KpD;
-    out->hf_stride = cols * KpF;
+    out->xf_stride = bf16 ? cols * KpD : 2 * KpD;
+    out->hf_stride = bf16 ? cols * KpF : 2 * KpF;
     out->h_ld = Fmax;
     out->total = off;
     return COLI_OK;
