@@ -15,6 +15,7 @@
 #include "coli_device.h"
 #include "coli_gemv.h"
 #include "coli_mfma.h"
+#include "coli_qmv.h"
 #include "coli_internal.h"
 #include "coli_router.h"
 #include "coli_stages.h"
@@ -633,6 +634,20 @@ extern "C" int coli_qgemv(int fmt, const void *W, const float *scale, const floa
     if (rc != COLI_OK) return rc;
     if (S == 0 || O == 0) return COLI_OK;
     const int64_t rb = coli_row_bytes(fmt, I);
+    if (qmv_supported(fmt, rb, I, O, W, x)) {
+        // matrix cores: whole 16-byte row segments, aligned operands
+        QmvArgs q = {};
+        q.W = (const uint8_t *)W;
+        q.scale = scale;
+        q.x = x;
+        q.y = y;
+        q.S = S;
+        q.I = I;
+        q.O = O;
+        q.rb = rb;
+        StageTimer t(kStQgemv, (hipStream_t)stream);
+        return to_status(qmv_launch(q, fmt, (hipStream_t)stream));
+    }
     GemvArgs a = {};
     a.w[0] = (const uint8_t *)W;
     a.s[0] = scale;

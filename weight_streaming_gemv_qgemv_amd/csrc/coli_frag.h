@@ -111,6 +111,13 @@ __device__ __forceinline__ uint4 gload16(const void *p)
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 __device__ __forceinline__ float gloadf(const float *p) { return *(g_float *)p; }
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const f32x4 g_f32x4;
+__device__ __forceinline__ float4 gload4f(const float *p)
+{
+    const f32x4 v = *(g_f32x4 *)p;
+    return make_float4(v.x, v.y, v.z, v.w);
+}
 
 __device__ __forceinline__ floatx4 mfma(const uint4 &a, const uint4 &b, floatx4 c)
 {

@@ -1,0 +1,28 @@
+// coli_qmv.h -- host interface of the dense matrix-core qgemv (coli_qmv.hip).
+#ifndef COLI_QMV_H
+#define COLI_QMV_H
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace coli {
+
+struct QmvArgs {
+    const uint8_t *W;     // [O, rb] packed rows
+    const float *scale;   // [O] (NULL: 1)
+    const float *x;       // [S, I]
+    float *y;             // [S, O]
+    int S, I, O;
+    int64_t rb;
+    int nkb;              // set by qmv_launch
+    int y_vec4;           // set by qmv_launch
+};
+
+// Formats int8 / int4 / int2 with 16-byte row segments, I a multiple of 4,
+// W and x 16-byte aligned and the matrix under 4 GB (32-bit row offsets).
+bool qmv_supported(int fmt, int64_t rb, int I, int O, const void *W, const float *x);
+hipError_t qmv_launch(QmvArgs a, int fmt, hipStream_t st);
+
+}  // namespace coli
+
+#endif

@@ -1,0 +1,288 @@
+// coli_qmv.hip -- the dense quantised matrix-vector product on the bf16
+// matrix cores, fp32-level accuracy:
+//   y[s, o] = scale[o] * sum_i v(o, i) x[s, i]
+// over int8 / int4 (nibble - 8) / int2 (crumb - 2) rows [glm.c@98759bf --
+// typedef QT, matmul_qt, matmul_q, matmul_i4, matmul_i2; metal@93cde63 --
+// mm_gemv].
+//
+// A block of 8 waves owns 16 MT consecutive output rows for one pass of up
+// to 8 activation rows; wave w multiplies the rows' k-blocks w, w + 8, ...
+// (a K-slice), so one block's loads cover its rows' whole width at once and
+// there are enough blocks for the chip even for a few thousand rows.  The
+// activations are split into bf16 hi/lo in the kernel (column 2t: hi of row
+// t, column 2t+1: lo) straight from the fp32 input, so the call needs no
+// scratch memory.  sum(x), needed to remove OFF * sum(x) from the code
+// products, is one more MFMA per step against a tile of ones.  The 8 waves'
+// partial tiles are added in wave order through LDS.
+#include "coli_device.h"
+#include "coli_frag.h"
+#include "coli_qmv.h"
+
+namespace coli {
+
+namespace {
+
+constexpr int kQmvWaves = 8;
+constexpr int kQmvTpp = 8;   // activation rows per pass
+
+typedef float f2v __attribute__((ext_vector_type(2)));
+typedef __bf16 b2v __attribute__((ext_vector_type(2)));
+
+// bf16 pair (a, b) -> one dword; `lo` lanes get the rounding residue instead:
+// round(a - hi(a)), round(b - hi(b)).
+__device__ __forceinline__ uint32_t hilo_pair(float a, float b, float lo)
+{
+    const b2v h = __builtin_convertvector(f2v{a, b}, b2v);
+    const uint32_t hu = __builtin_bit_cast(uint32_t, h);
+    const float ha = __uint_as_float(hu << 16), hb = __uint_as_float(hu & 0xFFFF0000u);
+    const b2v r = __builtin_convertvector(f2v{fmaf(-lo, ha, a), fmaf(-lo, hb, b)}, b2v);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+template <int FMT, int MT>
+__global__ __launch_bounds__(512) void k_qmv(QmvArgs a)
+{
+    using T = MF<FMT>;
+    constexpr int STEPS = T::STEPS, KB = T::KB, SEGS = T::SEGS, BITS = T::BITS, SPS = T::SPS;
+    constexpr int RB = 16 * MT;
+    constexpr float OFF = T::OFF;
+    constexpr uint32_t kbytes = KB * BITS / 8;
+    constexpr int RUN = FMT == kI2 ? 16 : 8;          // elements per staging run
+    // two round buffers of activation units -- per chunk, 2 nt columns (hi
+    // and lo of each live row) -- reused at the end for the partial tiles
+    extern __shared__ uint4 lds[];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 15, q = lane >> 4, lrow = lane >> 2, lchunk = lane & 3;
+    const int src4 = 4 * (4 * col + q);
+    const int row0 = blockIdx.x * RB;
+    const int t0 = blockIdx.y * kQmvTpp;
+    const int nt = min(kQmvTpp, a.S - t0);
+    const int nkb = a.nkb;
+    const int rounds = (nkb + kQmvWaves - 1) / kQmvWaves;
+    const int cs = 2 * nt;                              // columns per chunk in LDS
+    const int units = kQmvWaves * STEPS * 4 * cs;       // units per round buffer
+
+    uint32_t roff[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+        roff[mt] = (uint32_t)(min(row0 + 16 * mt + lrow, a.O - 1) * a.rb) + 16 * lchunk;
+    const uint32_t last_seg = (uint32_t)(a.rb - 16 - 16 * lchunk);
+
+    floatx4 acc[MT], accs = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    const uint32_t one2 = opaque_v(0x3F803F80u);   // bf16 (1, 1)
+    const uint4 ones = make_uint4(one2, one2, one2, one2);
+
+    // weights of this wave's k-block in round r (a clamped copy when it has
+    // none: the loads stay unconditional, the products are skipped)
+    auto loadW = [&](int r, uint4 (&w)[MT][SEGS]) {
+        const int kb = min(r * kQmvWaves + wave, nkb - 1);
+        const uint32_t b0 = (uint32_t)kb * kbytes;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int sg = 0; sg < SEGS; ++sg)
+                w[mt][sg] = gload16(a.W + (roff[mt] + min(b0 + 64 * sg, last_seg)));
+    };
+    // staging of round r: run u of the round (RUN consecutive elements of
+    // one live row) per thread and pass; zeros past I
+    constexpr int RUNS_PER_ROW = kQmvWaves * KB / RUN;
+    constexpr int PASSES = (RUNS_PER_ROW * kQmvTpp + 511) / 512;
+    auto loadX = [&](int r, float4 (&xv)[PASSES][RUN / 4]) {
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p) {
+            const int u = tid + 512 * p;
+            const int t = min(u / RUNS_PER_ROW, nt - 1);
+            const int e0 = r * kQmvWaves * KB + (u % RUNS_PER_ROW) * RUN;
+            const float *xr = a.x + (int64_t)(t0 + t) * a.I;
+            if (e0 + RUN <= a.I) {
+#pragma unroll
+                for (int i = 0; i < RUN / 4; ++i) xv[p][i] = gload4f(xr + e0 + 4 * i);
+            } else {
+#pragma unroll
+                for (int i = 0; i < RUN / 4; ++i) {
+                    float f[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) f[j] = e0 + 4 * i + j < a.I ? xr[e0 + 4 * i + j] : 0.f;
+                    xv[p][i] = make_float4(f[0], f[1], f[2], f[3]);
+                }
+            }
+        }
+    };
+    // ... split into bf16 hi (column 2t) and lo (column 2t+1) units in
+    // fragment order: slot pairs (2m, 2m+1) are elements int8 (2m, 2m+1),
+    // int4 (m, m+4), int2 (m, m+8) (and (m+4, m+12) for the odd step)
+    auto stageX = [&](int r, const float4 (&xv)[PASSES][RUN / 4], uint4 *buf) {
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p) {
+            const int u = tid + 512 * p;
+            if (u >= RUNS_PER_ROW * nt) break;   // live rows only
+            const int t = u / RUNS_PER_ROW;
+            const int e0 = (u % RUNS_PER_ROW) * RUN;   // inside the round
+            float v[RUN];
+#pragma unroll
+            for (int i = 0; i < RUN / 4; ++i) {
+                v[4 * i] = xv[p][i].x;
+                v[4 * i + 1] = xv[p][i].y;
+                v[4 * i + 2] = xv[p][i].z;
+                v[4 * i + 3] = xv[p][i].w;
+            }
+            int c, j;
+            pos_of<FMT>(e0, c, j);   // chunk inside the round (k-blocks from 0)
+#pragma unroll
+            for (int h = 0; h < RUN / 8; ++h) {
+                uint32_t hw[4], lw[4];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    int k0, k1;
+                    if constexpr (FMT == kI8) { k0 = 2 * m; k1 = 2 * m + 1; }
+                    else if constexpr (FMT == kI4) { k0 = m; k1 = m + 4; }
+                    else { k0 = m + 4 * h; k1 = m + 4 * h + 8; }
+                    hw[m] = hilo_pair(v[k0], v[k1], 0.f);
+                    lw[m] = hilo_pair(v[k0], v[k1], 1.f);
+                }
+                uint4 *dst = buf + (c + 4 * h) * cs + 2 * t;
+                dst[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+                dst[1] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+            }
+        }
+    };
+    auto compute = [&](uint4 (&w)[MT][SEGS], const uint4 *buf) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int sg = 0; sg < SEGS; ++sg) {
+                const uint4 u = w[mt][sg];
+                w[mt][sg] = make_uint4((uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)u.x),
+                                       (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)u.y),
+                                       (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)u.z),
+                                       (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)u.w));
+            }
+        // dead columns read the last live row's units
+        const int bcol = (col >> 1) < nt ? col : 2 * (nt - 1) + (col & 1);
+        const uint4 *bw = buf + (wave * STEPS * 4 + q) * cs + bcol;
+#pragma unroll
+        for (int s = 0; s < STEPS; ++s) {
+            const uint4 b = bw[s * 4 * cs];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma(codes<FMT>(w[mt][s / SPS], s % SPS), b, acc[mt]);
+            accs = mfma(ones, b, accs);
+        }
+    };
+
+    // Round r: the next round's activations and weights are requested (in
+    // that order: the wait before staging then covers the activations only),
+    // this round's products run from LDS, the next round is staged into the
+    // other buffer, barrier.
+    uint4 wA[MT][SEGS], wB[MT][SEGS];
+    float4 xv[PASSES][RUN / 4];
+    loadX(0, xv);
+    loadW(0, wA);
+    stageX(0, xv, lds);
+    __syncthreads();
+    for (int r = 0; r < rounds; r += 2) {
+        loadX(r + 1 < rounds ? r + 1 : r, xv);
+        loadW(r + 1 < rounds ? r + 1 : r, wB);
+        __builtin_amdgcn_sched_barrier(0);
+        if (r * kQmvWaves + wave < nkb) compute(wA, lds);
+        __builtin_amdgcn_sched_barrier(0);
+        if (r + 1 >= rounds) break;
+        stageX(r + 1, xv, lds + units);
+        __syncthreads();
+        loadX(r + 2 < rounds ? r + 2 : r + 1, xv);
+        loadW(r + 2 < rounds ? r + 2 : r + 1, wA);
+        __builtin_amdgcn_sched_barrier(0);
+        if ((r + 1) * kQmvWaves + wave < nkb) compute(wB, lds + units);
+        __builtin_amdgcn_sched_barrier(0);
+        if (r + 2 >= rounds) break;
+        stageX(r + 2, xv, lds);
+        __syncthreads();
+    }
+
+    // partial tiles of the 8 waves, added in wave order
+    __syncthreads();   // every wave is done with the round buffers
+    floatx4 *red = reinterpret_cast<floatx4 *>(lds);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) red[(wave * (MT + 1) + mt) * kWave + lane] = acc[mt];
+    red[(wave * (MT + 1) + MT) * kWave + lane] = accs;
+    __syncthreads();
+    if (wave >= MT) return;
+    const int mt = wave;
+    floatx4 v = red[mt * kWave + lane], xs4 = red[MT * kWave + lane];
+#pragma unroll
+    for (int w = 1; w < kQmvWaves; ++w) {
+        v += red[(w * (MT + 1) + mt) * kWave + lane];
+        xs4 += red[(w * (MT + 1) + MT) * kWave + lane];
+    }
+    // D[4q + r][col]: the lo column is added to the hi one
+    const float xs = xs4[0] + __shfl_xor(xs4[0], 1, kWave);
+    const int ob = row0 + 16 * mt + 4 * q;
+    float res[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const float vv = v[r] + __shfl_xor(v[r], 1, kWave);
+        const int o = min(ob + r, a.O - 1);
+        const float sc = a.scale ? a.scale[o] : 1.f;
+        res[r] = sc * (vv - OFF * xs);
+    }
+    const int tok = col >> 1;
+    if ((col & 1) == 0 && tok < nt) {
+        float *yp = a.y + (int64_t)(t0 + tok) * a.O;
+        if (a.y_vec4 && ob + 3 < a.O) {
+            *reinterpret_cast<float4 *>(yp + ob) = make_float4(res[0], res[1], res[2], res[3]);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (ob + r < a.O) yp[ob + r] = res[r];
+        }
+    }
+}
+
+template <int FMT, int MT>
+hipError_t launch_q(const QmvArgs &a, hipStream_t st)
+{
+    const int rb = 16 * MT;
+    const dim3 grid((unsigned)((a.O + rb - 1) / rb), (unsigned)((a.S + kQmvTpp - 1) / kQmvTpp));
+    // LDS: two round buffers for the widest pass, or the partial tiles
+    const int ntmax = a.S < kQmvTpp ? a.S : kQmvTpp;
+    const size_t stage = (size_t)2 * kQmvWaves * MF<FMT>::STEPS * 4 * (2 * ntmax) * 16;
+    const size_t red = (size_t)kQmvWaves * (MT + 1) * kWave * 16;
+    const size_t lds = stage > red ? stage : red;
+    auto kern = k_qmv<FMT, MT>;
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, grid, dim3(64 * kQmvWaves), lds, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool qmv_supported(int fmt, int64_t rb, int I, int O, const void *W, const float *x)
+{
+    if (fmt != kI8 && fmt != kI4 && fmt != kI2) return false;
+    return rb >= 16 && rb % 16 == 0 && I % 4 == 0 && ((uintptr_t)W & 15u) == 0 && ((uintptr_t)x & 15u) == 0 &&
+           (int64_t)O * rb < ((int64_t)1 << 32) - 4096;
+}
+
+hipError_t qmv_launch(QmvArgs a, int fmt, hipStream_t st)
+{
+    if (a.S <= 0 || a.O <= 0) return hipSuccess;
+    const int KB = fmt == kI8 ? MF<kI8>::KB : fmt == kI4 ? MF<kI4>::KB : MF<kI2>::KB;
+    a.nkb = (a.I + KB - 1) / KB;
+    a.y_vec4 = a.O % 4 == 0 && ((uintptr_t)a.y & 15u) == 0;
+    // 64 rows per block once that still gives at least 128 blocks (measured
+    // faster on the 12288-row matrices), else 32
+    const bool wide = (int64_t)a.O >= 64 * 128;
+    switch (fmt) {
+    case kI8: return wide ? launch_q<kI8, 4>(a, st) : launch_q<kI8, 2>(a, st);
+    case kI4: return wide ? launch_q<kI4, 4>(a, st) : launch_q<kI4, 2>(a, st);
+    case kI2: return wide ? launch_q<kI2, 4>(a, st) : launch_q<kI2, 2>(a, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace coli
