@@ -21,12 +21,13 @@
 //     products, is one more MFMA per step against a tile of ones, over the
 //     very bf16 values the products use;
 //   * an item is (group-pass, 128-row tile) for gate/up (32 rows per wave),
-//     (group-pass, 256-row tile) for down (64 rows per wave); the items of
-//     a contiguous run of group-passes go to one XCD (passes of one group
-//     run there together, so later passes find the weights in its L2),
-//     persistent blocks walk them in order, and each wave loads the next
-//     k-block's weights while it multiplies the current one, and the next
-//     item's first k-block during the current item's last.
+//     (group-pass, 256-row tile) for down (64 rows per wave); the items
+//     are shared out to the XCDs so that the passes of one group run on the
+//     same XCD at about the same time (later passes find the weights in its
+//     L2), persistent blocks walk them in order, and each wave loads the
+//     next k-block's weights and activations while it multiplies the
+//     current one, and the next item's first k-block during the current
+//     item's last.
 #include "coli_device.h"
 #include "coli_frag.h"
 #include "coli_dec.h"
@@ -117,10 +118,18 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
     const int src4 = 4 * (4 * col + q);
     const int xcd = blockIdx.x % kDecXcds, lb = blockIdx.x / kDecXcds;
     const int bpx = gridDim.x / kDecXcds;               // grid is a multiple of 8
+    // Items of an XCD, in order (adjacent items: the passes of one group,
+    // which then run there at about the same time and meet the weights in
+    // its L2):
+    //   gate/up (M = 2): all tiles of a contiguous run of group-passes;
+    //   down (M = 1): tiles x, x + 8, ... of every group-pass, so each XCD
+    //   streams the same share of every matrix.
+    // (each measured faster for its kernel on the 64-token layer)
     const int n_gp = cload(a.n_work);
-    const int gp_lo = (int)((int64_t)n_gp * xcd / kDecXcds);
-    const int gp_cnt = (int)((int64_t)n_gp * (xcd + 1) / kDecXcds) - gp_lo;
-    const int n_items = gp_cnt * a.tiles;
+    const int gp_lo = M == 2 ? (int)((int64_t)n_gp * xcd / kDecXcds) : 0;
+    const int gp_cnt = M == 2 ? (int)((int64_t)n_gp * (xcd + 1) / kDecXcds) - gp_lo : n_gp;
+    const int tpx = M == 2 ? a.tiles : (a.tiles - xcd + kDecXcds - 1) / kDecXcds;   // tiles per pass here
+    const int n_items = gp_cnt * tpx;
     if (lb >= n_items) return;
     const int nkb = a.kpad / KB;                        // even and >= 4 (kpad: multiple of 1024)
     constexpr uint32_t kbytes = KB * BITS / 8;
@@ -138,8 +147,8 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
         uint32_t boff;       // this lane's unit in its activation row (bytes)
     };
     auto make = [&](It &c, int it) {
-        c.gp = __builtin_amdgcn_readfirstlane(gp_lo + it / a.tiles);
-        c.tile = __builtin_amdgcn_readfirstlane(it % a.tiles);
+        c.gp = __builtin_amdgcn_readfirstlane(gp_lo + it / tpx);
+        c.tile = __builtin_amdgcn_readfirstlane(M == 2 ? it % tpx : xcd + kDecXcds * (it % tpx));
         const int wv = cload(a.work + c.gp);
         const int g = wv & 0x7FF, pass = wv >> 11;
         const bool extra = a.has_extra && g == a.ngroups;
@@ -328,19 +337,20 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
     It cur;
     make(cur, lb);
     int jn = lb + bpx;
-    uint4 wA[M][MT][SEGS], wB[M][MT][SEGS], bb[STEPS];
+    uint4 wA[M][MT][SEGS], wB[M][MT][SEGS], bA[STEPS], bB[STEPS];
+    loadB(cur, 0, bA);
     loadW(cur, 0, wA);
     for (;;) {
         for (int k = 0; k < nkb - 2; k += 2) {
-            loadB(cur, k, bb);
+            loadB(cur, k + 1, bB);
             loadW(cur, k + 1, wB);
             __builtin_amdgcn_sched_barrier(0);
-            compute(wA, bb);
+            compute(wA, bA);
             __builtin_amdgcn_sched_barrier(0);
-            loadB(cur, k + 1, bb);
+            loadB(cur, k + 2, bA);
             loadW(cur, k + 2, wA);
             __builtin_amdgcn_sched_barrier(0);
-            compute(wB, bb);
+            compute(wB, bB);
             __builtin_amdgcn_sched_barrier(0);
         }
         // last two k-blocks: the epilogue's scales, then the next item's
@@ -349,15 +359,15 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
         It nxt = cur;
         if (has_nxt) make(nxt, jn);
         load_epi(cur);
-        loadB(cur, nkb - 2, bb);
+        loadB(cur, nkb - 1, bB);
         loadW(cur, nkb - 1, wB);
         __builtin_amdgcn_sched_barrier(0);
-        compute(wA, bb);
+        compute(wA, bA);
         __builtin_amdgcn_sched_barrier(0);
-        loadB(cur, nkb - 1, bb);
+        loadB(nxt, 0, bA);
         loadW(nxt, 0, wA);
         __builtin_amdgcn_sched_barrier(0);
-        compute(wB, bb);
+        compute(wB, bB);
         __builtin_amdgcn_sched_barrier(0);
         epilogue(cur);
         if (!has_nxt) break;
