@@ -228,7 +228,7 @@ def run_prefill2048(args, dev):
     gu_flops = 2 * rows * 2 * D * F
     return dict(workload="moe_layer_prefill_2048_bf16", ms=ms, wall=wall, step_bytes=step_bytes,
                 tokens=S, stages=stages, uniq=uniq, flops=flops,
-                dominant=dict(kernel="k_mm<I4,2> (grouped expert gate/up + SwiGLU, bf16 matrix cores)",
+                dominant=dict(kernel="k_pre<I4,2> (grouped expert gate/up + SwiGLU, bf16 matrix cores)",
                               bytes_per_launch=(uniq + 1) * gu + S * D * 4 + rows * F * 4,
                               flops_per_launch=gu_flops, ms_per_launch=gu_ms / max(gu_n, 1),
                               launches=gu_n))

@@ -184,18 +184,20 @@ size_t coli_moe_workspace_bytes(int S, int K, int E, int D, int F,
  *              numbering), before the routing weight.
  *   router_part  fp64 partial router logits (scratch).
  *   xf, xsum, hf, hsum, work, n_work   matrix-core scratch and the
- *              device-built list of passes.  COLI_PREC_FP32: xf holds one row
- *              per token and hf one row per grouped row, each the row's
- *              activations (x, resp. the SwiGLU output) as bf16 hi/lo pairs
- *              in the kernels' fragment order (xf_stride / hf_stride bf16
- *              per row); xsum and hsum are empty.  COLI_PREC_BF16: xf and hf
- *              hold the activations per (expert, 32-row pass), xsum and hsum
- *              their sums (xf_stride / hf_stride bf16 per pass). */
+ *              device-built list of passes.  xf holds one row per token and
+ *              hf one row per grouped row: the row's activations (x, resp.
+ *              the SwiGLU output) in the kernels' fragment order,
+ *              xf_stride / hf_stride bf16 per row -- COLI_PREC_FP32: bf16
+ *              hi/lo pairs, xsum and hsum empty; COLI_PREC_BF16: bf16 values,
+ *              xsum = [S] per-token sums of the stored x, then per grouped
+ *              row its xf row (int32) and activation sum; hsum = per grouped
+ *              row KpF/32 partial sums of the stored h (KpF = F rounded up to
+ *              1024), then their totals. */
 typedef struct {
     int64_t flags, sig, idx, w, offsets, counts, row_pair, pair_row, h, y, router_part;
     int64_t xf, xsum, hf, hsum, work, n_work;
     int64_t n_pass_max;            /* passes the scratch is sized for */
-    int64_t xf_stride, hf_stride;  /* bf16 elements per row (fp32) or pass (bf16) */
+    int64_t xf_stride, hf_stride;  /* bf16 elements per row */
     int64_t h_ld;   /* row stride of h in floats (max of F and F_shared) */
     int64_t total;  /* == coli_moe_workspace_bytes(...) */
 } coli_ws_layout;

@@ -14,7 +14,7 @@
 #include "coli_dec.h"
 #include "coli_device.h"
 #include "coli_gemv.h"
-#include "coli_mfma.h"
+#include "coli_pre.h"
 #include "coli_qmv.h"
 #include "coli_internal.h"
 #include "coli_router.h"
@@ -316,7 +316,7 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
         uint16_t *xt = reinterpret_cast<uint16_t *>(ws + L.xf);
         uint16_t *ht = reinterpret_cast<uint16_t *>(ws + L.hf);
         const int64_t max_gp = L.n_pass_max;
-        const int kpD = (int)mm_kpad(D), kpF = (int)mm_kpad(F);
+        const int kpD = (int)coli__kpad(D), kpF = (int)coli__kpad(F);
         {
             StageTimer tp(kStPrep, st);
             if (xrows_launch(ex->fmt, x, D, S, D, kpD, xt, st) != hipSuccess) return COLI_EDEVICE;
@@ -400,16 +400,28 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
                                         (int)(al16(out) && al16(y) && D % 4 == 0), st));
     }
     if (mm) {
-        uint16_t *xf = reinterpret_cast<uint16_t *>(ws + L.xf);
-        float *xsum = reinterpret_cast<float *>(ws + L.xsum);
-        uint16_t *hf = reinterpret_cast<uint16_t *>(ws + L.hf);
-        float *hsum = reinterpret_cast<float *>(ws + L.hsum);
+        // bf16 precision: x as one bf16 row table per token, the SwiGLU
+        // output as one per grouped row; per-row activation sums
+        const int64_t rows = (int64_t)P + S;
+        const int kpD = (int)coli__kpad(D), kpF = (int)coli__kpad(F);
+        const int nparts = kpF / 32;
+        uint16_t *xt = reinterpret_cast<uint16_t *>(ws + L.xf);
+        float *tok_sum = reinterpret_cast<float *>(ws + L.xsum);
+        int32_t *act_row = reinterpret_cast<int32_t *>(ws + L.xsum + (int64_t)S * 4);
+        float *row_sum = reinterpret_cast<float *>(ws + L.xsum + ((int64_t)S + rows) * 4);
+        uint16_t *ht = reinterpret_cast<uint16_t *>(ws + L.hf);
+        float *hpart = reinterpret_cast<float *>(ws + L.hsum);
+        float *hsum = reinterpret_cast<float *>(ws + L.hsum + rows * nparts * 4);
         const int64_t max_gp = L.n_pass_max;
-        const int64_t kpD = mm_kpad(D), kpF = mm_kpad(F);
         {
-            MmArgs a = {};
-            a.tpp = tpp;
-            a.bf16 = bf16;
+            StageTimer tp(kStPrep, st);
+            if (xrows_bf16_launch(ex->fmt, x, D, S, D, kpD, xt, tok_sum, st) != hipSuccess) return COLI_EDEVICE;
+            if (pre_rows_launch(row_pair, P, K, S, tok_sum, act_row, row_sum, st) != hipSuccess)
+                return COLI_EDEVICE;
+        }
+        {
+            StageTimer tgu(kStGateUp, st);
+            PreArgs a = {};
             a.w[0] = (const uint8_t *)ex->w_gate;
             a.w[1] = (const uint8_t *)ex->w_up;
             a.s[0] = ex->s_gate;
@@ -428,38 +440,27 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
                 a.x_rows = S;
                 a.x_row0 = (int)shared_row0;
             }
-            a.I = D;
-            a.kpad = (int)kpD;
+            a.kpad = kpD;
             a.rb = rbD;
             a.offsets = offsets;
-            a.row_pair = row_pair;
-            a.K = K;
-            a.xrow_token = 1;
-            a.xf = xf;
-            a.xf_stride = L.xf_stride;
-            a.xsum = xsum;
             a.work = work;
             a.n_work = n_work;
+            a.act_row = act_row;
+            a.row_sum = row_sum;
+            a.act = xt;
             a.out = h;
             a.ldo = L.h_ld;
             a.out_vec4 = L.h_ld % 4 == 0 && al16(h);
-            a.hf = hf;
-            a.hf_stride = L.hf_stride;
-            a.hf_rows = (int)kpF;
-            a.hsum = hsum;
-            a.hsum_stride = max_gp * mm_pass_slots(bf16);
-            {
-                StageTimer tp(kStPrep, st);
-                if (xprep_launch(ex->fmt, a, x, D, max_gp, st) != hipSuccess) return COLI_EDEVICE;
-            }
-            StageTimer tgu(kStGateUp, st);
-            if (mm_launch(a, ex->fmt, 2, max_gp, st) != hipSuccess) return COLI_EDEVICE;
+            a.hf = ht;
+            a.hf_kpad = kpF;
+            a.hpart = hpart;
+            a.nparts = nparts;
+            if (pre_launch(a, ex->fmt, 2, max_gp, st) != hipSuccess) return COLI_EDEVICE;
         }
         {
             StageTimer tdn(kStDown, st);
-            MmArgs d = {};
-            d.tpp = tpp;
-            d.bf16 = bf16;
+            if (pre_sum_launch(hpart, nparts, (int)rows, hsum, st) != hipSuccess) return COLI_EDEVICE;
+            PreArgs d = {};
             d.w[0] = (const uint8_t *)ex->w_down;
             d.s[0] = ex->s_down;
             d.w_gstride = (int64_t)D * rbF;
@@ -474,28 +475,18 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
                 d.x_rows = S;
                 d.x_row0 = (int)shared_row0;
             }
-            d.I = F;
-            d.kpad = (int)kpF;
+            d.kpad = kpF;
             d.rb = rbF;
             d.offsets = offsets;
-            d.row_pair = row_pair;
-            d.K = K;
-            d.xrow_token = 0;
-            d.xf = hf;
-            d.xf_stride = L.hf_stride;
-            // the activations' sums: the gate/up tiles' partial sums, added up
-            // (into xsum, free once gate/up has run)
-            if (sum_parts_launch(hsum, (int)(kpF / mm_rows_per_block(2, bf16)), max_gp * mm_pass_slots(bf16),
-                                 max_gp * mm_pass_slots(bf16), xsum,
-                                 st) != hipSuccess)
-                return COLI_EDEVICE;
-            d.xsum = xsum;
             d.work = work;
             d.n_work = n_work;
+            d.act_row = nullptr;
+            d.row_sum = hsum;
+            d.act = ht;
             d.out = y;
             d.ldo = D;
             d.out_vec4 = D % 4 == 0 && al16(y);
-            if (mm_launch(d, ex->fmt, 1, max_gp, st) != hipSuccess) return COLI_EDEVICE;
+            if (pre_launch(d, ex->fmt, 1, max_gp, st) != hipSuccess) return COLI_EDEVICE;
         }
         if (sh && !sh_mm) {
             int rc = run_shared_valu(sh, x, S, D, h, L.h_ld, y, shared_row0, hint, st);

@@ -11,11 +11,15 @@
 
 #define COLI_MAX_E 1024 /* 16 scores per lane of a 64-wide wave */
 #define COLI_MAX_K 64
-/* rows ("tokens") per pass of the matrix-core expert kernels: in fp32
- * precision 8, as bf16 hi/lo column pairs of one 16-column MFMA tile; in
- * bf16 precision 32, one column each over two tiles */
+/* rows per pass of the matrix-core expert kernels: in fp32 precision 8, as
+ * bf16 hi/lo column pairs of one 16-column MFMA tile; in bf16 precision 64,
+ * one column each over four tiles */
 #define COLI_MM_TPP_FP32 8
-#define COLI_MM_TPP_BF16 32
+#define COLI_MM_TPP_BF16 64
+
+/* input width of the matrix-core products, rounded up to whole 1024-element
+ * k-block groups (the activations are zero past the real width) */
+static inline int64_t coli__kpad(int64_t I) { return (I + 1023) / 1024 * 1024; }
 
 #ifdef __cplusplus
 extern "C" {

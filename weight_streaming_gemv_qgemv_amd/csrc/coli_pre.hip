@@ -1,0 +1,524 @@
+// coli_pre.hip -- grouped expert products for prefill batches on the bf16
+// matrix cores (activations rounded once to bf16, fp32 accumulation).
+//
+// The products of the pages' MoE block [glm.c@98759bf -- moe, phase D;
+// glm.c@97c756a -- expert_gate_up, matmul_i4_pair; metal@93cde63 --
+// moe_gemv, moe_silu], for batches where an expert meets tens to thousands
+// of rows: per expert (group) and pass of up to 64 of its rows,
+//   gate/up:  h = silu(sg * (Vg x)) * (su * (Vu x))
+//   down:     y = sd * (Vd h)
+// Weight codes are exact bf16 values v + OFF (coli_frag.h); OFF * sum(x),
+// sum(x) being the sum of the stored bf16 activations of the row, is
+// removed per output.
+//
+// An item is (group-pass, 128 weight rows); a block of 4 waves takes it,
+// each wave 32 weight rows x all 64 pass rows (4 MFMA N-tiles), so each
+// weight byte read from memory meets 64 activation rows.  Per k-block the
+// pass rows' activations are staged from their bf16 row tables into LDS
+// (double-buffered, units XOR-swizzled by chunk so that both the staging
+// writes and the operand reads spread over the banks), while each wave has
+// the next k-block's weights in flight.  The row-table rows of an item's pass
+// rows and their activation sums are fetched one item ahead into LDS, so
+// no wait on global memory ever drains the weight stream.
+#include "coli_device.h"
+#include "coli_frag.h"
+#include "coli_pre.h"
+
+namespace coli {
+
+namespace {
+
+typedef __attribute__((address_space(3))) const void lds_void;
+
+constexpr int kPreWaves = 4;
+constexpr int kPreXcds = 8;
+constexpr int kPreNT = kPreTpp / 16;   // N-tiles per pass
+constexpr int kPreMT = 2;              // 16-row weight tiles per wave
+
+// ---------------------------------------------------------------- row tables
+template <int FMT>
+__global__ __launch_bounds__(256) void k_xrows_bf16(const float *__restrict__ x, int64_t ldx, int I,
+                                                    int kpad, uint16_t *__restrict__ table,
+                                                    float *__restrict__ sums, int vec)
+{
+    constexpr int RUN = FMT == kI2 ? 16 : 8;
+    __shared__ float red[4];
+    const int row = blockIdx.x, tid = threadIdx.x;
+    const float *xr = x + (int64_t)row * ldx;
+    uint16_t *dst = table + (int64_t)row * kpad;
+    const int nruns = kpad / RUN;
+    float sum = 0.f;
+    for (int r = tid; r < nruns; r += 256) {
+        const int e0 = r * RUN;
+        float v[RUN];
+        if (vec && e0 + RUN <= I) {
+#pragma unroll
+            for (int i = 0; i < RUN / 4; ++i) {
+                const float4 f = *reinterpret_cast<const float4 *>(xr + e0 + 4 * i);
+                v[4 * i] = f.x;
+                v[4 * i + 1] = f.y;
+                v[4 * i + 2] = f.z;
+                v[4 * i + 3] = f.w;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < RUN; ++i) v[i] = e0 + i < I ? xr[e0 + i] : 0.f;
+        }
+        uint16_t hv[RUN];
+#pragma unroll
+        for (int i = 0; i < RUN; ++i) {
+            hv[i] = bf16_rne(v[i]);
+            sum += bf16_f(hv[i]);
+        }
+        int c, j;
+        pos_of<FMT>(e0, c, j);
+        uint32_t hw[RUN / 2];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            int k0, k1;
+            if constexpr (FMT == kI8) { k0 = 2 * m; k1 = 2 * m + 1; }
+            else if constexpr (FMT == kI4) { k0 = m; k1 = m + 4; }
+            else { k0 = m; k1 = m + 8; }
+            hw[m] = (uint32_t)hv[k0] | ((uint32_t)hv[k1] << 16);
+            if constexpr (FMT == kI2) hw[4 + m] = (uint32_t)hv[m + 4] | ((uint32_t)hv[m + 12] << 16);
+        }
+#pragma unroll
+        for (int h = 0; h < RUN / 8; ++h)
+            *reinterpret_cast<uint4 *>(dst + (int64_t)(c + 4 * h) * 8) =
+                make_uint4(hw[4 * h], hw[4 * h + 1], hw[4 * h + 2], hw[4 * h + 3]);
+    }
+    sum = wave_sum(sum);
+    if ((tid & 63) == 0) red[tid >> 6] = sum;
+    __syncthreads();
+    if (tid == 0) sums[row] = (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+__global__ void k_pre_rows(const int32_t *__restrict__ row_pair, int P, int K, int S,
+                           const float *__restrict__ token_sum, int32_t *__restrict__ act_row,
+                           float *__restrict__ row_sum)
+{
+    const int r = blockIdx.x * blockDim.x + threadIdx.x;
+    if (r >= P + S) return;
+    int t = r < P ? row_pair[r] / K : r - P;
+    if (t < 0 || t >= S) t = 0;   // rows past the grouped slots (never read)
+    act_row[r] = t;
+    row_sum[r] = token_sum[t];
+}
+
+__global__ void k_pre_sum(const float *__restrict__ hpart, int nparts, int rows, float *__restrict__ row_sum)
+{
+    const int r = blockIdx.x * blockDim.x + threadIdx.x;
+    if (r >= rows) return;
+    const float *p = hpart + (int64_t)r * nparts;
+    float s = 0.f;
+    for (int i = 0; i < nparts; ++i) s += p[i];
+    row_sum[r] = s;
+}
+
+// ---------------------------------------------------------------- products
+// LDS DMA of 16 bytes per lane (lane L's bytes land at lds + 16 L), issued
+// from inline assembly: the compiler does not see it, so it neither makes
+// LDS reads wait for it nor counts it in its own waits -- the kernel orders
+// and waits for these loads itself.
+__device__ __forceinline__ void dma16(const void *g, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory");
+}
+
+template <int FMT, int M>
+__global__ __launch_bounds__(256) void k_pre(PreArgs a)
+{
+    using T = MF<FMT>;
+    constexpr int STEPS = T::STEPS, KB = T::KB, SEGS = T::SEGS, BITS = T::BITS, SPS = T::SPS;
+    constexpr int MT = kPreMT, NT = kPreNT, RPW = 16 * MT, RPB = kPreWaves * RPW;
+    static_assert(RPB == kPreRowsPerBlock, "rows per item");
+    constexpr float OFF = T::OFF;
+    constexpr int CH = STEPS * 4;               // 16-byte chunks of a row per k-block
+    constexpr int UNITS = CH * kPreTpp;         // units of one staged k-block
+    constexpr uint32_t kbytes = KB * BITS / 8;
+    __shared__ uint4 bsA[UNITS], bsB[UNITS];    // staged k-blocks (even, odd)
+    __shared__ int lrow[2][kPreTpp];            // row-table rows of an item's pass rows
+    __shared__ float lsum[2][kPreTpp];          // their activation sums
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 15, q = lane >> 4;
+    const int xcd = blockIdx.x % kPreXcds, lb = blockIdx.x / kPreXcds;
+    const int bpx = gridDim.x / kPreXcds;               // grid is a multiple of 8
+    // XCD x: all tiles of a contiguous run of group-passes (the passes of
+    // one group -- and their weights -- together)
+    const int n_gp = cload(a.n_work);
+    const int gp_lo = (int)((int64_t)n_gp * xcd / kPreXcds);
+    const int gp_cnt = (int)((int64_t)n_gp * (xcd + 1) / kPreXcds) - gp_lo;
+    const int n_items = gp_cnt * a.tiles;
+    if (lb >= n_items) return;                          // whole block, before any barrier
+    const int nkb = a.kpad / KB;                        // even and >= 4
+    const uint32_t last_seg = (uint32_t)(a.rb - 16 - 16 * q);
+    const uint8_t *actb = reinterpret_cast<const uint8_t *>(a.act);
+    const uint32_t arow = (uint32_t)(2 * a.kpad);       // bytes per row-table row
+
+    struct It {
+        int gp, tile, nt, r0t, Og;
+        const uint8_t *wb[M];
+        const float *sc[M];
+        uint32_t roff[MT];
+    };
+    auto make = [&](It &c, int it) {
+        c.gp = __builtin_amdgcn_readfirstlane(gp_lo + it / a.tiles);
+        c.tile = __builtin_amdgcn_readfirstlane(it % a.tiles);
+        const int wv = cload(a.work + c.gp);
+        const int g = wv & 0x7FF, pass = wv >> 11;
+        const bool extra = a.has_extra && g == a.ngroups;
+        int r0, cnt;
+        if (extra) {
+            r0 = a.x_row0;
+            cnt = a.x_rows;
+        } else {
+            r0 = cload(a.offsets + g);
+            cnt = cload(a.offsets + g + 1) - r0;
+        }
+        c.nt = min(kPreTpp, cnt - pass * kPreTpp);
+        c.r0t = r0 + pass * kPreTpp;
+        if (extra) {
+            c.Og = a.xO;
+#pragma unroll
+            for (int m = 0; m < M; ++m) { c.wb[m] = a.xw[m]; c.sc[m] = a.xs[m]; }
+        } else {
+            c.Og = a.O;
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                c.wb[m] = a.w[m] + (int64_t)g * a.w_gstride;
+                c.sc[m] = a.s[m] + (int64_t)g * a.s_gstride;
+            }
+        }
+        const int obase = c.tile * RPB + wave * RPW;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            c.roff[mt] = (uint32_t)(min(obase + 16 * mt + col, c.Og - 1) * a.rb) + 16 * q;
+    };
+    // pass rows of an item: row-table row and activation sum (threads < 64;
+    // dead rows repeat the last live one)
+    auto loadList = [&](const It &c, int &ar, float &rs) {
+        const int gr = c.r0t + min(tid & 63, c.nt - 1);
+        ar = a.act_row ? a.act_row[gr] : gr;
+        rs = a.row_sum[gr];
+    };
+    auto storeList = [&](int par, int ar, float rs) {
+        if (tid < kPreTpp) {
+            lrow[par][tid] = ar;
+            lsum[par][tid] = rs;
+        }
+    };
+    auto loadW = [&](const It &c, int kbi, uint4 (&w)[M][MT][SEGS]) {
+        const uint32_t b0 = (uint32_t)kbi * kbytes;
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int sg = 0; sg < SEGS; ++sg)
+                    w[m][mt][sg] = gload16(c.wb[m] + (c.roff[mt] + min(b0 + 64 * sg, last_seg)));
+    };
+    // Staging by LDS DMA (each lane's 16 bytes land at the instruction's LDS
+    // base + 16 lane): staged unit (pass row t = 16 n + col, chunk c = 4 s +
+    // q) sits at ((n STEPS + s) 16 + col) 4 + (q ^ (col >> 2)), so the
+    // operand reads of a quarter-wave hit 16 distinct bank groups.  One
+    // instruction fills one (n, s): lane L takes row 16 n + L / 4 and chunk
+    // 4 s + ((L & 3) ^ (L >> 4)) -- 64 contiguous bytes of each of 16 rows.
+    // Wave w stages N-tile n = w.
+    constexpr int SPW = NT * STEPS / kPreWaves;          // instructions per wave
+    static_assert(SPW == STEPS, "one N-tile per wave");
+    const int dq = (lane & 3) ^ (lane >> 4);
+    auto stageB = [&](int par, int kbi, const uint4 *buf) {
+        const uint32_t rowoff = (uint32_t)lrow[par][16 * wave + (lane >> 2)] * arow +
+                                (uint32_t)kbi * (CH * 16) + (uint32_t)dq * 16;
+        const uint32_t lbase = (uint32_t)(uintptr_t)(const lds_void *)(buf + wave * STEPS * 64);
+#pragma unroll
+        for (int s = 0; s < STEPS; ++s)
+            dma16(actb + (rowoff + (uint32_t)s * 64), __builtin_amdgcn_readfirstlane(lbase + s * 1024));
+    };
+
+    floatx4 acc[M][MT][NT];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int n = 0; n < NT; ++n) acc[m][mt][n] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    // one k-block: per MFMA step the live N-tiles' activation units from LDS
+    // and the M x MT x NT products; the weights were loaded in the operand
+    // layout (lane (q, col) holds row col, chunk q of each 64-byte segment)
+    auto compute = [&](const uint4 (&w)[M][MT][SEGS], const uint4 *buf, int ntl) {
+#pragma unroll
+        for (int s2 = 0; s2 < STEPS; ++s2) {
+            uint4 b[NT];
+#pragma unroll
+            for (int n = 0; n < NT; ++n) b[n] = buf[((n * STEPS + s2) * 16 + col) * 4 + (q ^ (col >> 2))];
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const uint4 cw = codes<FMT>(w[m][mt][s2 / SPS], s2 % SPS);
+#pragma unroll
+                    for (int n = 0; n < NT; ++n) acc[m][mt][n] = mfma(cw, b[n], acc[m][mt][n]);
+                }
+        }
+    };
+
+    float sreg[M][MT][4];
+    auto load_epi = [&](const It &c) {
+        const int obase = c.tile * RPB + wave * RPW;
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    sreg[m][mt][r] = gloadf(c.sc[m] + min(obase + 16 * mt + 4 * q + r, c.Og - 1));
+    };
+    // D[4q + r][col] of tile (m, mt, n): weight row obase + 16 mt + 4 q + r,
+    // pass row 16 n + col; xsv[n]: that row's activation sum
+    float xsv[NT];
+    auto epilogue = [&](const It &c) {
+        const int obase = c.tile * RPB + wave * RPW;
+        const int ntl = (c.nt + 15) / 16;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            if (n >= ntl) break;                      // uniform
+            const int t = 16 * n + col;
+            const bool live = t < c.nt;
+            const int64_t gr = c.r0t + t;
+            float hp = 0.f;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const int ob = obase + 16 * mt + 4 * q;
+                float res[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float y = sreg[0][mt][r] * (acc[0][mt][n][r] - OFF * xsv[n]);
+                    if constexpr (M == 2) {
+                        const float u = sreg[1][mt][r] * (acc[1][mt][n][r] - OFF * xsv[n]);
+                        y = silu_f(y) * u;
+                    }
+                    res[r] = ob + r < c.Og ? y : 0.f;
+                }
+                if (live) {
+                    float *op = a.out + gr * a.ldo;
+                    if (a.out_vec4 && ob + 3 < c.Og) {
+                        *reinterpret_cast<float4 *>(op + ob) = make_float4(res[0], res[1], res[2], res[3]);
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (ob + r < c.Og) op[ob + r] = res[r];
+                    }
+                }
+                if constexpr (M == 2) {
+                    // h as the down product's bf16 row table: this lane's
+                    // 4 outputs are half of one unit, the partner lane (q ^ 1,
+                    // int2: q ^ 2) holds the other half, the lower lane stores
+                    constexpr int PX = FMT == kI2 ? 32 : 16;
+                    const bool lowq = FMT == kI2 ? q < 2 : (q & 1) == 0;
+                    uint32_t hv[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        hv[r] = bf16_rne(res[r]);
+                        if (ob + r < a.hf_kpad) hp += bf16_f((uint16_t)hv[r]);
+                    }
+                    uint32_t pv[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) pv[r] = (uint32_t)__shfl_xor((int)hv[r], PX, kWave);
+                    if (lowq && live && ob < a.hf_kpad) {
+                        int cc, j;
+                        pos_of<FMT>(ob, cc, j);
+                        uint4 u;
+                        if constexpr (FMT == kI8)
+                            u = make_uint4(hv[0] | hv[1] << 16, hv[2] | hv[3] << 16,
+                                           pv[0] | pv[1] << 16, pv[2] | pv[3] << 16);
+                        else
+                            u = make_uint4(hv[0] | pv[0] << 16, hv[1] | pv[1] << 16,
+                                           hv[2] | pv[2] << 16, hv[3] | pv[3] << 16);
+                        *reinterpret_cast<uint4 *>(a.hf + gr * a.hf_kpad + (int64_t)cc * 8) = u;
+                    }
+                }
+            }
+            if constexpr (M == 2) {
+                // partial sum of the stored h of pass row t over this wave's
+                // 32 weight rows (4 lane groups q), in a fixed order
+                hp += __shfl_xor(hp, 16, kWave);
+                hp += __shfl_xor(hp, 32, kWave);
+                if (q == 0 && live) a.hpart[gr * a.nparts + c.tile * kPreWaves + wave] = hp;
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int n = 0; n < NT; ++n) acc[m][mt][n] = floatx4{0.f, 0.f, 0.f, 0.f};
+    };
+
+    // the staged k-block is complete once this wave's DMA loads are: they
+    // were issued before the NW weight loads of the next k-block
+    constexpr int NW = M * MT * SEGS;
+    // Half-step j (k-block j in LDS buffer rd, the next in wr):
+    //   1. the next weights are requested (NW loads);
+    //   2. wait until only those are in flight: this k-block's weights and
+    //      this wave's DMA of its activations (issued before them) are done;
+    //   3. barrier: every wave's DMA of k-block j is done, and every wave is
+    //      past the products of k-block j-1, which read wr;
+    //   4. the next k-block's activations are requested into wr (DMA);
+    //   5. the products of k-block j.
+    // The compiler's own wait for this k-block's weights is met by step 2.
+    auto step_sync = [&]() {
+        // vmcnt <= NW (bits 3:0 and 15:14), lgkmcnt = 0, expcnt not waited on
+        __builtin_amdgcn_s_waitcnt((NW & 15) | ((NW >> 4) << 14) | (7 << 4));
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+    auto half = [&](const uint4 *rd, const uint4 *wr, int spar, int skb, const It &wsrc, int wkb,
+                    uint4 (&wn)[M][MT][SEGS], const uint4 (&wc)[M][MT][SEGS], int ntl) {
+        loadW(wsrc, wkb, wn);
+        step_sync();
+        stageB(spar, skb, wr);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(wc, rd, ntl);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // prologue: the first item's pass rows; its first weights, then the DMA
+    // of its first k-block's activations into bsA
+    It cur;
+    make(cur, lb);
+    int par = 0;
+    {
+        int ar;
+        float rs;
+        loadList(cur, ar, rs);
+        storeList(0, ar, rs);
+    }
+    __syncthreads();
+    uint4 wA[M][MT][SEGS], wB[M][MT][SEGS];
+    loadW(cur, 0, wA);
+    stageB(0, 0, bsA);
+    int jn = lb + bpx;
+    // Even k-blocks are staged in bsA, odd ones in bsB (nkb is even).
+    for (;;) {
+        const bool has_nxt = jn < n_items;
+        It nxt = cur;
+        if (has_nxt) make(nxt, jn);
+        const int ntl = (cur.nt + 15) / 16;        // live N-tiles
+        int ar;
+        float rs;
+        loadList(nxt, ar, rs);     // stored after the first k-block
+        for (int k = 0; k < nkb - 2; k += 2) {
+            half(bsA, bsB, par, k + 1, cur, k + 1, wB, wA, ntl);
+            if (k == 0) storeList(par ^ 1, ar, rs);
+            half(bsB, bsA, par, k + 2, cur, k + 2, wA, wB, ntl);
+        }
+        // last two k-blocks: the epilogue's scales and row sums, then the
+        // next item's first k-block (a copy of this item's when there is none)
+        load_epi(cur);
+        half(bsA, bsB, par, nkb - 1, cur, nkb - 1, wB, wA, ntl);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) xsv[n] = lsum[par][min(16 * n + col, cur.nt - 1)];
+        half(bsB, bsA, par ^ 1, 0, nxt, 0, wA, wB, ntl);
+        epilogue(cur);
+        if (!has_nxt) break;
+        cur = nxt;
+        par ^= 1;
+        jn += bpx;
+    }
+    // every wave's DMA is complete before the block ends
+    __builtin_amdgcn_s_waitcnt(0);
+}
+
+int pre_resident_blocks(const void *kern, int *cache)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] > 0) return cache[dev];
+    int cus = 0, per = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kern, 256, 0) != hipSuccess || per <= 0)
+        per = 1;
+    cache[dev] = cus * per;
+    return cache[dev];
+}
+
+template <int FMT, int M>
+hipError_t launch_pre(const PreArgs &a, int64_t items, hipStream_t st)
+{
+    static int cache[64] = {0};
+    const void *kern = (const void *)k_pre<FMT, M>;
+    int64_t cap = pre_resident_blocks(kern, cache) / kPreXcds * kPreXcds;
+    if (cap < kPreXcds) cap = kPreXcds;
+    int64_t grid = (items + kPreXcds - 1) / kPreXcds * kPreXcds;
+    if (grid > cap) grid = cap;
+    if (grid < kPreXcds) grid = kPreXcds;
+    hipLaunchKernelGGL((k_pre<FMT, M>), dim3((unsigned)grid), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int pre_parts(int hf_kpad) { return (hf_kpad + kPreRowsPerBlock - 1) / kPreRowsPerBlock * kPreWaves; }
+
+hipError_t xrows_bf16_launch(int fmt, const float *x, int64_t ldx, int rows, int I, int kpad,
+                             uint16_t *table, float *sums, hipStream_t st)
+{
+    if (rows <= 0) return hipSuccess;
+    const int vec = ldx % 4 == 0 && ((uintptr_t)x & 15u) == 0;
+    switch (fmt) {
+    case kI8: hipLaunchKernelGGL(k_xrows_bf16<kI8>, dim3(rows), dim3(256), 0, st, x, ldx, I, kpad, table, sums, vec); break;
+    case kI4: hipLaunchKernelGGL(k_xrows_bf16<kI4>, dim3(rows), dim3(256), 0, st, x, ldx, I, kpad, table, sums, vec); break;
+    case kI2: hipLaunchKernelGGL(k_xrows_bf16<kI2>, dim3(rows), dim3(256), 0, st, x, ldx, I, kpad, table, sums, vec); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t pre_rows_launch(const int32_t *row_pair, int P, int K, int S, const float *token_sum,
+                           int32_t *act_row, float *row_sum, hipStream_t st)
+{
+    const int n = P + S;
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_pre_rows, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, row_pair, P, K, S,
+                       token_sum, act_row, row_sum);
+    return hipGetLastError();
+}
+
+hipError_t pre_sum_launch(const float *hpart, int nparts, int rows, float *row_sum, hipStream_t st)
+{
+    if (rows <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_pre_sum, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, hpart, nparts,
+                       rows, row_sum);
+    return hipGetLastError();
+}
+
+hipError_t pre_launch(PreArgs a, int fmt, int M, int64_t max_group_passes, hipStream_t st)
+{
+    int Ocover = a.O;
+    if (M == 2 && a.hf && a.hf_kpad > Ocover) Ocover = a.hf_kpad;
+    if (a.has_extra && a.xO > Ocover) Ocover = a.xO;
+    a.tiles = (Ocover + kPreRowsPerBlock - 1) / kPreRowsPerBlock;
+    if (M == 2 && a.nparts < a.tiles * kPreWaves) return hipErrorInvalidValue;
+    const int64_t items = max_group_passes * a.tiles;
+    if (M == 2) {
+        switch (fmt) {
+        case kI8: return launch_pre<kI8, 2>(a, items, st);
+        case kI4: return launch_pre<kI4, 2>(a, items, st);
+        case kI2: return launch_pre<kI2, 2>(a, items, st);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    switch (fmt) {
+    case kI8: return launch_pre<kI8, 1>(a, items, st);
+    case kI4: return launch_pre<kI4, 1>(a, items, st);
+    case kI2: return launch_pre<kI2, 1>(a, items, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace coli

@@ -158,25 +158,25 @@ int coli_moe_workspace_layout(int S, int K, int E, int D, int F, int F_shared,
     if (!mul_ok(rows, D, &t) || !mul_ok(t, 4, &t)) return COLI_ESHAPE;
     REGION(y, t);
     REGION(router_part, coli__router_partial_bytes(S, E, D));
-    /* matrix-core path, per (group, pass): the activations fragment-major
-     * (cols bf16 columns x input width rounded up to 1024), their sums, the
-     * SwiGLU output prepared the same way, its partial sums per gate/up item
-     * (128 rows in fp32 precision, 64 in bf16), and the work list.  fp32
-     * passes hold COLI_MM_TPP_FP32 rows as hi/lo column pairs (16 columns),
-     * bf16 passes COLI_MM_TPP_BF16 rows (32 columns). */
+    /* matrix-core path: the activations' row tables and sums (below), and
+     * the work list of (group, pass) entries; a pass is COLI_MM_TPP_FP32
+     * rows (fp32 precision) or COLI_MM_TPP_BF16 rows (bf16 precision). */
     const int bf16 = prec == COLI_PREC_BF16;
-    const int64_t tpp = bf16 ? COLI_MM_TPP_BF16 : COLI_MM_TPP_FP32, cols = bf16 ? 32 : 16;
+    const int64_t tpp = bf16 ? COLI_MM_TPP_BF16 : COLI_MM_TPP_FP32;
     int64_t ngp = (rows + tpp - 1) / tpp + (int64_t)E + 1;   /* passes */
-    int64_t KpD = round_up(D, 1024), KpF = round_up(Fmax, 1024), tilesF = KpF / 64;
+    int64_t KpD = round_up(D, 1024), KpF = round_up(Fmax, 1024);
     if (bf16) {
-        /* bf16 precision: per pass, its rows' activations fragment-major
-         * (32 columns), the same for the SwiGLU output, and their sums */
-        if (!mul_ok(ngp, 2 * cols * KpD, &t)) return COLI_ESHAPE;
+        /* bf16 precision: bf16 row tables of x (per token) and of the SwiGLU
+         * output (per grouped row); xsum: per-token sums of the stored x,
+         * then per grouped row its table row (int32) and activation sum;
+         * hsum: per grouped row KpF/32 partial sums of the stored h, then
+         * their totals */
+        if (!mul_ok((int64_t)S, 2 * KpD, &t)) return COLI_ESHAPE;
         REGION(xf, t);
-        REGION(xsum, ngp * cols * 4);
-        if (!mul_ok(ngp, 2 * cols * KpF, &t)) return COLI_ESHAPE;
+        REGION(xsum, ((int64_t)S + 2 * rows) * 4);
+        if (!mul_ok(rows, 2 * KpF, &t)) return COLI_ESHAPE;
         REGION(hf, t);
-        if (!mul_ok(tilesF * ngp, cols * 4, &t)) return COLI_ESHAPE;
+        if (!mul_ok(rows, KpF / 32 + 1, &t) || !mul_ok(t, 4, &t)) return COLI_ESHAPE;
         REGION(hsum, t);
     } else {
         /* fp32 precision: one row table per token (x) and per grouped row
@@ -192,8 +192,8 @@ int coli_moe_workspace_layout(int S, int K, int E, int D, int F, int F_shared,
     REGION(n_work, 64);
 #undef REGION
     out->n_pass_max = ngp;
-    out->xf_stride = bf16 ? cols * KpD : 2 * KpD;
-    out->hf_stride = bf16 ? cols * KpF : 2 * KpF;
+    out->xf_stride = bf16 ? KpD : 2 * KpD;
+    out->hf_stride = bf16 ? KpF : 2 * KpF;
     out->h_ld = Fmax;
     out->total = off;
     return COLI_OK;
