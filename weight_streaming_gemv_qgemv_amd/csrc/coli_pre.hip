@@ -15,8 +15,8 @@
 // each wave 32 weight rows x all 64 pass rows (4 MFMA N-tiles), so each
 // weight byte read from memory meets 64 activation rows.  Per k-block the
 // pass rows' activations are staged from their bf16 row tables into LDS
-// (double-buffered, units XOR-swizzled by chunk so that both the staging
-// writes and the operand reads spread over the banks), while each wave has
+// (double-buffered, units XOR-swizzled by chunk so that the operand reads
+// spread over the banks), while each wave has
 // the next k-block's weights in flight.  The row-table rows of an item's pass
 // rows and their activation sums are fetched one item ahead into LDS, so
 // no wait on global memory ever drains the weight stream.
@@ -220,14 +220,16 @@ __global__ __launch_bounds__(256) void k_pre(PreArgs a)
     };
     // Staging by LDS DMA (each lane's 16 bytes land at the instruction's LDS
     // base + 16 lane): staged unit (pass row t = 16 n + col, chunk c = 4 s +
-    // q) sits at ((n STEPS + s) 16 + col) 4 + (q ^ (col >> 2)), so the
-    // operand reads of a quarter-wave hit 16 distinct bank groups.  One
-    // instruction fills one (n, s): lane L takes row 16 n + L / 4 and chunk
-    // 4 s + ((L & 3) ^ (L >> 4)) -- 64 contiguous bytes of each of 16 rows.
+    // q) sits at ((n STEPS + s) 16 + col) 4 + (q ^ ((col >> 1) & 3)), a
+    // swizzle under which the operand reads (ds_read_b128) measured free of
+    // bank conflicts on gfx950 (q ^ (col >> 2) cost 4 conflict cycles per
+    // read).  One instruction fills one (n, s): lane L takes row 16 n + L / 4
+    // and chunk 4 s + ((L & 3) ^ ((L >> 3) & 3)) -- 64 contiguous bytes of
+    // each of 16 rows.
     // Wave w stages N-tile n = w.
     constexpr int SPW = NT * STEPS / kPreWaves;          // instructions per wave
     static_assert(SPW == STEPS, "one N-tile per wave");
-    const int dq = (lane & 3) ^ (lane >> 4);
+    const int dq = (lane & 3) ^ ((lane >> 3) & 3);
     auto stageB = [&](int par, int kbi, const uint4 *buf) {
         const uint32_t rowoff = (uint32_t)lrow[par][16 * wave + (lane >> 2)] * arow +
                                 (uint32_t)kbi * (CH * 16) + (uint32_t)dq * 16;
@@ -253,7 +255,7 @@ __global__ __launch_bounds__(256) void k_pre(PreArgs a)
         for (int s2 = 0; s2 < STEPS; ++s2) {
             uint4 b[NT];
 #pragma unroll
-            for (int n = 0; n < NT; ++n) b[n] = buf[((n * STEPS + s2) * 16 + col) * 4 + (q ^ (col >> 2))];
+            for (int n = 0; n < NT; ++n) b[n] = buf[((n * STEPS + s2) * 16 + col) * 4 + (q ^ ((col >> 1) & 3))];
 #pragma unroll
             for (int m = 0; m < M; ++m)
 #pragma unroll
