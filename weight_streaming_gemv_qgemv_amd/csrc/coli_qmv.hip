@@ -5,10 +5,13 @@
 // typedef QT, matmul_qt, matmul_q, matmul_i4, matmul_i2; metal@93cde63 --
 // mm_gemv].
 //
-// A block of 8 waves owns 16 MT consecutive output rows for one pass of up
-// to 8 activation rows; wave w multiplies the rows' k-blocks w, w + 8, ...
-// (a K-slice), so one block's loads cover its rows' whole width at once and
-// there are enough blocks for the chip even for a few thousand rows.  The
+// Two kernels.  k_qmv1 (one or two activation rows) issues every weight load
+// of the call up front; see its comment.  k_qmv (more rows): a block of 8
+// waves owns 16 MT consecutive output rows for one pass of up to 8
+// activation rows; wave w multiplies the rows' k-blocks w, w + 8, ... (a
+// K-slice) in rounds of 8 k-blocks, so one block's loads cover its rows'
+// whole width and there are enough blocks for the chip even for a few
+// thousand rows.  In both, the
 // activations are split into bf16 hi/lo in the kernel (column 2t: hi of row
 // t, column 2t+1: lo) straight from the fp32 input, so the call needs no
 // scratch memory.  sum(x), needed to remove OFF * sum(x) from the code
@@ -240,6 +243,205 @@ __global__ __launch_bounds__(512) void k_qmv(QmvArgs a)
     }
 }
 
+// ---------------------------------------------------------------- one shot
+// For few activation rows the whole product fits one round: a block of 8
+// waves owns 16 output rows for a pass of up to kQ1Tpp activation rows,
+// wave w takes the NKW consecutive k-blocks w NKW, ... of the rows, and
+// every weight load of the block is issued before anything waits.  The
+// pass's activations (the full width, as bf16 hi/lo units in fragment order)
+// are staged into LDS while the weights are in flight; their loads are
+// issued first, so the wait for them leaves the weight loads outstanding.
+// Blocks on one XCD (block id mod 8) take the passes of a row tile next to
+// each other, so the later passes find the tile's weights in that XCD's L2.
+constexpr int kQ1Tpp = 2;   // activation rows per pass
+
+template <int FMT, int NKW>
+__global__ __launch_bounds__(512) void k_qmv1(QmvArgs a, int passes, int ntiles)
+{
+    using T = MF<FMT>;
+    constexpr int STEPS = T::STEPS, KB = T::KB, SEGS = T::SEGS, BITS = T::BITS, SPS = T::SPS;
+    constexpr float OFF = T::OFF;
+    constexpr uint32_t kbytes = KB * BITS / 8;
+    constexpr int RUN = FMT == kI2 ? 16 : 8;              // elements per staging run
+    constexpr int XP = (kQmvWaves * NKW * KB / RUN * kQ1Tpp + 511) / 512;   // runs per thread
+    extern __shared__ uint4 lds[];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 15, q = lane >> 4, lrow = lane >> 2, lchunk = lane & 3;
+    const int src4 = 4 * (4 * col + q);
+    const int xcd = blockIdx.x % 8, jb = blockIdx.x / 8;
+    const int tile = (jb / passes) * 8 + xcd, pass = jb % passes;
+    if (tile >= ntiles) return;                           // whole block, before any barrier
+    const int row0 = tile * 16;
+    const int t0 = pass * kQ1Tpp;
+    const int nt = min(kQ1Tpp, a.S - t0);
+    const int nkb = a.nkb;
+    const int cs = 2 * nt;                                // columns per chunk in LDS
+    const int runs = nkb * KB / RUN;                      // staging runs per activation row
+
+    // activations first: this thread's runs (clamped to a live one)
+    float4 xv[XP][RUN / 4];
+#pragma unroll
+    for (int p = 0; p < XP; ++p) {
+        const int u = min(tid + 512 * p, runs * nt - 1);
+        const int t = u / runs, e0 = (u % runs) * RUN;
+        const float *xr = a.x + (int64_t)(t0 + t) * a.I;
+        if (e0 + RUN <= a.I) {
+#pragma unroll
+            for (int i = 0; i < RUN / 4; ++i) xv[p][i] = gload4f(xr + e0 + 4 * i);
+        } else {
+#pragma unroll
+            for (int i = 0; i < RUN / 4; ++i) {
+                float f[4];
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) f[jj] = e0 + 4 * i + jj < a.I ? xr[e0 + 4 * i + jj] : 0.f;
+                xv[p][i] = make_float4(f[0], f[1], f[2], f[3]);
+            }
+        }
+    }
+    // then every weight load of this wave (a clamped copy for k-blocks past
+    // the end: the loads stay unconditional, the products are skipped)
+    const uint32_t roff = (uint32_t)(min(row0 + lrow, a.O - 1) * a.rb) + 16 * lchunk;
+    const uint32_t last_seg = (uint32_t)(a.rb - 16 - 16 * lchunk);
+    uint4 w[NKW][SEGS];
+#pragma unroll
+    for (int i = 0; i < NKW; ++i) {
+        const uint32_t b0 = (uint32_t)min(wave * NKW + i, nkb - 1) * kbytes;
+#pragma unroll
+        for (int sg = 0; sg < SEGS; ++sg) w[i][sg] = gload16(a.W + (roff + min(b0 + 64 * sg, last_seg)));
+    }
+    // stage: run -> bf16 hi (column 2t) and lo (column 2t+1) units
+#pragma unroll
+    for (int p = 0; p < XP; ++p) {
+        const int u = tid + 512 * p;
+        if (u >= runs * nt) break;
+        const int t = u / runs, e0 = (u % runs) * RUN;
+        float v[RUN];
+#pragma unroll
+        for (int i = 0; i < RUN / 4; ++i) {
+            v[4 * i] = xv[p][i].x;
+            v[4 * i + 1] = xv[p][i].y;
+            v[4 * i + 2] = xv[p][i].z;
+            v[4 * i + 3] = xv[p][i].w;
+        }
+        int c, j;
+        pos_of<FMT>(e0, c, j);
+#pragma unroll
+        for (int h = 0; h < RUN / 8; ++h) {
+            uint32_t hw[4], lw[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                int k0, k1;
+                if constexpr (FMT == kI8) { k0 = 2 * m; k1 = 2 * m + 1; }
+                else if constexpr (FMT == kI4) { k0 = m; k1 = m + 4; }
+                else { k0 = m + 4 * h; k1 = m + 4 * h + 8; }
+                hw[m] = hilo_pair(v[k0], v[k1], 0.f);
+                lw[m] = hilo_pair(v[k0], v[k1], 1.f);
+            }
+            uint4 *dst = lds + (c + 4 * h) * cs + 2 * t;
+            dst[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+            dst[1] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        }
+    }
+    __syncthreads();
+
+    floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f}, accs = floatx4{0.f, 0.f, 0.f, 0.f};
+    const uint32_t one2 = opaque_v(0x3F803F80u);   // bf16 (1, 1)
+    const uint4 ones = make_uint4(one2, one2, one2, one2);
+    // dead columns read the last live row's units
+    const int bcol = (col >> 1) < nt ? col : 2 * (nt - 1) + (col & 1);
+#pragma unroll
+    for (int i = 0; i < NKW; ++i) {
+        const int kb = wave * NKW + i;
+        if (kb >= nkb) break;                         // uniform
+#pragma unroll
+        for (int sg = 0; sg < SEGS; ++sg) {
+            const uint4 u = w[i][sg];
+            w[i][sg] = make_uint4((uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)u.x),
+                                  (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)u.y),
+                                  (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)u.z),
+                                  (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)u.w));
+        }
+        const uint4 *bw = lds + (kb * STEPS * 4 + q) * cs + bcol;
+#pragma unroll
+        for (int s2 = 0; s2 < STEPS; ++s2) {
+            const uint4 b = bw[s2 * 4 * cs];
+            acc = mfma(codes<FMT>(w[i][s2 / SPS], s2 % SPS), b, acc);
+            accs = mfma(ones, b, accs);
+        }
+    }
+
+    // partial tiles of the 8 waves, added in wave order
+    __syncthreads();   // every wave is done with the staged activations
+    floatx4 *red = reinterpret_cast<floatx4 *>(lds);
+    red[(2 * wave) * kWave + lane] = acc;
+    red[(2 * wave + 1) * kWave + lane] = accs;
+    __syncthreads();
+    if (wave != 0) return;
+    floatx4 v = red[lane], xs4 = red[kWave + lane];
+#pragma unroll
+    for (int ww = 1; ww < kQmvWaves; ++ww) {
+        v += red[(2 * ww) * kWave + lane];
+        xs4 += red[(2 * ww + 1) * kWave + lane];
+    }
+    // D[4q + r][col]: the lo column is added to the hi one
+    const float xs = xs4[0] + __shfl_xor(xs4[0], 1, kWave);
+    const int ob = row0 + 4 * q;
+    float res[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const float vv = v[r] + __shfl_xor(v[r], 1, kWave);
+        const int o = min(ob + r, a.O - 1);
+        const float sc = a.scale ? a.scale[o] : 1.f;
+        res[r] = sc * (vv - OFF * xs);
+    }
+    const int tok = col >> 1;
+    if ((col & 1) == 0 && tok < nt) {
+        float *yp = a.y + (int64_t)(t0 + tok) * a.O;
+        if (a.y_vec4 && ob + 3 < a.O) {
+            *reinterpret_cast<float4 *>(yp + ob) = make_float4(res[0], res[1], res[2], res[3]);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (ob + r < a.O) yp[ob + r] = res[r];
+        }
+    }
+}
+
+template <int FMT, int NKW>
+hipError_t launch_q1(const QmvArgs &a, hipStream_t st)
+{
+    const int ntiles = (a.O + 15) / 16;
+    const int passes = (a.S + kQ1Tpp - 1) / kQ1Tpp;
+    const int64_t grid = (int64_t)(ntiles + 7) / 8 * 8 * passes;
+    if (grid <= 0 || grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const int ntmax = a.S < kQ1Tpp ? a.S : kQ1Tpp;
+    const size_t stage = (size_t)a.nkb * MF<FMT>::STEPS * 4 * (2 * ntmax) * 16;
+    const size_t red = (size_t)kQmvWaves * 2 * kWave * 16;
+    const size_t lds = stage > red ? stage : red;
+    auto kern = k_qmv1<FMT, NKW>;
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * kQmvWaves), lds, st, a, passes, ntiles);
+    return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_q1_nkw(const QmvArgs &a, int nkw, hipStream_t st)
+{
+    switch (nkw) {
+    case 1: return launch_q1<FMT, 1>(a, st);
+    case 2: return launch_q1<FMT, 2>(a, st);
+    case 3: return launch_q1<FMT, 3>(a, st);
+    case 4: return launch_q1<FMT, 4>(a, st);
+    case 5: return launch_q1<FMT, 5>(a, st);
+    case 6: return launch_q1<FMT, 6>(a, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 template <int FMT, int MT>
 hipError_t launch_q(const QmvArgs &a, hipStream_t st)
 {
@@ -274,6 +476,18 @@ hipError_t qmv_launch(QmvArgs a, int fmt, hipStream_t st)
     const int KB = fmt == kI8 ? MF<kI8>::KB : fmt == kI4 ? MF<kI4>::KB : MF<kI2>::KB;
     a.nkb = (a.I + KB - 1) / KB;
     a.y_vec4 = a.O % 4 == 0 && ((uintptr_t)a.y & 15u) == 0;
+    // one shot for one pass (measured faster there: int4 12288 x 6144 at one
+    // row 10.9 us against 14.8 us for the rounds below; from two passes on
+    // the rounds win) while a wave's k-blocks fit its registers
+    const int nkw = (a.nkb + kQmvWaves - 1) / kQmvWaves;
+    if (a.S <= kQ1Tpp && nkw <= 6) {
+        switch (fmt) {
+        case kI8: return launch_q1_nkw<kI8>(a, nkw, st);
+        case kI4: return launch_q1_nkw<kI4>(a, nkw, st);
+        case kI2: return launch_q1_nkw<kI2>(a, nkw, st);
+        default: return hipErrorInvalidValue;
+        }
+    }
     // 64 rows per block once that still gives at least 128 blocks (measured
     // faster on the 12288-row matrices), else 32
     const bool wide = (int64_t)a.O >= 64 * 128;
