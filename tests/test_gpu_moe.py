@@ -121,8 +121,9 @@ def test_moe_gemv_tiles_aligned(dev, orc, fmt):
     x = synth.activations(g, S, D)
     idx, w = synth.routing_uniform(g, S, K, E)
     idx[0, :] = [3, 4, 5, 6]
-    idx[1:12, 0] = 3          # one expert with many rows (several token passes)
-    for s in range(1, 12):
+    # one expert with 20 rows: two token passes, the second partial, with a
+    # dead second N-tile (passes of 16 rows as two 8-row tiles)
+    for s in range(1, 20):
         row = [3] + [e for e in g.permutation(E) if e != 3][:K - 1]
         idx[s] = row
     announce("moe tiles", fmt)

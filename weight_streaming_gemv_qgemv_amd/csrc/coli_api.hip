@@ -16,9 +16,13 @@
 #include "coli_gemv.h"
 #include "coli_pre.h"
 #include "coli_qmv.h"
+
 #include "coli_internal.h"
 #include "coli_router.h"
 #include "coli_stages.h"
+
+static_assert(COLI_MM_TPP_FP32 == coli::kDecTpp, "decode pass size");
+static_assert(COLI_MM_TPP_BF16 == coli::kPreTpp, "prefill pass size");
 
 namespace coli {
 
@@ -291,8 +295,8 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
                     al16(ex->w_down) && (ex->fmt == COLI_I8 || ex->fmt == COLI_I4 || ex->fmt == COLI_I2);
     const bool sh_mm = mm && sh && sh->fmt == ex->fmt && sh->F == F && al16(sh->w_gate) &&
                        al16(sh->w_up) && al16(sh->w_down);
-    // matrix-core passes: 8 rows as bf16 hi/lo column pairs (fp32-level
-    // accuracy) or 16 rows rounded once to bf16
+    // matrix-core passes: 16 rows as bf16 hi/lo column pairs (fp32-level
+    // accuracy) or 64 rows rounded once to bf16
     const int bf16 = prec == COLI_PREC_BF16 ? 1 : 0;
     const int tpp = bf16 ? COLI_MM_TPP_BF16 : COLI_MM_TPP_FP32;
     int32_t *work = reinterpret_cast<int32_t *>(ws + L.work);

@@ -13,11 +13,15 @@ namespace coli {
 // and its lo unit, so a row is 4 * kpad bytes.
 inline int64_t dec_row_bytes(int64_t kpad) { return 4 * kpad; }
 
+// Rows per pass of the decode kernels (two MFMA N-tiles of 8 rows, each row
+// a bf16 hi/lo column pair).
+constexpr int kDecTpp = 16;
+
 // Groups: group g < ngroups is expert g, whose rows are the grouped rows
 // offsets[g] .. offsets[g+1]-1; group ngroups (when has_extra) is the shared
 // expert, rows x_row0 .. x_row0 + x_rows - 1.  The work list (built on the
 // device) holds one entry g | pass << 11 per group-pass, a pass being up to
-// 8 rows of one group; *n_work is the number of entries.
+// kDecTpp rows of one group; *n_work is the number of entries.
 struct DecArgs {
     const uint8_t *w[2];
     const float *s[2];

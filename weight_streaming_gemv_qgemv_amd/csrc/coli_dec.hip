@@ -9,14 +9,15 @@
 // with Vg, Vu, Vd the dequantised int8 / int4 / int2 weights.
 //
 // Layout of the work:
-//   * a pass is up to 8 rows of one group; row t of the pass takes MFMA
-//     columns 2t (bf16 hi of its activations) and 2t+1 (bf16 lo), so the
-//     16-column tile carries fp32-accurate activations (|x - hi - lo| <=
-//     2^-16 |x|);
+//   * a pass is up to 16 rows of one group, two MFMA N-tiles of 8 rows; row
+//     t of a tile takes columns 2t (bf16 hi of its activations) and 2t+1
+//     (bf16 lo), so the tile carries fp32-accurate activations (|x - hi -
+//     lo| <= 2^-16 |x|); the second tile's products are skipped when the
+//     pass has 8 rows or fewer;
 //   * activations come from "row tables" (coli_dec.h): one row per
-//     activation row, in fragment order; a lane reads the 16-byte unit of its
-//     own column straight from global memory (L2), so the waves of a block
-//     never synchronise;
+//     activation row, in fragment order.  Per k-block the 4 waves of a block
+//     copy the pass's units into LDS by DMA (each unit once per block), one
+//     k-block ahead of the products, with one barrier per k-block;
 //   * sum(x) per column, needed to remove OFF * sum(x) from the code
 //     products, is one more MFMA per step against a tile of ones, over the
 //     very bf16 values the products use;
@@ -25,9 +26,8 @@
 //     are shared out to the XCDs so that the passes of one group run on the
 //     same XCD at about the same time (later passes find the weights in its
 //     L2), persistent blocks walk them in order, and each wave loads the
-//     next k-block's weights and activations while it multiplies the
-//     current one, and the next item's first k-block during the current
-//     item's last.
+//     next k-block's weights while it multiplies the current one, and the
+//     next item's first k-block during the current item's last.
 #include "coli_device.h"
 #include "coli_frag.h"
 #include "coli_dec.h"
@@ -38,7 +38,7 @@ namespace {
 
 constexpr int kDecWaves = 4;
 constexpr int kDecXcds = 8;
-constexpr int kDecTpp = 8;   // rows per pass
+constexpr int kDecNT = kDecTpp / 8;   // MFMA N-tiles per pass (8 rows: hi/lo column pairs)
 template <int M> struct DecTiles { static constexpr int MT = M == 2 ? 2 : 4; };
 
 // ---------------------------------------------------------------- row tables
@@ -104,14 +104,30 @@ __global__ __launch_bounds__(256) void k_xrows(const float *__restrict__ x, int6
 }
 
 // ---------------------------------------------------------------- products
+// LDS DMA of 16 bytes per lane (lane L's bytes land at lds + 16 L), issued
+// from inline assembly: the compiler does not see it, so it neither makes
+// LDS reads wait for it nor counts it in its own waits -- the kernel orders
+// and waits for these loads itself.
+__device__ __forceinline__ void dma16(const void *g, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
+
+typedef __attribute__((address_space(3))) const void lds_void;
+
 template <int FMT, int M>
 __global__ __launch_bounds__(256) void k_dec(DecArgs a)
 {
     using T = MF<FMT>;
     constexpr int STEPS = T::STEPS, KB = T::KB, SEGS = T::SEGS, BITS = T::BITS, SPS = T::SPS;
     constexpr int MT = DecTiles<M>::MT, RPW = 16 * MT, RPB = kDecWaves * RPW;
+    constexpr int NT = kDecNT;
     constexpr float OFF = T::OFF;
     constexpr uint32_t kChunkStep = 4 * 32;   // bytes between one step's chunks and the next's
+    constexpr int UNITS = NT * STEPS * kWave; // 16-byte units of one staged k-block
+    constexpr int IPW = NT * STEPS / kDecWaves;   // DMA instructions per wave and k-block
+    static_assert(IPW >= 1 && STEPS % IPW == 0, "a wave stages steps of one N-tile");
+    __shared__ uint4 bsA[UNITS], bsB[UNITS];   // staged k-blocks (even, odd)
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = lane & 15, q = lane >> 4, lrow = lane >> 2, lchunk = lane & 3;
@@ -130,7 +146,7 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
     const int gp_cnt = M == 2 ? (int)((int64_t)n_gp * (xcd + 1) / kDecXcds) - gp_lo : n_gp;
     const int tpx = M == 2 ? a.tiles : (a.tiles - xcd + kDecXcds - 1) / kDecXcds;   // tiles per pass here
     const int n_items = gp_cnt * tpx;
-    if (lb >= n_items) return;
+    if (lb >= n_items) return;                          // whole block, before any barrier
     const int nkb = a.kpad / KB;                        // even and >= 4 (kpad: multiple of 1024)
     constexpr uint32_t kbytes = KB * BITS / 8;
     // a lane's 16-byte segment past the row end is clamped to the row's last
@@ -138,13 +154,15 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
     const uint32_t last_seg = (uint32_t)(a.rb - 16 - 16 * lchunk);
     const uint8_t *actb = reinterpret_cast<const uint8_t *>(a.act);
     const uint32_t arow = (uint32_t)(4 * a.kpad);       // bytes per row-table row
+    // the N-tile and the first step this wave stages
+    const int nw = wave * IPW / STEPS, s0 = wave * IPW % STEPS;
 
     struct It {
         int gp, tile, nt, r0t, Og;
         const uint8_t *wb[M];
         const float *sc[M];
         uint32_t roff[MT];   // this lane's row (clamped) * rb + its 16-byte chunk
-        uint32_t boff;       // this lane's unit in its activation row (bytes)
+        uint32_t doff;       // the unit this lane stages, in its activation row (bytes)
     };
     auto make = [&](It &c, int it) {
         c.gp = __builtin_amdgcn_readfirstlane(gp_lo + it / tpx);
@@ -178,9 +196,10 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
             c.roff[mt] = (uint32_t)(min(obase + 16 * mt + lrow, c.Og - 1) * a.rb) + 16 * lchunk;
-        // activation row of each pass row, from scalar loads (dead columns
-        // repeat the last live row; their results are never stored)
-        const int t = col >> 1;
+        // activation row of the pass row whose unit this lane stages (pass
+        // row 8 nw + col / 2), from scalar loads; dead rows repeat the last
+        // live one (their results are never stored)
+        const int t = 8 * nw + (col >> 1);
         int ar = 0;
 #pragma unroll
         for (int u = 0; u < kDecTpp; ++u) {
@@ -191,7 +210,7 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
             else au = cload(a.row_pair + gr) / a.K;
             ar = t == u ? au : ar;
         }
-        c.boff = (uint32_t)ar * arow + 32 * q + 16 * (col & 1);
+        c.doff = (uint32_t)ar * arow + 32 * q + 16 * (col & 1);
     };
     auto loadW = [&](const It &c, int kbi, uint4 (&w)[M][MT][SEGS]) {
         const uint32_t b0 = (uint32_t)kbi * kbytes;
@@ -203,25 +222,36 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
                 for (int sg = 0; sg < SEGS; ++sg)
                     w[m][mt][sg] = gload16(c.wb[m] + (c.roff[mt] + min(b0 + 64 * sg, last_seg)));
     };
-    auto loadB = [&](const It &c, int kbi, uint4 (&b)[STEPS]) {
-        const uint32_t o = c.boff + (uint32_t)kbi * (STEPS * kChunkStep);
+    // Activations of k-block kbi into LDS by DMA: unit (n, step s, lane L)
+    // at (n STEPS + s) 64 + L is the B operand of lane L for N-tile n (pass
+    // rows 8n..8n+7) at step s.  Wave w issues IPW of the NT x STEPS
+    // instructions -- N-tile nw, steps s0.. -- none for a dead N-tile.
+    auto stageB = [&](const It &c, int kbi, const uint4 *buf) {
+        if (8 * nw >= c.nt) return;                     // uniform
+        const uint32_t o = c.doff + (uint32_t)(kbi * STEPS + s0) * kChunkStep;
+        const uint32_t lbase = (uint32_t)(uintptr_t)(const lds_void *)(buf + (nw * STEPS + s0) * kWave);
 #pragma unroll
-        for (int s = 0; s < STEPS; ++s) b[s] = gload16(actb + (o + s * kChunkStep));
+        for (int i = 0; i < IPW; ++i)
+            dma16(actb + (o + (uint32_t)i * kChunkStep), __builtin_amdgcn_readfirstlane(lbase + i * 1024));
     };
 
-    floatx4 acc[M][MT], accs;
+    floatx4 acc[M][MT][NT], accs[NT];
 #pragma unroll
-    for (int m = 0; m < M; ++m)
+    for (int n = 0; n < NT; ++n) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[m][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-    accs = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[m][mt][n] = floatx4{0.f, 0.f, 0.f, 0.f};
+        accs[n] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
     const uint32_t one2 = opaque_v(0x3F803F80u);       // bf16 (1, 1)
     const uint4 ones = make_uint4(one2, one2, one2, one2);
 
-    // one k-block: weights moved into the operand layout in place (lane
-    // (q, col) gets row col, chunk q, from lane 4 col + q), then per MFMA
-    // step the M x MT code products and the column sums
-    auto compute = [&](uint4 (&w)[M][MT][SEGS], const uint4 (&b)[STEPS]) {
+    // one k-block over the first NL N-tiles: weights moved into the operand
+    // layout in place (lane (q, col) gets row col, chunk q, from lane 4 col
+    // + q), then per MFMA step the M x MT code products and the column sums
+    auto compute_n = [&](auto nl, uint4 (&w)[M][MT][SEGS], const uint4 *buf) {
+        constexpr int NL = decltype(nl)::value;
 #pragma unroll
         for (int m = 0; m < M; ++m)
 #pragma unroll
@@ -236,13 +266,26 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
                 }
 #pragma unroll
         for (int s2 = 0; s2 < STEPS; ++s2) {
+            uint4 b[NL];
+#pragma unroll
+            for (int n = 0; n < NL; ++n) b[n] = buf[(n * STEPS + s2) * kWave + lane];
 #pragma unroll
             for (int m = 0; m < M; ++m)
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                    acc[m][mt] = mfma(codes<FMT>(w[m][mt][s2 / SPS], s2 % SPS), b[s2], acc[m][mt]);
-            accs = mfma(ones, b[s2], accs);
+                for (int mt = 0; mt < MT; ++mt) {
+                    const uint4 cw = codes<FMT>(w[m][mt][s2 / SPS], s2 % SPS);
+#pragma unroll
+                    for (int n = 0; n < NL; ++n) acc[m][mt][n] = mfma(cw, b[n], acc[m][mt][n]);
+                }
+#pragma unroll
+            for (int n = 0; n < NL; ++n) accs[n] = mfma(ones, b[n], accs[n]);
         }
+    };
+    auto compute = [&](uint4 (&w)[M][MT][SEGS], const uint4 *buf, int ntl) {
+        if constexpr (NT == 2) {
+            if (ntl == 2) { compute_n(std::integral_constant<int, 2>{}, w, buf); return; }
+        }
+        compute_n(std::integral_constant<int, 1>{}, w, buf);
     };
 
     float sreg[M][MT][4];
@@ -256,102 +299,134 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
                 for (int r = 0; r < 4; ++r)
                     sreg[m][mt][r] = gloadf(c.sc[m] + min(obase + 16 * mt + 4 * q + r, c.Og - 1));
     };
-    // D[4q + r][col] of tile (m, mt); the lo column is added to the hi one
+    // D[4q + r][col] of tile (m, mt, n); the lo column is added to the hi one
     auto epilogue = [&](const It &c) {
         const int obase = c.tile * RPB + wave * RPW;
-        const int tok = col >> 1;
-        const bool live = tok < c.nt;
-        const float xs = accs[0] + __shfl_xor(accs[0], 1, kWave);   // sum of hi + lo over k
+        const int ntl = (c.nt + 7) / 8;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            float v[M][4];
+        for (int n = 0; n < NT; ++n) {
+            if (n >= ntl) break;                        // uniform
+            const int tok = 8 * n + (col >> 1);
+            const bool live = tok < c.nt;
+            const float xs = accs[n][0] + __shfl_xor(accs[n][0], 1, kWave);   // sum of hi + lo over k
 #pragma unroll
-            for (int m = 0; m < M; ++m)
+            for (int mt = 0; mt < MT; ++mt) {
+                float v[M][4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) v[m][r] = acc[m][mt][r] + __shfl_xor(acc[m][mt][r], 1, kWave);
-            const int ob = obase + 16 * mt + 4 * q;
-            float res[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float y = sreg[0][mt][r] * (v[0][r] - OFF * xs);
-                if constexpr (M == 2) {
-                    const float u = sreg[1][mt][r] * (v[1][r] - OFF * xs);
-                    y = silu_f(y) * u;
-                }
-                res[r] = ob + r < c.Og ? y : 0.f;
-            }
-            if (live && (col & 1) == 0) {
-                float *op = a.out + (int64_t)(c.r0t + tok) * a.ldo;
-                if (a.out_vec4 && ob + 3 < c.Og) {
-                    *reinterpret_cast<float4 *>(op + ob) = make_float4(res[0], res[1], res[2], res[3]);
-                } else {
+                for (int m = 0; m < M; ++m)
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        if (ob + r < c.Og) op[ob + r] = res[r];
-                }
-            }
-            if constexpr (M == 2) {
-                if (a.hf) {
-                    // h as the down product's row table: this lane's 4
-                    // outputs are half of one unit (8 slots of a chunk), the
-                    // partner lane (q ^ 1, int2: q ^ 2) holds the other half,
-                    // and the lower lane of the pair stores the unit; even
-                    // columns store hi units, odd columns lo units
-                    constexpr int PX = FMT == kI2 ? 32 : 16;
-                    const bool lowq = FMT == kI2 ? q < 2 : (q & 1) == 0;
-                    uint32_t hv[4];
+                        v[m][r] = acc[m][mt][n][r] + __shfl_xor(acc[m][mt][n][r], 1, kWave);
+                const int ob = obase + 16 * mt + 4 * q;
+                float res[4];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const uint16_t h16 = bf16_rne(res[r]);
-                        hv[r] = (col & 1) ? bf16_rne(res[r] - bf16_f(h16)) : h16;
+                for (int r = 0; r < 4; ++r) {
+                    float y = sreg[0][mt][r] * (v[0][r] - OFF * xs);
+                    if constexpr (M == 2) {
+                        const float u = sreg[1][mt][r] * (v[1][r] - OFF * xs);
+                        y = silu_f(y) * u;
                     }
-                    uint32_t pv[4];
+                    res[r] = ob + r < c.Og ? y : 0.f;
+                }
+                if (live && (col & 1) == 0) {
+                    float *op = a.out + (int64_t)(c.r0t + tok) * a.ldo;
+                    if (a.out_vec4 && ob + 3 < c.Og) {
+                        *reinterpret_cast<float4 *>(op + ob) = make_float4(res[0], res[1], res[2], res[3]);
+                    } else {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) pv[r] = (uint32_t)__shfl_xor((int)hv[r], PX, kWave);
-                    if (lowq && live && ob < a.hf_kpad) {
-                        int cc, j;
-                        pos_of<FMT>(ob, cc, j);
-                        uint4 u;
-                        if constexpr (FMT == kI8)
-                            u = make_uint4(hv[0] | hv[1] << 16, hv[2] | hv[3] << 16,
-                                           pv[0] | pv[1] << 16, pv[2] | pv[3] << 16);
-                        else
-                            u = make_uint4(hv[0] | pv[0] << 16, hv[1] | pv[1] << 16,
-                                           hv[2] | pv[2] << 16, hv[3] | pv[3] << 16);
-                        *reinterpret_cast<uint4 *>(a.hf + (int64_t)(c.r0t + tok) * 2 * a.hf_kpad +
-                                                   (int64_t)(2 * cc + (col & 1)) * 8) = u;
+                        for (int r = 0; r < 4; ++r)
+                            if (ob + r < c.Og) op[ob + r] = res[r];
+                    }
+                }
+                if constexpr (M == 2) {
+                    if (a.hf) {
+                        // h as the down product's row table: this lane's 4
+                        // outputs are half of one unit (8 slots of a chunk),
+                        // the partner lane (q ^ 1, int2: q ^ 2) holds the
+                        // other half, and the lower lane of the pair stores
+                        // the unit; even columns store hi units, odd columns
+                        // lo units
+                        constexpr int PX = FMT == kI2 ? 32 : 16;
+                        const bool lowq = FMT == kI2 ? q < 2 : (q & 1) == 0;
+                        uint32_t hv[4];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const uint16_t h16 = bf16_rne(res[r]);
+                            hv[r] = (col & 1) ? bf16_rne(res[r] - bf16_f(h16)) : h16;
+                        }
+                        uint32_t pv[4];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) pv[r] = (uint32_t)__shfl_xor((int)hv[r], PX, kWave);
+                        if (lowq && live && ob < a.hf_kpad) {
+                            int cc, j;
+                            pos_of<FMT>(ob, cc, j);
+                            uint4 u;
+                            if constexpr (FMT == kI8)
+                                u = make_uint4(hv[0] | hv[1] << 16, hv[2] | hv[3] << 16,
+                                               pv[0] | pv[1] << 16, pv[2] | pv[3] << 16);
+                            else
+                                u = make_uint4(hv[0] | pv[0] << 16, hv[1] | pv[1] << 16,
+                                               hv[2] | pv[2] << 16, hv[3] | pv[3] << 16);
+                            *reinterpret_cast<uint4 *>(a.hf + (int64_t)(c.r0t + tok) * 2 * a.hf_kpad +
+                                                       (int64_t)(2 * cc + (col & 1)) * 8) = u;
+                        }
                     }
                 }
             }
         }
 #pragma unroll
-        for (int m = 0; m < M; ++m)
+        for (int n = 0; n < NT; ++n) {
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) acc[m][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-        accs = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int m = 0; m < M; ++m)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) acc[m][mt][n] = floatx4{0.f, 0.f, 0.f, 0.f};
+            accs[n] = floatx4{0.f, 0.f, 0.f, 0.f};
+        }
     };
 
-    // Every load below is issued unconditionally (selected sources), so the
-    // compiler's waits count them exactly: each product waits only for its
-    // own k-block, with the next k-block's weights in flight.
+    // the staged k-block is complete once this wave's DMA loads are: they
+    // were issued before the NW weight loads of the next k-block
+    constexpr int NW = M * MT * SEGS;
+    // Half-step j (k-block j in LDS buffer rd, the next in wr):
+    //   1. the next weights are requested (NW loads);
+    //   2. wait until only those are in flight: this k-block's weights and
+    //      this wave's DMA of its activations (issued before them) are done;
+    //   3. barrier: every wave's DMA of k-block j is done, and every wave is
+    //      past the products of k-block j-1, which read wr;
+    //   4. the next k-block's activations are requested into wr (DMA);
+    //   5. the products of k-block j.
+    // The compiler's own wait for this k-block's weights is met by step 2.
+    auto step_sync = [&]() {
+        // vmcnt <= NW (bits 3:0 and 15:14), lgkmcnt = 0, expcnt not waited on
+        __builtin_amdgcn_s_waitcnt((NW & 15) | ((NW >> 4) << 14) | (7 << 4));
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+    auto half = [&](const uint4 *rd, const uint4 *wr, const It &snext, int skb, const It &wsrc, int wkb,
+                    uint4 (&wn)[M][MT][SEGS], uint4 (&wc)[M][MT][SEGS], int ntl) {
+        loadW(wsrc, wkb, wn);
+        step_sync();
+        stageB(snext, skb, wr);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(wc, rd, ntl);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // prologue: the first item's first weights, then the DMA of its first
+    // k-block's activations into bsA.  Even k-blocks are staged in bsA, odd
+    // ones in bsB (nkb is even).
     It cur;
     make(cur, lb);
-    int jn = lb + bpx;
-    uint4 wA[M][MT][SEGS], wB[M][MT][SEGS], bA[STEPS], bB[STEPS];
-    loadB(cur, 0, bA);
+    uint4 wA[M][MT][SEGS], wB[M][MT][SEGS];
     loadW(cur, 0, wA);
+    stageB(cur, 0, bsA);
+    int jn = lb + bpx;
     for (;;) {
+        const int ntl = (cur.nt + 7) / 8;            // live N-tiles
         for (int k = 0; k < nkb - 2; k += 2) {
-            loadB(cur, k + 1, bB);
-            loadW(cur, k + 1, wB);
-            __builtin_amdgcn_sched_barrier(0);
-            compute(wA, bA);
-            __builtin_amdgcn_sched_barrier(0);
-            loadB(cur, k + 2, bA);
-            loadW(cur, k + 2, wA);
-            __builtin_amdgcn_sched_barrier(0);
-            compute(wB, bB);
-            __builtin_amdgcn_sched_barrier(0);
+            half(bsA, bsB, cur, k + 1, cur, k + 1, wB, wA, ntl);
+            half(bsB, bsA, cur, k + 2, cur, k + 2, wA, wB, ntl);
         }
         // last two k-blocks: the epilogue's scales, then the next item's
         // first k-block (a copy of this item's when there is none)
@@ -359,21 +434,15 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
         It nxt = cur;
         if (has_nxt) make(nxt, jn);
         load_epi(cur);
-        loadB(cur, nkb - 1, bB);
-        loadW(cur, nkb - 1, wB);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(wA, bA);
-        __builtin_amdgcn_sched_barrier(0);
-        loadB(nxt, 0, bA);
-        loadW(nxt, 0, wA);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(wB, bB);
-        __builtin_amdgcn_sched_barrier(0);
+        half(bsA, bsB, cur, nkb - 1, cur, nkb - 1, wB, wA, ntl);
+        half(bsB, bsA, nxt, 0, nxt, 0, wA, wB, ntl);
         epilogue(cur);
         if (!has_nxt) break;
         cur = nxt;
         jn += bpx;
     }
+    // every wave's DMA is complete before the block ends
+    __builtin_amdgcn_s_waitcnt(0);
 }
 
 int dec_resident_blocks(const void *kern, int *cache)

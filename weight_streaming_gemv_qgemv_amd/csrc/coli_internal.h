@@ -14,7 +14,7 @@
 /* rows per pass of the matrix-core expert kernels: in fp32 precision 8, as
  * bf16 hi/lo column pairs of one 16-column MFMA tile; in bf16 precision 64,
  * one column each over four tiles */
-#define COLI_MM_TPP_FP32 8
+#define COLI_MM_TPP_FP32 16
 #define COLI_MM_TPP_BF16 64
 
 /* input width of the matrix-core products, rounded up to whole 1024-element
