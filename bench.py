@@ -74,8 +74,11 @@ def recorded_traffic(workload, kernel_key):
     copy), or None when there is none for this workload or the kernel source
     has changed since the counters were taken."""
     import hashlib
-    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
-                        "moe_layer_decode64_traffic.md")
+    files = {"moe_layer_decode_64": "moe_layer_decode64_traffic.md",
+             "moe_layer_prefill_2048_bf16": "moe_layer_prefill2048_traffic.md"}
+    if workload not in files:
+        return None
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", files[workload])
     try:
         line = next(l for l in open(path) if l.startswith("traffic-json: "))
         rec = json.loads(line[len("traffic-json: "):])
@@ -229,6 +232,7 @@ def run_prefill2048(args, dev):
     return dict(workload="moe_layer_prefill_2048_bf16", ms=ms, wall=wall, step_bytes=step_bytes,
                 tokens=S, stages=stages, uniq=uniq, flops=flops,
                 dominant=dict(kernel="k_pre<I4,2> (grouped expert gate/up + SwiGLU, bf16 matrix cores)",
+                              traffic=recorded_traffic("moe_layer_prefill_2048_bf16", "k_pre<2, 2>"),
                               bytes_per_launch=(uniq + 1) * gu + S * D * 4 + rows * F * 4,
                               flops_per_launch=gu_flops, ms_per_launch=gu_ms / max(gu_n, 1),
                               launches=gu_n))
@@ -387,7 +391,8 @@ def main():
         line["dtype"] = "bf16 (int4 weights, fp32 accumulate)"
         line["roofline"] = {"bound": "mfma", "achieved": round(tf, 2) if tf else None,
                             "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                            "frac": round(tf / BF16_PEAK_TFLOPS, 4) if tf else None, "traffic": None,
+                            "frac": round(tf / BF16_PEAK_TFLOPS, 4) if tf else None,
+                            "traffic": dom.get("traffic"),
                             "kernel": dom["kernel"], "flops_per_launch": dom["flops_per_launch"],
                             "ms_per_launch": round(dom["ms_per_launch"], 5)}
         line["layer_mfma_utilisation"] = round(r["flops"] / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
