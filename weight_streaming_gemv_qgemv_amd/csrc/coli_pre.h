@@ -10,7 +10,7 @@ namespace coli {
 // Rows per pass of the prefill kernels (4 MFMA N-tiles of 16 columns).
 constexpr int kPreTpp = 64;
 // Weight rows per item of the paired (M = 2) and single (M = 1) product.
-constexpr int kPreRowsPerBlock = 128;
+constexpr int kPreRowsPerBlock = 256;
 
 // bf16 row tables: one row per activation row, kpad elements rounded once to
 // bf16 in fragment order (16-byte units of 8 elements), 2 * kpad bytes a row.
@@ -38,7 +38,7 @@ struct PreArgs {
     int out_vec4;
     // M == 2 only: the result as the next product's bf16 row table (rows =
     // grouped rows, hf_kpad elements) and its partial sums per row:
-    // hpart[r * nparts + p], p = tile * 4 + wave
+    // hpart[r * nparts + p], p = tile * 8 + wave
     uint16_t *hf;
     int hf_kpad;
     float *hpart;

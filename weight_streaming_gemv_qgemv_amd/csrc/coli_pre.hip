@@ -11,7 +11,7 @@
 // sum(x) being the sum of the stored bf16 activations of the row, is
 // removed per output.
 //
-// An item is (group-pass, 128 weight rows); a block of 4 waves takes it,
+// An item is (group-pass, 256 weight rows); a block of 8 waves takes it,
 // each wave 32 weight rows x all 64 pass rows (4 MFMA N-tiles), so each
 // weight byte read from memory meets 64 activation rows.  Per k-block the
 // pass rows' activations are staged from their bf16 row tables into LDS
@@ -30,7 +30,7 @@ namespace {
 
 typedef __attribute__((address_space(3))) const void lds_void;
 
-constexpr int kPreWaves = 4;
+constexpr int kPreWaves = 8;
 constexpr int kPreXcds = 8;
 constexpr int kPreNT = kPreTpp / 16;   // N-tiles per pass
 constexpr int kPreMT = 2;              // 16-row weight tiles per wave
@@ -126,7 +126,7 @@ __device__ __forceinline__ void dma16(const void *g, uint32_t lds)
 }
 
 template <int FMT, int M>
-__global__ __launch_bounds__(256) void k_pre(PreArgs a)
+__global__ __launch_bounds__(64 * kPreWaves) void k_pre(PreArgs a)
 {
     using T = MF<FMT>;
     constexpr int STEPS = T::STEPS, KB = T::KB, SEGS = T::SEGS, BITS = T::BITS, SPS = T::SPS;
@@ -226,17 +226,19 @@ __global__ __launch_bounds__(256) void k_pre(PreArgs a)
     // read).  One instruction fills one (n, s): lane L takes row 16 n + L / 4
     // and chunk 4 s + ((L & 3) ^ ((L >> 3) & 3)) -- 64 contiguous bytes of
     // each of 16 rows.
-    // Wave w stages N-tile n = w.
+    // Wave w issues instructions w SPW .. w SPW + SPW - 1 of the NT x STEPS
+    // (N-tile nw, steps s0..).
     constexpr int SPW = NT * STEPS / kPreWaves;          // instructions per wave
-    static_assert(SPW == STEPS, "one N-tile per wave");
+    static_assert(SPW >= 1 && STEPS % SPW == 0, "a wave stages steps of one N-tile");
+    const int nw = wave * SPW / STEPS, s0 = wave * SPW % STEPS;
     const int dq = (lane & 3) ^ ((lane >> 3) & 3);
     auto stageB = [&](int par, int kbi, const uint4 *buf) {
-        const uint32_t rowoff = (uint32_t)lrow[par][16 * wave + (lane >> 2)] * arow +
-                                (uint32_t)kbi * (CH * 16) + (uint32_t)dq * 16;
-        const uint32_t lbase = (uint32_t)(uintptr_t)(const lds_void *)(buf + wave * STEPS * 64);
+        const uint32_t rowoff = (uint32_t)lrow[par][16 * nw + (lane >> 2)] * arow +
+                                (uint32_t)kbi * (CH * 16) + (uint32_t)(s0 * 64 + dq * 16);
+        const uint32_t lbase = (uint32_t)(uintptr_t)(const lds_void *)(buf + (nw * STEPS + s0) * 64);
 #pragma unroll
-        for (int s = 0; s < STEPS; ++s)
-            dma16(actb + (rowoff + (uint32_t)s * 64), __builtin_amdgcn_readfirstlane(lbase + s * 1024));
+        for (int i = 0; i < SPW; ++i)
+            dma16(actb + (rowoff + (uint32_t)i * 64), __builtin_amdgcn_readfirstlane(lbase + i * 1024));
     };
 
     floatx4 acc[M][MT][NT];
@@ -443,7 +445,7 @@ int pre_resident_blocks(const void *kern, int *cache)
     int cus = 0, per = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kern, 256, 0) != hipSuccess || per <= 0)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kern, 64 * kPreWaves, 0) != hipSuccess || per <= 0)
         per = 1;
     cache[dev] = cus * per;
     return cache[dev];
@@ -459,7 +461,7 @@ hipError_t launch_pre(const PreArgs &a, int64_t items, hipStream_t st)
     int64_t grid = (items + kPreXcds - 1) / kPreXcds * kPreXcds;
     if (grid > cap) grid = cap;
     if (grid < kPreXcds) grid = kPreXcds;
-    hipLaunchKernelGGL((k_pre<FMT, M>), dim3((unsigned)grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_pre<FMT, M>), dim3((unsigned)grid), dim3(64 * kPreWaves), 0, st, a);
     return hipGetLastError();
 }
 
