@@ -413,6 +413,37 @@ int cor_moe(const cor_experts *ex, const cor_mlp *sh, const float *x, int S,
 }
 
 /* ------------------------------------------------------------------------
+ * Layer tail around the MoE block [glm.c@98759bf -- rmsnorm; the layer
+ * forward's post-attention half]: the residual stream x is normalised with
+ * the post-attention RMSNorm, the MoE block runs on the normalised rows, and
+ * its output is added back onto x.
+ *
+ * RMSNorm, in the precision the pages fix: the mean square is accumulated in
+ * fp64 (each square exact in fp64), converted once to fp32, eps added in
+ * fp32, r = 1 / sqrtf(.) in fp32, and each output is (x * r) * w rounded in
+ * fp32 after each product.  This is a function the pages define with fp32
+ * intermediates, so the oracle reproduces those roundings instead of
+ * carrying fp64 through.
+ * ------------------------------------------------------------------------ */
+void cor_rmsnorm(const float *x, const float *w, int S, int D, float eps, float *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int s = 0; s < S; ++s) {
+        const float *xs = x + (int64_t)s * D;
+        float *os = out + (int64_t)s * D;
+        double ms = 0.0;
+        for (int i = 0; i < D; ++i) ms += (double)xs[i] * (double)xs[i];
+        volatile float mean = (float)(ms / D);   /* one fp32 rounding, as on the pages */
+        volatile float den = sqrtf(mean + eps);
+        const float r = 1.0f / den;
+        for (int i = 0; i < D; ++i) {
+            volatile float xr = xs[i] * r;
+            os[i] = xr * w[i];
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------
  * Weight preparation helpers the pages define for filling QT tensors from
  * f32 weights; used by the tests to produce packed rows from known values,
  * never by the products above.

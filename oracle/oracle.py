@@ -55,6 +55,8 @@ def lib():
         L.cor_moe.restype = i32
         L.cor_moe.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, vp, i64,
                               vp, vp, vp, vp, vp, vp]
+        L.cor_rmsnorm.restype = None
+        L.cor_rmsnorm.argtypes = [vp, vp, i32, i32, C.c_float, vp]
         for name in ("cor_quantize_rows", "cor_pack_int4", "cor_pack_int2"):
             f = getattr(L, name)
             f.restype = None
@@ -184,6 +186,29 @@ def moe(ex: dict, shared: dict | None, x, idx, w, intermediates: bool = False):
                        rows, *ptrs)
     assert rc == 0, rc
     return res
+
+
+def rmsnorm(x, w, eps: float):
+    """Post-attention RMSNorm of each row of x [S, D] with weight w [D]
+    (fp64 mean square, fp32 scale and products, as the pages define it).
+    Returns fp32 [S, D]."""
+    x = _c(np.atleast_2d(x), np.float32)
+    w = _c(w, np.float32)
+    S, D = x.shape
+    assert w.shape == (D,)
+    out = np.empty((S, D), np.float32)
+    lib().cor_rmsnorm(_p(x), _p(w), S, D, float(eps), _p(out))
+    return out
+
+
+def layer_tail(x, norm_w, eps: float, ex: dict, shared: dict | None, idx, w):
+    """The layer tail: out = x + moe(rmsnorm(x)) for given routing.
+    Returns dict(out fp64 [S, D], mag fp64 [S, D] -- the MoE block's
+    magnitude, the bound's scale -- and n fp32 [S, D], the normalised rows)."""
+    n = rmsnorm(x, norm_w, eps)
+    r = moe(ex, shared, n, idx, w)
+    out = np.asarray(np.atleast_2d(x), np.float64) + r["out"]
+    return dict(out=out, mag=r["mag"], n=n)
 
 
 def quantize_rows(w, bits: int = 8):

@@ -358,3 +358,93 @@ def test_moe_invariants(orc):
     sk = orc.moe(ex, sh, x, idx2, w)
     ref = orc.moe(ex, sh, x, idx[:, :-1], w[:, :-1])
     np.testing.assert_array_equal(sk["out"], ref["out"])
+
+
+# ---------------------------------------------------------------- layer tail
+def _ulp32(v):
+    v = np.abs(np.asarray(v, np.float32))
+    return np.spacing(v).astype(np.float64)
+
+
+@pytest.mark.parametrize("case", _load("rmsnorm_small.json")["cases"], ids=lambda c: c["name"])
+def test_golden_rmsnorm(orc, case):
+    """Hand-worked rows: the fp32 result lies within max_ulp of the exact
+    real value of x / sqrt(mean(x^2) + eps) * w."""
+    x = np.array([case["x"]], np.float32)
+    got = orc.rmsnorm(x, np.array(case["w"], np.float32), case["eps"])[0].astype(np.float64)
+    exp = np.array(case["expected"], np.float64)
+    tol = case["max_ulp"] * _ulp32(exp)
+    assert np.all(np.abs(got - exp) <= tol), (got, exp)
+
+
+def test_rmsnorm_unit_rms(orc):
+    """w = 1, eps = 0: every output row has mean square 1 (up to fp32
+    rounding of the products)."""
+    g = synth.rng(61)
+    x = synth.activations(g, 9, 6144) * np.float32(3.7)
+    n = orc.rmsnorm(x, np.ones(6144, np.float32), 0.0).astype(np.float64)
+    np.testing.assert_allclose((n * n).mean(axis=1), 1.0, rtol=0, atol=2e-6)
+
+
+def test_rmsnorm_power_of_two_scale_and_weight(orc):
+    """eps = 0: scaling a row by 2^k changes the mean square by 4^k, the root
+    by 2^k and r by 2^-k, all exactly, so the output is unchanged bit for bit;
+    doubling w doubles the output exactly."""
+    g = synth.rng(62)
+    x = synth.activations(g, 5, 1000)
+    w = g.uniform(-2, 2, size=1000).astype(np.float32)
+    base = orc.rmsnorm(x, w, 0.0)
+    for k in (-3, 5):
+        assert np.array_equal(orc.rmsnorm(x * np.float32(2.0 ** k), w, 0.0), base)
+    assert np.array_equal(orc.rmsnorm(x, w * np.float32(2.0), 0.0), base * np.float32(2.0))
+
+
+def test_rmsnorm_rows_independent_and_eps_order(orc):
+    """Rows are normalised independently; eps sits under the square root
+    (a larger eps shrinks every output)."""
+    g = synth.rng(63)
+    x = synth.activations(g, 4, 64)
+    w = np.ones(64, np.float32)
+    full = orc.rmsnorm(x, w, 1e-5)
+    for s in range(4):
+        assert np.array_equal(orc.rmsnorm(x[s:s + 1], w, 1e-5)[0], full[s])
+    big = orc.rmsnorm(x, w, 10.0)
+    assert np.all(np.abs(big) <= np.abs(full))
+    ref = x.astype(np.float64) / np.sqrt((x.astype(np.float64) ** 2).mean(axis=1, keepdims=True) + 10.0)
+    np.testing.assert_allclose(big, ref, rtol=3e-7, atol=0)
+
+
+def test_layer_tail_zero_experts_pass_the_residual(orc):
+    """All-zero expert and shared weights (int4 nibble 8 everywhere): the MoE
+    block adds exactly 0, so the tail returns x unchanged."""
+    E, D, F, S, K = 6, 40, 24, 5, 3
+    ex, sh = _small_moe(64, E=E, D=D, F=F)
+    for t in (ex, sh):
+        for k in ("wg", "wu", "wd"):
+            t[k] = np.full_like(t[k], 0x88)
+    g = synth.rng(64, 1)
+    x = synth.activations(g, S, D)
+    idx, w = synth.routing_uniform(g, S, K, E)
+    r = orc.layer_tail(x, g.uniform(0.5, 1.5, size=D).astype(np.float32), 1e-5, ex, sh, idx, w)
+    assert np.array_equal(r["out"], x.astype(np.float64))
+
+
+def test_layer_tail_adds_the_block_on_the_normalised_rows(orc):
+    """The tail's output minus x is the MoE block of the RMSNorm rows, which
+    for K = 1, weight 1 and no shared expert is the textbook SwiGLU MLP of the
+    normalised row (library fp64)."""
+    E, D, F, S = 6, 40, 24, 4
+    ex, _ = _small_moe(65, E=E, D=D, F=F, shared=False)
+    g = synth.rng(65, 1)
+    x = synth.activations(g, S, D)
+    nw = g.uniform(0.5, 1.5, size=D).astype(np.float32)
+    idx = np.array([[2], [0], [5], [2]], np.int32)
+    r = orc.layer_tail(x, nw, 1e-5, ex, None, idx, np.ones((S, 1), np.float32))
+    for s in range(S):
+        e = idx[s, 0]
+        Gd = _dequant(orc, I4, ex["wg"][e], ex["sg"][e], D)
+        Ud = _dequant(orc, I4, ex["wu"][e], ex["su"][e], D)
+        Dd = _dequant(orc, I4, ex["wd"][e], ex["sd"][e], F)
+        ns = r["n"][s].astype(np.float64)
+        h = _silu(Gd @ ns) * (Ud @ ns)
+        np.testing.assert_allclose(r["out"][s] - x[s].astype(np.float64), Dd @ h, rtol=1e-9, atol=1e-9)
