@@ -137,7 +137,14 @@ def cpu_baseline_layer(bank, shared, Wr, bias, x, K, ntok):
     return dt, r["idx"]
 
 
-def run_layer64(args, dev):
+def run_tail64(args, dev):
+    """The 64-token decode layer as a layer tail: RMSNorm of the residual
+    stream, the MoE block on the normalised rows, residual add
+    (coli_moe_layer_tail)."""
+    return run_layer64(args, dev, tail=True)
+
+
+def run_layer64(args, dev, tail=False):
     import torch
     from weight_streaming_gemv_qgemv_amd import binding as b
     from weight_streaming_gemv_qgemv_amd import synth
@@ -159,28 +166,35 @@ def run_layer64(args, dev):
     idx_o = torch.empty((S, K), dtype=torch.int32, device=dev)
     w_o = torch.empty((S, K), dtype=torch.float32, device=dev)
     ws = b.alloc_workspace(b.moe_workspace_bytes(S, K, E, D, F, F), dev)
+    nw = to_dev(synth.rng(4002).uniform(0.5, 1.5, size=D).astype(np.float32), dev)
 
     def step(i):
         j = i & 1
-        b.moe_layer(rp, banks[j], sd[j], xd, out=out, idx_out=idx_o, w_out=w_o, ws=ws)
+        if tail:
+            b.moe_layer_tail(rp, banks[j], sd[j], xd, nw, 1e-5, out=out, idx_out=idx_o, w_out=w_o, ws=ws)
+        else:
+            b.moe_layer(rp, banks[j], sd[j], xd, out=out, idx_out=idx_o, w_out=w_o, ws=ws)
 
     step(0)
     torch.cuda.synchronize()
     uniq = int(np.unique(idx_o.cpu().numpy()).size)
     gu, dn = expert_bytes(fmt, D, F)
     step_bytes = (E * D * 4 + E * 4) + S * D * 4 + uniq * (gu + dn) + (gu + dn) + S * D * 4 + S * K * 8
+    if tail:
+        step_bytes += D * 4 + S * D * 4      # the norm weight, and x read again for the residual
     log(f"unique experts {uniq}; algorithmic bytes/step {step_bytes / 1e9:.4f} GB")
     ms, wall, stages = time_steps(step, args.steps, args.warmup)
     # dominant kernel: gate/up + SwiGLU (2/3 of the expert bytes), one launch per step
     gu_ms, gu_n = stages["gate_up"]
     gu_bytes = (uniq + 1) * gu + S * D * 4 + (S * K + S) * F * 4
-    res = dict(workload="moe_layer_decode_64", ms=ms, wall=wall, step_bytes=step_bytes,
+    res = dict(workload="moe_layer_tail_decode_64" if tail else "moe_layer_decode_64", ms=ms, wall=wall,
+               step_bytes=step_bytes,
                tokens=S, stages=stages, uniq=uniq,
                dominant=dict(kernel="k_dec<I4,2> (grouped expert gate/up + SwiGLU, matrix cores)",
                              bytes_per_launch=gu_bytes, ms_per_launch=gu_ms / max(gu_n, 1),
                              launches=gu_n,
                              traffic=recorded_traffic("moe_layer_decode_64", "k_dec<2, 2>")))
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not tail:
         ntok = args.cpu_tokens
         log(f"cpu baseline: oracle on {ntok} tokens")
         dt, sidx = cpu_baseline_layer(bank, shared, Wr, bias, x, K, ntok)
@@ -329,7 +343,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="layer64",
-                    choices=["layer64", "decode16", "qgemv", "prefill2048", "copy"])
+                    choices=["layer64", "tail64", "decode16", "qgemv", "prefill2048", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fmt", default="i4", choices=["f32", "i8", "i4", "i2"], help="qgemv workload")
     ap.add_argument("--tokens", type=int, default=1, help="qgemv workload: S")
@@ -349,7 +363,8 @@ def main():
     if args.workload == "copy":
         run_copy(args, dev)
         return
-    run = {"prefill2048": run_prefill2048, "layer64": run_layer64, "decode16": run_decode16, "qgemv": run_qgemv}[args.workload]
+    run = {"prefill2048": run_prefill2048, "layer64": run_layer64, "tail64": run_tail64,
+           "decode16": run_decode16, "qgemv": run_qgemv}[args.workload]
     r = run(args, dev)
     ms = r["ms"]
     gbs = r["step_bytes"] / (ms * 1e-3) / 1e9

@@ -192,10 +192,13 @@ size_t coli_moe_workspace_bytes(int S, int K, int E, int D, int F,
  *              xsum = [S] per-token sums of the stored x, then per grouped
  *              row its xf row (int32) and activation sum; hsum = per grouped
  *              row KpF/32 partial sums of the stored h (KpF = F rounded up to
- *              1024), then their totals. */
+ *              1024), then their totals.
+ *   xn         [S, D] fp32: the RMSNorm rows coli_moe_layer_tail feeds the
+ *              block. */
 typedef struct {
     int64_t flags, sig, idx, w, offsets, counts, row_pair, pair_row, h, y, router_part;
     int64_t xf, xsum, hf, hsum, work, n_work;
+    int64_t xn;                    /* coli_moe_layer_tail: [S, D] fp32 RMSNorm rows */
     int64_t n_pass_max;            /* passes the scratch is sized for */
     int64_t xf_stride, hf_stride;  /* bf16 elements per row */
     int64_t h_ld;   /* row stride of h in floats (max of F and F_shared) */
@@ -249,6 +252,25 @@ int coli_moe_layer(const coli_router_params *r, const coli_experts *ex,
                    int32_t *idx_out, float *w_out, int prec, void *ws,
                    size_t ws_bytes, void *stream);
 
+/* The layer tail around the MoE block: the post-attention RMSNorm of the
+ * residual stream, the block on the normalised rows, and the residual add
+ * [glm.c@98759bf -- rmsnorm; the layer forward's post-attention half]:
+ *     n_s   = rmsnorm(x_s) = (x_s * r_s) * norm_w,
+ *     r_s   = 1 / sqrtf((float)(sum_i x_si^2 / D) + eps)   (sum in fp64),
+ *     out_s = x_s + moe_layer(n_s)                          (fp32 add).
+ *   norm_w     [D] fp32 RMSNorm weight.   eps: >= 0 (the pages' default 1e-5).
+ *   x, out     [S, D] fp32; out may be x itself (in place).
+ *   other arguments as coli_moe_layer; the routing written to idx_out /
+ *   w_out is the one taken on the normalised rows, and the workspace region
+ *   xn receives them.
+ * Errors: as coli_moe_layer, and COLI_EINVAL for a NULL norm_w or a negative
+ * or NaN eps, COLI_EALIGN for a norm_w not 4-byte aligned. */
+int coli_moe_layer_tail(const coli_router_params *r, const coli_experts *ex,
+                        const coli_mlp *shared, const float *x, const float *norm_w,
+                        float eps, int S, const int32_t *pre_idx, const float *pre_w,
+                        float *out, int32_t *idx_out, float *w_out, int prec, void *ws,
+                        size_t ws_bytes, void *stream);
+
 /* Waits for `stream`, then reads the workspace flags the last MoE call on it
  * left.  *flags_out (host, may be NULL) receives the raw bits.  Returns
  * COLI_OK when none is set, COLI_EIDX when a routing id was skipped or
@@ -262,10 +284,11 @@ int coli_check_device_flags(const void *ws, void *stream, uint32_t *flags_out);
  * the number of timed launches since the last reset (host arrays of
  * COLI_NSTAGES entries; either may be NULL).  Stages: 0 router, 1 grouping,
  * 2 gate/up + SwiGLU, 3 down, 4 combine, 5 qgemv, 6 matrix-core preparation
- * (work list and activation fragments ahead of gate/up).  The pages time the same
+ * (work list and activation fragments ahead of gate/up), 7 RMSNorm of the
+ * layer tail.  The pages time the same
  * phases of their MoE block [metal@93cde63 -- moe_finish timers;
  * glm.c@98759bf -- profile counters]. */
-#define COLI_NSTAGES 7
+#define COLI_NSTAGES 8
 int coli_stage_timing(int enable);
 int coli_stage_times(double *ms, int64_t *calls, int reset);
 const char *coli_stage_name(int stage);

@@ -7,7 +7,7 @@ fp32.  Bar, elementwise on the layer output:
 with M_out the oracle's fp64 chain magnitude (sum_k |w_k| |sd[o]| sum_j
 |vd(o,j) h_j| plus the shared expert's term).  The per-row relative L2
 error is reported beside it.  Routing is Zipf(1.1)-skewed, so some experts
-carry many rows (several 16-row passes)."""
+carry many rows (several 64-row passes)."""
 import numpy as np
 import pytest
 

@@ -46,15 +46,15 @@ class RouterParams(C.Structure):
 class WsLayout(C.Structure):
     _fields_ = [(n, C.c_int64) for n in ("flags", "sig", "idx", "w", "offsets", "counts",
                                           "row_pair", "pair_row", "h", "y", "router_part",
-                                          "xf", "xsum", "hf", "hsum", "work", "n_work",
+                                          "xf", "xsum", "hf", "hsum", "work", "n_work", "xn",
                                           "n_pass_max", "xf_stride", "hf_stride", "h_ld", "total")]
 
 
 EXPORTS = ["coli_row_bytes", "coli_qgemv", "coli_router", "coli_router_workspace_bytes",
            "coli_moe_workspace_bytes", "coli_moe_workspace_layout", "coli_moe_gemv",
-           "coli_moe_layer", "coli_check_device_flags", "coli_strerror", "coli_version",
+           "coli_moe_layer", "coli_moe_layer_tail", "coli_check_device_flags", "coli_strerror", "coli_version",
            "coli_stage_timing", "coli_stage_times", "coli_stage_name"]
-NSTAGES = 7
+NSTAGES = 8
 
 _lib = None
 
@@ -86,6 +86,9 @@ def lib():
         L.coli_moe_layer.restype = i32
         L.coli_moe_layer.argtypes = [C.POINTER(RouterParams), C.POINTER(Experts), C.POINTER(Mlp),
                                      vp, i32, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+        L.coli_moe_layer_tail.restype = i32
+        L.coli_moe_layer_tail.argtypes = [C.POINTER(RouterParams), C.POINTER(Experts), C.POINTER(Mlp),
+                                          vp, vp, C.c_float, i32, vp, vp, vp, vp, vp, i32, vp, sz, vp]
         L.coli_check_device_flags.restype = i32
         L.coli_check_device_flags.argtypes = [vp, vp, C.POINTER(C.c_uint32)]
         L.coli_strerror.restype = C.c_char_p
@@ -213,6 +216,36 @@ def moe_gemv(ex: dict, x, idx, w, out=None, prec=PREC_FP32, ws=None, stream=None
     rc = lib().coli_moe_gemv(C.byref(es), _ptr(x), S, K, _ptr(idx), _ptr(w), _ptr(out), prec,
                              _ptr(ws), ws.numel(), _stream(stream))
     _check(rc, "coli_moe_gemv")
+    return out, ws
+
+
+def _router_struct(router_p, K):
+    return RouterParams(_ptr(router_p["w"]) if router_p else None,
+                        _ptr(router_p["bias"]) if router_p else None, K,
+                        int(router_p.get("norm_topk", 1)) if router_p else 1,
+                        float(router_p.get("routed_scale", 2.5)) if router_p else 1.0,
+                        float(router_p.get("topp", 0.0)) if router_p else 0.0)
+
+
+def moe_layer_tail(router_p: dict | None, ex: dict, shared: dict | None, x, norm_w, eps: float,
+                   pre_idx=None, pre_w=None, out=None, idx_out=None, w_out=None, prec=PREC_FP32,
+                   ws=None, K=None, stream=None):
+    """out = x + moe_layer(rmsnorm(x)); out may be x (in place)."""
+    S, D = x.shape
+    if K is None:
+        K = router_p["K"] if router_p else pre_idx.shape[1]
+    if out is None:
+        out = torch.empty((S, D), dtype=torch.float32, device=x.device)
+    Fs = shared["F"] if shared is not None else 0
+    if ws is None:
+        ws = alloc_workspace(moe_workspace_bytes(S, K, ex["E"], D, ex["F"], Fs, prec), x.device)
+    rp = _router_struct(router_p, K)
+    es = experts_struct(ex)
+    sp = C.byref(mlp_struct(shared)) if shared is not None else None
+    rc = lib().coli_moe_layer_tail(C.byref(rp), C.byref(es), sp, _ptr(x), _ptr(norm_w), float(eps), S,
+                                   _ptr(pre_idx), _ptr(pre_w), _ptr(out), _ptr(idx_out), _ptr(w_out),
+                                   prec, _ptr(ws), ws.numel(), _stream(stream))
+    _check(rc, "coli_moe_layer_tail")
     return out, ws
 
 

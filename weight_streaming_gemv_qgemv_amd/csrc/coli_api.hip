@@ -156,14 +156,16 @@ __global__ __launch_bounds__(1024) void k_group_scatter(const int32_t *__restric
 }
 
 // out[s, :] = sum_{kk: slot kept} w[s,kk] * y[row(s,kk), :]  (+ y[shared row]),
-// slots in order kk = 0..K-1, then the shared expert: a fixed order.
+// slots in order kk = 0..K-1, then the shared expert: a fixed order; with a
+// residual, out[s, :] = resid[s, :] + that sum (resid may be out itself: each
+// element is read and written by the same thread).
 // Block (s, c) covers columns [c * kCombineCols, +kCombineCols) of token s:
 // one float4 (vec4) or one float per thread, all K rows read together.
 constexpr int kCombineThreads = 256;
 __global__ __launch_bounds__(kCombineThreads) void k_combine(const float *__restrict__ y, int D, int K,
                                                  const int32_t *__restrict__ pair_row,
                                                  const float *__restrict__ w, int has_shared,
-                                                 int64_t shared_row0, float *__restrict__ out,
+                                                 int64_t shared_row0, const float *resid, float *out,
                                                  int vec4)
 {
     const int s = blockIdx.x;
@@ -190,6 +192,13 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(const float *__rest
             acc.z += v.z;
             acc.w += v.w;
         }
+        if (resid) {
+            const float4 r = *reinterpret_cast<const float4 *>(resid + (int64_t)s * D + d);
+            acc.x = r.x + acc.x;
+            acc.y = r.y + acc.y;
+            acc.z = r.z + acc.z;
+            acc.w = r.w + acc.w;
+        }
         *reinterpret_cast<float4 *>(out + (int64_t)s * D + d) = acc;
     } else {
         const int d = blockIdx.y * kCombineThreads + threadIdx.x;
@@ -201,20 +210,67 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(const float *__rest
             acc = fmaf(ws[kk], y[(int64_t)r * D + d], acc);
         }
         if (has_shared) acc += y[(shared_row0 + s) * (int64_t)D + d];
+        if (resid) acc = resid[(int64_t)s * D + d] + acc;
         out[(int64_t)s * D + d] = acc;
     }
 }
 
 hipError_t combine_launch(const float *y, int S, int D, int K, const int32_t *pair_row,
                           const float *w, int has_shared, int64_t shared_row0, float *out,
-                          int vec4, hipStream_t st)
+                          int vec4, hipStream_t st, const float *resid)
 {
     const int per = vec4 ? 4 * kCombineThreads : kCombineThreads;
     const dim3 grid((unsigned)S, (unsigned)((D + per - 1) / per));
     hipLaunchKernelGGL(k_combine, grid, dim3(kCombineThreads), 0, st, y, D, K, pair_row, w,
-                       has_shared, shared_row0, out, vec4);
+                       has_shared, shared_row0, resid, out, vec4);
     return hipGetLastError();
 }
+
+// Post-attention RMSNorm of one row per block [glm.c@98759bf -- rmsnorm]:
+// the mean square in fp64 (each square exact; per-thread sums over a fixed
+// stride, then a fixed-order tree), converted once to fp32, eps added in
+// fp32, r = 1 / sqrtf(.) (correctly rounded division and root), and each
+// output (x * r) * w rounded in fp32 after each product.
+constexpr int kNormThreads = 256;
+__global__ __launch_bounds__(kNormThreads) void k_rmsnorm(const float *__restrict__ x,
+                                                  const float *__restrict__ nw, int D, float eps,
+                                                  float *__restrict__ out, int vec4)
+{
+    __shared__ double red[kNormThreads / kWave];
+    const int s = blockIdx.x, tid = threadIdx.x;
+    const float *xs = x + (int64_t)s * D;
+    float *os = out + (int64_t)s * D;
+    double acc = 0.0;
+    if (vec4) {
+        for (int i = 4 * tid; i < D; i += 4 * kNormThreads) {
+            const float4 v = *reinterpret_cast<const float4 *>(xs + i);
+            acc += (double)v.x * (double)v.x;
+            acc += (double)v.y * (double)v.y;
+            acc += (double)v.z * (double)v.z;
+            acc += (double)v.w * (double)v.w;
+        }
+    } else {
+        for (int i = tid; i < D; i += kNormThreads) acc += (double)xs[i] * (double)xs[i];
+    }
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, kWave);
+    if ((tid & (kWave - 1)) == 0) red[tid / kWave] = acc;
+    __syncthreads();
+    const double ms = (red[0] + red[1]) + (red[2] + red[3]);
+    const float mean = (float)(ms / (double)D);
+    const float r = 1.0f / sqrtf(mean + eps);
+    if (vec4) {
+        for (int i = 4 * tid; i < D; i += 4 * kNormThreads) {
+            const float4 v = *reinterpret_cast<const float4 *>(xs + i);
+            const float4 g = *reinterpret_cast<const float4 *>(nw + i);
+            *reinterpret_cast<float4 *>(os + i) =
+                make_float4((v.x * r) * g.x, (v.y * r) * g.y, (v.z * r) * g.z, (v.w * r) * g.w);
+        }
+    } else {
+        for (int i = tid; i < D; i += kNormThreads) os[i] = (xs[i] * r) * nw[i];
+    }
+}
+static_assert(kNormThreads / kWave == 4, "fixed-order tree over 4 waves");
 
 inline bool al16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -274,7 +330,7 @@ int run_shared_valu(const coli_mlp *sh, const float *x, int S, int D, float *h, 
 // Grouped expert products: routed experts (+ shared) -> h -> y -> out.
 int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int S, int K,
                 const int32_t *idx, const float *w, float *out, int prec, uint8_t *ws,
-                const coli_ws_layout &L, hipStream_t st)
+                const coli_ws_layout &L, hipStream_t st, const float *resid = nullptr)
 {
     const int E = ex->E, D = ex->D, F = ex->F;
     const int P = S * K;
@@ -401,7 +457,7 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
         }
         StageTimer tcb(kStCombine, st);
         return to_status(combine_launch(y, S, D, K, pair_row, w, sh ? 1 : 0, shared_row0, out,
-                                        (int)(al16(out) && al16(y) && D % 4 == 0), st));
+                                        (int)(al16(out) && al16(y) && D % 4 == 0 && (!resid || al16(resid))), st, resid));
     }
     if (mm) {
         // bf16 precision: x as one bf16 row table per token, the SwiGLU
@@ -498,7 +554,7 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
         }
         StageTimer tcb(kStCombine, st);
         return to_status(combine_launch(y, S, D, K, pair_row, w, sh ? 1 : 0, shared_row0, out,
-                                        (int)(al16(out) && al16(y) && D % 4 == 0), st));
+                                        (int)(al16(out) && al16(y) && D % 4 == 0 && (!resid || al16(resid))), st, resid));
     }
     const bool sh_same_up = sh && sh->fmt == ex->fmt;
     const bool sh_same_down = sh && sh->fmt == ex->fmt && sh->F == F;
@@ -614,7 +670,7 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
     // ---- weighted combine, fixed order
     StageTimer tcb(kStCombine, st);
     return to_status(combine_launch(y, S, D, K, pair_row, w, sh ? 1 : 0, shared_row0, out,
-                                    (int)(al16(out) && al16(y) && D % 4 == 0), st));
+                                    (int)(al16(out) && al16(y) && D % 4 == 0 && (!resid || al16(resid))), st, resid));
 }
 
 }  // namespace
@@ -688,11 +744,12 @@ extern "C" int coli_moe_gemv(const coli_experts *ex, const float *x, int S, int 
     return run_experts(ex, nullptr, x, S, K, idx, w, out, prec, (uint8_t *)ws, L, (hipStream_t)stream);
 }
 
-extern "C" int coli_moe_layer(const coli_router_params *r, const coli_experts *ex,
-                              const coli_mlp *shared, const float *x, int S,
-                              const int32_t *pre_idx, const float *pre_w, float *out,
-                              int32_t *idx_out, float *w_out, int prec, void *ws,
-                              size_t ws_bytes, void *stream)
+// The MoE block on x; with resid, out = resid + block (the layer tail).
+static int moe_layer_impl(const coli_router_params *r, const coli_experts *ex,
+                          const coli_mlp *shared, const float *x, int S,
+                          const int32_t *pre_idx, const float *pre_w, float *out,
+                          int32_t *idx_out, float *w_out, int prec, void *ws,
+                          size_t ws_bytes, void *stream, const float *norm_w, float eps)
 {
     if (!r) return COLI_EINVAL;
     if ((pre_idx == nullptr) != (pre_w == nullptr)) return COLI_EINVAL;
@@ -708,6 +765,10 @@ extern "C" int coli_moe_layer(const coli_router_params *r, const coli_experts *e
         if (r->norm_topk != 0 && r->norm_topk != 1) return COLI_EINVAL;
         if (((uintptr_t)r->w & 3) || ((uintptr_t)r->bias & 3)) return COLI_EALIGN;
     }
+    if (norm_w) {
+        if (!(eps >= 0.f)) return COLI_EINVAL;   // also rejects NaN
+        if ((uintptr_t)norm_w & 3) return COLI_EALIGN;
+    }
     if (S == 0) return COLI_OK;
     coli_ws_layout L;
     rc = coli_moe_workspace_layout(S, K, ex->E, ex->D, ex->F, shared ? shared->F : 0, prec, &L);
@@ -716,6 +777,19 @@ extern "C" int coli_moe_layer(const coli_router_params *r, const coli_experts *e
     hipStream_t st = (hipStream_t)stream;
     const int32_t *idx = pre_idx;
     const float *w = pre_w;
+    const float *resid = nullptr;
+    if (norm_w) {
+        // the block runs on the normalised rows; x stays the residual
+        float *xn = reinterpret_cast<float *>(wsb + L.xn);
+        StageTimer tn(kStNorm, st);
+        const int D = ex->D;
+        const int vec4 = D % 4 == 0 && al16(x) && al16(norm_w) && al16(xn);
+        hipLaunchKernelGGL(k_rmsnorm, dim3((unsigned)S), dim3(kNormThreads), 0, st, x, norm_w, D, eps, xn,
+                           vec4);
+        if (hipGetLastError() != hipSuccess) return COLI_EDEVICE;
+        resid = x;
+        x = xn;
+    }
     if (run_router) {
         int32_t *ri = idx_out ? idx_out : reinterpret_cast<int32_t *>(wsb + L.idx);
         float *rw = w_out ? w_out : reinterpret_cast<float *>(wsb + L.w);
@@ -734,7 +808,28 @@ extern "C" int coli_moe_layer(const coli_router_params *r, const coli_experts *e
         if (w_out && hipMemcpyAsync(w_out, pre_w, n * 4, hipMemcpyDeviceToDevice, st) != hipSuccess)
             return COLI_EDEVICE;
     }
-    return run_experts(ex, shared, x, S, K, idx, w, out, prec, wsb, L, st);
+    return run_experts(ex, shared, x, S, K, idx, w, out, prec, wsb, L, st, resid);
+}
+
+extern "C" int coli_moe_layer(const coli_router_params *r, const coli_experts *ex,
+                              const coli_mlp *shared, const float *x, int S,
+                              const int32_t *pre_idx, const float *pre_w, float *out,
+                              int32_t *idx_out, float *w_out, int prec, void *ws,
+                              size_t ws_bytes, void *stream)
+{
+    return moe_layer_impl(r, ex, shared, x, S, pre_idx, pre_w, out, idx_out, w_out, prec, ws, ws_bytes,
+                          stream, nullptr, 0.f);
+}
+
+extern "C" int coli_moe_layer_tail(const coli_router_params *r, const coli_experts *ex,
+                                   const coli_mlp *shared, const float *x, const float *norm_w,
+                                   float eps, int S, const int32_t *pre_idx, const float *pre_w,
+                                   float *out, int32_t *idx_out, float *w_out, int prec, void *ws,
+                                   size_t ws_bytes, void *stream)
+{
+    if (!norm_w) return COLI_EINVAL;
+    return moe_layer_impl(r, ex, shared, x, S, pre_idx, pre_w, out, idx_out, w_out, prec, ws, ws_bytes,
+                          stream, norm_w, eps);
 }
 
 extern "C" int coli_check_device_flags(const void *ws, void *stream, uint32_t *flags_out)

@@ -7,7 +7,7 @@
 namespace coli {
 
 enum Stage { kStRouter = 0, kStGroup = 1, kStGateUp = 2, kStDown = 3, kStCombine = 4, kStQgemv = 5,
-             kStPrep = 6 };
+             kStPrep = 6, kStNorm = 7 };
 
 // Records a start event on construction and an end event on destruction
 // when stage timing is enabled; does nothing otherwise.

@@ -42,7 +42,7 @@ hipEvent_t take_event()
     return e;
 }
 
-const char *const kNames[COLI_NSTAGES] = {"router", "group", "gate_up", "down", "combine", "qgemv", "prep"};
+const char *const kNames[COLI_NSTAGES] = {"router", "group", "gate_up", "down", "combine", "qgemv", "prep", "norm"};
 
 }  // namespace
 

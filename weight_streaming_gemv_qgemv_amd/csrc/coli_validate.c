@@ -190,6 +190,8 @@ int coli_moe_workspace_layout(int S, int K, int E, int D, int F, int F_shared,
     }
     REGION(work, (ngp + 1) * 4);
     REGION(n_work, 64);
+    if (!mul_ok((int64_t)S, D, &t) || !mul_ok(t, 4, &t)) return COLI_ESHAPE;
+    REGION(xn, t);
 #undef REGION
     out->n_pass_max = ngp;
     out->xf_stride = bf16 ? KpD : 2 * KpD;
