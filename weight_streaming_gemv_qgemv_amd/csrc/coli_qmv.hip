@@ -179,6 +179,12 @@ __global__ __launch_bounds__(512) void k_qmv(QmvArgs a)
     // that order: the wait before staging then covers the activations only),
     // this round's products run from LDS, the next round is staged into the
     // other buffer, barrier.
+    // the epilogue wave's (wave mt < MT) scales, requested before anything else
+    float scp[4] = {1.f, 1.f, 1.f, 1.f};
+    if (wave < MT && a.scale) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) scp[r] = a.scale[min(row0 + 16 * wave + 4 * q + r, a.O - 1)];
+    }
     uint4 wA[MT][SEGS], wB[MT][SEGS];
     float4 xv[PASSES][RUN / 4];
     loadX(0, xv);
@@ -226,9 +232,7 @@ __global__ __launch_bounds__(512) void k_qmv(QmvArgs a)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const float vv = v[r] + __shfl_xor(v[r], 1, kWave);
-        const int o = min(ob + r, a.O - 1);
-        const float sc = a.scale ? a.scale[o] : 1.f;
-        res[r] = sc * (vv - OFF * xs);
+        res[r] = scp[r] * (vv - OFF * xs);
     }
     const int tok = col >> 1;
     if ((col & 1) == 0 && tok < nt) {
@@ -263,7 +267,8 @@ __global__ __launch_bounds__(512) void k_qmv1(QmvArgs a, int passes, int ntiles)
     constexpr float OFF = T::OFF;
     constexpr uint32_t kbytes = KB * BITS / 8;
     constexpr int RUN = FMT == kI2 ? 16 : 8;              // elements per staging run
-    constexpr int XP = (kQmvWaves * NKW * KB / RUN * kQ1Tpp + 511) / 512;   // runs per thread
+    constexpr int RW = NKW * KB / RUN;                    // staging runs per row in a wave's k-blocks
+    constexpr int XP = (RW * kQ1Tpp + kWave - 1) / kWave; // runs per lane
     extern __shared__ uint4 lds[];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -277,14 +282,25 @@ __global__ __launch_bounds__(512) void k_qmv1(QmvArgs a, int passes, int ntiles)
     const int nt = min(kQ1Tpp, a.S - t0);
     const int nkb = a.nkb;
     const int cs = 2 * nt;                                // columns per chunk in LDS
-    const int runs = nkb * KB / RUN;                      // staging runs per activation row
+    // this wave's k-blocks: kw0 .. kw0 + NKW - 1, those below nkb staged and
+    // multiplied
+    const int kw0 = wave * NKW;
+    const int rw = max(0, min(RW, (nkb - kw0) * (KB / RUN)));   // live runs per row
 
-    // activations first: this thread's runs (clamped to a live one)
+    // wave 0 finishes the block: its 4 scales per lane are requested first
+    float scp[4] = {1.f, 1.f, 1.f, 1.f};
+    if (wave == 0 && a.scale) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) scp[r] = a.scale[min(row0 + 4 * q + r, a.O - 1)];
+    }
+    // activations next: each wave stages the runs of its own k-blocks (a
+    // lane's dead runs read nothing: they start at I)
     float4 xv[XP][RUN / 4];
 #pragma unroll
     for (int p = 0; p < XP; ++p) {
-        const int u = min(tid + 512 * p, runs * nt - 1);
-        const int t = u / runs, e0 = (u % runs) * RUN;
+        const int u = lane + kWave * p;
+        const bool live = u < RW * nt && u % RW < rw;
+        const int t = live ? u / RW : 0, e0 = live ? kw0 * KB + (u % RW) * RUN : a.I;
         const float *xr = a.x + (int64_t)(t0 + t) * a.I;
         if (e0 + RUN <= a.I) {
 #pragma unroll
@@ -310,12 +326,14 @@ __global__ __launch_bounds__(512) void k_qmv1(QmvArgs a, int passes, int ntiles)
 #pragma unroll
         for (int sg = 0; sg < SEGS; ++sg) w[i][sg] = gload16(a.W + (roff + min(b0 + 64 * sg, last_seg)));
     }
-    // stage: run -> bf16 hi (column 2t) and lo (column 2t+1) units
+    // stage: run -> bf16 hi (column 2t) and lo (column 2t+1) units; the
+    // wave reads back only what it wrote, so no block barrier is needed
 #pragma unroll
     for (int p = 0; p < XP; ++p) {
-        const int u = tid + 512 * p;
-        if (u >= runs * nt) break;
-        const int t = u / runs, e0 = (u % runs) * RUN;
+        const int u = lane + kWave * p;
+        if (u >= RW * nt) break;
+        if (u % RW >= rw) continue;                   // past the last k-block
+        const int t = u / RW, e0 = kw0 * KB + (u % RW) * RUN;
         float v[RUN];
 #pragma unroll
         for (int i = 0; i < RUN / 4; ++i) {
@@ -343,7 +361,6 @@ __global__ __launch_bounds__(512) void k_qmv1(QmvArgs a, int passes, int ntiles)
             dst[1] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
         }
     }
-    __syncthreads();
 
     floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f}, accs = floatx4{0.f, 0.f, 0.f, 0.f};
     const uint32_t one2 = opaque_v(0x3F803F80u);   // bf16 (1, 1)
@@ -391,9 +408,7 @@ __global__ __launch_bounds__(512) void k_qmv1(QmvArgs a, int passes, int ntiles)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const float vv = v[r] + __shfl_xor(v[r], 1, kWave);
-        const int o = min(ob + r, a.O - 1);
-        const float sc = a.scale ? a.scale[o] : 1.f;
-        res[r] = sc * (vv - OFF * xs);
+        res[r] = scp[r] * (vv - OFF * xs);
     }
     const int tok = col >> 1;
     if ((col & 1) == 0 && tok < nt) {
