@@ -413,6 +413,64 @@ int cor_moe(const cor_experts *ex, const cor_mlp *sh, const float *x, int S,
 }
 
 /* ------------------------------------------------------------------------
+ * Integer-dot qgemv (IDOT) [glm.c@98759bf -- qrow_i8, dot_i8i8, dot_i4i8,
+ * matmul_q_idot, matmul_i4_idot]: each activation row is quantised to int8
+ * by its absolute maximum, the dot product with the int8 / int4 weight
+ * values is taken in exact integer arithmetic, and the result is scaled back
+ * in fp32.  A lossy variant by design; the pages fix every step in fp32:
+ *   amax = max_i |x_i|;  s = amax / 127 (at least 1e-12);  inv = 1 / s;
+ *   q_i = round-half-even(x_i * inv) as int8;
+ *   y[s,o] = ((float)dot(v(o,.), q) * scale[o]) * s,
+ * rounded in fp32 after each operation, which the oracle reproduces
+ * (volatile forces the roundings).  The dot itself is exact (int64 here).
+ * ------------------------------------------------------------------------ */
+float cor_qrow_i8(const float *x, int I, int8_t *q)
+{
+    float amax = 0.f;
+    for (int i = 0; i < I; ++i) {
+        float a = fabsf(x[i]);
+        if (a > amax) amax = a;
+    }
+    volatile float s = amax / 127.f;
+    if (s < 1e-12f) s = 1e-12f;
+    volatile float inv = 1.f / s;
+    for (int i = 0; i < I; ++i) {
+        volatile float t = x[i] * inv;
+        q[i] = (int8_t)lrintf(t);   /* round half to even (default mode) */
+    }
+    return s;
+}
+
+/* y [S,O] fp32; fmt int8 or int4 only (the pages' IDOT formats); also
+ * returns the exact integer dots in dot_out [S,O] (may be NULL). */
+int cor_qgemv_idot(int fmt, const void *W, const float *scale, const float *x,
+                   int S, int I, int O, float *y, int64_t *dot_out)
+{
+    if (fmt != OR_I8 && fmt != OR_I4) return -1;
+    int64_t rb = cor_row_bytes(fmt, I);
+    int8_t *xq = (int8_t *)malloc((size_t)S * I + 1);
+    float *sx = (float *)malloc((size_t)S * sizeof(float) + 4);
+    if (!xq || !sx) { free(xq); free(sx); return -2; }
+    for (int s = 0; s < S; ++s) sx[s] = cor_qrow_i8(x + (int64_t)s * I, I, xq + (int64_t)s * I);
+#pragma omp parallel for schedule(static)
+    for (int o = 0; o < O; ++o) {
+        const uint8_t *row = (const uint8_t *)W + (int64_t)o * rb;
+        for (int s = 0; s < S; ++s) {
+            const int8_t *qs = xq + (int64_t)s * I;
+            int64_t dot = 0;
+            for (int i = 0; i < I; ++i) dot += (int64_t)cor_unpack(fmt, row, i) * qs[i];
+            if (dot_out) dot_out[(int64_t)s * O + o] = dot;
+            volatile float d = (float)dot;
+            volatile float t = d * scale[o];
+            y[(int64_t)s * O + o] = t * sx[s];
+        }
+    }
+    free(xq);
+    free(sx);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------
  * Layer tail around the MoE block [glm.c@98759bf -- rmsnorm; the layer
  * forward's post-attention half]: the residual stream x is normalised with
  * the post-attention RMSNorm, the MoE block runs on the normalised rows, and

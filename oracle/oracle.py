@@ -55,6 +55,10 @@ def lib():
         L.cor_moe.restype = i32
         L.cor_moe.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, vp, i64,
                               vp, vp, vp, vp, vp, vp]
+        L.cor_qrow_i8.restype = C.c_float
+        L.cor_qrow_i8.argtypes = [vp, i32, vp]
+        L.cor_qgemv_idot.restype = i32
+        L.cor_qgemv_idot.argtypes = [i32, vp, vp, vp, i32, i32, i32, vp, vp]
         L.cor_rmsnorm.restype = None
         L.cor_rmsnorm.argtypes = [vp, vp, i32, i32, C.c_float, vp]
         for name in ("cor_quantize_rows", "cor_pack_int4", "cor_pack_int2"):
@@ -186,6 +190,33 @@ def moe(ex: dict, shared: dict | None, x, idx, w, intermediates: bool = False):
                        rows, *ptrs)
     assert rc == 0, rc
     return res
+
+
+def qrow_i8(x):
+    """Per-row int8 quantisation of x [S, I] by absmax/127 (the pages' IDOT
+    activations).  Returns (q int8 [S, I], s fp32 [S])."""
+    x = _c(np.atleast_2d(x), np.float32)
+    S, I = x.shape
+    q = np.empty((S, I), np.int8)
+    s = np.empty((S,), np.float32)
+    for r in range(S):
+        s[r] = lib().cor_qrow_i8(_p(x[r]), I, _p(q[r]))
+    return q, s
+
+
+def qgemv_idot(fmt: int, W, scale, x, O: int | None = None):
+    """Integer-dot qgemv (int8 / int4 weights): returns (y fp32 [S, O], the
+    exact integer dots int64 [S, O])."""
+    W = _c(W, np.uint8)
+    x = _c(np.atleast_2d(x), np.float32)
+    S, I = x.shape
+    O = W.shape[0] if O is None else O
+    sc = _c(scale, np.float32)
+    y = np.empty((S, O), np.float32)
+    dot = np.empty((S, O), np.int64)
+    rc = lib().cor_qgemv_idot(fmt, _p(W), _p(sc), _p(x), S, I, O, _p(y), _p(dot))
+    assert rc == 0, rc
+    return y, dot
 
 
 def rmsnorm(x, w, eps: float):

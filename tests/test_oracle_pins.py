@@ -448,3 +448,70 @@ def test_layer_tail_adds_the_block_on_the_normalised_rows(orc):
         ns = r["n"][s].astype(np.float64)
         h = _silu(Gd @ ns) * (Ud @ ns)
         np.testing.assert_allclose(r["out"][s] - x[s].astype(np.float64), Dd @ h, rtol=1e-9, atol=1e-9)
+
+
+# ---------------------------------------------------------------- IDOT
+@pytest.mark.parametrize("case", _load("idot_quant.json")["cases"], ids=lambda c: c["name"])
+def test_golden_idot_quantiser(orc, case):
+    q, s = orc.qrow_i8(np.array([case["x"]], np.float32))
+    assert s[0] == np.float32(case["s"])
+    np.testing.assert_array_equal(q[0], np.array(case["q"], np.int8))
+
+
+@pytest.mark.parametrize("fmt", [I8, I4])
+def test_idot_integer_dot_is_exact(orc, fmt):
+    """The dots are the integer matmul of the unpacked weight values and the
+    quantised rows (numpy int64 matmul of values written independently)."""
+    g = synth.rng(71, fmt)
+    O, I, S = 23, 333, 5
+    if fmt == I8:
+        V = g.integers(-128, 128, size=(O, I))
+        W = V.astype(np.int8).view(np.uint8)
+    else:
+        V = g.integers(-8, 8, size=(O, I))
+        W = _int4_bytes_from_values(V)
+    x = synth.activations(g, S, I)
+    q, _ = orc.qrow_i8(x)
+    _, dot = orc.qgemv_idot(fmt, W, np.ones(O, np.float32), x)
+    np.testing.assert_array_equal(dot, q.astype(np.int64) @ V.T.astype(np.int64))
+
+
+def test_idot_epilogue_exact_for_power_of_two_scales(orc):
+    """With s = 2^m (amax = 127 * 2^m) and scale[o] = 2^-k, y = dot * 2^(m-k)
+    exactly while |dot| < 2^24."""
+    g = synth.rng(72)
+    O, I = 16, 64
+    V = g.integers(-8, 8, size=(O, I))
+    W = _int4_bytes_from_values(V)
+    x = g.uniform(-1, 1, size=(2, I)).astype(np.float32) * np.float32(8.0)
+    x[0, 5] = 127.0 * 8.0          # s = 8
+    x[1, 9] = -127.0 / 4.0         # s = 1/4
+    x[1] = np.clip(x[1], -127.0 / 4.0, 127.0 / 4.0)
+    sc = np.float32(2.0) ** -g.integers(0, 6, size=O).astype(np.float32)
+    y, dot = orc.qgemv_idot(I4, W, sc, x)
+    s = np.array([8.0, 0.25])
+    assert np.all(np.abs(dot) < 2 ** 24)
+    np.testing.assert_array_equal(y.astype(np.float64), dot * sc[None, :].astype(np.float64) * s[:, None])
+
+
+@pytest.mark.parametrize("fmt", [I8, I4])
+def test_idot_error_against_exact_qgemv(orc, fmt):
+    """A lossy variant: on N(0,1) rows the relative RMS error against the
+    exact product stays at the sub-percent level the pages report (~0.3%)."""
+    g = synth.rng(73, fmt)
+    O, I, S = 64, 2048, 4
+    W = synth.weight_bytes(g, fmt, O, I)
+    sc = synth.scales(g, O)
+    x = synth.activations(g, S, I)
+    y, _ = orc.qgemv_idot(fmt, W, sc, x)
+    ref, _ = orc.qgemv(fmt, W, sc, x)
+    rel = np.sqrt(((y - ref) ** 2).mean() / (ref ** 2).mean())
+    assert rel < 1e-2, rel
+    assert rel > 1e-5, rel     # it is really the int8 path, not the exact one
+
+
+def test_idot_rejects_int2_and_f32(orc):
+    import pytest as _pt
+    for fmt in (F32, I2):
+        with _pt.raises(AssertionError):
+            orc.qgemv_idot(fmt, np.zeros((1, 4), np.uint8), np.ones(1, np.float32), np.ones((1, 4), np.float32))
