@@ -309,16 +309,26 @@ def run_qgemv(args, dev):
     copies = [Wd0] + [Wd0.clone() for _ in range(ncopy - 1)]
     scd, xd = to_dev(sc, dev), to_dev(x, dev)
     y = torch.empty((S, O), dtype=torch.float32, device=dev)
+    idot = getattr(args, "idot", False)
+    if idot:
+        if fmt not in (1, 2):
+            raise SystemExit("--idot takes --fmt i8 or i4")
+        wsq = b.alloc_workspace(b.qgemv_idot_workspace_bytes(S, I), dev)
 
     def step(i):
-        b.qgemv(fmt, copies[i % len(copies)], scd, xd, y)
+        if idot:
+            b.qgemv_idot(fmt, copies[i % len(copies)], scd, xd, y, ws=wsq)
+        else:
+            b.qgemv(fmt, copies[i % len(copies)], scd, xd, y)
 
     step_bytes = O * W.shape[1] + O * 4 + S * I * 4 + S * O * 4
     ms, wall, stages = time_steps(step, args.steps, args.warmup)
     q_ms, q_n = stages["qgemv"]
-    return dict(workload=f"qgemv_{args.fmt}_12288x6144_s{S}", ms=ms, wall=wall, step_bytes=step_bytes,
+    name = f"qgemv{'_idot' if idot else ''}_{args.fmt}_12288x6144_s{S}"
+    return dict(workload=name, ms=ms, wall=wall, step_bytes=step_bytes,
                 tokens=S, stages=stages, uniq=None,
-                dominant=dict(kernel=f"qgemv {args.fmt} (coli_qgemv)", bytes_per_launch=step_bytes,
+                dominant=dict(kernel=f"qgemv {args.fmt} ({'coli_qgemv_idot' if idot else 'coli_qgemv'})",
+                              bytes_per_launch=step_bytes,
                               ms_per_launch=q_ms / max(q_n, 1), launches=q_n))
 
 
@@ -347,6 +357,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fmt", default="i4", choices=["f32", "i8", "i4", "i2"], help="qgemv workload")
     ap.add_argument("--tokens", type=int, default=1, help="qgemv workload: S")
+    ap.add_argument("--idot", action="store_true", help="qgemv workload: the integer-dot variant")
     ap.add_argument("--cpu-tokens", type=int, default=64)
     args = ap.parse_args()
     if args.gpus != 1:

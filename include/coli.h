@@ -62,10 +62,10 @@ enum coli_status {
 /* Precision of the MoE expert products.
  *   COLI_PREC_FP32: fp32 activations, fp32 accumulation; every float output
  *     meets |y - y_ref| <= 1e-4 * (scale * sum |v * x|) + 1e-6.
- *     (The matrix cores take x as bf16 hi + lo, 8 rows per pass.)
+ *     (The matrix cores take x as bf16 hi + lo, 16 rows per pass.)
  *   COLI_PREC_BF16: activations -- x, and h for the down product -- rounded
  *     once to bf16, int weights converted exactly to bf16 for the matrix
- *     cores, fp32 accumulation, scale applied in fp32 after the sum, 16 rows
+ *     cores, fp32 accumulation, scale applied in fp32 after the sum, 64 rows
  *     per pass; bound 2e-2 of the same magnitude.  Meant for prefill-sized
  *     batches.  Shapes that take the vector-ALU kernels (rows that are not
  *     whole 16-byte segments) compute in fp32 under either value. */
@@ -90,6 +90,30 @@ int64_t coli_row_bytes(int fmt, int64_t I);
  * COLI_EDEVICE. */
 int coli_qgemv(int fmt, const void *W, const float *scale, const float *x,
                float *y, int S, int I, int O, void *stream);
+
+/* Integer-dot quantized matrix-vector product (IDOT), a lossy variant of
+ * coli_qgemv [glm.c@98759bf -- qrow_i8, dot_i8i8, dot_i4i8, matmul_q_idot,
+ * matmul_i4_idot]: each row of x is quantised to int8 by its absolute
+ * maximum,
+ *     s_s = max(max_i |x[s,i]| / 127, 1e-12),  q[s,i] = rint(x[s,i] * (1/s_s)),
+ * (fp32, round half to even), the dot product with the weight values is
+ * exact integer arithmetic, and
+ *     y[s, o] = ((float)dot(v(o, .), q[s, .]) * scale[o]) * s_s
+ * with each operation rounded in fp32 in that order.  The result is the
+ * definition's bit for bit; against coli_qgemv it differs by the int8
+ * rounding of x (about 0.3% RMS on the pages' measurements).
+ *   fmt    COLI_I8 or COLI_I4 (the pages' integer-dot formats).
+ *   W      [O, coli_row_bytes(fmt, I)] bytes, 16-byte aligned, the row a
+ *          whole number of 16-byte segments (I a multiple of 16 for int8,
+ *          of 32 for int4), I <= 8192 (int8) / 16384 (int4).
+ *   scale  [O] fp32 (required).   x [S, I] fp32.   y [S, O] fp32, overwritten.
+ *   ws     device workspace of ws_bytes >= coli_qgemv_idot_workspace_bytes(S, I)
+ *          bytes, 256-byte aligned: the quantised rows.
+ * Errors: COLI_EFMT, COLI_EINVAL, COLI_ESHAPE, COLI_EALIGN, COLI_ERANGE,
+ * COLI_EWORKSPACE, COLI_EDEVICE. */
+size_t coli_qgemv_idot_workspace_bytes(int S, int I);
+int coli_qgemv_idot(int fmt, const void *W, const float *scale, const float *x, float *y,
+                    int S, int I, int O, void *ws, size_t ws_bytes, void *stream);
 
 /* Router: sigmoid scores and noaux_tc top-K with one group
  * [glm.c@98759bf -- moe, phase A; metal@93cde63 -- r_router, r_top8,

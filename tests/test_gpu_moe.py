@@ -143,6 +143,23 @@ def test_moe_gemv_tiles_aligned(dev, orc, fmt):
     check_moe(orc, bank, None, x, idx, w, out, ws, lay, f"tiles fmt{fmt}")
 
 
+@pytest.mark.parametrize("fmt", [1, 2, 3])
+def test_moe_gemv_short_rows_matrix_cores(dev, orc, fmt):
+    """Widths whose rows are whole 16-byte segments but shorter than 64
+    bytes (int4 D=64, F=32: 32- and 16-byte rows) take the matrix-core
+    kernels with their chunk offsets clamped inside the row."""
+    from weight_streaming_gemv_qgemv_amd import binding as b
+    E, D, F, S, K = 8, 64, 32, 10, 3
+    bank = synth.expert_bank(30 + fmt, fmt, E, D, F)
+    g = synth.rng(31, fmt)
+    x = synth.activations(g, S, D)
+    idx, w = synth.routing_uniform(g, S, K, E)
+    announce("moe short rows", fmt)
+    out, ws = run_gemv(dev, dev_bank(bank, dev), x, idx, w)
+    lay = b.moe_workspace_layout(S, K, E, D, F)
+    check_moe(orc, bank, None, x, idx, w, out, ws, lay, f"short fmt{fmt}")
+
+
 def test_moe_gemv_skipped_and_bad_slots(dev, orc):
     from weight_streaming_gemv_qgemv_amd import binding as b
     E, D, F, S, K = 8, 256, 128, 6, 3

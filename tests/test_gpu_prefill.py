@@ -63,6 +63,21 @@ def test_prefill_bf16_small(dev, orc, fmt):
     assert rel_l2(out, ref["out"]) < 2e-2
 
 
+@pytest.mark.parametrize("fmt", [1, 2, 3])
+def test_prefill_bf16_short_rows(dev, orc, fmt):
+    """Rows of whole 16-byte segments shorter than 64 bytes (D=64, F=32)."""
+    E, D, F, S, K = 8, 64, 32, 90, 3
+    bank = synth.expert_bank(65 + fmt, fmt, E, D, F)
+    shared = synth.shared_mlp(65 + fmt, fmt, D, F)
+    g = synth.rng(66, fmt)
+    x = synth.activations(g, S, D)
+    idx, w = synth.routing_zipf(g, S, K, E)
+    announce("prefill bf16 short rows", fmt)
+    out, _ = run_layer(dev, bank, shared, x, idx, w, PREC_BF16)
+    ref = orc.moe(bank, shared, x, idx, w.astype(np.float64))
+    assert_within(out, ref["out"], ref["mag"], REL, what=f"prefill short fmt{fmt}")
+
+
 def test_prefill_bf16_unaligned_rows_take_fp32(dev, orc):
     """Rows that are not whole 16-byte segments take the vector-ALU kernels,
     which compute in fp32 under either precision."""

@@ -33,7 +33,7 @@ def test_tiny_shapes_brute_force(dev, orc, fmt):
     """Every (O, I) in a small grid, ragged I (unaligned rows), S up to 3."""
     g = synth.rng(100, fmt)
     for O in (1, 2, 5, 17, 40):
-        for I in (1, 2, 3, 7, 8, 15, 16, 31, 33, 40):
+        for I in (1, 2, 3, 7, 8, 15, 16, 31, 32, 33, 40, 64, 96):
             S = 1 + (O + I) % 3
             announce("qgemv tiny", fmt, O, I, S)
             W = synth.weight_bytes(g, fmt, O, I)

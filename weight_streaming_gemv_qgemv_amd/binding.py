@@ -52,7 +52,8 @@ class WsLayout(C.Structure):
 
 EXPORTS = ["coli_row_bytes", "coli_qgemv", "coli_router", "coli_router_workspace_bytes",
            "coli_moe_workspace_bytes", "coli_moe_workspace_layout", "coli_moe_gemv",
-           "coli_moe_layer", "coli_moe_layer_tail", "coli_check_device_flags", "coli_strerror", "coli_version",
+           "coli_moe_layer", "coli_moe_layer_tail", "coli_qgemv_idot",
+           "coli_qgemv_idot_workspace_bytes", "coli_check_device_flags", "coli_strerror", "coli_version",
            "coli_stage_timing", "coli_stage_times", "coli_stage_name"]
 NSTAGES = 8
 
@@ -86,6 +87,10 @@ def lib():
         L.coli_moe_layer.restype = i32
         L.coli_moe_layer.argtypes = [C.POINTER(RouterParams), C.POINTER(Experts), C.POINTER(Mlp),
                                      vp, i32, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+        L.coli_qgemv_idot_workspace_bytes.restype = sz
+        L.coli_qgemv_idot_workspace_bytes.argtypes = [i32, i32]
+        L.coli_qgemv_idot.restype = i32
+        L.coli_qgemv_idot.argtypes = [i32, vp, vp, vp, vp, i32, i32, i32, vp, sz, vp]
         L.coli_moe_layer_tail.restype = i32
         L.coli_moe_layer_tail.argtypes = [C.POINTER(RouterParams), C.POINTER(Experts), C.POINTER(Mlp),
                                           vp, vp, C.c_float, i32, vp, vp, vp, vp, vp, i32, vp, sz, vp]
@@ -144,6 +149,25 @@ def qgemv(fmt: int, W: torch.Tensor, scale, x: torch.Tensor, y: torch.Tensor | N
     rc = lib().coli_qgemv(fmt, _ptr(W), _ptr(scale), _ptr(x), _ptr(y), S, I, O, _stream(stream))
     _check(rc, "coli_qgemv")
     return y
+
+
+def qgemv_idot_workspace_bytes(S: int, I: int) -> int:
+    return int(lib().coli_qgemv_idot_workspace_bytes(S, I))
+
+
+def qgemv_idot(fmt: int, W: torch.Tensor, scale, x: torch.Tensor, y: torch.Tensor | None = None,
+               O: int | None = None, ws=None, stream=None):
+    """Integer-dot qgemv (int8 / int4): x quantised to int8 per row by absmax/127."""
+    S, I = x.shape
+    O = W.shape[0] if O is None else O
+    if y is None:
+        y = torch.empty((S, O), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = alloc_workspace(max(qgemv_idot_workspace_bytes(S, I), 256), x.device)
+    rc = lib().coli_qgemv_idot(fmt, _ptr(W), _ptr(scale), _ptr(x), _ptr(y), S, I, O, _ptr(ws), ws.numel(),
+                               _stream(stream))
+    _check(rc, "coli_qgemv_idot")
+    return y, ws
 
 
 def qgemv_raw(fmt, W, scale, x, y, S, I, O, stream=0) -> int:

@@ -16,6 +16,7 @@
 #include "coli_gemv.h"
 #include "coli_pre.h"
 #include "coli_qmv.h"
+#include "coli_idot.h"
 
 #include "coli_internal.h"
 #include "coli_router.h"
@@ -716,6 +717,44 @@ extern "C" int coli_qgemv(int fmt, const void *W, const float *scale, const floa
     a.aligned = (rb % 16 == 0) && al16(W);
     StageTimer t(kStQgemv, (hipStream_t)stream);
     return to_status(gemv_launch(a, fmt, 1, S, (hipStream_t)stream));
+}
+
+extern "C" size_t coli_qgemv_idot_workspace_bytes(int S, int I)
+{
+    if (S < 0 || I < 1) return 0;
+    return (size_t)idot_workspace_bytes(S, I);
+}
+
+extern "C" int coli_qgemv_idot(int fmt, const void *W, const float *scale, const float *x, float *y,
+                               int S, int I, int O, void *ws, size_t ws_bytes, void *stream)
+{
+    if (fmt != COLI_I8 && fmt != COLI_I4) return COLI_EFMT;
+    int rc = coli__check_qgemv(fmt, W, scale, x, y, S, I, O);
+    if (rc != COLI_OK) return rc;
+    if (S == 0 || O == 0) return COLI_OK;
+    if (I < 1) return COLI_ESHAPE;
+    const int64_t rb = coli_row_bytes(fmt, I);
+    if (rb % 16 != 0 || ((uintptr_t)W & 15u)) return COLI_EALIGN;
+    const int KB = idot_kblock(fmt);
+    if ((I + KB - 1) / KB > 8 * idot_max_kblocks_per_wave()) return COLI_ERANGE;
+    if ((int64_t)O * rb >= ((int64_t)1 << 32) - 4096) return COLI_ERANGE;
+    if (!ws || ws_bytes < (size_t)idot_workspace_bytes(S, I)) return COLI_EWORKSPACE;
+    if ((uintptr_t)ws & 255u) return COLI_EALIGN;
+    IdotArgs a = {};
+    a.W = (const uint8_t *)W;
+    a.scale = scale;
+    a.x = x;
+    a.y = y;
+    a.S = S;
+    a.I = I;
+    a.O = O;
+    a.rb = rb;
+    const int64_t tb = ((int64_t)S * idot_row_bytes(I) + 255) / 256 * 256;
+    a.table = (int8_t *)ws;
+    a.sx = reinterpret_cast<float *>((uint8_t *)ws + tb);
+    a.sq = reinterpret_cast<int *>((uint8_t *)ws + tb + (int64_t)S * 4);
+    StageTimer t(kStQgemv, (hipStream_t)stream);
+    return to_status(idot_launch(a, fmt, (hipStream_t)stream));
 }
 
 extern "C" int coli_router(const float *Wr, const float *bias, const float *x, int S, int E,

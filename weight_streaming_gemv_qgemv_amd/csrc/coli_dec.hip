@@ -151,7 +151,10 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
     constexpr uint32_t kbytes = KB * BITS / 8;
     // a lane's 16-byte segment past the row end is clamped to the row's last
     // one (it meets zero activations)
-    const uint32_t last_seg = (uint32_t)(a.rb - 16 - 16 * lchunk);
+    // (rows of fewer than 64 bytes: a chunk past the row end is read at the
+    // row's last chunk; it too meets zero activations)
+    const uint32_t coff = (uint32_t)min(16 * lchunk, (int)(a.rb - 16));
+    const uint32_t last_seg = (uint32_t)(a.rb - 16) - coff;
     const uint8_t *actb = reinterpret_cast<const uint8_t *>(a.act);
     const uint32_t arow = (uint32_t)(4 * a.kpad);       // bytes per row-table row
     // the N-tile and the first step this wave stages
@@ -195,7 +198,7 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
         const int obase = c.tile * RPB + wave * RPW;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
-            c.roff[mt] = (uint32_t)(min(obase + 16 * mt + lrow, c.Og - 1) * a.rb) + 16 * lchunk;
+            c.roff[mt] = (uint32_t)(min(obase + 16 * mt + lrow, c.Og - 1) * a.rb) + coff;
         // activation row of the pass row whose unit this lane stages (pass
         // row 8 nw + col / 2), from scalar loads; dead rows repeat the last
         // live one (their results are never stored)

@@ -152,7 +152,10 @@ __global__ __launch_bounds__(64 * kPreWaves) void k_pre(PreArgs a)
     const int n_items = gp_cnt * a.tiles;
     if (lb >= n_items) return;                          // whole block, before any barrier
     const int nkb = a.kpad / KB;                        // even and >= 4
-    const uint32_t last_seg = (uint32_t)(a.rb - 16 - 16 * q);
+    // a chunk past the end of a row shorter than 64 bytes is read at the
+    // row's last chunk (it meets zero activations)
+    const uint32_t coff = (uint32_t)min(16 * q, (int)(a.rb - 16));
+    const uint32_t last_seg = (uint32_t)(a.rb - 16) - coff;
     const uint8_t *actb = reinterpret_cast<const uint8_t *>(a.act);
     const uint32_t arow = (uint32_t)(2 * a.kpad);       // bytes per row-table row
 
@@ -193,7 +196,7 @@ __global__ __launch_bounds__(64 * kPreWaves) void k_pre(PreArgs a)
         const int obase = c.tile * RPB + wave * RPW;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
-            c.roff[mt] = (uint32_t)(min(obase + 16 * mt + col, c.Og - 1) * a.rb) + 16 * q;
+            c.roff[mt] = (uint32_t)(min(obase + 16 * mt + col, c.Og - 1) * a.rb) + coff;
     };
     // pass rows of an item: row-table row and activation sum (threads < 64;
     // dead rows repeat the last live one)

@@ -66,11 +66,14 @@ __global__ __launch_bounds__(512) void k_qmv(QmvArgs a)
     const int cs = 2 * nt;                              // columns per chunk in LDS
     const int units = kQmvWaves * STEPS * 4 * cs;       // units per round buffer
 
+    // a chunk past the end of a row shorter than 64 bytes is read at the
+    // row's last chunk (it meets zero activations)
+    const uint32_t coff = (uint32_t)min(16 * lchunk, (int)(a.rb - 16));
     uint32_t roff[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
-        roff[mt] = (uint32_t)(min(row0 + 16 * mt + lrow, a.O - 1) * a.rb) + 16 * lchunk;
-    const uint32_t last_seg = (uint32_t)(a.rb - 16 - 16 * lchunk);
+        roff[mt] = (uint32_t)(min(row0 + 16 * mt + lrow, a.O - 1) * a.rb) + coff;
+    const uint32_t last_seg = (uint32_t)(a.rb - 16) - coff;
 
     floatx4 acc[MT], accs = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -317,8 +320,9 @@ __global__ __launch_bounds__(512) void k_qmv1(QmvArgs a, int passes, int ntiles)
     }
     // then every weight load of this wave (a clamped copy for k-blocks past
     // the end: the loads stay unconditional, the products are skipped)
-    const uint32_t roff = (uint32_t)(min(row0 + lrow, a.O - 1) * a.rb) + 16 * lchunk;
-    const uint32_t last_seg = (uint32_t)(a.rb - 16 - 16 * lchunk);
+    const uint32_t coff = (uint32_t)min(16 * lchunk, (int)(a.rb - 16));   // short rows: see k_qmv
+    const uint32_t roff = (uint32_t)(min(row0 + lrow, a.O - 1) * a.rb) + coff;
+    const uint32_t last_seg = (uint32_t)(a.rb - 16) - coff;
     uint4 w[NKW][SEGS];
 #pragma unroll
     for (int i = 0; i < NKW; ++i) {
