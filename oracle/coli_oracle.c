@@ -413,6 +413,46 @@ int cor_moe(const cor_experts *ex, const cor_mlp *sh, const float *x, int S,
 }
 
 /* ------------------------------------------------------------------------
+ * Grouped-scale int4 (the pages' fmt 4, "int4-grouped") [docs-quickstart --
+ * qt_resolve_fmt; glm.c@98759bf -- qt_from_disk]: the int4 row layout, with
+ * one fp32 scale per group of gs consecutive elements along I instead of one
+ * per row; scale is [O, ng], ng = ceil(I / gs), the last group shorter when
+ * gs does not divide I:
+ *   y[s,o] = sum_g scale[o, g] * sum_{i in group g} v(o,i) x[s,i],
+ * in fp64; mag = sum_g |scale[o, g]| sum_{i in g} |v x|.
+ * ------------------------------------------------------------------------ */
+int cor_qgemv_grouped(const void *W, const float *scale, int gs, const float *x,
+                      int S, int I, int O, double *y, double *mag)
+{
+    if (gs < 1 || S < 0 || I < 0 || O < 0) return -1;
+    int64_t rb = cor_row_bytes(OR_I4, I);
+    int ng = (I + gs - 1) / gs;
+#pragma omp parallel for schedule(static)
+    for (int o = 0; o < O; ++o) {
+        const uint8_t *row = (const uint8_t *)W + (int64_t)o * rb;
+        for (int s = 0; s < S; ++s) {
+            const float *xs = x + (int64_t)s * I;
+            double acc = 0.0, am = 0.0;
+            for (int g = 0; g < ng; ++g) {
+                double part = 0.0, pm = 0.0;
+                int lo = g * gs, hi = lo + gs < I ? lo + gs : I;
+                for (int i = lo; i < hi; ++i) {
+                    double t = cor_unpack(OR_I4, row, i) * (double)xs[i];
+                    part += t;
+                    pm += fabs(t);
+                }
+                double sg = (double)scale[(int64_t)o * ng + g];
+                acc += sg * part;
+                am += fabs(sg) * pm;
+            }
+            y[(int64_t)s * O + o] = acc;
+            if (mag) mag[(int64_t)s * O + o] = am;
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------
  * Integer-dot qgemv (IDOT) [glm.c@98759bf -- qrow_i8, dot_i8i8, dot_i4i8,
  * matmul_q_idot, matmul_i4_idot]: each activation row is quantised to int8
  * by its absolute maximum, the dot product with the int8 / int4 weight

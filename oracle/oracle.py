@@ -55,6 +55,8 @@ def lib():
         L.cor_moe.restype = i32
         L.cor_moe.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, vp, i64,
                               vp, vp, vp, vp, vp, vp]
+        L.cor_qgemv_grouped.restype = i32
+        L.cor_qgemv_grouped.argtypes = [vp, vp, i32, vp, i32, i32, i32, vp, vp]
         L.cor_qrow_i8.restype = C.c_float
         L.cor_qrow_i8.argtypes = [vp, i32, vp]
         L.cor_qgemv_idot.restype = i32
@@ -190,6 +192,21 @@ def moe(ex: dict, shared: dict | None, x, idx, w, intermediates: bool = False):
                        rows, *ptrs)
     assert rc == 0, rc
     return res
+
+
+def qgemv_grouped(W, scale, gs: int, x, O: int | None = None):
+    """Grouped-scale int4 product (scale [O, ceil(I/gs)]); returns (y, mag) fp64."""
+    W = _c(W, np.uint8)
+    x = _c(np.atleast_2d(x), np.float32)
+    S, I = x.shape
+    O = W.shape[0] if O is None else O
+    sc = _c(scale, np.float32)
+    assert sc.size >= O * ((I + gs - 1) // gs)
+    y = np.empty((S, O), np.float64)
+    mag = np.empty((S, O), np.float64)
+    rc = lib().cor_qgemv_grouped(_p(W), _p(sc), int(gs), _p(x), S, I, O, _p(y), _p(mag))
+    assert rc == 0, rc
+    return y, mag
 
 
 def qrow_i8(x):

@@ -515,3 +515,52 @@ def test_idot_rejects_int2_and_f32(orc):
     for fmt in (F32, I2):
         with _pt.raises(AssertionError):
             orc.qgemv_idot(fmt, np.zeros((1, 4), np.uint8), np.ones(1, np.float32), np.ones((1, 4), np.float32))
+
+
+# ---------------------------------------------------------------- grouped int4
+def test_grouped_one_hot_reads_the_group_scale(orc):
+    """One-hot x at element j: y[o] = scale[o, j // gs] * v(o, j) exactly --
+    pins which scale each element takes, including a short last group."""
+    g = synth.rng(81)
+    O, I, gs = 5, 100, 32          # groups 0..3, the last one 4 elements
+    V = g.integers(-8, 8, size=(O, I))
+    W = _int4_bytes_from_values(V)
+    ng = (I + gs - 1) // gs
+    sc = (np.float32(2.0) ** -g.integers(0, 8, size=(O, ng))).astype(np.float32)
+    for j in (0, 31, 32, 63, 64, 95, 96, 99):
+        x = np.zeros((1, I), np.float32)
+        x[0, j] = 1.0
+        y, _ = orc.qgemv_grouped(W, sc, gs, x)
+        np.testing.assert_array_equal(y[0], sc[:, j // gs].astype(np.float64) * V[:, j])
+
+
+def test_grouped_reduces_to_per_row_scales(orc):
+    """gs = I (one group) is the per-row int4 product bit for bit; equal
+    scales across the groups agree with it to fp64 rounding."""
+    g = synth.rng(82)
+    O, I, S = 7, 256, 3
+    W = synth.weight_bytes(g, I4, O, I)
+    sc = synth.scales(g, O)
+    x = synth.activations(g, S, I)
+    ref, mref = orc.qgemv(I4, W, sc, x)
+    y, m = orc.qgemv_grouped(W, sc, I, x)
+    np.testing.assert_array_equal(y, ref)
+    np.testing.assert_array_equal(m, mref)
+    y2, _ = orc.qgemv_grouped(W, np.repeat(sc[:, None], 4, axis=1), 64, x)
+    np.testing.assert_allclose(y2, ref, rtol=1e-13, atol=1e-13)
+
+
+def test_grouped_exact_integers(orc):
+    """Integer x and power-of-two group scales: every partial sum is exact, so
+    the product equals an integer computation done with numpy."""
+    g = synth.rng(83)
+    O, I, gs = 9, 192, 64
+    V = g.integers(-8, 8, size=(O, I))
+    W = _int4_bytes_from_values(V)
+    sc = (np.float32(2.0) ** -g.integers(0, 6, size=(O, I // gs))).astype(np.float32)
+    x = g.integers(-4, 5, size=(2, I)).astype(np.float32)
+    y, _ = orc.qgemv_grouped(W, sc, gs, x)
+    parts = np.stack([x[:, k * gs:(k + 1) * gs].astype(np.int64) @ V[:, k * gs:(k + 1) * gs].T
+                      for k in range(I // gs)], axis=-1)          # [S, O, ng]
+    ref = (parts * sc[None, :, :].astype(np.float64)).sum(axis=-1)
+    np.testing.assert_array_equal(y, ref)
