@@ -310,6 +310,12 @@ def run_qgemv(args, dev):
     scd, xd = to_dev(sc, dev), to_dev(x, dev)
     y = torch.empty((S, O), dtype=torch.float32, device=dev)
     idot = getattr(args, "idot", False)
+    gs = getattr(args, "grouped", 0)
+    if gs:
+        if fmt != 2 or idot:
+            raise SystemExit("--grouped takes --fmt i4 (and not --idot)")
+        sc = synth.scales(g, O * (-(-I // gs))).reshape(O, -1)
+        scd = to_dev(sc, dev)
     if idot:
         if fmt not in (1, 2):
             raise SystemExit("--idot takes --fmt i8 or i4")
@@ -318,16 +324,25 @@ def run_qgemv(args, dev):
     def step(i):
         if idot:
             b.qgemv_idot(fmt, copies[i % len(copies)], scd, xd, y, ws=wsq)
+        elif gs:
+            b.qgemv_grouped(copies[i % len(copies)], scd, gs, xd, y)
         else:
             b.qgemv(fmt, copies[i % len(copies)], scd, xd, y)
 
-    step_bytes = O * W.shape[1] + O * 4 + S * I * 4 + S * O * 4
+    step_bytes = O * W.shape[1] + sc.nbytes + S * I * 4 + S * O * 4
     ms, wall, stages = time_steps(step, args.steps, args.warmup)
     q_ms, q_n = stages["qgemv"]
-    name = f"qgemv{'_idot' if idot else ''}_{args.fmt}_12288x6144_s{S}"
-    return dict(workload=name, ms=ms, wall=wall, step_bytes=step_bytes,
+    var = "_idot" if idot else f"_g{gs}" if gs else ""
+    entry = "coli_qgemv_idot" if idot else "coli_qgemv_grouped" if gs else "coli_qgemv"
+    name = f"qgemv{var}_{args.fmt}_12288x6144_s{S}"
+    wf = {0: "fp32", 1: "int8 per-row scale", 2: "int4 per-row scale", 3: "int2 per-row scale"}[fmt]
+    if idot:
+        wf += ", int8 activations (integer dot)"
+    if gs:
+        wf = f"int4 one scale per {gs} elements"
+    return dict(workload=name, ms=ms, wall=wall, step_bytes=step_bytes, weight_format=wf,
                 tokens=S, stages=stages, uniq=None,
-                dominant=dict(kernel=f"qgemv {args.fmt} ({'coli_qgemv_idot' if idot else 'coli_qgemv'})",
+                dominant=dict(kernel=f"qgemv {args.fmt} ({entry})",
                               bytes_per_launch=step_bytes,
                               ms_per_launch=q_ms / max(q_n, 1), launches=q_n))
 
@@ -358,6 +373,8 @@ def main():
     ap.add_argument("--fmt", default="i4", choices=["f32", "i8", "i4", "i2"], help="qgemv workload")
     ap.add_argument("--tokens", type=int, default=1, help="qgemv workload: S")
     ap.add_argument("--idot", action="store_true", help="qgemv workload: the integer-dot variant")
+    ap.add_argument("--grouped", type=int, default=0, metavar="GS",
+                    help="qgemv workload: grouped-scale int4, one scale per GS elements")
     ap.add_argument("--cpu-tokens", type=int, default=64)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -392,13 +409,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32 (int4 weights)",
+        "dtype": f"f32 ({r.get('weight_format', 'int4').split()[0]} weights)",
         "data": "synthetic",
         "config": {"workload": r["workload"], "tokens_per_step": r["tokens"],
                    "experts": 256 if r["uniq"] is not None else None,
                    "unique_experts_per_step": r["uniq"], "hidden": 6144,
                    "moe_inter": 2048, "top_k": 8 if r["uniq"] is not None else None,
-                   "weight_format": "int4 per-row scale",
+                   "weight_format": r.get("weight_format", "int4 per-row scale"),
                    "algorithmic_bytes_per_step": r["step_bytes"]},
         "tokens_per_s": round(r["tokens"] / (ms * 1e-3), 1),
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),

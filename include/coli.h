@@ -111,6 +111,22 @@ int coli_qgemv(int fmt, const void *W, const float *scale, const float *x,
  *          bytes, 256-byte aligned: the quantised rows.
  * Errors: COLI_EFMT, COLI_EINVAL, COLI_ESHAPE, COLI_EALIGN, COLI_ERANGE,
  * COLI_EWORKSPACE, COLI_EDEVICE. */
+/* Grouped-scale int4 matrix-vector product (the pages' fmt 4,
+ * "int4-grouped": int4 rows with one fp32 scale per group of gs consecutive
+ * elements along I instead of one per row) [docs-quickstart --
+ * qt_resolve_fmt; glm.c@98759bf -- qt_from_disk]:
+ *     y[s, o] = sum_g scale[o, g] * sum_{i in group g} v(o, i) * x[s, i],
+ * group g = elements g*gs .. min((g+1)*gs, I) - 1, v = nibble - 8.  Bound as
+ * coli_qgemv: |y - y_ref| <= 1e-4 * sum_g |scale[o,g]| sum |v x| + 1e-6.
+ *   W      [O, coli_row_bytes(COLI_I4, I)] bytes, 16-byte aligned, rows a
+ *          whole number of 16-byte segments (I a multiple of 32), I <= 12288.
+ *   scale  [O, ceil(I / gs)] fp32.   gs: 32, 64 or a multiple of 128.
+ *   x      [S, I] fp32, 16-byte aligned.   y [S, O] fp32, overwritten.
+ * Errors: COLI_EINVAL, COLI_ESHAPE, COLI_EALIGN, COLI_ERANGE (gs or I out of
+ * range), COLI_EDEVICE. */
+int coli_qgemv_grouped(const void *W, const float *scale, int gs, const float *x, float *y,
+                       int S, int I, int O, void *stream);
+
 size_t coli_qgemv_idot_workspace_bytes(int S, int I);
 int coli_qgemv_idot(int fmt, const void *W, const float *scale, const float *x, float *y,
                     int S, int I, int O, void *ws, size_t ws_bytes, void *stream);

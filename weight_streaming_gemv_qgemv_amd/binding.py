@@ -52,7 +52,7 @@ class WsLayout(C.Structure):
 
 EXPORTS = ["coli_row_bytes", "coli_qgemv", "coli_router", "coli_router_workspace_bytes",
            "coli_moe_workspace_bytes", "coli_moe_workspace_layout", "coli_moe_gemv",
-           "coli_moe_layer", "coli_moe_layer_tail", "coli_qgemv_idot",
+           "coli_moe_layer", "coli_moe_layer_tail", "coli_qgemv_idot", "coli_qgemv_grouped",
            "coli_qgemv_idot_workspace_bytes", "coli_check_device_flags", "coli_strerror", "coli_version",
            "coli_stage_timing", "coli_stage_times", "coli_stage_name"]
 NSTAGES = 8
@@ -87,6 +87,8 @@ def lib():
         L.coli_moe_layer.restype = i32
         L.coli_moe_layer.argtypes = [C.POINTER(RouterParams), C.POINTER(Experts), C.POINTER(Mlp),
                                      vp, i32, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+        L.coli_qgemv_grouped.restype = i32
+        L.coli_qgemv_grouped.argtypes = [vp, vp, i32, vp, vp, i32, i32, i32, vp]
         L.coli_qgemv_idot_workspace_bytes.restype = sz
         L.coli_qgemv_idot_workspace_bytes.argtypes = [i32, i32]
         L.coli_qgemv_idot.restype = i32
@@ -148,6 +150,18 @@ def qgemv(fmt: int, W: torch.Tensor, scale, x: torch.Tensor, y: torch.Tensor | N
         y = torch.empty((S, O), dtype=torch.float32, device=x.device)
     rc = lib().coli_qgemv(fmt, _ptr(W), _ptr(scale), _ptr(x), _ptr(y), S, I, O, _stream(stream))
     _check(rc, "coli_qgemv")
+    return y
+
+
+def qgemv_grouped(W: torch.Tensor, scale: torch.Tensor, gs: int, x: torch.Tensor,
+                  y: torch.Tensor | None = None, O: int | None = None, stream=None) -> torch.Tensor:
+    """Grouped-scale int4: scale [O, ceil(I/gs)], one per gs elements along I."""
+    S, I = x.shape
+    O = W.shape[0] if O is None else O
+    if y is None:
+        y = torch.empty((S, O), dtype=torch.float32, device=x.device)
+    rc = lib().coli_qgemv_grouped(_ptr(W), _ptr(scale), int(gs), _ptr(x), _ptr(y), S, I, O, _stream(stream))
+    _check(rc, "coli_qgemv_grouped")
     return y
 
 

@@ -719,6 +719,34 @@ extern "C" int coli_qgemv(int fmt, const void *W, const float *scale, const floa
     return to_status(gemv_launch(a, fmt, 1, S, (hipStream_t)stream));
 }
 
+extern "C" int coli_qgemv_grouped(const void *W, const float *scale, int gs, const float *x, float *y,
+                                  int S, int I, int O, void *stream)
+{
+    if (S < 0 || I < 0 || O < 0) return COLI_ESHAPE;
+    if (gs < 1) return COLI_ERANGE;
+    int rc = coli__check_qgemv(COLI_I4, W, scale, x, y, S, I, O);
+    if (rc != COLI_OK) return rc;
+    if (S == 0 || O == 0) return COLI_OK;
+    if (I < 1) return COLI_ESHAPE;
+    const int64_t rb = coli_row_bytes(COLI_I4, I);
+    if (!(gs == 32 || gs == 64 || (gs >= 128 && gs % 128 == 0))) return COLI_ERANGE;
+    if (I > 12288) return COLI_ERANGE;
+    if ((int64_t)O * rb >= ((int64_t)1 << 32) - 4096) return COLI_ERANGE;
+    if (!qmv_grouped_supported(rb, I, gs, W, x)) return COLI_EALIGN;
+    QmvArgs q = {};
+    q.W = (const uint8_t *)W;
+    q.scale = scale;
+    q.x = x;
+    q.y = y;
+    q.S = S;
+    q.I = I;
+    q.O = O;
+    q.rb = rb;
+    q.gs = gs;
+    StageTimer t(kStQgemv, (hipStream_t)stream);
+    return to_status(qmv_grouped_launch(q, (hipStream_t)stream));
+}
+
 extern "C" size_t coli_qgemv_idot_workspace_bytes(int S, int I)
 {
     if (S < 0 || I < 1) return 0;

@@ -480,6 +480,230 @@ hipError_t launch_q(const QmvArgs &a, hipStream_t st)
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- grouped int4
+// Grouped-scale int4 (one fp32 scale per gs elements along I) [docs-quickstart
+// -- qt_resolve_fmt; glm.c@98759bf -- qt_from_disk]: the one-shot structure
+// of k_qmv1, with the scale applied per group inside the sum.  A 64-byte
+// segment (128 elements) lies in one group when gs is a multiple of 128; for
+// gs = 64 / 32 it holds GPS = 2 / 4 groups, lane group q's 32 elements in
+// group q / (4 / GPS).  Per segment and group the code products and the
+// column sums are taken separately (the B operand zeroed outside the group's
+// lanes), then acc += scale[o, g] * (products - OFF * sum).  The block's
+// scales are staged in LDS as [group][16 rows].
+template <int GPS, int NKW>
+__global__ __launch_bounds__(512) void k_qmvg(QmvArgs a, int passes, int ntiles)
+{
+    using T = MF<kI4>;
+    constexpr int STEPS = T::STEPS, KB = T::KB, SPS = T::SPS;
+    constexpr float OFF = T::OFF;
+    constexpr uint32_t kbytes = KB / 2;
+    constexpr int RUN = 8;
+    constexpr int RW = NKW * KB / RUN;
+    constexpr int XP = (RW * kQ1Tpp + kWave - 1) / kWave;
+    extern __shared__ uint4 lds[];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 15, q = lane >> 4, lrow = lane >> 2, lchunk = lane & 3;
+    const int src4 = 4 * (4 * col + q);
+    const int xcd = blockIdx.x % 8, jb = blockIdx.x / 8;
+    const int tile = (jb / passes) * 8 + xcd, pass = jb % passes;
+    if (tile >= ntiles) return;                           // whole block, before any barrier
+    const int row0 = tile * 16;
+    const int t0 = pass * kQ1Tpp;
+    const int nt = min(kQ1Tpp, a.S - t0);
+    const int nkb = a.nkb, ng = a.ng, gs = a.gs;
+    const int cs = 2 * nt;
+    const int kw0 = wave * NKW;
+    const int rw = max(0, min(RW, (nkb - kw0) * (KB / RUN)));
+    // scales of the block's 16 rows, [group][row], after the largest staged
+    // activation area (kQ1Tpp rows)
+    float *sl = reinterpret_cast<float *>(lds + (int64_t)nkb * STEPS * 4 * (2 * kQ1Tpp));
+
+    // the block's scales first: 16 rows x ng groups, at most 16 x 384 (I <=
+    // 12288, gs >= 32), SCN per thread (rows past O read the last row's)
+    const int nsc = 16 * ng;
+    constexpr int SCN = 16 * 384 / 512;
+    float sv[SCN];
+#pragma unroll
+    for (int k = 0; k < SCN; ++k) {
+        const int i = min(tid + 512 * k, nsc - 1), r = i % 16, g = i / 16;
+        sv[k] = a.scale[(int64_t)min(row0 + r, a.O - 1) * ng + g];
+    }
+    // activations next
+    float4 xv[XP][RUN / 4];
+#pragma unroll
+    for (int p = 0; p < XP; ++p) {
+        const int u = lane + kWave * p;
+        const bool live = u < RW * nt && u % RW < rw;
+        const int t = live ? u / RW : 0, e0 = live ? kw0 * KB + (u % RW) * RUN : a.I;
+        const float *xr = a.x + (int64_t)(t0 + t) * a.I;
+        if (e0 + RUN <= a.I) {
+#pragma unroll
+            for (int i = 0; i < RUN / 4; ++i) xv[p][i] = gload4f(xr + e0 + 4 * i);
+        } else {
+#pragma unroll
+            for (int i = 0; i < RUN / 4; ++i) {
+                float f[4];
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) f[jj] = e0 + 4 * i + jj < a.I ? xr[e0 + 4 * i + jj] : 0.f;
+                xv[p][i] = make_float4(f[0], f[1], f[2], f[3]);
+            }
+        }
+    }
+    // then every weight load of this wave
+    const uint32_t coff = (uint32_t)min(16 * lchunk, (int)(a.rb - 16));   // short rows: see k_qmv
+    const uint32_t roff = (uint32_t)(min(row0 + lrow, a.O - 1) * a.rb) + coff;
+    const uint32_t last_seg = (uint32_t)(a.rb - 16) - coff;
+    uint4 w[NKW][2];
+#pragma unroll
+    for (int i = 0; i < NKW; ++i) {
+        const uint32_t b0 = (uint32_t)min(kw0 + i, nkb - 1) * kbytes;
+#pragma unroll
+        for (int sg = 0; sg < 2; ++sg) w[i][sg] = gload16(a.W + (roff + min(b0 + 64 * sg, last_seg)));
+    }
+    // scales into LDS, [group][row]
+#pragma unroll
+    for (int k = 0; k < SCN; ++k)
+        if (tid + 512 * k < nsc) sl[tid + 512 * k] = sv[k];
+    // activations into LDS: run -> bf16 hi / lo units (this wave's k-blocks)
+#pragma unroll
+    for (int p = 0; p < XP; ++p) {
+        const int u = lane + kWave * p;
+        if (u >= RW * nt) break;
+        if (u % RW >= rw) continue;
+        const int t = u / RW, e0 = kw0 * KB + (u % RW) * RUN;
+        float v[RUN];
+#pragma unroll
+        for (int i = 0; i < RUN / 4; ++i) {
+            v[4 * i] = xv[p][i].x;
+            v[4 * i + 1] = xv[p][i].y;
+            v[4 * i + 2] = xv[p][i].z;
+            v[4 * i + 3] = xv[p][i].w;
+        }
+        int c, j;
+        pos_of<kI4>(e0, c, j);
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            hw[m] = hilo_pair(v[m], v[m + 4], 0.f);
+            lw[m] = hilo_pair(v[m], v[m + 4], 1.f);
+        }
+        uint4 *dst = lds + c * cs + 2 * t;
+        dst[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        dst[1] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    }
+    __syncthreads();                                      // the scales are read by every wave
+
+    floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+    const uint32_t one2 = opaque_v(0x3F803F80u);           // bf16 (1, 1)
+    const uint4 ones = make_uint4(one2, one2, one2, one2);
+    const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+    const int bcol = (col >> 1) < nt ? col : 2 * (nt - 1) + (col & 1);
+    const int my_sub = q / (4 / GPS);                     // this lane group's group in a segment
+#pragma unroll
+    for (int i = 0; i < NKW; ++i) {
+        const int kb = kw0 + i;
+        if (kb >= nkb) break;                             // uniform
+#pragma unroll
+        for (int sg = 0; sg < 2; ++sg) {
+            const uint4 u = w[i][sg];
+            w[i][sg] = make_uint4((uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)u.x),
+                                  (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)u.y),
+                                  (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)u.z),
+                                  (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)u.w));
+        }
+        const uint4 *bw = lds + (kb * STEPS * 4 + q) * cs + bcol;
+#pragma unroll
+        for (int sg = 0; sg < 2; ++sg) {
+            floatx4 ap[GPS], sp[GPS];
+#pragma unroll
+            for (int j = 0; j < GPS; ++j) ap[j] = sp[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int sub = 0; sub < SPS; ++sub) {
+                const int s2 = sg * SPS + sub;
+                const uint4 b = bw[s2 * 4 * cs];
+                const uint4 cw = codes<kI4>(w[i][sg], sub);
+#pragma unroll
+                for (int j = 0; j < GPS; ++j) {
+                    const uint4 bj = GPS == 1 || my_sub == j ? b : zero;
+                    ap[j] = mfma(cw, bj, ap[j]);
+                    sp[j] = mfma(ones, bj, sp[j]);
+                }
+            }
+            // rows 4q + r of this lane, group of each part
+#pragma unroll
+            for (int j = 0; j < GPS; ++j) {
+                const int g = min((kb * KB + sg * 128 + j * (128 / GPS)) / gs, ng - 1);
+                const float4 s4 = *reinterpret_cast<const float4 *>(sl + g * 16 + 4 * q);
+                const float xsj = sp[j][0];
+                acc[0] += s4.x * (ap[j][0] - OFF * xsj);
+                acc[1] += s4.y * (ap[j][1] - OFF * xsj);
+                acc[2] += s4.z * (ap[j][2] - OFF * xsj);
+                acc[3] += s4.w * (ap[j][3] - OFF * xsj);
+            }
+        }
+    }
+
+    // partial tiles of the 8 waves, added in wave order
+    __syncthreads();
+    floatx4 *red = reinterpret_cast<floatx4 *>(lds);
+    red[wave * kWave + lane] = acc;
+    __syncthreads();
+    if (wave != 0) return;
+    floatx4 v = red[lane];
+#pragma unroll
+    for (int ww = 1; ww < kQmvWaves; ++ww) v += red[ww * kWave + lane];
+    const int ob = row0 + 4 * q;
+    float res[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) res[r] = v[r] + __shfl_xor(v[r], 1, kWave);   // hi + lo column
+    const int tok = col >> 1;
+    if ((col & 1) == 0 && tok < nt) {
+        float *yp = a.y + (int64_t)(t0 + tok) * a.O;
+        if (a.y_vec4 && ob + 3 < a.O) {
+            *reinterpret_cast<float4 *>(yp + ob) = make_float4(res[0], res[1], res[2], res[3]);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (ob + r < a.O) yp[ob + r] = res[r];
+        }
+    }
+}
+
+template <int GPS, int NKW>
+hipError_t launch_qg(const QmvArgs &a, hipStream_t st)
+{
+    const int ntiles = (a.O + 15) / 16;
+    const int passes = (a.S + kQ1Tpp - 1) / kQ1Tpp;
+    const int64_t grid = (int64_t)(ntiles + 7) / 8 * 8 * passes;
+    if (grid <= 0 || grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const size_t stage = (size_t)a.nkb * MF<kI4>::STEPS * 4 * (2 * kQ1Tpp) * 16 + (size_t)a.ng * 16 * 4;
+    const size_t red = (size_t)kQmvWaves * kWave * 16;     // the partial tiles, at the end
+    const size_t lds = stage > red ? stage : red;
+    if (lds > 160 * 1024) return hipErrorInvalidValue;
+    auto kern = k_qmvg<GPS, NKW>;
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * kQmvWaves), lds, st, a, passes, ntiles);
+    return hipGetLastError();
+}
+
+template <int GPS>
+hipError_t launch_qg_nkw(const QmvArgs &a, int nkw, hipStream_t st)
+{
+    switch (nkw) {
+    case 1: return launch_qg<GPS, 1>(a, st);
+    case 2: return launch_qg<GPS, 2>(a, st);
+    case 3: return launch_qg<GPS, 3>(a, st);
+    case 4: return launch_qg<GPS, 4>(a, st);
+    case 5: return launch_qg<GPS, 5>(a, st);
+    case 6: return launch_qg<GPS, 6>(a, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace
 
 bool qmv_supported(int fmt, int64_t rb, int I, int O, const void *W, const float *x)
@@ -516,6 +740,30 @@ hipError_t qmv_launch(QmvArgs a, int fmt, hipStream_t st)
     case kI2: return wide ? launch_q<kI2, 4>(a, st) : launch_q<kI2, 2>(a, st);
     default: return hipErrorInvalidValue;
     }
+}
+
+}  // namespace coli
+
+namespace coli {
+
+bool qmv_grouped_supported(int64_t rb, int I, int gs, const void *W, const float *x)
+{
+    const int nkb = (I + MF<kI4>::KB - 1) / MF<kI4>::KB;
+    return (gs == 32 || gs == 64 || (gs >= 128 && gs % 128 == 0)) && rb >= 16 && rb % 16 == 0 &&
+           I % 4 == 0 && ((uintptr_t)W & 15u) == 0 && ((uintptr_t)x & 15u) == 0 &&
+           (nkb + kQmvWaves - 1) / kQmvWaves <= 6;
+}
+
+hipError_t qmv_grouped_launch(QmvArgs a, hipStream_t st)
+{
+    if (a.S <= 0 || a.O <= 0) return hipSuccess;
+    a.nkb = (a.I + MF<kI4>::KB - 1) / MF<kI4>::KB;
+    a.ng = (a.I + a.gs - 1) / a.gs;
+    a.y_vec4 = a.O % 4 == 0 && ((uintptr_t)a.y & 15u) == 0;
+    const int nkw = (a.nkb + kQmvWaves - 1) / kQmvWaves;
+    if (a.gs == 32) return launch_qg_nkw<4>(a, nkw, st);
+    if (a.gs == 64) return launch_qg_nkw<2>(a, nkw, st);
+    return launch_qg_nkw<1>(a, nkw, st);
 }
 
 }  // namespace coli
