@@ -120,7 +120,8 @@ int coli_qgemv(int fmt, const void *W, const float *scale, const float *x,
  * coli_qgemv: |y - y_ref| <= 1e-4 * sum_g |scale[o,g]| sum |v x| + 1e-6.
  *   W      [O, coli_row_bytes(COLI_I4, I)] bytes, 16-byte aligned, rows a
  *          whole number of 16-byte segments (I a multiple of 32), I <= 12288.
- *   scale  [O, ceil(I / gs)] fp32.   gs: 32, 64 or a multiple of 128.
+ *   scale  [O, ceil(I / gs)] fp32, 16-byte aligned.   gs: 32, 64 or a multiple
+ *          of 128.
  *   x      [S, I] fp32, 16-byte aligned.   y [S, O] fp32, overwritten.
  * Errors: COLI_EINVAL, COLI_ESHAPE, COLI_EALIGN, COLI_ERANGE (gs or I out of
  * range), COLI_EDEVICE. */

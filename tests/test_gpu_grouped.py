@@ -134,6 +134,7 @@ def test_errors_and_empty(dev):
     # misaligned operands
     assert call(32, I, Wp=p(W) + 4) == b.EALIGN
     assert call(32, I, xp=p(x) + 4) == b.EALIGN
+    assert L.coli_qgemv_grouped(p(W), p(sc) + 4, 32, p(x), p(y), 2, I, O, None) == b.EALIGN
     # null operands
     assert L.coli_qgemv_grouped(None, p(sc), 32, p(x), p(y), 2, I, O, None) == b.EINVAL
     assert L.coli_qgemv_grouped(p(W), None, 32, p(x), p(y), 2, I, O, None) == b.EINVAL

@@ -732,7 +732,7 @@ extern "C" int coli_qgemv_grouped(const void *W, const float *scale, int gs, con
     if (!(gs == 32 || gs == 64 || (gs >= 128 && gs % 128 == 0))) return COLI_ERANGE;
     if (I > 12288) return COLI_ERANGE;
     if ((int64_t)O * rb >= ((int64_t)1 << 32) - 4096) return COLI_ERANGE;
-    if (!qmv_grouped_supported(rb, I, gs, W, x)) return COLI_EALIGN;
+    if (!qmv_grouped_supported(rb, I, gs, W, scale, x)) return COLI_EALIGN;
     QmvArgs q = {};
     q.W = (const uint8_t *)W;
     q.scale = scale;

@@ -25,8 +25,8 @@ bool qmv_supported(int fmt, int64_t rb, int I, int O, const void *W, const float
 hipError_t qmv_launch(QmvArgs a, int fmt, hipStream_t st);
 
 // Grouped-scale int4 (scale [O, ceil(I / gs)]): gs 32, 64 or a multiple of
-// 128; 16-byte row segments, 16-byte aligned W and x, I <= 12288.
-bool qmv_grouped_supported(int64_t rb, int I, int gs, const void *W, const float *x);
+// 128; 16-byte row segments, 16-byte aligned W, scale and x, I <= 12288.
+bool qmv_grouped_supported(int64_t rb, int I, int gs, const void *W, const float *scale, const float *x);
 hipError_t qmv_grouped_launch(QmvArgs a, hipStream_t st);
 
 }  // namespace coli

@@ -486,10 +486,14 @@ hipError_t launch_q(const QmvArgs &a, hipStream_t st)
 // of k_qmv1, with the scale applied per group inside the sum.  A 64-byte
 // segment (128 elements) lies in one group when gs is a multiple of 128; for
 // gs = 64 / 32 it holds GPS = 2 / 4 groups, lane group q's 32 elements in
-// group q / (4 / GPS).  Per segment and group the code products and the
-// column sums are taken separately (the B operand zeroed outside the group's
-// lanes), then acc += scale[o, g] * (products - OFF * sum).  The block's
-// scales are staged in LDS as [group][16 rows].
+// group q / (4 / GPS).  The groups take the product's spare columns: column
+// col = h + 2 t + 4 j holds token t's hi / lo part (h) restricted to the
+// segment's group j (the B operand is zero in the lane groups of other
+// groups), so one code product and one column-sum product per step serve
+// every group.  Per segment each lane adds scale[o, g(j)] * (products -
+// OFF * sum) for its column's group; the columns of one token are summed at
+// the end.  The block's scales (16 consecutive rows: one contiguous span of
+// 16 ng floats) are staged in LDS in row order.
 template <int GPS, int NKW>
 __global__ __launch_bounds__(512) void k_qmvg(QmvArgs a, int passes, int ntiles)
 {
@@ -500,6 +504,7 @@ __global__ __launch_bounds__(512) void k_qmvg(QmvArgs a, int passes, int ntiles)
     constexpr int RUN = 8;
     constexpr int RW = NKW * KB / RUN;
     constexpr int XP = (RW * kQ1Tpp + kWave - 1) / kWave;
+    static_assert(kQ1Tpp == 2, "columns h + 2t + 4j");
     extern __shared__ uint4 lds[];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -515,19 +520,31 @@ __global__ __launch_bounds__(512) void k_qmvg(QmvArgs a, int passes, int ntiles)
     const int cs = 2 * nt;
     const int kw0 = wave * NKW;
     const int rw = max(0, min(RW, (nkb - kw0) * (KB / RUN)));
-    // scales of the block's 16 rows, [group][row], after the largest staged
-    // activation area (kQ1Tpp rows)
-    float *sl = reinterpret_cast<float *>(lds + (int64_t)nkb * STEPS * 4 * (2 * kQ1Tpp));
+    // scales of the block's rows after the largest staged activation area
+    // (min(S, kQ1Tpp) rows)
+    const int ntmax = min(a.S, kQ1Tpp);
+    float *sl = reinterpret_cast<float *>(lds + (int64_t)nkb * STEPS * 4 * (2 * ntmax));
 
-    // the block's scales first: 16 rows x ng groups, at most 16 x 384 (I <=
-    // 12288, gs >= 32), SCN per thread (rows past O read the last row's)
-    const int nsc = 16 * ng;
-    constexpr int SCN = 16 * 384 / 512;
-    float sv[SCN];
+    // the block's scales first: rows row0 .. row0 + 15 (those below O) are
+    // the contiguous span scale[row0 * ng ..], 16-byte aligned (row0 * ng is a
+    // multiple of 16 and the base is aligned).  A k-block holds at most
+    // 2 GPS groups and a block at most 8 NKW k-blocks, so the span is at most
+    // 16 x 16 GPS NKW floats: SCN float4 per thread (checked at launch)
+    const int nsc = (min(row0 + 16, a.O) - row0) * ng;
+    const float *sbase = a.scale + (int64_t)row0 * ng;
+    constexpr int SCN = (GPS * NKW + 7) / 8;
+    float4 sv[SCN];
 #pragma unroll
     for (int k = 0; k < SCN; ++k) {
-        const int i = min(tid + 512 * k, nsc - 1), r = i % 16, g = i / 16;
-        sv[k] = a.scale[(int64_t)min(row0 + r, a.O - 1) * ng + g];
+        const int e = 4 * (tid + 512 * k);
+        if (e + 3 < nsc) {
+            sv[k] = gload4f(sbase + e);
+        } else {
+            float f[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) f[c] = e + c < nsc ? sbase[e + c] : 0.f;
+            sv[k] = make_float4(f[0], f[1], f[2], f[3]);
+        }
     }
     // activations next
     float4 xv[XP][RUN / 4];
@@ -561,10 +578,44 @@ __global__ __launch_bounds__(512) void k_qmvg(QmvArgs a, int passes, int ntiles)
 #pragma unroll
         for (int sg = 0; sg < 2; ++sg) w[i][sg] = gload16(a.W + (roff + min(b0 + 64 * sg, last_seg)));
     }
-    // scales into LDS, [group][row]
+    // scales into LDS in row order, row stride ngp = ng rounded up to 4 mod 16
+    // (the span's float4 land on consecutive banks; the epilogue's 16 reads,
+    // rows 4q .. 4q + 3 x four groups, on distinct banks)
+    const int ngp = (ng + 11) / 16 * 16 + 4;
+    {
+        const float inv = 1.0f / (float)ng;
+        auto split = [&](int e, int &r, int &g) {          // e = r ng + g, e < 6144
+            r = (int)((float)e * inv);                     // off by at most one
+            g = e - r * ng;
+            if (g < 0) { --r; g += ng; }
+            if (g >= ng) { ++r; g -= ng; }
+        };
+        if (ng % 4 == 0) {                                 // a float4 stays in one row
 #pragma unroll
-    for (int k = 0; k < SCN; ++k)
-        if (tid + 512 * k < nsc) sl[tid + 512 * k] = sv[k];
+            for (int k = 0; k < SCN; ++k) {
+                const int e = 4 * (tid + 512 * k);
+                if (e < nsc) {
+                    int r, g;
+                    split(e, r, g);
+                    *reinterpret_cast<float4 *>(sl + r * ngp + g) = sv[k];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < SCN; ++k) {
+                const float f[4] = {sv[k].x, sv[k].y, sv[k].z, sv[k].w};
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int e = 4 * (tid + 512 * k) + c;
+                    if (e < nsc) {
+                        int r, g;
+                        split(e, r, g);
+                        sl[r * ngp + g] = f[c];
+                    }
+                }
+            }
+        }
+    }
     // activations into LDS: run -> bf16 hi / lo units (this wave's k-blocks)
 #pragma unroll
     for (int p = 0; p < XP; ++p) {
@@ -597,9 +648,12 @@ __global__ __launch_bounds__(512) void k_qmvg(QmvArgs a, int passes, int ntiles)
     floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
     const uint32_t one2 = opaque_v(0x3F803F80u);           // bf16 (1, 1)
     const uint4 ones = make_uint4(one2, one2, one2, one2);
-    const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
-    const int bcol = (col >> 1) < nt ? col : 2 * (nt - 1) + (col & 1);
-    const int my_sub = q / (4 / GPS);                     // this lane group's group in a segment
+    // column col = h + 2 t + 4 j: token t (dead tokens read the last live
+    // one's units and are never written), group j of the segment
+    const int tcol = (col >> 1) & 1, jcol = col >> 2;
+    const int bcol = tcol < nt ? (col & 3) : 2 * (nt - 1) + (col & 1);
+    const bool mine = jcol == q / (4 / GPS);              // this lane group's elements are in group j
+    const int jofs = jcol * (128 / GPS);                  // first element of group j in a segment
 #pragma unroll
     for (int i = 0; i < NKW; ++i) {
         const int kb = kw0 + i;
@@ -615,32 +669,24 @@ __global__ __launch_bounds__(512) void k_qmvg(QmvArgs a, int passes, int ntiles)
         const uint4 *bw = lds + (kb * STEPS * 4 + q) * cs + bcol;
 #pragma unroll
         for (int sg = 0; sg < 2; ++sg) {
-            floatx4 ap[GPS], sp[GPS];
-#pragma unroll
-            for (int j = 0; j < GPS; ++j) ap[j] = sp[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+            floatx4 ap = floatx4{0.f, 0.f, 0.f, 0.f}, sp = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int sub = 0; sub < SPS; ++sub) {
                 const int s2 = sg * SPS + sub;
-                const uint4 b = bw[s2 * 4 * cs];
-                const uint4 cw = codes<kI4>(w[i][sg], sub);
-#pragma unroll
-                for (int j = 0; j < GPS; ++j) {
-                    const uint4 bj = GPS == 1 || my_sub == j ? b : zero;
-                    ap[j] = mfma(cw, bj, ap[j]);
-                    sp[j] = mfma(ones, bj, sp[j]);
-                }
+                const uint4 b0 = bw[s2 * 4 * cs];
+                const uint4 b = mine ? b0 : make_uint4(0u, 0u, 0u, 0u);
+                ap = mfma(codes<kI4>(w[i][sg], sub), b, ap);
+                sp = mfma(ones, b, sp);
             }
-            // rows 4q + r of this lane, group of each part
-#pragma unroll
-            for (int j = 0; j < GPS; ++j) {
-                const int g = min((kb * KB + sg * 128 + j * (128 / GPS)) / gs, ng - 1);
-                const float4 s4 = *reinterpret_cast<const float4 *>(sl + g * 16 + 4 * q);
-                const float xsj = sp[j][0];
-                acc[0] += s4.x * (ap[j][0] - OFF * xsj);
-                acc[1] += s4.y * (ap[j][1] - OFF * xsj);
-                acc[2] += s4.z * (ap[j][2] - OFF * xsj);
-                acc[3] += s4.w * (ap[j][3] - OFF * xsj);
-            }
+            // rows 4q + r, this column's group (dead groups: zero products)
+            const int g = min((kb * KB + sg * 128 + jofs) / gs, ng - 1);
+            const float *sr = sl + 4 * q * ngp + g;
+            const float4 s4 = make_float4(sr[0], sr[ngp], sr[2 * ngp], sr[3 * ngp]);
+            const float xs = sp[0];
+            acc[0] += s4.x * (ap[0] - OFF * xs);
+            acc[1] += s4.y * (ap[1] - OFF * xs);
+            acc[2] += s4.z * (ap[2] - OFF * xs);
+            acc[3] += s4.w * (ap[3] - OFF * xs);
         }
     }
 
@@ -656,9 +702,14 @@ __global__ __launch_bounds__(512) void k_qmvg(QmvArgs a, int passes, int ntiles)
     const int ob = row0 + 4 * q;
     float res[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) res[r] = v[r] + __shfl_xor(v[r], 1, kWave);   // hi + lo column
-    const int tok = col >> 1;
-    if ((col & 1) == 0 && tok < nt) {
+    for (int r = 0; r < 4; ++r) {
+        float t = v[r] + __shfl_xor(v[r], 1, kWave);      // hi + lo
+        if (GPS > 1) t += __shfl_xor(t, 4, kWave);        // groups j: 0 + 1, 2 + 3
+        if (GPS > 2) t += __shfl_xor(t, 8, kWave);        // (0 + 1) + (2 + 3)
+        res[r] = t;
+    }
+    const int tok = tcol;
+    if ((col & 1) == 0 && jcol == 0 && tok < nt) {
         float *yp = a.y + (int64_t)(t0 + tok) * a.O;
         if (a.y_vec4 && ob + 3 < a.O) {
             *reinterpret_cast<float4 *>(yp + ob) = make_float4(res[0], res[1], res[2], res[3]);
@@ -677,10 +728,12 @@ hipError_t launch_qg(const QmvArgs &a, hipStream_t st)
     const int passes = (a.S + kQ1Tpp - 1) / kQ1Tpp;
     const int64_t grid = (int64_t)(ntiles + 7) / 8 * 8 * passes;
     if (grid <= 0 || grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-    const size_t stage = (size_t)a.nkb * MF<kI4>::STEPS * 4 * (2 * kQ1Tpp) * 16 + (size_t)a.ng * 16 * 4;
+    const int ntmax = a.S < kQ1Tpp ? a.S : kQ1Tpp;
+    const size_t stage = (size_t)a.nkb * MF<kI4>::STEPS * 4 * (2 * ntmax) * 16 + (size_t)(a.ng + 15) * 16 * 4;
     const size_t red = (size_t)kQmvWaves * kWave * 16;     // the partial tiles, at the end
     const size_t lds = stage > red ? stage : red;
     if (lds > 160 * 1024) return hipErrorInvalidValue;
+    if (16 * a.ng > 4 * 512 * ((GPS * NKW + 7) / 8)) return hipErrorInvalidValue;   // the scale span
     auto kern = k_qmvg<GPS, NKW>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -746,11 +799,12 @@ hipError_t qmv_launch(QmvArgs a, int fmt, hipStream_t st)
 
 namespace coli {
 
-bool qmv_grouped_supported(int64_t rb, int I, int gs, const void *W, const float *x)
+bool qmv_grouped_supported(int64_t rb, int I, int gs, const void *W, const float *scale, const float *x)
 {
     const int nkb = (I + MF<kI4>::KB - 1) / MF<kI4>::KB;
     return (gs == 32 || gs == 64 || (gs >= 128 && gs % 128 == 0)) && rb >= 16 && rb % 16 == 0 &&
            I % 4 == 0 && ((uintptr_t)W & 15u) == 0 && ((uintptr_t)x & 15u) == 0 &&
+           ((uintptr_t)scale & 15u) == 0 &&
            (nkb + kQmvWaves - 1) / kQmvWaves <= 6;
 }
 
