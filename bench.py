@@ -252,6 +252,82 @@ def run_prefill2048(args, dev):
                               launches=gu_n))
 
 
+def run_ep_slice(args, dev, prefill):
+    """One GPU's share of the MoE block under expert parallelism over
+    `args.ep_slice` GPUs (256 / N experts each): the router (replicated, so
+    every GPU runs it), the local experts' grouped gate/up, SwiGLU and down
+    on the rows routed to them, and the shared expert.  The slice timed is
+    the one with the most routed rows, and it also holds the shared expert:
+    the step time of the slowest GPU.  The all-gather of x before and the
+    sum-reduction of the partial outputs after are not part of the step.
+    Routing: the router's own output on the synthetic rows (decode, 64
+    tokens) or the Zipf(1.1) routing of the prefill workload (2048 tokens,
+    bf16 matrix cores), remapped to local ids, other slots -1 (empty)."""
+    import torch
+    from weight_streaming_gemv_qgemv_amd import binding as b
+    from weight_streaming_gemv_qgemv_amd import synth
+    N = args.ep_slice
+    K, E, D, F, fmt = 8, 256, 6144, 2048, 2
+    if E % N:
+        raise SystemExit(f"--ep-slice {N}: 256 experts do not split evenly")
+    El = E // N
+    S = 2048 if prefill else 64
+    g = synth.rng(4500 if prefill else 4001)
+    Wr, bias = synth.router_weights(g, E, D)
+    x = synth.activations(g, S, D)
+    Wrd, biasd, xd = to_dev(Wr, dev), to_dev(bias, dev), to_dev(x, dev)
+    rws = b.alloc_workspace(b.router_workspace_bytes(S, E, D), dev)
+    if prefill:
+        idx, w = synth.routing_zipf(g, S, K, E)
+    else:
+        r = b.router(Wrd, biasd, xd, K, 1, 2.5, 0.0, ws=rws)
+        torch.cuda.synchronize()
+        idx, w = r["idx"].cpu().numpy(), r["w"].cpu().numpy()
+    rows_per_slice = np.bincount(idx.ravel() // El, minlength=N)
+    gsl = int(np.argmax(rows_per_slice))
+    lo = gsl * El
+    local = (idx >= lo) & (idx < lo + El)
+    idl = np.where(local, idx - lo, -1).astype(np.int32)
+    wl = np.where(local, w, 0.0).astype(np.float32)
+    log(f"slice {gsl} of {N}: experts {lo}..{lo + El - 1}, {int(local.sum())} routed rows "
+        f"(per slice: {rows_per_slice.tolist()})")
+    bank = synth.expert_bank(4000, fmt, E, D, F, experts=range(lo, lo + El))
+    bank["E"] = El
+    shared = synth.shared_mlp(4000, fmt, D, F)
+    banks = [bank_to_dev(bank, dev)]
+    banks.append(clone_bank(banks[0]))
+    sd = [bank_to_dev(shared, dev)]
+    sd.append(clone_bank(sd[0]))
+    idd, wd = to_dev(idl, dev), to_dev(wl, dev)
+    prec = 1 if prefill else 0
+    out = torch.empty((S, D), dtype=torch.float32, device=dev)
+    ws = b.alloc_workspace(b.moe_workspace_bytes(S, K, El, D, F, F, prec), dev)
+
+    def step(i):
+        j = i & 1
+        b.router(Wrd, biasd, xd, K, 1, 2.5, 0.0, ws=rws)
+        b.moe_layer(None, banks[j], sd[j], xd, pre_idx=idd, pre_w=wd, out=out, prec=prec, ws=ws)
+
+    uniq = int(np.unique(idl[idl >= 0]).size)
+    gu, dn = expert_bytes(fmt, D, F)
+    nrows = int(local.sum())
+    step_bytes = (E * D * 4 + E * 4) + S * D * 4 + uniq * (gu + dn) + (gu + dn) + S * D * 4 + S * K * 8
+    ms, wall, stages = time_steps(step, args.steps, args.warmup)
+    gu_ms, gu_n = stages["gate_up"]
+    rows = nrows + S
+    res = dict(workload=f"ep{N}_slice_{'prefill_2048_bf16' if prefill else 'decode_64'}", ms=ms,
+               wall=wall, step_bytes=step_bytes, tokens=S, stages=stages, uniq=uniq,
+               experts=El, ep=dict(gpus=N, slice=gsl, routed_rows=nrows,
+                                   rows_per_slice=rows_per_slice.tolist(), shared_expert_here=True),
+               dominant=dict(kernel=f"{'k_pre' if prefill else 'k_dec'}<I4,2> (grouped expert gate/up + SwiGLU)",
+                             bytes_per_launch=(uniq + 1) * gu + S * D * 4 + rows * F * 4,
+                             ms_per_launch=gu_ms / max(gu_n, 1), launches=gu_n))
+    if prefill:
+        res["flops"] = 2 * rows * 3 * D * F
+        res["dominant"]["flops_per_launch"] = 2 * rows * 2 * D * F
+    return res
+
+
 def run_decode16(args, dev):
     import torch
     from weight_streaming_gemv_qgemv_amd import binding as b
@@ -375,6 +451,10 @@ def main():
     ap.add_argument("--idot", action="store_true", help="qgemv workload: the integer-dot variant")
     ap.add_argument("--grouped", type=int, default=0, metavar="GS",
                     help="qgemv workload: grouped-scale int4, one scale per GS elements")
+    ap.add_argument("--ep-slice", type=int, default=0, metavar="N",
+                    help="layer64 / prefill2048: time one GPU's share under expert parallelism "
+                         "over N GPUs (256/N local experts; the slice with the most routed rows, "
+                         "with the shared expert)")
     ap.add_argument("--cpu-tokens", type=int, default=64)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -393,7 +473,12 @@ def main():
         return
     run = {"prefill2048": run_prefill2048, "layer64": run_layer64, "tail64": run_tail64,
            "decode16": run_decode16, "qgemv": run_qgemv}[args.workload]
-    r = run(args, dev)
+    if args.ep_slice:
+        if args.workload not in ("layer64", "prefill2048"):
+            raise SystemExit("--ep-slice applies to the layer64 and prefill2048 workloads")
+        r = run_ep_slice(args, dev, args.workload == "prefill2048")
+    else:
+        r = run(args, dev)
     ms = r["ms"]
     gbs = r["step_bytes"] / (ms * 1e-3) / 1e9
     dom = r["dominant"]
@@ -412,7 +497,7 @@ def main():
         "dtype": f"f32 ({r.get('weight_format', 'int4').split()[0]} weights)",
         "data": "synthetic",
         "config": {"workload": r["workload"], "tokens_per_step": r["tokens"],
-                   "experts": 256 if r["uniq"] is not None else None,
+                   "experts": r.get("experts", 256) if r["uniq"] is not None else None,
                    "unique_experts_per_step": r["uniq"], "hidden": 6144,
                    "moe_inter": 2048, "top_k": 8 if r["uniq"] is not None else None,
                    "weight_format": r.get("weight_format", "int4 per-row scale"),
@@ -428,6 +513,8 @@ def main():
                      "ms_per_launch": round(dom["ms_per_launch"], 5)},
         "context": {"pages_metal_moe_gemv_GBps": "358-389 (Apple-Silicon GPU, unified memory)"},
     }
+    if "ep" in r:
+        line["config"]["expert_parallel_share"] = r["ep"]
     if "flops" in r:
         # prefill: the matrix cores bound the dominant kernel
         tf = dom["flops_per_launch"] / (dom["ms_per_launch"] * 1e-3) / 1e12 if dom["ms_per_launch"] else None
