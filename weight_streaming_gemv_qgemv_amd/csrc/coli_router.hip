@@ -114,18 +114,43 @@ __global__ __launch_bounds__(256) void k_router_partial(const float *__restrict_
     }
 }
 
+// Order-preserving key of a finite float: a > b  <=>  key(a) > key(b) (-0
+// is first made +0, so equal values get equal keys); every key is > 0.
+__device__ __forceinline__ uint32_t order_key(float f)
+{
+    const uint32_t u = __float_as_uint(f + 0.0f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Wave-wide max / min of a 32-bit value on the DPP network (registers only):
+// pairs within quads, half rows and rows, then rows 0-1 into 1 and 3, rows
+// 0-2 into 3; lane 63 ends with the whole wave's result.
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_ext_u32(uint32_t v)
+{
+    const int id = MAX ? 0 : -1;
+    auto f = [](uint32_t a, uint32_t b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
+    v = f(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+    v = f(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+    v = f(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+    v = f(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x140, 0xF, 0xF, false));  // row_mirror
+    v = f(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x142, 0xA, 0xF, false));  // row_bcast:15
+    v = f(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x143, 0xC, 0xF, false));  // row_bcast:31
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 // One token per block.  First the block sums each score's slices in slice
 // order and takes the sigmoid in fp64, rounded once (scores go to `sig` and
 // to LDS).  Then the first wave runs the greedy top-K over
 // choice = sig + bias:
 //  - lane l owns experts e = l + 64 j (j < ceil(E/64) <= 16), so e rises
 //    with j; a lane's candidate is its first maximal untaken choice
-//    (strict '>' while j rises);
-//  - the wave reduces (value, index) pairs with "larger value, else lower
-//    index", a total order on finite values, so every lane agrees on the
-//    pick, which equals the sequential scan's first maximum;
-//  - the pick's owner marks it taken; lane 0 then runs the pages' tail
-//    (top-p, normalisation, routed_scale) sequentially in fp32.
+//    (strict '>' on order keys while j rises);
+//  - the wave's largest key wins; when several lanes hold it, the lowest
+//    e = 64 j + l among them (a second reduction), so the pick is the
+//    sequential scan's first maximum;
+//  - the pick's owner clears it; lane 0 then runs the pages' tail (top-p,
+//    normalisation, routed_scale) sequentially in fp32.
 __global__ __launch_bounds__(256) void k_router_topk(const double *__restrict__ part, int splits,
                                                      const float *__restrict__ bias, int S,
                                                      int E, int K, int norm_topk,
@@ -141,6 +166,14 @@ __global__ __launch_bounds__(256) void k_router_topk(const double *__restrict__ 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int s0 = blockIdx.x;
     const int nt = 1;
+    const int per = (E + 63) / 64;
+    // the selecting wave's biases, requested before anything else
+    float bz[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int e = lane + 64 * j;
+        bz[j] = (wave == 0 && j < per && e < E) ? bias[e] : 0.f;
+    }
     {
         const int64_t n = (int64_t)S * E;
         for (int i = threadIdx.x; i < nt * E; i += 256) {
@@ -166,51 +199,44 @@ __global__ __launch_bounds__(256) void k_router_topk(const double *__restrict__ 
     const int s = s0;
     if (wave != 0) return;   // whole waves leave; no block barrier below
     const float *sg = sig_s;
-    const int per = (E + 63) / 64;
-    float ch[16], sv[16];
+    float sv[16];
+    uint32_t key[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
         const int e = lane + 64 * j;
         const bool ok = j < per && e < E;
         sv[j] = ok ? sg[e] : 0.f;
-        ch[j] = ok ? sv[j] + bias[e] : 0.f;
+        key[j] = ok ? order_key(sv[j] + bz[j]) : 0u;     // choice = sig + bias (fp32)
     }
-    uint32_t live = 0;
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-        if (j < per && lane + 64 * j < E) live |= 1u << j;
     int *pick = pick_s;
     float *pw = pw_s;
     for (int kk = 0; kk < K; ++kk) {
-        float bv = 0.f;
-        int bi = 0x7FFFFFFF;
-        bool have = false;
+        uint32_t bk = 0;
+        int bj = 0;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            if (live & (1u << j)) {
-                if (!have || ch[j] > bv) { bv = ch[j]; bi = lane + 64 * j; have = true; }
+        for (int j = 0; j < 16; ++j)
+            if (key[j] > bk) { bk = key[j]; bj = j; }
+        const uint32_t m = wave_ext_u32<true>(bk);
+        int e = -1;
+        if (m != 0) {
+            const uint64_t tied = __ballot(bk == m);
+            if (__popcll(tied) == 1) {
+                const int wl = __ffsll((unsigned long long)tied) - 1;
+                e = 64 * __builtin_amdgcn_readlane(bj, wl) + wl;
+            } else {
+                e = (int)wave_ext_u32<false>(bk == m ? (uint32_t)(64 * bj + lane) : 0xFFFFFFFFu);
             }
         }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            const float ov = __shfl_xor(bv, off, kWave);
-            const int oi = __shfl_xor(bi, off, kWave);
-            const bool take = (oi != 0x7FFFFFFF) &&
-                              (bi == 0x7FFFFFFF || ov > bv || (ov == bv && oi < bi));
-            if (take) { bv = ov; bi = oi; }
-        }
-        bi = __shfl(bi, 0, kWave);
         float sbest = 0.f;
-        if (bi >= 0 && bi < E && (bi & 63) == lane) {
-            const int j = bi >> 6;
+        if (e >= 0 && (e & 63) == lane) {
+            const int j = e >> 6;
 #pragma unroll
             for (int jj = 0; jj < 16; ++jj)
-                if (jj == j) sbest = sv[jj];
-            live &= ~(1u << j);
+                if (jj == j) { sbest = sv[jj]; key[jj] = 0u; }
         }
-        sbest = __shfl(sbest, bi & 63, kWave);
+        if (e >= 0) sbest = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sbest), e & 63));
         if (lane == 0) {
-            pick[kk] = bi;
+            pick[kk] = e;
             pw[kk] = sbest;
         }
     }
