@@ -45,7 +45,7 @@ def check(got, ref, K, what, sig_ulps_allowed=2):
 @pytest.mark.parametrize("D", [64, 1000, 1001, 6144])   # 1001: unaligned rows, scalar loads
 def test_router_random(dev, orc, E, D):
     g = synth.rng(500, E, D)
-    for S in (1, 7, 64):
+    for S in (1, 7, 64, 300):            # 300: 64-token tiles, the last one ragged
         K = min(8, E)
         announce("router", E, D, S, K)
         Wr, b = synth.router_weights(g, E, D)

@@ -32,8 +32,10 @@ int coli__check_router(const float *Wr, const float *bias, const float *x,
                        const int32_t *idx, const float *w, const float *sig,
                        const void *ws, size_t ws_bytes);
 /* Router logits are summed over d in `splits` slices of `*slice` elements
- * (a multiple of 16), chosen so the fp64 matrix-core grid fills the chip;
- * the partial sums need coli__router_partial_bytes() of scratch. */
+ * (a multiple of 16), chosen so the fp64 matrix-core grid of
+ * coli__router_token_tile(S) x 64 tiles fills the chip; the partial sums
+ * need coli__router_partial_bytes() of scratch. */
+int coli__router_token_tile(int S);
 int coli__router_splits(int S, int E, int D, int *slice);
 int64_t coli__router_partial_bytes(int S, int E, int D);
 

@@ -28,73 +28,103 @@ typedef double double4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kRouterMaxE = 1024;   // the experts a wave holds: 16 per lane
 
-// Partial logits over one d-slice for a tile of 16 tokens x 64 experts
-// (4 waves, 16 experts each).  v_mfma_f64_16x16x4f64 operand layout:
+// Partial logits over one d-slice for a tile of 16 TSUB tokens x 64 experts
+// (4 waves, 16 experts each; a wave multiplies its expert fragment into
+// TSUB token sub-tiles, so larger batches re-read the router rows less).
+// v_mfma_f64_16x16x4f64 operand layout:
 //   A (16 x 4):  lane l holds A[l % 16][l / 16]
 //   B (4 x 16):  lane l holds B[l / 16][l % 16]
 //   D (16 x 16): lane l, element r holds D[4 * r + l / 16][l % 16]
 //                (the fp64 variant interleaves rows across the lane groups)
 // A = router rows (experts), B = x rows (tokens) transposed.  Each lane
-// reads 4 consecutive d of its expert row and of its token row, and feeds
-// them to 4 consecutive MFMAs, so MFMA k-slot l/16 at step j is
-// d = d0 + 4 * (l / 16) + j: every product Wr[e,d] * x[s,d] is formed once.
+// reads 4 consecutive d of its expert row and of its token rows, and feeds
+// them to 4 consecutive MFMAs per sub-tile, so MFMA k-slot l/16 at step j
+// is d = d0 + 4 * (l / 16) + j: every product Wr[e,d] * x[s,d] is formed
+// once, and each sub-tile's sum runs over d in the same order.
 // VEC: rows are 16-byte aligned and D % 4 == 0, so the 4 values are one
-// 16-byte load; the loads of 6 steps (96 d) are issued together and the
-// next 6 steps are in flight while the current ones are multiplied.
-template <bool VEC>
+// 16-byte load; the loads of kSteps 16-d steps are issued together and the
+// next ones are in flight while the current ones are multiplied.
+template <bool VEC, int TSUB>
 __global__ __launch_bounds__(256) void k_router_partial(const float *__restrict__ Wr,
                                                         const float *__restrict__ x, int S,
                                                         int E, int D, int slice,
                                                         double *__restrict__ part)
 {
-    constexpr int kSteps = 6;   // 16-d steps per chunk
+    constexpr int kSteps = TSUB == 1 ? 6 : 2;   // 16-d steps per chunk
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int t0 = blockIdx.x * 16;
+    const int t0 = blockIdx.x * 16 * TSUB;
     const int e0 = blockIdx.y * 64 + wave * 16;
     const int split = blockIdx.z;
     const int dbeg = split * slice;
     const int dend = min(D, dbeg + slice);
     const int row = lane & 15, kg = lane >> 4;
-    const int e = e0 + row, t = t0 + row;
+    const int e = e0 + row;
     const float *wp = (e < E) ? Wr + (int64_t)e * D : nullptr;
-    const float *xp = (t < S) ? x + (int64_t)t * D : nullptr;
-    double4_t acc = {0.0, 0.0, 0.0, 0.0};
-    auto load = [&](int d0, float4 (&wa)[kSteps], float4 (&xb)[kSteps]) {
+    const float *xp[TSUB];
+#pragma unroll
+    for (int u = 0; u < TSUB; ++u) {
+        const int t = t0 + 16 * u + row;
+        xp[u] = (t < S) ? x + (int64_t)t * D : nullptr;
+    }
+    double4_t acc[TSUB];
+#pragma unroll
+    for (int u = 0; u < TSUB; ++u) acc[u] = double4_t{0.0, 0.0, 0.0, 0.0};
+    auto ld4 = [&](const float *p, int d) {
+        float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (VEC) {
+            // d and dend are multiples of 4: the 4 values are all in or all out
+            if (p && d < dend) a = *reinterpret_cast<const float4 *>(p + d);
+        } else {
+            float av[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) av[j] = (p && d + j < dend) ? p[d + j] : 0.f;
+            a = make_float4(av[0], av[1], av[2], av[3]);
+        }
+        return a;
+    };
+    auto load = [&](int d0, float4 (&wa)[kSteps], float4 (&xb)[kSteps][TSUB]) {
 #pragma unroll
         for (int st = 0; st < kSteps; ++st) {
             const int d = d0 + 16 * st + 4 * kg;
-            float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-            if (VEC) {
-                // d and dend are multiples of 4: the 4 values are all in or all out
+            if constexpr (TSUB == 1 && VEC) {
+                float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
                 if (d < dend) {
                     if (wp) a = *reinterpret_cast<const float4 *>(wp + d);
-                    if (xp) b = *reinterpret_cast<const float4 *>(xp + d);
+                    if (xp[0]) b = *reinterpret_cast<const float4 *>(xp[0] + d);
                 }
-            } else {
-                float av[4], bv[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const bool in = d + j < dend;
-                    av[j] = (wp && in) ? wp[d + j] : 0.f;
-                    bv[j] = (xp && in) ? xp[d + j] : 0.f;
-                }
-                a = make_float4(av[0], av[1], av[2], av[3]);
-                b = make_float4(bv[0], bv[1], bv[2], bv[3]);
+                wa[st] = a;
+                xb[st][0] = b;
+                continue;
             }
-            wa[st] = a;
-            xb[st] = b;
+            wa[st] = ld4(wp, d);
+#pragma unroll
+            for (int u = 0; u < TSUB; ++u) xb[st][u] = ld4(xp[u], d);
         }
     };
-    auto product = [&](const float4 (&wa)[kSteps], const float4 (&xb)[kSteps]) {
+    auto product = [&](const float4 (&wa)[kSteps], const float4 (&xb)[kSteps][TSUB]) {
 #pragma unroll
         for (int st = 0; st < kSteps; ++st) {
-            acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)wa[st].x, (double)xb[st].x, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)wa[st].y, (double)xb[st].y, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)wa[st].z, (double)xb[st].z, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)wa[st].w, (double)xb[st].w, acc, 0, 0, 0);
+            if constexpr (TSUB == 1) {
+                acc[0] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)wa[st].x, (double)xb[st][0].x, acc[0], 0, 0, 0);
+                acc[0] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)wa[st].y, (double)xb[st][0].y, acc[0], 0, 0, 0);
+                acc[0] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)wa[st].z, (double)xb[st][0].z, acc[0], 0, 0, 0);
+                acc[0] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)wa[st].w, (double)xb[st][0].w, acc[0], 0, 0, 0);
+                continue;
+            }
+            const double a[4] = {(double)wa[st].x, (double)wa[st].y, (double)wa[st].z, (double)wa[st].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+#pragma unroll
+                for (int u = 0; u < TSUB; ++u) {
+                    const float4 b = xb[st][u];
+                    const float bj = j == 0 ? b.x : j == 1 ? b.y : j == 2 ? b.z : b.w;
+                    acc[u] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[j], (double)bj, acc[u], 0, 0, 0);
+                }
+            }
         }
     };
-    float4 wa0[kSteps], xb0[kSteps], wa1[kSteps], xb1[kSteps];
+    float4 wa0[kSteps], wa1[kSteps];
+    float4 xb0[kSteps][TSUB], xb1[kSteps][TSUB];
     load(dbeg, wa0, xb0);
     for (int d0 = dbeg; d0 < dend; d0 += 32 * kSteps) {
         load(d0 + 16 * kSteps, wa1, xb1);   // past dend: all zeros, no access
@@ -103,13 +133,16 @@ __global__ __launch_bounds__(256) void k_router_partial(const float *__restrict_
         load(d0 + 32 * kSteps, wa0, xb0);
         product(wa1, xb1);
     }
-    // D[i][j]: i = expert row 4*r + kg, j = token column `row`
-    const int tt = t0 + row;
-    if (tt < S) {
+    // D[i][j]: i = expert row 4*r + kg, j = token column `row` of sub-tile u
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int ee = e0 + 4 * r + kg;
-            if (ee < E) part[((int64_t)split * S + tt) * E + ee] = acc[r];
+    for (int u = 0; u < TSUB; ++u) {
+        const int tt = t0 + 16 * u + row;
+        if (tt < S) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int ee = e0 + 4 * r + kg;
+                if (ee < E) part[((int64_t)split * S + tt) * E + ee] = acc[u][r];
+            }
         }
     }
 }
@@ -287,12 +320,20 @@ hipError_t router_launch(const float *Wr, const float *bias, const float *x, int
     if (S <= 0) return hipSuccess;
     int slice = 0;
     const int splits = coli__router_splits(S, E, D, &slice);
-    dim3 grid((S + 15) / 16, (E + 63) / 64, splits);
+    const int tt = coli__router_token_tile(S);
+    dim3 grid((S + tt - 1) / tt, (E + 63) / 64, splits);
     const bool vec = D % 4 == 0 && ((uintptr_t)Wr & 15u) == 0 && ((uintptr_t)x & 15u) == 0;
-    if (vec)
-        hipLaunchKernelGGL(k_router_partial<true>, grid, dim3(256), 0, st, Wr, x, S, E, D, slice, part);
-    else
-        hipLaunchKernelGGL(k_router_partial<false>, grid, dim3(256), 0, st, Wr, x, S, E, D, slice, part);
+    if (tt == 64) {
+        if (vec)
+            hipLaunchKernelGGL((k_router_partial<true, 4>), grid, dim3(256), 0, st, Wr, x, S, E, D, slice, part);
+        else
+            hipLaunchKernelGGL((k_router_partial<false, 4>), grid, dim3(256), 0, st, Wr, x, S, E, D, slice, part);
+    } else {
+        if (vec)
+            hipLaunchKernelGGL((k_router_partial<true, 1>), grid, dim3(256), 0, st, Wr, x, S, E, D, slice, part);
+        else
+            hipLaunchKernelGGL((k_router_partial<false, 1>), grid, dim3(256), 0, st, Wr, x, S, E, D, slice, part);
+    }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     if (E > kRouterMaxE) return hipErrorInvalidValue;

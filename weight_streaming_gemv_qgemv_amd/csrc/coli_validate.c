@@ -100,9 +100,15 @@ int coli__check_router(const float *Wr, const float *bias, const float *x,
 
 static int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
+int coli__router_token_tile(int S)
+{
+    return S >= 256 ? 64 : 16;   /* 64: each router row fragment feeds 4 token tiles */
+}
+
 int coli__router_splits(int S, int E, int D, int *slice)
 {
-    int64_t tiles = (int64_t)((S + 15) / 16) * ((E + 63) / 64);
+    const int tt = coli__router_token_tile(S);
+    int64_t tiles = (int64_t)((S + tt - 1) / tt) * ((E + 63) / 64);
     int64_t want = tiles > 0 ? (512 + tiles - 1) / tiles : 1;
     int64_t maxs = D / 64 > 0 ? D / 64 : 1;
     if (want > maxs) want = maxs;
