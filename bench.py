@@ -209,6 +209,19 @@ def run_layer64(args, dev, tail=False):
     return res
 
 
+def per_expert_roofline_s(rows_per_expert, expert_bytes_total, D, F):
+    """The prefill layer's bound: every expert (the shared one last) streams
+    its weights once and multiplies them into its rows, so it takes at least
+    max(bytes / HBM peak, flops / bf16 matrix peak); the layer at least the
+    sum over experts (the router and the activations are left out)."""
+    t = 0.0
+    for r in rows_per_expert:
+        if r <= 0:
+            continue
+        t += max(expert_bytes_total / (HBM_PEAK_GBS * 1e9), 2.0 * r * 3 * D * F / (BF16_PEAK_TFLOPS * 1e12))
+    return t
+
+
 def run_prefill2048(args, dev):
     """2048 tokens through the layer in bf16 precision: the router runs and
     is timed (coli_router), the experts take a fixed Zipf(1.1)-skewed
@@ -240,11 +253,12 @@ def run_prefill2048(args, dev):
     step_bytes = (E * D * 4 + E * 4) + S * D * 4 + uniq * (gu + dn) + (gu + dn) + S * D * 4 + S * K * 8
     rows = S * K + S
     flops = 2 * rows * 3 * D * F            # gate, up, down on every routed and shared row
+    t_star = per_expert_roofline_s(np.bincount(idx.ravel(), minlength=E).tolist() + [S], gu + dn, D, F)
     ms, wall, stages = time_steps(step, args.steps, args.warmup)
     gu_ms, gu_n = stages["gate_up"]
     gu_flops = 2 * rows * 2 * D * F
     return dict(workload="moe_layer_prefill_2048_bf16", ms=ms, wall=wall, step_bytes=step_bytes,
-                tokens=S, stages=stages, uniq=uniq, flops=flops,
+                tokens=S, stages=stages, uniq=uniq, flops=flops, t_star=t_star,
                 dominant=dict(kernel="k_pre<I4,2> (grouped expert gate/up + SwiGLU, bf16 matrix cores)",
                               traffic=recorded_traffic("moe_layer_prefill_2048_bf16", "k_pre<2, 2>"),
                               bytes_per_launch=(uniq + 1) * gu + S * D * 4 + rows * F * 4,
@@ -325,6 +339,8 @@ def run_ep_slice(args, dev, prefill):
     if prefill:
         res["flops"] = 2 * rows * 3 * D * F
         res["dominant"]["flops_per_launch"] = 2 * rows * 2 * D * F
+        res["t_star"] = per_expert_roofline_s(np.bincount(idl[idl >= 0].ravel(), minlength=El).tolist() + [S],
+                                              gu + dn, D, F)
     return res
 
 
@@ -526,6 +542,9 @@ def main():
                             "kernel": dom["kernel"], "flops_per_launch": dom["flops_per_launch"],
                             "ms_per_launch": round(dom["ms_per_launch"], 5)}
         line["layer_mfma_utilisation"] = round(r["flops"] / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
+        if "t_star" in r:
+            line["per_expert_roofline"] = {"t_star_ms": round(r["t_star"] * 1e3, 5),
+                                           "frac_of_step": round(r["t_star"] * 1e3 / ms, 4)}
     if "cpu" in r:
         c = r["cpu"]
         line["cpu_baseline"] = {"value": round(c["value"], 4), "unit": c["unit"], "cores": c["cores"],
