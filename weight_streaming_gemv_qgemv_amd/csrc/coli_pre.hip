@@ -144,8 +144,9 @@ __global__ __launch_bounds__(64 * kPreWaves) void k_pre(PreArgs a)
     const int col = lane & 15, q = lane >> 4;
     const int xcd = blockIdx.x % kPreXcds, lb = blockIdx.x / kPreXcds;
     const int bpx = gridDim.x / kPreXcds;               // grid is a multiple of 8
-    // XCD x: all tiles of a contiguous run of group-passes (the passes of
-    // one group -- and their weights -- together)
+    // XCD x: a contiguous run of group-passes, tile-major: the blocks of an
+    // XCD work on one weight tile for consecutive passes at a time, so the
+    // passes of a large group read that tile together from the XCD's L2
     const int n_gp = cload(a.n_work);
     const int gp_lo = (int)((int64_t)n_gp * xcd / kPreXcds);
     const int gp_cnt = (int)((int64_t)n_gp * (xcd + 1) / kPreXcds) - gp_lo;
@@ -166,8 +167,8 @@ __global__ __launch_bounds__(64 * kPreWaves) void k_pre(PreArgs a)
         uint32_t roff[MT];
     };
     auto make = [&](It &c, int it) {
-        c.gp = __builtin_amdgcn_readfirstlane(gp_lo + it / a.tiles);
-        c.tile = __builtin_amdgcn_readfirstlane(it % a.tiles);
+        c.gp = __builtin_amdgcn_readfirstlane(gp_lo + it % gp_cnt);
+        c.tile = __builtin_amdgcn_readfirstlane(it / gp_cnt);
         const int wv = cload(a.work + c.gp);
         const int g = wv & 0x7FF, pass = wv >> 11;
         const bool extra = a.has_extra && g == a.ngroups;
