@@ -114,6 +114,32 @@ def test_dense_sweep_12288x6144(dev, orc, fmt):
         assert_within(got, ref, mag, REL, what=f"fmt{fmt} S{S}")
 
 
+@pytest.mark.parametrize("fmt", [1, 2, 3])
+def test_many_rows_ragged(dev, orc, fmt):
+    """Over 8192 rows with a ragged last 16-row tile (O = 8209), ragged I,
+    one and two activation rows; every output written, sampled rows (the
+    first and last 40 included) checked against the oracle."""
+    import torch
+    from weight_streaming_gemv_qgemv_amd import binding as b
+    g = synth.rng(2500, fmt)
+    O = 8209
+    for I in (1024, 3000, 6144):
+        W = synth.weight_bytes(g, fmt, O, I)
+        sc = synth.scales(g, O)
+        Wd, scd = to_dev(W, dev), to_dev(sc, dev)
+        rows = np.unique(np.concatenate([g.choice(O, 400, replace=False), np.arange(O - 40, O), np.arange(40)]))
+        for S in (1, 2):
+            announce("qgemv many rows", fmt, O, I, S)
+            x = synth.activations(g, S, I)
+            y = torch.full((S, O), float("nan"), dtype=torch.float32, device=dev)
+            b.qgemv(fmt, Wd, scd, to_dev(x, dev), y)
+            torch.cuda.synchronize()
+            got = y.cpu().numpy()
+            assert np.isfinite(got).all(), "rows left unwritten"
+            ref, mag = orc.qgemv(fmt, W[rows], sc[rows], x)
+            assert_within(got[:, rows], ref, mag, REL, what=f"fmt{fmt} I{I} S{S}")
+
+
 def test_edges_empty_and_zero_width(dev):
     import torch
     from weight_streaming_gemv_qgemv_amd import binding as b
