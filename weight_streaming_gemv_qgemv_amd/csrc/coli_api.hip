@@ -172,19 +172,34 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(const float *__rest
     const int s = blockIdx.x;
     const int32_t *pr = pair_row + (int64_t)s * K;
     const float *ws = w + (int64_t)s * K;
+    // slots in runs of kCombineRun: the run's rows are all requested before
+    // the first is added, the additions stay in slot order
+    constexpr int kCombineRun = 8;
     if (vec4) {
         const int d = (blockIdx.y * kCombineThreads + threadIdx.x) * 4;
         if (d >= D) return;
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int kk = 0; kk < K; ++kk) {
-            const int r = pr[kk];
-            if (r < 0) continue;
-            const float wk = ws[kk];
-            const float4 v = *reinterpret_cast<const float4 *>(y + (int64_t)r * D + d);
-            acc.x = fmaf(wk, v.x, acc.x);
-            acc.y = fmaf(wk, v.y, acc.y);
-            acc.z = fmaf(wk, v.z, acc.z);
-            acc.w = fmaf(wk, v.w, acc.w);
+        for (int k0 = 0; k0 < K; k0 += kCombineRun) {
+            int r[kCombineRun];
+            float wk[kCombineRun];
+            float4 v[kCombineRun];
+#pragma unroll
+            for (int j = 0; j < kCombineRun; ++j) {
+                r[j] = k0 + j < K ? pr[k0 + j] : -1;
+                wk[j] = k0 + j < K ? ws[k0 + j] : 0.f;
+            }
+#pragma unroll
+            for (int j = 0; j < kCombineRun; ++j)
+                v[j] = r[j] >= 0 ? *reinterpret_cast<const float4 *>(y + (int64_t)r[j] * D + d)
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int j = 0; j < kCombineRun; ++j) {
+                if (r[j] < 0) continue;
+                acc.x = fmaf(wk[j], v[j].x, acc.x);
+                acc.y = fmaf(wk[j], v[j].y, acc.y);
+                acc.z = fmaf(wk[j], v[j].z, acc.z);
+                acc.w = fmaf(wk[j], v[j].w, acc.w);
+            }
         }
         if (has_shared) {
             const float4 v = *reinterpret_cast<const float4 *>(y + (shared_row0 + s) * (int64_t)D + d);
@@ -205,10 +220,16 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(const float *__rest
         const int d = blockIdx.y * kCombineThreads + threadIdx.x;
         if (d >= D) return;
         float acc = 0.f;
-        for (int kk = 0; kk < K; ++kk) {
-            const int r = pr[kk];
-            if (r < 0) continue;
-            acc = fmaf(ws[kk], y[(int64_t)r * D + d], acc);
+        for (int k0 = 0; k0 < K; k0 += kCombineRun) {
+            int r[kCombineRun];
+            float v[kCombineRun];
+#pragma unroll
+            for (int j = 0; j < kCombineRun; ++j) r[j] = k0 + j < K ? pr[k0 + j] : -1;
+#pragma unroll
+            for (int j = 0; j < kCombineRun; ++j) v[j] = r[j] >= 0 ? y[(int64_t)r[j] * D + d] : 0.f;
+#pragma unroll
+            for (int j = 0; j < kCombineRun; ++j)
+                if (r[j] >= 0) acc = fmaf(ws[k0 + j], v[j], acc);
         }
         if (has_shared) acc += y[(shared_row0 + s) * (int64_t)D + d];
         if (resid) acc = resid[(int64_t)s * D + d] + acc;
