@@ -235,11 +235,16 @@ size_t coli_moe_workspace_bytes(int S, int K, int E, int D, int F,
  *              row KpF/32 partial sums of the stored h (KpF = F rounded up to
  *              1024), then their totals.
  *   xn         [S, D] fp32: the RMSNorm rows coli_moe_layer_tail feeds the
- *              block. */
+ *              block.
+ *   gpart      grouping of more than 1024 slots (S K > 1024): per chunk of
+ *              1024 slots E int32 counts, turned into the chunk's first
+ *              position per expert, then one flags word per chunk. */
 typedef struct {
     int64_t flags, sig, idx, w, offsets, counts, row_pair, pair_row, h, y, router_part;
     int64_t xf, xsum, hf, hsum, work, n_work;
     int64_t xn;                    /* coli_moe_layer_tail: [S, D] fp32 RMSNorm rows */
+    int64_t gpart;                 /* grouping of more than 1024 slots: per 1024-slot
+                                      chunk, E counts / first positions and a flags word */
     int64_t n_pass_max;            /* passes the scratch is sized for */
     int64_t xf_stride, hf_stride;  /* bf16 elements per row */
     int64_t h_ld;   /* row stride of h in floats (max of F and F_shared) */

@@ -194,6 +194,37 @@ def test_moe_gemv_skipped_and_bad_slots(dev, orc):
     assert_within(out, ref["out"], ref["mag"], REL, what="dup")
 
 
+def test_moe_gemv_chunked_grouping(dev, orc):
+    """More than 1024 slots take the chunked grouping: 400 tokens x 3 slots
+    (two chunks; token 341's slots 1023-1025 straddle the boundary), skewed
+    routing, empty slots; then a bad id and a duplicate across the boundary
+    are skipped / computed twice and flagged."""
+    from weight_streaming_gemv_qgemv_amd import binding as b
+    E, D, F, S, K = 40, 256, 128, 400, 3
+    bank = synth.expert_bank(32, 2, E, D, F)
+    g = synth.rng(33)
+    x = synth.activations(g, S, D)
+    idx, w = synth.routing_zipf(g, S, K, E)
+    idx[5, 1] = -1
+    idx[350, 2] = -1
+    announce("moe chunked grouping")
+    out, ws = run_gemv(dev, dev_bank(bank, dev), x, idx, w)
+    lay = b.moe_workspace_layout(S, K, E, D, F)
+    check_moe(orc, bank, None, x, idx, w, out, ws, lay, "chunked")
+    assert b.check_device_flags(ws) == (b.OK, 0)
+    bad = idx.copy()
+    bad[10, 0] = E + 1
+    bad[341, 1] = bad[341, 0]      # slot 1024 repeats slot 1023
+    announce("moe chunked grouping, bad and duplicate ids")
+    out, ws = run_gemv(dev, dev_bank(bank, dev), x, bad, w)
+    rc, flags = b.check_device_flags(ws)
+    assert rc == b.EIDX and flags & 1 and flags & 2
+    masked = bad.copy()
+    masked[(masked < 0) | (masked >= E)] = -1
+    ref = orc.moe(bank, None, x, masked, w.astype(np.float64))
+    assert_within(out, ref["out"], ref["mag"], REL, what="chunked bad/dup")
+
+
 def test_moe_layer_small_with_router_and_shared(dev, orc):
     import torch
     from weight_streaming_gemv_qgemv_amd import binding as b

@@ -46,7 +46,7 @@ class RouterParams(C.Structure):
 class WsLayout(C.Structure):
     _fields_ = [(n, C.c_int64) for n in ("flags", "sig", "idx", "w", "offsets", "counts",
                                           "row_pair", "pair_row", "h", "y", "router_part",
-                                          "xf", "xsum", "hf", "hsum", "work", "n_work", "xn",
+                                          "xf", "xsum", "hf", "hsum", "work", "n_work", "xn", "gpart",
                                           "n_pass_max", "xf_stride", "hf_stride", "h_ld", "total")]
 
 

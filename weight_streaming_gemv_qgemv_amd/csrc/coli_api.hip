@@ -156,6 +156,145 @@ __global__ __launch_bounds__(1024) void k_group_scatter(const int32_t *__restric
     }
 }
 
+// Chunked grouping for large batches (P > COLI_GROUP_CHUNK slots): the same
+// outputs as k_group_count + k_group_scatter, with the slots cut into chunks
+// so that a wave scans one expert over one chunk only.
+//   k_group_hist:  block (expert group, chunk) -> hist[c][e] = the chunk's
+//                  slots of expert e; block (0, c) validates the chunk
+//                  (flags word C E + c);
+//   k_group_prefix: one block: counts, offsets (exclusive prefix over e),
+//                  the work list and n_work, the flags, and hist[c][e]
+//                  turned into the chunk's first position for expert e
+//                  (offsets[e] + the earlier chunks' counts);
+//   k_group_place: block (expert group, chunk): the stable scatter of the
+//                  chunk's slots from those first positions.
+constexpr int kChunk = COLI_GROUP_CHUNK;
+
+__global__ __launch_bounds__(1024) void k_group_hist(const int32_t *__restrict__ idx, int P, int K,
+                                                     int E, int32_t *__restrict__ gpart)
+{
+    __shared__ int32_t sidx[kChunk];
+    __shared__ uint32_t sflag;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int e = blockIdx.x * kGroupWaves + wave, c = blockIdx.y, C = gridDim.y;
+    const int base = c * kChunk, n = min(kChunk, P - base);
+    if (threadIdx.x == 0) sflag = 0u;
+    for (int i = threadIdx.x; i < n; i += blockDim.x) sidx[i] = idx[base + i];
+    __syncthreads();
+    if (e < E) {
+        int count = 0;
+        for (int k = 0; k < n; k += 64) {
+            const int i = k + lane;
+            count += __popcll(__ballot(i < n && sidx[i] == e));
+        }
+        if (lane == 0) gpart[(int64_t)c * E + e] = count;
+    }
+    if (blockIdx.x == 0) {
+        uint32_t f = 0u;
+        for (int i = threadIdx.x; i < n; i += blockDim.x) {
+            const int p = base + i, v = sidx[i];
+            if (v < -1 || v >= E) f |= kFlagBadId;
+            if (v >= 0) {
+                const int s0 = (p / K) * K;
+                for (int q = s0; q < p; ++q)
+                    if (idx[q] == v) { f |= kFlagDup; break; }
+            }
+        }
+        if (f) atomicOr(&sflag, f);
+        __syncthreads();
+        if (threadIdx.x == 0) gpart[(int64_t)C * E + c] = (int32_t)sflag;
+    }
+}
+
+__global__ __launch_bounds__(1024) void k_group_prefix(int E, int C, int32_t *__restrict__ gpart,
+                                                       int32_t *__restrict__ counts,
+                                                       int32_t *__restrict__ offsets, int extra_rows,
+                                                       int tpp, int32_t *__restrict__ work,
+                                                       int32_t *__restrict__ n_work,
+                                                       uint32_t *__restrict__ flags)
+{
+    __shared__ int32_t tot[1024];
+    __shared__ int32_t wsum[16][2];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    int ce = 0;
+    if (t < E)
+        for (int c = 0; c < C; ++c) ce += gpart[(int64_t)c * E + t];
+    tot[t] = ce;
+    // exclusive prefix over experts of the counts and of the passes
+    int v = ce, pv = t < E ? (ce + tpp - 1) / tpp : 0;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int a = __shfl_up(v, o, kWave), b = __shfl_up(pv, o, kWave);
+        if (lane >= o) { v += a; pv += b; }
+    }
+    if (lane == 63) { wsum[wave][0] = v; wsum[wave][1] = pv; }
+    __syncthreads();
+    int wo = 0, wpo = 0;
+    for (int ww = 0; ww < wave; ++ww) { wo += wsum[ww][0]; wpo += wsum[ww][1]; }
+    const int off = wo + v - ce;                                  // exclusive
+    const int np = t < E ? (ce + tpp - 1) / tpp : 0;
+    const int ppart = wpo + pv - np;
+    if (t < E) {
+        counts[t] = ce;
+        offsets[t] = off;
+        if (t == E - 1) offsets[E] = off + ce;
+        if (work) {
+            for (int p = 0; p < np; ++p) work[ppart + p] = t | (p << 11);
+            if (t == E - 1) {
+                const int nx = (extra_rows + tpp - 1) / tpp;
+                for (int p = 0; p < nx; ++p) work[ppart + np + p] = E | (p << 11);
+                *n_work = ppart + np + nx;
+            }
+        }
+        // the chunks' first positions for expert t
+        int run = off;
+        for (int c = 0; c < C; ++c) {
+            const int h = gpart[(int64_t)c * E + t];
+            gpart[(int64_t)c * E + t] = run;
+            run += h;
+        }
+    }
+    if (t == 0) {
+        uint32_t f = 0u;
+        for (int c = 0; c < C; ++c) f |= (uint32_t)gpart[(int64_t)C * E + c];
+        flags[0] = f;
+    }
+}
+
+__global__ __launch_bounds__(1024) void k_group_place(const int32_t *__restrict__ idx, int P, int E,
+                                                      const int32_t *__restrict__ gpart,
+                                                      int32_t *__restrict__ row_pair,
+                                                      int32_t *__restrict__ pair_row)
+{
+    __shared__ int32_t sidx[kChunk];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int e = blockIdx.x * kGroupWaves + wave, c = blockIdx.y;
+    const int base = c * kChunk, n = min(kChunk, P - base);
+    for (int i = threadIdx.x; i < n; i += blockDim.x) sidx[i] = idx[base + i];
+    __syncthreads();
+    if (e < E) {
+        int pos0 = gpart[(int64_t)c * E + e];
+        for (int k = 0; k < n; k += 64) {
+            const int i = k + lane;
+            const bool hit = i < n && sidx[i] == e;
+            const uint64_t m = __ballot(hit);
+            if (hit) {
+                const uint64_t below = lane ? (m & ((~0ull) >> (64 - lane))) : 0ull;
+                const int pos = pos0 + __popcll(below);
+                row_pair[pos] = base + i;
+                pair_row[base + i] = pos;
+            }
+            pos0 += __popcll(m);
+        }
+    }
+    if (blockIdx.x == 0) {
+        for (int i = threadIdx.x; i < n; i += blockDim.x) {
+            const int v = sidx[i];
+            if (v < 0 || v >= E) pair_row[base + i] = -1;
+        }
+    }
+}
+
 // out[s, :] = sum_{kk: slot kept} w[s,kk] * y[row(s,kk), :]  (+ y[shared row]),
 // slots in order kk = 0..K-1, then the shared expert: a fixed order; with a
 // residual, out[s, :] = resid[s, :] + that sum (resid may be out itself: each
@@ -381,13 +520,27 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
     int32_t *n_work = reinterpret_cast<int32_t *>(ws + L.n_work);
     {
     StageTimer tg(kStGroup, st);
-    hipLaunchKernelGGL(k_group_count, dim3(gblocks), dim3(1024), 0, st, idx, P, K, E, counts,
-                       flags);
-    err = hipGetLastError();
-    if (err != hipSuccess) return COLI_EDEVICE;
-    hipLaunchKernelGGL(k_group_scatter, dim3(gblocks), dim3(1024), 0, st, idx, P, E, counts,
-                       offsets, row_pair, pair_row, sh_mm ? S : 0, tpp,
-                       mm ? work : nullptr, n_work);
+    if (P > kChunk) {
+        const int C = (P + kChunk - 1) / kChunk;
+        int32_t *gpart = reinterpret_cast<int32_t *>(ws + L.gpart);
+        hipLaunchKernelGGL(k_group_hist, dim3(gblocks, C), dim3(1024), 0, st, idx, P, K, E, gpart);
+        err = hipGetLastError();
+        if (err != hipSuccess) return COLI_EDEVICE;
+        hipLaunchKernelGGL(k_group_prefix, dim3(1), dim3(1024), 0, st, E, C, gpart, counts, offsets,
+                           sh_mm ? S : 0, tpp, mm ? work : nullptr, n_work, flags);
+        err = hipGetLastError();
+        if (err != hipSuccess) return COLI_EDEVICE;
+        hipLaunchKernelGGL(k_group_place, dim3(gblocks, C), dim3(1024), 0, st, idx, P, E, gpart,
+                           row_pair, pair_row);
+    } else {
+        hipLaunchKernelGGL(k_group_count, dim3(gblocks), dim3(1024), 0, st, idx, P, K, E, counts,
+                           flags);
+        err = hipGetLastError();
+        if (err != hipSuccess) return COLI_EDEVICE;
+        hipLaunchKernelGGL(k_group_scatter, dim3(gblocks), dim3(1024), 0, st, idx, P, E, counts,
+                           offsets, row_pair, pair_row, sh_mm ? S : 0, tpp,
+                           mm ? work : nullptr, n_work);
+    }
     err = hipGetLastError();
     if (err != hipSuccess) return COLI_EDEVICE;
     }

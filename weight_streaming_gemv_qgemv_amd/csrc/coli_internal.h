@@ -10,6 +10,8 @@
 #include "coli.h"
 
 #define COLI_MAX_E 1024 /* 16 scores per lane of a 64-wide wave */
+/* slots per chunk of the chunked grouping (batches of more than one chunk) */
+#define COLI_GROUP_CHUNK 1024
 #define COLI_MAX_K 64
 /* rows per pass of the matrix-core expert kernels: in fp32 precision 8, as
  * bf16 hi/lo column pairs of one 16-column MFMA tile; in bf16 precision 64,

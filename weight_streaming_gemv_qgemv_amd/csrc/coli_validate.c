@@ -198,6 +198,13 @@ int coli_moe_workspace_layout(int S, int K, int E, int D, int F, int F_shared,
     REGION(n_work, 64);
     if (!mul_ok((int64_t)S, D, &t) || !mul_ok(t, 4, &t)) return COLI_ESHAPE;
     REGION(xn, t);
+    /* chunked grouping: per chunk of COLI_GROUP_CHUNK slots, E counts (then
+     * the chunk's first position per expert) and a flags word */
+    {
+        const int64_t C = (P + COLI_GROUP_CHUNK - 1) / COLI_GROUP_CHUNK;
+        if (!mul_ok(C, (int64_t)E + 1, &t) || !mul_ok(t, 4, &t)) return COLI_ESHAPE;
+        REGION(gpart, t);
+    }
 #undef REGION
     out->n_pass_max = ngp;
     out->xf_stride = bf16 ? KpD : 2 * KpD;
