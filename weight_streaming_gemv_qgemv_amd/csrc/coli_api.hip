@@ -213,13 +213,18 @@ __global__ __launch_bounds__(1024) void k_group_prefix(int E, int C, int32_t *__
                                                        int32_t *__restrict__ n_work,
                                                        uint32_t *__restrict__ flags)
 {
-    __shared__ int32_t tot[1024];
+    // the per-chunk counts are read once, coalesced, into LDS when they fit
+    // (C E <= 8192), so the per-expert loops below run on LDS
+    __shared__ int32_t hs[8192];
     __shared__ int32_t wsum[16][2];
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const bool in_lds = (int64_t)C * E <= 8192;
+    if (in_lds)
+        for (int i = t; i < C * E; i += 1024) hs[i] = gpart[i];
+    __syncthreads();
     int ce = 0;
     if (t < E)
-        for (int c = 0; c < C; ++c) ce += gpart[(int64_t)c * E + t];
-    tot[t] = ce;
+        for (int c = 0; c < C; ++c) ce += in_lds ? hs[c * E + t] : gpart[(int64_t)c * E + t];
     // exclusive prefix over experts of the counts and of the passes
     int v = ce, pv = t < E ? (ce + tpp - 1) / tpp : 0;
 #pragma unroll
@@ -249,7 +254,7 @@ __global__ __launch_bounds__(1024) void k_group_prefix(int E, int C, int32_t *__
         // the chunks' first positions for expert t
         int run = off;
         for (int c = 0; c < C; ++c) {
-            const int h = gpart[(int64_t)c * E + t];
+            const int h = in_lds ? hs[c * E + t] : gpart[(int64_t)c * E + t];
             gpart[(int64_t)c * E + t] = run;
             run += h;
         }
