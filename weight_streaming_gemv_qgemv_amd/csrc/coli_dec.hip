@@ -15,14 +15,14 @@
 //     lo| <= 2^-16 |x|); the second tile's products are skipped when the
 //     pass has 8 rows or fewer;
 //   * activations come from "row tables" (coli_dec.h): one row per
-//     activation row, in fragment order.  Per k-block the 4 waves of a block
+//     activation row, in fragment order.  Per k-block the waves of a block
 //     copy the pass's units into LDS by DMA (each unit once per block), one
 //     k-block ahead of the products, with one barrier per k-block;
 //   * sum(x) per column, needed to remove OFF * sum(x) from the code
 //     products, is one more MFMA per step against a tile of ones, over the
 //     very bf16 values the products use;
-//   * an item is (group-pass, 128-row tile) for gate/up (32 rows per wave),
-//     (group-pass, 256-row tile) for down (64 rows per wave); the items
+//   * an item is (group-pass, 128-row tile) for gate/up (4 waves of 32
+//     rows), (group-pass, 128-row tile) for down (2 waves of 64 rows); the items
 //     are shared out to the XCDs so that the passes of one group run on the
 //     same XCD at about the same time (later passes find the weights in its
 //     L2), persistent blocks walk them in order, and each wave loads the
@@ -36,10 +36,11 @@ namespace coli {
 
 namespace {
 
-constexpr int kDecWaves = 4;
 constexpr int kDecXcds = 8;
 constexpr int kDecNT = kDecTpp / 8;   // MFMA N-tiles per pass (8 rows: hi/lo column pairs)
-template <int M> struct DecTiles { static constexpr int MT = M == 2 ? 2 : 4; };
+// per product: 16-row tiles per wave, waves per block (gate/up 4 x 32 rows,
+// down 2 x 64 rows: measured fastest for each on the 64- and 16-token layers)
+template <int M> struct DecTiles { static constexpr int MT = M == 2 ? 2 : 4, W = M == 2 ? 4 : 2; };
 
 // ---------------------------------------------------------------- row tables
 // Block (row, part): runs of RUN consecutive elements (8: one chunk; int2
@@ -120,7 +121,7 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
 {
     using T = MF<FMT>;
     constexpr int STEPS = T::STEPS, KB = T::KB, SEGS = T::SEGS, BITS = T::BITS, SPS = T::SPS;
-    constexpr int MT = DecTiles<M>::MT, RPW = 16 * MT, RPB = kDecWaves * RPW;
+    constexpr int MT = DecTiles<M>::MT, kDecWaves = DecTiles<M>::W, RPW = 16 * MT, RPB = kDecWaves * RPW;
     constexpr int NT = kDecNT;
     constexpr float OFF = T::OFF;
     constexpr uint32_t kChunkStep = 4 * 32;   // bytes between one step's chunks and the next's
@@ -448,7 +449,7 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
     __builtin_amdgcn_s_waitcnt(0);
 }
 
-int dec_resident_blocks(const void *kern, int *cache)
+int dec_resident_blocks(const void *kern, int threads, int *cache)
 {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
@@ -456,7 +457,7 @@ int dec_resident_blocks(const void *kern, int *cache)
     int cus = 0, per = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kern, 256, 0) != hipSuccess || per <= 0)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kern, threads, 0) != hipSuccess || per <= 0)
         per = 1;
     cache[dev] = cus * per;
     return cache[dev];
@@ -467,18 +468,22 @@ hipError_t launch_dec(const DecArgs &a, int64_t items, hipStream_t st)
 {
     static int cache[64] = {0};
     const void *kern = (const void *)k_dec<FMT, M>;
-    int64_t cap = dec_resident_blocks(kern, cache) / kDecXcds * kDecXcds;
+    constexpr int threads = 64 * DecTiles<M>::W;
+    int64_t cap = dec_resident_blocks(kern, threads, cache) / kDecXcds * kDecXcds;
     if (cap < kDecXcds) cap = kDecXcds;
     int64_t grid = (items + kDecXcds - 1) / kDecXcds * kDecXcds;
     if (grid > cap) grid = cap;
     if (grid < kDecXcds) grid = kDecXcds;
-    hipLaunchKernelGGL((k_dec<FMT, M>), dim3((unsigned)grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_dec<FMT, M>), dim3((unsigned)grid), dim3(threads), 0, st, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-int dec_rows_per_block(int M) { return kDecWaves * 16 * (M == 2 ? DecTiles<2>::MT : DecTiles<1>::MT); }
+int dec_rows_per_block(int M)
+{
+    return M == 2 ? DecTiles<2>::W * 16 * DecTiles<2>::MT : DecTiles<1>::W * 16 * DecTiles<1>::MT;
+}
 
 hipError_t xrows_launch(int fmt, const float *x, int64_t ldx, int rows, int I, int kpad,
                         uint16_t *table, hipStream_t st)
