@@ -7,7 +7,8 @@
  *   - Every array argument is a DEVICE pointer (memory the caller allocated
  *     on the current HIP device, e.g. a torch tensor's data_ptr()), unless the
  *     argument says "host".  The library never allocates, frees or keeps any
- *     caller memory and holds no state between calls.
+ *     caller memory and holds no state between calls, apart from the
+ *     optional stage timer (coli_stage_timing).
  *   - Arrays are dense, row-major (C-contiguous).  A packed weight matrix
  *     [O, I] is stored as O rows of coli_row_bytes(fmt, I) bytes each.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
@@ -18,6 +19,15 @@
  *     checks run on the host before anything is enqueued; on an error nothing
  *     is launched and no output is touched.  The library never aborts or exits.
  *   - Sizes of 0 are allowed where stated (an empty batch enqueues nothing).
+ *
+ * Typical use (one MoE layer per call, decode or prefill):
+ *   size_t nb = coli_moe_workspace_bytes(S, K, E, D, F, F_shared, prec);
+ *   (allocate nb device bytes, 256-byte aligned, once per shape)
+ *   coli_moe_layer(&router, &experts, &shared, x, S, NULL, NULL, out,
+ *                  idx_out, w_out, prec, ws, nb, stream);
+ *   coli_check_device_flags(ws, stream, NULL);   (optional: bad routing ids)
+ * and for a single quantized matrix: coli_qgemv(fmt, W, scale, x, y, S, I, O,
+ * stream), which needs no workspace.
  *
  * Sources (page title -- section):
  *   glm.c@98759bf  colibri-strix c/glm.c, commit 98759bf
