@@ -137,6 +137,36 @@ def cpu_baseline_layer(bank, shared, Wr, bias, x, K, ntok):
     return dt, r["idx"]
 
 
+def host_info():
+    """Logical CPUs this process may use and the CPU model string."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return n, model
+
+
+def single_thread(fn):
+    """Run fn() with the oracle on one host thread; returns (seconds, result)."""
+    from oracle import oracle
+    prev = oracle.set_threads(1)
+    try:
+        t0 = time.perf_counter()
+        out = fn()
+        return time.perf_counter() - t0, out
+    finally:
+        oracle.set_threads(prev)
+
+
 def run_tail64(args, dev):
     """The 64-token decode layer as a layer tail: RMSNorm of the residual
     stream, the MoE block on the normalised rows, residual add
@@ -206,6 +236,15 @@ def run_layer64(args, dev, tail=False):
                           sample=f"router + MoE layer on the first {ntok} of the 64 tokens "
                                  f"({su} unique experts), {dt:.2f} s",
                           tokens_per_s=ntok / dt, seconds=dt)
+        n1 = min(args.cpu_tokens_1t, ntok)
+        if n1 > 0:
+            log(f"cpu baseline: oracle on {n1} tokens, one thread")
+            dt1, (_, idx1) = single_thread(lambda: cpu_baseline_layer(bank, shared, Wr, bias, x, K, n1))
+            u1 = int(np.unique(idx1).size)
+            sb1 = (E * D * 4 + E * 4) + n1 * D * 4 + u1 * (gu + dn) + (gu + dn) + n1 * D * 4
+            res["cpu"]["single_thread"] = dict(
+                value=sb1 / dt1 / 1e9, tokens_per_s=n1 / dt1, seconds=dt1,
+                sample=f"router + MoE layer on the first {n1} tokens ({u1} unique experts)")
     return res
 
 
@@ -374,15 +413,23 @@ def run_decode16(args, dev):
                              ms_per_launch=gu_ms / max(gu_n, 1), launches=gu_n))
     if not args.no_cpu_baseline:
         from oracle import oracle
-        n = args.cpu_tokens
+        n = min(args.cpu_tokens, S)
+        run = lambda m: oracle.moe(bank, None, x[:m], idx[:m], w[:m].astype(np.float64))
         t0 = time.perf_counter()
-        oracle.moe(bank, None, x[:n], idx[:n], w[:n].astype(np.float64))
+        run(n)
         dt = time.perf_counter() - t0
         su = int(np.unique(idx[:n]).size)
         res["cpu"] = dict(value=(n * D * 8 + su * (gu + dn)) / dt / 1e9, unit="GB/s",
                           cores=oracle.num_threads(), kind="oracle",
-                          sample=f"routed experts for the first {n} of 16 tokens ({su} unique "
+                          sample=f"routed experts for the first {n} of {S} tokens ({su} unique "
                                  f"experts), {dt:.2f} s", tokens_per_s=n / dt, seconds=dt)
+        n1 = min(args.cpu_tokens_1t, n)
+        if n1 > 0:
+            dt1, _ = single_thread(lambda: run(n1))
+            u1 = int(np.unique(idx[:n1]).size)
+            res["cpu"]["single_thread"] = dict(
+                value=(n1 * D * 8 + u1 * (gu + dn)) / dt1 / 1e9, tokens_per_s=n1 / dt1,
+                seconds=dt1, sample=f"routed experts for the first {n1} tokens ({u1} unique experts)")
     return res
 
 
@@ -472,6 +519,8 @@ def main():
                          "over N GPUs (256/N local experts; the slice with the most routed rows, "
                          "with the shared expert)")
     ap.add_argument("--cpu-tokens", type=int, default=64)
+    ap.add_argument("--cpu-tokens-1t", type=int, default=8,
+                    help="tokens of the one-thread oracle timing (0 skips it)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build measures the per-GPU share of the "
@@ -547,9 +596,17 @@ def main():
                                            "frac_of_step": round(r["t_star"] * 1e3 / ms, 4)}
     if "cpu" in r:
         c = r["cpu"]
+        nproc, model = host_info()
         line["cpu_baseline"] = {"value": round(c["value"], 4), "unit": c["unit"], "cores": c["cores"],
                                 "kind": c["kind"], "sample": c["sample"],
-                                "tokens_per_s": round(c["tokens_per_s"], 3)}
+                                "tokens_per_s": round(c["tokens_per_s"], 3),
+                                "nproc": nproc, "cpu_model": model}
+        if "single_thread" in c:
+            st = c["single_thread"]
+            line["cpu_baseline"]["single_thread"] = {
+                "value": round(st["value"], 4), "unit": c["unit"], "cores": 1,
+                "tokens_per_s": round(st["tokens_per_s"], 3), "sample": st["sample"],
+                "seconds": round(st["seconds"], 2)}
     print(json.dumps(line), flush=True)
 
 

@@ -40,6 +40,21 @@ int cor_num_threads(void)
 #endif
 }
 
+/* Host threads for the parallel loops that follow (n >= 1). Work is split
+ * over output rows or tokens, each result summed by one thread in a fixed
+ * order, so the thread count changes timing only, never a value. Returns
+ * the previous count. */
+int cor_set_threads(int n)
+{
+    const int prev = cor_num_threads();
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+    return prev;
+}
+
 /* Bytes of one packed row of I elements [glm.c@98759bf -- qt_bytes]. */
 int64_t cor_row_bytes(int fmt, int64_t I)
 {

@@ -45,6 +45,8 @@ def lib():
         L.cor_unpack.restype = dp
         L.cor_unpack.argtypes = [i32, vp, i64]
         L.cor_num_threads.restype = i32
+        L.cor_set_threads.restype = i32
+        L.cor_set_threads.argtypes = [i32]
         L.cor_qgemv.restype = i32
         L.cor_qgemv.argtypes = [i32, vp, vp, vp, i32, i32, i32, vp, vp]
         L.cor_qgemv_d.restype = i32
@@ -81,6 +83,11 @@ def _c(a, dtype):
 
 def num_threads() -> int:
     return int(lib().cor_num_threads())
+
+
+def set_threads(n: int) -> int:
+    """Host threads for later oracle calls; returns the previous count."""
+    return int(lib().cor_set_threads(int(n)))
 
 
 def row_bytes(fmt: int, I: int) -> int:

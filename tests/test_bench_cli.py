@@ -49,3 +49,37 @@ def test_per_expert_roofline_closed_forms():
     lo, hi = int(r_star), int(r_star) + 1
     assert bench.per_expert_roofline_s([lo], B, D, F) == pytest.approx(hbm)
     assert bench.per_expert_roofline_s([hi], B, D, F) == pytest.approx(flop(hi))
+
+
+def test_host_info_reports_cpus_and_model():
+    import bench
+    n, model = bench.host_info()
+    assert n >= 1
+    assert isinstance(model, str) and model
+
+
+def test_oracle_thread_count_changes_no_value():
+    """The oracle splits work over rows or tokens, one thread per result, so
+    one thread and all threads give the same bits; set_threads restores."""
+    import numpy as np
+    from oracle import oracle
+    from weight_streaming_gemv_qgemv_amd import synth
+    g = synth.rng(9100)
+    O, I, S = 37, 512, 3
+    W = synth.weight_bytes(g, 2, O, I)
+    sc = synth.scales(g, O)
+    x = synth.activations(g, S, I)
+    Wr, bias = synth.router_weights(g, 16, I)
+    y_all, _ = oracle.qgemv(2, W, sc, x)
+    r_all = oracle.router(Wr, bias, x, 4, 1, 2.5)
+    prev = oracle.set_threads(1)
+    try:
+        assert oracle.num_threads() == 1
+        y_one, _ = oracle.qgemv(2, W, sc, x)
+        r_one = oracle.router(Wr, bias, x, 4, 1, 2.5)
+    finally:
+        assert oracle.set_threads(prev) == 1
+    assert oracle.num_threads() == prev
+    assert np.array_equal(y_all, y_one)
+    assert np.array_equal(r_all["idx"], r_one["idx"])
+    assert np.array_equal(r_all["w"], r_one["w"])
