@@ -30,134 +30,106 @@ namespace coli {
 namespace {
 
 constexpr int kGroupWaves = 16;          // experts per block in the grouping kernels
-constexpr int kWin = 8192;               // slots staged in LDS at a time (32 KB)
 
 // Flags written by the grouping kernel (plain stores from block 0).
 constexpr uint32_t kFlagBadId = 1u;
 constexpr uint32_t kFlagDup = 2u;
 
-// Count the slots of each expert; block 0 also validates every slot.
-__global__ __launch_bounds__(1024) void k_group_count(const int32_t *__restrict__ idx, int P,
-                                                      int K, int E, int32_t *__restrict__ counts,
-                                                      uint32_t *__restrict__ flags)
+// Grouping of at most COLI_GROUP_CHUNK slots, one launch.  Every block
+// stages all slots in LDS and counts the slots of every expert there (LDS
+// atomics: integer counts, so the order of the adds does not matter), which
+// gives each of its experts the exclusive prefix of the counts without an
+// earlier launch.  Block 0 also writes the counts and validates every slot.
+// Each expert's wave then writes its offset and, when `work` is given, the
+// matrix-core work list entries of its group (passes of `tpp` rows, entry
+// g | pass << 11, in group order; the wave of the last expert adds those of
+// the extra group g = E (extra_rows rows) and the count), and scatters the
+// expert's slots into its group in slot order (stable).
+__global__ __launch_bounds__(1024) void k_group_one(const int32_t *__restrict__ idx, int P, int K,
+                                                    int E, int32_t *__restrict__ counts,
+                                                    int32_t *__restrict__ offsets,
+                                                    int32_t *__restrict__ row_pair,
+                                                    int32_t *__restrict__ pair_row, int extra_rows,
+                                                    int tpp, int32_t *__restrict__ work,
+                                                    int32_t *__restrict__ n_work,
+                                                    uint32_t *__restrict__ flags)
 {
-    __shared__ int32_t sidx[kWin];
+    __shared__ int32_t sidx[COLI_GROUP_CHUNK];
+    __shared__ int32_t cnt[COLI_MAX_E];
     __shared__ uint32_t sflag;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int e = blockIdx.x * kGroupWaves + wave;
-    if (threadIdx.x == 0) sflag = 0u;
-    int count = 0;
-    for (int base = 0; base < P; base += kWin) {
-        const int n = min(kWin, P - base);
-        __syncthreads();
-        for (int i = threadIdx.x; i < n; i += blockDim.x) sidx[i] = idx[base + i];
-        __syncthreads();
-        if (e < E) {
-            for (int c = 0; c < n; c += 64) {
-                const int i = c + lane;
-                const bool hit = i < n && sidx[i] == e;
-                count += __popcll(__ballot(hit));
-            }
-        }
-        if (blockIdx.x == 0) {
-            uint32_t f = 0u;
-            for (int i = threadIdx.x; i < n; i += blockDim.x) {
-                const int p = base + i;
-                const int v = sidx[i];
-                if (v < -1 || v >= E) f |= kFlagBadId;
-                if (v >= 0) {
-                    const int s0 = (p / K) * K;
-                    for (int q = s0; q < p; ++q)
-                        if (idx[q] == v) { f |= kFlagDup; break; }
-                }
-            }
-            if (f) atomicOr(&sflag, f);
-        }
+    for (int i = t; i < E; i += 1024) cnt[i] = 0;
+    if (t == 0) sflag = 0u;
+    __syncthreads();
+    for (int i = t; i < P; i += 1024) {
+        const int v = idx[i];
+        sidx[i] = v;
+        if (v >= 0 && v < E) atomicAdd(&cnt[v], 1);
     }
-    if (e < E && lane == 0) counts[e] = count;
+    __syncthreads();
     if (blockIdx.x == 0) {
-        __syncthreads();
-        if (threadIdx.x == 0) flags[0] = sflag;
-    }
-}
-
-// Exclusive prefix of the counts per expert, then a stable scatter of every
-// slot of the expert into its group.  When `work` is given, each expert's
-// wave also writes the matrix-core work list entries of its group (passes of
-// `tpp` rows, entry g | pass << 11, in group order), and the wave of the last
-// expert adds those of the extra group g = E (extra_rows rows) and the count.
-__global__ __launch_bounds__(1024) void k_group_scatter(const int32_t *__restrict__ idx, int P,
-                                                        int E, const int32_t *__restrict__ counts,
-                                                        int32_t *__restrict__ offsets,
-                                                        int32_t *__restrict__ row_pair,
-                                                        int32_t *__restrict__ pair_row,
-                                                        int extra_rows, int tpp,
-                                                        int32_t *__restrict__ work,
-                                                        int32_t *__restrict__ n_work)
-{
-    __shared__ int32_t sidx[kWin];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int e = blockIdx.x * kGroupWaves + wave;
-    int off = 0;
-    if (e < E) {
-        int part = 0, ppart = 0;
-        for (int j = lane; j < e; j += 64) {
-            const int c = counts[j];
-            part += c;
-            ppart += (c + tpp - 1) / tpp;
-        }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            part += __shfl_xor(part, o, kWave);
-            ppart += __shfl_xor(ppart, o, kWave);
-        }
-        off = part;
-        const int ce = counts[e];
-        if (lane == 0) {
-            offsets[e] = off;
-            if (e == E - 1) offsets[E] = off + ce;
-        }
-        if (work) {
-            const int np = (ce + tpp - 1) / tpp;
-            for (int p = lane; p < np; p += 64) work[ppart + p] = e | (p << 11);
-            if (e == E - 1) {
-                const int nx = (extra_rows + tpp - 1) / tpp;
-                for (int p = lane; p < nx; p += 64) work[ppart + np + p] = E | (p << 11);
-                if (lane == 0) *n_work = ppart + np + nx;
+        // ids in [-1, E), and no expert twice among one token's K slots
+        uint32_t f = 0u;
+        for (int i = t; i < P; i += 1024) {
+            const int v = sidx[i];
+            if (v < -1 || v >= E) f |= kFlagBadId;
+            if (v >= 0) {
+                const int s0 = (i / K) * K;
+                for (int q = s0; q < i; ++q)
+                    if (sidx[q] == v) { f |= kFlagDup; break; }
             }
+            if (v < 0 || v >= E) pair_row[i] = -1;
+        }
+        if (f) atomicOr(&sflag, f);
+        for (int i = t; i < E; i += 1024) counts[i] = cnt[i];
+        __syncthreads();
+        if (t == 0) flags[0] = sflag;
+    }
+    if (e >= E) return;   // whole waves; no barrier below
+    int part = 0, ppart = 0;
+    for (int j = lane; j < e; j += 64) {
+        const int c = cnt[j];
+        part += c;
+        ppart += (c + tpp - 1) / tpp;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        part += __shfl_xor(part, o, kWave);
+        ppart += __shfl_xor(ppart, o, kWave);
+    }
+    const int off = part;
+    const int ce = cnt[e];
+    if (lane == 0) {
+        offsets[e] = off;
+        if (e == E - 1) offsets[E] = off + ce;
+    }
+    if (work) {
+        const int np = (ce + tpp - 1) / tpp;
+        for (int p = lane; p < np; p += 64) work[ppart + p] = e | (p << 11);
+        if (e == E - 1) {
+            const int nx = (extra_rows + tpp - 1) / tpp;
+            for (int p = lane; p < nx; p += 64) work[ppart + np + p] = E | (p << 11);
+            if (lane == 0) *n_work = ppart + np + nx;
         }
     }
     int run = 0;
-    for (int base = 0; base < P; base += kWin) {
-        const int n = min(kWin, P - base);
-        __syncthreads();
-        for (int i = threadIdx.x; i < n; i += blockDim.x) sidx[i] = idx[base + i];
-        __syncthreads();
-        if (e < E) {
-            for (int c = 0; c < n; c += 64) {
-                const int i = c + lane;
-                const bool hit = i < n && sidx[i] == e;
-                const uint64_t m = __ballot(hit);
-                if (hit) {
-                    const uint64_t below = lane ? (m & ((~0ull) >> (64 - lane))) : 0ull;
-                    const int pos = off + run + __popcll(below);
-                    row_pair[pos] = base + i;
-                    pair_row[base + i] = pos;
-                }
-                run += __popcll(m);
-            }
+    for (int c = 0; c < P; c += 64) {
+        const int i = c + lane;
+        const bool hit = i < P && sidx[i] == e;
+        const uint64_t m = __ballot(hit);
+        if (hit) {
+            const uint64_t below = lane ? (m & ((~0ull) >> (64 - lane))) : 0ull;
+            const int pos = off + run + __popcll(below);
+            row_pair[pos] = i;
+            pair_row[i] = pos;
         }
-        if (blockIdx.x == 0) {
-            for (int i = threadIdx.x; i < n; i += blockDim.x) {
-                const int v = sidx[i];
-                if (v < 0 || v >= E) pair_row[base + i] = -1;
-            }
-        }
+        run += __popcll(m);
     }
 }
 
 // Chunked grouping for large batches (P > COLI_GROUP_CHUNK slots): the same
-// outputs as k_group_count + k_group_scatter, with the slots cut into chunks
+// outputs as k_group_one, with the slots cut into chunks
 // so that a wave scans one expert over one chunk only.
 //   k_group_hist:  block (expert group, chunk) -> hist[c][e] = the chunk's
 //                  slots of expert e; block (0, c) validates the chunk
@@ -538,13 +510,9 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
         hipLaunchKernelGGL(k_group_place, dim3(gblocks, C), dim3(1024), 0, st, idx, P, E, gpart,
                            row_pair, pair_row);
     } else {
-        hipLaunchKernelGGL(k_group_count, dim3(gblocks), dim3(1024), 0, st, idx, P, K, E, counts,
-                           flags);
-        err = hipGetLastError();
-        if (err != hipSuccess) return COLI_EDEVICE;
-        hipLaunchKernelGGL(k_group_scatter, dim3(gblocks), dim3(1024), 0, st, idx, P, E, counts,
-                           offsets, row_pair, pair_row, sh_mm ? S : 0, tpp,
-                           mm ? work : nullptr, n_work);
+        hipLaunchKernelGGL(k_group_one, dim3(gblocks), dim3(1024), 0, st, idx, P, K, E, counts,
+                           offsets, row_pair, pair_row, sh_mm ? S : 0, tpp, mm ? work : nullptr,
+                           n_work, flags);
     }
     err = hipGetLastError();
     if (err != hipSuccess) return COLI_EDEVICE;
