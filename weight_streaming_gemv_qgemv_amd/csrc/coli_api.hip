@@ -17,6 +17,7 @@
 #include "coli_pre.h"
 #include "coli_qmv.h"
 #include "coli_idot.h"
+#include "coli_xrows.h"
 
 #include "coli_internal.h"
 #include "coli_router.h"
@@ -45,6 +46,16 @@ constexpr uint32_t kFlagDup = 2u;
 // g | pass << 11, in group order; the wave of the last expert adds those of
 // the extra group g = E (extra_rows rows) and the count), and scatters the
 // expert's slots into its group in slot order (stable).
+// XF >= 0: blocks gblocks .. gblocks + rows - 1 instead write the activation
+// row tables of the rows of x for weight format XF (coli_xrows.h), work
+// that does not depend on the routing and so shares the launch.
+struct XrowsJob {
+    const float *x;
+    int64_t ldx;
+    int I, kpad, vec;
+    uint16_t *table;
+};
+template <int XF>
 __global__ __launch_bounds__(1024) void k_group_one(const int32_t *__restrict__ idx, int P, int K,
                                                     int E, int32_t *__restrict__ counts,
                                                     int32_t *__restrict__ offsets,
@@ -52,12 +63,23 @@ __global__ __launch_bounds__(1024) void k_group_one(const int32_t *__restrict__ 
                                                     int32_t *__restrict__ pair_row, int extra_rows,
                                                     int tpp, int32_t *__restrict__ work,
                                                     int32_t *__restrict__ n_work,
-                                                    uint32_t *__restrict__ flags)
+                                                    uint32_t *__restrict__ flags, int gblocks,
+                                                    XrowsJob xj)
 {
     __shared__ int32_t sidx[COLI_GROUP_CHUNK];
     __shared__ int32_t cnt[COLI_MAX_E];
     __shared__ uint32_t sflag;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    if constexpr (XF >= 0) {
+        if ((int)blockIdx.x >= gblocks) {   // whole block, before any barrier
+            const int row = (int)blockIdx.x - gblocks;
+            const float *xr = xj.x + (int64_t)row * xj.ldx;
+            uint16_t *dst = xj.table + (int64_t)row * 2 * xj.kpad;
+            const int nruns = xj.kpad / xrows_run_len<XF>();
+            for (int r = t; r < nruns; r += 1024) xrows_run<XF>(xr, xj.I, r, dst, xj.vec);
+            return;
+        }
+    }
     const int e = blockIdx.x * kGroupWaves + wave;
     for (int i = t; i < E; i += 1024) cnt[i] = 0;
     if (t == 0) sflag = 0u;
@@ -495,6 +517,9 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
     const int tpp = bf16 ? COLI_MM_TPP_BF16 : COLI_MM_TPP_FP32;
     int32_t *work = reinterpret_cast<int32_t *>(ws + L.work);
     int32_t *n_work = reinterpret_cast<int32_t *>(ws + L.n_work);
+    // fp32 matrix-core path with one grouping launch: that launch also
+    // writes x's row tables
+    const bool x_fused = mm && !bf16 && P <= kChunk;
     {
     StageTimer tg(kStGroup, st);
     if (P > kChunk) {
@@ -510,9 +535,19 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
         hipLaunchKernelGGL(k_group_place, dim3(gblocks, C), dim3(1024), 0, st, idx, P, E, gpart,
                            row_pair, pair_row);
     } else {
-        hipLaunchKernelGGL(k_group_one, dim3(gblocks), dim3(1024), 0, st, idx, P, K, E, counts,
-                           offsets, row_pair, pair_row, sh_mm ? S : 0, tpp, mm ? work : nullptr,
-                           n_work, flags);
+        // the fp32 matrix-core path's row tables of x ride along
+        XrowsJob xj = {x, D, D, (int)coli__kpad(D), (int)(D % 4 == 0 && al16(x)),
+                       reinterpret_cast<uint16_t *>(ws + L.xf)};
+        const int xg = x_fused ? S : 0;
+#define COLI_GROUP_ONE(XF)                                                                         \
+    hipLaunchKernelGGL(k_group_one<XF>, dim3(gblocks + xg), dim3(1024), 0, st, idx, P, K, E, counts, \
+                       offsets, row_pair, pair_row, sh_mm ? S : 0, tpp, mm ? work : nullptr, n_work, \
+                       flags, gblocks, xj)
+        if (!x_fused) COLI_GROUP_ONE(-1);
+        else if (ex->fmt == kI8) COLI_GROUP_ONE(kI8);
+        else if (ex->fmt == kI4) COLI_GROUP_ONE(kI4);
+        else COLI_GROUP_ONE(kI2);
+#undef COLI_GROUP_ONE
     }
     err = hipGetLastError();
     if (err != hipSuccess) return COLI_EDEVICE;
@@ -527,7 +562,8 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
         const int kpD = (int)coli__kpad(D), kpF = (int)coli__kpad(F);
         {
             StageTimer tp(kStPrep, st);
-            if (xrows_launch(ex->fmt, x, D, S, D, kpD, xt, st) != hipSuccess) return COLI_EDEVICE;
+            if (!x_fused && xrows_launch(ex->fmt, x, D, S, D, kpD, xt, st) != hipSuccess)
+                return COLI_EDEVICE;
         }
         {
             StageTimer tgu(kStGateUp, st);

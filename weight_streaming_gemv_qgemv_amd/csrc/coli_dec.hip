@@ -31,6 +31,7 @@
 #include "coli_device.h"
 #include "coli_frag.h"
 #include "coli_dec.h"
+#include "coli_xrows.h"
 
 namespace coli {
 
@@ -43,65 +44,16 @@ constexpr int kDecNT = kDecTpp / 8;   // MFMA N-tiles per pass (8 rows: hi/lo co
 template <int M> struct DecTiles { static constexpr int MT = M == 2 ? 2 : 4, W = M == 2 ? 4 : 2; };
 
 // ---------------------------------------------------------------- row tables
-// Block (row, part): runs of RUN consecutive elements (8: one chunk; int2
-// 16: the chunks of an even/odd step pair) split into bf16 hi/lo and stored
-// as the chunk's two 16-byte units.  Elements past I are zeros.
+// Block (row, part): the row's runs (coli_xrows.h), 256 per part.
 template <int FMT>
 __global__ __launch_bounds__(256) void k_xrows(const float *__restrict__ x, int64_t ldx, int I,
                                                int kpad, uint16_t *__restrict__ table, int vec)
 {
-    constexpr int RUN = FMT == kI2 ? 16 : 8;
     const int row = blockIdx.x;
     const float *xr = x + (int64_t)row * ldx;
     uint16_t *dst = table + (int64_t)row * 2 * kpad;
-    const int nruns = kpad / RUN;
-    for (int r = blockIdx.y * 256 + threadIdx.x; r < nruns; r += gridDim.y * 256) {
-        const int e0 = r * RUN;
-        float v[RUN];
-        if (vec && e0 + RUN <= I) {
-#pragma unroll
-            for (int i = 0; i < RUN / 4; ++i) {
-                const float4 f = *reinterpret_cast<const float4 *>(xr + e0 + 4 * i);
-                v[4 * i] = f.x;
-                v[4 * i + 1] = f.y;
-                v[4 * i + 2] = f.z;
-                v[4 * i + 3] = f.w;
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < RUN; ++i) v[i] = e0 + i < I ? xr[e0 + i] : 0.f;
-        }
-        uint16_t hv[RUN], lv[RUN];
-#pragma unroll
-        for (int i = 0; i < RUN; ++i) {
-            hv[i] = bf16_rne(v[i]);
-            lv[i] = bf16_rne(v[i] - bf16_f(hv[i]));
-        }
-        // slot pairs (2m, 2m+1) of each chunk, in the order the unpacking
-        // produces the weight codes
-        int c, j;
-        pos_of<FMT>(e0, c, j);
-        uint32_t hw[RUN / 2], lw[RUN / 2];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            int k0, k1;
-            if constexpr (FMT == kI8) { k0 = 2 * m; k1 = 2 * m + 1; }
-            else if constexpr (FMT == kI4) { k0 = m; k1 = m + 4; }
-            else { k0 = m; k1 = m + 8; }
-            hw[m] = (uint32_t)hv[k0] | ((uint32_t)hv[k1] << 16);
-            lw[m] = (uint32_t)lv[k0] | ((uint32_t)lv[k1] << 16);
-            if constexpr (FMT == kI2) {
-                hw[4 + m] = (uint32_t)hv[m + 4] | ((uint32_t)hv[m + 12] << 16);
-                lw[4 + m] = (uint32_t)lv[m + 4] | ((uint32_t)lv[m + 12] << 16);
-            }
-        }
-#pragma unroll
-        for (int h = 0; h < RUN / 8; ++h) {
-            uint16_t *u = dst + (int64_t)(c + 4 * h) * 16;   // chunk c + 4h: next MFMA step
-            *reinterpret_cast<uint4 *>(u) = make_uint4(hw[4 * h], hw[4 * h + 1], hw[4 * h + 2], hw[4 * h + 3]);
-            *reinterpret_cast<uint4 *>(u + 8) = make_uint4(lw[4 * h], lw[4 * h + 1], lw[4 * h + 2], lw[4 * h + 3]);
-        }
-    }
+    const int nruns = kpad / xrows_run_len<FMT>();
+    for (int r = blockIdx.y * 256 + threadIdx.x; r < nruns; r += gridDim.y * 256) xrows_run<FMT>(xr, I, r, dst, vec);
 }
 
 // ---------------------------------------------------------------- products
