@@ -438,7 +438,8 @@ def run_qgemv(args, dev):
     from weight_streaming_gemv_qgemv_amd import binding as b
     from weight_streaming_gemv_qgemv_amd import synth
     fmt = {"f32": 0, "i8": 1, "i4": 2, "i2": 3}[args.fmt]
-    O, I, S = 12288, 6144, args.tokens
+    O, I = (int(v) for v in getattr(args, "shape", "12288x6144").lower().split("x"))
+    S = args.tokens
     g = synth.rng(4200, fmt)
     W = synth.weight_bytes(g, fmt, O, I)
     sc = synth.scales(g, O)
@@ -473,14 +474,14 @@ def run_qgemv(args, dev):
     q_ms, q_n = stages["qgemv"]
     var = "_idot" if idot else f"_g{gs}" if gs else ""
     entry = "coli_qgemv_idot" if idot else "coli_qgemv_grouped" if gs else "coli_qgemv"
-    name = f"qgemv{var}_{args.fmt}_12288x6144_s{S}"
+    name = f"qgemv{var}_{args.fmt}_{O}x{I}_s{S}"
     wf = {0: "fp32", 1: "int8 per-row scale", 2: "int4 per-row scale", 3: "int2 per-row scale"}[fmt]
     if idot:
         wf += ", int8 activations (integer dot)"
     if gs:
         wf = f"int4 one scale per {gs} elements"
     return dict(workload=name, ms=ms, wall=wall, step_bytes=step_bytes, weight_format=wf,
-                tokens=S, stages=stages, uniq=None,
+                tokens=S, stages=stages, uniq=None, O=O, I=I,
                 dominant=dict(kernel=f"qgemv {args.fmt} ({entry})",
                               bytes_per_launch=step_bytes,
                               ms_per_launch=q_ms / max(q_n, 1), launches=q_n))
@@ -511,6 +512,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fmt", default="i4", choices=["f32", "i8", "i4", "i2"], help="qgemv workload")
     ap.add_argument("--tokens", type=int, default=1, help="qgemv workload: S")
+    ap.add_argument("--shape", default="12288x6144", metavar="OxI",
+                    help="qgemv workload: output rows x input width (512x1024: the small, "
+                         "L2-resident case, timed over a >= 1 GiB rotation of weight copies)")
     ap.add_argument("--idot", action="store_true", help="qgemv workload: the integer-dot variant")
     ap.add_argument("--grouped", type=int, default=0, metavar="GS",
                     help="qgemv workload: grouped-scale int4, one scale per GS elements")
@@ -561,12 +565,16 @@ def main():
         "vs_baseline": None,
         "dtype": f"f32 ({r.get('weight_format', 'int4').split()[0]} weights)",
         "data": "synthetic",
-        "config": {"workload": r["workload"], "tokens_per_step": r["tokens"],
-                   "experts": r.get("experts", 256) if r["uniq"] is not None else None,
-                   "unique_experts_per_step": r["uniq"], "hidden": 6144,
-                   "moe_inter": 2048, "top_k": 8 if r["uniq"] is not None else None,
-                   "weight_format": r.get("weight_format", "int4 per-row scale"),
-                   "algorithmic_bytes_per_step": r["step_bytes"]},
+        "config": ({"workload": r["workload"], "tokens_per_step": r["tokens"],
+                    "experts": r.get("experts", 256),
+                    "unique_experts_per_step": r["uniq"], "hidden": 6144,
+                    "moe_inter": 2048, "top_k": 8,
+                    "weight_format": r.get("weight_format", "int4 per-row scale"),
+                    "algorithmic_bytes_per_step": r["step_bytes"]} if r["uniq"] is not None else
+                   {"workload": r["workload"], "tokens_per_step": r["tokens"],
+                    "out_rows": r["O"], "in_width": r["I"],
+                    "weight_format": r.get("weight_format", "int4 per-row scale"),
+                    "algorithmic_bytes_per_step": r["step_bytes"]}),
         "tokens_per_s": round(r["tokens"] / (ms * 1e-3), 1),
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "stage_ms_per_step": {k: round(v[0] / max(v[1], 1), 5) for k, v in r["stages"].items() if v[1]},
