@@ -340,8 +340,9 @@ int coli_check_device_flags(const void *ws, void *stream, uint32_t *flags_out);
  * the number of timed launches since the last reset (host arrays of
  * COLI_NSTAGES entries; either may be NULL).  Stages: 0 router, 1 grouping,
  * 2 gate/up + SwiGLU, 3 down, 4 combine, 5 qgemv, 6 matrix-core preparation
- * (work list and activation fragments ahead of gate/up), 7 RMSNorm of the
- * layer tail.  The pages time the same
+ * (activation fragments and per-row sums ahead of gate/up, where the grouping
+ * launch does not already write them: fp32 precision up to 1024 slots, the
+ * grouping stage covers them), 7 RMSNorm of the layer tail.  The pages time the same
  * phases of their MoE block [metal@93cde63 -- moe_finish timers;
  * glm.c@98759bf -- profile counters]. */
 #define COLI_NSTAGES 8

@@ -560,10 +560,9 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
         uint16_t *ht = reinterpret_cast<uint16_t *>(ws + L.hf);
         const int64_t max_gp = L.n_pass_max;
         const int kpD = (int)coli__kpad(D), kpF = (int)coli__kpad(F);
-        {
+        if (!x_fused) {   // else the grouping launch wrote them
             StageTimer tp(kStPrep, st);
-            if (!x_fused && xrows_launch(ex->fmt, x, D, S, D, kpD, xt, st) != hipSuccess)
-                return COLI_EDEVICE;
+            if (xrows_launch(ex->fmt, x, D, S, D, kpD, xt, st) != hipSuccess) return COLI_EDEVICE;
         }
         {
             StageTimer tgu(kStGateUp, st);
