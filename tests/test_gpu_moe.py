@@ -225,6 +225,39 @@ def test_moe_gemv_chunked_grouping(dev, orc):
     assert_within(out, ref["out"], ref["mag"], REL, what="chunked bad/dup")
 
 
+@pytest.mark.parametrize("fmt", [1, 2, 3])
+def test_moe_gemv_one_launch_grouping_limit(dev, orc, fmt):
+    """The one-launch grouping (which also writes x's row tables) at its
+    largest batch, 128 tokens x 8 slots = 1024 slots, and one token more
+    (1032 slots: the chunked grouping and the separate row-table kernel);
+    skewed routing with empty slots, and a bad id in the last slot."""
+    from weight_streaming_gemv_qgemv_amd import binding as b
+    E, D, F, K = 36, 256, 128, 8
+    bank = synth.expert_bank(60 + fmt, fmt, E, D, F)
+    bd = dev_bank(bank, dev)
+    for S in (128, 129):
+        g = synth.rng(61, fmt, S)
+        x = synth.activations(g, S, D)
+        idx, w = synth.routing_zipf(g, S, K, E)
+        idx[3, 2] = -1
+        idx[S - 1, 5] = -1
+        announce("moe grouping limit", fmt, S)
+        out, ws = run_gemv(dev, bd, x, idx, w)
+        lay = b.moe_workspace_layout(S, K, E, D, F)
+        check_moe(orc, bank, None, x, idx, w, out, ws, lay, f"limit S{S}")
+        assert b.check_device_flags(ws) == (b.OK, 0)
+        bad = idx.copy()
+        bad[S - 1, K - 1] = E
+        announce("moe grouping limit, bad id", fmt, S)
+        out, ws = run_gemv(dev, bd, x, bad, w)
+        rc, flags = b.check_device_flags(ws)
+        assert rc == b.EIDX and flags & 1
+        masked = bad.copy()
+        masked[(masked < 0) | (masked >= E)] = -1
+        ref = orc.moe(bank, None, x, masked, w.astype(np.float64))
+        assert_within(out, ref["out"], ref["mag"], REL, what=f"limit bad S{S}")
+
+
 def test_moe_layer_small_with_router_and_shared(dev, orc):
     import torch
     from weight_streaming_gemv_qgemv_amd import binding as b
