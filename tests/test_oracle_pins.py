@@ -377,6 +377,19 @@ def test_golden_rmsnorm(orc, case):
     assert np.all(np.abs(got - exp) <= tol), (got, exp)
 
 
+@pytest.mark.parametrize("case", _load("rmsnorm_small.json")["fp32_order_cases"], ids=lambda c: c["name"])
+def test_golden_rmsnorm_rounding_order(orc, case):
+    """Rows where w != 1 and r is inexact, so (x * r) * w and x * (r * w)
+    round differently in fp32: the oracle gives the pages' left-to-right
+    bits exactly, and the fixture's other order really differs."""
+    x = np.array([case["x"]], np.float32)
+    got = orc.rmsnorm(x, np.array(case["w"], np.float32), case["eps"])[0]
+    exp = np.array(case["expected"], np.float32)
+    other = np.array(case["other_order"], np.float32)
+    assert np.any(other != exp)
+    np.testing.assert_array_equal(got.view(np.uint32), exp.view(np.uint32))
+
+
 def test_rmsnorm_unit_rms(orc):
     """w = 1, eps = 0: every output row has mean square 1 (up to fp32
     rounding of the products)."""
@@ -474,6 +487,36 @@ def test_idot_integer_dot_is_exact(orc, fmt):
     q, _ = orc.qrow_i8(x)
     _, dot = orc.qgemv_idot(fmt, W, np.ones(O, np.float32), x)
     np.testing.assert_array_equal(dot, q.astype(np.int64) @ V.T.astype(np.int64))
+
+
+@pytest.mark.parametrize("case", _load("idot_epilogue.json")["cases"], ids=lambda c: c["name"])
+def test_golden_idot_epilogue_order(orc, case):
+    """Hand-worked (dot, scale, s) with non-power-of-two scale and s, where
+    ((float)dot * scale) * s differs in fp32 from the other association
+    orders: the oracle's quantised row, integer dot and y match the worked
+    values bit for bit."""
+    fmt = I8 if case["fmt"] == "i8" else I4
+    v = np.array([case["v"]], np.int64)
+    W = v.astype(np.int8).view(np.uint8) if fmt == I8 else _int4_bytes_from_values(v)
+    x = np.array([case["x"]], np.float32)
+    sc = np.array([case["scale"]], np.float32)
+    q, s = orc.qrow_i8(x)
+    assert s[0] == np.float32(case["s"])
+    np.testing.assert_array_equal(q[0], np.array(case["q"], np.int8))
+    y, dot = orc.qgemv_idot(fmt, W, sc, x)
+    assert int(dot[0, 0]) == case["dot"]
+    exp = np.float32(case["y"])
+    assert "0x%08x" % int(exp.view(np.uint32)) == case["y_bits"]
+    assert np.float32(case["other_orders"][0]) != exp     # dot * (scale * s) rounds differently
+    assert y[0, 0].view(np.uint32) == exp.view(np.uint32), (y[0, 0], exp)
+
+
+def test_golden_idot_epilogue_cases_catch_each_order():
+    """Across the fixture, each other association order of the epilogue
+    differs from the worked value in at least one case."""
+    cases = _load("idot_epilogue.json")["cases"]
+    for k in range(2):
+        assert any(np.float32(c["other_orders"][k]) != np.float32(c["y"]) for c in cases)
 
 
 def test_idot_epilogue_exact_for_power_of_two_scales(orc):
