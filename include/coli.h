@@ -121,6 +121,10 @@ int coli_qgemv(int fmt, const void *W, const float *scale, const float *x,
  *          bytes, 256-byte aligned: the quantised rows.
  * Errors: COLI_EFMT, COLI_EINVAL, COLI_ESHAPE, COLI_EALIGN, COLI_ERANGE,
  * COLI_EWORKSPACE, COLI_EDEVICE. */
+size_t coli_qgemv_idot_workspace_bytes(int S, int I);
+int coli_qgemv_idot(int fmt, const void *W, const float *scale, const float *x, float *y,
+                    int S, int I, int O, void *ws, size_t ws_bytes, void *stream);
+
 /* Grouped-scale int4 matrix-vector product (the pages' fmt 4,
  * "int4-grouped": int4 rows with one fp32 scale per group of gs consecutive
  * elements along I instead of one per row) [docs-quickstart --
@@ -137,10 +141,6 @@ int coli_qgemv(int fmt, const void *W, const float *scale, const float *x,
  * range), COLI_EDEVICE. */
 int coli_qgemv_grouped(const void *W, const float *scale, int gs, const float *x, float *y,
                        int S, int I, int O, void *stream);
-
-size_t coli_qgemv_idot_workspace_bytes(int S, int I);
-int coli_qgemv_idot(int fmt, const void *W, const float *scale, const float *x, float *y,
-                    int S, int I, int O, void *ws, size_t ws_bytes, void *stream);
 
 /* Router: sigmoid scores and noaux_tc top-K with one group
  * [glm.c@98759bf -- moe, phase A; metal@93cde63 -- r_router, r_top8,
@@ -281,6 +281,12 @@ int coli_moe_workspace_layout(int S, int K, int E, int D, int F, int F_shared,
  * An id < -1 or >= E is skipped and a listed-twice expert is computed twice;
  * both set a flag that coli_check_device_flags() reports.
  * 1 <= K <= 64, 1 <= E <= 1024, S >= 0, D, F >= 1.
+ * Size limit (COLI_ERANGE otherwise): every expert matrix (F * row_bytes(D)
+ * and D * row_bytes(F), routed and shared) and every activation table --
+ * S rows, and S*K (+ S with a shared expert) rows, of 4 (COLI_PREC_FP32) or
+ * 2 (COLI_PREC_BF16) bytes per element of D resp. max(F, F_shared) rounded
+ * up to 1024 -- stays below 2^32 - 4096 bytes.  At D = 6144, F = 2048, K = 8
+ * with a shared expert that is S <= 58254 tokens per call (fp32 precision).
  * Errors: COLI_EINVAL, COLI_EFMT, COLI_ESHAPE, COLI_ERANGE, COLI_EALIGN,
  * COLI_EWORKSPACE, COLI_EDEVICE. */
 int coli_moe_gemv(const coli_experts *ex, const float *x, int S, int K,

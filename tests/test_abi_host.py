@@ -131,6 +131,37 @@ def test_moe_rejects_before_launch(L):
                             0, FAKE, need, None) == b.EINVAL
 
 
+def test_moe_refuses_sizes_past_32bit_offsets(L):
+    """The expert kernels use 32-bit byte offsets into one weight matrix and
+    one activation table; sizes past 2^32 - 4096 bytes are refused on the
+    host (COLI_ERANGE) instead of wrapping on the device."""
+    from weight_streaming_gemv_qgemv_amd import binding as b
+    E, D, F, K = 256, 6144, 2048, 8
+    ex = b.Experts(2, E, D, F, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    sh = b.Mlp(2, F, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    rp = b.RouterParams(FAKE, FAKE, K, 1, 2.5, 0.0)
+
+    def layer(S, shared, prec):
+        # one byte short of the workspace: a size that passes the range check
+        # stops at the workspace check, so nothing is ever launched
+        need = b.moe_workspace_bytes(S, K, E, D, F, F if shared else 0, prec)
+        return L.coli_moe_layer(C.byref(rp), C.byref(ex), C.byref(sh) if shared else None, FAKE, S,
+                                FAKE, FAKE, FAKE, None, None, prec, FAKE, need - 1, None)
+
+    # fp32 precision: (9 S rows) x 4 x 2048 bytes of SwiGLU table
+    assert layer(58255, True, 0) == b.ERANGE
+    assert layer(58254, True, 0) == b.EWORKSPACE
+    assert layer(65536, False, 0) == b.ERANGE        # 8 S rows
+    assert layer(65535, False, 0) == b.EWORKSPACE
+    # bf16 precision: 2 bytes per element, twice the tokens
+    assert layer(2 * 58255, True, 1) == b.ERANGE
+    assert layer(2 * 58254, True, 1) == b.EWORKSPACE
+    # one expert matrix of 2^32 bytes (int4, D = 2^20, F = 8192)
+    big = b.Experts(2, 4, 1 << 20, 8192, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    need = b.moe_workspace_bytes(1, 2, 4, 1 << 20, 8192, 0, 0)
+    assert L.coli_moe_gemv(C.byref(big), FAKE, 1, 2, FAKE, FAKE, FAKE, 0, FAKE, need - 1, None) == b.ERANGE
+
+
 def test_workspace_layout_is_consistent(L):
     from weight_streaming_gemv_qgemv_amd import binding as b
     for (S, K, E, D, F, Fs) in [(1, 1, 1, 1, 1, 0), (64, 8, 256, 6144, 2048, 2048),

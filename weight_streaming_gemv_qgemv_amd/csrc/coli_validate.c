@@ -238,6 +238,30 @@ static int check_mlp_tensors(int fmt, int D, int F, const void *wg, const void *
     return COLI_OK;
 }
 
+/* The expert kernels address one weight matrix, and one activation row
+ * table, with 32-bit byte offsets (cheaper address arithmetic in the inner
+ * loop).  Both must stay below 2^32 - 4096 bytes: per matrix F * rb(D) and
+ * D * rb(F) (routed and shared), and the row tables of x (S rows) and of the
+ * SwiGLU output (S K rows, plus S for a shared expert), 4 (fp32 precision)
+ * or 2 (bf16 precision) bytes per element of the width rounded up to 1024. */
+static int check_off32(const coli_experts *ex, const coli_mlp *sh, int S, int K, int prec)
+{
+    const int64_t lim = ((int64_t)1 << 32) - 4096;
+    const int64_t Fmax = sh && sh->F > ex->F ? sh->F : ex->F;
+    const int64_t eb = prec == COLI_PREC_BF16 ? 2 : 4;
+    const int64_t rows = (int64_t)S * K + (sh ? S : 0);
+    int64_t t;
+    if (!mul_ok(coli_row_bytes(ex->fmt, ex->D), ex->F, &t) || t >= lim) return COLI_ERANGE;
+    if (!mul_ok(coli_row_bytes(ex->fmt, ex->F), ex->D, &t) || t >= lim) return COLI_ERANGE;
+    if (sh) {
+        if (!mul_ok(coli_row_bytes(sh->fmt, ex->D), sh->F, &t) || t >= lim) return COLI_ERANGE;
+        if (!mul_ok(coli_row_bytes(sh->fmt, sh->F), ex->D, &t) || t >= lim) return COLI_ERANGE;
+    }
+    if (!mul_ok((int64_t)S, eb * coli__kpad(ex->D), &t) || t >= lim) return COLI_ERANGE;
+    if (!mul_ok(rows, eb * coli__kpad(Fmax), &t) || t >= lim) return COLI_ERANGE;
+    return COLI_OK;
+}
+
 int coli__check_moe(const coli_experts *ex, const coli_mlp *sh, const float *x,
                     int S, int K, const int32_t *idx, const float *w,
                     const float *out, int prec, const void *ws, size_t ws_bytes,
@@ -260,6 +284,8 @@ int coli__check_moe(const coli_experts *ex, const coli_mlp *sh, const float *x,
     if (!mul_ok((int64_t)S, ex->D, &t) || !mul_ok(t, 4, &t)) return COLI_ESHAPE;
     size_t need = coli_moe_workspace_bytes(S, K, ex->E, ex->D, ex->F, sh ? sh->F : 0, prec);
     if (need == 0) return COLI_ESHAPE;
+    rc = check_off32(ex, sh, S, K, prec);
+    if (rc) return rc;
     if (S == 0) return COLI_OK;
     if (!x || !out) return COLI_EINVAL;
     if (need_routing && (!idx || !w)) return COLI_EINVAL;
