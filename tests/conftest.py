@@ -28,3 +28,18 @@ def glm_bank():
     bank = synth.expert_bank(3000, 2, 256, 6144, 2048)
     shared = synth.shared_mlp(3000, 2, 6144, 2048)
     return bank, shared
+
+
+def pytest_terminal_summary(terminalreporter):
+    """The router tests' smallest relative gap between neighbouring choices
+    (a case below 2^-20 fails as ambiguous)."""
+    try:
+        from gpu_helpers import ROUTER_GAPS
+    except ImportError:
+        return
+    if not ROUTER_GAPS:
+        return
+    what, gap = min(ROUTER_GAPS, key=lambda t: t[1])
+    terminalreporter.write_line(
+        f"router choice gaps: {len(ROUTER_GAPS)} cases, smallest {gap:.3e} ({what}); "
+        f"ambiguous below {2.0 ** -20:.3e}")

@@ -40,3 +40,34 @@ def assert_within(got, ref, mag, rel, absol=1e-6, what=""):
         f"{what}: {int((err > bound).sum())} of {err.size} outside tolerance; worst at {worst}: "
         f"got {got[worst]!r} ref {ref[worst]!r} bound {bound[worst]!r}")
     return float(ratio.max()) if ratio.size else 0.0
+
+
+# Smallest relative gap between neighbouring router choices seen by the
+# tests, (what, gap) per checked case; printed in the session summary.
+ROUTER_GAPS = []
+AMBIGUOUS_REL = 2.0 ** -20
+
+
+def choice_gap(sig, bias, K):
+    """Smallest relative gap between neighbours among each token's K+1
+    largest choices c = sig + bias (the fp32 add the router makes), exact
+    ties left out (the lowest expert index settles those the same way on
+    both sides).  A near tie at or inside the K-th pick could flip on a
+    one-ulp difference of a score, so such a case is ambiguous."""
+    c = (np.asarray(sig, np.float32) + np.asarray(bias, np.float32)[None, :]).astype(np.float64)
+    n = min(K + 1, c.shape[1])
+    top = -np.sort(-c, axis=1)[:, :n]
+    gaps = top[:, :-1] - top[:, 1:]
+    rel = np.where(gaps > 0, gaps / np.maximum(np.abs(top[:, :-1]), 1e-300), np.inf)
+    return float(rel.min()) if rel.size else float("inf")
+
+
+def assert_unambiguous(sig, bias, K, what):
+    """Records the case's smallest choice gap and fails it as ambiguous when
+    the gap is below 2^-20 of the key, never passing it silently."""
+    gap = choice_gap(sig, bias, K)
+    ROUTER_GAPS.append((what, gap))
+    print(f"[router gap] {what}: {gap:.3e}", flush=True)
+    if gap < AMBIGUOUS_REL:
+        pytest.fail(f"{what}: ambiguous routing case, neighbouring choices {gap:.3e} apart "
+                    f"(relative), below 2^-20")

@@ -16,7 +16,7 @@ never a device result."""
 import numpy as np
 import pytest
 
-from gpu_helpers import announce, assert_within, need_gpu, to_dev
+from gpu_helpers import announce, assert_unambiguous, assert_within, need_gpu, to_dev
 from weight_streaming_gemv_qgemv_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -290,6 +290,54 @@ def test_moe_layer_small_with_router_and_shared(dev, orc):
     assert_within(out2.cpu().numpy(), ref["out"], ref["mag"], REL, what="shared only")
 
 
+def run_layer_topp(dev, bank_d, shared_d, Wr, bias, x, K, topp):
+    import torch
+    from weight_streaming_gemv_qgemv_amd import binding as b
+    S = x.shape[0]
+    rp = dict(w=to_dev(Wr, dev), bias=to_dev(bias, dev), K=K, norm_topk=1, routed_scale=2.5, topp=topp)
+    idx_o = torch.empty((S, K), dtype=torch.int32, device=dev)
+    w_o = torch.empty((S, K), dtype=torch.float32, device=dev)
+    out, ws = b.moe_layer(rp, bank_d, shared_d, to_dev(x, dev), idx_out=idx_o, w_out=w_o)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), idx_o.cpu().numpy(), w_o.cpu().numpy(), ws
+
+
+def check_topp_routing(orc, Wr, bias, x, K, topp, idx, w, what):
+    """The router's ragged top-p output as the layer used it: ids (with -1
+    past keff) exact, keff below K for some tokens, weights within 1e-6."""
+    r = orc.router(Wr, bias, x, K, 1, 2.5, topp)
+    assert_unambiguous(r["sig"], bias, K, what)
+    np.testing.assert_array_equal(idx, r["idx"], err_msg=what)
+    keff = (idx >= 0).sum(axis=1)
+    np.testing.assert_array_equal(keff, r["keff"], err_msg=what)
+    assert np.all(idx[np.arange(K)[None, :] >= keff[:, None]] == -1)
+    assert np.any(keff < K), f"{what}: no token was truncated"
+    np.testing.assert_allclose(w, r["w"], rtol=1e-6, atol=1e-7, err_msg=what)
+    return r
+
+
+@pytest.mark.parametrize("topp", [0.3, 0.85])
+def test_moe_layer_topp_small(dev, orc, topp):
+    """coli_moe_layer with top-p routing (glm.c@98759bf -- moe, phase A,
+    TOPP): the router's ragged keff feeds the grouping, the products and the
+    combine in one call; out against the oracle's block on the oracle's
+    truncated routing, intermediates and grouping included."""
+    from weight_streaming_gemv_qgemv_amd import binding as b
+    E, D, F, S, K = 24, 512, 256, 37, 6
+    bank = synth.expert_bank(42, 2, E, D, F)
+    shared = synth.shared_mlp(42, 2, D, F)
+    g = synth.rng(43, int(topp * 100))
+    Wr, bias = synth.router_weights(g, E, D)
+    Wr *= 8     # logits of a few units: the top scores spread, keff varies
+    x = synth.activations(g, S, D)
+    announce("moe layer topp small", topp)
+    out, idx, w, ws = run_layer_topp(dev, dev_bank(bank, dev), dev_bank(shared, dev), Wr, bias, x, K, topp)
+    r = check_topp_routing(orc, Wr, bias, x, K, topp, idx, w, f"topp{topp} small")
+    lay = b.moe_workspace_layout(S, K, E, D, F, F)
+    check_moe(orc, bank, shared, x, r["idx"], r["w"], out, ws, lay, f"layer topp{topp}")
+    assert b.check_device_flags(ws) == (b.OK, 0)
+
+
 def test_moe_layer_empty_batch(dev):
     import torch
     from weight_streaming_gemv_qgemv_amd import binding as b
@@ -344,3 +392,22 @@ def test_layer_decode_64_tokens(dev, orc, glm_bank):
     toks = np.sort(g.choice(S, 16, replace=False))
     ref = orc.moe(bank, shared, x[toks], r["idx"][toks], r["w"][toks])
     assert_within(out.cpu().numpy()[toks], ref["out"], ref["mag"], REL, what="layer64")
+
+
+@pytest.mark.parametrize("topp", [0.3, 0.85])
+def test_layer_decode_64_tokens_topp(dev, orc, glm_bank, topp):
+    """The 64-token layer (router N(0,0.02), bias U[-0.1,0.1], 256 int4
+    experts of 6144 x 2048, shared expert) with top-p routing: ids and keff
+    exact on all 64 tokens, out on 16 sampled tokens against the oracle's
+    block on its own truncated routing."""
+    bank, shared = glm_bank
+    g = synth.rng(3003, int(topp * 100))
+    S, K, E, D = 64, 8, 256, 6144
+    Wr, bias = synth.router_weights(g, E, D)
+    x = synth.activations(g, S, D)
+    announce("moe layer 64 tokens topp", topp)
+    out, idx, w, _ = run_layer_topp(dev, dev_bank(bank, dev), dev_bank(shared, dev), Wr, bias, x, K, topp)
+    r = check_topp_routing(orc, Wr, bias, x, K, topp, idx, w, f"topp{topp} layer64")
+    toks = np.sort(g.choice(S, 16, replace=False))
+    ref = orc.moe(bank, shared, x[toks], r["idx"][toks], r["w"][toks])
+    assert_within(out[toks], ref["out"], ref["mag"], REL, what=f"layer64 topp{topp}")
