@@ -298,11 +298,7 @@ def moe_layer(router_p: dict | None, ex: dict, shared: dict | None, x, pre_idx=N
     nb = moe_workspace_bytes(S, K, ex["E"], D, ex["F"], Fs, prec)
     if ws is None:
         ws = alloc_workspace(nb, x.device)
-    rp = RouterParams(_ptr(router_p["w"]) if router_p else None,
-                      _ptr(router_p["bias"]) if router_p else None, K,
-                      int(router_p.get("norm_topk", 1)) if router_p else 1,
-                      float(router_p.get("routed_scale", 2.5)) if router_p else 1.0,
-                      float(router_p.get("topp", 0.0)) if router_p else 0.0)
+    rp = _router_struct(router_p, K)
     es = experts_struct(ex)
     sp = C.byref(mlp_struct(shared)) if shared is not None else None
     rc = lib().coli_moe_layer(C.byref(rp), C.byref(es), sp, _ptr(x), S, _ptr(pre_idx),
