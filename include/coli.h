@@ -333,6 +333,29 @@ int coli_moe_layer_tail(const coli_router_params *r, const coli_experts *ex,
                         float *out, int32_t *idx_out, float *w_out, int prec, void *ws,
                         size_t ws_bytes, void *stream);
 
+/* coli_moe_layer for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and arguments without ws / ws_bytes.  The scratch is
+ * a static device array of COLI_NOALLOC_SCRATCH_BYTES (64 MiB) that each GPU
+ * the library runs on holds until the process ends; the call allocates
+ * nothing (no hipMalloc / hipFree, no allocating library routine).  Sizes
+ * whose coli_moe_workspace_bytes() exceeds it are refused with COLI_ERANGE
+ * before any device work (128 decode tokens of 256 experts of 6144 x 2048,
+ * K = 8, with a shared expert, need 55 MiB at COLI_PREC_FP32).  All calls on
+ * one GPU share that GPU's array, which keeps the last call's contents; every
+ * region a call reads is written earlier in the same call, so nothing needs
+ * clearing between calls.  Calls that overlap on one GPU -- on different
+ * streams, or from host threads without ordering -- race and give wrong
+ * results: the caller orders them (one stream, or events).  Bad routing ids
+ * are skipped as in coli_moe_layer, but their flags are not reported (no
+ * workspace to pass to coli_check_device_flags).
+ * Errors: as coli_moe_layer, COLI_ERANGE for a too-large size. */
+#define COLI_NOALLOC_SCRATCH_BYTES (64u << 20)
+int coli_moe_layer_noalloc(const coli_router_params *r, const coli_experts *ex,
+                           const coli_mlp *shared, const float *x, int S,
+                           const int32_t *pre_idx, const float *pre_w, float *out,
+                           int32_t *idx_out, float *w_out, int prec, void *stream);
+
 /* Waits for `stream`, then reads the workspace flags the last MoE call on it
  * left.  *flags_out (host, may be NULL) receives the raw bits.  Returns
  * COLI_OK when none is set, COLI_EIDX when a routing id was skipped or

@@ -162,6 +162,19 @@ def test_moe_refuses_sizes_past_32bit_offsets(L):
     assert L.coli_moe_gemv(C.byref(big), FAKE, 1, 2, FAKE, FAKE, FAKE, 0, FAKE, need - 1, None) == b.ERANGE
 
 
+def test_noalloc_layer_refuses_before_any_device_call(L):
+    """coli_moe_layer_noalloc: a workspace past its static scratch is refused
+    (COLI_ERANGE) before the device is touched, and NULL structs are EINVAL."""
+    from weight_streaming_gemv_qgemv_amd import binding as b
+    ex = b.Experts(2, 256, 6144, 2048, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    rp = b.RouterParams(FAKE, FAKE, 8, 1, 2.5, 0.0)
+    f = L.coli_moe_layer_noalloc
+    assert f(C.byref(rp), C.byref(ex), None, FAKE, 300, None, None, FAKE, None, None, 0, None) == b.ERANGE
+    assert f(None, C.byref(ex), None, FAKE, 4, None, None, FAKE, None, None, 0, None) == b.EINVAL
+    assert f(C.byref(rp), None, None, FAKE, 4, None, None, FAKE, None, None, 0, None) == b.EINVAL
+    assert f(C.byref(rp), C.byref(ex), None, FAKE, 0, None, None, FAKE, None, None, 0, None) == b.OK
+
+
 def test_workspace_layout_is_consistent(L):
     from weight_streaming_gemv_qgemv_amd import binding as b
     for (S, K, E, D, F, Fs) in [(1, 1, 1, 1, 1, 0), (64, 8, 256, 6144, 2048, 2048),

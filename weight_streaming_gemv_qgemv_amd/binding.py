@@ -54,7 +54,7 @@ EXPORTS = ["coli_row_bytes", "coli_qgemv", "coli_router", "coli_router_workspace
            "coli_moe_workspace_bytes", "coli_moe_workspace_layout", "coli_moe_gemv",
            "coli_moe_layer", "coli_moe_layer_tail", "coli_qgemv_idot", "coli_qgemv_grouped",
            "coli_qgemv_idot_workspace_bytes", "coli_check_device_flags", "coli_strerror", "coli_version",
-           "coli_stage_timing", "coli_stage_times", "coli_stage_name"]
+           "coli_stage_timing", "coli_stage_times", "coli_stage_name", "coli_moe_layer_noalloc"]
 NSTAGES = 8
 
 _lib = None
@@ -87,6 +87,9 @@ def lib():
         L.coli_moe_layer.restype = i32
         L.coli_moe_layer.argtypes = [C.POINTER(RouterParams), C.POINTER(Experts), C.POINTER(Mlp),
                                      vp, i32, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+        L.coli_moe_layer_noalloc.restype = i32
+        L.coli_moe_layer_noalloc.argtypes = [C.POINTER(RouterParams), C.POINTER(Experts), C.POINTER(Mlp),
+                                             vp, i32, vp, vp, vp, vp, vp, i32, vp]
         L.coli_qgemv_grouped.restype = i32
         L.coli_qgemv_grouped.argtypes = [vp, vp, i32, vp, vp, i32, i32, i32, vp]
         L.coli_qgemv_idot_workspace_bytes.restype = sz
@@ -306,6 +309,22 @@ def moe_layer(router_p: dict | None, ex: dict, shared: dict | None, x, pre_idx=N
                               _ptr(ws), ws.numel(), _stream(stream))
     _check(rc, "coli_moe_layer")
     return out, ws
+
+
+def moe_layer_noalloc(router_p: dict | None, ex: dict, shared: dict | None, x, out, pre_idx=None,
+                      pre_w=None, idx_out=None, w_out=None, prec=PREC_FP32, K=None, stream=None) -> int:
+    """coli_moe_layer on the library's static scratch: the caller passes every
+    input and output (out included); nothing is allocated.  Returns the
+    status code."""
+    S = x.shape[0]
+    if K is None:
+        K = router_p["K"] if router_p else pre_idx.shape[1]
+    rp = _router_struct(router_p, K)
+    es = experts_struct(ex)
+    sp = C.byref(mlp_struct(shared)) if shared is not None else None
+    return int(lib().coli_moe_layer_noalloc(C.byref(rp), C.byref(es), sp, _ptr(x), S, _ptr(pre_idx),
+                                            _ptr(pre_w), _ptr(out), _ptr(idx_out), _ptr(w_out), prec,
+                                            _stream(stream)))
 
 
 def stage_timing(enable: bool) -> None:

@@ -10,6 +10,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "coli.h"
 #include "coli_dec.h"
 #include "coli_device.h"
@@ -1068,6 +1070,55 @@ extern "C" int coli_moe_layer(const coli_router_params *r, const coli_experts *e
 {
     return moe_layer_impl(r, ex, shared, x, S, pre_idx, pre_w, out, idx_out, w_out, prec, ws, ws_bytes,
                           stream, nullptr, 0.f);
+}
+
+// ---------------------------------------------------------------- no allocation
+// The MoE layer for callers that cannot allocate: its scratch is one static
+// device array, which every GPU the library runs on holds (at its own
+// address) until the process ends.  Host code never passes the array's name
+// to a kernel (on the host it is only a stand-in for the symbol): the device
+// address is looked up once per device with hipGetSymbolAddress and kept.
+static __device__ __align__(256) uint8_t scratch[COLI_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<uintptr_t> g_scratch_ptr[kMaxDevices];
+
+// The current device's copy of `scratch` (looked up on the first call made
+// with that device current).
+int scratch_ptr(void **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return COLI_EDEVICE;
+    if (dev < 0 || dev >= kMaxDevices) return COLI_EDEVICE;
+    uintptr_t p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return COLI_EDEVICE;
+        p = (uintptr_t)ptr;
+        g_scratch_ptr[dev].store(p, std::memory_order_release);   // same value from any racing caller
+    }
+    *out = (void *)p;
+    return COLI_OK;
+}
+}  // namespace
+
+extern "C" int coli_moe_layer_noalloc(const coli_router_params *r, const coli_experts *ex,
+                                      const coli_mlp *shared, const float *x, int S,
+                                      const int32_t *pre_idx, const float *pre_w, float *out,
+                                      int32_t *idx_out, float *w_out, int prec, void *stream)
+{
+    if (!r || !ex) return COLI_EINVAL;
+    const size_t need = coli_moe_workspace_bytes(S, r->K, ex->E, ex->D, ex->F, shared ? shared->F : 0, prec);
+    if (need > (size_t)COLI_NOALLOC_SCRATCH_BYTES) return COLI_ERANGE;   // before any device call
+    if (need == 0 || S == 0)   // invalid sizes or an empty batch: the ordinary checks answer
+        return moe_layer_impl(r, ex, shared, x, S, pre_idx, pre_w, out, idx_out, w_out, prec, nullptr, 0,
+                              stream, nullptr, 0.f);
+    void *ws = nullptr;
+    const int rc = scratch_ptr(&ws);
+    if (rc != COLI_OK) return rc;
+    return moe_layer_impl(r, ex, shared, x, S, pre_idx, pre_w, out, idx_out, w_out, prec, ws, need, stream,
+                          nullptr, 0.f);
 }
 
 extern "C" int coli_moe_layer_tail(const coli_router_params *r, const coli_experts *ex,
