@@ -61,6 +61,22 @@ def bank_to_dev(bank, dev):
     return out
 
 
+def apply_layout(args, banks, shared=None, D=6144):
+    """The expert banks (and shared experts) in the layout asked for: with
+    --layout tiled each is repacked once on the device (coli_pack_tiled, a
+    load-time step outside the timed region) and the row-major copy freed."""
+    import torch
+    from weight_streaming_gemv_qgemv_amd import binding as b
+    if getattr(args, "layout", "rows") != "tiled":
+        return banks, shared
+    banks = [b.tile_mlps(bk) for bk in banks]
+    if shared is not None:
+        shared = [b.tile_mlps(sh, D) for sh in shared]
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return banks, shared
+
+
 def clone_bank(bd):
     out = dict(bd)
     for k in ("wg", "wu", "wd", "sg", "su", "sd"):
@@ -91,13 +107,39 @@ def recorded_traffic(workload, kernel_key):
     return None if k is None else int(k["fetch_bytes"] + k["write_bytes"])
 
 
-def time_steps(step, steps, warmup):
+REPS = 20
+
+
+RAMP_S = 0.25
+
+
+def clock_ramp(step, seconds):
+    """Untimed steps, back to back, for `seconds` of wall time before the
+    warm-up: after the host-side setup the GPU starts from a low clock, and
+    the first tens of milliseconds of work run ~9% slower.  Returns the steps
+    it ran."""
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            step(n)
+            n += 1
+        torch.cuda.synchronize()
+    return n
+
+
+def time_steps(step, steps, warmup, reps=REPS):
     """Warm up, then time exactly `steps` steps between two synchronisations
-    (stage events off).  A second pass of `steps` steps records a HIP event
-    pair around every stage on the stream the kernels run on; it gives the
-    per-kernel durations used for the roofline and the stage breakdown."""
+    (stage events off): the reported step time.  Then `reps` more blocks of
+    `steps` steps, each between its own event pair, give the median and the
+    minimum step time over repetitions.  A last pass of `steps` steps records
+    a HIP event pair around every stage on the stream the kernels run on; it
+    gives the per-kernel durations used for the roofline and the stage
+    breakdown."""
     import torch
     from weight_streaming_gemv_qgemv_amd import binding as b
+    ramp_steps = clock_ramp(step, RAMP_S)
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
@@ -111,30 +153,48 @@ def time_steps(step, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms = t0.elapsed_time(t1) / steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    n = warmup + steps
+    for r in range(reps):
+        for i in range(steps):
+            step(n)
+            n += 1
+        ev[r + 1].record()
+    torch.cuda.synchronize()
+    per = sorted(ev[r].elapsed_time(ev[r + 1]) / steps for r in range(reps))
+    rep_stats = dict(reps=reps, steps_per_rep=steps, ms_per_step_median=float(np.median(per)),
+                     ms_per_step_min=per[0], ms_per_step_max=per[-1],
+                     clock_ramp_s=RAMP_S, clock_ramp_steps=ramp_steps)
     b.stage_times(reset=True)
     b.stage_timing(True)
     s0 = torch.cuda.Event(enable_timing=True)
     s1 = torch.cuda.Event(enable_timing=True)
     s0.record()
     for i in range(steps):
-        step(warmup + steps + i)
+        step(n + i)
     s1.record()
     torch.cuda.synchronize()
     b.stage_timing(False)
     stages = b.stage_times(reset=True)
     stages["_step_ms_with_stage_events"] = (s0.elapsed_time(s1), steps)
+    stages["_reps"] = rep_stats
     return ms, wall, stages
 
 
-def cpu_baseline_layer(bank, shared, Wr, bias, x, K, ntok):
-    """The oracle as it stands, on the first `ntok` tokens of the same input."""
+def cpu_baseline_layer(bank, shared, Wr, bias, x, K, ntok, runs=1):
+    """The oracle as it stands, on the first `ntok` tokens of the same input:
+    the median wall time over `runs` runs (clock_gettime through
+    time.perf_counter), and the routing it took."""
     from oracle import oracle
     xs = x[:ntok]
-    t0 = time.perf_counter()
-    r = oracle.router(Wr, bias, xs, K, 1, 2.5)
-    oracle.moe(bank, shared, xs, r["idx"], r["w"])
-    dt = time.perf_counter() - t0
-    return dt, r["idx"]
+    times = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        r = oracle.router(Wr, bias, xs, K, 1, 2.5)
+        oracle.moe(bank, shared, xs, r["idx"], r["w"])
+        times.append(time.perf_counter() - t0)
+    return float(np.median(times)), r["idx"]
 
 
 def host_info():
@@ -190,6 +250,7 @@ def run_layer64(args, dev, tail=False):
     banks.append(clone_bank(banks[0]))
     sd = [bank_to_dev(shared, dev)]
     sd.append(clone_bank(sd[0]))
+    banks, sd = apply_layout(args, banks, sd, D)
     rp = dict(w=to_dev(Wr, dev), bias=to_dev(bias, dev), K=K, norm_topk=1, routed_scale=2.5)
     xd = to_dev(x, dev)
     out = torch.empty((S, D), dtype=torch.float32, device=dev)
@@ -227,24 +288,25 @@ def run_layer64(args, dev, tail=False):
     if not args.no_cpu_baseline and not tail:
         ntok = args.cpu_tokens
         log(f"cpu baseline: oracle on {ntok} tokens")
-        dt, sidx = cpu_baseline_layer(bank, shared, Wr, bias, x, K, ntok)
+        dt, sidx = cpu_baseline_layer(bank, shared, Wr, bias, x, K, ntok, runs=args.cpu_runs)
         su = int(np.unique(sidx).size)
         sb = (E * D * 4 + E * 4) + ntok * D * 4 + su * (gu + dn) + (gu + dn) + ntok * D * 4
         from oracle import oracle
         res["cpu"] = dict(value=sb / dt / 1e9, unit="GB/s", cores=oracle.num_threads(),
                           kind="oracle",
                           sample=f"router + MoE layer on the first {ntok} of the 64 tokens "
-                                 f"({su} unique experts), {dt:.2f} s",
+                                 f"({su} unique experts), median of {args.cpu_runs} runs, {dt:.2f} s each",
                           tokens_per_s=ntok / dt, seconds=dt)
         n1 = min(args.cpu_tokens_1t, ntok)
         if n1 > 0:
             log(f"cpu baseline: oracle on {n1} tokens, one thread")
-            dt1, (_, idx1) = single_thread(lambda: cpu_baseline_layer(bank, shared, Wr, bias, x, K, n1))
+            _, (dt1, idx1) = single_thread(lambda: cpu_baseline_layer(bank, shared, Wr, bias, x, K, n1,
+                                                                      runs=3))
             u1 = int(np.unique(idx1).size)
             sb1 = (E * D * 4 + E * 4) + n1 * D * 4 + u1 * (gu + dn) + (gu + dn) + n1 * D * 4
             res["cpu"]["single_thread"] = dict(
                 value=sb1 / dt1 / 1e9, tokens_per_s=n1 / dt1, seconds=dt1,
-                sample=f"router + MoE layer on the first {n1} tokens ({u1} unique experts)")
+                sample=f"router + MoE layer on the first {n1} tokens ({u1} unique experts), median of 3 runs")
     return res
 
 
@@ -277,6 +339,7 @@ def run_prefill2048(args, dev):
     x = synth.activations(g, S, D)
     idx, w = synth.routing_zipf(g, S, K, E)
     bd, sd = bank_to_dev(bank, dev), bank_to_dev(shared, dev)
+    (bd,), (sd,) = apply_layout(args, [bd], [sd], D)
     xd, idd, wd = to_dev(x, dev), to_dev(idx, dev), to_dev(w, dev)
     Wrd, bd_bias = to_dev(Wr, dev), to_dev(bias, dev)
     out = torch.empty((S, D), dtype=torch.float32, device=dev)
@@ -351,6 +414,7 @@ def run_ep_slice(args, dev, prefill):
     banks.append(clone_bank(banks[0]))
     sd = [bank_to_dev(shared, dev)]
     sd.append(clone_bank(sd[0]))
+    banks, sd = apply_layout(args, banks, sd, D)
     idd, wd = to_dev(idl, dev), to_dev(wl, dev)
     prec = 1 if prefill else 0
     out = torch.empty((S, D), dtype=torch.float32, device=dev)
@@ -394,6 +458,7 @@ def run_decode16(args, dev):
     idx, w = synth.routing_uniform(g, S, K, E)
     banks = [bank_to_dev(bank, dev)]
     banks.append(clone_bank(banks[0]))
+    banks, _ = apply_layout(args, banks)
     xd, idd, wd = to_dev(x, dev), to_dev(idx, dev), to_dev(w, dev)
     out = torch.empty((S, D), dtype=torch.float32, device=dev)
     ws = b.alloc_workspace(b.moe_workspace_bytes(S, K, E, D, F), dev)
@@ -522,9 +587,15 @@ def main():
                     help="layer64 / prefill2048: time one GPU's share under expert parallelism "
                          "over N GPUs (256/N local experts; the slice with the most routed rows, "
                          "with the shared expert)")
+    ap.add_argument("--layout", default="tiled", choices=["rows", "tiled"],
+                    help="expert weight layout: the tiled copy the library reads fastest "
+                         "(coli_pack_tiled, made once at load time, outside the timed steps), "
+                         "or the pages' row-major rows as given")
     ap.add_argument("--cpu-tokens", type=int, default=64)
-    ap.add_argument("--cpu-tokens-1t", type=int, default=8,
+    ap.add_argument("--cpu-tokens-1t", type=int, default=4,
                     help="tokens of the one-thread oracle timing (0 skips it)")
+    ap.add_argument("--cpu-runs", type=int, default=5,
+                    help="runs of the oracle timing; the median is reported")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build measures the per-GPU share of the "
@@ -563,7 +634,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": f"f32 ({r.get('weight_format', 'int4').split()[0]} weights)",
+        "dtype": ("fp32 (vector ALUs, fp32 weights)" if r.get("weight_format") == "fp32" else
+                  f"fp32 activations as bf16 hi+lo pairs on the bf16 matrix cores, fp32 accumulate "
+                  f"({r.get('weight_format', 'int4').split()[0]} weights as exact bf16 codes)"),
         "data": "synthetic",
         "config": ({"workload": r["workload"], "tokens_per_step": r["tokens"],
                     "experts": r.get("experts", 256),
@@ -577,7 +650,9 @@ def main():
                     "algorithmic_bytes_per_step": r["step_bytes"]}),
         "tokens_per_s": round(r["tokens"] / (ms * 1e-3), 1),
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
-        "stage_ms_per_step": {k: round(v[0] / max(v[1], 1), 5) for k, v in r["stages"].items() if v[1]},
+        "stage_ms_per_step": {k: round(v[0] / max(v[1], 1), 5) for k, v in r["stages"].items()
+                              if not k.startswith("_reps") and v[1]},
+        "timing": {k: (round(v, 5) if isinstance(v, float) else v) for k, v in r["stages"]["_reps"].items()},
         "roofline": {"bound": "hbm", "achieved": round(ach, 2) if ach else None,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(ach / HBM_PEAK_GBS, 4) if ach else None,
@@ -588,6 +663,8 @@ def main():
     }
     if "ep" in r:
         line["config"]["expert_parallel_share"] = r["ep"]
+    if r["uniq"] is not None:
+        line["config"]["weight_layout"] = args.layout
     if "flops" in r:
         # prefill: the matrix cores bound the dominant kernel
         tf = dom["flops_per_launch"] / (dom["ms_per_launch"] * 1e-3) / 1e12 if dom["ms_per_launch"] else None

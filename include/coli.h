@@ -175,28 +175,70 @@ int coli_router(const float *Wr, const float *bias, const float *x, int S,
  * invalid arguments).  Host only. */
 size_t coli_router_workspace_bytes(int S, int E, int D);
 
+/* Weight layouts of the MoE tensors.
+ *   COLI_LAYOUT_ROWS  : the pages' row-major packed rows, [O, coli_row_bytes]
+ *                       per matrix.
+ *   COLI_LAYOUT_TILED : the same bytes regrouped by coli_pack_tiled() so that
+ *                       the matrix cores read each weight chunk with one
+ *                       contiguous 1 KB load per wave (see there). */
+enum coli_layout { COLI_LAYOUT_ROWS = 0, COLI_LAYOUT_TILED = 1 };
+
+/* Bytes of the tiled copy of `count` stacked [O, I] matrices of format fmt
+ * (COLI_I8 / I4 / I2), or -1 for invalid arguments.  It is count * ceil(O /
+ * 16) * ceil(coli_row_bytes(fmt, I) / 64) * 1024, equal to the row-major size
+ * when O is a multiple of 16 and a row a multiple of 64 bytes.  Host only. */
+int64_t coli_tiled_bytes(int fmt, int64_t count, int O, int I);
+
+/* Writes the tiled layout of `count` stacked row-major matrices W [count, O,
+ * coli_row_bytes(fmt, I)] into dst [coli_tiled_bytes(fmt, count, O, I)] --
+ * caller memory, 16-byte aligned, not overlapping W; nothing is allocated.
+ * The values are the pages' row formats unchanged [glm.c@98759bf -- typedef
+ * QT, pack_int4, pack_int2]; only their order in memory changes.  A matrix is
+ * cut into units of 16 rows x 64 bytes (1 KB): unit (m, g) holds rows 16m ..
+ * 16m+15, bytes 64g .. 64g+63 of each, and inside it bytes 16L .. 16L+15,
+ * L = 16q + c (q < 4, c < 16), are row 16m+c's bytes 64g+16q .. +15 -- the
+ * order in which a 64-lane wave feeds 16 rows to the bf16 matrix-core
+ * operand.  Units are ordered by groups of 8 row tiles (128 rows; the last
+ * group may hold fewer), inside a group by segment g, then by row tile:
+ * offset (1024 *) (8 T NS + g n_T + m mod 8), T = m / 8, NS = ceil(rb / 64),
+ * n_T = min(8, ceil(O/16) - 8 T).  Bytes past a row's end and rows past O
+ * are zero.  Each matrix's tiled bytes follow the previous one's.
+ * W needs whole 16-byte row segments (coli_row_bytes(fmt, I) % 16 == 0) and
+ * 16-byte alignment.  Asynchronous on `stream`.
+ * Errors: COLI_EFMT, COLI_EINVAL (NULL), COLI_ESHAPE, COLI_EALIGN,
+ * COLI_EDEVICE. */
+int coli_pack_tiled(int fmt, const void *W, int64_t count, int O, int I, void *dst, void *stream);
+
 /* Routed experts stacked in one allocation per tensor
  * [glm.c@98759bf -- typedef ESlot; metal@93cde63 -- moe_submit]:
  *   w_gate, w_up  [E, F, coli_row_bytes(fmt, D)] bytes,
  *   w_down        [E, D, coli_row_bytes(fmt, F)] bytes,
  *   s_gate, s_up  [E, F] fp32,   s_down [E, D] fp32.
- * fmt is one of COLI_I8 / I4 / I2 (all three tensors share it). */
+ * fmt is one of COLI_I8 / I4 / I2 (all three tensors share it).
+ * layout COLI_LAYOUT_ROWS (0), or COLI_LAYOUT_TILED: then each weight tensor
+ * is the coli_pack_tiled() copy of the stack above (w_gate of E matrices
+ * [F, D], w_down of E matrices [D, F]), 16-byte aligned, with whole 16-byte
+ * row segments (rows of D and of F). */
 typedef struct {
     int fmt;
     int E, D, F;
     const void *w_gate, *w_up, *w_down;
     const float *s_gate, *s_up, *s_down;
+    int layout;
 } coli_experts;
 
 /* One SwiGLU MLP applied with weight 1 to every token: the shared expert
  * [glm.c@98759bf -- moe, phase E; dense_mlp]:  down(silu(gate x) * up x).
  *   w_gate, w_up [F, coli_row_bytes(fmt, D)], w_down [D, coli_row_bytes(fmt, F)],
- *   s_gate, s_up [F], s_down [D].  D is the experts' D. */
+ *   s_gate, s_up [F], s_down [D].  D is the experts' D.
+ *   layout as coli_experts (one matrix each); a tiled shared expert needs
+ *   tiled routed experts of the same fmt and F. */
 typedef struct {
     int fmt;
     int F;
     const void *w_gate, *w_up, *w_down;
     const float *s_gate, *s_up, *s_down;
+    int layout;
 } coli_mlp;
 
 /* Router parameters for coli_moe_layer (see coli_router).  E and D are the

@@ -175,6 +175,40 @@ def test_noalloc_layer_refuses_before_any_device_call(L):
     assert f(C.byref(rp), C.byref(ex), None, FAKE, 0, None, None, FAKE, None, None, 0, None) == b.OK
 
 
+def test_tiled_layout_host_checks(L):
+    """coli_tiled_bytes and the refusals of coli_pack_tiled / tiled experts
+    (no device work)."""
+    from weight_streaming_gemv_qgemv_amd import binding as b
+    assert b.tiled_bytes(2, 256, 2048, 6144) == 256 * 2048 * 3072      # whole units: no padding
+    assert b.tiled_bytes(2, 1, 17, 96) == 2 * 1 * 1024                  # 2 row tiles x 1 segment
+    assert b.tiled_bytes(1, 3, 40, 160) == 3 * 3 * 3 * 1024
+    assert b.tiled_bytes(0, 1, 16, 64) == -1 and b.tiled_bytes(2, -1, 16, 64) == -1
+    p = L.coli_pack_tiled
+    assert p(0, FAKE, 1, 16, 64, FAKE, None) == b.EFMT
+    assert p(2, FAKE, 1, 16, 40, FAKE, None) == b.EALIGN      # 20-byte rows
+    assert p(2, FAKE + 4, 1, 16, 64, FAKE, None) == b.EALIGN
+    assert p(2, None, 1, 16, 64, FAKE, None) == b.EINVAL
+    assert p(2, FAKE, -1, 16, 64, FAKE, None) == b.ESHAPE
+    assert p(2, FAKE, 0, 16, 64, FAKE, None) == b.OK            # nothing to pack
+    E, D, F, S, K = 8, 64, 32, 4, 2
+    need = b.moe_workspace_bytes(S, K, E, D, F, F, 0)
+
+    def layer(ex, sh):
+        return L.coli_moe_layer(C.byref(b.RouterParams(FAKE, FAKE, K, 1, 2.5, 0.0)), C.byref(ex),
+                                C.byref(sh) if sh else None, FAKE, S, FAKE, FAKE, FAKE, None, None, 0,
+                                FAKE, need - 1, None)
+    rows = b.Experts(2, E, D, F, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0)
+    tiled = b.Experts(2, E, D, F, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1)
+    sh_t = b.Mlp(2, F, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1)
+    sh_r = b.Mlp(2, F, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0)
+    assert layer(tiled, sh_t) == b.EWORKSPACE                  # valid up to the workspace
+    assert layer(tiled, sh_r) == b.EWORKSPACE                  # row-major shared: vector ALUs
+    assert layer(rows, sh_t) == b.EINVAL                       # tiled shared needs tiled experts
+    assert layer(b.Experts(2, E, D, F, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 7), None) == b.EINVAL
+    odd = b.Experts(2, E, 40, F, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1)   # 20-byte rows of D
+    assert layer(odd, None) == b.EALIGN
+
+
 def test_workspace_layout_is_consistent(L):
     from weight_streaming_gemv_qgemv_amd import binding as b
     for (S, K, E, D, F, Fs) in [(1, 1, 1, 1, 1, 0), (64, 8, 256, 6144, 2048, 2048),

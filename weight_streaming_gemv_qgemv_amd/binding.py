@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_PKG, "libcoli.so")
 
 F32, I8, I4, I2 = 0, 1, 2, 3
 PREC_FP32, PREC_BF16 = 0, 1
+LAYOUT_ROWS, LAYOUT_TILED = 0, 1
 OK, EINVAL, ESHAPE, EFMT, EALIGN, ERANGE, EWORKSPACE, EDEVICE, EIDX = 0, -1, -2, -3, -4, -5, -6, -7, -8
 
 
@@ -29,13 +30,15 @@ class ColiError(RuntimeError):
 class Experts(C.Structure):
     _fields_ = [("fmt", C.c_int), ("E", C.c_int), ("D", C.c_int), ("F", C.c_int),
                 ("w_gate", C.c_void_p), ("w_up", C.c_void_p), ("w_down", C.c_void_p),
-                ("s_gate", C.c_void_p), ("s_up", C.c_void_p), ("s_down", C.c_void_p)]
+                ("s_gate", C.c_void_p), ("s_up", C.c_void_p), ("s_down", C.c_void_p),
+                ("layout", C.c_int)]
 
 
 class Mlp(C.Structure):
     _fields_ = [("fmt", C.c_int), ("F", C.c_int),
                 ("w_gate", C.c_void_p), ("w_up", C.c_void_p), ("w_down", C.c_void_p),
-                ("s_gate", C.c_void_p), ("s_up", C.c_void_p), ("s_down", C.c_void_p)]
+                ("s_gate", C.c_void_p), ("s_up", C.c_void_p), ("s_down", C.c_void_p),
+                ("layout", C.c_int)]
 
 
 class RouterParams(C.Structure):
@@ -54,7 +57,8 @@ EXPORTS = ["coli_row_bytes", "coli_qgemv", "coli_router", "coli_router_workspace
            "coli_moe_workspace_bytes", "coli_moe_workspace_layout", "coli_moe_gemv",
            "coli_moe_layer", "coli_moe_layer_tail", "coli_qgemv_idot", "coli_qgemv_grouped",
            "coli_qgemv_idot_workspace_bytes", "coli_check_device_flags", "coli_strerror", "coli_version",
-           "coli_stage_timing", "coli_stage_times", "coli_stage_name", "coli_moe_layer_noalloc"]
+           "coli_stage_timing", "coli_stage_times", "coli_stage_name", "coli_moe_layer_noalloc",
+           "coli_tiled_bytes", "coli_pack_tiled"]
 NSTAGES = 8
 
 _lib = None
@@ -87,6 +91,10 @@ def lib():
         L.coli_moe_layer.restype = i32
         L.coli_moe_layer.argtypes = [C.POINTER(RouterParams), C.POINTER(Experts), C.POINTER(Mlp),
                                      vp, i32, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+        L.coli_tiled_bytes.restype = i64
+        L.coli_tiled_bytes.argtypes = [i32, i64, i32, i32]
+        L.coli_pack_tiled.restype = i32
+        L.coli_pack_tiled.argtypes = [i32, vp, i64, i32, i32, vp, vp]
         L.coli_moe_layer_noalloc.restype = i32
         L.coli_moe_layer_noalloc.argtypes = [C.POINTER(RouterParams), C.POINTER(Experts), C.POINTER(Mlp),
                                              vp, i32, vp, vp, vp, vp, vp, i32, vp]
@@ -219,12 +227,46 @@ def router(Wr, bias, x, K: int, norm_topk: int = 1, routed_scale: float = 2.5, t
 # ------------------------------------------------------------------ MoE
 def experts_struct(ex: dict) -> Experts:
     return Experts(ex["fmt"], ex["E"], ex["D"], ex["F"], _ptr(ex["wg"]), _ptr(ex["wu"]),
-                   _ptr(ex["wd"]), _ptr(ex["sg"]), _ptr(ex["su"]), _ptr(ex["sd"]))
+                   _ptr(ex["wd"]), _ptr(ex["sg"]), _ptr(ex["su"]), _ptr(ex["sd"]),
+                   int(ex.get("layout", LAYOUT_ROWS)))
 
 
 def mlp_struct(sh: dict) -> Mlp:
     return Mlp(sh["fmt"], sh["F"], _ptr(sh["wg"]), _ptr(sh["wu"]), _ptr(sh["wd"]),
-               _ptr(sh["sg"]), _ptr(sh["su"]), _ptr(sh["sd"]))
+               _ptr(sh["sg"]), _ptr(sh["su"]), _ptr(sh["sd"]), int(sh.get("layout", LAYOUT_ROWS)))
+
+
+# ------------------------------------------------------------------ tiled layout
+def tiled_bytes(fmt: int, count: int, O: int, I: int) -> int:
+    return int(lib().coli_tiled_bytes(fmt, count, O, I))
+
+
+def pack_tiled(fmt: int, W: torch.Tensor, count: int, O: int, I: int, dst: torch.Tensor | None = None,
+               stream=None) -> torch.Tensor:
+    """The tiled copy of `count` stacked row-major [O, I] matrices (uint8)."""
+    nb = tiled_bytes(fmt, count, O, I)
+    if nb < 0:
+        raise ColiError(ESHAPE, "coli_tiled_bytes")
+    if dst is None:
+        dst = torch.empty((max(nb, 16),), dtype=torch.uint8, device=W.device)
+    rc = lib().coli_pack_tiled(fmt, _ptr(W), count, O, I, _ptr(dst), _stream(stream))
+    _check(rc, "coli_pack_tiled")
+    return dst
+
+
+def tile_mlps(ex: dict, D: int | None = None) -> dict:
+    """A copy of an experts dict (stacked E experts) or of a shared-expert
+    dict (one matrix each; pass the width D) with its weights in the tiled
+    layout; the scales are the original tensors."""
+    n = ex.get("E", 1)
+    D = ex["D"] if D is None else D
+    F = ex["F"]
+    out = dict(ex)
+    out["wg"] = pack_tiled(ex["fmt"], ex["wg"], n, F, D)
+    out["wu"] = pack_tiled(ex["fmt"], ex["wu"], n, F, D)
+    out["wd"] = pack_tiled(ex["fmt"], ex["wd"], n, D, F)
+    out["layout"] = LAYOUT_TILED
+    return out
 
 
 def moe_workspace_bytes(S, K, E, D, F, F_shared=0, prec=PREC_FP32) -> int:

@@ -19,7 +19,8 @@ INC = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libcoli.so")
 BUILD = os.path.join(ROOT, "_build")
 
-HIP_SOURCES = ["coli_gemv.hip", "coli_dec.hip", "coli_pre.hip", "coli_qmv.hip", "coli_idot.hip", "coli_router.hip", "coli_api.hip", "coli_stages.hip"]
+HIP_SOURCES = ["coli_gemv.hip", "coli_dec.hip", "coli_pre.hip", "coli_qmv.hip", "coli_idot.hip", "coli_router.hip", "coli_api.hip", "coli_stages.hip",
+               "coli_tiled.hip"]
 C_SOURCES = ["coli_validate.c"]
 
 ARCH = os.environ.get("COLI_OFFLOAD_ARCH", "gfx950")

@@ -511,8 +511,13 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
     // matrix-core path: whole 16-byte row segments, 16-byte aligned tensors
     const bool mm = rbD % 16 == 0 && rbF % 16 == 0 && al16(ex->w_gate) && al16(ex->w_up) &&
                     al16(ex->w_down) && (ex->fmt == COLI_I8 || ex->fmt == COLI_I4 || ex->fmt == COLI_I2);
-    const bool sh_mm = mm && sh && sh->fmt == ex->fmt && sh->F == F && al16(sh->w_gate) &&
-                       al16(sh->w_up) && al16(sh->w_down);
+    const bool sh_mm = mm && sh && sh->fmt == ex->fmt && sh->F == F && sh->layout == ex->layout &&
+                       al16(sh->w_gate) && al16(sh->w_up) && al16(sh->w_down);
+    // tiled weights: matrix cores only (the host checks guarantee mm)
+    const int tiled = ex->layout == COLI_LAYOUT_TILED ? 1 : 0;
+    if (tiled && !mm) return COLI_EALIGN;
+    const int64_t gstrD = tiled ? coli_tiled_bytes(ex->fmt, 1, F, D) : (int64_t)F * rbD;   // gate, up
+    const int64_t gstrF = tiled ? coli_tiled_bytes(ex->fmt, 1, D, F) : (int64_t)D * rbF;   // down
     // matrix-core passes: 16 rows as bf16 hi/lo column pairs (fp32-level
     // accuracy) or 64 rows rounded once to bf16
     const int bf16 = prec == COLI_PREC_BF16 ? 1 : 0;
@@ -573,7 +578,8 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
             a.w[1] = (const uint8_t *)ex->w_up;
             a.s[0] = ex->s_gate;
             a.s[1] = ex->s_up;
-            a.w_gstride = (int64_t)F * rbD;
+            a.w_gstride = gstrD;
+            a.tiled = tiled;
             a.s_gstride = F;
             a.ngroups = E;
             a.O = F;
@@ -609,7 +615,8 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
             DecArgs d = {};
             d.w[0] = (const uint8_t *)ex->w_down;
             d.s[0] = ex->s_down;
-            d.w_gstride = (int64_t)D * rbF;
+            d.w_gstride = gstrF;
+            d.tiled = tiled;
             d.s_gstride = D;
             d.ngroups = E;
             d.O = D;
@@ -671,7 +678,8 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
             a.w[1] = (const uint8_t *)ex->w_up;
             a.s[0] = ex->s_gate;
             a.s[1] = ex->s_up;
-            a.w_gstride = (int64_t)F * rbD;
+            a.w_gstride = gstrD;
+            a.tiled = tiled;
             a.s_gstride = F;
             a.ngroups = E;
             a.O = F;
@@ -708,7 +716,8 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
             PreArgs d = {};
             d.w[0] = (const uint8_t *)ex->w_down;
             d.s[0] = ex->s_down;
-            d.w_gstride = (int64_t)D * rbF;
+            d.w_gstride = gstrF;
+            d.tiled = tiled;
             d.s_gstride = D;
             d.ngroups = E;
             d.O = D;

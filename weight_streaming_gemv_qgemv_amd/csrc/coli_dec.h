@@ -48,6 +48,8 @@ struct DecArgs {
     // (rows = grouped rows, kpad = hf_kpad, same weight format)
     uint16_t *hf;
     int hf_kpad;
+    int tiled;               // weights in the tiled layout (coli_pack_tiled); w_gstride
+                             // is then the tiled bytes of one matrix
     int tiles;               // set by dec_launch
 };
 

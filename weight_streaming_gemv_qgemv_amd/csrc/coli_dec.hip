@@ -68,7 +68,7 @@ __device__ __forceinline__ void dma16(const void *g, uint32_t lds)
 
 typedef __attribute__((address_space(3))) const void lds_void;
 
-template <int FMT, int M>
+template <int FMT, int M, bool TILED>
 __global__ __launch_bounds__(256) void k_dec(DecArgs a)
 {
     using T = MF<FMT>;
@@ -95,9 +95,10 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
     //   streams the same share of every matrix.
     // (each measured faster for its kernel on the 64-token layer)
     const int n_gp = cload(a.n_work);
-    const int gp_lo = M == 2 ? (int)((int64_t)n_gp * xcd / kDecXcds) : 0;
-    const int gp_cnt = M == 2 ? (int)((int64_t)n_gp * (xcd + 1) / kDecXcds) - gp_lo : n_gp;
-    const int tpx = M == 2 ? a.tiles : (a.tiles - xcd + kDecXcds - 1) / kDecXcds;   // tiles per pass here
+    constexpr bool RUNS = M == 2;
+    const int gp_lo = RUNS ? (int)((int64_t)n_gp * xcd / kDecXcds) : 0;
+    const int gp_cnt = RUNS ? (int)((int64_t)n_gp * (xcd + 1) / kDecXcds) - gp_lo : n_gp;
+    const int tpx = RUNS ? a.tiles : (a.tiles - xcd + kDecXcds - 1) / kDecXcds;   // tiles per pass here
     const int n_items = gp_cnt * tpx;
     if (lb >= n_items) return;                          // whole block, before any barrier
     const int nkb = a.kpad / KB;                        // even and >= 4 (kpad: multiple of 1024)
@@ -108,6 +109,9 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
     // row's last chunk; it too meets zero activations)
     const uint32_t coff = (uint32_t)min(16 * lchunk, (int)(a.rb - 16));
     const uint32_t last_seg = (uint32_t)(a.rb - 16) - coff;
+    // tiled layout: segments per row; a k-block past the row end reads the
+    // last segment (it meets zero activations)
+    const int ns = (int)((a.rb + 63) / 64);
     const uint8_t *actb = reinterpret_cast<const uint8_t *>(a.act);
     const uint32_t arow = (uint32_t)(4 * a.kpad);       // bytes per row-table row
     // the N-tile and the first step this wave stages
@@ -117,12 +121,14 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
         int gp, tile, nt, r0t, Og;
         const uint8_t *wb[M];
         const float *sc[M];
-        uint32_t roff[MT];   // this lane's row (clamped) * rb + its 16-byte chunk
+        uint32_t roff[MT];   // rows: this lane's row (clamped) * rb + its 16-byte chunk;
+                             // tiled: its row tile's first unit + 16 lane
+        uint32_t gstr;       // tiled: bytes from one segment's unit to the next
         uint32_t doff;       // the unit this lane stages, in its activation row (bytes)
     };
     auto make = [&](It &c, int it) {
         c.gp = __builtin_amdgcn_readfirstlane(gp_lo + it / tpx);
-        c.tile = __builtin_amdgcn_readfirstlane(M == 2 ? it % tpx : xcd + kDecXcds * (it % tpx));
+        c.tile = __builtin_amdgcn_readfirstlane(RUNS ? it % tpx : xcd + kDecXcds * (it % tpx));
         const int wv = cload(a.work + c.gp);
         const int g = wv & 0x7FF, pass = wv >> 11;
         const bool extra = a.has_extra && g == a.ngroups;
@@ -149,9 +155,20 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
             }
         }
         const int obase = c.tile * RPB + wave * RPW;
+        if constexpr (TILED) {
+            // the wave's row tiles lie in one group of the layout (a row tile
+            // past the matrix is clamped to the last one: its results are
+            // never stored)
+            const int mt16 = (c.Og + 15) / 16;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-            c.roff[mt] = (uint32_t)(min(obase + 16 * mt + lrow, c.Og - 1) * a.rb) + coff;
+            for (int mt = 0; mt < MT; ++mt) c.roff[mt] = tiled_base(min(obase / 16 + mt, mt16 - 1), ns) + 16 * lane;
+            c.gstr = __builtin_amdgcn_readfirstlane(tiled_gstride(min(obase / 16, mt16 - 1), mt16));
+        } else {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                c.roff[mt] = (uint32_t)(min(obase + 16 * mt + lrow, c.Og - 1) * a.rb) + coff;
+            c.gstr = 0;
+        }
         // activation row of the pass row whose unit this lane stages (pass
         // row 8 nw + col / 2), from scalar loads; dead rows repeat the last
         // live one (their results are never stored)
@@ -168,7 +185,24 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
         }
         c.doff = (uint32_t)ar * arow + 32 * q + 16 * (col & 1);
     };
+    // Tiled weights are loaded with the non-temporal hint: each unit is read
+    // once per pass, and keeping that stream out of L2 leaves the activation
+    // row tables, reused by every tile of a pass, resident there (64-token
+    // layer: gate/up 322 -> 301 us).  Row-major weights keep plain loads:
+    // there the two 64-byte halves of a 128-byte line come from two load
+    // instructions, which then fetch the line twice (gate/up 337 -> 411 us).
     auto loadW = [&](const It &c, int kbi, uint4 (&w)[M][MT][SEGS]) {
+        if constexpr (TILED) {
+#pragma unroll
+            for (int sg = 0; sg < SEGS; ++sg) {
+                const uint32_t go = (uint32_t)min(kbi * SEGS + sg, ns - 1) * c.gstr;
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) w[m][mt][sg] = gload16_nt(c.wb[m] + (c.roff[mt] + go));
+            }
+            return;
+        }
         const uint32_t b0 = (uint32_t)kbi * kbytes;
 #pragma unroll
         for (int m = 0; m < M; ++m)
@@ -177,6 +211,34 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
 #pragma unroll
                 for (int sg = 0; sg < SEGS; ++sg)
                     w[m][mt][sg] = gload16(c.wb[m] + (c.roff[mt] + min(b0 + 64 * sg, last_seg)));
+    };
+    // tiled layout: the loads of one k-block, by value (a pointer to an
+    // item would keep it in memory and its uniform bases in vector registers)
+    struct Ld {
+        const uint8_t *wb[M];
+        uint32_t roff[MT];
+        uint32_t gstr;
+        int kbi;
+        bool on;
+    };
+    auto ld_of = [&](const It &c, int kbi) {
+        Ld l;
+#pragma unroll
+        for (int m = 0; m < M; ++m) l.wb[m] = c.wb[m];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) l.roff[mt] = c.roff[mt];
+        l.gstr = c.gstr;
+        l.kbi = kbi;
+        l.on = true;
+        return l;
+    };
+    // segment sg of that k-block's weights into w[.][.][sg]
+    auto loadSeg = [&](const Ld &l, int sg, uint4 (&w)[M][MT][SEGS]) {
+        const uint32_t go = (uint32_t)min(l.kbi * SEGS + sg, ns - 1) * l.gstr;
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) w[m][mt][sg] = gload16_nt(l.wb[m] + (l.roff[mt] + go));
     };
     // Activations of k-block kbi into LDS by DMA: unit (n, step s, lane L)
     // at (n STEPS + s) 64 + L is the B operand of lane L for N-tile n (pass
@@ -206,20 +268,59 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
     // one k-block over the first NL N-tiles: weights moved into the operand
     // layout in place (lane (q, col) gets row col, chunk q, from lane 4 col
     // + q), then per MFMA step the M x MT code products and the column sums
-    auto compute_n = [&](auto nl, uint4 (&w)[M][MT][SEGS], const uint4 *buf) {
+    // rc (tiled layout only; rc.on false: none): as soon as the products of
+    // a segment are done, that segment of rc's k-block is requested into the
+    // same registers
+    auto compute_n = [&](auto nl, uint4 (&w)[M][MT][SEGS], const uint4 *buf, Ld rc) {
         constexpr int NL = decltype(nl)::value;
+        if constexpr (!TILED) {   // the tiled layout arrives in the operand layout
 #pragma unroll
-        for (int m = 0; m < M; ++m)
+            for (int m = 0; m < M; ++m)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
+                for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int sg = 0; sg < SEGS; ++sg) {
-                    const uint4 v = w[m][mt][sg];
-                    w[m][mt][sg] = make_uint4((uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)v.x),
-                                              (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)v.y),
-                                              (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)v.z),
-                                              (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)v.w));
+                    for (int sg = 0; sg < SEGS; ++sg) {
+                        const uint4 v = w[m][mt][sg];
+                        w[m][mt][sg] = make_uint4((uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)v.x),
+                                                  (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)v.y),
+                                                  (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)v.z),
+                                                  (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)v.w));
+                    }
+        }
+        if constexpr (TILED) {
+            // One MFMA step at a time behind a scheduling barrier, each
+            // weight word passed through an empty asm first (codes_late):
+            // left free, the
+            // compiler computes every step's nibble shifts up front (merging
+            // them from both N-tile branches into the block before the
+            // branch) and needs ~90 more registers, half the occupancy.  The
+            // next step's activation units are read before the barrier.
+            uint4 b[NL], bn[NL];
+#pragma unroll
+            for (int n = 0; n < NL; ++n) b[n] = buf[(n * STEPS) * kWave + lane];
+#pragma unroll
+            for (int s2 = 0; s2 < STEPS; ++s2) {
+                if (s2 + 1 < STEPS) {
+#pragma unroll
+                    for (int n = 0; n < NL; ++n) bn[n] = buf[(n * STEPS + s2 + 1) * kWave + lane];
                 }
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) {
+                        const uint4 cw = codes_late<FMT>(w[m][mt][s2 / SPS], s2 % SPS);
+#pragma unroll
+                        for (int n = 0; n < NL; ++n) acc[m][mt][n] = mfma(cw, b[n], acc[m][mt][n]);
+                    }
+#pragma unroll
+                for (int n = 0; n < NL; ++n) accs[n] = mfma(ones, b[n], accs[n]);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int n = 0; n < NL; ++n) b[n] = bn[n];
+                if (rc.on && (s2 + 1) % SPS == 0) loadSeg(rc, s2 / SPS, w);
+            }
+            return;
+        }
 #pragma unroll
         for (int s2 = 0; s2 < STEPS; ++s2) {
             uint4 b[NL];
@@ -237,11 +338,16 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
             for (int n = 0; n < NL; ++n) accs[n] = mfma(ones, b[n], accs[n]);
         }
     };
-    auto compute = [&](uint4 (&w)[M][MT][SEGS], const uint4 *buf, int ntl) {
+    auto compute_r = [&](uint4 (&w)[M][MT][SEGS], const uint4 *buf, int ntl, Ld rc) {
         if constexpr (NT == 2) {
-            if (ntl == 2) { compute_n(std::integral_constant<int, 2>{}, w, buf); return; }
+            if (ntl == 2) { compute_n(std::integral_constant<int, 2>{}, w, buf, rc); return; }
         }
-        compute_n(std::integral_constant<int, 1>{}, w, buf);
+        compute_n(std::integral_constant<int, 1>{}, w, buf, rc);
+    };
+    auto compute = [&](uint4 (&w)[M][MT][SEGS], const uint4 *buf, int ntl) {
+        Ld none{};
+        none.on = false;
+        compute_r(w, buf, ntl, none);
     };
 
     float sreg[M][MT][4];
@@ -369,6 +475,62 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
         __builtin_amdgcn_sched_barrier(0);
     };
 
+    if constexpr (TILED) {
+        // Tiled weights: the loads of k-block j + 2 are issued into k-block
+        // j's registers while j is multiplied (segment by segment, as each
+        // is consumed), so the wait at k-block j + 2 is for loads issued two
+        // k-blocks earlier -- the latency tolerance of three weight buffers
+        // in the registers of two.  VMEM order: ... DMA(j), [compute j - 1:
+        // W(j + 1)], wait (vmcnt <= NW: W(j) and DMA(j) done), DMA(j + 1),
+        // [compute j: W(j + 2)], ...; k-blocks past an item's end are the
+        // next item's first two (the block's last item re-reads its own last
+        // k-block, from L2).  The epilogue's scale loads are issued after a
+        // wait, so they never hold back the weight loads.
+        It cur;
+        make(cur, lb);
+        int jn = lb + bpx;
+        uint4 wA[M][MT][SEGS], wB[M][MT][SEGS];
+        loadW(cur, 0, wA);
+        stageB(cur, 0, bsA);
+        loadW(cur, 1, wB);
+        // one k-block: its products from weights w and activations buf
+        // (k-block kb in LDS), the next k-block's activations staged into
+        // nbuf, and the loads of l recycled into w
+        auto kstep = [&](int ntl, uint4 (&w)[M][MT][SEGS], const uint4 *buf, const It &sc, int skb,
+                         const uint4 *nbuf, const Ld &l, bool epi = false) {
+            step_sync();
+            stageB(sc, skb, nbuf);
+            if (epi) load_epi(cur);   // after the wait: it does not hold back the weights
+            __builtin_amdgcn_sched_barrier(0);
+            compute_r(w, buf, ntl, l);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        auto kloop = [&](int nl) {
+            for (int k = 0; k < nkb - 2; k += 2) {
+                kstep(nl, wA, bsA, cur, k + 1, bsB, ld_of(cur, k + 2));
+                kstep(nl, wB, bsB, cur, k + 2, bsA, ld_of(cur, k + 3));
+            }
+            // the last two: the epilogue's scales, then the next item's
+            // first two k-blocks (the block's last item re-reads its own
+            // last k-block, from L2) and its first activations
+            const bool has_nxt = jn < n_items;
+            It nxt = cur;
+            if (has_nxt) make(nxt, jn);
+            kstep(nl, wA, bsA, cur, nkb - 1, bsB, has_nxt ? ld_of(nxt, 0) : ld_of(cur, nkb - 1), true);
+            kstep(nl, wB, bsB, nxt, 0, bsA, has_nxt ? ld_of(nxt, 1) : ld_of(cur, nkb - 1));
+            return nxt;
+        };
+        for (;;) {
+            It nxt = kloop((cur.nt + 7) / 8);
+            epilogue(cur);
+            if (jn >= n_items) break;
+            cur = nxt;
+            jn += bpx;
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        return;
+    }
+
     // prologue: the first item's first weights, then the DMA of its first
     // k-block's activations into bsA.  Even k-blocks are staged in bsA, odd
     // ones in bsB (nkb is even).
@@ -415,18 +577,18 @@ int dec_resident_blocks(const void *kern, int threads, int *cache)
     return cache[dev];
 }
 
-template <int FMT, int M>
+template <int FMT, int M, bool TILED>
 hipError_t launch_dec(const DecArgs &a, int64_t items, hipStream_t st)
 {
     static int cache[64] = {0};
-    const void *kern = (const void *)k_dec<FMT, M>;
+    const void *kern = (const void *)k_dec<FMT, M, TILED>;
     constexpr int threads = 64 * DecTiles<M>::W;
     int64_t cap = dec_resident_blocks(kern, threads, cache) / kDecXcds * kDecXcds;
     if (cap < kDecXcds) cap = kDecXcds;
     int64_t grid = (items + kDecXcds - 1) / kDecXcds * kDecXcds;
     if (grid > cap) grid = cap;
     if (grid < kDecXcds) grid = kDecXcds;
-    hipLaunchKernelGGL((k_dec<FMT, M>), dim3((unsigned)grid), dim3(threads), 0, st, a);
+    hipLaunchKernelGGL((k_dec<FMT, M, TILED>), dim3((unsigned)grid), dim3(threads), 0, st, a);
     return hipGetLastError();
 }
 
@@ -462,20 +624,20 @@ hipError_t dec_launch(DecArgs a, int fmt, int M, int64_t max_group_passes, hipSt
     const int rpb = dec_rows_per_block(M);
     a.tiles = (Ocover + rpb - 1) / rpb;
     const int64_t items = max_group_passes * a.tiles;
+#define COLI_DEC_CASES(MM, TT)                                      \
+    switch (fmt) {                                                 \
+    case kI8: return launch_dec<kI8, MM, TT>(a, items, st);        \
+    case kI4: return launch_dec<kI4, MM, TT>(a, items, st);        \
+    case kI2: return launch_dec<kI2, MM, TT>(a, items, st);        \
+    default: return hipErrorInvalidValue;                          \
+    }
     if (M == 2) {
-        switch (fmt) {
-        case kI8: return launch_dec<kI8, 2>(a, items, st);
-        case kI4: return launch_dec<kI4, 2>(a, items, st);
-        case kI2: return launch_dec<kI2, 2>(a, items, st);
-        default: return hipErrorInvalidValue;
-        }
+        if (a.tiled) COLI_DEC_CASES(2, true)
+        COLI_DEC_CASES(2, false)
     }
-    switch (fmt) {
-    case kI8: return launch_dec<kI8, 1>(a, items, st);
-    case kI4: return launch_dec<kI4, 1>(a, items, st);
-    case kI2: return launch_dec<kI2, 1>(a, items, st);
-    default: return hipErrorInvalidValue;
-    }
+    if (a.tiled) COLI_DEC_CASES(1, true)
+    COLI_DEC_CASES(1, false)
+#undef COLI_DEC_CASES
 }
 
 }  // namespace coli

@@ -91,6 +91,27 @@ template <> __device__ __forceinline__ uint4 codes<kI8>(const uint4 &w, int s)
                       bf_pair_of_bytes(b1, 2));
 }
 
+// codes<FMT>(w, s) with the word(s) step s reads first passed through an
+// empty asm statement: the compiler can then neither compute them ahead of
+// that point nor merge them with an identical computation on another path.
+template <int FMT> __device__ __forceinline__ uint4 codes_late(const uint4 &w, int s)
+{
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if constexpr (FMT == kI8) {
+        uint32_t a = wsel(w, 2 * s), b = wsel(w, 2 * s + 1);
+        asm volatile("" : "+v"(a), "+v"(b));
+        if (s == 0) { v.x = a; v.y = b; }
+        else { v.z = a; v.w = b; }
+        return codes<FMT>(v, s);
+    } else {
+        const int d = FMT == kI4 ? s : s >> 1;
+        uint32_t a = wsel(w, d);
+        asm volatile("" : "+v"(a));
+        v.x = a;
+        return codes<FMT>(v, FMT == kI4 ? 0 : (s & 1));
+    }
+}
+
 __device__ __forceinline__ uint16_t bf16_rne(float f)
 {
     uint32_t u = __float_as_uint(f);
@@ -111,6 +132,13 @@ __device__ __forceinline__ uint4 gload16(const void *p)
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 __device__ __forceinline__ float gloadf(const float *p) { return *(g_float *)p; }
+// A streaming load (non-temporal hint): data read once, kept out of the way
+// of the small tables that are reused from L2.
+__device__ __forceinline__ uint4 gload16_nt(const void *p)
+{
+    const u32x4 v = __builtin_nontemporal_load((g_u32x4 *)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) const f32x4 g_f32x4;
 __device__ __forceinline__ float4 gload4f(const float *p)
@@ -156,6 +184,28 @@ template <int FMT> __device__ __forceinline__ void pos_of(int e, int &c, int &j)
         j = 2 * (k & 3) + (uu >> 3);
     }
     c = (kbi * T::STEPS + sg * T::SPS + sub) * 4 + q;
+}
+
+// Tiled weight layout (coli_pack_tiled): a matrix is cut into 1 KB units of
+// 16 rows x 64 bytes, each unit in the A-operand lane order (lane 16 q + c
+// holds row c's bytes 16 q .. 16 q + 15 of the segment), so a wave loads a
+// row tile's segment with one contiguous 1 KB load and needs no transpose.
+// Units are ordered by groups of kTileGroup row tiles (128 rows), inside a
+// group by segment, then by row tile: the units of one group and one k-block
+// are one contiguous run.  ns = segments per row (ceil(rb / 64)), mt16 = row
+// tiles (ceil(O / 16)).
+constexpr int kTileGroup = 8;
+// byte offset of unit (m, 0)
+__device__ __forceinline__ uint32_t tiled_base(int m, int ns)
+{
+    const int T = m / kTileGroup, mm = m - T * kTileGroup;
+    return (uint32_t)(T * kTileGroup * ns + mm) * 1024u;
+}
+// bytes from unit (m, g) to unit (m, g + 1)
+__device__ __forceinline__ uint32_t tiled_gstride(int m, int mt16)
+{
+    const int T = m / kTileGroup;
+    return (uint32_t)min(kTileGroup, mt16 - T * kTileGroup) * 1024u;
 }
 
 // Work-list and group-offset reads: written by an earlier kernel and never

@@ -43,6 +43,8 @@ struct PreArgs {
     int hf_kpad;
     float *hpart;
     int nparts;
+    int tiled;               // weights in the tiled layout (coli_pack_tiled); w_gstride
+                             // is then the tiled bytes of one matrix
     int tiles;               // set by pre_launch
 };
 

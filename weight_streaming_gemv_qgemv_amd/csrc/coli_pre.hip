@@ -125,7 +125,7 @@ __device__ __forceinline__ void dma16(const void *g, uint32_t lds)
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory");
 }
 
-template <int FMT, int M>
+template <int FMT, int M, bool TILED>
 __global__ __launch_bounds__(64 * kPreWaves) void k_pre(PreArgs a)
 {
     using T = MF<FMT>;
@@ -157,6 +157,9 @@ __global__ __launch_bounds__(64 * kPreWaves) void k_pre(PreArgs a)
     // row's last chunk (it meets zero activations)
     const uint32_t coff = (uint32_t)min(16 * q, (int)(a.rb - 16));
     const uint32_t last_seg = (uint32_t)(a.rb - 16) - coff;
+    // tiled layout: segments per row; a k-block past the row end reads the
+    // last segment (it meets zero activations)
+    const int ns = (int)((a.rb + 63) / 64);
     const uint8_t *actb = reinterpret_cast<const uint8_t *>(a.act);
     const uint32_t arow = (uint32_t)(2 * a.kpad);       // bytes per row-table row
 
@@ -164,7 +167,9 @@ __global__ __launch_bounds__(64 * kPreWaves) void k_pre(PreArgs a)
         int gp, tile, nt, r0t, Og;
         const uint8_t *wb[M];
         const float *sc[M];
-        uint32_t roff[MT];
+        uint32_t roff[MT];   // rows: this lane's row (clamped) * rb + its chunk;
+                             // tiled: its row tile's first unit + 16 lane
+        uint32_t gstr;       // tiled: bytes from one segment's unit to the next
     };
     auto make = [&](It &c, int it) {
         c.gp = __builtin_amdgcn_readfirstlane(gp_lo + it % gp_cnt);
@@ -195,9 +200,19 @@ __global__ __launch_bounds__(64 * kPreWaves) void k_pre(PreArgs a)
             }
         }
         const int obase = c.tile * RPB + wave * RPW;
+        if constexpr (TILED) {
+            // the wave's row tiles lie in one group of the layout (a row tile
+            // past the matrix is clamped to the last one: never stored)
+            const int mt16 = (c.Og + 15) / 16;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-            c.roff[mt] = (uint32_t)(min(obase + 16 * mt + col, c.Og - 1) * a.rb) + coff;
+            for (int mt = 0; mt < MT; ++mt) c.roff[mt] = tiled_base(min(obase / 16 + mt, mt16 - 1), ns) + 16 * lane;
+            c.gstr = tiled_gstride(min(obase / 16, mt16 - 1), mt16);
+        } else {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                c.roff[mt] = (uint32_t)(min(obase + 16 * mt + col, c.Og - 1) * a.rb) + coff;
+            c.gstr = 0;
+        }
     };
     // pass rows of an item: row-table row and activation sum (threads < 64;
     // dead rows repeat the last live one)
@@ -213,6 +228,17 @@ __global__ __launch_bounds__(64 * kPreWaves) void k_pre(PreArgs a)
         }
     };
     auto loadW = [&](const It &c, int kbi, uint4 (&w)[M][MT][SEGS]) {
+        if constexpr (TILED) {
+#pragma unroll
+            for (int sg = 0; sg < SEGS; ++sg) {
+                const uint32_t go = (uint32_t)min(kbi * SEGS + sg, ns - 1) * c.gstr;
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) w[m][mt][sg] = gload16(c.wb[m] + (c.roff[mt] + go));
+            }
+            return;
+        }
         const uint32_t b0 = (uint32_t)kbi * kbytes;
 #pragma unroll
         for (int m = 0; m < M; ++m)
@@ -455,17 +481,17 @@ int pre_resident_blocks(const void *kern, int *cache)
     return cache[dev];
 }
 
-template <int FMT, int M>
+template <int FMT, int M, bool TILED>
 hipError_t launch_pre(const PreArgs &a, int64_t items, hipStream_t st)
 {
     static int cache[64] = {0};
-    const void *kern = (const void *)k_pre<FMT, M>;
+    const void *kern = (const void *)k_pre<FMT, M, TILED>;
     int64_t cap = pre_resident_blocks(kern, cache) / kPreXcds * kPreXcds;
     if (cap < kPreXcds) cap = kPreXcds;
     int64_t grid = (items + kPreXcds - 1) / kPreXcds * kPreXcds;
     if (grid > cap) grid = cap;
     if (grid < kPreXcds) grid = kPreXcds;
-    hipLaunchKernelGGL((k_pre<FMT, M>), dim3((unsigned)grid), dim3(64 * kPreWaves), 0, st, a);
+    hipLaunchKernelGGL((k_pre<FMT, M, TILED>), dim3((unsigned)grid), dim3(64 * kPreWaves), 0, st, a);
     return hipGetLastError();
 }
 
@@ -513,20 +539,20 @@ hipError_t pre_launch(PreArgs a, int fmt, int M, int64_t max_group_passes, hipSt
     a.tiles = (Ocover + kPreRowsPerBlock - 1) / kPreRowsPerBlock;
     if (M == 2 && a.nparts < a.tiles * kPreWaves) return hipErrorInvalidValue;
     const int64_t items = max_group_passes * a.tiles;
+#define COLI_PRE_CASES(MM, TT)                                      \
+    switch (fmt) {                                                 \
+    case kI8: return launch_pre<kI8, MM, TT>(a, items, st);        \
+    case kI4: return launch_pre<kI4, MM, TT>(a, items, st);        \
+    case kI2: return launch_pre<kI2, MM, TT>(a, items, st);        \
+    default: return hipErrorInvalidValue;                          \
+    }
     if (M == 2) {
-        switch (fmt) {
-        case kI8: return launch_pre<kI8, 2>(a, items, st);
-        case kI4: return launch_pre<kI4, 2>(a, items, st);
-        case kI2: return launch_pre<kI2, 2>(a, items, st);
-        default: return hipErrorInvalidValue;
-        }
+        if (a.tiled) COLI_PRE_CASES(2, true)
+        COLI_PRE_CASES(2, false)
     }
-    switch (fmt) {
-    case kI8: return launch_pre<kI8, 1>(a, items, st);
-    case kI4: return launch_pre<kI4, 1>(a, items, st);
-    case kI2: return launch_pre<kI2, 1>(a, items, st);
-    default: return hipErrorInvalidValue;
-    }
+    if (a.tiled) COLI_PRE_CASES(1, true)
+    COLI_PRE_CASES(1, false)
+#undef COLI_PRE_CASES
 }
 
 }  // namespace coli

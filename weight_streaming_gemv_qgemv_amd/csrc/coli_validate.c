@@ -221,20 +221,56 @@ size_t coli_moe_workspace_bytes(int S, int K, int E, int D, int F, int F_shared,
     return (size_t)L.total;
 }
 
-static int check_mlp_tensors(int fmt, int D, int F, const void *wg, const void *wu,
+int64_t coli_tiled_bytes(int fmt, int64_t count, int O, int I)
+{
+    if (fmt != COLI_I8 && fmt != COLI_I4 && fmt != COLI_I2) return -1;
+    if (count < 0 || O < 0 || I < 0) return -1;
+    const int64_t rb = coli_row_bytes(fmt, I);
+    int64_t t;
+    if (!mul_ok(((int64_t)O + 15) / 16, (rb + 63) / 64, &t) || !mul_ok(t, 1024, &t) || !mul_ok(t, count, &t))
+        return -1;
+    return t;
+}
+
+/* Bytes of one weight matrix [O, I] in the given layout. */
+static int64_t matrix_bytes(int fmt, int layout, int O, int I)
+{
+    int64_t t;
+    if (layout == COLI_LAYOUT_TILED) return coli_tiled_bytes(fmt, 1, O, I);
+    if (!mul_ok(coli_row_bytes(fmt, I), O, &t)) return -1;
+    return t;
+}
+
+static int check_mlp_tensors(int fmt, int layout, int D, int F, const void *wg, const void *wu,
                              const void *wd, const float *sg, const float *su,
                              const float *sd, int64_t count)
 {
     if (fmt != COLI_I8 && fmt != COLI_I4 && fmt != COLI_I2) return COLI_EFMT;
+    if (layout != COLI_LAYOUT_ROWS && layout != COLI_LAYOUT_TILED) return COLI_EINVAL;
     if (F < 1 || D < 1) return COLI_ESHAPE;
-    int64_t a, b;
-    if (!mul_ok(coli_row_bytes(fmt, D), F, &a) || !mul_ok(a, count, &a) ||
-        !mul_ok(coli_row_bytes(fmt, F), D, &b) || !mul_ok(b, count, &b))
-        return COLI_ESHAPE;
+    int64_t a = matrix_bytes(fmt, layout, F, D), b = matrix_bytes(fmt, layout, D, F);
+    if (a < 0 || b < 0 || !mul_ok(a, count, &a) || !mul_ok(b, count, &b)) return COLI_ESHAPE;
     if (!wg || !wu || !wd || !sg || !su || !sd) return COLI_EINVAL;
     if (!aligned(wg, 4) || !aligned(wu, 4) || !aligned(wd, 4) || !aligned(sg, 4) ||
         !aligned(su, 4) || !aligned(sd, 4))
         return COLI_EALIGN;
+    /* the tiled layout is read by the matrix-core kernels only */
+    if (layout == COLI_LAYOUT_TILED &&
+        (coli_row_bytes(fmt, D) % 16 || coli_row_bytes(fmt, F) % 16 || !aligned(wg, 16) ||
+         !aligned(wu, 16) || !aligned(wd, 16)))
+        return COLI_EALIGN;
+    return COLI_OK;
+}
+
+int coli__check_pack(int fmt, const void *W, int64_t count, int O, int I, const void *dst)
+{
+    if (fmt != COLI_I8 && fmt != COLI_I4 && fmt != COLI_I2) return COLI_EFMT;
+    if (count < 0 || O < 0 || I < 0 || coli_tiled_bytes(fmt, count, O, I) < 0) return COLI_ESHAPE;
+    int64_t t;
+    if (!mul_ok(coli_row_bytes(fmt, I), O, &t) || !mul_ok(t, count, &t)) return COLI_ESHAPE;
+    if (count == 0 || O == 0 || I == 0) return COLI_OK;
+    if (!W || !dst) return COLI_EINVAL;
+    if (coli_row_bytes(fmt, I) % 16 || !aligned(W, 16) || !aligned(dst, 16)) return COLI_EALIGN;
     return COLI_OK;
 }
 
@@ -251,11 +287,15 @@ static int check_off32(const coli_experts *ex, const coli_mlp *sh, int S, int K,
     const int64_t eb = prec == COLI_PREC_BF16 ? 2 : 4;
     const int64_t rows = (int64_t)S * K + (sh ? S : 0);
     int64_t t;
-    if (!mul_ok(coli_row_bytes(ex->fmt, ex->D), ex->F, &t) || t >= lim) return COLI_ERANGE;
-    if (!mul_ok(coli_row_bytes(ex->fmt, ex->F), ex->D, &t) || t >= lim) return COLI_ERANGE;
+    t = matrix_bytes(ex->fmt, ex->layout, ex->F, ex->D);
+    if (t < 0 || t >= lim) return COLI_ERANGE;
+    t = matrix_bytes(ex->fmt, ex->layout, ex->D, ex->F);
+    if (t < 0 || t >= lim) return COLI_ERANGE;
     if (sh) {
-        if (!mul_ok(coli_row_bytes(sh->fmt, ex->D), sh->F, &t) || t >= lim) return COLI_ERANGE;
-        if (!mul_ok(coli_row_bytes(sh->fmt, sh->F), ex->D, &t) || t >= lim) return COLI_ERANGE;
+        t = matrix_bytes(sh->fmt, sh->layout, sh->F, ex->D);
+        if (t < 0 || t >= lim) return COLI_ERANGE;
+        t = matrix_bytes(sh->fmt, sh->layout, ex->D, sh->F);
+        if (t < 0 || t >= lim) return COLI_ERANGE;
     }
     if (!mul_ok((int64_t)S, eb * coli__kpad(ex->D), &t) || t >= lim) return COLI_ERANGE;
     if (!mul_ok(rows, eb * coli__kpad(Fmax), &t) || t >= lim) return COLI_ERANGE;
@@ -271,14 +311,18 @@ int coli__check_moe(const coli_experts *ex, const coli_mlp *sh, const float *x,
     if (prec != COLI_PREC_FP32 && prec != COLI_PREC_BF16) return COLI_EINVAL;
     if (S < 0 || K < 0 || ex->E < 0 || ex->D < 0 || ex->F < 0) return COLI_ESHAPE;
     if (ex->E < 1 || ex->E > COLI_MAX_E || K < 1 || K > COLI_MAX_K) return COLI_ERANGE;
-    int rc = check_mlp_tensors(ex->fmt, ex->D, ex->F, ex->w_gate, ex->w_up, ex->w_down,
+    int rc = check_mlp_tensors(ex->fmt, ex->layout, ex->D, ex->F, ex->w_gate, ex->w_up, ex->w_down,
                                ex->s_gate, ex->s_up, ex->s_down, ex->E);
     if (rc) return rc;
     if (sh) {
         if (sh->F < 1) return COLI_ESHAPE;
-        rc = check_mlp_tensors(sh->fmt, ex->D, sh->F, sh->w_gate, sh->w_up, sh->w_down,
+        rc = check_mlp_tensors(sh->fmt, sh->layout, ex->D, sh->F, sh->w_gate, sh->w_up, sh->w_down,
                                sh->s_gate, sh->s_up, sh->s_down, 1);
         if (rc) return rc;
+        /* a tiled shared expert runs as one more group of the routed kernels */
+        if (sh->layout == COLI_LAYOUT_TILED &&
+            (ex->layout != COLI_LAYOUT_TILED || sh->fmt != ex->fmt || sh->F != ex->F))
+            return COLI_EINVAL;
     }
     int64_t t;
     if (!mul_ok((int64_t)S, ex->D, &t) || !mul_ok(t, 4, &t)) return COLI_ESHAPE;
