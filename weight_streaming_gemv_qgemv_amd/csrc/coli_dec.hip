@@ -268,10 +268,7 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
     // one k-block over the first NL N-tiles: weights moved into the operand
     // layout in place (lane (q, col) gets row col, chunk q, from lane 4 col
     // + q), then per MFMA step the M x MT code products and the column sums
-    // rc (tiled layout only; rc.on false: none): as soon as the products of
-    // a segment are done, that segment of rc's k-block is requested into the
-    // same registers
-    auto compute_n = [&](auto nl, uint4 (&w)[M][MT][SEGS], const uint4 *buf, Ld rc) {
+    auto compute_n = [&](auto nl, uint4 (&w)[M][MT][SEGS], const uint4 *buf, int rkb) {
         constexpr int NL = decltype(nl)::value;
         if constexpr (!TILED) {   // the tiled layout arrives in the operand layout
 #pragma unroll
@@ -290,17 +287,20 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
         if constexpr (TILED) {
             // One MFMA step at a time behind a scheduling barrier, each
             // weight word passed through an empty asm first (codes_late):
-            // left free, the
-            // compiler computes every step's nibble shifts up front (merging
-            // them from both N-tile branches into the block before the
-            // branch) and needs ~90 more registers, half the occupancy.  The
-            // next step's activation units are read before the barrier.
+            // left free, the compiler computes every step's nibble shifts up
+            // front (merging them from both N-tile branches into the block
+            // before the branch) and needs ~90 more registers, half the
+            // occupancy.  The next step's activation units are read before
+            // the barrier.  Only the steps of segment rc_sg (< 0: all).
+            const int sg = rkb;
             uint4 b[NL], bn[NL];
+            const int s_lo = sg < 0 ? 0 : sg * SPS, s_hi = sg < 0 ? STEPS : s_lo + SPS;
 #pragma unroll
-            for (int n = 0; n < NL; ++n) b[n] = buf[(n * STEPS) * kWave + lane];
+            for (int n = 0; n < NL; ++n) b[n] = buf[(n * STEPS + s_lo) * kWave + lane];
 #pragma unroll
             for (int s2 = 0; s2 < STEPS; ++s2) {
-                if (s2 + 1 < STEPS) {
+                if (s2 < s_lo || s2 >= s_hi) continue;
+                if (s2 + 1 < s_hi) {
 #pragma unroll
                     for (int n = 0; n < NL; ++n) bn[n] = buf[(n * STEPS + s2 + 1) * kWave + lane];
                 }
@@ -317,7 +317,6 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int n = 0; n < NL; ++n) b[n] = bn[n];
-                if (rc.on && (s2 + 1) % SPS == 0) loadSeg(rc, s2 / SPS, w);
             }
             return;
         }
@@ -338,16 +337,27 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
             for (int n = 0; n < NL; ++n) accs[n] = mfma(ones, b[n], accs[n]);
         }
     };
-    auto compute_r = [&](uint4 (&w)[M][MT][SEGS], const uint4 *buf, int ntl, Ld rc) {
+    // the products of k-block buf (tiled: of segment sg only, sg < 0: all)
+    // over the live N-tiles
+    auto compute_s = [&](uint4 (&w)[M][MT][SEGS], const uint4 *buf, int ntl, int sg) {
         if constexpr (NT == 2) {
-            if (ntl == 2) { compute_n(std::integral_constant<int, 2>{}, w, buf, rc); return; }
+            if (ntl == 2) { compute_n(std::integral_constant<int, 2>{}, w, buf, sg); return; }
         }
-        compute_n(std::integral_constant<int, 1>{}, w, buf, rc);
+        compute_n(std::integral_constant<int, 1>{}, w, buf, sg);
     };
-    auto compute = [&](uint4 (&w)[M][MT][SEGS], const uint4 *buf, int ntl) {
-        Ld none{};
-        none.on = false;
-        compute_r(w, buf, ntl, none);
+    auto compute = [&](uint4 (&w)[M][MT][SEGS], const uint4 *buf, int ntl) { compute_s(w, buf, ntl, -1); };
+    // Tiled: segment by segment, and as soon as a segment's products are
+    // done that segment of rc's k-block is requested into the same
+    // registers.  The loads sit after the N-tile branch has joined: a
+    // register with a load in flight that the branches had placed apart
+    // would be copied at the join, and the copy waits for every load.
+    auto compute_r = [&](uint4 (&w)[M][MT][SEGS], const uint4 *buf, int ntl, Ld rc) {
+#pragma unroll
+        for (int sg = 0; sg < SEGS; ++sg) {
+            compute_s(w, buf, ntl, sg);
+            __builtin_amdgcn_sched_barrier(0);
+            if (rc.on) loadSeg(rc, sg, w);
+        }
     };
 
     float sreg[M][MT][4];
@@ -361,10 +371,18 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
                 for (int r = 0; r < 4; ++r)
                     sreg[m][mt][r] = gloadf(c.sc[m] + min(obase + 16 * mt + 4 * q + r, c.Og - 1));
     };
-    // D[4q + r][col] of tile (m, mt, n); the lo column is added to the hi one
-    auto epilogue = [&](const It &c) {
+    // D[4q + r][col] of tile (m, mt, n); the lo column is added to the hi one.
+    // Returns the number of store instructions issued when that number is
+    // known (the uniform fast path: the wave's rows inside the matrix -- and
+    // for gate/up inside the down product's row table -- and 16-byte stores:
+    // one per live N-tile and row tile, and one more for the row table), else
+    // 0.  The tiled loop's next wait lets exactly that many stores stay in
+    // flight.
+    auto epilogue = [&](const It &c) -> int {
         const int obase = c.tile * RPB + wave * RPW;
         const int ntl = (c.nt + 7) / 8;
+        const bool fast = a.out_vec4 && obase + RPW <= c.Og;
+        const bool hfast = M == 2 && a.hf && obase + RPW <= a.hf_kpad;
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
             if (n >= ntl) break;                        // uniform
@@ -390,8 +408,11 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
                     }
                     res[r] = ob + r < c.Og ? y : 0.f;
                 }
-                if (live && (col & 1) == 0) {
-                    float *op = a.out + (int64_t)(c.r0t + tok) * a.ldo;
+                float *op = a.out + (int64_t)(c.r0t + tok) * a.ldo;
+                if (fast) {   // uniform
+                    if (live && (col & 1) == 0)
+                        *reinterpret_cast<float4 *>(op + ob) = make_float4(res[0], res[1], res[2], res[3]);
+                } else if (live && (col & 1) == 0) {
                     if (a.out_vec4 && ob + 3 < c.Og) {
                         *reinterpret_cast<float4 *>(op + ob) = make_float4(res[0], res[1], res[2], res[3]);
                     } else {
@@ -419,7 +440,7 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
                         uint32_t pv[4];
 #pragma unroll
                         for (int r = 0; r < 4; ++r) pv[r] = (uint32_t)__shfl_xor((int)hv[r], PX, kWave);
-                        if (lowq && live && ob < a.hf_kpad) {
+                        if (lowq && live && (hfast || ob < a.hf_kpad)) {
                             int cc, j;
                             pos_of<FMT>(ob, cc, j);
                             uint4 u;
@@ -444,6 +465,8 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
                 for (int mt = 0; mt < MT; ++mt) acc[m][mt][n] = floatx4{0.f, 0.f, 0.f, 0.f};
             accs[n] = floatx4{0.f, 0.f, 0.f, 0.f};
         }
+        if (!fast || (M == 2 && a.hf && !hfast)) return 0;
+        return ntl * MT * (M == 2 && a.hf ? 2 : 1);
     };
 
     // the staged k-block is complete once this wave's DMA loads are: they
@@ -461,6 +484,20 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
     auto step_sync = [&]() {
         // vmcnt <= NW (bits 3:0 and 15:14), lgkmcnt = 0, expcnt not waited on
         __builtin_amdgcn_s_waitcnt((NW & 15) | ((NW >> 4) << 14) | (7 << 4));
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+    // the same with `extra` more VMEM operations (stores) issued after the
+    // next k-block's weights: 0, or an epilogue's known store count
+    auto step_sync_x = [&](int extra) {
+        constexpr int L = 7 << 4;
+        switch (extra) {   // uniform; an unexpected count waits for everything but NW
+        case 4: __builtin_amdgcn_s_waitcnt(((NW + 4) & 15) | (((NW + 4) >> 4) << 14) | L); break;
+        case 8: __builtin_amdgcn_s_waitcnt(((NW + 8) & 15) | (((NW + 8) >> 4) << 14) | L); break;
+        case 16: __builtin_amdgcn_s_waitcnt(((NW + 16) & 15) | (((NW + 16) >> 4) << 14) | L); break;
+        default: __builtin_amdgcn_s_waitcnt((NW & 15) | ((NW >> 4) << 14) | L); break;
+        }
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
@@ -497,16 +534,19 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
         // (k-block kb in LDS), the next k-block's activations staged into
         // nbuf, and the loads of l recycled into w
         auto kstep = [&](int ntl, uint4 (&w)[M][MT][SEGS], const uint4 *buf, const It &sc, int skb,
-                         const uint4 *nbuf, const Ld &l, bool epi = false) {
-            step_sync();
+                         const uint4 *nbuf, const Ld &l, bool epi = false, int extra = 0) {
+            step_sync_x(extra);
             stageB(sc, skb, nbuf);
             if (epi) load_epi(cur);   // after the wait: it does not hold back the weights
             __builtin_amdgcn_sched_barrier(0);
             compute_r(w, buf, ntl, l);
             __builtin_amdgcn_sched_barrier(0);
         };
-        auto kloop = [&](int nl) {
-            for (int k = 0; k < nkb - 2; k += 2) {
+        // extra: the stores the previous item's epilogue left in flight
+        auto kloop = [&](int nl, int extra) {
+            kstep(nl, wA, bsA, cur, 1, bsB, ld_of(cur, 2), false, extra);
+            kstep(nl, wB, bsB, cur, 2, bsA, ld_of(cur, 3));
+            for (int k = 2; k < nkb - 2; k += 2) {
                 kstep(nl, wA, bsA, cur, k + 1, bsB, ld_of(cur, k + 2));
                 kstep(nl, wB, bsB, cur, k + 2, bsA, ld_of(cur, k + 3));
             }
@@ -520,9 +560,10 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
             kstep(nl, wB, bsB, nxt, 0, bsA, has_nxt ? ld_of(nxt, 1) : ld_of(cur, nkb - 1));
             return nxt;
         };
+        int extra = 0;
         for (;;) {
-            It nxt = kloop((cur.nt + 7) / 8);
-            epilogue(cur);
+            It nxt = kloop((cur.nt + 7) / 8, extra);
+            extra = epilogue(cur);
             if (jn >= n_items) break;
             cur = nxt;
             jn += bpx;
