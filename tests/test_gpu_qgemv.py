@@ -44,6 +44,25 @@ def test_tiny_shapes_brute_force(dev, orc, fmt):
             assert_within(got, ref, mag, REL, what=f"fmt{fmt} O{O} I{I} S{S}")
 
 
+@pytest.mark.parametrize("fmt", [1, 2, 3])
+@pytest.mark.parametrize("O", [4100, 8200, 12290])
+def test_tiles_per_block_ragged(dev, orc, fmt, O):
+    """Row counts whose one-shot launch takes 2 (4100 rows) or 3 (8200, 12290
+    rows) tiles of 16 rows per block, with a last group only partly inside
+    the matrix (and a last tile of 4 / 8 / 2 rows); exact-integer inputs, so
+    the result is the oracle's bit for bit.  S = 1 and 2 (one pass)."""
+    I = 1024
+    g = synth.rng(250, fmt, O)
+    W = synth.weight_bytes(g, fmt, O, I)
+    sc = synth.exact_scales(g, O)
+    for S in (1, 2):
+        announce("qgemv tiles per block", fmt, O, S)
+        x = synth.exact_activations(g, S, I)
+        ref, _ = orc.qgemv(fmt, W, sc, x)
+        got = run_gpu(dev, fmt, W, sc, x, O)
+        np.testing.assert_array_equal(got, ref.astype(np.float32), err_msg=f"fmt{fmt} O{O} S{S}")
+
+
 @pytest.mark.parametrize("fmt", [0, 1, 2, 3])
 @pytest.mark.parametrize("O,I", [(37, 40), (300, 1000), (257, 4096), (64, 8192 + 64)])
 def test_exact_integer_bitwise(dev, orc, fmt, O, I):

@@ -146,6 +146,22 @@ def _check(rc: int, what: str):
         raise ColiError(rc, what)
 
 
+def _nbytes(t) -> int | None:
+    """Bytes a tensor argument holds (None for a raw pointer or None)."""
+    if t is None or isinstance(t, int):
+        return None
+    return t.numel() * t.element_size()
+
+
+def _need(t, nbytes: int, what: str):
+    """The library takes raw pointers and cannot see allocation sizes: a
+    tensor smaller than the call reads or writes is refused here, before
+    anything runs on the device."""
+    have = _nbytes(t)
+    if have is not None and have < nbytes:
+        raise ColiError(ESHAPE, f"{what}: tensor holds {have} bytes, the call needs {nbytes}")
+
+
 def row_bytes(fmt: int, I: int) -> int:
     return int(lib().coli_row_bytes(fmt, I))
 
@@ -156,9 +172,14 @@ def qgemv(fmt: int, W: torch.Tensor, scale, x: torch.Tensor, y: torch.Tensor | N
     """y[s,o] = scale[o] * sum_i v(o,i) x[s,i]; W [O, row_bytes] uint8 (or f32 [O, I])."""
     S, I = x.shape
     if O is None:
+        if W.dim() != 2:
+            raise ColiError(EINVAL, "qgemv: pass O for a weight tensor that is not [O, row bytes]")
         O = W.shape[0]
     if y is None:
         y = torch.empty((S, O), dtype=torch.float32, device=x.device)
+    _need(W, O * row_bytes(fmt, I), "qgemv W")
+    _need(scale, 4 * O, "qgemv scale")
+    _need(y, 4 * S * O, "qgemv y")
     rc = lib().coli_qgemv(fmt, _ptr(W), _ptr(scale), _ptr(x), _ptr(y), S, I, O, _stream(stream))
     _check(rc, "coli_qgemv")
     return y
@@ -168,9 +189,15 @@ def qgemv_grouped(W: torch.Tensor, scale: torch.Tensor, gs: int, x: torch.Tensor
                   y: torch.Tensor | None = None, O: int | None = None, stream=None) -> torch.Tensor:
     """Grouped-scale int4: scale [O, ceil(I/gs)], one per gs elements along I."""
     S, I = x.shape
-    O = W.shape[0] if O is None else O
+    if O is None:
+        if W.dim() != 2:
+            raise ColiError(EINVAL, "qgemv_grouped: pass O for a weight tensor that is not [O, row bytes]")
+        O = W.shape[0]
     if y is None:
         y = torch.empty((S, O), dtype=torch.float32, device=x.device)
+    _need(W, O * row_bytes(I4, I), "qgemv_grouped W")
+    _need(scale, 4 * O * (-(-I // max(int(gs), 1))), "qgemv_grouped scale")
+    _need(y, 4 * S * O, "qgemv_grouped y")
     rc = lib().coli_qgemv_grouped(_ptr(W), _ptr(scale), int(gs), _ptr(x), _ptr(y), S, I, O, _stream(stream))
     _check(rc, "coli_qgemv_grouped")
     return y
@@ -184,9 +211,15 @@ def qgemv_idot(fmt: int, W: torch.Tensor, scale, x: torch.Tensor, y: torch.Tenso
                O: int | None = None, ws=None, stream=None):
     """Integer-dot qgemv (int8 / int4): x quantised to int8 per row by absmax/127."""
     S, I = x.shape
-    O = W.shape[0] if O is None else O
+    if O is None:
+        if W.dim() != 2:
+            raise ColiError(EINVAL, "qgemv_idot: pass O for a weight tensor that is not [O, row bytes]")
+        O = W.shape[0]
     if y is None:
         y = torch.empty((S, O), dtype=torch.float32, device=x.device)
+    _need(W, O * row_bytes(fmt, I), "qgemv_idot W")
+    _need(scale, 4 * O, "qgemv_idot scale")
+    _need(y, 4 * S * O, "qgemv_idot y")
     if ws is None:
         ws = alloc_workspace(max(qgemv_idot_workspace_bytes(S, I), 256), x.device)
     rc = lib().coli_qgemv_idot(fmt, _ptr(W), _ptr(scale), _ptr(x), _ptr(y), S, I, O, _ptr(ws), ws.numel(),
@@ -225,13 +258,32 @@ def router(Wr, bias, x, K: int, norm_topk: int = 1, routed_scale: float = 2.5, t
 
 
 # ------------------------------------------------------------------ MoE
+def _check_mlp_sizes(d: dict, n: int, D: int, F: int, what: str):
+    """Weight and scale tensors of n stacked experts of width D x F hold at
+    least the bytes their layout needs."""
+    fmt, lay = d["fmt"], int(d.get("layout", LAYOUT_ROWS))
+    if lay == LAYOUT_TILED:
+        gu, dn = tiled_bytes(fmt, n, F, D), tiled_bytes(fmt, n, D, F)
+    else:
+        gu, dn = n * F * row_bytes(fmt, D), n * D * row_bytes(fmt, F)
+    _need(d["wg"], gu, what + " w_gate")
+    _need(d["wu"], gu, what + " w_up")
+    _need(d["wd"], dn, what + " w_down")
+    _need(d["sg"], 4 * n * F, what + " s_gate")
+    _need(d["su"], 4 * n * F, what + " s_up")
+    _need(d["sd"], 4 * n * D, what + " s_down")
+
+
 def experts_struct(ex: dict) -> Experts:
+    _check_mlp_sizes(ex, ex["E"], ex["D"], ex["F"], "experts")
     return Experts(ex["fmt"], ex["E"], ex["D"], ex["F"], _ptr(ex["wg"]), _ptr(ex["wu"]),
                    _ptr(ex["wd"]), _ptr(ex["sg"]), _ptr(ex["su"]), _ptr(ex["sd"]),
                    int(ex.get("layout", LAYOUT_ROWS)))
 
 
-def mlp_struct(sh: dict) -> Mlp:
+def mlp_struct(sh: dict, D: int | None = None) -> Mlp:
+    if D is not None:
+        _check_mlp_sizes(sh, 1, D, sh["F"], "shared expert")
     return Mlp(sh["fmt"], sh["F"], _ptr(sh["wg"]), _ptr(sh["wu"]), _ptr(sh["wd"]),
                _ptr(sh["sg"]), _ptr(sh["su"]), _ptr(sh["sd"]), int(sh.get("layout", LAYOUT_ROWS)))
 
@@ -249,6 +301,8 @@ def pack_tiled(fmt: int, W: torch.Tensor, count: int, O: int, I: int, dst: torch
         raise ColiError(ESHAPE, "coli_tiled_bytes")
     if dst is None:
         dst = torch.empty((max(nb, 16),), dtype=torch.uint8, device=W.device)
+    _need(W, count * O * row_bytes(fmt, I), "pack_tiled W")
+    _need(dst, nb, "pack_tiled dst")
     rc = lib().coli_pack_tiled(fmt, _ptr(W), count, O, I, _ptr(dst), _stream(stream))
     _check(rc, "coli_pack_tiled")
     return dst
@@ -287,15 +341,26 @@ def alloc_workspace(nbytes: int, device) -> torch.Tensor:
     return t
 
 
+def _check_layer_io(ex: dict, x, S: int, K: int, out, tensors_sk: dict):
+    """x and out hold S rows of the experts' width; each routing tensor S K."""
+    D = ex["D"]
+    if x.dim() != 2 or x.shape[1] != D:
+        raise ColiError(ESHAPE, f"x must be [S, {D}] (the experts' width), got {tuple(x.shape)}")
+    _need(out, 4 * S * D, "out")
+    for name, t in tensors_sk.items():
+        _need(t, 4 * S * K, name)
+
+
 def moe_gemv(ex: dict, x, idx, w, out=None, prec=PREC_FP32, ws=None, stream=None):
     S, D = x.shape
     K = idx.shape[1]
     if out is None:
         out = torch.empty((S, D), dtype=torch.float32, device=x.device)
+    _check_layer_io(ex, x, S, K, out, {"idx": idx, "w": w})
+    es = experts_struct(ex)
     nb = moe_workspace_bytes(S, K, ex["E"], D, ex["F"], 0, prec)
     if ws is None:
         ws = alloc_workspace(nb, x.device)
-    es = experts_struct(ex)
     rc = lib().coli_moe_gemv(C.byref(es), _ptr(x), S, K, _ptr(idx), _ptr(w), _ptr(out), prec,
                              _ptr(ws), ws.numel(), _stream(stream))
     _check(rc, "coli_moe_gemv")
@@ -319,12 +384,15 @@ def moe_layer_tail(router_p: dict | None, ex: dict, shared: dict | None, x, norm
         K = router_p["K"] if router_p else pre_idx.shape[1]
     if out is None:
         out = torch.empty((S, D), dtype=torch.float32, device=x.device)
+    _check_layer_io(ex, x, S, K, out, {"pre_idx": pre_idx, "pre_w": pre_w, "idx_out": idx_out,
+                                       "w_out": w_out})
+    _need(norm_w, 4 * D, "norm_w")
+    rp = _router_struct(router_p, K)
+    es = experts_struct(ex)
+    sp = C.byref(mlp_struct(shared, D)) if shared is not None else None
     Fs = shared["F"] if shared is not None else 0
     if ws is None:
         ws = alloc_workspace(moe_workspace_bytes(S, K, ex["E"], D, ex["F"], Fs, prec), x.device)
-    rp = _router_struct(router_p, K)
-    es = experts_struct(ex)
-    sp = C.byref(mlp_struct(shared)) if shared is not None else None
     rc = lib().coli_moe_layer_tail(C.byref(rp), C.byref(es), sp, _ptr(x), _ptr(norm_w), float(eps), S,
                                    _ptr(pre_idx), _ptr(pre_w), _ptr(out), _ptr(idx_out), _ptr(w_out),
                                    prec, _ptr(ws), ws.numel(), _stream(stream))
@@ -339,13 +407,15 @@ def moe_layer(router_p: dict | None, ex: dict, shared: dict | None, x, pre_idx=N
         K = router_p["K"] if router_p else pre_idx.shape[1]
     if out is None:
         out = torch.empty((S, D), dtype=torch.float32, device=x.device)
+    _check_layer_io(ex, x, S, K, out, {"pre_idx": pre_idx, "pre_w": pre_w, "idx_out": idx_out,
+                                       "w_out": w_out})
+    rp = _router_struct(router_p, K)
+    es = experts_struct(ex)
+    sp = C.byref(mlp_struct(shared, D)) if shared is not None else None
     Fs = shared["F"] if shared is not None else 0
     nb = moe_workspace_bytes(S, K, ex["E"], D, ex["F"], Fs, prec)
     if ws is None:
         ws = alloc_workspace(nb, x.device)
-    rp = _router_struct(router_p, K)
-    es = experts_struct(ex)
-    sp = C.byref(mlp_struct(shared)) if shared is not None else None
     rc = lib().coli_moe_layer(C.byref(rp), C.byref(es), sp, _ptr(x), S, _ptr(pre_idx),
                               _ptr(pre_w), _ptr(out), _ptr(idx_out), _ptr(w_out), prec,
                               _ptr(ws), ws.numel(), _stream(stream))
@@ -358,12 +428,14 @@ def moe_layer_noalloc(router_p: dict | None, ex: dict, shared: dict | None, x, o
     """coli_moe_layer on the library's static scratch: the caller passes every
     input and output (out included); nothing is allocated.  Returns the
     status code."""
-    S = x.shape[0]
+    S, D = x.shape
     if K is None:
         K = router_p["K"] if router_p else pre_idx.shape[1]
+    _check_layer_io(ex, x, S, K, out, {"pre_idx": pre_idx, "pre_w": pre_w, "idx_out": idx_out,
+                                       "w_out": w_out})
     rp = _router_struct(router_p, K)
     es = experts_struct(ex)
-    sp = C.byref(mlp_struct(shared)) if shared is not None else None
+    sp = C.byref(mlp_struct(shared, D)) if shared is not None else None
     return int(lib().coli_moe_layer_noalloc(C.byref(rp), C.byref(es), sp, _ptr(x), S, _ptr(pre_idx),
                                             _ptr(pre_w), _ptr(out), _ptr(idx_out), _ptr(w_out), prec,
                                             _stream(stream)))

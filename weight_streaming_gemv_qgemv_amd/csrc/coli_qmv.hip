@@ -42,6 +42,40 @@ __device__ __forceinline__ uint32_t hilo_pair(float a, float b, float lo)
     return __builtin_bit_cast(uint32_t, r);
 }
 
+// Staging loads of one run of RUN activations (elements e0 .. e0 + RUN - 1
+// of row xr): unconditional 16-byte loads, from the run when it lies whole
+// inside the row, else from x0 (the first row's first elements, always in
+// bounds: rows hold at least RUN elements on these kernels) -- a value the
+// staging then discards: it stages zeros for a run past the row end, and
+// reads the one run crossing it element by element in a branch of its own.  A divergent choice between vector and element loads writing
+// the same registers made the compiler wait for the first loads before
+// issuing the second, for every run, before the weight loads were issued.
+template <int RUN>
+__device__ __forceinline__ void xrun_issue(const float *xr, const float *x0, int e0, int I,
+                                           float4 (&v)[RUN / 4])
+{
+    const float *src = e0 + RUN <= I ? xr + e0 : x0;
+#pragma unroll
+    for (int i = 0; i < RUN / 4; ++i) v[i] = gload4f(src + 4 * i);
+}
+template <int RUN>
+__device__ __forceinline__ void xrun_values(const float4 (&xv)[RUN / 4], float (&v)[RUN])
+{
+#pragma unroll
+    for (int i = 0; i < RUN / 4; ++i) {
+        v[4 * i] = xv[i].x;
+        v[4 * i + 1] = xv[i].y;
+        v[4 * i + 2] = xv[i].z;
+        v[4 * i + 3] = xv[i].w;
+    }
+}
+template <int RUN>
+__device__ __forceinline__ void xrun_elements(const float *xr, int e0, int I, float (&v)[RUN])
+{
+#pragma unroll
+    for (int i = 0; i < RUN; ++i) v[i] = e0 + i < I ? xr[e0 + i] : 0.f;
+}
+
 template <int FMT, int MT>
 __global__ __launch_bounds__(512) void k_qmv(QmvArgs a)
 {
@@ -127,32 +161,29 @@ __global__ __launch_bounds__(512) void k_qmv(QmvArgs a)
             if (u >= RUNS_PER_ROW * nt) break;   // live rows only
             const int t = u / RUNS_PER_ROW;
             const int e0 = (u % RUNS_PER_ROW) * RUN;   // inside the round
-            float v[RUN];
-#pragma unroll
-            for (int i = 0; i < RUN / 4; ++i) {
-                v[4 * i] = xv[p][i].x;
-                v[4 * i + 1] = xv[p][i].y;
-                v[4 * i + 2] = xv[p][i].z;
-                v[4 * i + 3] = xv[p][i].w;
-            }
             int c, j;
             pos_of<FMT>(e0, c, j);   // chunk inside the round (k-blocks from 0)
+            auto put = [&](const float (&v)[RUN]) {
 #pragma unroll
-            for (int h = 0; h < RUN / 8; ++h) {
-                uint32_t hw[4], lw[4];
+                for (int h = 0; h < RUN / 8; ++h) {
+                    uint32_t hw[4], lw[4];
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    int k0, k1;
-                    if constexpr (FMT == kI8) { k0 = 2 * m; k1 = 2 * m + 1; }
-                    else if constexpr (FMT == kI4) { k0 = m; k1 = m + 4; }
-                    else { k0 = m + 4 * h; k1 = m + 4 * h + 8; }
-                    hw[m] = hilo_pair(v[k0], v[k1], 0.f);
-                    lw[m] = hilo_pair(v[k0], v[k1], 1.f);
+                    for (int m = 0; m < 4; ++m) {
+                        int k0, k1;
+                        if constexpr (FMT == kI8) { k0 = 2 * m; k1 = 2 * m + 1; }
+                        else if constexpr (FMT == kI4) { k0 = m; k1 = m + 4; }
+                        else { k0 = m + 4 * h; k1 = m + 4 * h + 8; }
+                        hw[m] = hilo_pair(v[k0], v[k1], 0.f);
+                        lw[m] = hilo_pair(v[k0], v[k1], 1.f);
+                    }
+                    uint4 *dst = buf + (c + 4 * h) * cs + 2 * t;
+                    dst[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+                    dst[1] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
                 }
-                uint4 *dst = buf + (c + 4 * h) * cs + 2 * t;
-                dst[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-                dst[1] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-            }
+            };
+            float v[RUN];
+            xrun_values<RUN>(xv[p], v);   // loadX left zeros past I
+            put(v);
         }
     };
     auto compute = [&](uint4 (&w)[MT][SEGS], const uint4 *buf) {
@@ -252,9 +283,12 @@ __global__ __launch_bounds__(512) void k_qmv(QmvArgs a)
 
 // ---------------------------------------------------------------- one shot
 // For few activation rows the whole product fits one round: a block of 8
-// waves owns 16 output rows for a pass of up to kQ1Tpp activation rows,
-// wave w takes the NKW consecutive k-blocks w NKW, ... of the rows, and
-// every weight load of the block is issued before anything waits.  The
+// waves owns MTB tiles of 16 output rows for a pass of up to kQ1Tpp
+// activation rows, wave w takes the NKW consecutive k-blocks w NKW, ... of
+// the rows, and every weight load of the block is issued before anything
+// waits.  Several tiles per block keep the launch near one block per CU
+// (12288 rows: 256 blocks of 48 rows) -- fewer, longer-lived waves, and
+// the activations staged once per 16 MTB rows.  The
 // pass's activations (the full width, as bf16 hi/lo units in fragment order)
 // are staged into LDS while the weights are in flight; their loads are
 // issued first, so the wait for them leaves the weight loads outstanding.
@@ -262,7 +296,7 @@ __global__ __launch_bounds__(512) void k_qmv(QmvArgs a)
 // each other, so the later passes find the tile's weights in that XCD's L2.
 constexpr int kQ1Tpp = 2;   // activation rows per pass
 
-template <int FMT, int NKW>
+template <int FMT, int NKW, int MTB>
 __global__ __launch_bounds__(512) void k_qmv1(QmvArgs a, int passes, int ntiles)
 {
     using T = MF<FMT>;
@@ -278,9 +312,9 @@ __global__ __launch_bounds__(512) void k_qmv1(QmvArgs a, int passes, int ntiles)
     const int col = lane & 15, q = lane >> 4, lrow = lane >> 2, lchunk = lane & 3;
     const int src4 = 4 * (4 * col + q);
     const int xcd = blockIdx.x % 8, jb = blockIdx.x / 8;
-    const int tile = (jb / passes) * 8 + xcd, pass = jb % passes;
-    if (tile >= ntiles) return;                           // whole block, before any barrier
-    const int row0 = tile * 16;
+    const int tgroup = (jb / passes) * 8 + xcd, pass = jb % passes;
+    if (tgroup * MTB >= ntiles) return;                   // whole block, before any barrier
+    const int row0 = tgroup * MTB * 16;                   // the block's first row
     const int t0 = pass * kQ1Tpp;
     const int nt = min(kQ1Tpp, a.S - t0);
     const int nkb = a.nkb;
@@ -290,11 +324,11 @@ __global__ __launch_bounds__(512) void k_qmv1(QmvArgs a, int passes, int ntiles)
     const int kw0 = wave * NKW;
     const int rw = max(0, min(RW, (nkb - kw0) * (KB / RUN)));   // live runs per row
 
-    // wave 0 finishes the block: its 4 scales per lane are requested first
+    // wave mt < MTB finishes tile mt: its 4 scales per lane are requested first
     float scp[4] = {1.f, 1.f, 1.f, 1.f};
-    if (wave == 0 && a.scale) {
+    if (wave < MTB && a.scale) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) scp[r] = a.scale[min(row0 + 4 * q + r, a.O - 1)];
+        for (int r = 0; r < 4; ++r) scp[r] = a.scale[min(row0 + 16 * wave + 4 * q + r, a.O - 1)];
     }
     // activations next: each wave stages the runs of its own k-blocks (a
     // lane's dead runs read nothing: they start at I)
@@ -304,31 +338,23 @@ __global__ __launch_bounds__(512) void k_qmv1(QmvArgs a, int passes, int ntiles)
         const int u = lane + kWave * p;
         const bool live = u < RW * nt && u % RW < rw;
         const int t = live ? u / RW : 0, e0 = live ? kw0 * KB + (u % RW) * RUN : a.I;
-        const float *xr = a.x + (int64_t)(t0 + t) * a.I;
-        if (e0 + RUN <= a.I) {
-#pragma unroll
-            for (int i = 0; i < RUN / 4; ++i) xv[p][i] = gload4f(xr + e0 + 4 * i);
-        } else {
-#pragma unroll
-            for (int i = 0; i < RUN / 4; ++i) {
-                float f[4];
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) f[jj] = e0 + 4 * i + jj < a.I ? xr[e0 + 4 * i + jj] : 0.f;
-                xv[p][i] = make_float4(f[0], f[1], f[2], f[3]);
-            }
-        }
+        xrun_issue<RUN>(a.x + (int64_t)(t0 + t) * a.I, a.x, e0, a.I, xv[p]);
     }
     // then every weight load of this wave (a clamped copy for k-blocks past
     // the end: the loads stay unconditional, the products are skipped)
     const uint32_t coff = (uint32_t)min(16 * lchunk, (int)(a.rb - 16));   // short rows: see k_qmv
-    const uint32_t roff = (uint32_t)(min(row0 + lrow, a.O - 1) * a.rb) + coff;
     const uint32_t last_seg = (uint32_t)(a.rb - 16) - coff;
-    uint4 w[NKW][SEGS];
+    uint4 w[MTB][NKW][SEGS];
 #pragma unroll
-    for (int i = 0; i < NKW; ++i) {
-        const uint32_t b0 = (uint32_t)min(wave * NKW + i, nkb - 1) * kbytes;
+    for (int mt = 0; mt < MTB; ++mt) {
+        const uint32_t roff = (uint32_t)(min(row0 + 16 * mt + lrow, a.O - 1) * a.rb) + coff;
 #pragma unroll
-        for (int sg = 0; sg < SEGS; ++sg) w[i][sg] = gload16(a.W + (roff + min(b0 + 64 * sg, last_seg)));
+        for (int i = 0; i < NKW; ++i) {
+            const uint32_t b0 = (uint32_t)min(wave * NKW + i, nkb - 1) * kbytes;
+#pragma unroll
+            for (int sg = 0; sg < SEGS; ++sg)
+                w[mt][i][sg] = gload16(a.W + (roff + min(b0 + 64 * sg, last_seg)));
+        }
     }
     // stage: run -> bf16 hi (column 2t) and lo (column 2t+1) units; the
     // wave reads back only what it wrote, so no block barrier is needed
@@ -338,35 +364,43 @@ __global__ __launch_bounds__(512) void k_qmv1(QmvArgs a, int passes, int ntiles)
         if (u >= RW * nt) break;
         if (u % RW >= rw) continue;                   // past the last k-block
         const int t = u / RW, e0 = kw0 * KB + (u % RW) * RUN;
-        float v[RUN];
-#pragma unroll
-        for (int i = 0; i < RUN / 4; ++i) {
-            v[4 * i] = xv[p][i].x;
-            v[4 * i + 1] = xv[p][i].y;
-            v[4 * i + 2] = xv[p][i].z;
-            v[4 * i + 3] = xv[p][i].w;
-        }
         int c, j;
         pos_of<FMT>(e0, c, j);
+        auto put = [&](const float (&v)[RUN]) {
 #pragma unroll
-        for (int h = 0; h < RUN / 8; ++h) {
-            uint32_t hw[4], lw[4];
+            for (int h = 0; h < RUN / 8; ++h) {
+                uint32_t hw[4], lw[4];
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                int k0, k1;
-                if constexpr (FMT == kI8) { k0 = 2 * m; k1 = 2 * m + 1; }
-                else if constexpr (FMT == kI4) { k0 = m; k1 = m + 4; }
-                else { k0 = m + 4 * h; k1 = m + 4 * h + 8; }
-                hw[m] = hilo_pair(v[k0], v[k1], 0.f);
-                lw[m] = hilo_pair(v[k0], v[k1], 1.f);
+                for (int m = 0; m < 4; ++m) {
+                    int k0, k1;
+                    if constexpr (FMT == kI8) { k0 = 2 * m; k1 = 2 * m + 1; }
+                    else if constexpr (FMT == kI4) { k0 = m; k1 = m + 4; }
+                    else { k0 = m + 4 * h; k1 = m + 4 * h + 8; }
+                    hw[m] = hilo_pair(v[k0], v[k1], 0.f);
+                    lw[m] = hilo_pair(v[k0], v[k1], 1.f);
+                }
+                uint4 *dst = lds + (c + 4 * h) * cs + 2 * t;
+                dst[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+                dst[1] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
             }
-            uint4 *dst = lds + (c + 4 * h) * cs + 2 * t;
-            dst[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-            dst[1] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        };
+        float v[RUN];
+        if (e0 + RUN <= a.I) {
+            xrun_values<RUN>(xv[p], v);
+            put(v);
+        } else if (e0 >= a.I) {   // the k-block's padding past the row end
+#pragma unroll
+            for (int i = 0; i < RUN; ++i) v[i] = 0.f;
+            put(v);
+        } else {   // the run crossing the row end
+            xrun_elements<RUN>(a.x + (int64_t)(t0 + t) * a.I, e0, a.I, v);
+            put(v);
         }
     }
 
-    floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f}, accs = floatx4{0.f, 0.f, 0.f, 0.f};
+    floatx4 acc[MTB], accs = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int mt = 0; mt < MTB; ++mt) acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
     const uint32_t one2 = opaque_v(0x3F803F80u);   // bf16 (1, 1)
     const uint4 ones = make_uint4(one2, one2, one2, one2);
     // dead columns read the last live row's units
@@ -376,38 +410,44 @@ __global__ __launch_bounds__(512) void k_qmv1(QmvArgs a, int passes, int ntiles)
         const int kb = wave * NKW + i;
         if (kb >= nkb) break;                         // uniform
 #pragma unroll
-        for (int sg = 0; sg < SEGS; ++sg) {
-            const uint4 u = w[i][sg];
-            w[i][sg] = make_uint4((uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)u.x),
-                                  (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)u.y),
-                                  (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)u.z),
-                                  (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)u.w));
-        }
+        for (int mt = 0; mt < MTB; ++mt)
+#pragma unroll
+            for (int sg = 0; sg < SEGS; ++sg) {
+                const uint4 u = w[mt][i][sg];
+                w[mt][i][sg] = make_uint4((uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)u.x),
+                                          (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)u.y),
+                                          (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)u.z),
+                                          (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)u.w));
+            }
         const uint4 *bw = lds + (kb * STEPS * 4 + q) * cs + bcol;
 #pragma unroll
         for (int s2 = 0; s2 < STEPS; ++s2) {
             const uint4 b = bw[s2 * 4 * cs];
-            acc = mfma(codes<FMT>(w[i][s2 / SPS], s2 % SPS), b, acc);
+#pragma unroll
+            for (int mt = 0; mt < MTB; ++mt) acc[mt] = mfma(codes<FMT>(w[mt][i][s2 / SPS], s2 % SPS), b, acc[mt]);
             accs = mfma(ones, b, accs);
         }
     }
 
-    // partial tiles of the 8 waves, added in wave order
+    // partial tiles of the 8 waves, added in wave order; wave mt < MTB adds
+    // tile mt
     __syncthreads();   // every wave is done with the staged activations
     floatx4 *red = reinterpret_cast<floatx4 *>(lds);
-    red[(2 * wave) * kWave + lane] = acc;
-    red[(2 * wave + 1) * kWave + lane] = accs;
+#pragma unroll
+    for (int mt = 0; mt < MTB; ++mt) red[(wave * (MTB + 1) + mt) * kWave + lane] = acc[mt];
+    red[(wave * (MTB + 1) + MTB) * kWave + lane] = accs;
     __syncthreads();
-    if (wave != 0) return;
-    floatx4 v = red[lane], xs4 = red[kWave + lane];
+    if (wave >= MTB) return;
+    const int mt = wave;
+    floatx4 v = red[mt * kWave + lane], xs4 = red[MTB * kWave + lane];
 #pragma unroll
     for (int ww = 1; ww < kQmvWaves; ++ww) {
-        v += red[(2 * ww) * kWave + lane];
-        xs4 += red[(2 * ww + 1) * kWave + lane];
+        v += red[(ww * (MTB + 1) + mt) * kWave + lane];
+        xs4 += red[(ww * (MTB + 1) + MTB) * kWave + lane];
     }
     // D[4q + r][col]: the lo column is added to the hi one
     const float xs = xs4[0] + __shfl_xor(xs4[0], 1, kWave);
-    const int ob = row0 + 4 * q;
+    const int ob = row0 + 16 * mt + 4 * q;
     float res[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -427,18 +467,19 @@ __global__ __launch_bounds__(512) void k_qmv1(QmvArgs a, int passes, int ntiles)
     }
 }
 
-template <int FMT, int NKW>
+template <int FMT, int NKW, int MTB>
 hipError_t launch_q1(const QmvArgs &a, hipStream_t st)
 {
     const int ntiles = (a.O + 15) / 16;
+    const int ngroups = (ntiles + MTB - 1) / MTB;
     const int passes = (a.S + kQ1Tpp - 1) / kQ1Tpp;
-    const int64_t grid = (int64_t)(ntiles + 7) / 8 * 8 * passes;
+    const int64_t grid = (int64_t)(ngroups + 7) / 8 * 8 * passes;
     if (grid <= 0 || grid > 0x7FFFFFFF) return hipErrorInvalidValue;
     const int ntmax = a.S < kQ1Tpp ? a.S : kQ1Tpp;
     const size_t stage = (size_t)a.nkb * MF<FMT>::STEPS * 4 * (2 * ntmax) * 16;
-    const size_t red = (size_t)kQmvWaves * 2 * kWave * 16;
+    const size_t red = (size_t)kQmvWaves * (MTB + 1) * kWave * 16;
     const size_t lds = stage > red ? stage : red;
-    auto kern = k_qmv1<FMT, NKW>;
+    auto kern = k_qmv1<FMT, NKW, MTB>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
@@ -447,16 +488,29 @@ hipError_t launch_q1(const QmvArgs &a, hipStream_t st)
     return hipGetLastError();
 }
 
+// Tiles per block: about one block per CU (256), at most three, and at most
+// as many weight loads per wave as measured to fit the registers.
+template <int FMT, int NKW>
+hipError_t launch_q1_mtb(const QmvArgs &a, hipStream_t st)
+{
+    const int ntiles = (a.O + 15) / 16;
+    int mtb = (ntiles + 255) / 256;
+    if (mtb > 3) mtb = 3;
+    if (NKW * mtb > 9) mtb = 9 / NKW;
+    if (mtb >= 3) return launch_q1<FMT, NKW, (NKW <= 3 ? 3 : 1)>(a, st);
+    if (mtb == 2) return launch_q1<FMT, NKW, (NKW <= 4 ? 2 : 1)>(a, st);
+    return launch_q1<FMT, NKW, 1>(a, st);
+}
 template <int FMT>
 hipError_t launch_q1_nkw(const QmvArgs &a, int nkw, hipStream_t st)
 {
     switch (nkw) {
-    case 1: return launch_q1<FMT, 1>(a, st);
-    case 2: return launch_q1<FMT, 2>(a, st);
-    case 3: return launch_q1<FMT, 3>(a, st);
-    case 4: return launch_q1<FMT, 4>(a, st);
-    case 5: return launch_q1<FMT, 5>(a, st);
-    case 6: return launch_q1<FMT, 6>(a, st);
+    case 1: return launch_q1_mtb<FMT, 1>(a, st);
+    case 2: return launch_q1_mtb<FMT, 2>(a, st);
+    case 3: return launch_q1_mtb<FMT, 3>(a, st);
+    case 4: return launch_q1_mtb<FMT, 4>(a, st);
+    case 5: return launch_q1_mtb<FMT, 5>(a, st);
+    case 6: return launch_q1_mtb<FMT, 6>(a, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -553,19 +607,9 @@ __global__ __launch_bounds__(512) void k_qmvg(QmvArgs a, int passes, int ntiles)
         const int u = lane + kWave * p;
         const bool live = u < RW * nt && u % RW < rw;
         const int t = live ? u / RW : 0, e0 = live ? kw0 * KB + (u % RW) * RUN : a.I;
-        const float *xr = a.x + (int64_t)(t0 + t) * a.I;
-        if (e0 + RUN <= a.I) {
-#pragma unroll
-            for (int i = 0; i < RUN / 4; ++i) xv[p][i] = gload4f(xr + e0 + 4 * i);
-        } else {
-#pragma unroll
-            for (int i = 0; i < RUN / 4; ++i) {
-                float f[4];
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) f[jj] = e0 + 4 * i + jj < a.I ? xr[e0 + 4 * i + jj] : 0.f;
-                xv[p][i] = make_float4(f[0], f[1], f[2], f[3]);
-            }
-        }
+        // rows are whole 16-byte segments (I a multiple of 32): a live run
+        // is whole inside the row or wholly past it (staged as zeros)
+        xrun_issue<RUN>(a.x + (int64_t)(t0 + t) * a.I, a.x, e0, a.I, xv[p]);
     }
     // then every weight load of this wave
     const uint32_t coff = (uint32_t)min(16 * lchunk, (int)(a.rb - 16));   // short rows: see k_qmv
@@ -624,12 +668,12 @@ __global__ __launch_bounds__(512) void k_qmvg(QmvArgs a, int passes, int ntiles)
         if (u % RW >= rw) continue;
         const int t = u / RW, e0 = kw0 * KB + (u % RW) * RUN;
         float v[RUN];
+        // I is a multiple of 32: a run is whole inside the row or wholly in
+        // the k-block's padding past I (zeros)
+        xrun_values<RUN>(xv[p], v);
+        if (e0 >= a.I) {
 #pragma unroll
-        for (int i = 0; i < RUN / 4; ++i) {
-            v[4 * i] = xv[p][i].x;
-            v[4 * i + 1] = xv[p][i].y;
-            v[4 * i + 2] = xv[p][i].z;
-            v[4 * i + 3] = xv[p][i].w;
+            for (int i = 0; i < RUN; ++i) v[i] = 0.f;
         }
         int c, j;
         pos_of<kI4>(e0, c, j);
