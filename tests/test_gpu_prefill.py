@@ -110,3 +110,39 @@ def test_prefill_2048_tokens(dev, orc, glm_bank):
     ref = orc.moe(bank, shared, x[toks], idx[toks], w[toks].astype(np.float64))
     assert_within(out[toks], ref["out"], ref["mag"], REL, what="prefill2048")
     assert rel_l2(out[toks], ref["out"]) < 2e-2
+
+
+def expected_work(counts, extra, tpp=64):
+    """The prefill work list: entry g | pass << 11 for each tpp-row pass of
+    each group (experts, then the shared expert's group), sorted by the
+    pass's live 16-row tiles (4, 3, 2, 1), group and pass order inside a
+    class; ends = [total, end of class 0, .., end of class 3]."""
+    classes = [[] for _ in range(tpp // 16)]
+    for g, c in enumerate(list(counts) + [extra]):
+        for p in range(-(-int(c) // tpp)):
+            live = min(tpp, int(c) - p * tpp)
+            classes[tpp // 16 - -(-live // 16)].append(g | (p << 11))
+    ends = np.cumsum([len(c) for c in classes]).tolist()
+    return [e for c in classes for e in c], [ends[-1]] + ends
+
+
+@pytest.mark.parametrize("S,K,E", [(90, 3, 8), (300, 4, 16), (1000, 8, 64)])
+def test_prefill_work_list_classes(dev, S, K, E):
+    """The grouping's prefill work list, from both grouping paths (one
+    launch for at most 1024 slots, chunked beyond), exactly."""
+    from weight_streaming_gemv_qgemv_amd import binding as b
+    D, F = 256, 128
+    bank = synth.expert_bank(80, 2, E, D, F)
+    shared = synth.shared_mlp(80, 2, D, F)
+    g = synth.rng(81, S)
+    x = synth.activations(g, S, D)
+    idx, w = synth.routing_zipf(g, S, K, E)
+    announce("prefill work list", S, K, E)
+    _, ws = run_layer(dev, bank, shared, x, idx, w, PREC_BF16)
+    L = b.moe_workspace_layout(S, K, E, D, F, F, PREC_BF16)
+    raw = ws.cpu().numpy()
+    ends = raw[L["n_work"]:L["n_work"] + 20].view(np.int32)
+    want, want_ends = expected_work(np.bincount(idx.ravel(), minlength=E), S)
+    assert ends[:5].tolist() == want_ends
+    got = raw[L["work"]:L["work"] + 4 * len(want)].view(np.int32)
+    assert got.tolist() == want

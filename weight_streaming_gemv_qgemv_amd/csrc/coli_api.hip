@@ -33,6 +33,45 @@ namespace coli {
 namespace {
 
 constexpr int kGroupWaves = 16;          // experts per block in the grouping kernels
+constexpr int kWorkClasses = 4;          // classes of a class-sorted work list
+
+// Passes of a group of `rows` rows, counted by class into n[]: unsorted
+// (cls == 0) every pass is class 0; class-sorted, class c holds the passes
+// with tpp / 16 - c live 16-row tiles: the full passes in class 0 and the
+// last, partial pass in the class of its live tiles (tpp / 16 <= 4).
+__device__ __forceinline__ void add_passes(int rows, int tpp, int cls, int *n)
+{
+    if (!cls) {
+        n[0] += (rows + tpp - 1) / tpp;
+        return;
+    }
+    const int full = rows / tpp, rem = rows - full * tpp;
+    n[0] += full;
+    if (rem > 0) n[tpp / 16 - (rem + 15) / 16] += 1;
+}
+
+// Work-list entries of group g (rows rows): pass p goes to the slot of its
+// class, start[c] + pre[c] (+ p in class 0, which holds passes 0, 1, ...);
+// passes p0, p0 + step, ...
+__device__ __forceinline__ void write_passes(int32_t *work, int g, int rows, int tpp, int cls,
+                                             const int *start, const int *pre, int p0, int step)
+{
+    const int np = (rows + tpp - 1) / tpp;
+    for (int p = p0; p < np; p += step) {
+        const int live = min(tpp, rows - p * tpp);
+        const int c = cls ? tpp / 16 - (live + 15) / 16 : 0;
+        work[start[c] + pre[c] + (c == 0 ? p : 0)] = g | (p << 11);
+    }
+}
+
+// n_work[0] = the number of entries; class-sorted, n_work[1 + c] = the end
+// of class c.
+__device__ __forceinline__ void write_ends(int32_t *n_work, int cls, const int *start, const int *tot)
+{
+    n_work[0] = start[kWorkClasses - 1] + tot[kWorkClasses - 1];
+    if (cls)
+        for (int c = 0; c < kWorkClasses; ++c) n_work[1 + c] = start[c] + tot[c];
+}
 
 // Flags written by the grouping kernel (plain stores from block 0).
 constexpr uint32_t kFlagBadId = 1u;
@@ -45,9 +84,10 @@ constexpr uint32_t kFlagDup = 2u;
 // earlier launch.  Block 0 also writes the counts and validates every slot.
 // Each expert's wave then writes its offset and, when `work` is given, the
 // matrix-core work list entries of its group (passes of `tpp` rows, entry
-// g | pass << 11, in group order; the wave of the last expert adds those of
-// the extra group g = E (extra_rows rows) and the count), and scatters the
-// expert's slots into its group in slot order (stable).
+// g | pass << 11, in group order within each class, cls: sorted by class;
+// the wave of the last expert adds those of the extra group g = E
+// (extra_rows rows) and the ends), and scatters the expert's slots into its
+// group in slot order (stable).
 // XF >= 0: blocks gblocks .. gblocks + rows - 1 instead write the activation
 // row tables of the rows of x for weight format XF (coli_xrows.h), work
 // that does not depend on the routing and so shares the launch.
@@ -63,7 +103,7 @@ __global__ __launch_bounds__(1024) void k_group_one(const int32_t *__restrict__ 
                                                     int32_t *__restrict__ offsets,
                                                     int32_t *__restrict__ row_pair,
                                                     int32_t *__restrict__ pair_row, int extra_rows,
-                                                    int tpp, int32_t *__restrict__ work,
+                                                    int tpp, int cls, int32_t *__restrict__ work,
                                                     int32_t *__restrict__ n_work,
                                                     uint32_t *__restrict__ flags, int gblocks,
                                                     XrowsJob xj)
@@ -111,16 +151,25 @@ __global__ __launch_bounds__(1024) void k_group_one(const int32_t *__restrict__ 
         if (t == 0) flags[0] = sflag;
     }
     if (e >= E) return;   // whole waves; no barrier below
-    int part = 0, ppart = 0;
-    for (int j = lane; j < e; j += 64) {
+    // rows and passes per class of the experts before e (pre) and of all
+    // experts (tot)
+    int part = 0, pre[kWorkClasses] = {0, 0, 0, 0}, tot[kWorkClasses] = {0, 0, 0, 0};
+    for (int j = lane; j < E; j += 64) {
         const int c = cnt[j];
-        part += c;
-        ppart += (c + tpp - 1) / tpp;
+        if (j < e) {
+            part += c;
+            add_passes(c, tpp, cls, pre);
+        }
+        add_passes(c, tpp, cls, tot);
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
         part += __shfl_xor(part, o, kWave);
-        ppart += __shfl_xor(ppart, o, kWave);
+#pragma unroll
+        for (int c = 0; c < kWorkClasses; ++c) {
+            pre[c] += __shfl_xor(pre[c], o, kWave);
+            tot[c] += __shfl_xor(tot[c], o, kWave);
+        }
     }
     const int off = part;
     const int ce = cnt[e];
@@ -129,12 +178,17 @@ __global__ __launch_bounds__(1024) void k_group_one(const int32_t *__restrict__ 
         if (e == E - 1) offsets[E] = off + ce;
     }
     if (work) {
-        const int np = (ce + tpp - 1) / tpp;
-        for (int p = lane; p < np; p += 64) work[ppart + p] = e | (p << 11);
+        int xpre[kWorkClasses], start[kWorkClasses];
+#pragma unroll
+        for (int c = 0; c < kWorkClasses; ++c) xpre[c] = tot[c];   // the extra group follows every expert
+        add_passes(extra_rows, tpp, cls, tot);
+        start[0] = 0;
+#pragma unroll
+        for (int c = 1; c < kWorkClasses; ++c) start[c] = start[c - 1] + tot[c - 1];
+        write_passes(work, e, ce, tpp, cls, start, pre, lane, 64);
         if (e == E - 1) {
-            const int nx = (extra_rows + tpp - 1) / tpp;
-            for (int p = lane; p < nx; p += 64) work[ppart + np + p] = E | (p << 11);
-            if (lane == 0) *n_work = ppart + np + nx;
+            write_passes(work, E, extra_rows, tpp, cls, start, xpre, lane, 64);
+            if (lane == 0) write_ends(n_work, cls, start, tot);
         }
     }
     int run = 0;
@@ -205,14 +259,14 @@ __global__ __launch_bounds__(1024) void k_group_hist(const int32_t *__restrict__
 __global__ __launch_bounds__(1024) void k_group_prefix(int E, int C, int32_t *__restrict__ gpart,
                                                        int32_t *__restrict__ counts,
                                                        int32_t *__restrict__ offsets, int extra_rows,
-                                                       int tpp, int32_t *__restrict__ work,
+                                                       int tpp, int cls, int32_t *__restrict__ work,
                                                        int32_t *__restrict__ n_work,
                                                        uint32_t *__restrict__ flags)
 {
     // the per-chunk counts are read once, coalesced, into LDS when they fit
     // (C E <= 8192), so the per-expert loops below run on LDS
     __shared__ int32_t hs[8192];
-    __shared__ int32_t wsum[16][2];
+    __shared__ int32_t wsum[16][1 + kWorkClasses];
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const bool in_lds = (int64_t)C * E <= 8192;
     if (in_lds)
@@ -221,30 +275,57 @@ __global__ __launch_bounds__(1024) void k_group_prefix(int E, int C, int32_t *__
     int ce = 0;
     if (t < E)
         for (int c = 0; c < C; ++c) ce += in_lds ? hs[c * E + t] : gpart[(int64_t)c * E + t];
-    // exclusive prefix over experts of the counts and of the passes
-    int v = ce, pv = t < E ? (ce + tpp - 1) / tpp : 0;
+    // exclusive prefix over experts of the counts and of the passes per
+    // class; tot: the passes per class of all experts
+    int own[kWorkClasses] = {0, 0, 0, 0};
+    if (t < E) add_passes(ce, tpp, cls, own);
+    int v = ce, pv[kWorkClasses];
+#pragma unroll
+    for (int c = 0; c < kWorkClasses; ++c) pv[c] = own[c];
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-        const int a = __shfl_up(v, o, kWave), b = __shfl_up(pv, o, kWave);
-        if (lane >= o) { v += a; pv += b; }
+        const int a = __shfl_up(v, o, kWave);
+        if (lane >= o) v += a;
+#pragma unroll
+        for (int c = 0; c < kWorkClasses; ++c) {
+            const int b = __shfl_up(pv[c], o, kWave);
+            if (lane >= o) pv[c] += b;
+        }
     }
-    if (lane == 63) { wsum[wave][0] = v; wsum[wave][1] = pv; }
+    if (lane == 63) {
+        wsum[wave][0] = v;
+#pragma unroll
+        for (int c = 0; c < kWorkClasses; ++c) wsum[wave][1 + c] = pv[c];
+    }
     __syncthreads();
-    int wo = 0, wpo = 0;
-    for (int ww = 0; ww < wave; ++ww) { wo += wsum[ww][0]; wpo += wsum[ww][1]; }
+    int wo = 0, pre[kWorkClasses], tot[kWorkClasses];
+#pragma unroll
+    for (int c = 0; c < kWorkClasses; ++c) { pre[c] = pv[c] - own[c]; tot[c] = 0; }
+    for (int ww = 0; ww < 16; ++ww) {
+        if (ww < wave) wo += wsum[ww][0];
+#pragma unroll
+        for (int c = 0; c < kWorkClasses; ++c) {
+            if (ww < wave) pre[c] += wsum[ww][1 + c];
+            tot[c] += wsum[ww][1 + c];
+        }
+    }
     const int off = wo + v - ce;                                  // exclusive
-    const int np = t < E ? (ce + tpp - 1) / tpp : 0;
-    const int ppart = wpo + pv - np;
     if (t < E) {
         counts[t] = ce;
         offsets[t] = off;
         if (t == E - 1) offsets[E] = off + ce;
         if (work) {
-            for (int p = 0; p < np; ++p) work[ppart + p] = t | (p << 11);
+            int xpre[kWorkClasses], start[kWorkClasses];
+#pragma unroll
+            for (int c = 0; c < kWorkClasses; ++c) xpre[c] = tot[c];
+            add_passes(extra_rows, tpp, cls, tot);
+            start[0] = 0;
+#pragma unroll
+            for (int c = 1; c < kWorkClasses; ++c) start[c] = start[c - 1] + tot[c - 1];
+            write_passes(work, t, ce, tpp, cls, start, pre, 0, 1);
             if (t == E - 1) {
-                const int nx = (extra_rows + tpp - 1) / tpp;
-                for (int p = 0; p < nx; ++p) work[ppart + np + p] = E | (p << 11);
-                *n_work = ppart + np + nx;
+                write_passes(work, E, extra_rows, tpp, cls, start, xpre, 0, 1);
+                write_ends(n_work, cls, start, tot);
             }
         }
         // the chunks' first positions for expert t
@@ -536,7 +617,7 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
         err = hipGetLastError();
         if (err != hipSuccess) return COLI_EDEVICE;
         hipLaunchKernelGGL(k_group_prefix, dim3(1), dim3(1024), 0, st, E, C, gpart, counts, offsets,
-                           sh_mm ? S : 0, tpp, mm ? work : nullptr, n_work, flags);
+                           sh_mm ? S : 0, tpp, bf16, mm ? work : nullptr, n_work, flags);
         err = hipGetLastError();
         if (err != hipSuccess) return COLI_EDEVICE;
         hipLaunchKernelGGL(k_group_place, dim3(gblocks, C), dim3(1024), 0, st, idx, P, E, gpart,
@@ -548,7 +629,7 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
         const int xg = x_fused ? S : 0;
 #define COLI_GROUP_ONE(XF)                                                                         \
     hipLaunchKernelGGL(k_group_one<XF>, dim3(gblocks + xg), dim3(1024), 0, st, idx, P, K, E, counts, \
-                       offsets, row_pair, pair_row, sh_mm ? S : 0, tpp, mm ? work : nullptr, n_work, \
+                       offsets, row_pair, pair_row, sh_mm ? S : 0, tpp, bf16, mm ? work : nullptr, n_work, \
                        flags, gblocks, xj)
         if (!x_fused) COLI_GROUP_ONE(-1);
         else if (ex->fmt == kI8) COLI_GROUP_ONE(kI8);

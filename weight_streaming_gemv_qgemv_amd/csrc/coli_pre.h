@@ -9,8 +9,11 @@ namespace coli {
 
 // Rows per pass of the prefill kernels (4 MFMA N-tiles of 16 columns).
 constexpr int kPreTpp = 64;
-// Weight rows per item of the paired (M = 2) and single (M = 1) product.
-constexpr int kPreRowsPerBlock = 256;
+// Weight rows per item of the paired (M = 2: 8 waves x 32) and single
+// (M = 1: 8 waves x 64) product: the single product, with half the
+// accumulators, gives each wave more rows, so that each staged activation
+// unit meets as many weight rows.
+constexpr int pre_rows_per_item(int M) { return M == 2 ? 256 : 512; }
 
 // bf16 row tables: one row per activation row, kpad elements rounded once to
 // bf16 in fragment order (16-byte units of 8 elements), 2 * kpad bytes a row.

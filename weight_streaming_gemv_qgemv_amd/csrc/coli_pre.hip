@@ -11,15 +11,16 @@
 // sum(x) being the sum of the stored bf16 activations of the row, is
 // removed per output.
 //
-// An item is (group-pass, 256 weight rows); a block of 8 waves takes it,
-// each wave 32 weight rows x all 64 pass rows (4 MFMA N-tiles), so each
-// weight byte read from memory meets 64 activation rows.  Per k-block the
-// pass rows' activations are staged from their bf16 row tables into LDS
-// (double-buffered, units XOR-swizzled by chunk so that the operand reads
-// spread over the banks), while each wave has
-// the next k-block's weights in flight.  The row-table rows of an item's pass
-// rows and their activation sums are fetched one item ahead into LDS, so
-// no wait on global memory ever drains the weight stream.
+// An item is (group-pass, 256 weight rows for gate/up, 512 for down); a
+// block of 8 waves takes it, each wave 32 (64) weight rows x the pass's live
+// rows (up to 4 MFMA N-tiles of 16), so each weight byte read from memory
+// meets up to 64 activation rows.  Per k-block the pass rows' activations
+// are staged from their bf16 row tables into LDS (double-buffered, units
+// XOR-swizzled by chunk so that the operand reads spread over the banks),
+// while each wave has the next weights in flight (tiled weights: two
+// k-blocks ahead).  The row-table rows of an item's pass rows and their
+// activation sums are fetched one item ahead into LDS, so no wait on global
+// memory ever drains the weight stream.
 #include "coli_device.h"
 #include "coli_frag.h"
 #include "coli_pre.h"
@@ -33,7 +34,8 @@ typedef __attribute__((address_space(3))) const void lds_void;
 constexpr int kPreWaves = 8;
 constexpr int kPreXcds = 8;
 constexpr int kPreNT = kPreTpp / 16;   // N-tiles per pass
-constexpr int kPreMT = 2;              // 16-row weight tiles per wave
+constexpr int kPreMT = 2;              // 16-row weight tiles per wave (gate/up)
+constexpr int kPreMTDown = 4;          // the same for the single product (down)
 
 // ---------------------------------------------------------------- row tables
 template <int FMT>
@@ -130,8 +132,8 @@ __global__ __launch_bounds__(64 * kPreWaves) void k_pre(PreArgs a)
 {
     using T = MF<FMT>;
     constexpr int STEPS = T::STEPS, KB = T::KB, SEGS = T::SEGS, BITS = T::BITS, SPS = T::SPS;
-    constexpr int MT = kPreMT, NT = kPreNT, RPW = 16 * MT, RPB = kPreWaves * RPW;
-    static_assert(RPB == kPreRowsPerBlock, "rows per item");
+    constexpr int MT = M == 2 ? kPreMT : kPreMTDown, NT = kPreNT, RPW = 16 * MT, RPB = kPreWaves * RPW;
+    static_assert(RPB == pre_rows_per_item(M), "rows per item");
     constexpr float OFF = T::OFF;
     constexpr int CH = STEPS * 4;               // 16-byte chunks of a row per k-block
     constexpr int UNITS = CH * kPreTpp;         // units of one staged k-block
@@ -144,14 +146,6 @@ __global__ __launch_bounds__(64 * kPreWaves) void k_pre(PreArgs a)
     const int col = lane & 15, q = lane >> 4;
     const int xcd = blockIdx.x % kPreXcds, lb = blockIdx.x / kPreXcds;
     const int bpx = gridDim.x / kPreXcds;               // grid is a multiple of 8
-    // XCD x: a contiguous run of group-passes, tile-major: the blocks of an
-    // XCD work on one weight tile for consecutive passes at a time, so the
-    // passes of a large group read that tile together from the XCD's L2
-    const int n_gp = cload(a.n_work);
-    const int gp_lo = (int)((int64_t)n_gp * xcd / kPreXcds);
-    const int gp_cnt = (int)((int64_t)n_gp * (xcd + 1) / kPreXcds) - gp_lo;
-    const int n_items = gp_cnt * a.tiles;
-    if (lb >= n_items) return;                          // whole block, before any barrier
     const int nkb = a.kpad / KB;                        // even and >= 4
     // a chunk past the end of a row shorter than 64 bytes is read at the
     // row's last chunk (it meets zero activations)
@@ -162,6 +156,25 @@ __global__ __launch_bounds__(64 * kPreWaves) void k_pre(PreArgs a)
     const int ns = (int)((a.rb + 63) / 64);
     const uint8_t *actb = reinterpret_cast<const uint8_t *>(a.act);
     const uint32_t arow = (uint32_t)(2 * a.kpad);       // bytes per row-table row
+    const int dq = (lane & 3) ^ ((lane >> 3) & 3);
+
+    // The work list is sorted by the passes' live N-tiles (NL = 4, 3, 2, 1:
+    // with skewed routing most groups are a few rows, and a pass multiplies
+    // only its live tiles); the classes run one after the other, each with
+    // its own code, so no N-tile branch sits in the product loop.
+    auto run = [&](auto nlc, int w0, int w1) {
+    constexpr int NL = decltype(nlc)::value;
+    // XCD x: a contiguous run of the class's group-passes, pass-major: the
+    // blocks of an XCD work on all weight tiles of a few consecutive passes
+    // at a time, so a pass's activations are read from memory once for all
+    // its tiles, and consecutive passes of a large group share each tile's
+    // weights through the XCD's L2 (this measured less memory traffic and
+    // time than tile-major order)
+    const int n_gp = w1 - w0;
+    const int gp_lo = w0 + (int)((int64_t)n_gp * xcd / kPreXcds);
+    const int gp_cnt = w0 + (int)((int64_t)n_gp * (xcd + 1) / kPreXcds) - gp_lo;
+    const int n_items = gp_cnt * a.tiles;
+    if (lb >= n_items) return;                          // whole block, before any barrier
 
     struct It {
         int gp, tile, nt, r0t, Og;
@@ -172,8 +185,8 @@ __global__ __launch_bounds__(64 * kPreWaves) void k_pre(PreArgs a)
         uint32_t gstr;       // tiled: bytes from one segment's unit to the next
     };
     auto make = [&](It &c, int it) {
-        c.gp = __builtin_amdgcn_readfirstlane(gp_lo + it % gp_cnt);
-        c.tile = __builtin_amdgcn_readfirstlane(it / gp_cnt);
+        c.gp = __builtin_amdgcn_readfirstlane(gp_lo + it / a.tiles);
+        c.tile = __builtin_amdgcn_readfirstlane(it % a.tiles);
         const int wv = cload(a.work + c.gp);
         const int g = wv & 0x7FF, pass = wv >> 11;
         const bool extra = a.has_extra && g == a.ngroups;
@@ -248,6 +261,14 @@ __global__ __launch_bounds__(64 * kPreWaves) void k_pre(PreArgs a)
                 for (int sg = 0; sg < SEGS; ++sg)
                     w[m][mt][sg] = gload16(c.wb[m] + (c.roff[mt] + min(b0 + 64 * sg, last_seg)));
     };
+    // tiled: segment sg of k-block kbi of item c's weights into w[.][.][sg]
+    auto loadSeg = [&](const It &c, int kbi, int sg, uint4 (&w)[M][MT][SEGS]) {
+        const uint32_t go = (uint32_t)min(kbi * SEGS + sg, ns - 1) * c.gstr;
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) w[m][mt][sg] = gload16(c.wb[m] + (c.roff[mt] + go));
+    };
     // Staging by LDS DMA (each lane's 16 bytes land at the instruction's LDS
     // base + 16 lane): staged unit (pass row t = 16 n + col, chunk c = 4 s +
     // q) sits at ((n STEPS + s) 16 + col) 4 + (q ^ ((col >> 1) & 3)), a
@@ -255,46 +276,49 @@ __global__ __launch_bounds__(64 * kPreWaves) void k_pre(PreArgs a)
     // bank conflicts on gfx950 (q ^ (col >> 2) cost 4 conflict cycles per
     // read).  One instruction fills one (n, s): lane L takes row 16 n + L / 4
     // and chunk 4 s + ((L & 3) ^ ((L >> 3) & 3)) -- 64 contiguous bytes of
-    // each of 16 rows.
-    // Wave w issues instructions w SPW .. w SPW + SPW - 1 of the NT x STEPS
-    // (N-tile nw, steps s0..).
-    constexpr int SPW = NT * STEPS / kPreWaves;          // instructions per wave
-    static_assert(SPW >= 1 && STEPS % SPW == 0, "a wave stages steps of one N-tile");
-    const int nw = wave * SPW / STEPS, s0 = wave * SPW % STEPS;
-    const int dq = (lane & 3) ^ ((lane >> 3) & 3);
+    // each of 16 rows.  Instruction i = n STEPS + s of the NL x STEPS is
+    // issued by wave i % 8.
+    constexpr int NI = NL * STEPS, IPW = (NI + kPreWaves - 1) / kPreWaves;
     auto stageB = [&](int par, int kbi, const uint4 *buf) {
-        const uint32_t rowoff = (uint32_t)lrow[par][16 * nw + (lane >> 2)] * arow +
-                                (uint32_t)kbi * (CH * 16) + (uint32_t)(s0 * 64 + dq * 16);
-        const uint32_t lbase = (uint32_t)(uintptr_t)(const lds_void *)(buf + (nw * STEPS + s0) * 64);
+        const uint32_t lbuf = (uint32_t)(uintptr_t)(const lds_void *)buf;
 #pragma unroll
-        for (int i = 0; i < SPW; ++i)
-            dma16(actb + (rowoff + (uint32_t)i * 64), __builtin_amdgcn_readfirstlane(lbase + i * 1024));
+        for (int j = 0; j < IPW; ++j) {
+            const int i = wave + kPreWaves * j;
+            if (NI % kPreWaves == 0 || i < NI) {        // uniform
+                const int n = i / STEPS, s = i % STEPS;
+                const uint32_t rowoff = (uint32_t)lrow[par][16 * n + (lane >> 2)] * arow +
+                                        (uint32_t)kbi * (CH * 16) + (uint32_t)(s * 64 + dq * 16);
+                dma16(actb + rowoff, __builtin_amdgcn_readfirstlane(lbuf + (uint32_t)i * 1024));
+            }
+        }
     };
 
-    floatx4 acc[M][MT][NT];
+    floatx4 acc[M][MT][NL];
 #pragma unroll
     for (int m = 0; m < M; ++m)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int n = 0; n < NT; ++n) acc[m][mt][n] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int n = 0; n < NL; ++n) acc[m][mt][n] = floatx4{0.f, 0.f, 0.f, 0.f};
 
     // one k-block: per MFMA step the live N-tiles' activation units from LDS
-    // and the M x MT x NT products; the weights were loaded in the operand
+    // and the M x MT x NL products; the weights were loaded in the operand
     // layout (lane (q, col) holds row col, chunk q of each 64-byte segment)
-    auto compute = [&](const uint4 (&w)[M][MT][SEGS], const uint4 *buf, int ntl) {
+    // (sg >= 0: only the steps of segment sg)
+    auto compute = [&](const uint4 (&w)[M][MT][SEGS], const uint4 *buf, int sg = -1) {
 #pragma unroll
         for (int s2 = 0; s2 < STEPS; ++s2) {
-            uint4 b[NT];
+            if (sg >= 0 && s2 / SPS != sg) continue;
+            uint4 b[NL];
 #pragma unroll
-            for (int n = 0; n < NT; ++n) b[n] = buf[((n * STEPS + s2) * 16 + col) * 4 + (q ^ ((col >> 1) & 3))];
+            for (int n = 0; n < NL; ++n) b[n] = buf[((n * STEPS + s2) * 16 + col) * 4 + (q ^ ((col >> 1) & 3))];
 #pragma unroll
             for (int m = 0; m < M; ++m)
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
                     const uint4 cw = codes<FMT>(w[m][mt][s2 / SPS], s2 % SPS);
 #pragma unroll
-                    for (int n = 0; n < NT; ++n) acc[m][mt][n] = mfma(cw, b[n], acc[m][mt][n]);
+                    for (int n = 0; n < NL; ++n) acc[m][mt][n] = mfma(cw, b[n], acc[m][mt][n]);
                 }
         }
     };
@@ -312,13 +336,19 @@ __global__ __launch_bounds__(64 * kPreWaves) void k_pre(PreArgs a)
     };
     // D[4q + r][col] of tile (m, mt, n): weight row obase + 16 mt + 4 q + r,
     // pass row 16 n + col; xsv[n]: that row's activation sum
-    float xsv[NT];
-    auto epilogue = [&](const It &c) {
+    float xsv[NL];
+    // Stores of the uniform fast path (the wave's rows inside the matrix and,
+    // for gate/up, inside h's row table; 16-byte result stores): per N-tile
+    // one per row tile, and for gate/up one more per row tile (h) and one
+    // (its partial sums).  Every one is issued: each of the NL tiles has a
+    // live row.
+    constexpr int kStores = NL * (MT + (M == 2 ? MT + 1 : 0));
+    // returns kStores on the fast path, else 0
+    auto epilogue = [&](const It &c) -> int {
         const int obase = c.tile * RPB + wave * RPW;
-        const int ntl = (c.nt + 15) / 16;
+        const bool fast = a.out_vec4 && obase + RPW <= c.Og && (M == 1 || obase + RPW <= a.hf_kpad);
 #pragma unroll
-        for (int n = 0; n < NT; ++n) {
-            if (n >= ntl) break;                      // uniform
+        for (int n = 0; n < NL; ++n) {
             const int t = 16 * n + col;
             const bool live = t < c.nt;
             const int64_t gr = c.r0t + t;
@@ -338,7 +368,7 @@ __global__ __launch_bounds__(64 * kPreWaves) void k_pre(PreArgs a)
                 }
                 if (live) {
                     float *op = a.out + gr * a.ldo;
-                    if (a.out_vec4 && ob + 3 < c.Og) {
+                    if (fast || (a.out_vec4 && ob + 3 < c.Og)) {
                         *reinterpret_cast<float4 *>(op + ob) = make_float4(res[0], res[1], res[2], res[3]);
                     } else {
 #pragma unroll
@@ -361,7 +391,7 @@ __global__ __launch_bounds__(64 * kPreWaves) void k_pre(PreArgs a)
                     uint32_t pv[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) pv[r] = (uint32_t)__shfl_xor((int)hv[r], PX, kWave);
-                    if (lowq && live && ob < a.hf_kpad) {
+                    if (lowq && live && (fast || ob < a.hf_kpad)) {
                         int cc, j;
                         pos_of<FMT>(ob, cc, j);
                         uint4 u;
@@ -388,7 +418,8 @@ __global__ __launch_bounds__(64 * kPreWaves) void k_pre(PreArgs a)
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int n = 0; n < NT; ++n) acc[m][mt][n] = floatx4{0.f, 0.f, 0.f, 0.f};
+                for (int n = 0; n < NL; ++n) acc[m][mt][n] = floatx4{0.f, 0.f, 0.f, 0.f};
+        return fast ? kStores : 0;
     };
 
     // the staged k-block is complete once this wave's DMA loads are: they
@@ -411,12 +442,12 @@ __global__ __launch_bounds__(64 * kPreWaves) void k_pre(PreArgs a)
         asm volatile("" ::: "memory");
     };
     auto half = [&](const uint4 *rd, const uint4 *wr, int spar, int skb, const It &wsrc, int wkb,
-                    uint4 (&wn)[M][MT][SEGS], const uint4 (&wc)[M][MT][SEGS], int ntl) {
+                    uint4 (&wn)[M][MT][SEGS], const uint4 (&wc)[M][MT][SEGS]) {
         loadW(wsrc, wkb, wn);
         step_sync();
         stageB(spar, skb, wr);
         __builtin_amdgcn_sched_barrier(0);
-        compute(wc, rd, ntl);
+        compute(wc, rd);
         __builtin_amdgcn_sched_barrier(0);
     };
 
@@ -436,35 +467,124 @@ __global__ __launch_bounds__(64 * kPreWaves) void k_pre(PreArgs a)
     loadW(cur, 0, wA);
     stageB(0, 0, bsA);
     int jn = lb + bpx;
+
+    if constexpr (TILED) {
+        // Tiled weights: the loads of k-block j + 2 are issued into k-block
+        // j's registers while j is multiplied, segment by segment as each is
+        // consumed, so the wait at k-block j + 2 is for loads issued two
+        // k-blocks earlier.  VMEM order per k-block j: wait, barrier, DMA of
+        // j + 1, [the epilogue's scale loads], products of j with W(j + 2)
+        // after each segment.  The wait before j needs W(j) and DMA(j): only
+        // W(j + 1) (NW), plus what came after it -- the next item's pass-row
+        // loads (2, or 1 without a row map) and the last epilogue's stores --
+        // may stay in flight.
+        // K-blocks past an item's end are the next item's first two (the
+        // block's last item re-reads its own last k-block, from L2).
+        loadW(cur, 1, wB);
+        auto wait_vm = [&](auto nc) {
+            constexpr int N = decltype(nc)::value;
+            static_assert(N < 64, "vmcnt field");
+            __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+        };
+        // after is 0, or the pass-row loads (nlist: 2 with a row map, else
+        // 1) plus 0 or kStores
+        const int nlist = a.act_row ? 2 : 1;
+        auto sync_x = [&](int after) {
+            asm volatile("" ::: "memory");
+            if (after == 2 + kStores) wait_vm(std::integral_constant<int, NW + 2 + kStores>{});
+            else if (after == 1 + kStores) wait_vm(std::integral_constant<int, NW + 1 + kStores>{});
+            else if (after == 2) wait_vm(std::integral_constant<int, NW + 2>{});
+            else if (after == 1) wait_vm(std::integral_constant<int, NW + 1>{});
+            else wait_vm(std::integral_constant<int, NW>{});
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        };
+        // products of k-block kb from w and buf; DMA of (spar, skb) into
+        // nbuf; W(lc, lkb) recycled into w
+        auto kstep = [&](uint4 (&w)[M][MT][SEGS], const uint4 *buf, int spar, int skb, const uint4 *nbuf,
+                         const It &lc, int lkb, bool epi = false, int after = 0) {
+            sync_x(after);
+            stageB(spar, skb, nbuf);
+            if (epi) load_epi(cur);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int sg = 0; sg < SEGS; ++sg) {
+                compute(w, buf, sg);
+                __builtin_amdgcn_sched_barrier(0);
+                loadSeg(lc, lkb, sg, w);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        int stores = 0;
+        for (;;) {
+            const bool has_nxt = jn < n_items;
+            It nxt = cur;
+            if (has_nxt) make(nxt, jn);
+            int ar;
+            float rs;
+            loadList(nxt, ar, rs);
+            kstep(wA, bsA, par, 1, bsB, cur, 2, false, nlist + stores);
+            storeList(par ^ 1, ar, rs);
+            kstep(wB, bsB, par, 2, bsA, cur, 3);
+            for (int k = 2; k < nkb - 2; k += 2) {
+                kstep(wA, bsA, par, k + 1, bsB, cur, k + 2);
+                kstep(wB, bsB, par, k + 2, bsA, cur, k + 3);
+            }
+            kstep(wA, bsA, par, nkb - 1, bsB, has_nxt ? nxt : cur, has_nxt ? 0 : nkb - 1, true);
+#pragma unroll
+            for (int n = 0; n < NL; ++n) xsv[n] = lsum[par][min(16 * n + col, cur.nt - 1)];
+            kstep(wB, bsB, par ^ 1, 0, bsA, has_nxt ? nxt : cur, has_nxt ? 1 : nkb - 1);
+            stores = epilogue(cur);
+            if (!has_nxt) break;
+            cur = nxt;
+            par ^= 1;
+            jn += bpx;
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        return;
+    }
     // Even k-blocks are staged in bsA, odd ones in bsB (nkb is even).
     for (;;) {
         const bool has_nxt = jn < n_items;
         It nxt = cur;
         if (has_nxt) make(nxt, jn);
-        const int ntl = (cur.nt + 15) / 16;        // live N-tiles
         int ar;
         float rs;
         loadList(nxt, ar, rs);     // stored after the first k-block
         for (int k = 0; k < nkb - 2; k += 2) {
-            half(bsA, bsB, par, k + 1, cur, k + 1, wB, wA, ntl);
+            half(bsA, bsB, par, k + 1, cur, k + 1, wB, wA);
             if (k == 0) storeList(par ^ 1, ar, rs);
-            half(bsB, bsA, par, k + 2, cur, k + 2, wA, wB, ntl);
+            half(bsB, bsA, par, k + 2, cur, k + 2, wA, wB);
         }
         // last two k-blocks: the epilogue's scales and row sums, then the
         // next item's first k-block (a copy of this item's when there is none)
         load_epi(cur);
-        half(bsA, bsB, par, nkb - 1, cur, nkb - 1, wB, wA, ntl);
+        half(bsA, bsB, par, nkb - 1, cur, nkb - 1, wB, wA);
 #pragma unroll
-        for (int n = 0; n < NT; ++n) xsv[n] = lsum[par][min(16 * n + col, cur.nt - 1)];
-        half(bsB, bsA, par ^ 1, 0, nxt, 0, wA, wB, ntl);
-        epilogue(cur);
+        for (int n = 0; n < NL; ++n) xsv[n] = lsum[par][min(16 * n + col, cur.nt - 1)];
+        half(bsB, bsA, par ^ 1, 0, nxt, 0, wA, wB);
+        (void)epilogue(cur);
         if (!has_nxt) break;
         cur = nxt;
         par ^= 1;
         jn += bpx;
     }
-    // every wave's DMA is complete before the block ends
+    // every wave's DMA is complete before the class ends (the next class's
+    // first DMA, after a barrier, may fill the same LDS)
     __builtin_amdgcn_s_waitcnt(0);
+    };
+
+    static_assert(NT == 4, "classes of 4, 3, 2 and 1 live N-tiles");
+    const int e0 = cload(a.n_work + 1), e1 = cload(a.n_work + 2), e2 = cload(a.n_work + 3);
+    const int e3 = cload(a.n_work + 4);
+    run(std::integral_constant<int, 4>{}, 0, e0);
+    __syncthreads();
+    run(std::integral_constant<int, 3>{}, e0, e1);
+    __syncthreads();
+    run(std::integral_constant<int, 2>{}, e1, e2);
+    __syncthreads();
+    run(std::integral_constant<int, 1>{}, e2, e3);
 }
 
 int pre_resident_blocks(const void *kern, int *cache)
@@ -497,7 +617,7 @@ hipError_t launch_pre(const PreArgs &a, int64_t items, hipStream_t st)
 
 }  // namespace
 
-int pre_parts(int hf_kpad) { return (hf_kpad + kPreRowsPerBlock - 1) / kPreRowsPerBlock * kPreWaves; }
+int pre_parts(int hf_kpad) { return (hf_kpad + pre_rows_per_item(2) - 1) / pre_rows_per_item(2) * kPreWaves; }
 
 hipError_t xrows_bf16_launch(int fmt, const float *x, int64_t ldx, int rows, int I, int kpad,
                              uint16_t *table, float *sums, hipStream_t st)
@@ -536,7 +656,7 @@ hipError_t pre_launch(PreArgs a, int fmt, int M, int64_t max_group_passes, hipSt
     int Ocover = a.O;
     if (M == 2 && a.hf && a.hf_kpad > Ocover) Ocover = a.hf_kpad;
     if (a.has_extra && a.xO > Ocover) Ocover = a.xO;
-    a.tiles = (Ocover + kPreRowsPerBlock - 1) / kPreRowsPerBlock;
+    a.tiles = (Ocover + pre_rows_per_item(M) - 1) / pre_rows_per_item(M);
     if (M == 2 && a.nparts < a.tiles * kPreWaves) return hipErrorInvalidValue;
     const int64_t items = max_group_passes * a.tiles;
 #define COLI_PRE_CASES(MM, TT)                                      \
