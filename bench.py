@@ -84,27 +84,73 @@ def clone_bank(bd):
     return out
 
 
+def source_hash(files):
+    """sha256 over the named kernel sources (repository-relative), in order."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(os.path.dirname(os.path.abspath(__file__)), f), "rb").read())
+    return h.hexdigest()
+
+
+def profile_record(fname, tag, workload):
+    """The machine-readable line `tag: {json}` of a committed rocprofv3
+    summary under profiles/, or None when the file or line is missing, it is
+    for another workload, or the kernel sources it names have changed since
+    the profile was taken (sha256 over them)."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", fname)
+    try:
+        line = next(l for l in open(path) if l.startswith(tag + ": "))
+        rec = json.loads(line[len(tag) + 2:])
+        if rec.get("workload") != workload or source_hash(rec["sources"]) != rec.get("sha256"):
+            return None
+    except (OSError, StopIteration, ValueError, KeyError, TypeError):
+        return None
+    return rec
+
+
+PROFILE_FILES = {"moe_layer_decode_64": ("moe_layer_decode64_kernels.md", "moe_layer_decode64_traffic.md"),
+                 "moe_layer_prefill_2048_bf16": ("moe_layer_prefill2048_kernels.md",
+                                                 "moe_layer_prefill2048_traffic.md")}
+
+
 def recorded_traffic(workload, kernel_key):
     """HBM bytes per launch of one kernel from the committed rocprofv3
     counter summary (FETCH_SIZE + WRITE_SIZE, calibrated against a plain
-    copy), or None when there is none for this workload or the kernel source
-    has changed since the counters were taken."""
-    import hashlib
-    files = {"moe_layer_decode_64": "moe_layer_decode64_traffic.md",
-             "moe_layer_prefill_2048_bf16": "moe_layer_prefill2048_traffic.md"}
-    if workload not in files:
+    copy), or None when there is none for this workload or the kernel sources
+    have changed since the counters were taken."""
+    if workload not in PROFILE_FILES:
         return None
-    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", files[workload])
-    try:
-        line = next(l for l in open(path) if l.startswith("traffic-json: "))
-        rec = json.loads(line[len("traffic-json: "):])
-        src = open(os.path.join(os.path.dirname(os.path.abspath(__file__)), rec["source"]), "rb").read()
-    except (OSError, StopIteration, ValueError, KeyError):
-        return None
-    if rec.get("workload") != workload or hashlib.sha256(src).hexdigest() != rec.get("sha256"):
-        return None
-    k = rec.get("per_launch", {}).get(kernel_key)
+    rec = profile_record(PROFILE_FILES[workload][1], "traffic-json", workload)
+    k = rec.get("per_launch", {}).get(kernel_key) if rec else None
     return None if k is None else int(k["fetch_bytes"] + k["write_bytes"])
+
+
+def recorded_trace_ms(workload, kernel_key):
+    """Average duration (ms) of one kernel in the committed rocprofv3 kernel
+    trace of this workload (the same bench command), or None as above."""
+    if workload not in PROFILE_FILES:
+        return None
+    rec = profile_record(PROFILE_FILES[workload][0], "trace-json", workload)
+    k = rec.get("avg_us", {}).get(kernel_key) if rec else None
+    return None if k is None else k * 1e-3
+
+
+def kernel_key(name, args):
+    """rocprofv3's name of the int4 gate/up kernel for the layout in use."""
+    return f"{name}<2, 2, {'true' if getattr(args, 'layout', 'rows') == 'tiled' else 'false'}>"
+
+
+def trace_roofline(dom, units_per_launch, peak):
+    """The roofline fraction implied by the committed rocprofv3 trace's
+    average duration of the dominant kernel (None when that trace is stale or
+    missing), beside the live event-based one."""
+    t = dom.get("trace_ms")
+    if not t:
+        return None
+    ach = units_per_launch / (t * 1e-3)
+    return {"ms_per_launch": round(t, 5), "achieved": round(ach, 2), "frac": round(ach / peak, 4),
+            "event_over_trace": round(dom["ms_per_launch"] / t, 4) if dom["ms_per_launch"] else None}
 
 
 REPS = 20
@@ -284,7 +330,8 @@ def run_layer64(args, dev, tail=False):
                dominant=dict(kernel="k_dec<I4,2> (grouped expert gate/up + SwiGLU, matrix cores)",
                              bytes_per_launch=gu_bytes, ms_per_launch=gu_ms / max(gu_n, 1),
                              launches=gu_n,
-                             traffic=recorded_traffic("moe_layer_decode_64", "k_dec<2, 2>")))
+                             traffic=recorded_traffic("moe_layer_decode_64", kernel_key("k_dec", args)),
+                             trace_ms=recorded_trace_ms("moe_layer_decode_64", kernel_key("k_dec", args))))
     if not args.no_cpu_baseline and not tail:
         ntok = args.cpu_tokens
         log(f"cpu baseline: oracle on {ntok} tokens")
@@ -362,7 +409,8 @@ def run_prefill2048(args, dev):
     return dict(workload="moe_layer_prefill_2048_bf16", ms=ms, wall=wall, step_bytes=step_bytes,
                 tokens=S, stages=stages, uniq=uniq, flops=flops, t_star=t_star,
                 dominant=dict(kernel="k_pre<I4,2> (grouped expert gate/up + SwiGLU, bf16 matrix cores)",
-                              traffic=recorded_traffic("moe_layer_prefill_2048_bf16", "k_pre<2, 2>"),
+                              traffic=recorded_traffic("moe_layer_prefill_2048_bf16", kernel_key("k_pre", args)),
+                              trace_ms=recorded_trace_ms("moe_layer_prefill_2048_bf16", kernel_key("k_pre", args)),
                               bytes_per_launch=(uniq + 1) * gu + S * D * 4 + rows * F * 4,
                               flops_per_launch=gu_flops, ms_per_launch=gu_ms / max(gu_n, 1),
                               launches=gu_n))
@@ -658,7 +706,8 @@ def main():
                      "frac": round(ach / HBM_PEAK_GBS, 4) if ach else None,
                      "traffic": dom.get("traffic"), "kernel": dom["kernel"],
                      "algorithmic_bytes_per_launch": dom["bytes_per_launch"],
-                     "ms_per_launch": round(dom["ms_per_launch"], 5)},
+                     "ms_per_launch": round(dom["ms_per_launch"], 5),
+                     "trace": trace_roofline(dom, dom["bytes_per_launch"] / 1e9, HBM_PEAK_GBS)},
         "context": {"pages_metal_moe_gemv_GBps": "358-389 (Apple-Silicon GPU, unified memory)"},
     }
     if "ep" in r:
@@ -674,7 +723,8 @@ def main():
                             "frac": round(tf / BF16_PEAK_TFLOPS, 4) if tf else None,
                             "traffic": dom.get("traffic"),
                             "kernel": dom["kernel"], "flops_per_launch": dom["flops_per_launch"],
-                            "ms_per_launch": round(dom["ms_per_launch"], 5)}
+                            "ms_per_launch": round(dom["ms_per_launch"], 5),
+                            "trace": trace_roofline(dom, dom["flops_per_launch"] / 1e12, BF16_PEAK_TFLOPS)}
         line["layer_mfma_utilisation"] = round(r["flops"] / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
         if "t_star" in r:
             line["per_expert_roofline"] = {"t_star_ms": round(r["t_star"] * 1e3, 5),
