@@ -653,7 +653,7 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
             if (xrows_launch(ex->fmt, x, D, S, D, kpD, xt, st) != hipSuccess) return COLI_EDEVICE;
         }
         {
-            StageTimer tgu(kStGateUp, st);
+            StageTimer tgu(kStGateUp, st, true);
             DecArgs a = {};
             a.w[0] = (const uint8_t *)ex->w_gate;
             a.w[1] = (const uint8_t *)ex->w_up;
@@ -692,7 +692,7 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
             if (dec_launch(a, ex->fmt, 2, max_gp, st) != hipSuccess) return COLI_EDEVICE;
         }
         {
-            StageTimer tdn(kStDown, st);
+            StageTimer tdn(kStDown, st, true);
             DecArgs d = {};
             d.w[0] = (const uint8_t *)ex->w_down;
             d.s[0] = ex->s_down;
@@ -753,7 +753,7 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
                 return COLI_EDEVICE;
         }
         {
-            StageTimer tgu(kStGateUp, st);
+            StageTimer tgu(kStGateUp, st, true);
             PreArgs a = {};
             a.w[0] = (const uint8_t *)ex->w_gate;
             a.w[1] = (const uint8_t *)ex->w_up;

@@ -28,8 +28,11 @@
 //     L2), persistent blocks walk them in order, and each wave loads the
 //     next k-block's weights while it multiplies the current one, and the
 //     next item's first k-block during the current item's last.
+#include <hip/hip_ext.h>
+
 #include "coli_device.h"
 #include "coli_frag.h"
+#include "coli_stages.h"
 #include "coli_dec.h"
 #include "coli_xrows.h"
 
@@ -629,7 +632,12 @@ hipError_t launch_dec(const DecArgs &a, int64_t items, hipStream_t st)
     int64_t grid = (items + kDecXcds - 1) / kDecXcds * kDecXcds;
     if (grid > cap) grid = cap;
     if (grid < kDecXcds) grid = kDecXcds;
-    hipLaunchKernelGGL((k_dec<FMT, M, TILED>), dim3((unsigned)grid), dim3(threads), 0, st, a);
+    const KernelEvents ev = take_kernel_events();   // timed stage: events at the kernel's bounds
+    if (ev.start)
+        hipExtLaunchKernelGGL((k_dec<FMT, M, TILED>), dim3((unsigned)grid), dim3(threads), 0, st, ev.start,
+                              ev.stop, 0, a);
+    else
+        hipLaunchKernelGGL((k_dec<FMT, M, TILED>), dim3((unsigned)grid), dim3(threads), 0, st, a);
     return hipGetLastError();
 }
 

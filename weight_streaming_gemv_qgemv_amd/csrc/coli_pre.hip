@@ -21,8 +21,11 @@
 // k-blocks ahead).  The row-table rows of an item's pass rows and their
 // activation sums are fetched one item ahead into LDS, so no wait on global
 // memory ever drains the weight stream.
+#include <hip/hip_ext.h>
+
 #include "coli_device.h"
 #include "coli_frag.h"
+#include "coli_stages.h"
 #include "coli_pre.h"
 
 namespace coli {
@@ -611,7 +614,12 @@ hipError_t launch_pre(const PreArgs &a, int64_t items, hipStream_t st)
     int64_t grid = (items + kPreXcds - 1) / kPreXcds * kPreXcds;
     if (grid > cap) grid = cap;
     if (grid < kPreXcds) grid = kPreXcds;
-    hipLaunchKernelGGL((k_pre<FMT, M, TILED>), dim3((unsigned)grid), dim3(64 * kPreWaves), 0, st, a);
+    const KernelEvents ev = take_kernel_events();   // timed stage: events at the kernel's bounds
+    if (ev.start)
+        hipExtLaunchKernelGGL((k_pre<FMT, M, TILED>), dim3((unsigned)grid), dim3(64 * kPreWaves), 0, st,
+                              ev.start, ev.stop, 0, a);
+    else
+        hipLaunchKernelGGL((k_pre<FMT, M, TILED>), dim3((unsigned)grid), dim3(64 * kPreWaves), 0, st, a);
     return hipGetLastError();
 }
 

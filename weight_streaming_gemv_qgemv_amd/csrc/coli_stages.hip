@@ -46,20 +46,52 @@ const char *const kNames[COLI_NSTAGES] = {"router", "group", "gate_up", "down", 
 
 }  // namespace
 
-StageTimer::StageTimer(int stage, hipStream_t st) : stage_(stage), st_(st)
+namespace {
+// the events a one-kernel stage offers its launch, and whether it took them
+thread_local KernelEvents t_offer;
+thread_local bool t_taken = false;
+}  // namespace
+
+KernelEvents take_kernel_events()
+{
+    KernelEvents e = t_offer;
+    t_offer = KernelEvents{};
+    if (e.start) t_taken = true;
+    return e;
+}
+
+StageTimer::StageTimer(int stage, hipStream_t st, bool one_kernel) : stage_(stage), st_(st)
 {
     std::lock_guard<std::mutex> g(g_mu);
     if (!g_on) return;
     a_ = take_event();
     b_ = take_event();
-    if (a_ && b_) (void)hipEventRecord((hipEvent_t)a_, st_);
+    if (!a_ || !b_) return;
+    one_ = one_kernel;
+    if (one_) {
+        t_offer = KernelEvents{(hipEvent_t)a_, (hipEvent_t)b_};
+        t_taken = false;
+    } else {
+        (void)hipEventRecord((hipEvent_t)a_, st_);
+    }
 }
 
 StageTimer::~StageTimer()
 {
     std::lock_guard<std::mutex> g(g_mu);
     if (!a_ || !b_) return;
-    (void)hipEventRecord((hipEvent_t)b_, st_);
+    if (one_) {
+        const bool used = t_taken;
+        t_offer = KernelEvents{};
+        t_taken = false;
+        if (!used) {   // no launch took them (an error path): nothing to time
+            g_pool.push_back((hipEvent_t)a_);
+            g_pool.push_back((hipEvent_t)b_);
+            return;
+        }
+    } else {
+        (void)hipEventRecord((hipEvent_t)b_, st_);
+    }
     g_pending.push_back(Rec{stage_, (hipEvent_t)a_, (hipEvent_t)b_});
 }
 
