@@ -526,6 +526,129 @@ int cor_qgemv_idot(int fmt, const void *W, const float *scale, const float *x,
 }
 
 /* ------------------------------------------------------------------------
+ * The MoE block on the integer-dot path [glm.c@98759bf -- moe, phase D, with
+ * the expert matmuls taking the IDOT branch of matmul_qt (matmul_q_idot /
+ * matmul_i4_idot)]: each product quantises its input row as cor_qrow_i8 does
+ * and takes the exact integer dot, scaled back in fp32 in the pages' order:
+ *   token row:  qx, sx = qrow_i8(x[s])        (once; every expert of the
+ *                                              token and the shared expert)
+ *   g[o] = ((float)dot(vg(o,.), qx) * sg[o]) * sx,   u[o] alike
+ *   h[o] = silu(g[o]) * u[o],  silu(z) = z / (1 + expf(-z)), each step fp32
+ *   qh, sh = qrow_i8(h)
+ *   y[o] = ((float)dot(vd(o,.), qh) * sd[o]) * sh
+ *   out[s] = sum_kk w[s,kk] y_kk + y_shared     (fp64 of the fp32 y)
+ * h_in (may be NULL): [pair_rows, F] fp32; when given, the down product of
+ * pair row p quantises h_in's row p instead of the h computed here (so a
+ * caller can check another implementation's down products on its own h).
+ * Outputs (each may be NULL): h_out [pair_rows, F], g_out [pair_rows, F] (the
+ * gate product) and y_out [pair_rows, D] fp32, pair row p = s K + kk, the
+ * shared expert's at S K + s (when pair_rows == S K + S).  Returns 0, -1 on an expert id >= E or an int16 /
+ * int2 format, -2 on allocation failure.
+ * ------------------------------------------------------------------------ */
+static void idot_rows(int fmt, const uint8_t *W, int64_t rb, const float *sc, int O, int I,
+                      const int8_t *q, float sq, float *out)
+{
+    for (int o = 0; o < O; ++o) {
+        const uint8_t *row = W + (int64_t)o * rb;
+        int64_t dot = 0;
+        for (int i = 0; i < I; ++i) dot += (int64_t)cor_unpack(fmt, row, i) * q[i];
+        volatile float d = (float)dot;
+        volatile float t = d * sc[o];
+        out[o] = t * sq;
+    }
+}
+
+static void idot_mlp(int fmt, int D, int F, const uint8_t *wg, const uint8_t *wu, const uint8_t *wd,
+                     const float *sg, const float *su, const float *sd, const int8_t *qx, float sx,
+                     const float *h_in, float *g, float *u, float *h, int8_t *qh, float *y)
+{
+    int64_t rbD = cor_row_bytes(fmt, D), rbF = cor_row_bytes(fmt, F);
+    idot_rows(fmt, wg, rbD, sg, F, D, qx, sx, g);
+    idot_rows(fmt, wu, rbD, su, F, D, qx, sx, u);
+    for (int o = 0; o < F; ++o) {
+        volatile float e = expf(-g[o]);
+        volatile float den = 1.0f + e;
+        volatile float sl = g[o] / den;
+        h[o] = sl * u[o];
+    }
+    float sh = cor_qrow_i8(h_in ? h_in : h, F, qh);
+    idot_rows(fmt, wd, rbF, sd, D, F, qh, sh, y);
+}
+
+int cor_moe_idot(const cor_experts *ex, const cor_mlp *sh, const float *x, int S, int K,
+                 const int32_t *idx, const double *w, const float *h_in, int64_t pair_rows,
+                 double *out, float *h_out, float *y_out, float *g_out)
+{
+    int E = ex->E, D = ex->D, F = ex->F, fmt = ex->fmt;
+    if (fmt != OR_I8 && fmt != OR_I4) return -1;
+    if (sh && (sh->fmt != fmt || sh->F != F)) return -1;
+    int64_t rbD = cor_row_bytes(fmt, D), rbF = cor_row_bytes(fmt, F);
+    for (int64_t p = 0; p < (int64_t)S * K; ++p)
+        if (idx[p] >= E) return -1;
+    int rc = 0;
+#pragma omp parallel
+    {
+        int8_t *qx = (int8_t *)malloc((size_t)D + 1), *qh = (int8_t *)malloc((size_t)F + 1);
+        float *g = (float *)malloc((size_t)F * sizeof(float)), *u = (float *)malloc((size_t)F * sizeof(float));
+        float *h = (float *)malloc((size_t)F * sizeof(float)), *y = (float *)malloc((size_t)D * sizeof(float));
+        int ok = qx && qh && g && u && h && y;
+        if (!ok) {
+#pragma omp atomic write
+            rc = -2;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int s = 0; s < S; ++s) {
+            if (!ok) continue;
+            double *os = out + (int64_t)s * D;
+            for (int d = 0; d < D; ++d) os[d] = 0.0;
+            float sx = cor_qrow_i8(x + (int64_t)s * D, D, qx);
+            for (int kk = 0; kk <= K; ++kk) {
+                int64_t p;
+                const uint8_t *wg, *wu, *wd;
+                const float *sg, *su, *sd;
+                double wk;
+                if (kk < K) {
+                    p = (int64_t)s * K + kk;
+                    int e = idx[p];
+                    if (e < 0) continue;
+                    wg = (const uint8_t *)ex->wg + (int64_t)e * F * rbD;
+                    wu = (const uint8_t *)ex->wu + (int64_t)e * F * rbD;
+                    wd = (const uint8_t *)ex->wd + (int64_t)e * D * rbF;
+                    sg = ex->sg + (int64_t)e * F;
+                    su = ex->su + (int64_t)e * F;
+                    sd = ex->sd + (int64_t)e * D;
+                    wk = w[p];
+                } else {
+                    if (!sh) break;
+                    p = (int64_t)S * K + s;
+                    wg = (const uint8_t *)sh->wg;
+                    wu = (const uint8_t *)sh->wu;
+                    wd = (const uint8_t *)sh->wd;
+                    sg = sh->sg;
+                    su = sh->su;
+                    sd = sh->sd;
+                    wk = 1.0;
+                }
+                const int have = p < pair_rows;
+                idot_mlp(fmt, D, F, wg, wu, wd, sg, su, sd, qx, sx,
+                         h_in && have ? h_in + p * F : NULL, g, u, h, qh, y);
+                for (int d = 0; d < D; ++d) os[d] += wk * (double)y[d];
+                if (h_out && have) memcpy(h_out + p * F, h, (size_t)F * sizeof(float));
+                if (y_out && have) memcpy(y_out + p * D, y, (size_t)D * sizeof(float));
+                if (g_out && have) memcpy(g_out + p * F, g, (size_t)F * sizeof(float));
+            }
+        }
+        free(qx);
+        free(qh);
+        free(g);
+        free(u);
+        free(h);
+        free(y);
+    }
+    return rc;
+}
+
+/* ------------------------------------------------------------------------
  * Layer tail around the MoE block [glm.c@98759bf -- rmsnorm; the layer
  * forward's post-attention half]: the residual stream x is normalised with
  * the post-attention RMSNorm, the MoE block runs on the normalised rows, and

@@ -61,6 +61,8 @@ def lib():
         L.cor_qgemv_grouped.argtypes = [vp, vp, i32, vp, i32, i32, i32, vp, vp]
         L.cor_qrow_i8.restype = C.c_float
         L.cor_qrow_i8.argtypes = [vp, i32, vp]
+        L.cor_moe_idot.restype = i32
+        L.cor_moe_idot.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, i64, vp, vp, vp, vp]
         L.cor_qgemv_idot.restype = i32
         L.cor_qgemv_idot.argtypes = [i32, vp, vp, vp, i32, i32, i32, vp, vp]
         L.cor_rmsnorm.restype = None
@@ -199,6 +201,50 @@ def moe(ex: dict, shared: dict | None, x, idx, w, intermediates: bool = False):
                        rows, *ptrs)
     assert rc == 0, rc
     return res
+
+
+def moe_idot(ex: dict, shared: dict | None, x, idx, w, h_in=None):
+    """MoE output on the pages' integer-dot path (int8 / int4 experts): x
+    quantised per token, every product an exact integer dot with the pages'
+    fp32 epilogue, h = silu(g) * u in fp32, quantised per row for the down
+    product.  Arrays as for moe().  h_in: optional [S*K (+ S), F] fp32 rows
+    (pair numbering) the down products quantise instead of the oracle's own h.
+    Returns dict(out fp64 [S, D], h, g fp32 [rows, F], y fp32 [rows, D]);
+    g is the gate product (the argument of silu)."""
+    x = _c(np.atleast_2d(x), np.float32)
+    idx = _c(idx, np.int32)
+    wd = _c(w, np.float64)
+    S, K = idx.shape
+    D, F = ex["D"], ex["F"]
+    keep = [x, idx, wd]
+
+    def arr(a):
+        a = np.ascontiguousarray(a)
+        keep.append(a)
+        return _p(a)
+
+    e = _Experts(ex["fmt"], ex["E"], D, F, arr(ex["wg"]), arr(ex["wu"]), arr(ex["wd"]),
+                 arr(_c(ex["sg"], np.float32)), arr(_c(ex["su"], np.float32)),
+                 arr(_c(ex["sd"], np.float32)))
+    sp = None
+    if shared is not None:
+        sm = _Mlp(shared["fmt"], shared["F"], arr(shared["wg"]), arr(shared["wu"]),
+                  arr(shared["wd"]), arr(_c(shared["sg"], np.float32)),
+                  arr(_c(shared["su"], np.float32)), arr(_c(shared["sd"], np.float32)))
+        sp = C.pointer(sm)
+    rows = S * K + (S if shared is not None else 0)
+    hin = None
+    if h_in is not None:
+        hin = _c(h_in, np.float32)
+        assert hin.shape == (rows, F)
+    out = np.empty((S, D), np.float64)
+    h = np.zeros((rows, F), np.float32)
+    y = np.zeros((rows, D), np.float32)
+    gv = np.zeros((rows, F), np.float32)
+    rc = lib().cor_moe_idot(C.byref(e), sp, _p(x), S, K, _p(idx), _p(wd),
+                            _p(hin) if hin is not None else None, rows, _p(out), _p(h), _p(y), _p(gv))
+    assert rc == 0, rc
+    return dict(out=out, h=h, y=y, g=gv)
 
 
 def qgemv_grouped(W, scale, gs: int, x, O: int | None = None):

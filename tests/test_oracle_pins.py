@@ -607,3 +607,70 @@ def test_grouped_exact_integers(orc):
                       for k in range(I // gs)], axis=-1)          # [S, O, ng]
     ref = (parts * sc[None, :, :].astype(np.float64)).sum(axis=-1)
     np.testing.assert_array_equal(y, ref)
+
+
+# ---------------------------------------------------------------- IDOT MoE
+def _silu_f32(z):
+    z = np.asarray(z, np.float32)
+    e = np.exp(-z).astype(np.float32)
+    return (z / (np.float32(1.0) + e)).astype(np.float32)
+
+
+@pytest.mark.parametrize("fmt", [1, 2])
+def test_moe_idot_one_expert_is_the_dense_idot_chain(orc, fmt):
+    """The integer-dot MoE block with one slot (w = 1, no shared expert)
+    reduces to the pinned dense IDOT products: g and u are qgemv_idot of x,
+    h = silu(g) * u in fp32 (to a few ulp: expf is the platform's), the
+    down output is qgemv_idot of the block's own h bit for bit, and out is
+    that y exactly."""
+    E, D, F, S = 3, 160, 96, 4
+    bank = synth.expert_bank(31, fmt, E, D, F)
+    g = synth.rng(32, fmt)
+    x = synth.activations(g, S, D)
+    e = 1
+    idx = np.full((S, 1), e, np.int32)
+    w = np.ones((S, 1), np.float32)
+    r = orc.moe_idot(bank, None, x, idx, w)
+    gv, _ = orc.qgemv_idot(fmt, bank["wg"][e], bank["sg"][e], x)
+    uv, _ = orc.qgemv_idot(fmt, bank["wu"][e], bank["su"][e], x)
+    h = (_silu_f32(gv) * uv).astype(np.float32)
+    np.testing.assert_allclose(r["h"], h, rtol=4e-7, atol=1e-30)
+    yv, _ = orc.qgemv_idot(fmt, bank["wd"][e], bank["sd"][e], r["h"])
+    np.testing.assert_array_equal(r["y"].view(np.uint32), yv.view(np.uint32))
+    np.testing.assert_array_equal(r["out"], yv.astype(np.float64))
+
+
+def test_moe_idot_h_in_feeds_the_down_product(orc):
+    """Given h_in, each pair's down product quantises h_in's row: y equals
+    qgemv_idot(Wd, h_in) bit for bit, whatever the block's own h was."""
+    fmt, E, D, F, S, K = 2, 4, 128, 64, 3, 2
+    bank = synth.expert_bank(33, fmt, E, D, F)
+    g = synth.rng(34)
+    x = synth.activations(g, S, D)
+    idx = np.array([[0, 3], [2, 1], [3, 0]], np.int32)
+    w = np.full((S, K), 0.5, np.float32)
+    h_in = g.standard_normal((S * K, F)).astype(np.float32)
+    r = orc.moe_idot(bank, None, x, idx, w, h_in=h_in)
+    for p in range(S * K):
+        e = idx.ravel()[p]
+        yv, _ = orc.qgemv_idot(fmt, bank["wd"][e], bank["sd"][e], h_in[p:p + 1])
+        np.testing.assert_array_equal(r["y"][p].view(np.uint32), yv[0].view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", [1, 2])
+def test_moe_idot_near_the_exact_block(orc, fmt):
+    """The lossy path stays near the exact fp64 block: every output row within
+    5% relative L2 (two int8 quantisations per token and expert; the pages
+    report about 0.3% RMS per product on real activations), so a dropped
+    term, a wrong scale or a misrouted row fails."""
+    E, D, F, S, K = 6, 256, 128, 6, 3
+    bank = synth.expert_bank(35, fmt, E, D, F)
+    shared = synth.shared_mlp(35, fmt, D, F)
+    g = synth.rng(36, fmt)
+    x = synth.activations(g, S, D)
+    idx, w = synth.routing_uniform(g, S, K, E)
+    r = orc.moe_idot(bank, shared, x, idx, w)
+    ref = orc.moe(bank, shared, x, idx, w.astype(np.float64))["out"]
+    err = np.linalg.norm(r["out"] - ref, axis=1) / np.linalg.norm(ref, axis=1)
+    assert err.max() < 5e-2, err
+    assert err.max() > 1e-5   # it is the lossy path, not the exact one
