@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 matrix peak
+INT8_PEAK_TOPS = 5000.0         # MI355X dense int8 matrix peak (TOP/s)
 METRIC = "int4 expert-GEMV HBM GB/s (% of peak) + MoE-layer decode tokens/s"
 
 
@@ -391,11 +392,13 @@ def run_prefill2048(args, dev):
     Wrd, bd_bias = to_dev(Wr, dev), to_dev(bias, dev)
     out = torch.empty((S, D), dtype=torch.float32, device=dev)
     rws = b.alloc_workspace(b.router_workspace_bytes(S, E, D), dev)
-    ws = b.alloc_workspace(b.moe_workspace_bytes(S, K, E, D, F, F, 1), dev)
+    ws = b.alloc_workspace(b.moe_workspace_bytes(S, K, E, D, F, F, 2 if args.idot else 1), dev)
+
+    prec = 2 if args.idot else 1
 
     def step(i):
         b.router(Wrd, bd_bias, xd, K, 1, 2.5, 0.0, ws=rws)
-        b.moe_layer(None, bd, sd, xd, pre_idx=idd, pre_w=wd, out=out, prec=1, ws=ws)
+        b.moe_layer(None, bd, sd, xd, pre_idx=idd, pre_w=wd, out=out, prec=prec, ws=ws)
 
     uniq = int(np.unique(idx).size)
     gu, dn = expert_bytes(fmt, D, F)
@@ -406,6 +409,16 @@ def run_prefill2048(args, dev):
     ms, wall, stages = time_steps(step, args.steps, args.warmup)
     gu_ms, gu_n = stages["gate_up"]
     gu_flops = 2 * rows * 2 * D * F
+    if args.idot:
+        # int8 activations on the int8 matrix cores: ops counted as the flops
+        # of the same products, against the int8 dense peak
+        return dict(workload="moe_layer_prefill_2048_idot", ms=ms, wall=wall, step_bytes=step_bytes,
+                    tokens=S, stages=stages, uniq=uniq, flops=flops, t_star=t_star, idot=True,
+                    dominant=dict(kernel="k_preid<I4,2> (grouped expert gate/up + SwiGLU, int8 matrix cores)",
+                                  traffic=None, trace_ms=None,
+                                  bytes_per_launch=(uniq + 1) * gu + S * D + rows * F * 4,
+                                  flops_per_launch=gu_flops, ms_per_launch=gu_ms / max(gu_n, 1),
+                                  launches=gu_n))
     return dict(workload="moe_layer_prefill_2048_bf16", ms=ms, wall=wall, step_bytes=step_bytes,
                 tokens=S, stages=stages, uniq=uniq, flops=flops, t_star=t_star,
                 dominant=dict(kernel="k_pre<I4,2> (grouped expert gate/up + SwiGLU, bf16 matrix cores)",
@@ -628,7 +641,8 @@ def main():
     ap.add_argument("--shape", default="12288x6144", metavar="OxI",
                     help="qgemv workload: output rows x input width (512x1024: the small, "
                          "L2-resident case, timed over a >= 1 GiB rotation of weight copies)")
-    ap.add_argument("--idot", action="store_true", help="qgemv workload: the integer-dot variant")
+    ap.add_argument("--idot", action="store_true",
+                    help="qgemv and prefill2048 workloads: the integer-dot (int8 activation) variant")
     ap.add_argument("--grouped", type=int, default=0, metavar="GS",
                     help="qgemv workload: grouped-scale int4, one scale per GS elements")
     ap.add_argument("--ep-slice", type=int, default=0, metavar="N",
@@ -656,6 +670,10 @@ def main():
     dev = torch.device("cuda:0")
     from weight_streaming_gemv_qgemv_amd import binding as b
     b.lib()
+    if args.idot and args.workload not in ("qgemv", "prefill2048"):
+        raise SystemExit("--idot applies to the qgemv and prefill2048 workloads")
+    if args.idot and args.workload == "prefill2048" and (args.layout != "tiled" or args.ep_slice):
+        raise SystemExit("prefill2048 --idot runs on the tiled layout, without --ep-slice")
     if args.workload == "copy":
         run_copy(args, dev)
         return
@@ -717,15 +735,17 @@ def main():
     if "flops" in r:
         # prefill: the matrix cores bound the dominant kernel
         tf = dom["flops_per_launch"] / (dom["ms_per_launch"] * 1e-3) / 1e12 if dom["ms_per_launch"] else None
-        line["dtype"] = "bf16 (int4 weights, fp32 accumulate)"
+        peak = INT8_PEAK_TOPS if r.get("idot") else BF16_PEAK_TFLOPS
+        line["dtype"] = ("int8 activations (per-row absmax/127) x int4 weights, exact int32 dot, "
+                         "fp32 epilogue" if r.get("idot") else "bf16 (int4 weights, fp32 accumulate)")
         line["roofline"] = {"bound": "mfma", "achieved": round(tf, 2) if tf else None,
-                            "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                            "frac": round(tf / BF16_PEAK_TFLOPS, 4) if tf else None,
+                            "peak": peak, "unit": "TOP/s" if r.get("idot") else "TFLOP/s",
+                            "frac": round(tf / peak, 4) if tf else None,
                             "traffic": dom.get("traffic"),
                             "kernel": dom["kernel"], "flops_per_launch": dom["flops_per_launch"],
                             "ms_per_launch": round(dom["ms_per_launch"], 5),
-                            "trace": trace_roofline(dom, dom["flops_per_launch"] / 1e12, BF16_PEAK_TFLOPS)}
-        line["layer_mfma_utilisation"] = round(r["flops"] / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
+                            "trace": trace_roofline(dom, dom["flops_per_launch"] / 1e12, peak)}
+        line["layer_mfma_utilisation"] = round(r["flops"] / (ms * 1e-3) / 1e12 / peak, 4)
         if "t_star" in r:
             line["per_expert_roofline"] = {"t_star_ms": round(r["t_star"] * 1e3, 5),
                                            "frac_of_step": round(r["t_star"] * 1e3 / ms, 4)}

@@ -78,8 +78,21 @@ enum coli_status {
  *     cores, fp32 accumulation, scale applied in fp32 after the sum, 64 rows
  *     per pass; bound 2e-2 of the same magnitude.  Meant for prefill-sized
  *     batches.  Shapes that take the vector-ALU kernels (rows that are not
- *     whole 16-byte segments) compute in fp32 under either value. */
-enum coli_prec { COLI_PREC_FP32 = 0, COLI_PREC_BF16 = 1 };
+ *     whole 16-byte segments) compute in fp32 under either value.
+ *   COLI_PREC_IDOT: the pages' integer-dot path [glm.c@98759bf -- qrow_i8,
+ *     dot_i4i8, dot_i8i8, matmul_q_idot; the moe block's expert matmuls]:
+ *     x per token, and h per grouped row, quantised to int8 by its absolute
+ *     maximum (s = max|v| / 127, at least 1e-12, q = round-half-even(v / s)
+ *     with 1/s in fp32), the dot with the int weight values exact in int32
+ *     (v_mfma_i32_16x16x64_i8), then ((float)dot * scale[o]) * s, rounded
+ *     in fp32 in that order; gate/up give h = silu(g) * u in fp32.  Lossy
+ *     by design (int8 activations, about 0.3% RMS per product on the
+ *     pages' measurements): every integer dot and its epilogue equal the
+ *     definition's bit for bit.  int8 or int4 experts in the tiled layout
+ *     only (and a shared expert of the same format, F and layout), D and F
+ *     at most 16384; else COLI_EFMT / COLI_EINVAL / COLI_ERANGE.  64 rows
+ *     per pass, as COLI_PREC_BF16. */
+enum coli_prec { COLI_PREC_FP32 = 0, COLI_PREC_BF16 = 1, COLI_PREC_IDOT = 2 };
 
 /* Bytes in one packed row of I elements, or -1 for an unknown fmt / I < 0
  * [glm.c@98759bf -- qt_bytes].  Host only; no device work. */
@@ -285,7 +298,11 @@ size_t coli_moe_workspace_bytes(int S, int K, int E, int D, int F,
  *              xsum = [S] per-token sums of the stored x, then per grouped
  *              row its xf row (int32) and activation sum; hsum = per grouped
  *              row KpF/32 partial sums of the stored h (KpF = F rounded up to
- *              1024), then their totals.
+ *              1024), then their totals; COLI_PREC_IDOT: int8 values (KpD,
+ *              resp. KpF, bytes a row), xsum = per token its scale and four
+ *              partial sums of its int8 values, then per grouped row its xf
+ *              row, scale and sum; hsum = per grouped row the scale and four
+ *              partial sums of h's int8 row, then its scale and sum.
  *   xn         [S, D] fp32: the RMSNorm rows coli_moe_layer_tail feeds the
  *              block.
  *   gpart      grouping of more than 1024 slots (S K > 1024): per chunk of
@@ -318,15 +335,15 @@ int coli_moe_workspace_layout(int S, int K, int E, int D, int F, int F_shared,
  *   ex     routed experts (device pointers inside; the struct itself is host).
  *   x      [S, D] fp32.   idx [S, K] int32: an expert id, or -1 = empty slot.
  *   w      [S, K] fp32.   out [S, D] fp32, overwritten.
- *   prec   COLI_PREC_FP32 or COLI_PREC_BF16.
+ *   prec   COLI_PREC_FP32, COLI_PREC_BF16 or COLI_PREC_IDOT.
  *   ws     device workspace of ws_bytes >= coli_moe_workspace_bytes(S,K,E,D,F,0,prec).
  * An id < -1 or >= E is skipped and a listed-twice expert is computed twice;
  * both set a flag that coli_check_device_flags() reports.
  * 1 <= K <= 64, 1 <= E <= 1024, S >= 0, D, F >= 1.
  * Size limit (COLI_ERANGE otherwise): every expert matrix (F * row_bytes(D)
  * and D * row_bytes(F), routed and shared) and every activation table --
- * S rows, and S*K (+ S with a shared expert) rows, of 4 (COLI_PREC_FP32) or
- * 2 (COLI_PREC_BF16) bytes per element of D resp. max(F, F_shared) rounded
+ * S rows, and S*K (+ S with a shared expert) rows, of 4 (COLI_PREC_FP32),
+ * 2 (COLI_PREC_BF16) or 1 (COLI_PREC_IDOT) bytes per element of D resp. max(F, F_shared) rounded
  * up to 1024 -- stays below 2^32 - 4096 bytes.  At D = 6144, F = 2048, K = 8
  * with a shared expert that is S <= 58254 tokens per call (fp32 precision).
  * Errors: COLI_EINVAL, COLI_EFMT, COLI_ESHAPE, COLI_ERANGE, COLI_EALIGN,

@@ -222,3 +222,39 @@ def test_workspace_layout_is_consistent(L):
         rows = S * K + (S if Fs else 0)
         assert lay["y"] + rows * D * 4 <= lay["total"]
         assert lay["h"] + rows * max(F, Fs) * 4 <= lay["y"]
+
+
+def test_idot_precision_host_checks(L):
+    """COLI_PREC_IDOT takes int8 / int4 experts in the tiled layout (and a
+    shared expert of the same format, F and layout) only; the workspace
+    regions hold the int8 tables, scales and sums of S tokens and of the
+    grouped rows."""
+    from weight_streaming_gemv_qgemv_amd import binding as b
+    E, D, F, S, K = 8, 64, 32, 4, 2
+
+    def layer(ex, sh):
+        # one byte short of the workspace this call needs: a call the checks
+        # accept stops at COLI_EWORKSPACE, before any device work
+        need = b.moe_workspace_bytes(S, K, E, ex.D, ex.F, sh.F if sh else 0, b.PREC_IDOT)
+        assert need > 0
+        return L.coli_moe_layer(C.byref(b.RouterParams(FAKE, FAKE, K, 1, 2.5, 0.0)), C.byref(ex),
+                                C.byref(sh) if sh else None, FAKE, S, FAKE, FAKE, FAKE, None, None,
+                                b.PREC_IDOT, FAKE, need - 1, None)
+    tiled4 = b.Experts(2, E, D, F, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1)
+    assert layer(tiled4, None) == b.EWORKSPACE                 # valid up to the workspace
+    assert layer(b.Experts(1, E, D, F, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1), None) == b.EWORKSPACE
+    assert layer(b.Experts(3, E, D, 2 * F, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1), None) == b.EFMT  # int2
+    assert layer(b.Experts(2, E, D, F, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0), None) == b.EINVAL  # rows
+    assert layer(tiled4, b.Mlp(2, F, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0)) == b.EINVAL  # rows shared
+    assert layer(tiled4, b.Mlp(2, 2 * F, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1)) == b.EINVAL
+    assert layer(tiled4, b.Mlp(2, F, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1)) == b.EWORKSPACE
+    wide = b.Experts(2, E, 16416, F, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1)
+    assert layer(wide, None) == b.ERANGE
+    for Fs in (0, F):
+        lay = b.moe_workspace_layout(S, K, E, D, F, Fs, b.PREC_IDOT)
+        rows = S * K + (S if Fs else 0)
+        kp = lambda n: (n + 1023) // 1024 * 1024
+        assert lay["xsum"] - lay["xf"] >= S * kp(D)
+        assert lay["hf"] - lay["xsum"] >= (5 * S + 3 * rows) * 4
+        assert lay["hsum"] - lay["hf"] >= rows * kp(F)
+        assert lay["work"] - lay["hsum"] >= rows * 7 * 4

@@ -78,6 +78,23 @@ def test_prefill_bf16_short_rows(dev, orc, fmt):
     assert_within(out, ref["out"], ref["mag"], REL, what=f"prefill short fmt{fmt}")
 
 
+@pytest.mark.parametrize("fmt", [1, 2])
+def test_prefill_bf16_no_shared_expert(dev, orc, fmt):
+    """The matrix-core prefill path without a shared expert (the workspace
+    then has no shared rows: the grouped-row tables are sized P = S K) and
+    with empty slots."""
+    E, D, F, S, K = 12, 1024, 512, 200, 4
+    bank = synth.expert_bank(75 + fmt, fmt, E, D, F)
+    g = synth.rng(76, fmt)
+    x = synth.activations(g, S, D)
+    idx, w = synth.routing_zipf(g, S, K, E)
+    idx[::5, 2] = -1
+    announce("prefill bf16 no shared", fmt)
+    out, _ = run_layer(dev, bank, None, x, idx, w, PREC_BF16)
+    ref = orc.moe(bank, None, x, idx, w.astype(np.float64))
+    assert_within(out, ref["out"], ref["mag"], REL, what=f"prefill no shared fmt{fmt}")
+
+
 def test_prefill_bf16_unaligned_rows_take_fp32(dev, orc):
     """Rows that are not whole 16-byte segments take the vector-ALU kernels,
     which compute in fp32 under either precision."""

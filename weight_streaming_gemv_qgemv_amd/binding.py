@@ -16,7 +16,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libcoli.so")
 
 F32, I8, I4, I2 = 0, 1, 2, 3
-PREC_FP32, PREC_BF16 = 0, 1
+PREC_FP32, PREC_BF16, PREC_IDOT = 0, 1, 2
 LAYOUT_ROWS, LAYOUT_TILED = 0, 1
 OK, EINVAL, ESHAPE, EFMT, EALIGN, ERANGE, EWORKSPACE, EDEVICE, EIDX = 0, -1, -2, -3, -4, -5, -6, -7, -8
 

@@ -601,13 +601,14 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
     const int64_t gstrF = tiled ? coli_tiled_bytes(ex->fmt, 1, D, F) : (int64_t)D * rbF;   // down
     // matrix-core passes: 16 rows as bf16 hi/lo column pairs (fp32-level
     // accuracy) or 64 rows rounded once to bf16
-    const int bf16 = prec == COLI_PREC_BF16 ? 1 : 0;
-    const int tpp = bf16 ? COLI_MM_TPP_BF16 : COLI_MM_TPP_FP32;
+    const int bf16 = prec == COLI_PREC_BF16 ? 1 : 0, idot = prec == COLI_PREC_IDOT ? 1 : 0;
+    if (idot && !(mm && tiled && (!sh || sh_mm))) return COLI_EINVAL;   // the host checks rule these out
+    const int tpp = bf16 || idot ? COLI_MM_TPP_BF16 : COLI_MM_TPP_FP32;
     int32_t *work = reinterpret_cast<int32_t *>(ws + L.work);
     int32_t *n_work = reinterpret_cast<int32_t *>(ws + L.n_work);
     // fp32 matrix-core path with one grouping launch: that launch also
     // writes x's row tables
-    const bool x_fused = mm && !bf16 && P <= kChunk;
+    const bool x_fused = mm && prec == COLI_PREC_FP32 && P <= kChunk;
     {
     StageTimer tg(kStGroup, st);
     if (P > kChunk) {
@@ -617,7 +618,7 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
         err = hipGetLastError();
         if (err != hipSuccess) return COLI_EDEVICE;
         hipLaunchKernelGGL(k_group_prefix, dim3(1), dim3(1024), 0, st, E, C, gpart, counts, offsets,
-                           sh_mm ? S : 0, tpp, bf16, mm ? work : nullptr, n_work, flags);
+                           sh_mm ? S : 0, tpp, bf16 | idot, mm ? work : nullptr, n_work, flags);
         err = hipGetLastError();
         if (err != hipSuccess) return COLI_EDEVICE;
         hipLaunchKernelGGL(k_group_place, dim3(gblocks, C), dim3(1024), 0, st, idx, P, E, gpart,
@@ -629,7 +630,7 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
         const int xg = x_fused ? S : 0;
 #define COLI_GROUP_ONE(XF)                                                                         \
     hipLaunchKernelGGL(k_group_one<XF>, dim3(gblocks + xg), dim3(1024), 0, st, idx, P, K, E, counts, \
-                       offsets, row_pair, pair_row, sh_mm ? S : 0, tpp, bf16, mm ? work : nullptr, n_work, \
+                       offsets, row_pair, pair_row, sh_mm ? S : 0, tpp, bf16 | idot, mm ? work : nullptr, n_work, \
                        flags, gblocks, xj)
         if (!x_fused) COLI_GROUP_ONE(-1);
         else if (ex->fmt == kI8) COLI_GROUP_ONE(kI8);
@@ -641,7 +642,7 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
     if (err != hipSuccess) return COLI_EDEVICE;
     }
 
-    if (mm && !bf16) {
+    if (mm && prec == COLI_PREC_FP32) {
         // fp32 precision: x as one row table per token, the SwiGLU output as
         // one per grouped row
         uint16_t *xt = reinterpret_cast<uint16_t *>(ws + L.xf);
@@ -732,10 +733,111 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
         return to_status(combine_launch(y, S, D, K, pair_row, w, sh ? 1 : 0, shared_row0, out,
                                         (int)(al16(out) && al16(y) && D % 4 == 0 && (!resid || al16(resid))), st, resid));
     }
+    if (idot) {
+        // integer dots: x quantised once per token, the SwiGLU output once
+        // per grouped row (int8 tables, scales and sums of the int8 values)
+        const int64_t rows = (int64_t)P + (sh ? S : 0);   // grouped rows (the workspace has no shared rows without one)
+        const int64_t kqD = coli__kpad(D), kqF = coli__kpad(F);
+        int8_t *xt = reinterpret_cast<int8_t *>(ws + L.xf);
+        float *tok_sx = reinterpret_cast<float *>(ws + L.xsum);
+        int *tok_sq = reinterpret_cast<int *>(ws + L.xsum + (int64_t)S * 4);
+        int32_t *act_row = reinterpret_cast<int32_t *>(ws + L.xsum + (int64_t)5 * S * 4);
+        float *row_sx = reinterpret_cast<float *>(ws + L.xsum + ((int64_t)5 * S + rows) * 4);
+        int *row_sq = reinterpret_cast<int *>(ws + L.xsum + ((int64_t)5 * S + 2 * rows) * 4);
+        int8_t *ht = reinterpret_cast<int8_t *>(ws + L.hf);
+        float *h_sx = reinterpret_cast<float *>(ws + L.hsum);
+        int *h_sq = reinterpret_cast<int *>(ws + L.hsum + rows * 4);
+        float *hrow_sx = reinterpret_cast<float *>(ws + L.hsum + rows * 5 * 4);
+        int *hrow_sq = reinterpret_cast<int *>(ws + L.hsum + rows * 6 * 4);
+        const int64_t max_gp = L.n_pass_max;
+        {
+            StageTimer tp(kStPrep, st);
+            if (qrow_launch(ex->fmt, x, S, D, kqD, xt, tok_sx, tok_sq, st) != hipSuccess) return COLI_EDEVICE;
+            if (idrows_launch(row_pair, P, K, S, (int)rows, tok_sx, tok_sq, act_row, row_sx, row_sq, st) !=
+                hipSuccess)
+                return COLI_EDEVICE;
+        }
+        {
+            StageTimer tgu(kStGateUp, st, true);
+            PreIdArgs a = {};
+            a.w[0] = (const uint8_t *)ex->w_gate;
+            a.w[1] = (const uint8_t *)ex->w_up;
+            a.s[0] = ex->s_gate;
+            a.s[1] = ex->s_up;
+            a.w_gstride = gstrD;
+            a.s_gstride = F;
+            a.ngroups = E;
+            a.O = F;
+            if (sh) {
+                a.has_extra = 1;
+                a.xw[0] = (const uint8_t *)sh->w_gate;
+                a.xw[1] = (const uint8_t *)sh->w_up;
+                a.xs[0] = sh->s_gate;
+                a.xs[1] = sh->s_up;
+                a.xO = F;
+                a.x_rows = S;
+                a.x_row0 = (int)shared_row0;
+            }
+            a.I = D;
+            a.rb = rbD;
+            a.kq = kqD;
+            a.offsets = offsets;
+            a.work = work;
+            a.n_work = n_work;
+            a.act_row = act_row;
+            a.row_sx = row_sx;
+            a.row_sq = row_sq;
+            a.act = xt;
+            a.out = h;
+            a.ldo = L.h_ld;
+            a.out_vec4 = L.h_ld % 4 == 0 && al16(h);
+            if (preid_launch(a, ex->fmt, 2, max_gp, st) != hipSuccess) return COLI_EDEVICE;
+        }
+        {
+            StageTimer tdn(kStDown, st);
+            // h rows are F wide (a shared expert has the same F here)
+            if (qrow_launch(ex->fmt, h, (int)rows, F, kqF, ht, h_sx, h_sq, st) != hipSuccess ||
+                idrows_launch(nullptr, 0, K, (int)rows, (int)rows, h_sx, h_sq, nullptr, hrow_sx, hrow_sq, st) !=
+                    hipSuccess)
+                return COLI_EDEVICE;
+            PreIdArgs d = {};
+            d.w[0] = (const uint8_t *)ex->w_down;
+            d.s[0] = ex->s_down;
+            d.w_gstride = gstrF;
+            d.s_gstride = D;
+            d.ngroups = E;
+            d.O = D;
+            if (sh) {
+                d.has_extra = 1;
+                d.xw[0] = (const uint8_t *)sh->w_down;
+                d.xs[0] = sh->s_down;
+                d.xO = D;
+                d.x_rows = S;
+                d.x_row0 = (int)shared_row0;
+            }
+            d.I = F;
+            d.rb = rbF;
+            d.kq = kqF;
+            d.offsets = offsets;
+            d.work = work;
+            d.n_work = n_work;
+            d.act_row = nullptr;
+            d.row_sx = hrow_sx;
+            d.row_sq = hrow_sq;
+            d.act = ht;
+            d.out = y;
+            d.ldo = D;
+            d.out_vec4 = D % 4 == 0 && al16(y);
+            if (preid_launch(d, ex->fmt, 1, max_gp, st) != hipSuccess) return COLI_EDEVICE;
+        }
+        StageTimer tcb(kStCombine, st);
+        return to_status(combine_launch(y, S, D, K, pair_row, w, sh ? 1 : 0, shared_row0, out,
+                                        (int)(al16(out) && al16(y) && D % 4 == 0 && (!resid || al16(resid))), st, resid));
+    }
     if (mm) {
         // bf16 precision: x as one bf16 row table per token, the SwiGLU
         // output as one per grouped row; per-row activation sums
-        const int64_t rows = (int64_t)P + S;
+        const int64_t rows = (int64_t)P + (sh ? S : 0);   // grouped rows (the workspace has no shared rows without one)
         const int kpD = (int)coli__kpad(D), kpF = (int)coli__kpad(F);
         const int nparts = kpF / 32;
         uint16_t *xt = reinterpret_cast<uint16_t *>(ws + L.xf);
@@ -749,7 +851,7 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
         {
             StageTimer tp(kStPrep, st);
             if (xrows_bf16_launch(ex->fmt, x, D, S, D, kpD, xt, tok_sum, st) != hipSuccess) return COLI_EDEVICE;
-            if (pre_rows_launch(row_pair, P, K, S, tok_sum, act_row, row_sum, st) != hipSuccess)
+            if (pre_rows_launch(row_pair, P, K, S, (int)(rows - P), tok_sum, act_row, row_sum, st) != hipSuccess)
                 return COLI_EDEVICE;
         }
         {

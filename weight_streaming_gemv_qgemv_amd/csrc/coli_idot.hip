@@ -27,9 +27,13 @@
 //         stored in that order.  Nibbles are taken as codes 0..15 (value +
 //         8): 8 * sum(q) is removed from the integer dot.
 // A step st of a row is 4 units of 16 bytes (q = 0..3) at byte 64 st.
+#include <hip/hip_ext.h>
+
 #include "coli_device.h"
 #include "coli_frag.h"
 #include "coli_idot.h"
+#include "coli_pre.h"
+#include "coli_stages.h"
 
 namespace coli {
 
@@ -248,6 +252,392 @@ __global__ __launch_bounds__(512) void k_idot(IdotArgs a, int passes, int ntiles
     }
 }
 
+// ---------------------------------------------------------------- experts
+// Integer-dot grouped expert products for prefill batches: the items,
+// classes (passes sorted by live 16-row N-tiles), pass-major XCD order and
+// pipeline of the bf16 prefill kernel on tiled weights -- each wave 32
+// (gate/up) or 64 (down) weight rows x the pass's live rows; per k-block the
+// pass rows' int8 units are staged into LDS by direct-to-LDS loads (double
+// buffered), and the weights of k-block j + 2 are loaded into k-block j's
+// registers as each segment is consumed -- but the products are exact int32
+// dots on v_mfma_i32_16x16x64_i8, and the epilogue is the pages' fp32 one.
+// The tiled weight unit (16 rows x 64 bytes, lane 16 q + c = row c, bytes
+// 16 q..16 q + 15) is the A operand's layout as it is.
+__global__ void k_idrows(const int32_t *__restrict__ row_pair, int P, int K, int S, int rows,
+                         const float *__restrict__ sx, const int *__restrict__ sq,
+                         int32_t *__restrict__ act_row, float *__restrict__ row_sx,
+                         int *__restrict__ row_sq)
+{
+    const int r = blockIdx.x * blockDim.x + threadIdx.x;
+    if (r >= rows) return;
+    int t = r;
+    if (row_pair) {
+        t = r < P ? row_pair[r] / K : r - P;
+        if (t < 0 || t >= S) t = 0;   // rows past the grouped slots (never read)
+        act_row[r] = t;
+    }
+    row_sx[r] = sx[t];
+    int v = 0;
+#pragma unroll
+    for (int p = 0; p < kQMaxParts; ++p) v += sq[(int64_t)t * kQMaxParts + p];
+    row_sq[r] = v;
+}
+
+typedef __attribute__((address_space(3))) const void lds_void_i;
+
+__device__ __forceinline__ void dma16_i(const void *g, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory");
+}
+
+constexpr int kPidWaves = 8;
+constexpr int kPidXcds = 8;
+constexpr int kPidNT = kPreTpp / 16;
+
+template <int FMT, int M>
+__global__ __launch_bounds__(64 * kPidWaves) void k_preid(PreIdArgs a)
+{
+    constexpr int SEGS = 2;                          // 64-byte tiled segments per k-block
+    constexpr int SPSI = FMT == kI4 ? 2 : 1;         // i8 MFMA steps per segment
+    constexpr int STEPS = SEGS * SPSI;
+    constexpr int KB = ID<FMT>::KB;                  // elements per k-block
+    static_assert(ID<FMT>::SPK == STEPS, "steps per k-block");
+    constexpr int MT = M == 2 ? 2 : 4, NT = kPidNT, RPW = 16 * MT, RPB = kPidWaves * RPW;
+    static_assert(RPB == pre_rows_per_item(M), "rows per item");
+    constexpr int UNITS = NT * STEPS * 64;           // 16-byte units of one staged k-block
+    __shared__ uint4 bsA[UNITS], bsB[UNITS];
+    __shared__ int lrow[2][kPreTpp];
+    __shared__ float lsx[2][kPreTpp];
+    __shared__ int lsq[2][kPreTpp];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 15, q = lane >> 4;
+    const int xcd = blockIdx.x % kPidXcds, lb = blockIdx.x / kPidXcds;
+    const int bpx = gridDim.x / kPidXcds;
+    const int nkb = (int)(a.kq / KB);                  // a multiple of 4
+    const int ns = (int)((a.rb + 63) / 64);
+    const uint8_t *actb = reinterpret_cast<const uint8_t *>(a.act);
+    const uint32_t arow = (uint32_t)a.kq;
+    const int dq = (lane & 3) ^ ((lane >> 3) & 3);
+    // VMEM loads of one loadList: the table row (with a row map), the scale,
+    // and for int4 the int8 sum (int8 codes need no correction: the compiler
+    // drops that load, and the count below must match what is issued)
+    const int nlist = (a.act_row ? 2 : 1) + (FMT == kI4 ? 1 : 0);
+
+    auto run = [&](auto nlc, int w0, int w1) {
+    constexpr int NL = decltype(nlc)::value;
+    const int n_gp = w1 - w0;
+    const int gp_lo = w0 + (int)((int64_t)n_gp * xcd / kPidXcds);
+    const int gp_cnt = w0 + (int)((int64_t)n_gp * (xcd + 1) / kPidXcds) - gp_lo;
+    const int n_items = gp_cnt * a.tiles;
+    if (lb >= n_items) return;                       // whole block, before any barrier
+
+    struct It {
+        int tile, nt, r0t, Og;
+        const uint8_t *wb[M];
+        const float *sc[M];
+        uint32_t roff[MT];
+        uint32_t gstr;
+    };
+    auto make = [&](It &c, int it) {
+        const int gp = __builtin_amdgcn_readfirstlane(gp_lo + it / a.tiles);
+        c.tile = __builtin_amdgcn_readfirstlane(it % a.tiles);
+        const int wv = cload(a.work + gp);
+        const int g = wv & 0x7FF, pass = wv >> 11;
+        const bool extra = a.has_extra && g == a.ngroups;
+        int r0, cnt;
+        if (extra) {
+            r0 = a.x_row0;
+            cnt = a.x_rows;
+        } else {
+            r0 = cload(a.offsets + g);
+            cnt = cload(a.offsets + g + 1) - r0;
+        }
+        c.nt = min(kPreTpp, cnt - pass * kPreTpp);
+        c.r0t = r0 + pass * kPreTpp;
+        if (extra) {
+            c.Og = a.xO;
+#pragma unroll
+            for (int m = 0; m < M; ++m) { c.wb[m] = a.xw[m]; c.sc[m] = a.xs[m]; }
+        } else {
+            c.Og = a.O;
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                c.wb[m] = a.w[m] + (int64_t)g * a.w_gstride;
+                c.sc[m] = a.s[m] + (int64_t)g * a.s_gstride;
+            }
+        }
+        const int obase = c.tile * RPB + wave * RPW;
+        const int mt16 = (c.Og + 15) / 16;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) c.roff[mt] = tiled_base(min(obase / 16 + mt, mt16 - 1), ns) + 16 * lane;
+        c.gstr = tiled_gstride(min(obase / 16, mt16 - 1), mt16);
+    };
+    // pass rows: table row, scale and (int4) int8 sum (dead rows repeat the
+    // last live one); nlist loads
+    auto loadList = [&](const It &c, int &ar, float &rs, int &rq) {
+        const int gr = c.r0t + min(tid & 63, c.nt - 1);
+        ar = a.act_row ? a.act_row[gr] : gr;
+        rs = a.row_sx[gr];
+        rq = FMT == kI4 ? a.row_sq[gr] : 0;
+    };
+    auto storeList = [&](int par, int ar, float rs, int rq) {
+        if (tid < kPreTpp) {
+            lrow[par][tid] = ar;
+            lsx[par][tid] = rs;
+            lsq[par][tid] = rq;
+        }
+    };
+    auto loadSeg = [&](const It &c, int kbi, int sg, uint4 (&w)[M][MT][SEGS]) {
+        const uint32_t go = (uint32_t)min(kbi * SEGS + sg, ns - 1) * c.gstr;
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) w[m][mt][sg] = gload16(c.wb[m] + (c.roff[mt] + go));
+    };
+    auto loadW = [&](const It &c, int kbi, uint4 (&w)[M][MT][SEGS]) {
+#pragma unroll
+        for (int sg = 0; sg < SEGS; ++sg) loadSeg(c, kbi, sg, w);
+    };
+    // Staging: unit (pass row t = 16 n + col, step s, chunk q) at
+    // ((n STEPS + s) 16 + col) 4 + (q ^ ((col >> 1) & 3)); instruction
+    // i = n STEPS + s fills one (n, s) -- lane L takes row 16 n + L / 4,
+    // chunk (L & 3) ^ ((L >> 3) & 3) -- and is issued by wave i % 8.
+    constexpr int NI = NL * STEPS, IPW = (NI + kPidWaves - 1) / kPidWaves;
+    auto stageB = [&](int par, int kbi, const uint4 *buf) {
+        const uint32_t lbuf = (uint32_t)(uintptr_t)(lds_void_i *)buf;
+#pragma unroll
+        for (int j = 0; j < IPW; ++j) {
+            const int i = wave + kPidWaves * j;
+            if (NI % kPidWaves == 0 || i < NI) {        // uniform
+                const int n = i / STEPS, st = i % STEPS;
+                const uint32_t off = (uint32_t)lrow[par][16 * n + (lane >> 2)] * arow +
+                                     (uint32_t)(kbi * STEPS + st) * 64u + (uint32_t)dq * 16u;
+                dma16_i(actb + off, __builtin_amdgcn_readfirstlane(lbuf + (uint32_t)i * 1024));
+            }
+        }
+    };
+
+    int4v acc[M][MT][NL];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int n = 0; n < NL; ++n) acc[m][mt][n] = int4v{0, 0, 0, 0};
+
+    // the steps of segment sg of one k-block
+    auto compute = [&](const uint4 (&w)[M][MT][SEGS], const uint4 *buf, int sg) {
+#pragma unroll
+        for (int s2 = 0; s2 < STEPS; ++s2) {
+            if (s2 / SPSI != sg) continue;
+            int4v b[NL];
+#pragma unroll
+            for (int n = 0; n < NL; ++n) {
+                const uint4 u = buf[((n * STEPS + s2) * 16 + col) * 4 + (q ^ ((col >> 1) & 3))];
+                b[n] = int4v{(int)u.x, (int)u.y, (int)u.z, (int)u.w};
+            }
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const int4v A = icodes<FMT>(w[m][mt][sg], s2 % SPSI);
+#pragma unroll
+                    for (int n = 0; n < NL; ++n)
+                        acc[m][mt][n] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, b[n], acc[m][mt][n], 0, 0, 0);
+                }
+        }
+    };
+
+    float sreg[M][MT][4];
+    auto load_epi = [&](const It &c) {
+        const int obase = c.tile * RPB + wave * RPW;
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    sreg[m][mt][r] = gloadf(c.sc[m] + min(obase + 16 * mt + 4 * q + r, c.Og - 1));
+    };
+    // D[4q + r][col] of tile (m, mt, n): weight row obase + 16 mt + 4 q + r,
+    // pass row 16 n + col.  The pages' epilogue, each step rounded in fp32:
+    // ((float)dot * scale) * s_row, dot less 8 * sum(q) for int4 (the codes
+    // are nibbles 0..15); gate/up: silu(g) * u.  Stores of the uniform fast
+    // path (16-byte stores, the wave's rows inside the matrix): one per live
+    // N-tile and row tile, every one issued (each tile has a live row).
+    float rsx[NL];
+    int rsq[NL];
+    constexpr int kStores = NL * MT;
+    auto epilogue = [&](const It &c) -> int {
+        const int obase = c.tile * RPB + wave * RPW;
+        const bool fast = a.out_vec4 && obase + RPW <= c.Og;
+#pragma unroll
+        for (int n = 0; n < NL; ++n) {
+            const int t = 16 * n + col;
+            const bool live = t < c.nt;
+            const int64_t gr = c.r0t + t;
+            const int corr = FMT == kI4 ? 8 * rsq[n] : 0;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const int ob = obase + 16 * mt + 4 * q;
+                float res[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float y = ((float)(acc[0][mt][n][r] - corr) * sreg[0][mt][r]) * rsx[n];
+                    if constexpr (M == 2) {
+                        const float u = ((float)(acc[1][mt][n][r] - corr) * sreg[1][mt][r]) * rsx[n];
+                        y = silu_f(y) * u;
+                    }
+                    res[r] = y;
+                }
+                if (live) {
+                    float *op = a.out + gr * a.ldo;
+                    if (fast || (a.out_vec4 && ob + 3 < c.Og)) {
+                        *reinterpret_cast<float4 *>(op + ob) = make_float4(res[0], res[1], res[2], res[3]);
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (ob + r < c.Og) op[ob + r] = res[r];
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int n = 0; n < NL; ++n) acc[m][mt][n] = int4v{0, 0, 0, 0};
+        return fast ? kStores : 0;
+    };
+
+    constexpr int NW = M * MT * SEGS;
+    auto wait_vm = [&](auto nc) {
+        constexpr int N = decltype(nc)::value;
+        static_assert(N < 64, "vmcnt field");
+        __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+    };
+    // Before k-block j's products: W(j) and DMA(j) must be done; W(j + 1)
+    // (NW) and what followed it -- the next item's pass-row loads (nlist)
+    // and the last epilogue's stores -- may stay in flight.
+    auto sync_x = [&](int after) {
+        asm volatile("" ::: "memory");
+        if (after == 3 + kStores) wait_vm(std::integral_constant<int, NW + 3 + kStores>{});
+        else if (after == 2 + kStores) wait_vm(std::integral_constant<int, NW + 2 + kStores>{});
+        else if (after == 1 + kStores) wait_vm(std::integral_constant<int, NW + 1 + kStores>{});
+        else if (after == 3) wait_vm(std::integral_constant<int, NW + 3>{});
+        else if (after == 2) wait_vm(std::integral_constant<int, NW + 2>{});
+        else if (after == 1) wait_vm(std::integral_constant<int, NW + 1>{});
+        else wait_vm(std::integral_constant<int, NW>{});
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+
+    It cur;
+    make(cur, lb);
+    int par = 0;
+    {
+        int ar, rq;
+        float rs;
+        loadList(cur, ar, rs, rq);
+        storeList(0, ar, rs, rq);
+    }
+    __syncthreads();
+    uint4 wA[M][MT][SEGS], wB[M][MT][SEGS];
+    loadW(cur, 0, wA);
+    stageB(0, 0, bsA);
+    loadW(cur, 1, wB);
+    int jn = lb + bpx;
+    auto kstep = [&](uint4 (&w)[M][MT][SEGS], const uint4 *buf, int spar, int skb, const uint4 *nbuf,
+                     const It &lc, int lkb, bool epi = false, int after = 0) {
+        sync_x(after);
+        stageB(spar, skb, nbuf);
+        if (epi) load_epi(cur);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int sg = 0; sg < SEGS; ++sg) {
+            compute(w, buf, sg);
+            __builtin_amdgcn_sched_barrier(0);
+            loadSeg(lc, lkb, sg, w);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    int stores = 0;
+    for (;;) {
+        const bool has_nxt = jn < n_items;
+        It nxt = cur;
+        if (has_nxt) make(nxt, jn);
+        int ar, rq;
+        float rs;
+        loadList(nxt, ar, rs, rq);
+        kstep(wA, bsA, par, 1, bsB, cur, 2, false, nlist + stores);
+        storeList(par ^ 1, ar, rs, rq);
+        kstep(wB, bsB, par, 2, bsA, cur, 3);
+        for (int k = 2; k < nkb - 2; k += 2) {
+            kstep(wA, bsA, par, k + 1, bsB, cur, k + 2);
+            kstep(wB, bsB, par, k + 2, bsA, cur, k + 3);
+        }
+        kstep(wA, bsA, par, nkb - 1, bsB, has_nxt ? nxt : cur, has_nxt ? 0 : nkb - 1, true);
+#pragma unroll
+        for (int n = 0; n < NL; ++n) {
+            rsx[n] = lsx[par][min(16 * n + col, cur.nt - 1)];
+            rsq[n] = lsq[par][min(16 * n + col, cur.nt - 1)];
+        }
+        kstep(wB, bsB, par ^ 1, 0, bsA, has_nxt ? nxt : cur, has_nxt ? 1 : nkb - 1);
+        stores = epilogue(cur);
+        if (!has_nxt) break;
+        cur = nxt;
+        par ^= 1;
+        jn += bpx;
+    }
+    // every wave's DMA is complete before the class ends (the next class's
+    // first DMA, after a barrier, may fill the same LDS)
+    __builtin_amdgcn_s_waitcnt(0);
+    };
+
+    static_assert(NT == 4, "classes of 4, 3, 2 and 1 live N-tiles");
+    const int e0 = cload(a.n_work + 1), e1 = cload(a.n_work + 2), e2 = cload(a.n_work + 3);
+    const int e3 = cload(a.n_work + 4);
+    run(std::integral_constant<int, 4>{}, 0, e0);
+    __syncthreads();
+    run(std::integral_constant<int, 3>{}, e0, e1);
+    __syncthreads();
+    run(std::integral_constant<int, 2>{}, e1, e2);
+    __syncthreads();
+    run(std::integral_constant<int, 1>{}, e2, e3);
+}
+
+template <int FMT, int M>
+hipError_t launch_preid(const PreIdArgs &a, int64_t items, hipStream_t st)
+{
+    static int cache[64] = {0};
+    const void *kern = (const void *)k_preid<FMT, M>;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (cache[dev] <= 0) {
+        int cus = 0, per = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kern, 64 * kPidWaves, 0) != hipSuccess || per <= 0)
+            per = 1;
+        cache[dev] = cus * per;
+    }
+    int64_t cap = cache[dev] / kPidXcds * kPidXcds;
+    if (cap < kPidXcds) cap = kPidXcds;
+    int64_t grid = (items + kPidXcds - 1) / kPidXcds * kPidXcds;
+    if (grid > cap) grid = cap;
+    if (grid < kPidXcds) grid = kPidXcds;
+    const KernelEvents ev = take_kernel_events();   // timed stage: events at the kernel's bounds
+    if (ev.start)
+        hipExtLaunchKernelGGL((k_preid<FMT, M>), dim3((unsigned)grid), dim3(64 * kPidWaves), 0, st, ev.start,
+                              ev.stop, 0, a);
+    else
+        hipLaunchKernelGGL((k_preid<FMT, M>), dim3((unsigned)grid), dim3(64 * kPidWaves), 0, st, a);
+    return hipGetLastError();
+}
+
 template <int FMT, int NKW>
 hipError_t launch_idot(const IdotArgs &a, hipStream_t st)
 {
@@ -286,6 +676,43 @@ int64_t idot_workspace_bytes(int S, int I)
 
 int idot_max_kblocks_per_wave() { return kIdMaxNkw; }
 int idot_kblock(int fmt) { return fmt == kI8 ? ID<kI8>::KB : ID<kI4>::KB; }
+
+hipError_t qrow_launch(int fmt, const float *x, int rows, int I, int64_t kq, int8_t *table, float *sx,
+                       int *sq, hipStream_t st)
+{
+    if (rows <= 0) return hipSuccess;
+    if (kq < I || kq % 256 || kq > (int64_t)kQPart * kQMaxParts || (fmt != kI8 && fmt != kI4))
+        return hipErrorInvalidValue;
+    const int vec = I % 4 == 0 && ((uintptr_t)x & 15u) == 0;
+    const dim3 qg((unsigned)rows, kQMaxParts);
+    if (fmt == kI8)
+        hipLaunchKernelGGL(k_qrow<kI8>, qg, dim3(256), 0, st, x, I, kq, vec, table, sx, sq);
+    else
+        hipLaunchKernelGGL(k_qrow<kI4>, qg, dim3(256), 0, st, x, I, kq, vec, table, sx, sq);
+    return hipGetLastError();
+}
+
+hipError_t idrows_launch(const int32_t *row_pair, int P, int K, int S, int rows, const float *sx,
+                         const int *sq, int32_t *act_row, float *row_sx, int *row_sq, hipStream_t st)
+{
+    if (rows <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_idrows, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, row_pair, P, K, S, rows,
+                       sx, sq, act_row, row_sx, row_sq);
+    return hipGetLastError();
+}
+
+hipError_t preid_launch(PreIdArgs a, int fmt, int M, int64_t max_group_passes, hipStream_t st)
+{
+    if (fmt != kI8 && fmt != kI4) return hipErrorInvalidValue;
+    if (a.kq % idot_kblock(fmt) || (a.kq / idot_kblock(fmt)) % 4 || a.kq < 4 * idot_kblock(fmt))
+        return hipErrorInvalidValue;
+    int Ocover = a.O;
+    if (a.has_extra && a.xO > Ocover) Ocover = a.xO;
+    a.tiles = (Ocover + pre_rows_per_item(M) - 1) / pre_rows_per_item(M);
+    const int64_t items = max_group_passes * a.tiles;
+    if (M == 2) return fmt == kI8 ? launch_preid<kI8, 2>(a, items, st) : launch_preid<kI4, 2>(a, items, st);
+    return fmt == kI8 ? launch_preid<kI8, 1>(a, items, st) : launch_preid<kI4, 1>(a, items, st);
+}
 
 hipError_t idot_launch(IdotArgs a, int fmt, hipStream_t st)
 {

@@ -56,9 +56,9 @@ struct PreArgs {
 hipError_t xrows_bf16_launch(int fmt, const float *x, int64_t ldx, int rows, int I, int kpad,
                              uint16_t *table, float *sums, hipStream_t st);
 // act_row / row_sum of the gate/up product: grouped row r < P is slot
-// row_pair[r] (token row_pair[r] / K), rows P..P+S-1 are the shared
-// expert's tokens 0..S-1.
-hipError_t pre_rows_launch(const int32_t *row_pair, int P, int K, int S, const float *token_sum,
+// row_pair[r] (token row_pair[r] / K), rows P..P+extra-1 are the shared
+// expert's tokens 0..extra-1 (extra: S with a shared expert, else 0).
+hipError_t pre_rows_launch(const int32_t *row_pair, int P, int K, int S, int extra, const float *token_sum,
                            int32_t *act_row, float *row_sum, hipStream_t st);
 // row_sum[r] = sum_p hpart[r * nparts + p] in p order.
 hipError_t pre_sum_launch(const float *hpart, int nparts, int rows, float *row_sum, hipStream_t st);

@@ -98,12 +98,12 @@ __global__ __launch_bounds__(256) void k_xrows_bf16(const float *__restrict__ x,
     if (tid == 0) sums[row] = (red[0] + red[1]) + (red[2] + red[3]);
 }
 
-__global__ void k_pre_rows(const int32_t *__restrict__ row_pair, int P, int K, int S,
+__global__ void k_pre_rows(const int32_t *__restrict__ row_pair, int P, int K, int S, int n,
                            const float *__restrict__ token_sum, int32_t *__restrict__ act_row,
                            float *__restrict__ row_sum)
 {
     const int r = blockIdx.x * blockDim.x + threadIdx.x;
-    if (r >= P + S) return;
+    if (r >= n) return;
     int t = r < P ? row_pair[r] / K : r - P;
     if (t < 0 || t >= S) t = 0;   // rows past the grouped slots (never read)
     act_row[r] = t;
@@ -641,12 +641,12 @@ hipError_t xrows_bf16_launch(int fmt, const float *x, int64_t ldx, int rows, int
     return hipGetLastError();
 }
 
-hipError_t pre_rows_launch(const int32_t *row_pair, int P, int K, int S, const float *token_sum,
+hipError_t pre_rows_launch(const int32_t *row_pair, int P, int K, int S, int extra, const float *token_sum,
                            int32_t *act_row, float *row_sum, hipStream_t st)
 {
-    const int n = P + S;
+    const int n = P + extra;
     if (n <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_pre_rows, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, row_pair, P, K, S,
+    hipLaunchKernelGGL(k_pre_rows, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, row_pair, P, K, S, n,
                        token_sum, act_row, row_sum);
     return hipGetLastError();
 }

@@ -139,7 +139,7 @@ int coli_moe_workspace_layout(int S, int K, int E, int D, int F, int F_shared,
 {
     if (!out) return COLI_EINVAL;
     if (S < 0 || K < 1 || E < 1 || D < 1 || F < 1 || F_shared < 0) return COLI_ESHAPE;
-    if (prec != COLI_PREC_FP32 && prec != COLI_PREC_BF16) return COLI_EINVAL;
+    if (prec != COLI_PREC_FP32 && prec != COLI_PREC_BF16 && prec != COLI_PREC_IDOT) return COLI_EINVAL;
     int64_t P, rows, Fmax = F > F_shared ? F : F_shared, t, off = 0;
     if (!mul_ok((int64_t)S, K, &P)) return COLI_ESHAPE;
     rows = P + (F_shared > 0 ? S : 0);
@@ -167,11 +167,23 @@ int coli_moe_workspace_layout(int S, int K, int E, int D, int F, int F_shared,
     /* matrix-core path: the activations' row tables and sums (below), and
      * the work list of (group, pass) entries; a pass is COLI_MM_TPP_FP32
      * rows (fp32 precision) or COLI_MM_TPP_BF16 rows (bf16 precision). */
-    const int bf16 = prec == COLI_PREC_BF16;
-    const int64_t tpp = bf16 ? COLI_MM_TPP_BF16 : COLI_MM_TPP_FP32;
+    const int bf16 = prec == COLI_PREC_BF16, idot = prec == COLI_PREC_IDOT;
+    const int64_t tpp = bf16 || idot ? COLI_MM_TPP_BF16 : COLI_MM_TPP_FP32;
     int64_t ngp = (rows + tpp - 1) / tpp + (int64_t)E + 1;   /* passes */
     int64_t KpD = round_up(D, 1024), KpF = round_up(Fmax, 1024);
-    if (bf16) {
+    if (idot) {
+        /* integer dots: int8 row tables of x (per token) and of the SwiGLU
+         * output (per grouped row), KpD / KpF bytes a row; xsum: per token
+         * its scale and four partial sums, then per grouped row its table
+         * row, scale and sum; hsum: per grouped row the scale and four
+         * partial sums of h's row, then its scale and sum again */
+        if (!mul_ok((int64_t)S, KpD, &t)) return COLI_ESHAPE;
+        REGION(xf, t);
+        REGION(xsum, ((int64_t)5 * S + 3 * rows) * 4);
+        if (!mul_ok(rows, KpF, &t)) return COLI_ESHAPE;
+        REGION(hf, t);
+        REGION(hsum, rows * 7 * 4);
+    } else if (bf16) {
         /* bf16 precision: bf16 row tables of x (per token) and of the SwiGLU
          * output (per grouped row); xsum: per-token sums of the stored x,
          * then per grouped row its table row (int32) and activation sum;
@@ -207,8 +219,8 @@ int coli_moe_workspace_layout(int S, int K, int E, int D, int F, int F_shared,
     }
 #undef REGION
     out->n_pass_max = ngp;
-    out->xf_stride = bf16 ? KpD : 2 * KpD;
-    out->hf_stride = bf16 ? KpF : 2 * KpF;
+    out->xf_stride = idot ? KpD / 2 : bf16 ? KpD : 2 * KpD;
+    out->hf_stride = idot ? KpF / 2 : bf16 ? KpF : 2 * KpF;
     out->h_ld = Fmax;
     out->total = off;
     return COLI_OK;
@@ -284,7 +296,7 @@ static int check_off32(const coli_experts *ex, const coli_mlp *sh, int S, int K,
 {
     const int64_t lim = ((int64_t)1 << 32) - 4096;
     const int64_t Fmax = sh && sh->F > ex->F ? sh->F : ex->F;
-    const int64_t eb = prec == COLI_PREC_BF16 ? 2 : 4;
+    const int64_t eb = prec == COLI_PREC_IDOT ? 1 : prec == COLI_PREC_BF16 ? 2 : 4;
     const int64_t rows = (int64_t)S * K + (sh ? S : 0);
     int64_t t;
     t = matrix_bytes(ex->fmt, ex->layout, ex->F, ex->D);
@@ -308,7 +320,7 @@ int coli__check_moe(const coli_experts *ex, const coli_mlp *sh, const float *x,
                     int need_routing)
 {
     if (!ex) return COLI_EINVAL;
-    if (prec != COLI_PREC_FP32 && prec != COLI_PREC_BF16) return COLI_EINVAL;
+    if (prec != COLI_PREC_FP32 && prec != COLI_PREC_BF16 && prec != COLI_PREC_IDOT) return COLI_EINVAL;
     if (S < 0 || K < 0 || ex->E < 0 || ex->D < 0 || ex->F < 0) return COLI_ESHAPE;
     if (ex->E < 1 || ex->E > COLI_MAX_E || K < 1 || K > COLI_MAX_K) return COLI_ERANGE;
     int rc = check_mlp_tensors(ex->fmt, ex->layout, ex->D, ex->F, ex->w_gate, ex->w_up, ex->w_down,
@@ -323,6 +335,15 @@ int coli__check_moe(const coli_experts *ex, const coli_mlp *sh, const float *x,
         if (sh->layout == COLI_LAYOUT_TILED &&
             (ex->layout != COLI_LAYOUT_TILED || sh->fmt != ex->fmt || sh->F != ex->F))
             return COLI_EINVAL;
+    }
+    if (prec == COLI_PREC_IDOT) {
+        /* the integer-dot kernels: int8 / int4, tiled, rows of whole 16-byte
+         * segments, widths within the quantiser's 16384 */
+        if (ex->fmt != COLI_I8 && ex->fmt != COLI_I4) return COLI_EFMT;
+        if (ex->layout != COLI_LAYOUT_TILED) return COLI_EINVAL;
+        if (coli_row_bytes(ex->fmt, ex->D) % 16 || coli_row_bytes(ex->fmt, ex->F) % 16) return COLI_ESHAPE;
+        if (ex->D > 16384 || ex->F > 16384) return COLI_ERANGE;
+        if (sh && (sh->layout != COLI_LAYOUT_TILED || sh->fmt != ex->fmt || sh->F != ex->F)) return COLI_EINVAL;
     }
     int64_t t;
     if (!mul_ok((int64_t)S, ex->D, &t) || !mul_ok(t, 4, &t)) return COLI_ESHAPE;
