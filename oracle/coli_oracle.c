@@ -120,6 +120,30 @@ static double qdot(int fmt, const uint8_t *row, const double *x, int64_t I,
     return scale * acc;
 }
 
+/* The grouped-scale form of qdot [docs-quickstart -- qt_resolve_fmt, the
+ * int4-grouped format]: sum_g sc[g] * sum_{i in group g} v(i) x[i], groups
+ * of gs consecutive elements (the last one shorter), in fp64; mag =
+ * sum_g |sc[g]| sum_{i in g} |v x|. */
+static double qdot_grouped(int fmt, const uint8_t *row, const double *x, int64_t I, int gs,
+                           const float *sc, double *mag)
+{
+    double acc = 0.0, am = 0.0;
+    int64_t ng = (I + gs - 1) / gs;
+    for (int64_t g = 0; g < ng; ++g) {
+        double part = 0.0, pm = 0.0;
+        int64_t lo = g * gs, hi = lo + gs < I ? lo + gs : I;
+        for (int64_t i = lo; i < hi; ++i) {
+            double t = cor_unpack(fmt, row, i) * x[i];
+            part += t;
+            pm += fabs(t);
+        }
+        acc += (double)sc[g] * part;
+        am += fabs((double)sc[g]) * pm;
+    }
+    if (mag) *mag = am;
+    return acc;
+}
+
 /* y[s,o] = scale[o] * sum_i v(o,i) x[s,i] over x given in fp64.
  * W is [O, row_bytes(I)] row-major; y and mag are [S,O] (mag may be NULL). */
 int cor_qgemv_d(int fmt, const void *W, const float *scale, const double *x,
@@ -291,36 +315,45 @@ int cor_router(const float *Wr, const float *bias, const float *x, int S,
 typedef struct {
     int fmt, E, D, F;
     const void *wg, *wu, *wd;   /* [E,F,rb(D)], [E,F,rb(D)], [E,D,rb(F)] */
-    const float *sg, *su, *sd;  /* [E,F], [E,F], [E,D] */
+    const float *sg, *su, *sd;  /* [E,F], [E,F], [E,D]; grouped: [E,F,ceil(D/gs)], .., [E,D,ceil(F/gs)] */
+    int gs;                     /* 0: one scale per row; else int4 with one scale per gs elements */
 } cor_experts;
 
 typedef struct {
     int fmt, F;
     const void *wg, *wu, *wd;   /* [F,rb(D)], [F,rb(D)], [D,rb(F)] */
-    const float *sg, *su, *sd;  /* [F], [F], [D] */
+    const float *sg, *su, *sd;  /* [F], [F], [D]; grouped as for cor_experts */
+    int gs;
 } cor_mlp;
 
 static double silu_d(double z) { return z / (1.0 + exp(-z)); }
 
 /* One SwiGLU MLP on one fp64 row.  Buffers: g,u,h [F]; y, ymag [D].
  * Optional gmag/umag [F] receive the two projections' magnitudes. */
-static void mlp_row(int fmt, int D, int F, const uint8_t *wg, const uint8_t *wu,
+static void mlp_row(int fmt, int gs, int D, int F, const uint8_t *wg, const uint8_t *wu,
                     const uint8_t *wd, const float *sg, const float *su,
                     const float *sd, const double *x, double *g, double *u,
                     double *h, double *gmag, double *umag, double *y,
                     double *ymag)
 {
     int64_t rbD = cor_row_bytes(fmt, D), rbF = cor_row_bytes(fmt, F);
+    int64_t ngD = gs > 0 ? (D + gs - 1) / gs : 1, ngF = gs > 0 ? (F + gs - 1) / gs : 1;
     for (int j = 0; j < F; ++j) {
         double mg, mu;
-        g[j] = qdot(fmt, wg + (int64_t)j * rbD, x, D, sg ? sg[j] : 1.0, &mg);
-        u[j] = qdot(fmt, wu + (int64_t)j * rbD, x, D, su ? su[j] : 1.0, &mu);
+        if (gs > 0) {
+            g[j] = qdot_grouped(fmt, wg + (int64_t)j * rbD, x, D, gs, sg + j * ngD, &mg);
+            u[j] = qdot_grouped(fmt, wu + (int64_t)j * rbD, x, D, gs, su + j * ngD, &mu);
+        } else {
+            g[j] = qdot(fmt, wg + (int64_t)j * rbD, x, D, sg ? sg[j] : 1.0, &mg);
+            u[j] = qdot(fmt, wu + (int64_t)j * rbD, x, D, su ? su[j] : 1.0, &mu);
+        }
         if (gmag) gmag[j] = mg;
         if (umag) umag[j] = mu;
         h[j] = silu_d(g[j]) * u[j];
     }
     for (int o = 0; o < D; ++o)
-        y[o] = qdot(fmt, wd + (int64_t)o * rbF, h, F, sd ? sd[o] : 1.0, &ymag[o]);
+        y[o] = gs > 0 ? qdot_grouped(fmt, wd + (int64_t)o * rbF, h, F, gs, sd + o * ngF, &ymag[o])
+                      : qdot(fmt, wd + (int64_t)o * rbF, h, F, sd ? sd[o] : 1.0, &ymag[o]);
 }
 
 /* Full MoE combine for S tokens.
@@ -343,6 +376,11 @@ int cor_moe(const cor_experts *ex, const cor_mlp *sh, const float *x, int S,
     int E = ex->E, D = ex->D, F = ex->F, fmt = ex->fmt;
     int Fs = sh ? sh->F : 0;
     int64_t rbD = cor_row_bytes(fmt, D), rbF = cor_row_bytes(fmt, F);
+    /* scales per row: one, or one per group of gs elements */
+    int64_t ngD = ex->gs > 0 ? (D + ex->gs - 1) / ex->gs : 1;
+    int64_t ngF = ex->gs > 0 ? (F + ex->gs - 1) / ex->gs : 1;
+    if (ex->gs < 0 || (ex->gs > 0 && fmt != OR_I4)) return -1;
+    if (sh && (sh->gs < 0 || (sh->gs > 0 && sh->fmt != OR_I4))) return -1;
     int64_t rbDs = sh ? cor_row_bytes(sh->fmt, D) : 0;
     int64_t rbFs = sh ? cor_row_bytes(sh->fmt, Fs) : 0;
     int Fmax = F > Fs ? F : Fs;
@@ -378,13 +416,13 @@ int cor_moe(const cor_experts *ex, const cor_mlp *sh, const float *x, int S,
                     int64_t p = (int64_t)s * K + kk;
                     int e = idx[p];
                     if (e < 0) continue;
-                    mlp_row(fmt, D, F,
+                    mlp_row(fmt, ex->gs, D, F,
                             (const uint8_t *)ex->wg + (int64_t)e * F * rbD,
                             (const uint8_t *)ex->wu + (int64_t)e * F * rbD,
                             (const uint8_t *)ex->wd + (int64_t)e * D * rbF,
-                            ex->sg ? ex->sg + (int64_t)e * F : NULL,
-                            ex->su ? ex->su + (int64_t)e * F : NULL,
-                            ex->sd ? ex->sd + (int64_t)e * D : NULL,
+                            ex->sg ? ex->sg + (int64_t)e * F * ngD : NULL,
+                            ex->su ? ex->su + (int64_t)e * F * ngD : NULL,
+                            ex->sd ? ex->sd + (int64_t)e * D * ngF : NULL,
                             xd, g, u, h, gm, um, y, ym);
                     double wk = w[p];
                     for (int d = 0; d < D; ++d) {
@@ -399,7 +437,7 @@ int cor_moe(const cor_experts *ex, const cor_mlp *sh, const float *x, int S,
                     if (y_out) memcpy(y_out + p * D, y, (size_t)D * sizeof(double));
                 }
                 if (sh) {
-                    mlp_row(sh->fmt, D, Fs, (const uint8_t *)sh->wg,
+                    mlp_row(sh->fmt, sh->gs, D, Fs, (const uint8_t *)sh->wg,
                             (const uint8_t *)sh->wu, (const uint8_t *)sh->wd,
                             sh->sg, sh->su, sh->sd, xd, g, u, h, gm, um, y, ym);
                     for (int d = 0; d < D; ++d) {
@@ -581,7 +619,7 @@ int cor_moe_idot(const cor_experts *ex, const cor_mlp *sh, const float *x, int S
 {
     int E = ex->E, D = ex->D, F = ex->F, fmt = ex->fmt;
     if (fmt != OR_I8 && fmt != OR_I4) return -1;
-    if (sh && (sh->fmt != fmt || sh->F != F)) return -1;
+    if (ex->gs != 0 || (sh && (sh->fmt != fmt || sh->F != F || sh->gs != 0))) return -1;
     int64_t rbD = cor_row_bytes(fmt, D), rbF = cor_row_bytes(fmt, F);
     for (int64_t p = 0; p < (int64_t)S * K; ++p)
         if (idx[p] >= E) return -1;

@@ -146,21 +146,23 @@ def router(Wr, bias, x, K: int, norm_topk: int = 1, routed_scale: float = 2.5,
 class _Experts(C.Structure):
     _fields_ = [("fmt", C.c_int), ("E", C.c_int), ("D", C.c_int), ("F", C.c_int),
                 ("wg", C.c_void_p), ("wu", C.c_void_p), ("wd", C.c_void_p),
-                ("sg", C.c_void_p), ("su", C.c_void_p), ("sd", C.c_void_p)]
+                ("sg", C.c_void_p), ("su", C.c_void_p), ("sd", C.c_void_p), ("gs", C.c_int)]
 
 
 class _Mlp(C.Structure):
     _fields_ = [("fmt", C.c_int), ("F", C.c_int),
                 ("wg", C.c_void_p), ("wu", C.c_void_p), ("wd", C.c_void_p),
-                ("sg", C.c_void_p), ("su", C.c_void_p), ("sd", C.c_void_p)]
+                ("sg", C.c_void_p), ("su", C.c_void_p), ("sd", C.c_void_p), ("gs", C.c_int)]
 
 
 def moe(ex: dict, shared: dict | None, x, idx, w, intermediates: bool = False):
     """MoE output for S tokens.
 
-    ex: dict(fmt, E, D, F, wg, wu, wd, sg, su, sd) with host arrays stacked
-        per expert ([E,F,rb(D)], [E,F,rb(D)], [E,D,rb(F)], [E,F], [E,F], [E,D]).
-    shared: dict(fmt, F, wg, wu, wd, sg, su, sd) or None.
+    ex: dict(fmt, E, D, F, wg, wu, wd, sg, su, sd[, gs]) with host arrays
+        stacked per expert ([E,F,rb(D)], [E,F,rb(D)], [E,D,rb(F)], [E,F],
+        [E,F], [E,D]); with gs > 0 (int4 only) one scale per gs elements:
+        sg, su [E,F,ceil(D/gs)], sd [E,D,ceil(F/gs)].
+    shared: dict(fmt, F, wg, wu, wd, sg, su, sd[, gs]) or None.
     idx [S,K] int32 (entries < 0 skipped), w [S,K] (widened to fp64).
     Returns dict(out, mag) plus, when intermediates, per-pair rows
     (pair p = s*K + k; shared rows follow at S*K + s): h, g, u, gmag, umag, y.
@@ -179,12 +181,13 @@ def moe(ex: dict, shared: dict | None, x, idx, w, intermediates: bool = False):
 
     e = _Experts(ex["fmt"], ex["E"], D, F, arr(ex["wg"]), arr(ex["wu"]), arr(ex["wd"]),
                  arr(_c(ex["sg"], np.float32)), arr(_c(ex["su"], np.float32)),
-                 arr(_c(ex["sd"], np.float32)))
+                 arr(_c(ex["sd"], np.float32)), int(ex.get("gs", 0)))
     sp = None
     if shared is not None:
         s = _Mlp(shared["fmt"], shared["F"], arr(shared["wg"]), arr(shared["wu"]),
                  arr(shared["wd"]), arr(_c(shared["sg"], np.float32)),
-                 arr(_c(shared["su"], np.float32)), arr(_c(shared["sd"], np.float32)))
+                 arr(_c(shared["su"], np.float32)), arr(_c(shared["sd"], np.float32)),
+                 int(shared.get("gs", 0)))
         sp = C.pointer(s)
     out = np.empty((S, D), np.float64)
     mag = np.empty((S, D), np.float64)
@@ -225,12 +228,13 @@ def moe_idot(ex: dict, shared: dict | None, x, idx, w, h_in=None):
 
     e = _Experts(ex["fmt"], ex["E"], D, F, arr(ex["wg"]), arr(ex["wu"]), arr(ex["wd"]),
                  arr(_c(ex["sg"], np.float32)), arr(_c(ex["su"], np.float32)),
-                 arr(_c(ex["sd"], np.float32)))
+                 arr(_c(ex["sd"], np.float32)), int(ex.get("gs", 0)))
     sp = None
     if shared is not None:
         sm = _Mlp(shared["fmt"], shared["F"], arr(shared["wg"]), arr(shared["wu"]),
                   arr(shared["wd"]), arr(_c(shared["sg"], np.float32)),
-                  arr(_c(shared["su"], np.float32)), arr(_c(shared["sd"], np.float32)))
+                  arr(_c(shared["su"], np.float32)), arr(_c(shared["sd"], np.float32)),
+                 int(shared.get("gs", 0)))
         sp = C.pointer(sm)
     rows = S * K + (S if shared is not None else 0)
     hin = None

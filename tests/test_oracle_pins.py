@@ -674,3 +674,57 @@ def test_moe_idot_near_the_exact_block(orc, fmt):
     err = np.linalg.norm(r["out"] - ref, axis=1) / np.linalg.norm(ref, axis=1)
     assert err.max() < 5e-2, err
     assert err.max() > 1e-5   # it is the lossy path, not the exact one
+
+
+# ---------------------------------------------------------------- grouped-scale experts
+def test_moe_grouped_one_slot_is_the_grouped_qgemv_chain(orc):
+    """Grouped-scale int4 experts with one slot (w = 1, no shared expert):
+    g and u are the pinned grouped qgemv of x, h = silu(g) u, and the down
+    output the grouped qgemv of h -- all fp64, to rounding order."""
+    E, D, F, S, gs = 3, 160, 96, 4, 32
+    bank = synth.expert_bank(41, 2, E, D, F, gs=gs)
+    g = synth.rng(42)
+    x = synth.activations(g, S, D)
+    e = 2
+    idx = np.full((S, 1), e, np.int32)
+    w = np.ones((S, 1), np.float64)
+    r = orc.moe(bank, None, x, idx, w, intermediates=True)
+    gv, _ = orc.qgemv_grouped(bank["wg"][e], bank["sg"][e], gs, x)
+    uv, _ = orc.qgemv_grouped(bank["wu"][e], bank["su"][e], gs, x)
+    np.testing.assert_allclose(r["g"], gv, rtol=1e-13, atol=1e-300)
+    np.testing.assert_allclose(r["u"], uv, rtol=1e-13, atol=1e-300)
+    h = gv / (1.0 + np.exp(-gv)) * uv
+    np.testing.assert_allclose(r["h"], h, rtol=1e-12)
+
+
+def test_moe_grouped_onehot_and_reductions(orc):
+    """One-hot x through one expert selects one group's scale: g[o] =
+    sg[o, j // gs] * v(o, j) exactly; gs = D with sg[o, 0] equals the per-row
+    expert; equal scales in every group equal the per-row expert."""
+    E, D, F, gs = 2, 128, 64, 32
+    bank = synth.expert_bank(43, 2, E, D, F, gs=gs)
+    for j in (0, 31, 32, 95, 127):
+        x = np.zeros((1, D), np.float32)
+        x[0, j] = 1.0
+        r = orc.moe(bank, None, x, np.array([[1]], np.int32), np.ones((1, 1)), intermediates=True)
+        v = np.array([orc_unpack(bank["wg"][1][o], j) for o in range(F)], np.float64)
+        np.testing.assert_array_equal(r["g"][0], bank["sg"][1][:, j // gs].astype(np.float64) * v)
+    g = synth.rng(44)
+    x = synth.activations(g, 3, D)
+    idx = np.array([[0], [1], [0]], np.int32)
+    w = np.ones((3, 1))
+    rowb = synth.expert_bank(43, 2, E, D, F)           # same weights, per-row scales
+    ref = orc.moe(rowb, None, x, idx, w)["out"]
+    got = orc.moe(dict(bank, gs=D, sg=rowb["sg"][:, :, None], su=rowb["su"][:, :, None],
+                       sd=np.repeat(rowb["sd"][:, :, None], (F + D - 1) // D, axis=2)), None, x, idx, w)["out"]
+    np.testing.assert_allclose(got, ref, rtol=1e-13, atol=1e-300)
+    eq = dict(bank, sg=np.repeat(rowb["sg"][:, :, None], D // gs, axis=2),
+              su=np.repeat(rowb["su"][:, :, None], D // gs, axis=2),
+              sd=np.repeat(rowb["sd"][:, :, None], F // gs, axis=2))
+    np.testing.assert_allclose(orc.moe(eq, None, x, idx, w)["out"], ref, rtol=1e-12, atol=1e-300)
+
+
+def orc_unpack(row, j):
+    """int4 element j of a packed row: nibble low-first, value nibble - 8."""
+    b = int(row[j // 2])
+    return ((b >> 4) if j % 2 else (b & 15)) - 8

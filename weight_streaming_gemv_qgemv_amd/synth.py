@@ -103,31 +103,48 @@ def routing_zipf(g: np.random.Generator, S: int, K: int, E: int, alpha: float = 
     return idx, w
 
 
-def expert_bank(seed: int, fmt: int, E: int, D: int, F: int, experts=None):
+def group_scales(g: np.random.Generator, O: int, I: int, gs: int) -> np.ndarray:
+    """One scale per gs elements of each of O rows: [O, ceil(I / gs)]."""
+    return g.uniform(0.001, 0.02, size=(O, (I + gs - 1) // gs)).astype(np.float32)
+
+
+def expert_bank(seed: int, fmt: int, E: int, D: int, F: int, experts=None, gs: int = 0):
     """Stacked expert weights; expert e is drawn from its own stream
     (seed, e), so any subset can be regenerated alone.  Returns a dict with
-    wg, wu [E,F,rb(D)], wd [E,D,rb(F)], sg, su [E,F], sd [E,D]."""
+    wg, wu [E,F,rb(D)], wd [E,D,rb(F)], sg, su [E,F], sd [E,D]; with gs > 0
+    (grouped-scale int4) sg, su [E,F,ceil(D/gs)], sd [E,D,ceil(F/gs)] and
+    gs (the weights are the same as with gs = 0)."""
     rbD, rbF = packed_row_bytes(fmt, D), packed_row_bytes(fmt, F)
     ids = range(E) if experts is None else experts
     n = len(ids)
+    sdim = (lambda O, I: (O,)) if gs <= 0 else (lambda O, I: (O, (I + gs - 1) // gs))
     out = dict(fmt=fmt, E=E, D=D, F=F,
                wg=np.empty((n, F, rbD), np.uint8), wu=np.empty((n, F, rbD), np.uint8),
                wd=np.empty((n, D, rbF), np.uint8),
-               sg=np.empty((n, F), np.float32), su=np.empty((n, F), np.float32),
-               sd=np.empty((n, D), np.float32))
+               sg=np.empty((n,) + sdim(F, D), np.float32), su=np.empty((n,) + sdim(F, D), np.float32),
+               sd=np.empty((n,) + sdim(D, F), np.float32))
+    if gs > 0:
+        out["gs"] = gs
     for j, e in enumerate(ids):
         g = rng(seed, int(e))
         out["wg"][j] = weight_bytes(g, fmt, F, D)
         out["wu"][j] = weight_bytes(g, fmt, F, D)
         out["wd"][j] = weight_bytes(g, fmt, D, F)
-        out["sg"][j] = scales(g, F)
-        out["su"][j] = scales(g, F)
-        out["sd"][j] = scales(g, D)
+        if gs > 0:
+            out["sg"][j] = group_scales(g, F, D, gs)
+            out["su"][j] = group_scales(g, F, D, gs)
+            out["sd"][j] = group_scales(g, D, F, gs)
+        else:
+            out["sg"][j] = scales(g, F)
+            out["su"][j] = scales(g, F)
+            out["sd"][j] = scales(g, D)
     return out
 
 
-def shared_mlp(seed: int, fmt: int, D: int, F: int):
+def shared_mlp(seed: int, fmt: int, D: int, F: int, gs: int = 0):
     g = rng(seed, 1_000_003)
-    return dict(fmt=fmt, F=F, wg=weight_bytes(g, fmt, F, D), wu=weight_bytes(g, fmt, F, D),
-                wd=weight_bytes(g, fmt, D, F), sg=scales(g, F), su=scales(g, F),
-                sd=scales(g, D))
+    wg, wu, wd = weight_bytes(g, fmt, F, D), weight_bytes(g, fmt, F, D), weight_bytes(g, fmt, D, F)
+    if gs > 0:
+        return dict(fmt=fmt, F=F, wg=wg, wu=wu, wd=wd, sg=group_scales(g, F, D, gs),
+                    su=group_scales(g, F, D, gs), sd=group_scales(g, D, F, gs), gs=gs)
+    return dict(fmt=fmt, F=F, wg=wg, wu=wu, wd=wd, sg=scales(g, F), su=scales(g, F), sd=scales(g, D))
