@@ -193,8 +193,12 @@ size_t coli_router_workspace_bytes(int S, int E, int D);
  *                       per matrix.
  *   COLI_LAYOUT_TILED : the same bytes regrouped by coli_pack_tiled() so that
  *                       the matrix cores read each weight chunk with one
- *                       contiguous 1 KB load per wave (see there). */
-enum coli_layout { COLI_LAYOUT_ROWS = 0, COLI_LAYOUT_TILED = 1 };
+ *                       contiguous 1 KB load per wave (see there).
+ *   COLI_LAYOUT_TILED_GROUPED : grouped-scale int4 (gs > 0) only: the tiled
+ *                       layout with each segment's 16 words transposed
+ *                       (coli_pack_tiled_grouped), and the scales packed by
+ *                       coli_pack_scales_grouped. */
+enum coli_layout { COLI_LAYOUT_ROWS = 0, COLI_LAYOUT_TILED = 1, COLI_LAYOUT_TILED_GROUPED = 2 };
 
 /* Bytes of the tiled copy of `count` stacked [O, I] matrices of format fmt
  * (COLI_I8 / I4 / I2), or -1 for invalid arguments.  It is count * ceil(O /
@@ -222,6 +226,31 @@ int64_t coli_tiled_bytes(int fmt, int64_t count, int O, int I);
  * COLI_EDEVICE. */
 int coli_pack_tiled(int fmt, const void *W, int64_t count, int O, int I, void *dst, void *stream);
 
+/* The grouped tiled layout of int4 matrices with one scale per gs elements
+ * (the pages' int4-grouped format [docs-quickstart -- qt_resolve_fmt]): the
+ * coli_pack_tiled layout of COLI_I4 rows (same size, coli_tiled_bytes) with
+ * the 16 four-byte words of each row's 64-byte segment transposed -- word 4q
+ * + s of the unit row comes from word 4s + q of the segment -- so that the
+ * matrix cores' step s (the s-th word of every lane chunk) covers 32
+ * consecutive elements 32 s .. 32 s + 31, one group of 32 or a part of a
+ * larger group.  Arguments and errors as coli_pack_tiled (fmt COLI_I4). */
+int coli_pack_tiled_grouped(const void *W, int64_t count, int O, int I, void *dst, void *stream);
+
+/* Bytes of the packed group scales of `count` stacked [O, I] matrices with
+ * one scale per gs elements: count * ceil(O / 16) * (kpad / gs) * 64, kpad =
+ * I rounded up to 1024; -1 for invalid arguments (gs not one of 32, 64, 128,
+ * 256, 512, 1024).  Host only. */
+int64_t coli_grouped_scale_bytes(int64_t count, int O, int I, int gs);
+
+/* Packs scales S [count, O, ceil(I / gs)] fp32 (row o's groups consecutive)
+ * into dst [coli_grouped_scale_bytes(count, O, I, gs) bytes]: per matrix,
+ * per 16-row tile t and group g, the 16 rows' scales of g (64 bytes) at
+ * float offset (t * (kpad / gs) + g) * 16 -- zero for rows past O and groups
+ * past ceil(I / gs).  Caller memory, 16-byte aligned; nothing is allocated.
+ * Asynchronous on `stream`.  Errors: COLI_EINVAL (NULL), COLI_ESHAPE,
+ * COLI_ERANGE (gs), COLI_EALIGN, COLI_EDEVICE. */
+int coli_pack_scales_grouped(const float *S, int64_t count, int O, int I, int gs, float *dst, void *stream);
+
 /* Routed experts stacked in one allocation per tensor
  * [glm.c@98759bf -- typedef ESlot; metal@93cde63 -- moe_submit]:
  *   w_gate, w_up  [E, F, coli_row_bytes(fmt, D)] bytes,
@@ -231,27 +260,37 @@ int coli_pack_tiled(int fmt, const void *W, int64_t count, int O, int I, void *d
  * layout COLI_LAYOUT_ROWS (0), or COLI_LAYOUT_TILED: then each weight tensor
  * is the coli_pack_tiled() copy of the stack above (w_gate of E matrices
  * [F, D], w_down of E matrices [D, F]), 16-byte aligned, with whole 16-byte
- * row segments (rows of D and of F). */
+ * row segments (rows of D and of F).
+ * gs: 0 (one scale per row), or grouped-scale int4 [docs-quickstart --
+ * qt_resolve_fmt]: fmt COLI_I4, one scale per gs (32, 64, .., 1024)
+ * consecutive elements along the row, layout COLI_LAYOUT_TILED_GROUPED --
+ * the weights packed by coli_pack_tiled_grouped, s_gate / s_up the
+ * coli_pack_scales_grouped copies of [E, F, ceil(D/gs)] and s_down of
+ * [E, D, ceil(F/gs)] (16-byte aligned):
+ *     y[o] = sum_g s[o, g] * sum_{i in group g} v(o, i) x_i.
+ * Grouped experts run at COLI_PREC_FP32 only (other prec: COLI_EFMT). */
 typedef struct {
     int fmt;
     int E, D, F;
     const void *w_gate, *w_up, *w_down;
     const float *s_gate, *s_up, *s_down;
     int layout;
+    int gs;
 } coli_experts;
 
 /* One SwiGLU MLP applied with weight 1 to every token: the shared expert
  * [glm.c@98759bf -- moe, phase E; dense_mlp]:  down(silu(gate x) * up x).
  *   w_gate, w_up [F, coli_row_bytes(fmt, D)], w_down [D, coli_row_bytes(fmt, F)],
  *   s_gate, s_up [F], s_down [D].  D is the experts' D.
- *   layout as coli_experts (one matrix each); a tiled shared expert needs
- *   tiled routed experts of the same fmt and F. */
+ *   layout and gs as coli_experts (one matrix each); a tiled shared expert
+ *   needs tiled routed experts of the same fmt, F, layout and gs. */
 typedef struct {
     int fmt;
     int F;
     const void *w_gate, *w_up, *w_down;
     const float *s_gate, *s_up, *s_down;
     int layout;
+    int gs;
 } coli_mlp;
 
 /* Router parameters for coli_moe_layer (see coli_router).  E and D are the

@@ -258,3 +258,50 @@ def test_idot_precision_host_checks(L):
         assert lay["hf"] - lay["xsum"] >= (5 * S + 3 * rows) * 4
         assert lay["hsum"] - lay["hf"] >= rows * kp(F)
         assert lay["work"] - lay["hsum"] >= rows * 7 * 4
+
+
+def test_grouped_scale_host_checks(L):
+    """Grouped-scale int4 experts: gs one of 32 .. 1024, fmt int4, the grouped
+    tiled layout exactly when gs > 0, fp32 precision only, a tiled shared
+    expert of the same gs; the packed scale sizes (no device work)."""
+    from weight_streaming_gemv_qgemv_amd import binding as b
+    assert b.grouped_scale_bytes(1, 16, 64, 32) == 1 * 1 * (1024 // 32) * 64
+    assert b.grouped_scale_bytes(3, 17, 1025, 128) == 3 * 2 * (2048 // 128) * 64
+    assert b.grouped_scale_bytes(256, 2048, 6144, 128) == 256 * 128 * 48 * 64
+    for bad in (0, 16, 48, 2048):
+        assert b.grouped_scale_bytes(1, 16, 64, bad) == -1
+    ps = L.coli_pack_scales_grouped
+    assert ps(FAKE, 1, 16, 64, 48, FAKE, None) == b.ERANGE
+    assert ps(FAKE, 1, 16, 64, 32, FAKE + 4, None) == b.EALIGN
+    assert ps(None, 1, 16, 64, 32, FAKE, None) == b.EINVAL
+    assert ps(FAKE, 0, 16, 64, 32, FAKE, None) == b.OK
+    pt = L.coli_pack_tiled_grouped
+    assert pt(FAKE, 1, 16, 40, FAKE, None) == b.EALIGN          # 20-byte rows
+    assert pt(None, 1, 16, 64, FAKE, None) == b.EINVAL
+    assert pt(FAKE, 0, 16, 64, FAKE, None) == b.OK
+    E, D, F, S, K = 8, 64, 64, 4, 2
+
+    def layer(ex, sh, prec=b.PREC_FP32):
+        need = b.moe_workspace_bytes(S, K, E, ex.D, ex.F, sh.F if sh else 0, prec)
+        assert need > 0
+        return L.coli_moe_layer(C.byref(b.RouterParams(FAKE, FAKE, K, 1, 2.5, 0.0)), C.byref(ex),
+                                C.byref(sh) if sh else None, FAKE, S, FAKE, FAKE, FAKE, None, None,
+                                prec, FAKE, need - 1, None)
+
+    def ex(fmt=2, layout=2, gs=32):
+        return b.Experts(fmt, E, D, F, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, layout, gs)
+
+    def sh(layout=2, gs=32, Fs=F):
+        return b.Mlp(2, Fs, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, layout, gs)
+    assert layer(ex(), None) == b.EWORKSPACE                     # valid up to the workspace
+    assert layer(ex(gs=1024), sh(gs=1024)) == b.EWORKSPACE
+    assert layer(ex(), sh(layout=0, gs=0)) == b.EWORKSPACE       # row-major shared, per-row scales
+    assert layer(ex(gs=48), None) == b.ERANGE
+    assert layer(ex(layout=1), None) == b.EINVAL                 # grouped scales need layout 2
+    assert layer(ex(gs=0), None) == b.EINVAL                     # layout 2 needs grouped scales
+    assert layer(ex(fmt=1), None) == b.EFMT                      # int4 only
+    assert layer(ex(), None, b.PREC_BF16) == b.EFMT
+    assert layer(ex(), None, b.PREC_IDOT) == b.EFMT
+    assert layer(ex(), sh(gs=64)) == b.EINVAL                    # shared gs differs
+    assert layer(ex(), sh(Fs=2 * F)) == b.EINVAL
+    assert layer(b.Experts(2, E, D, F, FAKE, FAKE, FAKE, FAKE + 4, FAKE, FAKE, 2, 32), None) == b.EALIGN

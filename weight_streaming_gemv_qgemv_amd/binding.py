@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_PKG, "libcoli.so")
 
 F32, I8, I4, I2 = 0, 1, 2, 3
 PREC_FP32, PREC_BF16, PREC_IDOT = 0, 1, 2
-LAYOUT_ROWS, LAYOUT_TILED = 0, 1
+LAYOUT_ROWS, LAYOUT_TILED, LAYOUT_TILED_GROUPED = 0, 1, 2
 OK, EINVAL, ESHAPE, EFMT, EALIGN, ERANGE, EWORKSPACE, EDEVICE, EIDX = 0, -1, -2, -3, -4, -5, -6, -7, -8
 
 
@@ -31,14 +31,14 @@ class Experts(C.Structure):
     _fields_ = [("fmt", C.c_int), ("E", C.c_int), ("D", C.c_int), ("F", C.c_int),
                 ("w_gate", C.c_void_p), ("w_up", C.c_void_p), ("w_down", C.c_void_p),
                 ("s_gate", C.c_void_p), ("s_up", C.c_void_p), ("s_down", C.c_void_p),
-                ("layout", C.c_int)]
+                ("layout", C.c_int), ("gs", C.c_int)]
 
 
 class Mlp(C.Structure):
     _fields_ = [("fmt", C.c_int), ("F", C.c_int),
                 ("w_gate", C.c_void_p), ("w_up", C.c_void_p), ("w_down", C.c_void_p),
                 ("s_gate", C.c_void_p), ("s_up", C.c_void_p), ("s_down", C.c_void_p),
-                ("layout", C.c_int)]
+                ("layout", C.c_int), ("gs", C.c_int)]
 
 
 class RouterParams(C.Structure):
@@ -58,7 +58,8 @@ EXPORTS = ["coli_row_bytes", "coli_qgemv", "coli_router", "coli_router_workspace
            "coli_moe_layer", "coli_moe_layer_tail", "coli_qgemv_idot", "coli_qgemv_grouped",
            "coli_qgemv_idot_workspace_bytes", "coli_check_device_flags", "coli_strerror", "coli_version",
            "coli_stage_timing", "coli_stage_times", "coli_stage_name", "coli_moe_layer_noalloc",
-           "coli_tiled_bytes", "coli_pack_tiled"]
+           "coli_tiled_bytes", "coli_pack_tiled", "coli_pack_tiled_grouped", "coli_grouped_scale_bytes",
+           "coli_pack_scales_grouped"]
 NSTAGES = 8
 
 _lib = None
@@ -95,6 +96,12 @@ def lib():
         L.coli_tiled_bytes.argtypes = [i32, i64, i32, i32]
         L.coli_pack_tiled.restype = i32
         L.coli_pack_tiled.argtypes = [i32, vp, i64, i32, i32, vp, vp]
+        L.coli_pack_tiled_grouped.restype = i32
+        L.coli_pack_tiled_grouped.argtypes = [vp, i64, i32, i32, vp, vp]
+        L.coli_grouped_scale_bytes.restype = i64
+        L.coli_grouped_scale_bytes.argtypes = [i64, i32, i32, i32]
+        L.coli_pack_scales_grouped.restype = i32
+        L.coli_pack_scales_grouped.argtypes = [vp, i64, i32, i32, i32, vp, vp]
         L.coli_moe_layer_noalloc.restype = i32
         L.coli_moe_layer_noalloc.argtypes = [C.POINTER(RouterParams), C.POINTER(Experts), C.POINTER(Mlp),
                                              vp, i32, vp, vp, vp, vp, vp, i32, vp]
@@ -261,31 +268,38 @@ def router(Wr, bias, x, K: int, norm_topk: int = 1, routed_scale: float = 2.5, t
 def _check_mlp_sizes(d: dict, n: int, D: int, F: int, what: str):
     """Weight and scale tensors of n stacked experts of width D x F hold at
     least the bytes their layout needs."""
-    fmt, lay = d["fmt"], int(d.get("layout", LAYOUT_ROWS))
-    if lay == LAYOUT_TILED:
+    fmt, lay, gs = d["fmt"], int(d.get("layout", LAYOUT_ROWS)), int(d.get("gs", 0))
+    if lay in (LAYOUT_TILED, LAYOUT_TILED_GROUPED):
         gu, dn = tiled_bytes(fmt, n, F, D), tiled_bytes(fmt, n, D, F)
     else:
         gu, dn = n * F * row_bytes(fmt, D), n * D * row_bytes(fmt, F)
     _need(d["wg"], gu, what + " w_gate")
     _need(d["wu"], gu, what + " w_up")
     _need(d["wd"], dn, what + " w_down")
-    _need(d["sg"], 4 * n * F, what + " s_gate")
-    _need(d["su"], 4 * n * F, what + " s_up")
-    _need(d["sd"], 4 * n * D, what + " s_down")
+    if gs and lay == LAYOUT_TILED_GROUPED:
+        sgu, sdn = grouped_scale_bytes(n, F, D, gs), grouped_scale_bytes(n, D, F, gs)
+        if sgu < 0 or sdn < 0:
+            raise ColiError(ERANGE, what + " gs")
+    else:
+        sgu, sdn = 4 * n * F, 4 * n * D
+    _need(d["sg"], sgu, what + " s_gate")
+    _need(d["su"], sgu, what + " s_up")
+    _need(d["sd"], sdn, what + " s_down")
 
 
 def experts_struct(ex: dict) -> Experts:
     _check_mlp_sizes(ex, ex["E"], ex["D"], ex["F"], "experts")
     return Experts(ex["fmt"], ex["E"], ex["D"], ex["F"], _ptr(ex["wg"]), _ptr(ex["wu"]),
                    _ptr(ex["wd"]), _ptr(ex["sg"]), _ptr(ex["su"]), _ptr(ex["sd"]),
-                   int(ex.get("layout", LAYOUT_ROWS)))
+                   int(ex.get("layout", LAYOUT_ROWS)), int(ex.get("gs", 0)))
 
 
 def mlp_struct(sh: dict, D: int | None = None) -> Mlp:
     if D is not None:
         _check_mlp_sizes(sh, 1, D, sh["F"], "shared expert")
     return Mlp(sh["fmt"], sh["F"], _ptr(sh["wg"]), _ptr(sh["wu"]), _ptr(sh["wd"]),
-               _ptr(sh["sg"]), _ptr(sh["su"]), _ptr(sh["sd"]), int(sh.get("layout", LAYOUT_ROWS)))
+               _ptr(sh["sg"]), _ptr(sh["su"]), _ptr(sh["sd"]), int(sh.get("layout", LAYOUT_ROWS)),
+               int(sh.get("gs", 0)))
 
 
 # ------------------------------------------------------------------ tiled layout
@@ -308,14 +322,63 @@ def pack_tiled(fmt: int, W: torch.Tensor, count: int, O: int, I: int, dst: torch
     return dst
 
 
+def pack_tiled_grouped(W: torch.Tensor, count: int, O: int, I: int, dst: torch.Tensor | None = None,
+                       stream=None) -> torch.Tensor:
+    """The grouped tiled copy of `count` stacked row-major int4 [O, I]
+    matrices (uint8)."""
+    nb = tiled_bytes(I4, count, O, I)
+    if nb < 0:
+        raise ColiError(ESHAPE, "coli_tiled_bytes")
+    if dst is None:
+        dst = torch.empty((max(nb, 16),), dtype=torch.uint8, device=W.device)
+    _need(W, count * O * row_bytes(I4, I), "pack_tiled_grouped W")
+    _need(dst, nb, "pack_tiled_grouped dst")
+    rc = lib().coli_pack_tiled_grouped(_ptr(W), count, O, I, _ptr(dst), _stream(stream))
+    _check(rc, "coli_pack_tiled_grouped")
+    return dst
+
+
+def grouped_scale_bytes(count: int, O: int, I: int, gs: int) -> int:
+    return int(lib().coli_grouped_scale_bytes(count, O, I, gs))
+
+
+def pack_scales_grouped(S: torch.Tensor, count: int, O: int, I: int, gs: int,
+                        dst: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Group scales [count, O, ceil(I / gs)] fp32 packed per 16-row tile and
+    group (float32 tensor of grouped_scale_bytes / 4 elements)."""
+    nb = grouped_scale_bytes(count, O, I, gs)
+    if nb < 0:
+        raise ColiError(ERANGE, "coli_grouped_scale_bytes")
+    if dst is None:
+        dst = torch.empty((max(nb // 4, 4),), dtype=torch.float32, device=S.device)
+    _need(S, 4 * count * O * ((I + gs - 1) // gs), "pack_scales_grouped S")
+    _need(dst, nb, "pack_scales_grouped dst")
+    rc = lib().coli_pack_scales_grouped(_ptr(S), count, O, I, gs, _ptr(dst), _stream(stream))
+    _check(rc, "coli_pack_scales_grouped")
+    return dst
+
+
 def tile_mlps(ex: dict, D: int | None = None) -> dict:
     """A copy of an experts dict (stacked E experts) or of a shared-expert
     dict (one matrix each; pass the width D) with its weights in the tiled
-    layout; the scales are the original tensors."""
+    layout; the scales are the original tensors -- or, for grouped-scale
+    int4 (a "gs" entry), weights and scales in the grouped tiled layout."""
     n = ex.get("E", 1)
     D = ex["D"] if D is None else D
     F = ex["F"]
     out = dict(ex)
+    gs = int(ex.get("gs", 0))
+    if gs:
+        if ex["fmt"] != I4:
+            raise ColiError(EFMT, "tile_mlps: grouped scales need int4")
+        out["wg"] = pack_tiled_grouped(ex["wg"], n, F, D)
+        out["wu"] = pack_tiled_grouped(ex["wu"], n, F, D)
+        out["wd"] = pack_tiled_grouped(ex["wd"], n, D, F)
+        out["sg"] = pack_scales_grouped(ex["sg"], n, F, D, gs)
+        out["su"] = pack_scales_grouped(ex["su"], n, F, D, gs)
+        out["sd"] = pack_scales_grouped(ex["sd"], n, D, F, gs)
+        out["layout"] = LAYOUT_TILED_GROUPED
+        return out
     out["wg"] = pack_tiled(ex["fmt"], ex["wg"], n, F, D)
     out["wu"] = pack_tiled(ex["fmt"], ex["wu"], n, F, D)
     out["wd"] = pack_tiled(ex["fmt"], ex["wd"], n, D, F)

@@ -595,8 +595,12 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
     const bool sh_mm = mm && sh && sh->fmt == ex->fmt && sh->F == F && sh->layout == ex->layout &&
                        al16(sh->w_gate) && al16(sh->w_up) && al16(sh->w_down);
     // tiled weights: matrix cores only (the host checks guarantee mm)
-    const int tiled = ex->layout == COLI_LAYOUT_TILED ? 1 : 0;
+    const int tiled = ex->layout != COLI_LAYOUT_ROWS ? 1 : 0;
     if (tiled && !mm) return COLI_EALIGN;
+    // grouped-scale int4 (fp32 precision, grouped tiled layout): group
+    // scales packed [row tile][group][16 rows], kpad / gs groups per row
+    const int gs = ex->gs;
+    if (gs && (prec != COLI_PREC_FP32 || ex->layout != COLI_LAYOUT_TILED_GROUPED || !mm)) return COLI_EINVAL;
     const int64_t gstrD = tiled ? coli_tiled_bytes(ex->fmt, 1, F, D) : (int64_t)F * rbD;   // gate, up
     const int64_t gstrF = tiled ? coli_tiled_bytes(ex->fmt, 1, D, F) : (int64_t)D * rbF;   // down
     // matrix-core passes: 16 rows as bf16 hi/lo column pairs (fp32-level
@@ -662,7 +666,9 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
             a.s[1] = ex->s_up;
             a.w_gstride = gstrD;
             a.tiled = tiled;
-            a.s_gstride = F;
+            a.s_gstride = gs ? (int64_t)((F + 15) / 16) * (kpD / gs) * 16 : F;
+            a.gs_spg = gs / 32;
+            a.gs_ngp = gs ? kpD / gs : 0;
             a.ngroups = E;
             a.O = F;
             if (sh_mm) {
@@ -699,7 +705,9 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
             d.s[0] = ex->s_down;
             d.w_gstride = gstrF;
             d.tiled = tiled;
-            d.s_gstride = D;
+            d.s_gstride = gs ? (int64_t)((D + 15) / 16) * (kpF / gs) * 16 : D;
+            d.gs_spg = gs / 32;
+            d.gs_ngp = gs ? kpF / gs : 0;
             d.ngroups = E;
             d.O = D;
             if (sh_mm) {

@@ -50,6 +50,11 @@ struct DecArgs {
     int hf_kpad;
     int tiled;               // weights in the tiled layout (coli_pack_tiled); w_gstride
                              // is then the tiled bytes of one matrix
+    // grouped-scale int4 (0: one scale per row): steps of 32 elements per
+    // group, and groups per row of the packed scales ([row tile][gs_ngp][16]
+    // floats per matrix, s_gstride floats apart); weights in the grouped tiled
+    // layout (coli_pack_tiled_grouped)
+    int gs_spg, gs_ngp;
     int tiles;               // set by dec_launch
 };
 

@@ -71,7 +71,11 @@ __device__ __forceinline__ void dma16(const void *g, uint32_t lds)
 
 typedef __attribute__((address_space(3))) const void lds_void;
 
-template <int FMT, int M, bool TILED>
+// SPG > 0: grouped-scale int4 (one scale per 32 SPG elements; SPG = 8
+// stands for every group of 256 or more, a.gs_spg steps) on the grouped
+// tiled layout, whose segments hold MFMA step s' of lane q as elements
+// 32 s' + 8 q .. + 7, so that each step covers 32 consecutive elements.
+template <int FMT, int M, bool TILED, int SPG = 0>
 __global__ __launch_bounds__(256) void k_dec(DecArgs a)
 {
     using T = MF<FMT>;
@@ -84,6 +88,13 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
     constexpr int IPW = NT * STEPS / kDecWaves;   // DMA instructions per wave and k-block
     static_assert(IPW >= 1 && STEPS % IPW == 0, "a wave stages steps of one N-tile");
     __shared__ uint4 bsA[UNITS], bsB[UNITS];   // staged k-blocks (even, odd)
+    // grouped scales: per wave and k-block its M x MT row tiles' scales of
+    // the k-block's NGK groups, 16 rows each (64 bytes), NSI KB a wave
+    constexpr bool GS = SPG > 0;
+    static_assert(!GS || (TILED && FMT == kI4), "grouped scales: tiled int4");
+    constexpr int NGK = GS ? (SPG < 8 ? 8 / SPG : 1) : 1;
+    constexpr int NSI = GS ? (M * MT * NGK * 64 + 1023) / 1024 : 0;
+    __shared__ float4 ssA[GS ? kDecWaves * NSI * 64 : 1], ssB[GS ? kDecWaves * NSI * 64 : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = lane & 15, q = lane >> 4, lrow = lane >> 2, lchunk = lane & 3;
@@ -186,7 +197,10 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
             else au = cload(a.row_pair + gr) / a.K;
             ar = t == u ? au : ar;
         }
-        c.doff = (uint32_t)ar * arow + 32 * q + 16 * (col & 1);
+        // the unit of chunk q of step s' of a segment sits at byte 32 (4 s' +
+        // q) of the segment's 512 bytes; on the grouped layout lane q of step
+        // s' takes the unit at 32 (4 q + s')
+        c.doff = (uint32_t)ar * arow + (GS ? 128 * q : 32 * q) + 16 * (col & 1);
     };
     // Tiled weights are loaded with the non-temporal hint: each unit is read
     // once per pass, and keeping that stream out of L2 leaves the activation
@@ -249,14 +263,48 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
     // instructions -- N-tile nw, steps s0.. -- none for a dead N-tile.
     auto stageB = [&](const It &c, int kbi, const uint4 *buf) {
         if (8 * nw >= c.nt) return;                     // uniform
-        const uint32_t o = c.doff + (uint32_t)(kbi * STEPS + s0) * kChunkStep;
         const uint32_t lbase = (uint32_t)(uintptr_t)(const lds_void *)(buf + (nw * STEPS + s0) * kWave);
+        if constexpr (GS) {
+#pragma unroll
+            for (int i = 0; i < IPW; ++i) {
+                const uint32_t st = (uint32_t)(kbi * STEPS + s0 + i);
+                dma16(actb + (c.doff + 512u * (st >> 2) + 32u * (st & 3u)),
+                      __builtin_amdgcn_readfirstlane(lbase + i * 1024));
+            }
+            return;
+        }
+        const uint32_t o = c.doff + (uint32_t)(kbi * STEPS + s0) * kChunkStep;
 #pragma unroll
         for (int i = 0; i < IPW; ++i)
             dma16(actb + (o + (uint32_t)i * kChunkStep), __builtin_amdgcn_readfirstlane(lbase + i * 1024));
     };
+    // Grouped scales of k-block kbi into this wave's region of sbuf: scale
+    // tensors packed as [row tile][group][16 rows] (coli_pack_scales_grouped),
+    // so a row tile's NGK groups of one k-block are 64 NGK contiguous bytes;
+    // byte b of the region is row tile b / (64 NGK) (m major), its byte
+    // b % (64 NGK); lanes past the region read its last 16 bytes again.
+    const int ngp = GS ? a.gs_ngp : 0;
+    auto stageS = [&](const It &c, int kbi, const float4 *sbuf) {
+        if constexpr (GS) {
+            const int g0 = kbi * 8 / a.gs_spg;
+            const uint32_t lbase = (uint32_t)(uintptr_t)(const lds_void *)(sbuf + wave * NSI * 64);
+            const int mt16 = (c.Og + 15) / 16;
+            const int obt = (c.tile * RPB + wave * RPW) / 16;
+#pragma unroll
+            for (int k = 0; k < NSI; ++k) {
+                const int b = min(1024 * k + 16 * lane, M * MT * NGK * 64 - 16);
+                const int ti = b / (64 * NGK), within = b - ti * (64 * NGK);
+                const int m = ti / MT, mt = ti - m * MT;
+                const int rt = min(obt + mt, mt16 - 1);
+                const float *src = c.sc[m] + ((int64_t)rt * ngp + g0) * 16 + within / 4;
+                dma16(src, __builtin_amdgcn_readfirstlane(lbase + k * 1024));
+            }
+        }
+    };
 
     floatx4 acc[M][MT][NT], accs[NT];
+    // grouped scales: the scaled sum of the finished groups
+    floatx4 tot[GS ? M : 1][GS ? MT : 1][GS ? NT : 1];
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
 #pragma unroll
@@ -265,13 +313,44 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
             for (int mt = 0; mt < MT; ++mt) acc[m][mt][n] = floatx4{0.f, 0.f, 0.f, 0.f};
         accs[n] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
+    if constexpr (GS) {
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) tot[m][mt][n] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+    const floatx4 zero4 = floatx4{0.f, 0.f, 0.f, 0.f};
     const uint32_t one2 = opaque_v(0x3F803F80u);       // bf16 (1, 1)
     const uint4 ones = make_uint4(one2, one2, one2, one2);
 
     // one k-block over the first NL N-tiles: weights moved into the operand
     // layout in place (lane (q, col) gets row col, chunk q, from lane 4 col
     // + q), then per MFMA step the M x MT code products and the column sums
-    auto compute_n = [&](auto nl, uint4 (&w)[M][MT][SEGS], const uint4 *buf, int rkb) {
+    // GS: after the last step of each group its products, less OFF times its
+    // column sums, are scaled by the group's scales (from sbuf, the k-block
+    // ckb's) and added to tot; the next group starts from zero
+    auto flush = [&](auto nl, const float4 *sbuf, int gl) {
+        constexpr int NL = decltype(nl)::value;
+        if constexpr (GS) {
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const float4 sv = sbuf[wave * NSI * 64 + ((m * MT + mt) * NGK + gl) * 4 + q];
+#pragma unroll
+                    for (int n = 0; n < NL; ++n) {
+                        tot[m][mt][n][0] = fmaf(sv.x, fmaf(-OFF, accs[n][0], acc[m][mt][n][0]), tot[m][mt][n][0]);
+                        tot[m][mt][n][1] = fmaf(sv.y, fmaf(-OFF, accs[n][1], acc[m][mt][n][1]), tot[m][mt][n][1]);
+                        tot[m][mt][n][2] = fmaf(sv.z, fmaf(-OFF, accs[n][2], acc[m][mt][n][2]), tot[m][mt][n][2]);
+                        tot[m][mt][n][3] = fmaf(sv.w, fmaf(-OFF, accs[n][3], acc[m][mt][n][3]), tot[m][mt][n][3]);
+                    }
+                }
+        }
+    };
+    auto compute_n = [&](auto nl, uint4 (&w)[M][MT][SEGS], const uint4 *buf, int rkb,
+                         const float4 *sbuf = nullptr, int ckb = 0) {
         constexpr int NL = decltype(nl)::value;
         if constexpr (!TILED) {   // the tiled layout arrives in the operand layout
 #pragma unroll
@@ -307,16 +386,29 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
 #pragma unroll
                     for (int n = 0; n < NL; ++n) bn[n] = buf[(n * STEPS + s2 + 1) * kWave + lane];
                 }
+                // grouped scales: a group starts from zero -- at steps s2 % SPG
+                // == 0, or (SPG = 8) at the first step of a k-block whose
+                // first element starts a group
+                const bool fresh = GS && (SPG < 8 ? s2 % (SPG < 8 ? SPG : 1) == 0
+                                                  : s2 == 0 && (ckb * 8) % a.gs_spg == 0);
 #pragma unroll
                 for (int m = 0; m < M; ++m)
 #pragma unroll
                     for (int mt = 0; mt < MT; ++mt) {
                         const uint4 cw = codes_late<FMT>(w[m][mt][s2 / SPS], s2 % SPS);
 #pragma unroll
-                        for (int n = 0; n < NL; ++n) acc[m][mt][n] = mfma(cw, b[n], acc[m][mt][n]);
+                        for (int n = 0; n < NL; ++n)
+                            acc[m][mt][n] = mfma(cw, b[n], fresh ? zero4 : acc[m][mt][n]);
                     }
 #pragma unroll
-                for (int n = 0; n < NL; ++n) accs[n] = mfma(ones, b[n], accs[n]);
+                for (int n = 0; n < NL; ++n) accs[n] = mfma(ones, b[n], fresh ? zero4 : accs[n]);
+                if constexpr (GS) {
+                    if constexpr (SPG < 8) {
+                        if ((s2 + 1) % SPG == 0) flush(nl, sbuf, s2 / SPG);
+                    } else if (s2 == STEPS - 1 && (ckb == nkb - 1 || ((ckb + 1) * 8) % a.gs_spg == 0)) {
+                        flush(nl, sbuf, 0);   // uniform
+                    }
+                }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int n = 0; n < NL; ++n) b[n] = bn[n];
@@ -342,11 +434,12 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
     };
     // the products of k-block buf (tiled: of segment sg only, sg < 0: all)
     // over the live N-tiles
-    auto compute_s = [&](uint4 (&w)[M][MT][SEGS], const uint4 *buf, int ntl, int sg) {
+    auto compute_s = [&](uint4 (&w)[M][MT][SEGS], const uint4 *buf, int ntl, int sg,
+                         const float4 *sbuf = nullptr, int ckb = 0) {
         if constexpr (NT == 2) {
-            if (ntl == 2) { compute_n(std::integral_constant<int, 2>{}, w, buf, sg); return; }
+            if (ntl == 2) { compute_n(std::integral_constant<int, 2>{}, w, buf, sg, sbuf, ckb); return; }
         }
-        compute_n(std::integral_constant<int, 1>{}, w, buf, sg);
+        compute_n(std::integral_constant<int, 1>{}, w, buf, sg, sbuf, ckb);
     };
     auto compute = [&](uint4 (&w)[M][MT][SEGS], const uint4 *buf, int ntl) { compute_s(w, buf, ntl, -1); };
     // Tiled: segment by segment, and as soon as a segment's products are
@@ -354,10 +447,11 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
     // registers.  The loads sit after the N-tile branch has joined: a
     // register with a load in flight that the branches had placed apart
     // would be copied at the join, and the copy waits for every load.
-    auto compute_r = [&](uint4 (&w)[M][MT][SEGS], const uint4 *buf, int ntl, Ld rc) {
+    auto compute_r = [&](uint4 (&w)[M][MT][SEGS], const uint4 *buf, int ntl, Ld rc,
+                         const float4 *sbuf = nullptr, int ckb = 0) {
 #pragma unroll
         for (int sg = 0; sg < SEGS; ++sg) {
-            compute_s(w, buf, ntl, sg);
+            compute_s(w, buf, ntl, sg, sbuf, ckb);
             __builtin_amdgcn_sched_barrier(0);
             if (rc.on) loadSeg(rc, sg, w);
         }
@@ -365,6 +459,7 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
 
     float sreg[M][MT][4];
     auto load_epi = [&](const It &c) {
+        if constexpr (GS) return;   // grouped scales were applied group by group
         const int obase = c.tile * RPB + wave * RPW;
 #pragma unroll
         for (int m = 0; m < M; ++m)
@@ -398,17 +493,25 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
 #pragma unroll
                 for (int m = 0; m < M; ++m)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        v[m][r] = acc[m][mt][n][r] + __shfl_xor(acc[m][mt][n][r], 1, kWave);
+                    for (int r = 0; r < 4; ++r) {
+                        if constexpr (GS)
+                            v[m][r] = tot[m][mt][n][r] + __shfl_xor(tot[m][mt][n][r], 1, kWave);
+                        else
+                            v[m][r] = acc[m][mt][n][r] + __shfl_xor(acc[m][mt][n][r], 1, kWave);
+                    }
                 const int ob = obase + 16 * mt + 4 * q;
                 float res[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    float y = sreg[0][mt][r] * (v[0][r] - OFF * xs);
-                    if constexpr (M == 2) {
-                        const float u = sreg[1][mt][r] * (v[1][r] - OFF * xs);
-                        y = silu_f(y) * u;
+                    float y, u;
+                    if constexpr (GS) {
+                        y = v[0][r];
+                        u = M == 2 ? v[M - 1][r] : 0.f;
+                    } else {
+                        y = sreg[0][mt][r] * (v[0][r] - OFF * xs);
+                        u = M == 2 ? sreg[M - 1][mt][r] * (v[M - 1][r] - OFF * xs) : 0.f;
                     }
+                    if constexpr (M == 2) y = silu_f(y) * u;
                     res[r] = ob + r < c.Og ? y : 0.f;
                 }
                 float *op = a.out + (int64_t)(c.r0t + tok) * a.ldo;
@@ -465,7 +568,10 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
 #pragma unroll
             for (int m = 0; m < M; ++m)
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) acc[m][mt][n] = floatx4{0.f, 0.f, 0.f, 0.f};
+                for (int mt = 0; mt < MT; ++mt) {
+                    acc[m][mt][n] = floatx4{0.f, 0.f, 0.f, 0.f};
+                    if constexpr (GS) tot[m][mt][n] = floatx4{0.f, 0.f, 0.f, 0.f};
+                }
             accs[n] = floatx4{0.f, 0.f, 0.f, 0.f};
         }
         if (!fast || (M == 2 && a.hf && !hfast)) return 0;
@@ -532,17 +638,21 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
         uint4 wA[M][MT][SEGS], wB[M][MT][SEGS];
         loadW(cur, 0, wA);
         stageB(cur, 0, bsA);
+        stageS(cur, 0, ssA);
         loadW(cur, 1, wB);
         // one k-block: its products from weights w and activations buf
-        // (k-block kb in LDS), the next k-block's activations staged into
-        // nbuf, and the loads of l recycled into w
+        // (k-block kb in LDS), the next k-block's activations (and grouped
+        // scales) staged into nbuf, and the loads of l recycled into w; the
+        // scale DMA is issued with the activation DMA, before the weights
         auto kstep = [&](int ntl, uint4 (&w)[M][MT][SEGS], const uint4 *buf, const It &sc, int skb,
                          const uint4 *nbuf, const Ld &l, bool epi = false, int extra = 0) {
             step_sync_x(extra);
             stageB(sc, skb, nbuf);
+            const bool even = buf == bsA;
+            stageS(sc, skb, even ? ssB : ssA);
             if (epi) load_epi(cur);   // after the wait: it does not hold back the weights
             __builtin_amdgcn_sched_barrier(0);
-            compute_r(w, buf, ntl, l);
+            compute_r(w, buf, ntl, l, even ? ssA : ssB, skb > 0 ? skb - 1 : nkb - 1);
             __builtin_amdgcn_sched_barrier(0);
         };
         // extra: the stores the previous item's epilogue left in flight
@@ -621,11 +731,11 @@ int dec_resident_blocks(const void *kern, int threads, int *cache)
     return cache[dev];
 }
 
-template <int FMT, int M, bool TILED>
+template <int FMT, int M, bool TILED, int SPG = 0>
 hipError_t launch_dec(const DecArgs &a, int64_t items, hipStream_t st)
 {
     static int cache[64] = {0};
-    const void *kern = (const void *)k_dec<FMT, M, TILED>;
+    const void *kern = (const void *)k_dec<FMT, M, TILED, SPG>;
     constexpr int threads = 64 * DecTiles<M>::W;
     int64_t cap = dec_resident_blocks(kern, threads, cache) / kDecXcds * kDecXcds;
     if (cap < kDecXcds) cap = kDecXcds;
@@ -634,10 +744,10 @@ hipError_t launch_dec(const DecArgs &a, int64_t items, hipStream_t st)
     if (grid < kDecXcds) grid = kDecXcds;
     const KernelEvents ev = take_kernel_events();   // timed stage: events at the kernel's bounds
     if (ev.start)
-        hipExtLaunchKernelGGL((k_dec<FMT, M, TILED>), dim3((unsigned)grid), dim3(threads), 0, st, ev.start,
-                              ev.stop, 0, a);
+        hipExtLaunchKernelGGL((k_dec<FMT, M, TILED, SPG>), dim3((unsigned)grid), dim3(threads), 0, st,
+                              ev.start, ev.stop, 0, a);
     else
-        hipLaunchKernelGGL((k_dec<FMT, M, TILED>), dim3((unsigned)grid), dim3(threads), 0, st, a);
+        hipLaunchKernelGGL((k_dec<FMT, M, TILED, SPG>), dim3((unsigned)grid), dim3(threads), 0, st, a);
     return hipGetLastError();
 }
 
@@ -673,6 +783,19 @@ hipError_t dec_launch(DecArgs a, int fmt, int M, int64_t max_group_passes, hipSt
     const int rpb = dec_rows_per_block(M);
     a.tiles = (Ocover + rpb - 1) / rpb;
     const int64_t items = max_group_passes * a.tiles;
+    if (a.gs_spg > 0) {   // grouped-scale int4, grouped tiled layout
+        if (fmt != kI4 || !a.tiled) return hipErrorInvalidValue;
+        const int spg = a.gs_spg;
+#define COLI_DEC_GS(MM)                                                          \
+        if (spg == 1) return launch_dec<kI4, MM, true, 1>(a, items, st);         \
+        if (spg == 2) return launch_dec<kI4, MM, true, 2>(a, items, st);         \
+        if (spg == 4) return launch_dec<kI4, MM, true, 4>(a, items, st);         \
+        if (spg % 8 == 0) return launch_dec<kI4, MM, true, 8>(a, items, st);     \
+        return hipErrorInvalidValue;
+        if (M == 2) { COLI_DEC_GS(2) }
+        COLI_DEC_GS(1)
+#undef COLI_DEC_GS
+    }
 #define COLI_DEC_CASES(MM, TT)                                      \
     switch (fmt) {                                                 \
     case kI8: return launch_dec<kI8, MM, TT>(a, items, st);        \

@@ -42,6 +42,7 @@ int coli__router_splits(int S, int E, int D, int *slice);
 int64_t coli__router_partial_bytes(int S, int E, int D);
 
 int coli__check_pack(int fmt, const void *W, int64_t count, int O, int I, const void *dst);
+int coli__check_pack_scales(const float *S, int64_t count, int O, int I, int gs, const float *dst);
 int coli__check_moe(const coli_experts *ex, const coli_mlp *sh, const float *x,
                     int S, int K, const int32_t *idx, const float *w,
                     const float *out, int prec, const void *ws, size_t ws_bytes,

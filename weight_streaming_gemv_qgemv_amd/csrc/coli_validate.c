@@ -248,17 +248,29 @@ int64_t coli_tiled_bytes(int fmt, int64_t count, int O, int I)
 static int64_t matrix_bytes(int fmt, int layout, int O, int I)
 {
     int64_t t;
-    if (layout == COLI_LAYOUT_TILED) return coli_tiled_bytes(fmt, 1, O, I);
+    if (layout == COLI_LAYOUT_TILED || layout == COLI_LAYOUT_TILED_GROUPED)
+        return coli_tiled_bytes(fmt, 1, O, I);
     if (!mul_ok(coli_row_bytes(fmt, I), O, &t)) return -1;
     return t;
 }
 
-static int check_mlp_tensors(int fmt, int layout, int D, int F, const void *wg, const void *wu,
+static int valid_gs(int gs)
+{
+    return gs == 32 || gs == 64 || gs == 128 || gs == 256 || gs == 512 || gs == 1024;
+}
+
+static int check_mlp_tensors(int fmt, int layout, int gs, int D, int F, const void *wg, const void *wu,
                              const void *wd, const float *sg, const float *su,
                              const float *sd, int64_t count)
 {
     if (fmt != COLI_I8 && fmt != COLI_I4 && fmt != COLI_I2) return COLI_EFMT;
-    if (layout != COLI_LAYOUT_ROWS && layout != COLI_LAYOUT_TILED) return COLI_EINVAL;
+    if (layout != COLI_LAYOUT_ROWS && layout != COLI_LAYOUT_TILED && layout != COLI_LAYOUT_TILED_GROUPED)
+        return COLI_EINVAL;
+    /* grouped scales: int4 in the grouped tiled layout, and only there */
+    if (gs != 0 && !valid_gs(gs)) return COLI_ERANGE;
+    if ((gs != 0) != (layout == COLI_LAYOUT_TILED_GROUPED)) return COLI_EINVAL;
+    if (gs != 0 && fmt != COLI_I4) return COLI_EFMT;
+    if (gs != 0 && (!aligned(sg, 16) || !aligned(su, 16) || !aligned(sd, 16))) return COLI_EALIGN;
     if (F < 1 || D < 1) return COLI_ESHAPE;
     int64_t a = matrix_bytes(fmt, layout, F, D), b = matrix_bytes(fmt, layout, D, F);
     if (a < 0 || b < 0 || !mul_ok(a, count, &a) || !mul_ok(b, count, &b)) return COLI_ESHAPE;
@@ -266,8 +278,8 @@ static int check_mlp_tensors(int fmt, int layout, int D, int F, const void *wg, 
     if (!aligned(wg, 4) || !aligned(wu, 4) || !aligned(wd, 4) || !aligned(sg, 4) ||
         !aligned(su, 4) || !aligned(sd, 4))
         return COLI_EALIGN;
-    /* the tiled layout is read by the matrix-core kernels only */
-    if (layout == COLI_LAYOUT_TILED &&
+    /* the tiled layouts are read by the matrix-core kernels only */
+    if (layout != COLI_LAYOUT_ROWS &&
         (coli_row_bytes(fmt, D) % 16 || coli_row_bytes(fmt, F) % 16 || !aligned(wg, 16) ||
          !aligned(wu, 16) || !aligned(wd, 16)))
         return COLI_EALIGN;
@@ -323,19 +335,20 @@ int coli__check_moe(const coli_experts *ex, const coli_mlp *sh, const float *x,
     if (prec != COLI_PREC_FP32 && prec != COLI_PREC_BF16 && prec != COLI_PREC_IDOT) return COLI_EINVAL;
     if (S < 0 || K < 0 || ex->E < 0 || ex->D < 0 || ex->F < 0) return COLI_ESHAPE;
     if (ex->E < 1 || ex->E > COLI_MAX_E || K < 1 || K > COLI_MAX_K) return COLI_ERANGE;
-    int rc = check_mlp_tensors(ex->fmt, ex->layout, ex->D, ex->F, ex->w_gate, ex->w_up, ex->w_down,
+    int rc = check_mlp_tensors(ex->fmt, ex->layout, ex->gs, ex->D, ex->F, ex->w_gate, ex->w_up, ex->w_down,
                                ex->s_gate, ex->s_up, ex->s_down, ex->E);
     if (rc) return rc;
     if (sh) {
         if (sh->F < 1) return COLI_ESHAPE;
-        rc = check_mlp_tensors(sh->fmt, sh->layout, ex->D, sh->F, sh->w_gate, sh->w_up, sh->w_down,
+        rc = check_mlp_tensors(sh->fmt, sh->layout, sh->gs, ex->D, sh->F, sh->w_gate, sh->w_up, sh->w_down,
                                sh->s_gate, sh->s_up, sh->s_down, 1);
         if (rc) return rc;
         /* a tiled shared expert runs as one more group of the routed kernels */
-        if (sh->layout == COLI_LAYOUT_TILED &&
-            (ex->layout != COLI_LAYOUT_TILED || sh->fmt != ex->fmt || sh->F != ex->F))
+        if (sh->layout != COLI_LAYOUT_ROWS &&
+            (ex->layout != sh->layout || sh->fmt != ex->fmt || sh->F != ex->F || sh->gs != ex->gs))
             return COLI_EINVAL;
     }
+    if (ex->gs != 0 && prec != COLI_PREC_FP32) return COLI_EFMT;   /* grouped scales: fp32 kernels only */
     if (prec == COLI_PREC_IDOT) {
         /* the integer-dot kernels: int8 / int4, tiled, rows of whole 16-byte
          * segments, widths within the quantiser's 16384 */
@@ -358,5 +371,24 @@ int coli__check_moe(const coli_experts *ex, const coli_mlp *sh, const float *x,
         return COLI_EALIGN;
     if (!ws || ws_bytes < need) return COLI_EWORKSPACE;
     if (!aligned(ws, ALIGN_WS)) return COLI_EALIGN;
+    return COLI_OK;
+}
+
+int64_t coli_grouped_scale_bytes(int64_t count, int O, int I, int gs)
+{
+    if (count < 0 || O < 0 || I < 0 || !valid_gs(gs)) return -1;
+    int64_t t;
+    const int64_t ngp = coli__kpad(I) / gs;
+    if (!mul_ok(count, (O + 15) / 16, &t) || !mul_ok(t, ngp, &t) || !mul_ok(t, 64, &t)) return -1;
+    return t;
+}
+
+int coli__check_pack_scales(const float *S, int64_t count, int O, int I, int gs, const float *dst)
+{
+    if (!valid_gs(gs)) return COLI_ERANGE;
+    if (count < 0 || O < 0 || I < 0 || coli_grouped_scale_bytes(count, O, I, gs) < 0) return COLI_ESHAPE;
+    if (count == 0 || O == 0 || I == 0) return COLI_OK;
+    if (!S || !dst) return COLI_EINVAL;
+    if (!aligned(S, 4) || !aligned(dst, 16)) return COLI_EALIGN;
     return COLI_OK;
 }
