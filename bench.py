@@ -42,11 +42,14 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def expert_bytes(fmt, D, F):
+def expert_bytes(fmt, D, F, gs=0):
+    """Bytes of one expert's gate+up and down matrices with their scales
+    (one per row, or with gs > 0 one per gs elements of a row)."""
     from weight_streaming_gemv_qgemv_amd import synth
     rbD, rbF = synth.packed_row_bytes(fmt, D), synth.packed_row_bytes(fmt, F)
-    gate_up = 2 * F * rbD + 2 * F * 4
-    down = D * rbF + D * 4
+    sD, sF = (-(-D // gs), -(-F // gs)) if gs else (1, 1)
+    gate_up = 2 * F * rbD + 2 * F * sD * 4
+    down = D * rbF + D * sF * 4
     return gate_up, down
 
 
@@ -138,8 +141,14 @@ def recorded_trace_ms(workload, kernel_key):
 
 
 def kernel_key(name, args):
-    """rocprofv3's name of the int4 gate/up kernel for the layout in use."""
-    return f"{name}<2, 2, {'true' if getattr(args, 'layout', 'rows') == 'tiled' else 'false'}>"
+    """rocprofv3's name of the int4 gate/up kernel for the layout in use (and
+    for k_dec its group-scale variant: 0, or 32-element steps per group, 8
+    for every group of 256 or more)."""
+    tiled = 'true' if getattr(args, 'layout', 'rows') == 'tiled' else 'false'
+    if name != "k_dec":
+        return f"{name}<2, 2, {tiled}>"
+    gs = getattr(args, "grouped", 0)
+    return f"{name}<2, 2, {tiled}, {min(gs // 32, 8) if gs else 0}>"
 
 
 def trace_roofline(dom, units_per_launch, peak):
@@ -286,9 +295,10 @@ def run_layer64(args, dev, tail=False):
     from weight_streaming_gemv_qgemv_amd import binding as b
     from weight_streaming_gemv_qgemv_amd import synth
     S, K, E, D, F, fmt = 64, 8, 256, 6144, 2048, 2
-    log("generating 256 int4 experts + shared expert (host)")
-    bank = synth.expert_bank(4000, fmt, E, D, F)
-    shared = synth.shared_mlp(4000, fmt, D, F)
+    gs = args.grouped
+    log("generating 256 int4 experts + shared expert (host)" + (f", one scale per {gs} elements" if gs else ""))
+    bank = synth.expert_bank(4000, fmt, E, D, F, gs=gs)
+    shared = synth.shared_mlp(4000, fmt, D, F, gs=gs)
     g = synth.rng(4001)
     Wr, bias = synth.router_weights(g, E, D)
     x = synth.activations(g, S, D)
@@ -316,7 +326,7 @@ def run_layer64(args, dev, tail=False):
     step(0)
     torch.cuda.synchronize()
     uniq = int(np.unique(idx_o.cpu().numpy()).size)
-    gu, dn = expert_bytes(fmt, D, F)
+    gu, dn = expert_bytes(fmt, D, F, gs)
     step_bytes = (E * D * 4 + E * 4) + S * D * 4 + uniq * (gu + dn) + (gu + dn) + S * D * 4 + S * K * 8
     if tail:
         step_bytes += D * 4 + S * D * 4      # the norm weight, and x read again for the residual
@@ -325,14 +335,17 @@ def run_layer64(args, dev, tail=False):
     # dominant kernel: gate/up + SwiGLU (2/3 of the expert bytes), one launch per step
     gu_ms, gu_n = stages["gate_up"]
     gu_bytes = (uniq + 1) * gu + S * D * 4 + (S * K + S) * F * 4
-    res = dict(workload="moe_layer_tail_decode_64" if tail else "moe_layer_decode_64", ms=ms, wall=wall,
+    wl = ("moe_layer_tail_decode_64" if tail else "moe_layer_decode_64") + (f"_g{gs}" if gs else "")
+    res = dict(workload=wl, ms=ms, wall=wall,
                step_bytes=step_bytes,
                tokens=S, stages=stages, uniq=uniq,
                dominant=dict(kernel="k_dec<I4,2> (grouped expert gate/up + SwiGLU, matrix cores)",
                              bytes_per_launch=gu_bytes, ms_per_launch=gu_ms / max(gu_n, 1),
                              launches=gu_n,
-                             traffic=recorded_traffic("moe_layer_decode_64", kernel_key("k_dec", args)),
-                             trace_ms=recorded_trace_ms("moe_layer_decode_64", kernel_key("k_dec", args))))
+                             traffic=recorded_traffic(wl, kernel_key("k_dec", args)),
+                             trace_ms=recorded_trace_ms(wl, kernel_key("k_dec", args))))
+    if gs:
+        res["weight_format"] = f"int4 grouped scales (one per {gs} elements)"
     if not args.no_cpu_baseline and not tail:
         ntok = args.cpu_tokens
         log(f"cpu baseline: oracle on {ntok} tokens")
@@ -644,7 +657,8 @@ def main():
     ap.add_argument("--idot", action="store_true",
                     help="qgemv and prefill2048 workloads: the integer-dot (int8 activation) variant")
     ap.add_argument("--grouped", type=int, default=0, metavar="GS",
-                    help="qgemv workload: grouped-scale int4, one scale per GS elements")
+                    help="qgemv, layer64 and tail64 workloads: grouped-scale int4, one scale per GS "
+                         "elements (layer64 / tail64: tiled layout, fp32 precision)")
     ap.add_argument("--ep-slice", type=int, default=0, metavar="N",
                     help="layer64 / prefill2048: time one GPU's share under expert parallelism "
                          "over N GPUs (256/N local experts; the slice with the most routed rows, "
@@ -674,6 +688,10 @@ def main():
         raise SystemExit("--idot applies to the qgemv and prefill2048 workloads")
     if args.idot and args.workload == "prefill2048" and (args.layout != "tiled" or args.ep_slice):
         raise SystemExit("prefill2048 --idot runs on the tiled layout, without --ep-slice")
+    if args.grouped and args.workload not in ("qgemv", "layer64", "tail64"):
+        raise SystemExit("--grouped applies to the qgemv, layer64 and tail64 workloads")
+    if args.grouped and args.workload != "qgemv" and (args.layout != "tiled" or args.ep_slice):
+        raise SystemExit("grouped experts run on the tiled layout, without --ep-slice")
     if args.workload == "copy":
         run_copy(args, dev)
         return

@@ -76,7 +76,7 @@ typedef __attribute__((address_space(3))) const void lds_void;
 // tiled layout, whose segments hold MFMA step s' of lane q as elements
 // 32 s' + 8 q .. + 7, so that each step covers 32 consecutive elements.
 template <int FMT, int M, bool TILED, int SPG = 0>
-__global__ __launch_bounds__(256) void k_dec(DecArgs a)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SPG > 0 ? 2 : 1))) void k_dec(DecArgs a)
 {
     using T = MF<FMT>;
     constexpr int STEPS = T::STEPS, KB = T::KB, SEGS = T::SEGS, BITS = T::BITS, SPS = T::SPS;
@@ -296,7 +296,12 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
                 const int ti = b / (64 * NGK), within = b - ti * (64 * NGK);
                 const int m = ti / MT, mt = ti - m * MT;
                 const int rt = min(obt + mt, mt16 - 1);
-                const float *src = c.sc[m] + ((int64_t)rt * ngp + g0) * 16 + within / 4;
+                // m varies across lanes: a select, not an index (an indexed
+                // per-lane read of c.sc would put the item in scratch memory)
+                const float *sb = c.sc[0];
+#pragma unroll
+                for (int mm = 1; mm < M; ++mm) sb = m == mm ? c.sc[mm] : sb;
+                const float *src = sb + ((int64_t)rt * ngp + g0) * 16 + within / 4;
                 dma16(src, __builtin_amdgcn_readfirstlane(lbase + k * 1024));
             }
         }
@@ -324,6 +329,15 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
     const floatx4 zero4 = floatx4{0.f, 0.f, 0.f, 0.f};
     const uint32_t one2 = opaque_v(0x3F803F80u);       // bf16 (1, 1)
     const uint4 ones = make_uint4(one2, one2, one2, one2);
+    // groups of one or two steps: the group's -OFF times its column sums is
+    // made by the matrix cores (A = bf16 -OFF, exact) and is the C operand
+    // the group's first product starts from, so a group's flush is one
+    // multiply-add per output (the VALU work is what bounds these groups)
+    constexpr bool CI = GS && SPG <= 2;
+    constexpr uint32_t noff_bf = __builtin_bit_cast(uint32_t, -OFF) >> 16;
+    static_assert(!CI || (__builtin_bit_cast(uint32_t, -OFF) & 0xFFFFu) == 0, "-OFF is a bf16 value");
+    const uint32_t noff2 = opaque_v(noff_bf | noff_bf << 16);
+    const uint4 noffs = make_uint4(noff2, noff2, noff2, noff2);
 
     // one k-block over the first NL N-tiles: weights moved into the operand
     // layout in place (lane (q, col) gets row col, chunk q, from lane 4 col
@@ -341,10 +355,17 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
                     const float4 sv = sbuf[wave * NSI * 64 + ((m * MT + mt) * NGK + gl) * 4 + q];
 #pragma unroll
                     for (int n = 0; n < NL; ++n) {
-                        tot[m][mt][n][0] = fmaf(sv.x, fmaf(-OFF, accs[n][0], acc[m][mt][n][0]), tot[m][mt][n][0]);
-                        tot[m][mt][n][1] = fmaf(sv.y, fmaf(-OFF, accs[n][1], acc[m][mt][n][1]), tot[m][mt][n][1]);
-                        tot[m][mt][n][2] = fmaf(sv.z, fmaf(-OFF, accs[n][2], acc[m][mt][n][2]), tot[m][mt][n][2]);
-                        tot[m][mt][n][3] = fmaf(sv.w, fmaf(-OFF, accs[n][3], acc[m][mt][n][3]), tot[m][mt][n][3]);
+                        if constexpr (CI) {   // the products started from -OFF times the column sums
+                            tot[m][mt][n][0] = fmaf(sv.x, acc[m][mt][n][0], tot[m][mt][n][0]);
+                            tot[m][mt][n][1] = fmaf(sv.y, acc[m][mt][n][1], tot[m][mt][n][1]);
+                            tot[m][mt][n][2] = fmaf(sv.z, acc[m][mt][n][2], tot[m][mt][n][2]);
+                            tot[m][mt][n][3] = fmaf(sv.w, acc[m][mt][n][3], tot[m][mt][n][3]);
+                        } else {
+                            tot[m][mt][n][0] = fmaf(sv.x, fmaf(-OFF, accs[n][0], acc[m][mt][n][0]), tot[m][mt][n][0]);
+                            tot[m][mt][n][1] = fmaf(sv.y, fmaf(-OFF, accs[n][1], acc[m][mt][n][1]), tot[m][mt][n][1]);
+                            tot[m][mt][n][2] = fmaf(sv.z, fmaf(-OFF, accs[n][2], acc[m][mt][n][2]), tot[m][mt][n][2]);
+                            tot[m][mt][n][3] = fmaf(sv.w, fmaf(-OFF, accs[n][3], acc[m][mt][n][3]), tot[m][mt][n][3]);
+                        }
                     }
                 }
         }
@@ -386,11 +407,19 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
 #pragma unroll
                     for (int n = 0; n < NL; ++n) bn[n] = buf[(n * STEPS + s2 + 1) * kWave + lane];
                 }
-                // grouped scales: a group starts from zero -- at steps s2 % SPG
-                // == 0, or (SPG = 8) at the first step of a k-block whose
-                // first element starts a group
-                const bool fresh = GS && (SPG < 8 ? s2 % (SPG < 8 ? SPG : 1) == 0
-                                                  : s2 == 0 && (ckb * 8) % a.gs_spg == 0);
+                // grouped scales: a group of fewer than 8 steps starts from
+                // zero at steps s2 % SPG == 0 (a group of a k-block or more,
+                // SPG = 8, finds its sums zeroed by the last group's flush)
+                const bool fresh = GS && SPG < 8 && s2 % (SPG < 8 ? SPG : 1) == 0;
+                if constexpr (CI) {
+                    if (fresh) {   // the group's steps: this one and (SPG = 2) the next
+#pragma unroll
+                        for (int n = 0; n < NL; ++n) {
+                            accs[n] = mfma(noffs, b[n], zero4);
+                            if constexpr (SPG == 2) accs[n] = mfma(noffs, bn[n], accs[n]);
+                        }
+                    }
+                }
 #pragma unroll
                 for (int m = 0; m < M; ++m)
 #pragma unroll
@@ -398,15 +427,25 @@ __global__ __launch_bounds__(256) void k_dec(DecArgs a)
                         const uint4 cw = codes_late<FMT>(w[m][mt][s2 / SPS], s2 % SPS);
 #pragma unroll
                         for (int n = 0; n < NL; ++n)
-                            acc[m][mt][n] = mfma(cw, b[n], fresh ? zero4 : acc[m][mt][n]);
+                            acc[m][mt][n] = mfma(cw, b[n], fresh ? (CI ? accs[n] : zero4) : acc[m][mt][n]);
                     }
+                if constexpr (!CI) {
 #pragma unroll
-                for (int n = 0; n < NL; ++n) accs[n] = mfma(ones, b[n], fresh ? zero4 : accs[n]);
+                    for (int n = 0; n < NL; ++n) accs[n] = mfma(ones, b[n], fresh ? zero4 : accs[n]);
+                }
                 if constexpr (GS) {
                     if constexpr (SPG < 8) {
                         if ((s2 + 1) % SPG == 0) flush(nl, sbuf, s2 / SPG);
                     } else if (s2 == STEPS - 1 && (ckb == nkb - 1 || ((ckb + 1) * 8) % a.gs_spg == 0)) {
                         flush(nl, sbuf, 0);   // uniform
+#pragma unroll
+                        for (int n = 0; n < NL; ++n) {
+#pragma unroll
+                            for (int m = 0; m < M; ++m)
+#pragma unroll
+                                for (int mt = 0; mt < MT; ++mt) acc[m][mt][n] = zero4;
+                            accs[n] = zero4;
+                        }
                     }
                 }
                 __builtin_amdgcn_sched_barrier(0);
