@@ -384,7 +384,19 @@ __global__ __launch_bounds__(1024) void k_group_place(const int32_t *__restrict_
 // Block (s, c) covers columns [c * kCombineCols, +kCombineCols) of token s:
 // one float4 (vec4) or one float per thread, all K rows read together.
 constexpr int kCombineThreads = 256;
-__global__ __launch_bounds__(kCombineThreads) void k_combine(const float *__restrict__ y, int D, int K,
+// y rows in fp32, or (bf16-precision layers) rounded to bf16
+__device__ __forceinline__ float4 yload4(const float *y, int64_t i) { return *reinterpret_cast<const float4 *>(y + i); }
+__device__ __forceinline__ float4 yload4(const uint16_t *y, int64_t i)
+{
+    const uint2 u = *reinterpret_cast<const uint2 *>(y + i);
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
+}
+__device__ __forceinline__ float yload1(const float *y, int64_t i) { return y[i]; }
+__device__ __forceinline__ float yload1(const uint16_t *y, int64_t i) { return __uint_as_float((uint32_t)y[i] << 16); }
+
+template <typename YT>
+__global__ __launch_bounds__(kCombineThreads) void k_combine(const YT *__restrict__ y, int D, int K,
                                                  const int32_t *__restrict__ pair_row,
                                                  const float *__restrict__ w, int has_shared,
                                                  int64_t shared_row0, const float *resid, float *out,
@@ -411,8 +423,7 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(const float *__rest
             }
 #pragma unroll
             for (int j = 0; j < kCombineRun; ++j)
-                v[j] = r[j] >= 0 ? *reinterpret_cast<const float4 *>(y + (int64_t)r[j] * D + d)
-                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+                v[j] = r[j] >= 0 ? yload4(y, (int64_t)r[j] * D + d) : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
             for (int j = 0; j < kCombineRun; ++j) {
                 if (r[j] < 0) continue;
@@ -423,7 +434,7 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(const float *__rest
             }
         }
         if (has_shared) {
-            const float4 v = *reinterpret_cast<const float4 *>(y + (shared_row0 + s) * (int64_t)D + d);
+            const float4 v = yload4(y, (shared_row0 + s) * (int64_t)D + d);
             acc.x += v.x;
             acc.y += v.y;
             acc.z += v.z;
@@ -447,25 +458,31 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(const float *__rest
 #pragma unroll
             for (int j = 0; j < kCombineRun; ++j) r[j] = k0 + j < K ? pr[k0 + j] : -1;
 #pragma unroll
-            for (int j = 0; j < kCombineRun; ++j) v[j] = r[j] >= 0 ? y[(int64_t)r[j] * D + d] : 0.f;
+            for (int j = 0; j < kCombineRun; ++j) v[j] = r[j] >= 0 ? yload1(y, (int64_t)r[j] * D + d) : 0.f;
 #pragma unroll
             for (int j = 0; j < kCombineRun; ++j)
                 if (r[j] >= 0) acc = fmaf(ws[k0 + j], v[j], acc);
         }
-        if (has_shared) acc += y[(shared_row0 + s) * (int64_t)D + d];
+        if (has_shared) acc += yload1(y, (shared_row0 + s) * (int64_t)D + d);
         if (resid) acc = resid[(int64_t)s * D + d] + acc;
         out[(int64_t)s * D + d] = acc;
     }
 }
 
+// y_bf16: the y rows are bf16 (uint16_t elements, same row stride D)
 hipError_t combine_launch(const float *y, int S, int D, int K, const int32_t *pair_row,
                           const float *w, int has_shared, int64_t shared_row0, float *out,
-                          int vec4, hipStream_t st, const float *resid)
+                          int vec4, hipStream_t st, const float *resid, int y_bf16 = 0)
 {
     const int per = vec4 ? 4 * kCombineThreads : kCombineThreads;
     const dim3 grid((unsigned)S, (unsigned)((D + per - 1) / per));
-    hipLaunchKernelGGL(k_combine, grid, dim3(kCombineThreads), 0, st, y, D, K, pair_row, w,
-                       has_shared, shared_row0, resid, out, vec4);
+    if (y_bf16)
+        hipLaunchKernelGGL(k_combine<uint16_t>, grid, dim3(kCombineThreads), 0, st,
+                           reinterpret_cast<const uint16_t *>(y), D, K, pair_row, w, has_shared, shared_row0,
+                           resid, out, vec4);
+    else
+        hipLaunchKernelGGL(k_combine<float>, grid, dim3(kCombineThreads), 0, st, y, D, K, pair_row, w,
+                           has_shared, shared_row0, resid, out, vec4);
     return hipGetLastError();
 }
 
@@ -856,6 +873,7 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
         float *hpart = reinterpret_cast<float *>(ws + L.hsum);
         float *hsum = reinterpret_cast<float *>(ws + L.hsum + rows * nparts * 4);
         const int64_t max_gp = L.n_pass_max;
+        const int ybf = sh && !sh_mm ? 0 : 1;
         {
             StageTimer tp(kStPrep, st);
             if (xrows_bf16_launch(ex->fmt, x, D, S, D, kpD, xt, tok_sum, st) != hipSuccess) return COLI_EDEVICE;
@@ -892,9 +910,7 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
             a.act_row = act_row;
             a.row_sum = row_sum;
             a.act = xt;
-            a.out = h;
-            a.ldo = L.h_ld;
-            a.out_vec4 = L.h_ld % 4 == 0 && al16(h);
+            a.out = nullptr;   // h only as the down product's bf16 row table
             a.hf = ht;
             a.hf_kpad = kpF;
             a.hpart = hpart;
@@ -930,6 +946,9 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
             d.act = ht;
             d.out = y;
             d.ldo = D;
+            // y rounded to bf16 (half the bytes written here and read by the
+            // combine), unless a vector-ALU shared expert writes fp32 rows
+            d.out_bf16 = ybf;
             d.out_vec4 = D % 4 == 0 && al16(y);
             if (pre_launch(d, ex->fmt, 1, max_gp, st) != hipSuccess) return COLI_EDEVICE;
         }
@@ -939,7 +958,8 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
         }
         StageTimer tcb(kStCombine, st);
         return to_status(combine_launch(y, S, D, K, pair_row, w, sh ? 1 : 0, shared_row0, out,
-                                        (int)(al16(out) && al16(y) && D % 4 == 0 && (!resid || al16(resid))), st, resid));
+                                        (int)(al16(out) && al16(y) && D % 4 == 0 && (!resid || al16(resid))), st, resid,
+                                        ybf));
     }
     const bool sh_same_up = sh && sh->fmt == ex->fmt;
     const bool sh_same_down = sh && sh->fmt == ex->fmt && sh->F == F;

@@ -63,10 +63,12 @@ __global__ __launch_bounds__(256) void k_xrows(const float *__restrict__ x, int6
 // LDS DMA of 16 bytes per lane (lane L's bytes land at lds + 16 L), issued
 // from inline assembly: the compiler does not see it, so it neither makes
 // LDS reads wait for it nor counts it in its own waits -- the kernel orders
-// and waits for these loads itself.
+// and waits for these loads itself.  On this GPU family an LDS DMA that
+// reads M0 right after an SALU write of M0 needs one wait state (the s_nop),
+// which the compiler cannot insert inside the asm.
 __device__ __forceinline__ void dma16(const void *g, uint32_t lds)
 {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
 }
 
 typedef __attribute__((address_space(3))) const void lds_void;

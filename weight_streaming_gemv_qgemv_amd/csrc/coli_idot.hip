@@ -287,7 +287,7 @@ typedef __attribute__((address_space(3))) const void lds_void_i;
 
 __device__ __forceinline__ void dma16_i(const void *g, uint32_t lds)
 {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory");
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
 }
 
 constexpr int kPidWaves = 8;

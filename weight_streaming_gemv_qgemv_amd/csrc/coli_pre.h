@@ -36,9 +36,11 @@ struct PreArgs {
     const int *act_row;     // row-table row of grouped row r (NULL: r itself)
     const float *row_sum;   // [grouped row] sum of that row's stored activations
     const uint16_t *act;    // bf16 row table of the activations
-    float *out;             // fp32 result rows (grouped row r at out + r * ldo)
+    float *out;             // result rows (grouped row r at out + r * ldo elements); gate/up:
+                            // NULL for none (the down product reads the row table hf)
     int64_t ldo;
-    int out_vec4;
+    int out_vec4;           // 16-byte aligned rows (fp32) / 8-byte aligned rows (bf16)
+    int out_bf16;           // down: the result rows rounded to bf16 (uint16_t elements)
     // M == 2 only: the result as the next product's bf16 row table (rows =
     // grouped rows, hf_kpad elements) and its partial sums per row:
     // hpart[r * nparts + p], p = tile * 8 + wave

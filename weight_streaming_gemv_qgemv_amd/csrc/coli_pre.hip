@@ -124,10 +124,11 @@ __global__ void k_pre_sum(const float *__restrict__ hpart, int nparts, int rows,
 // LDS DMA of 16 bytes per lane (lane L's bytes land at lds + 16 L), issued
 // from inline assembly: the compiler does not see it, so it neither makes
 // LDS reads wait for it nor counts it in its own waits -- the kernel orders
-// and waits for these loads itself.
+// and waits for these loads itself (s_nop: the wait state an LDS DMA needs
+// after an SALU write of M0).
 __device__ __forceinline__ void dma16(const void *g, uint32_t lds)
 {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory");
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
 }
 
 template <int FMT, int M, bool TILED>
@@ -341,15 +342,19 @@ __global__ __launch_bounds__(64 * kPreWaves) void k_pre(PreArgs a)
     // pass row 16 n + col; xsv[n]: that row's activation sum
     float xsv[NL];
     // Stores of the uniform fast path (the wave's rows inside the matrix and,
-    // for gate/up, inside h's row table; 16-byte result stores): per N-tile
-    // one per row tile, and for gate/up one more per row tile (h) and one
+    // for gate/up, inside h's row table; 16-byte (bf16: 8-byte) result
+    // stores): per N-tile one per row tile (gate/up: only with a result
+    // array), and for gate/up one more per row tile (h's row table) and one
     // (its partial sums).  Every one is issued: each of the NL tiles has a
     // live row.
     constexpr int kStores = NL * (MT + (M == 2 ? MT + 1 : 0));
-    // returns kStores on the fast path, else 0
+    constexpr int kStoresT = NL * (M == 2 ? MT + 1 : MT);   // gate/up without a result array
+    const bool has_out = M == 1 || a.out != nullptr;
+    // returns kStores (kStoresT) on the fast path, else 0
     auto epilogue = [&](const It &c) -> int {
         const int obase = c.tile * RPB + wave * RPW;
-        const bool fast = a.out_vec4 && obase + RPW <= c.Og && (M == 1 || obase + RPW <= a.hf_kpad);
+        const bool fast = (!has_out || a.out_vec4) && obase + RPW <= c.Og &&
+                          (M == 1 || obase + RPW <= a.hf_kpad);
 #pragma unroll
         for (int n = 0; n < NL; ++n) {
             const int t = 16 * n + col;
@@ -369,14 +374,28 @@ __global__ __launch_bounds__(64 * kPreWaves) void k_pre(PreArgs a)
                     }
                     res[r] = ob + r < c.Og ? y : 0.f;
                 }
-                if (live) {
-                    float *op = a.out + gr * a.ldo;
-                    if (fast || (a.out_vec4 && ob + 3 < c.Og)) {
-                        *reinterpret_cast<float4 *>(op + ob) = make_float4(res[0], res[1], res[2], res[3]);
-                    } else {
+                if (live && has_out) {
+                    if (M == 1 && a.out_bf16) {
+                        uint16_t *op = reinterpret_cast<uint16_t *>(a.out) + gr * a.ldo;
+                        uint32_t hb[4];
 #pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            if (ob + r < c.Og) op[ob + r] = res[r];
+                        for (int r = 0; r < 4; ++r) hb[r] = bf16_rne(res[r]);
+                        if (fast || (a.out_vec4 && ob + 3 < c.Og)) {
+                            *reinterpret_cast<uint2 *>(op + ob) = make_uint2(hb[0] | hb[1] << 16, hb[2] | hb[3] << 16);
+                        } else {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                if (ob + r < c.Og) op[ob + r] = (uint16_t)hb[r];
+                        }
+                    } else {
+                        float *op = a.out + gr * a.ldo;
+                        if (fast || (a.out_vec4 && ob + 3 < c.Og)) {
+                            *reinterpret_cast<float4 *>(op + ob) = make_float4(res[0], res[1], res[2], res[3]);
+                        } else {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                if (ob + r < c.Og) op[ob + r] = res[r];
+                        }
                     }
                 }
                 if constexpr (M == 2) {
@@ -422,7 +441,7 @@ __global__ __launch_bounds__(64 * kPreWaves) void k_pre(PreArgs a)
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                 for (int n = 0; n < NL; ++n) acc[m][mt][n] = floatx4{0.f, 0.f, 0.f, 0.f};
-        return fast ? kStores : 0;
+        return fast ? (has_out ? kStores : kStoresT) : 0;
     };
 
     // the staged k-block is complete once this wave's DMA loads are: they
@@ -490,12 +509,14 @@ __global__ __launch_bounds__(64 * kPreWaves) void k_pre(PreArgs a)
             __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
         };
         // after is 0, or the pass-row loads (nlist: 2 with a row map, else
-        // 1) plus 0 or kStores
+        // 1) plus 0, kStores or kStoresT
         const int nlist = a.act_row ? 2 : 1;
         auto sync_x = [&](int after) {
             asm volatile("" ::: "memory");
             if (after == 2 + kStores) wait_vm(std::integral_constant<int, NW + 2 + kStores>{});
             else if (after == 1 + kStores) wait_vm(std::integral_constant<int, NW + 1 + kStores>{});
+            else if (after == 2 + kStoresT) wait_vm(std::integral_constant<int, NW + 2 + kStoresT>{});
+            else if (after == 1 + kStoresT) wait_vm(std::integral_constant<int, NW + 1 + kStoresT>{});
             else if (after == 2) wait_vm(std::integral_constant<int, NW + 2>{});
             else if (after == 1) wait_vm(std::integral_constant<int, NW + 1>{});
             else wait_vm(std::integral_constant<int, NW>{});
