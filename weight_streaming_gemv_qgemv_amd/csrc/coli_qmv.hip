@@ -515,6 +515,21 @@ hipError_t launch_q1_nkw(const QmvArgs &a, int nkw, hipStream_t st)
     }
 }
 
+// compute units of the current device (cached per device)
+int64_t qmv_cus()
+{
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] <= 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        cache[dev] = cus;
+    }
+    return cache[dev];
+}
+
 template <int FMT, int MT>
 hipError_t launch_q(const QmvArgs &a, hipStream_t st)
 {
@@ -828,15 +843,29 @@ hipError_t qmv_launch(QmvArgs a, int fmt, hipStream_t st)
         default: return hipErrorInvalidValue;
         }
     }
-    // 64 rows per block once that still gives at least 128 blocks (measured
-    // faster on the 12288-row matrices), else 32
+    // 64 or 48 rows per block once that still gives at least 128 blocks, else
+    // 32 (each block stages every activation row, so fewer rows per block
+    // cost activation traffic): of 64 and 48 the one whose blocks fill the
+    // last round of CUs best, 64 on a tie (12288 rows: 256 blocks of 48
+    // against 192 of 64 -- int8 8 rows 22.0 -> 20.0 us, int4 16.7 -> 16.3 us)
     const bool wide = (int64_t)a.O >= 64 * 128;
+    int mt = 2;
+    if (wide) {
+        const int64_t cus = qmv_cus();
+        auto fill = [&](int rows) {
+            const int64_t blocks = (a.O + rows - 1) / rows, rounds = (blocks + cus - 1) / cus;
+            return (double)blocks / (double)(rounds * cus);
+        };
+        mt = fill(48) > fill(64) ? 3 : 4;
+    }
+#define COLI_Q_MT(F) return mt == 4 ? launch_q<F, 4>(a, st) : mt == 3 ? launch_q<F, 3>(a, st) : launch_q<F, 2>(a, st)
     switch (fmt) {
-    case kI8: return wide ? launch_q<kI8, 4>(a, st) : launch_q<kI8, 2>(a, st);
-    case kI4: return wide ? launch_q<kI4, 4>(a, st) : launch_q<kI4, 2>(a, st);
-    case kI2: return wide ? launch_q<kI2, 4>(a, st) : launch_q<kI2, 2>(a, st);
+    case kI8: COLI_Q_MT(kI8);
+    case kI4: COLI_Q_MT(kI4);
+    case kI2: COLI_Q_MT(kI2);
     default: return hipErrorInvalidValue;
     }
+#undef COLI_Q_MT
 }
 
 }  // namespace coli
