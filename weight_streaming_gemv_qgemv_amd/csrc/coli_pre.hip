@@ -283,18 +283,30 @@ __global__ __launch_bounds__(64 * kPreWaves) void k_pre(PreArgs a)
     // each of 16 rows.  Instruction i = n STEPS + s of the NL x STEPS is
     // issued by wave i % 8.
     constexpr int NI = NL * STEPS, IPW = (NI + kPreWaves - 1) / kPreWaves;
-    auto stageB = [&](int par, int kbi, const uint4 *buf) {
+    // this lane's byte offset, in the row tables, of its unit of instruction
+    // j at k-block 0 for the pass rows of list par (an LDS read)
+    auto stage_base = [&](int par, uint32_t (&rb)[IPW]) {
+#pragma unroll
+        for (int j = 0; j < IPW; ++j) {
+            const int i = min(wave + kPreWaves * j, NI - 1);
+            const int n = i / STEPS, s = i % STEPS;
+            rb[j] = (uint32_t)lrow[par][16 * n + (lane >> 2)] * arow + (uint32_t)(s * 64 + dq * 16);
+        }
+    };
+    auto stageB_r = [&](const uint32_t (&rb)[IPW], int kbi, const uint4 *buf) {
         const uint32_t lbuf = (uint32_t)(uintptr_t)(const lds_void *)buf;
 #pragma unroll
         for (int j = 0; j < IPW; ++j) {
             const int i = wave + kPreWaves * j;
-            if (NI % kPreWaves == 0 || i < NI) {        // uniform
-                const int n = i / STEPS, s = i % STEPS;
-                const uint32_t rowoff = (uint32_t)lrow[par][16 * n + (lane >> 2)] * arow +
-                                        (uint32_t)kbi * (CH * 16) + (uint32_t)(s * 64 + dq * 16);
-                dma16(actb + rowoff, __builtin_amdgcn_readfirstlane(lbuf + (uint32_t)i * 1024));
-            }
+            if (NI % kPreWaves == 0 || i < NI)          // uniform
+                dma16(actb + (rb[j] + (uint32_t)kbi * (CH * 16)),
+                      __builtin_amdgcn_readfirstlane(lbuf + (uint32_t)i * 1024));
         }
+    };
+    auto stageB = [&](int par, int kbi, const uint4 *buf) {
+        uint32_t rb[IPW];
+        stage_base(par, rb);
+        stageB_r(rb, kbi, buf);
     };
 
     floatx4 acc[M][MT][NL];
@@ -526,10 +538,14 @@ __global__ __launch_bounds__(64 * kPreWaves) void k_pre(PreArgs a)
         };
         // products of k-block kb from w and buf; DMA of (spar, skb) into
         // nbuf; W(lc, lkb) recycled into w
+        // the current item's staging offsets, taken once per item (the
+        // next item's first k-block is staged from its list directly)
+        uint32_t rbc[IPW];
         auto kstep = [&](uint4 (&w)[M][MT][SEGS], const uint4 *buf, int spar, int skb, const uint4 *nbuf,
                          const It &lc, int lkb, bool epi = false, int after = 0) {
             sync_x(after);
-            stageB(spar, skb, nbuf);
+            if (spar == par) stageB_r(rbc, skb, nbuf);
+            else stageB(spar, skb, nbuf);
             if (epi) load_epi(cur);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -548,6 +564,7 @@ __global__ __launch_bounds__(64 * kPreWaves) void k_pre(PreArgs a)
             int ar;
             float rs;
             loadList(nxt, ar, rs);
+            stage_base(par, rbc);
             kstep(wA, bsA, par, 1, bsB, cur, 2, false, nlist + stores);
             storeList(par ^ 1, ar, rs);
             kstep(wB, bsB, par, 2, bsA, cur, 3);
