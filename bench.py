@@ -392,9 +392,10 @@ def run_prefill2048(args, dev):
     from weight_streaming_gemv_qgemv_amd import binding as b
     from weight_streaming_gemv_qgemv_amd import synth
     S, K, E, D, F, fmt = 2048, 8, 256, 6144, 2048, 2
-    log("generating 256 int4 experts + shared expert (host)")
-    bank = synth.expert_bank(4000, fmt, E, D, F)
-    shared = synth.shared_mlp(4000, fmt, D, F)
+    gs = args.grouped
+    log("generating 256 int4 experts + shared expert (host)" + (f", one scale per {gs} elements" if gs else ""))
+    bank = synth.expert_bank(4000, fmt, E, D, F, gs=gs)
+    shared = synth.shared_mlp(4000, fmt, D, F, gs=gs)
     g = synth.rng(4500)
     Wr, bias = synth.router_weights(g, E, D)
     x = synth.activations(g, S, D)
@@ -405,16 +406,16 @@ def run_prefill2048(args, dev):
     Wrd, bd_bias = to_dev(Wr, dev), to_dev(bias, dev)
     out = torch.empty((S, D), dtype=torch.float32, device=dev)
     rws = b.alloc_workspace(b.router_workspace_bytes(S, E, D), dev)
-    ws = b.alloc_workspace(b.moe_workspace_bytes(S, K, E, D, F, F, 2 if args.idot else 1), dev)
-
-    prec = 2 if args.idot else 1
+    # grouped scales run on the fp32-precision kernels
+    prec = 2 if args.idot else 0 if gs else 1
+    ws = b.alloc_workspace(b.moe_workspace_bytes(S, K, E, D, F, F, prec), dev)
 
     def step(i):
         b.router(Wrd, bd_bias, xd, K, 1, 2.5, 0.0, ws=rws)
         b.moe_layer(None, bd, sd, xd, pre_idx=idd, pre_w=wd, out=out, prec=prec, ws=ws)
 
     uniq = int(np.unique(idx).size)
-    gu, dn = expert_bytes(fmt, D, F)
+    gu, dn = expert_bytes(fmt, D, F, gs)
     step_bytes = (E * D * 4 + E * 4) + S * D * 4 + uniq * (gu + dn) + (gu + dn) + S * D * 4 + S * K * 8
     rows = S * K + S
     flops = 2 * rows * 3 * D * F            # gate, up, down on every routed and shared row
@@ -430,6 +431,16 @@ def run_prefill2048(args, dev):
                     dominant=dict(kernel="k_preid<I4,2> (grouped expert gate/up + SwiGLU, int8 matrix cores)",
                                   traffic=None, trace_ms=None,
                                   bytes_per_launch=(uniq + 1) * gu + S * D + rows * F * 4,
+                                  flops_per_launch=gu_flops, ms_per_launch=gu_ms / max(gu_n, 1),
+                                  launches=gu_n))
+    if gs:
+        return dict(workload=f"moe_layer_prefill_2048_g{gs}_fp32", ms=ms, wall=wall, step_bytes=step_bytes,
+                    tokens=S, stages=stages, uniq=uniq, flops=flops, t_star=t_star,
+                    weight_format=f"int4 grouped scales (one per {gs} elements)",
+                    dominant=dict(kernel="k_dec<I4,2,SPG> (grouped-scale gate/up + SwiGLU, fp32-precision "
+                                         "matrix-core kernels, 16-row passes)",
+                                  traffic=None, trace_ms=None,
+                                  bytes_per_launch=(uniq + 1) * gu + S * D * 4 + rows * F * 4,
                                   flops_per_launch=gu_flops, ms_per_launch=gu_ms / max(gu_n, 1),
                                   launches=gu_n))
     return dict(workload="moe_layer_prefill_2048_bf16", ms=ms, wall=wall, step_bytes=step_bytes,
@@ -657,8 +668,8 @@ def main():
     ap.add_argument("--idot", action="store_true",
                     help="qgemv and prefill2048 workloads: the integer-dot (int8 activation) variant")
     ap.add_argument("--grouped", type=int, default=0, metavar="GS",
-                    help="qgemv, layer64 and tail64 workloads: grouped-scale int4, one scale per GS "
-                         "elements (layer64 / tail64: tiled layout, fp32 precision)")
+                    help="qgemv, layer64, tail64 and prefill2048 workloads: grouped-scale int4, one "
+                         "scale per GS elements (the MoE workloads: tiled layout, fp32 precision)")
     ap.add_argument("--ep-slice", type=int, default=0, metavar="N",
                     help="layer64 / prefill2048: time one GPU's share under expert parallelism "
                          "over N GPUs (256/N local experts; the slice with the most routed rows, "
@@ -688,10 +699,10 @@ def main():
         raise SystemExit("--idot applies to the qgemv and prefill2048 workloads")
     if args.idot and args.workload == "prefill2048" and (args.layout != "tiled" or args.ep_slice):
         raise SystemExit("prefill2048 --idot runs on the tiled layout, without --ep-slice")
-    if args.grouped and args.workload not in ("qgemv", "layer64", "tail64"):
-        raise SystemExit("--grouped applies to the qgemv, layer64 and tail64 workloads")
-    if args.grouped and args.workload != "qgemv" and (args.layout != "tiled" or args.ep_slice):
-        raise SystemExit("grouped experts run on the tiled layout, without --ep-slice")
+    if args.grouped and args.workload not in ("qgemv", "layer64", "tail64", "prefill2048"):
+        raise SystemExit("--grouped applies to the qgemv, layer64, tail64 and prefill2048 workloads")
+    if args.grouped and args.workload != "qgemv" and (args.layout != "tiled" or args.ep_slice or args.idot):
+        raise SystemExit("grouped experts run on the tiled layout, without --ep-slice or --idot")
     if args.workload == "copy":
         run_copy(args, dev)
         return
@@ -755,7 +766,10 @@ def main():
         tf = dom["flops_per_launch"] / (dom["ms_per_launch"] * 1e-3) / 1e12 if dom["ms_per_launch"] else None
         peak = INT8_PEAK_TOPS if r.get("idot") else BF16_PEAK_TFLOPS
         line["dtype"] = ("int8 activations (per-row absmax/127) x int4 weights, exact int32 dot, "
-                         "fp32 epilogue" if r.get("idot") else "bf16 (int4 weights, fp32 accumulate)")
+                         "fp32 epilogue" if r.get("idot") else
+                         "fp32 activations as bf16 hi+lo pairs on the bf16 matrix cores, fp32 accumulate "
+                         "(grouped-scale int4 weights as exact bf16 codes)" if "weight_format" in r else
+                         "bf16 (int4 weights, fp32 accumulate)")
         line["roofline"] = {"bound": "mfma", "achieved": round(tf, 2) if tf else None,
                             "peak": peak, "unit": "TOP/s" if r.get("idot") else "TFLOP/s",
                             "frac": round(tf / peak, 4) if tf else None,

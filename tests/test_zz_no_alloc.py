@@ -78,6 +78,47 @@ def test_noalloc_small_two_calls(dev, orc, prec):
     _same(_both(dev, None, bd, sd, x, K, prec, pre_idx=idx, pre_w=w), f"given prec{prec}")
 
 
+@pytest.mark.parametrize("gs", [32, 128])
+def test_noalloc_grouped_scales_two_calls(dev, orc, gs):
+    """Grouped-scale int4 experts (grouped tiled layout, fp32 precision)
+    through the static scratch: bit for bit coli_moe_layer, and within the
+    oracle's bound."""
+    from weight_streaming_gemv_qgemv_amd import binding as b
+    E, D, F, K = 24, 512, 256, 4
+    bank = synth.expert_bank(93, 2, E, D, F, gs=gs)
+    shared = synth.shared_mlp(93, 2, D, F, gs=gs)
+    g = synth.rng(94, gs)
+    Wr, bias = synth.router_weights(g, E, D)
+    td, tsd = b.tile_mlps(_bank_dev(bank, dev)), b.tile_mlps(_bank_dev(shared, dev), D)
+    rp = dict(w=to_dev(Wr, dev), bias=to_dev(bias, dev), K=K, norm_topk=1, routed_scale=2.5)
+    for S in (40, 9):
+        x = synth.activations(g, S, D)
+        announce("noalloc grouped", gs, S)
+        res = _both(dev, rp, td, tsd, x, K)
+        _same(res, f"grouped gs{gs} S{S}")
+        r = orc.router(Wr, bias, x, K, 1, 2.5)
+        ref = orc.moe(bank, shared, x, r["idx"], r["w"])
+        assert_within(res[3], ref["out"], ref["mag"], 1e-4, what=f"noalloc grouped gs{gs} S{S}")
+
+
+@pytest.mark.parametrize("fmt", [1, 2])
+def test_noalloc_integer_dots_two_calls(dev, fmt):
+    """The integer-dot expert path (tiled int8 / int4) through the static
+    scratch: bit for bit coli_moe_layer on the same inputs."""
+    from weight_streaming_gemv_qgemv_amd import binding as b
+    E, D, F, K = 24, 512, 256, 4
+    bank = synth.expert_bank(95, fmt, E, D, F)
+    shared = synth.shared_mlp(95, fmt, D, F)
+    g = synth.rng(96, fmt)
+    Wr, bias = synth.router_weights(g, E, D)
+    td, tsd = b.tile_mlps(_bank_dev(bank, dev)), b.tile_mlps(_bank_dev(shared, dev), D)
+    rp = dict(w=to_dev(Wr, dev), bias=to_dev(bias, dev), K=K, norm_topk=1, routed_scale=2.5)
+    for S in (40, 9):
+        x = synth.activations(g, S, D)
+        announce("noalloc idot", fmt, S)
+        _same(_both(dev, rp, td, tsd, x, K, prec=b.PREC_IDOT), f"idot fmt{fmt} S{S}")
+
+
 def test_noalloc_layer_64_then_16_tokens(dev, glm_bank):
     """The 64-token layer (router, 256 int4 experts of 6144 x 2048, shared
     expert), then 16 tokens, through the static scratch."""
