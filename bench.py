@@ -406,8 +406,7 @@ def run_prefill2048(args, dev):
     Wrd, bd_bias = to_dev(Wr, dev), to_dev(bias, dev)
     out = torch.empty((S, D), dtype=torch.float32, device=dev)
     rws = b.alloc_workspace(b.router_workspace_bytes(S, E, D), dev)
-    # grouped scales run on the fp32-precision kernels
-    prec = 2 if args.idot else 0 if gs else 1
+    prec = 2 if args.idot else 1
     ws = b.alloc_workspace(b.moe_workspace_bytes(S, K, E, D, F, F, prec), dev)
 
     def step(i):
@@ -434,11 +433,10 @@ def run_prefill2048(args, dev):
                                   flops_per_launch=gu_flops, ms_per_launch=gu_ms / max(gu_n, 1),
                                   launches=gu_n))
     if gs:
-        return dict(workload=f"moe_layer_prefill_2048_g{gs}_fp32", ms=ms, wall=wall, step_bytes=step_bytes,
+        return dict(workload=f"moe_layer_prefill_2048_g{gs}_bf16", ms=ms, wall=wall, step_bytes=step_bytes,
                     tokens=S, stages=stages, uniq=uniq, flops=flops, t_star=t_star,
                     weight_format=f"int4 grouped scales (one per {gs} elements)",
-                    dominant=dict(kernel="k_dec<I4,2,SPG> (grouped-scale gate/up + SwiGLU, fp32-precision "
-                                         "matrix-core kernels, 16-row passes)",
+                    dominant=dict(kernel="k_pre<I4,2,SPG> (grouped-scale gate/up + SwiGLU, bf16 matrix cores)",
                                   traffic=None, trace_ms=None,
                                   bytes_per_launch=(uniq + 1) * gu + S * D * 4 + rows * F * 4,
                                   flops_per_launch=gu_flops, ms_per_launch=gu_ms / max(gu_n, 1),
@@ -669,7 +667,7 @@ def main():
                     help="qgemv and prefill2048 workloads: the integer-dot (int8 activation) variant")
     ap.add_argument("--grouped", type=int, default=0, metavar="GS",
                     help="qgemv, layer64, tail64 and prefill2048 workloads: grouped-scale int4, one "
-                         "scale per GS elements (the MoE workloads: tiled layout, fp32 precision)")
+                         "scale per GS elements (the MoE workloads: tiled layout)")
     ap.add_argument("--ep-slice", type=int, default=0, metavar="N",
                     help="layer64 / prefill2048: time one GPU's share under expert parallelism "
                          "over N GPUs (256/N local experts; the slice with the most routed rows, "
@@ -767,8 +765,7 @@ def main():
         peak = INT8_PEAK_TOPS if r.get("idot") else BF16_PEAK_TFLOPS
         line["dtype"] = ("int8 activations (per-row absmax/127) x int4 weights, exact int32 dot, "
                          "fp32 epilogue" if r.get("idot") else
-                         "fp32 activations as bf16 hi+lo pairs on the bf16 matrix cores, fp32 accumulate "
-                         "(grouped-scale int4 weights as exact bf16 codes)" if "weight_format" in r else
+                         "bf16 (grouped-scale int4 weights, fp32 accumulate per group)" if "weight_format" in r else
                          "bf16 (int4 weights, fp32 accumulate)")
         line["roofline"] = {"bound": "mfma", "achieved": round(tf, 2) if tf else None,
                             "peak": peak, "unit": "TOP/s" if r.get("idot") else "TFLOP/s",

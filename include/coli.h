@@ -268,7 +268,8 @@ int coli_pack_scales_grouped(const float *S, int64_t count, int O, int I, int gs
  * coli_pack_scales_grouped copies of [E, F, ceil(D/gs)] and s_down of
  * [E, D, ceil(F/gs)] (16-byte aligned):
  *     y[o] = sum_g s[o, g] * sum_{i in group g} v(o, i) x_i.
- * Grouped experts run at COLI_PREC_FP32 only (other prec: COLI_EFMT). */
+ * Grouped experts run at COLI_PREC_FP32 or COLI_PREC_BF16 (COLI_PREC_IDOT:
+ * COLI_EFMT). */
 typedef struct {
     int fmt;
     int E, D, F;

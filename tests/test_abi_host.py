@@ -262,8 +262,9 @@ def test_idot_precision_host_checks(L):
 
 def test_grouped_scale_host_checks(L):
     """Grouped-scale int4 experts: gs one of 32 .. 1024, fmt int4, the grouped
-    tiled layout exactly when gs > 0, fp32 precision only, a tiled shared
-    expert of the same gs; the packed scale sizes (no device work)."""
+    tiled layout exactly when gs > 0, fp32 or bf16 precision (no integer
+    dots), a tiled shared expert of the same gs; the packed scale sizes (no
+    device work)."""
     from weight_streaming_gemv_qgemv_amd import binding as b
     assert b.grouped_scale_bytes(1, 16, 64, 32) == 1 * 1 * (1024 // 32) * 64
     assert b.grouped_scale_bytes(3, 17, 1025, 128) == 3 * 2 * (2048 // 128) * 64
@@ -300,7 +301,7 @@ def test_grouped_scale_host_checks(L):
     assert layer(ex(layout=1), None) == b.EINVAL                 # grouped scales need layout 2
     assert layer(ex(gs=0), None) == b.EINVAL                     # layout 2 needs grouped scales
     assert layer(ex(fmt=1), None) == b.EFMT                      # int4 only
-    assert layer(ex(), None, b.PREC_BF16) == b.EFMT
+    assert layer(ex(), None, b.PREC_BF16) == b.EWORKSPACE         # the bf16 prefill kernels take them too
     assert layer(ex(), None, b.PREC_IDOT) == b.EFMT
     assert layer(ex(), sh(gs=64)) == b.EINVAL                    # shared gs differs
     assert layer(ex(), sh(Fs=2 * F)) == b.EINVAL

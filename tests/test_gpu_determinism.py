@@ -54,13 +54,14 @@ def test_layer_bits_repeat(dev, fmt, prec):
     assert differ == 0, f"{differ} of {REPS - 1} repeats differ"
 
 
-@pytest.mark.parametrize("gs", [32, 128, 512])
-def test_grouped_layer_bits_repeat(dev, gs):
-    """Grouped-scale int4 experts (the fp32 kernels with the group scales
-    staged beside the activations)."""
+@pytest.mark.parametrize("gs,prec", [(32, 0), (128, 0), (512, 0), (32, 1), (64, 1), (128, 1), (512, 1)])
+def test_grouped_layer_bits_repeat(dev, gs, prec):
+    """Grouped-scale int4 experts (the fp32 and bf16 kernels with the group
+    scales staged beside the activations)."""
     import torch
     from weight_streaming_gemv_qgemv_amd import binding as b
-    E, D, F, K, S = 16, 1024, 512, 4, 64
+    E, D, F, K = 16, 1024, 512, 4
+    S = 64 if prec == 0 else 300
     bank = synth.expert_bank(95, 2, E, D, F, gs=gs)
     shared = synth.shared_mlp(95, 2, D, F, gs=gs)
     g = synth.rng(96, gs)
@@ -69,12 +70,12 @@ def test_grouped_layer_bits_repeat(dev, gs):
     td = b.tile_mlps(_dev_bank(bank, dev))
     tsd = b.tile_mlps(_dev_bank(shared, dev), D)
     xd, idd, wd = to_dev(x, dev), to_dev(idx, dev), to_dev(w, dev)
-    ws = b.alloc_workspace(b.moe_workspace_bytes(S, K, E, D, F, F), dev)
-    announce("determinism grouped", gs)
+    ws = b.alloc_workspace(b.moe_workspace_bytes(S, K, E, D, F, F, prec), dev)
+    announce("determinism grouped", gs, prec)
     first = None
     differ = 0
     for _ in range(REPS):
-        out, _ = b.moe_layer(None, td, tsd, xd, pre_idx=idd, pre_w=wd, ws=ws)
+        out, _ = b.moe_layer(None, td, tsd, xd, pre_idx=idd, pre_w=wd, ws=ws, prec=prec)
         o = out.cpu().numpy()
         if first is None:
             first = o

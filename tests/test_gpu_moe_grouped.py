@@ -5,7 +5,8 @@ matrix-core expert kernels.
   scale layout written out here in numpy from their definitions in coli.h
   (byte work: exact).
 * The MoE outputs are checked against the oracle's grouped-scale MoE (fp64,
-  one scale per group) at the fp32-precision bar, over every group size the
+  one scale per group) at the fp32-precision bar (1e-4) and, on the bf16
+  prefill kernels, at the prefill bar (2e-2), over every group size the
   kernels specialise (32, 64, 128 and the groups of 256 or more that span
   k-blocks), ragged widths whose last group is partial, a shared expert, the
   64-token layer and the 2048-token Zipf layer."""
@@ -104,8 +105,30 @@ def test_moe_gemv_grouped(dev, orc, D, F, gs):
     assert_within(out.cpu().numpy(), ref["out"], ref["mag"], 1e-4, what=f"grouped D{D} F{F} gs{gs}")
 
 
+@pytest.mark.parametrize("D,F,gs", [(512, 256, 32), (512, 256, 64), (512, 256, 128), (1024, 512, 256),
+                                    (2048, 1024, 512), (96, 160, 64), (2080, 544, 32), (1056, 800, 256)])
+def test_moe_gemv_grouped_bf16(dev, orc, D, F, gs):
+    """The bf16 prefill kernels on grouped-scale experts (activations rounded
+    once to bf16): the prefill bar, 2e-2 of the chain magnitude."""
+    import torch
+    from weight_streaming_gemv_qgemv_amd import binding as b
+    E, S, K = 12, 150, 4
+    bank = synth.expert_bank(6700 + gs, 2, E, D, F, gs=gs)
+    g = synth.rng(6701, D, F, gs)
+    x = synth.activations(g, S, D)
+    idx, w = synth.routing_zipf(g, S, K, E)
+    idx[2, 1] = -1
+    td = b.tile_mlps(_dev(bank, dev))
+    announce("moe gemv grouped bf16", D, F, gs)
+    out, _ = b.moe_gemv(td, to_dev(x, dev), to_dev(idx, dev), to_dev(w, dev), prec=b.PREC_BF16)
+    torch.cuda.synchronize()
+    ref = orc.moe(bank, None, x, idx, w.astype(np.float64))
+    assert_within(out.cpu().numpy(), ref["out"], ref["mag"], 2e-2, what=f"grouped bf16 D{D} F{F} gs{gs}")
+
+
 @pytest.mark.parametrize("gs", [32, 128])
-def test_moe_layer_grouped_with_shared_and_router(dev, orc, gs):
+@pytest.mark.parametrize("prec", [0, 1])
+def test_moe_layer_grouped_with_shared_and_router(dev, orc, gs, prec):
     import torch
     from weight_streaming_gemv_qgemv_amd import binding as b
     E, D, F, S, K = 24, 512, 256, 41, 6
@@ -118,16 +141,17 @@ def test_moe_layer_grouped_with_shared_and_router(dev, orc, gs):
     rp = dict(w=to_dev(Wr, dev), bias=to_dev(bias, dev), K=K, norm_topk=1, routed_scale=2.5)
     idx_o = torch.empty((S, K), dtype=torch.int32, device=dev)
     w_o = torch.empty((S, K), dtype=torch.float32, device=dev)
-    announce("moe layer grouped", gs)
-    out, _ = b.moe_layer(rp, td, tsd, to_dev(x, dev), idx_out=idx_o, w_out=w_o)
+    announce("moe layer grouped", gs, prec)
+    out, _ = b.moe_layer(rp, td, tsd, to_dev(x, dev), idx_out=idx_o, w_out=w_o, prec=prec)
     torch.cuda.synchronize()
     r = orc.router(Wr, bias, x, K, 1, 2.5)
     np.testing.assert_array_equal(idx_o.cpu().numpy(), r["idx"])
     ref = orc.moe(bank, shared, x, r["idx"], r["w"])
-    assert_within(out.cpu().numpy(), ref["out"], ref["mag"], 1e-4, what=f"grouped layer gs{gs}")
-    # grouped experts run at fp32 precision only
+    assert_within(out.cpu().numpy(), ref["out"], ref["mag"], 2e-2 if prec else 1e-4,
+                  what=f"grouped layer gs{gs} prec{prec}")
+    # no integer dots on grouped experts
     with pytest.raises(b.ColiError):
-        b.moe_layer(rp, td, tsd, to_dev(x, dev), prec=b.PREC_BF16)
+        b.moe_layer(rp, td, tsd, to_dev(x, dev), prec=b.PREC_IDOT)
 
 
 def _glm_grouped(glm_bank, gs, seed):
@@ -187,4 +211,26 @@ def test_prefill_2048_grouped(dev, orc, glm_bank):
     toks = np.sort(g.choice(S, 8, replace=False))
     ref = orc.moe(bank, shared, x[toks], idx[toks], w[toks].astype(np.float64))
     assert_within(out.cpu().numpy()[toks], ref["out"], ref["mag"], 1e-4, what="prefill 2048 grouped")
+    del td, tsd
+
+
+@pytest.mark.parametrize("gs", [32, 128])
+def test_prefill_2048_grouped_bf16(dev, orc, glm_bank, gs):
+    """The 2048-token Zipf layer with grouped scales on the bf16 prefill
+    kernels: within the prefill bar of the oracle on 8 sampled tokens."""
+    import torch
+    from weight_streaming_gemv_qgemv_amd import binding as b
+    bank, shared = _glm_grouped(glm_bank, gs, 6800)
+    S, K, E, D = 2048, 8, 256, 6144
+    g = synth.rng(6801, gs)
+    x = synth.activations(g, S, D)
+    idx, w = synth.routing_zipf(g, S, K, E)
+    td, tsd = b.tile_mlps(_dev(bank, dev)), b.tile_mlps(_dev(shared, dev), D)
+    announce("prefill 2048 grouped bf16", gs)
+    out, _ = b.moe_layer(None, td, tsd, to_dev(x, dev), pre_idx=to_dev(idx, dev), pre_w=to_dev(w, dev),
+                         prec=b.PREC_BF16)
+    torch.cuda.synchronize()
+    toks = np.sort(g.choice(S, 8, replace=False))
+    ref = orc.moe(bank, shared, x[toks], idx[toks], w[toks].astype(np.float64))
+    assert_within(out.cpu().numpy()[toks], ref["out"], ref["mag"], 2e-2, what=f"prefill 2048 grouped bf16 gs{gs}")
     del td, tsd

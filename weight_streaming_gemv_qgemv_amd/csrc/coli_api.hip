@@ -617,7 +617,7 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
     // grouped-scale int4 (fp32 precision, grouped tiled layout): group
     // scales packed [row tile][group][16 rows], kpad / gs groups per row
     const int gs = ex->gs;
-    if (gs && (prec != COLI_PREC_FP32 || ex->layout != COLI_LAYOUT_TILED_GROUPED || !mm)) return COLI_EINVAL;
+    if (gs && (prec == COLI_PREC_IDOT || ex->layout != COLI_LAYOUT_TILED_GROUPED || !mm)) return COLI_EINVAL;
     const int64_t gstrD = tiled ? coli_tiled_bytes(ex->fmt, 1, F, D) : (int64_t)F * rbD;   // gate, up
     const int64_t gstrF = tiled ? coli_tiled_bytes(ex->fmt, 1, D, F) : (int64_t)D * rbF;   // down
     // matrix-core passes: 16 rows as bf16 hi/lo column pairs (fp32-level
@@ -864,7 +864,7 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
         // output as one per grouped row; per-row activation sums
         const int64_t rows = (int64_t)P + (sh ? S : 0);   // grouped rows (the workspace has no shared rows without one)
         const int kpD = (int)coli__kpad(D), kpF = (int)coli__kpad(F);
-        const int nparts = kpF / 32;
+        const int nparts = pre_parts(kpF, gs != 0);   // h's partial sums per grouped row
         uint16_t *xt = reinterpret_cast<uint16_t *>(ws + L.xf);
         float *tok_sum = reinterpret_cast<float *>(ws + L.xsum);
         int32_t *act_row = reinterpret_cast<int32_t *>(ws + L.xsum + (int64_t)S * 4);
@@ -889,7 +889,9 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
             a.s[1] = ex->s_up;
             a.w_gstride = gstrD;
             a.tiled = tiled;
-            a.s_gstride = F;
+            a.s_gstride = gs ? (int64_t)((F + 15) / 16) * (kpD / gs) * 16 : F;
+            a.gs_spg = gs / 32;
+            a.gs_ngp = gs ? kpD / gs : 0;
             a.ngroups = E;
             a.O = F;
             if (sh_mm) {
@@ -925,7 +927,9 @@ int run_experts(const coli_experts *ex, const coli_mlp *sh, const float *x, int 
             d.s[0] = ex->s_down;
             d.w_gstride = gstrF;
             d.tiled = tiled;
-            d.s_gstride = D;
+            d.s_gstride = gs ? (int64_t)((D + 15) / 16) * (kpF / gs) * 16 : D;
+            d.gs_spg = gs / 32;
+            d.gs_ngp = gs ? kpF / gs : 0;
             d.ngroups = E;
             d.O = D;
             if (sh_mm) {

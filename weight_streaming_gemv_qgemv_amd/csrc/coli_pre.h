@@ -13,7 +13,9 @@ constexpr int kPreTpp = 64;
 // (M = 1: 8 waves x 64) product: the single product, with half the
 // accumulators, gives each wave more rows, so that each staged activation
 // unit meets as many weight rows.
-constexpr int pre_rows_per_item(int M) { return M == 2 ? 256 : 512; }
+// Grouped-scale int4 (gs > 0) keeps a running total per output beside the
+// group's sums, so a wave takes half the rows: 128 and 256.
+constexpr int pre_rows_per_item(int M, bool gs = false) { return (M == 2 ? 256 : 512) >> (gs ? 1 : 0); }
 
 // bf16 row tables: one row per activation row, kpad elements rounded once to
 // bf16 in fragment order (16-byte units of 8 elements), 2 * kpad bytes a row.
@@ -50,6 +52,11 @@ struct PreArgs {
     int nparts;
     int tiled;               // weights in the tiled layout (coli_pack_tiled); w_gstride
                              // is then the tiled bytes of one matrix
+    // grouped-scale int4 (0: one scale per row): 32-element MFMA steps per
+    // group (gs / 32) and groups per row (kpad / gs); weights in the grouped
+    // tiled layout, scales [row tile][group][16 rows] (coli_pack_scales_grouped,
+    // s_gstride floats per matrix)
+    int gs_spg, gs_ngp;
     int tiles;               // set by pre_launch
 };
 
@@ -65,7 +72,7 @@ hipError_t pre_rows_launch(const int32_t *row_pair, int P, int K, int S, int ext
 // row_sum[r] = sum_p hpart[r * nparts + p] in p order.
 hipError_t pre_sum_launch(const float *hpart, int nparts, int rows, float *row_sum, hipStream_t st);
 hipError_t pre_launch(PreArgs a, int fmt, int M, int64_t max_group_passes, hipStream_t st);
-int pre_parts(int hf_kpad);
+int pre_parts(int hf_kpad, bool gs = false);
 
 }  // namespace coli
 

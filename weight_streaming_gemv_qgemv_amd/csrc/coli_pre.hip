@@ -131,13 +131,31 @@ __device__ __forceinline__ void dma16(const void *g, uint32_t lds)
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
 }
 
-template <int FMT, int M, bool TILED>
+// SPG > 0: grouped-scale int4 (one scale per 32 SPG elements; SPG = 8
+// stands for every group of 256 or more, a.gs_spg steps) on the grouped
+// tiled layout, whose segments hold MFMA step s' of lane q as elements
+// 32 s' + 8 q .. + 7, so each step covers 32 consecutive elements: the pass
+// rows' units are staged from the row tables in that order, a group's
+// products start from zero (groups of one or two steps: from -OFF times
+// their column sums, made by the matrix cores) and at its last step are
+// scaled by the group's scales (staged per k-block beside the activations)
+// into a running total per output.
+template <int FMT, int M, bool TILED, int SPG = 0>
 __global__ __launch_bounds__(64 * kPreWaves) void k_pre(PreArgs a)
 {
     using T = MF<FMT>;
     constexpr int STEPS = T::STEPS, KB = T::KB, SEGS = T::SEGS, BITS = T::BITS, SPS = T::SPS;
-    constexpr int MT = M == 2 ? kPreMT : kPreMTDown, NT = kPreNT, RPW = 16 * MT, RPB = kPreWaves * RPW;
-    static_assert(RPB == pre_rows_per_item(M), "rows per item");
+    constexpr bool GS = SPG > 0;
+    static_assert(!GS || (TILED && FMT == kI4), "grouped scales: tiled int4");
+    constexpr int MT = (M == 2 ? kPreMT : kPreMTDown) / (GS ? 2 : 1), NT = kPreNT, RPW = 16 * MT,
+                  RPB = kPreWaves * RPW;
+    static_assert(RPB == pre_rows_per_item(M, GS), "rows per item");
+    // grouped scales: per wave and k-block its M x MT row tiles' scales of
+    // the k-block's NGK groups, 16 rows each (64 bytes): one DMA per wave
+    constexpr int NGK = GS ? (SPG < 8 ? 8 / SPG : 1) : 1;
+    constexpr int SREG = M * MT * NGK * 64;
+    static_assert(!GS || SREG <= 1024, "a wave's k-block scales in one DMA");
+    __shared__ float4 ssA[GS ? kPreWaves * 64 : 1], ssB[GS ? kPreWaves * 64 : 1];
     constexpr float OFF = T::OFF;
     constexpr int CH = STEPS * 4;               // 16-byte chunks of a row per k-block
     constexpr int UNITS = CH * kPreTpp;         // units of one staged k-block
@@ -290,7 +308,11 @@ __global__ __launch_bounds__(64 * kPreWaves) void k_pre(PreArgs a)
         for (int j = 0; j < IPW; ++j) {
             const int i = min(wave + kPreWaves * j, NI - 1);
             const int n = i / STEPS, s = i % STEPS;
-            rb[j] = (uint32_t)lrow[par][16 * n + (lane >> 2)] * arow + (uint32_t)(s * 64 + dq * 16);
+            // the unit of (step s, chunk dq): fragment-order unit 4 s + dq of
+            // the k-block; on the grouped layout unit 4 dq + s' of segment s / 4
+            const uint32_t u = GS ? (uint32_t)((s >> 2) * 256 + dq * 64 + (s & 3) * 16)
+                                  : (uint32_t)(s * 64 + dq * 16);
+            rb[j] = (uint32_t)lrow[par][16 * n + (lane >> 2)] * arow + u;
         }
     };
     auto stageB_r = [&](const uint32_t (&rb)[IPW], int kbi, const uint4 *buf) {
@@ -309,25 +331,139 @@ __global__ __launch_bounds__(64 * kPreWaves) void k_pre(PreArgs a)
         stageB_r(rb, kbi, buf);
     };
 
+    // Grouped scales of k-block kbi of item c into this wave's 1 KB of sbuf:
+    // the scale tensors are packed [row tile][group][16 rows], so a row
+    // tile's NGK groups of one k-block are 64 NGK contiguous bytes; byte b of
+    // the region is row tile b / (64 NGK) (m major), its byte b % (64 NGK);
+    // lanes past the region read its last 16 bytes again.
+    const int ngp = GS ? a.gs_ngp : 0;
+    auto stageS = [&](const It &c, int kbi, const float4 *sbuf) {
+        if constexpr (GS) {
+            const int g0 = kbi * 8 / a.gs_spg;
+            const uint32_t lbase = (uint32_t)(uintptr_t)(const lds_void *)(sbuf + wave * 64);
+            const int mt16 = (c.Og + 15) / 16;
+            const int obt = (c.tile * RPB + wave * RPW) / 16;
+            const int b = min(16 * lane, SREG - 16);
+            const int ti = b / (64 * NGK), within = b - ti * (64 * NGK);
+            const int m = ti / MT, mt = ti - m * MT;
+            const int rt = min(obt + mt, mt16 - 1);
+            // m varies across lanes: a select, not an index
+            const float *sb = c.sc[0];
+#pragma unroll
+            for (int mm = 1; mm < M; ++mm) sb = m == mm ? c.sc[mm] : sb;
+            dma16(sb + ((int64_t)rt * ngp + g0) * 16 + within / 4, __builtin_amdgcn_readfirstlane(lbase));
+        }
+    };
+
     floatx4 acc[M][MT][NL];
+    // grouped scales: the group's column sums (times -OFF for groups of one
+    // or two steps) and the scaled total of the finished groups
+    floatx4 accs[GS ? NL : 1], tot[GS ? M : 1][GS ? MT : 1][GS ? NL : 1];
+    const floatx4 zero4 = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int m = 0; m < M; ++m)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int n = 0; n < NL; ++n) acc[m][mt][n] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int n = 0; n < NL; ++n) acc[m][mt][n] = zero4;
+    if constexpr (GS) {
+#pragma unroll
+        for (int n = 0; n < NL; ++n) {
+            accs[n] = zero4;
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) tot[m][mt][n] = zero4;
+        }
+    }
+    constexpr bool CI = GS && SPG <= 2;
+    constexpr uint32_t noff_bf = __builtin_bit_cast(uint32_t, -OFF) >> 16;
+    static_assert(!CI || (__builtin_bit_cast(uint32_t, -OFF) & 0xFFFFu) == 0, "-OFF is a bf16 value");
+    const uint32_t noff2 = opaque_v(CI ? noff_bf | noff_bf << 16 : 0x3F803F80u);   // bf16 -OFF pairs, else ones
+    const uint4 cs_op = make_uint4(noff2, noff2, noff2, noff2);
+    // after the last step of group gl of the k-block whose scales are in
+    // sbuf: its products (less OFF times its column sums) times its scales
+    // into tot
+    auto flush = [&](const float4 *sbuf, int gl) {
+        if constexpr (GS) {
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const float4 sv = sbuf[wave * 64 + ((m * MT + mt) * NGK + gl) * 4 + q];
+#pragma unroll
+                    for (int n = 0; n < NL; ++n) {
+                        floatx4 v = acc[m][mt][n];
+                        if constexpr (!CI) {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) v[r] = fmaf(-OFF, accs[n][r], v[r]);
+                        }
+                        tot[m][mt][n][0] = fmaf(sv.x, v[0], tot[m][mt][n][0]);
+                        tot[m][mt][n][1] = fmaf(sv.y, v[1], tot[m][mt][n][1]);
+                        tot[m][mt][n][2] = fmaf(sv.z, v[2], tot[m][mt][n][2]);
+                        tot[m][mt][n][3] = fmaf(sv.w, v[3], tot[m][mt][n][3]);
+                    }
+                }
+        }
+    };
 
     // one k-block: per MFMA step the live N-tiles' activation units from LDS
     // and the M x MT x NL products; the weights were loaded in the operand
     // layout (lane (q, col) holds row col, chunk q of each 64-byte segment)
-    // (sg >= 0: only the steps of segment sg)
-    auto compute = [&](const uint4 (&w)[M][MT][SEGS], const uint4 *buf, int sg = -1) {
+    // (sg >= 0: only the steps of segment sg; grouped scales: sbuf holds the
+    // scales of this k-block, ckb)
+    auto compute = [&](const uint4 (&w)[M][MT][SEGS], const uint4 *buf, int sg = -1,
+                       const float4 *sbuf = nullptr, int ckb = 0) {
 #pragma unroll
         for (int s2 = 0; s2 < STEPS; ++s2) {
             if (sg >= 0 && s2 / SPS != sg) continue;
             uint4 b[NL];
 #pragma unroll
             for (int n = 0; n < NL; ++n) b[n] = buf[((n * STEPS + s2) * 16 + col) * 4 + (q ^ ((col >> 1) & 3))];
+            if constexpr (GS) {
+                // a group of fewer than 8 steps starts at steps s2 % SPG == 0;
+                // one of a k-block or more (SPG = 8) finds its sums zeroed by
+                // the last group's flush
+                const bool fresh = SPG < 8 && s2 % (SPG < 8 ? SPG : 1) == 0;
+                if constexpr (CI) {
+                    if (fresh) {   // the group's steps: this one and (SPG = 2) the next
+#pragma unroll
+                        for (int n = 0; n < NL; ++n) {
+                            accs[n] = mfma(cs_op, b[n], zero4);
+                            if constexpr (SPG == 2)
+                                accs[n] = mfma(cs_op, buf[((n * STEPS + s2 + 1) * 16 + col) * 4 + (q ^ ((col >> 1) & 3))],
+                                               accs[n]);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) {
+                        const uint4 cw = codes<FMT>(w[m][mt][s2 / SPS], s2 % SPS);
+#pragma unroll
+                        for (int n = 0; n < NL; ++n)
+                            acc[m][mt][n] = mfma(cw, b[n], fresh ? (CI ? accs[n] : zero4) : acc[m][mt][n]);
+                    }
+                if constexpr (!CI) {
+#pragma unroll
+                    for (int n = 0; n < NL; ++n) accs[n] = mfma(cs_op, b[n], fresh ? zero4 : accs[n]);
+                }
+                if constexpr (SPG < 8) {
+                    if ((s2 + 1) % SPG == 0) flush(sbuf, s2 / SPG);
+                } else if (s2 == STEPS - 1 && (ckb == nkb - 1 || ((ckb + 1) * 8) % a.gs_spg == 0)) {
+                    flush(sbuf, 0);   // uniform
+#pragma unroll
+                    for (int n = 0; n < NL; ++n) {
+#pragma unroll
+                        for (int m = 0; m < M; ++m)
+#pragma unroll
+                            for (int mt = 0; mt < MT; ++mt) acc[m][mt][n] = zero4;
+                        accs[n] = zero4;
+                    }
+                }
+                continue;
+            }
 #pragma unroll
             for (int m = 0; m < M; ++m)
 #pragma unroll
@@ -341,6 +477,7 @@ __global__ __launch_bounds__(64 * kPreWaves) void k_pre(PreArgs a)
 
     float sreg[M][MT][4];
     auto load_epi = [&](const It &c) {
+        if constexpr (GS) return;   // grouped scales were applied group by group
         const int obase = c.tile * RPB + wave * RPW;
 #pragma unroll
         for (int m = 0; m < M; ++m)
@@ -379,11 +516,15 @@ __global__ __launch_bounds__(64 * kPreWaves) void k_pre(PreArgs a)
                 float res[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    float y = sreg[0][mt][r] * (acc[0][mt][n][r] - OFF * xsv[n]);
-                    if constexpr (M == 2) {
-                        const float u = sreg[1][mt][r] * (acc[1][mt][n][r] - OFF * xsv[n]);
-                        y = silu_f(y) * u;
+                    float y, u = 0.f;
+                    if constexpr (GS) {
+                        y = tot[0][mt][n][r];
+                        if constexpr (M == 2) u = tot[GS ? 1 : 0][mt][n][r];
+                    } else {
+                        y = sreg[0][mt][r] * (acc[0][mt][n][r] - OFF * xsv[n]);
+                        if constexpr (M == 2) u = sreg[1][mt][r] * (acc[1][mt][n][r] - OFF * xsv[n]);
                     }
+                    if constexpr (M == 2) y = silu_f(y) * u;
                     res[r] = ob + r < c.Og ? y : 0.f;
                 }
                 if (live && has_out) {
@@ -452,7 +593,10 @@ __global__ __launch_bounds__(64 * kPreWaves) void k_pre(PreArgs a)
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int n = 0; n < NL; ++n) acc[m][mt][n] = floatx4{0.f, 0.f, 0.f, 0.f};
+                for (int n = 0; n < NL; ++n) {
+                    acc[m][mt][n] = zero4;
+                    if constexpr (GS) tot[m][mt][n] = zero4;
+                }
         return fast ? (has_out ? kStores : kStoresT) : 0;
     };
 
@@ -500,6 +644,7 @@ __global__ __launch_bounds__(64 * kPreWaves) void k_pre(PreArgs a)
     uint4 wA[M][MT][SEGS], wB[M][MT][SEGS];
     loadW(cur, 0, wA);
     stageB(0, 0, bsA);
+    stageS(cur, 0, ssA);
     int jn = lb + bpx;
 
     if constexpr (TILED) {
@@ -541,16 +686,20 @@ __global__ __launch_bounds__(64 * kPreWaves) void k_pre(PreArgs a)
         // the current item's staging offsets, taken once per item (the
         // next item's first k-block is staged from its list directly)
         uint32_t rbc[IPW];
+        // (grouped scales: k-block skb's scales, of item si, are staged with
+        // its activations, into the scale buffer of the same parity)
         auto kstep = [&](uint4 (&w)[M][MT][SEGS], const uint4 *buf, int spar, int skb, const uint4 *nbuf,
-                         const It &lc, int lkb, bool epi = false, int after = 0) {
+                         const It &lc, int lkb, const It &si, bool epi = false, int after = 0) {
             sync_x(after);
             if (spar == par) stageB_r(rbc, skb, nbuf);
             else stageB(spar, skb, nbuf);
+            const bool even = buf == bsA;
+            stageS(si, skb, even ? ssB : ssA);
             if (epi) load_epi(cur);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int sg = 0; sg < SEGS; ++sg) {
-                compute(w, buf, sg);
+                compute(w, buf, sg, even ? ssA : ssB, skb > 0 ? skb - 1 : nkb - 1);
                 __builtin_amdgcn_sched_barrier(0);
                 loadSeg(lc, lkb, sg, w);
             }
@@ -565,17 +714,17 @@ __global__ __launch_bounds__(64 * kPreWaves) void k_pre(PreArgs a)
             float rs;
             loadList(nxt, ar, rs);
             stage_base(par, rbc);
-            kstep(wA, bsA, par, 1, bsB, cur, 2, false, nlist + stores);
+            kstep(wA, bsA, par, 1, bsB, cur, 2, cur, false, nlist + stores);
             storeList(par ^ 1, ar, rs);
-            kstep(wB, bsB, par, 2, bsA, cur, 3);
+            kstep(wB, bsB, par, 2, bsA, cur, 3, cur);
             for (int k = 2; k < nkb - 2; k += 2) {
-                kstep(wA, bsA, par, k + 1, bsB, cur, k + 2);
-                kstep(wB, bsB, par, k + 2, bsA, cur, k + 3);
+                kstep(wA, bsA, par, k + 1, bsB, cur, k + 2, cur);
+                kstep(wB, bsB, par, k + 2, bsA, cur, k + 3, cur);
             }
-            kstep(wA, bsA, par, nkb - 1, bsB, has_nxt ? nxt : cur, has_nxt ? 0 : nkb - 1, true);
+            kstep(wA, bsA, par, nkb - 1, bsB, has_nxt ? nxt : cur, has_nxt ? 0 : nkb - 1, cur, true);
 #pragma unroll
             for (int n = 0; n < NL; ++n) xsv[n] = lsum[par][min(16 * n + col, cur.nt - 1)];
-            kstep(wB, bsB, par ^ 1, 0, bsA, has_nxt ? nxt : cur, has_nxt ? 1 : nkb - 1);
+            kstep(wB, bsB, par ^ 1, 0, bsA, has_nxt ? nxt : cur, has_nxt ? 1 : nkb - 1, nxt);
             stores = epilogue(cur);
             if (!has_nxt) break;
             cur = nxt;
@@ -642,11 +791,11 @@ int pre_resident_blocks(const void *kern, int *cache)
     return cache[dev];
 }
 
-template <int FMT, int M, bool TILED>
+template <int FMT, int M, bool TILED, int SPG = 0>
 hipError_t launch_pre(const PreArgs &a, int64_t items, hipStream_t st)
 {
     static int cache[64] = {0};
-    const void *kern = (const void *)k_pre<FMT, M, TILED>;
+    const void *kern = (const void *)k_pre<FMT, M, TILED, SPG>;
     int64_t cap = pre_resident_blocks(kern, cache) / kPreXcds * kPreXcds;
     if (cap < kPreXcds) cap = kPreXcds;
     int64_t grid = (items + kPreXcds - 1) / kPreXcds * kPreXcds;
@@ -654,16 +803,19 @@ hipError_t launch_pre(const PreArgs &a, int64_t items, hipStream_t st)
     if (grid < kPreXcds) grid = kPreXcds;
     const KernelEvents ev = take_kernel_events();   // timed stage: events at the kernel's bounds
     if (ev.start)
-        hipExtLaunchKernelGGL((k_pre<FMT, M, TILED>), dim3((unsigned)grid), dim3(64 * kPreWaves), 0, st,
+        hipExtLaunchKernelGGL((k_pre<FMT, M, TILED, SPG>), dim3((unsigned)grid), dim3(64 * kPreWaves), 0, st,
                               ev.start, ev.stop, 0, a);
     else
-        hipLaunchKernelGGL((k_pre<FMT, M, TILED>), dim3((unsigned)grid), dim3(64 * kPreWaves), 0, st, a);
+        hipLaunchKernelGGL((k_pre<FMT, M, TILED, SPG>), dim3((unsigned)grid), dim3(64 * kPreWaves), 0, st, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-int pre_parts(int hf_kpad) { return (hf_kpad + pre_rows_per_item(2) - 1) / pre_rows_per_item(2) * kPreWaves; }
+int pre_parts(int hf_kpad, bool gs)
+{
+    return (hf_kpad + pre_rows_per_item(2, gs) - 1) / pre_rows_per_item(2, gs) * kPreWaves;
+}
 
 hipError_t xrows_bf16_launch(int fmt, const float *x, int64_t ldx, int rows, int I, int kpad,
                              uint16_t *table, float *sums, hipStream_t st)
@@ -702,9 +854,24 @@ hipError_t pre_launch(PreArgs a, int fmt, int M, int64_t max_group_passes, hipSt
     int Ocover = a.O;
     if (M == 2 && a.hf && a.hf_kpad > Ocover) Ocover = a.hf_kpad;
     if (a.has_extra && a.xO > Ocover) Ocover = a.xO;
-    a.tiles = (Ocover + pre_rows_per_item(M) - 1) / pre_rows_per_item(M);
+    const bool gs = a.gs_spg > 0;
+    const int rpi = pre_rows_per_item(M, gs);
+    a.tiles = (Ocover + rpi - 1) / rpi;
     if (M == 2 && a.nparts < a.tiles * kPreWaves) return hipErrorInvalidValue;
     const int64_t items = max_group_passes * a.tiles;
+    if (gs) {   // grouped-scale int4, grouped tiled layout
+        if (fmt != kI4 || !a.tiled) return hipErrorInvalidValue;
+        const int spg = a.gs_spg;
+#define COLI_PRE_GS(MM)                                                          \
+        if (spg == 1) return launch_pre<kI4, MM, true, 1>(a, items, st);         \
+        if (spg == 2) return launch_pre<kI4, MM, true, 2>(a, items, st);         \
+        if (spg == 4) return launch_pre<kI4, MM, true, 4>(a, items, st);         \
+        if (spg % 8 == 0) return launch_pre<kI4, MM, true, 8>(a, items, st);     \
+        return hipErrorInvalidValue;
+        if (M == 2) { COLI_PRE_GS(2) }
+        COLI_PRE_GS(1)
+#undef COLI_PRE_GS
+    }
 #define COLI_PRE_CASES(MM, TT)                                      \
     switch (fmt) {                                                 \
     case kI8: return launch_pre<kI8, MM, TT>(a, items, st);        \

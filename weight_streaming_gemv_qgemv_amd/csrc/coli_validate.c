@@ -187,14 +187,15 @@ int coli_moe_workspace_layout(int S, int K, int E, int D, int F, int F_shared,
         /* bf16 precision: bf16 row tables of x (per token) and of the SwiGLU
          * output (per grouped row); xsum: per-token sums of the stored x,
          * then per grouped row its table row (int32) and activation sum;
-         * hsum: per grouped row KpF/32 partial sums of the stored h, then
-         * their totals */
+         * hsum: per grouped row KpF/16 partial sums of the stored h (KpF/32
+         * with one scale per row, KpF/16 with grouped scales, whose items
+         * have half the rows), then their totals */
         if (!mul_ok((int64_t)S, 2 * KpD, &t)) return COLI_ESHAPE;
         REGION(xf, t);
         REGION(xsum, ((int64_t)S + 2 * rows) * 4);
         if (!mul_ok(rows, 2 * KpF, &t)) return COLI_ESHAPE;
         REGION(hf, t);
-        if (!mul_ok(rows, KpF / 32 + 1, &t) || !mul_ok(t, 4, &t)) return COLI_ESHAPE;
+        if (!mul_ok(rows, KpF / 16 + 1, &t) || !mul_ok(t, 4, &t)) return COLI_ESHAPE;
         REGION(hsum, t);
     } else {
         /* fp32 precision: one row table per token (x) and per grouped row
@@ -348,7 +349,7 @@ int coli__check_moe(const coli_experts *ex, const coli_mlp *sh, const float *x,
             (ex->layout != sh->layout || sh->fmt != ex->fmt || sh->F != ex->F || sh->gs != ex->gs))
             return COLI_EINVAL;
     }
-    if (ex->gs != 0 && prec != COLI_PREC_FP32) return COLI_EFMT;   /* grouped scales: fp32 kernels only */
+    if (ex->gs != 0 && prec == COLI_PREC_IDOT) return COLI_EFMT;   /* no integer dots with grouped scales */
     if (prec == COLI_PREC_IDOT) {
         /* the integer-dot kernels: int8 / int4, tiled, rows of whole 16-byte
          * segments, widths within the quantiser's 16384 */
