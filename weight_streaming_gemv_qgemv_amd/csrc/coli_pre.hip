@@ -450,7 +450,11 @@ __global__ __launch_bounds__(64 * kPreWaves) void k_pre(PreArgs a)
                     for (int n = 0; n < NL; ++n) accs[n] = mfma(cs_op, b[n], fresh ? zero4 : accs[n]);
                 }
                 if constexpr (SPG < 8) {
-                    if ((s2 + 1) % SPG == 0) flush(sbuf, s2 / SPG);
+                    // a uniform branch the compiler cannot fold (a.gs_spg is
+                    // SPG here) keeps each flush a scheduling region of its
+                    // own; without it the scheduler runs later steps' work
+                    // ahead of the flushes and spills (gs 32: 2.2 KB per lane)
+                    if ((s2 + 1) % SPG == 0 && a.gs_spg == SPG) flush(sbuf, s2 / SPG);
                 } else if (s2 == STEPS - 1 && (ckb == nkb - 1 || ((ckb + 1) * 8) % a.gs_spg == 0)) {
                     flush(sbuf, 0);   // uniform
 #pragma unroll
