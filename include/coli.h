@@ -325,9 +325,12 @@ size_t coli_moe_workspace_bytes(int S, int K, int E, int D, int F,
  *   pair_row   [S*K] int32: inverse map (-1 for a skipped slot).
  *   counts     [E] int32: rows per expert.
  *   h          [S*K + S, Fmax] fp32: SwiGLU output per grouped row; the
- *              shared expert's row for token s is S*K + s.
+ *              shared expert's row for token s is S*K + s (COLI_PREC_BF16
+ *              keeps the SwiGLU output only as the bf16 row table hf).
  *   y          [S*K + S, D] fp32: expert output per grouped row (same
- *              numbering), before the routing weight.
+ *              numbering), before the routing weight; COLI_PREC_BF16: rounded
+ *              to bf16 (uint16 elements, row stride D), unless a shared
+ *              expert of another format or width runs on the vector ALUs.
  *   router_part  fp64 partial router logits (scratch).
  *   xf, xsum, hf, hsum, work, n_work   matrix-core scratch and the
  *              device-built list of passes.  xf holds one row per token and
@@ -337,8 +340,8 @@ size_t coli_moe_workspace_bytes(int S, int K, int E, int D, int F,
  *              hi/lo pairs, xsum and hsum empty; COLI_PREC_BF16: bf16 values,
  *              xsum = [S] per-token sums of the stored x, then per grouped
  *              row its xf row (int32) and activation sum; hsum = per grouped
- *              row KpF/32 partial sums of the stored h (KpF = F rounded up to
- *              1024), then their totals; COLI_PREC_IDOT: int8 values (KpD,
+ *              row KpF/32 (grouped-scale experts: KpF/16) partial sums of the
+ *              stored h (KpF = F rounded up to 1024), then their totals; COLI_PREC_IDOT: int8 values (KpD,
  *              resp. KpF, bytes a row), xsum = per token its scale and four
  *              partial sums of its int8 values, then per grouped row its xf
  *              row, scale and sum; hsum = per grouped row the scale and four
