@@ -141,12 +141,10 @@ def recorded_trace_ms(workload, kernel_key):
 
 
 def kernel_key(name, args):
-    """rocprofv3's name of the int4 gate/up kernel for the layout in use (and
-    for k_dec its group-scale variant: 0, or 32-element steps per group, 8
-    for every group of 256 or more)."""
+    """rocprofv3's name of the int4 gate/up kernel (k_dec, k_pre) for the
+    layout in use and its group-scale variant: 0, or the 32-element steps per
+    group, 8 for every group of 256 or more."""
     tiled = 'true' if getattr(args, 'layout', 'rows') == 'tiled' else 'false'
-    if name != "k_dec":
-        return f"{name}<2, 2, {tiled}>"
     gs = getattr(args, "grouped", 0)
     return f"{name}<2, 2, {tiled}, {min(gs // 32, 8) if gs else 0}>"
 

@@ -222,6 +222,13 @@ def test_workspace_layout_is_consistent(L):
         rows = S * K + (S if Fs else 0)
         assert lay["y"] + rows * D * 4 <= lay["total"]
         assert lay["h"] + rows * max(F, Fs) * 4 <= lay["y"]
+        # bf16 precision: h's partial sums per grouped row, as many parts as
+        # the grouped-scale prefill items need (KpF / 16), then the totals
+        lb = b.moe_workspace_layout(S, K, E, D, F, Fs, b.PREC_BF16)
+        kpf = -(-max(F, Fs) // 1024) * 1024
+        ends = sorted(v for k, v in lb.items() if not k.endswith(("_ld", "_stride", "_max")) and v >= 0)
+        nxt = min([v for v in ends if v > lb["hsum"]] + [lb["total"]])
+        assert nxt - lb["hsum"] >= rows * (kpf // 16 + 1) * 4
 
 
 def test_idot_precision_host_checks(L):
