@@ -50,12 +50,14 @@ def test_tiles_per_block_ragged(dev, orc, fmt, O):
     """Row counts whose one-shot launch takes 2 (4100 rows) or 3 (8200, 12290
     rows) tiles of 16 rows per block, with a last group only partly inside
     the matrix (and a last tile of 4 / 8 / 2 rows); exact-integer inputs, so
-    the result is the oracle's bit for bit.  S = 1 and 2 (one pass)."""
+    the result is the oracle's bit for bit.  S = 1 and 2 (the one-pass
+    kernel), 3 and 8 (one pass of the rounds kernel) and 9 (two passes, the
+    second of one row)."""
     I = 1024
     g = synth.rng(250, fmt, O)
     W = synth.weight_bytes(g, fmt, O, I)
     sc = synth.exact_scales(g, O)
-    for S in (1, 2):
+    for S in (1, 2, 3, 8, 9):
         announce("qgemv tiles per block", fmt, O, S)
         x = synth.exact_activations(g, S, I)
         ref, _ = orc.qgemv(fmt, W, sc, x)
@@ -64,7 +66,7 @@ def test_tiles_per_block_ragged(dev, orc, fmt, O):
 
 
 @pytest.mark.parametrize("fmt", [0, 1, 2, 3])
-@pytest.mark.parametrize("O,I", [(37, 40), (300, 1000), (257, 4096), (64, 8192 + 64)])
+@pytest.mark.parametrize("O,I", [(37, 40), (300, 1000), (257, 4096), (64, 8192 + 64), (40, 16384 + 40)])
 def test_exact_integer_bitwise(dev, orc, fmt, O, I):
     """Integer x in [-4, 4] and scales 2^-k: the device result must equal the
     oracle bit for bit, whatever its summation order."""
@@ -136,8 +138,8 @@ def test_dense_sweep_12288x6144(dev, orc, fmt):
 @pytest.mark.parametrize("fmt", [1, 2, 3])
 def test_many_rows_ragged(dev, orc, fmt):
     """Over 8192 rows with a ragged last 16-row tile (O = 8209), ragged I,
-    one and two activation rows; every output written, sampled rows (the
-    first and last 40 included) checked against the oracle."""
+    one, two and five activation rows; every output written, sampled rows
+    (the first and last 40 included) checked against the oracle."""
     import torch
     from weight_streaming_gemv_qgemv_amd import binding as b
     g = synth.rng(2500, fmt)
@@ -147,7 +149,7 @@ def test_many_rows_ragged(dev, orc, fmt):
         sc = synth.scales(g, O)
         Wd, scd = to_dev(W, dev), to_dev(sc, dev)
         rows = np.unique(np.concatenate([g.choice(O, 400, replace=False), np.arange(O - 40, O), np.arange(40)]))
-        for S in (1, 2):
+        for S in (1, 2, 5):
             announce("qgemv many rows", fmt, O, I, S)
             x = synth.activations(g, S, I)
             y = torch.full((S, O), float("nan"), dtype=torch.float32, device=dev)

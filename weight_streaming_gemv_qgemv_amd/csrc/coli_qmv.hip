@@ -11,7 +11,10 @@
 // activation rows; wave w multiplies the rows' k-blocks w, w + 8, ... (a
 // K-slice) in rounds of 8 k-blocks, so one block's loads cover its rows'
 // whole width and there are enough blocks for the chip even for a few
-// thousand rows.  In both, the
+// thousand rows.  In both, each lane loads its matrix-core operand straight
+// from the row-major rows (lane 16 q + c: row c, bytes 16 q .. 16 q + 15 of
+// each 64-byte segment; measured faster than coalesced row loads transposed
+// with ds_bpermute, except for int8 rows in k_qmv), and the
 // activations are split into bf16 hi/lo in the kernel (column 2t: hi of row
 // t, column 2t+1: lo) straight from the fp32 input, so the call needs no
 // scratch memory.  sum(x), needed to remove OFF * sum(x) from the code
@@ -41,6 +44,18 @@ __device__ __forceinline__ uint32_t hilo_pair(float a, float b, float lo)
     const b2v r = __builtin_convertvector(f2v{fmaf(-lo, ha, a), fmaf(-lo, hb, b)}, b2v);
     return __builtin_bit_cast(uint32_t, r);
 }
+
+// LDS slot of a staged activation unit inside its chunk.  One LDS pass of a
+// 16-byte access serves 8 lanes; the staging lanes of a pass write 8
+// different chunks of one column (in each format's chunk order), the
+// products' lanes read 8 columns of one chunk.  XOR-ing the column with these
+// bits of the chunk index puts every pass's 8 writes into 8 different bank
+// groups for the int8, int4 and int2 chunk orders alike (with the column
+// alone, int4 and int2 writes collided 2- to 8-way); a read pass keeps its
+// one chunk, so its columns stay distinct.  swz16: chunks of 16 column
+// units; swz4: chunks of 4.
+__device__ __forceinline__ int swz16(int c) { return ((c ^ (c >> 2)) & 6) | (c & 9); }
+__device__ __forceinline__ int swz4(int c) { return (((c >> 1) ^ (c >> 3)) & 1) | ((((c >> 2) ^ (c >> 4)) & 1) << 1); }
 
 // Staging loads of one run of RUN activations (elements e0 .. e0 + RUN - 1
 // of row xr): unconditional 16-byte loads, from the run when it lies whole
@@ -85,20 +100,25 @@ __global__ __launch_bounds__(512) void k_qmv(QmvArgs a)
     constexpr float OFF = T::OFF;
     constexpr uint32_t kbytes = KB * BITS / 8;
     constexpr int RUN = FMT == kI2 ? 16 : 8;          // elements per staging run
-    // two round buffers of activation units -- per chunk, 2 nt columns (hi
-    // and lo of each live row) -- reused at the end for the partial tiles
+    // two round buffers of activation units -- per chunk 16 column units (hi
+    // and lo of each row) at column ^ swz16(chunk) -- reused at the end for
+    // the partial tiles
     extern __shared__ uint4 lds[];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int col = lane & 15, q = lane >> 4, lrow = lane >> 2, lchunk = lane & 3;
+    const int col = lane & 15, q = lane >> 4;
+    // int8: coalesced row loads (lane 4 r + k: row r, bytes 16 k ..)
+    // transposed into the operand layout with ds_bpermute -- 2-3% faster
+    // here than the direct operand loads the other formats take
+    constexpr bool XPOSE = FMT == kI8;
+    const int lrow = XPOSE ? lane >> 2 : col, lchunk = XPOSE ? lane & 3 : q;
     const int src4 = 4 * (4 * col + q);
     const int row0 = blockIdx.x * RB;
     const int t0 = blockIdx.y * kQmvTpp;
     const int nt = min(kQmvTpp, a.S - t0);
     const int nkb = a.nkb;
     const int rounds = (nkb + kQmvWaves - 1) / kQmvWaves;
-    const int cs = 2 * nt;                              // columns per chunk in LDS
-    const int units = kQmvWaves * STEPS * 4 * cs;       // units per round buffer
+    constexpr int units = kQmvWaves * STEPS * 4 * 16;   // units per round buffer
 
     // a chunk past the end of a row shorter than 64 bytes is read at the
     // row's last chunk (it meets zero activations)
@@ -176,9 +196,10 @@ __global__ __launch_bounds__(512) void k_qmv(QmvArgs a)
                         hw[m] = hilo_pair(v[k0], v[k1], 0.f);
                         lw[m] = hilo_pair(v[k0], v[k1], 1.f);
                     }
-                    uint4 *dst = buf + (c + 4 * h) * cs + 2 * t;
-                    dst[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-                    dst[1] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+                    const int cc = c + 4 * h;
+                    uint4 *dst = buf + cc * 16;
+                    dst[(2 * t) ^ swz16(cc)] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+                    dst[(2 * t + 1) ^ swz16(cc)] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
                 }
             };
             float v[RUN];
@@ -187,22 +208,24 @@ __global__ __launch_bounds__(512) void k_qmv(QmvArgs a)
         }
     };
     auto compute = [&](uint4 (&w)[MT][SEGS], const uint4 *buf) {
+        if constexpr (XPOSE) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+            for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int sg = 0; sg < SEGS; ++sg) {
-                const uint4 u = w[mt][sg];
-                w[mt][sg] = make_uint4((uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)u.x),
-                                       (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)u.y),
-                                       (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)u.z),
-                                       (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)u.w));
-            }
+                for (int sg = 0; sg < SEGS; ++sg) {
+                    const uint4 u = w[mt][sg];
+                    w[mt][sg] = make_uint4((uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)u.x),
+                                           (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)u.y),
+                                           (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)u.z),
+                                           (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)u.w));
+                }
+        }
         // dead columns read the last live row's units
         const int bcol = (col >> 1) < nt ? col : 2 * (nt - 1) + (col & 1);
-        const uint4 *bw = buf + (wave * STEPS * 4 + q) * cs + bcol;
 #pragma unroll
         for (int s = 0; s < STEPS; ++s) {
-            const uint4 b = bw[s * 4 * cs];
+            const int cq = (wave * STEPS + s) * 4 + q;
+            const uint4 b = buf[cq * 16 + (bcol ^ swz16(cq))];
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma(codes<FMT>(w[mt][s / SPS], s % SPS), b, acc[mt]);
             accs = mfma(ones, b, accs);
@@ -309,8 +332,7 @@ __global__ __launch_bounds__(512) void k_qmv1(QmvArgs a, int passes, int ntiles)
     extern __shared__ uint4 lds[];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int col = lane & 15, q = lane >> 4, lrow = lane >> 2, lchunk = lane & 3;
-    const int src4 = 4 * (4 * col + q);
+    const int col = lane & 15, q = lane >> 4;
     const int xcd = blockIdx.x % 8, jb = blockIdx.x / 8;
     const int tgroup = (jb / passes) * 8 + xcd, pass = jb % passes;
     if (tgroup * MTB >= ntiles) return;                   // whole block, before any barrier
@@ -318,7 +340,6 @@ __global__ __launch_bounds__(512) void k_qmv1(QmvArgs a, int passes, int ntiles)
     const int t0 = pass * kQ1Tpp;
     const int nt = min(kQ1Tpp, a.S - t0);
     const int nkb = a.nkb;
-    const int cs = 2 * nt;                                // columns per chunk in LDS
     // this wave's k-blocks: kw0 .. kw0 + NKW - 1, those below nkb staged and
     // multiplied
     const int kw0 = wave * NKW;
@@ -342,12 +363,12 @@ __global__ __launch_bounds__(512) void k_qmv1(QmvArgs a, int passes, int ntiles)
     }
     // then every weight load of this wave (a clamped copy for k-blocks past
     // the end: the loads stay unconditional, the products are skipped)
-    const uint32_t coff = (uint32_t)min(16 * lchunk, (int)(a.rb - 16));   // short rows: see k_qmv
+    const uint32_t coff = (uint32_t)min(16 * q, (int)(a.rb - 16));   // short rows: see k_qmv
     const uint32_t last_seg = (uint32_t)(a.rb - 16) - coff;
     uint4 w[MTB][NKW][SEGS];
 #pragma unroll
     for (int mt = 0; mt < MTB; ++mt) {
-        const uint32_t roff = (uint32_t)(min(row0 + 16 * mt + lrow, a.O - 1) * a.rb) + coff;
+        const uint32_t roff = (uint32_t)(min(row0 + 16 * mt + col, a.O - 1) * a.rb) + coff;
 #pragma unroll
         for (int i = 0; i < NKW; ++i) {
             const uint32_t b0 = (uint32_t)min(wave * NKW + i, nkb - 1) * kbytes;
@@ -379,9 +400,10 @@ __global__ __launch_bounds__(512) void k_qmv1(QmvArgs a, int passes, int ntiles)
                     hw[m] = hilo_pair(v[k0], v[k1], 0.f);
                     lw[m] = hilo_pair(v[k0], v[k1], 1.f);
                 }
-                uint4 *dst = lds + (c + 4 * h) * cs + 2 * t;
-                dst[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-                dst[1] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+                const int cc = c + 4 * h;
+                uint4 *dst = lds + cc * 4;
+                dst[(2 * t) ^ swz4(cc)] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+                dst[(2 * t + 1) ^ swz4(cc)] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
             }
         };
         float v[RUN];
@@ -410,19 +432,9 @@ __global__ __launch_bounds__(512) void k_qmv1(QmvArgs a, int passes, int ntiles)
         const int kb = wave * NKW + i;
         if (kb >= nkb) break;                         // uniform
 #pragma unroll
-        for (int mt = 0; mt < MTB; ++mt)
-#pragma unroll
-            for (int sg = 0; sg < SEGS; ++sg) {
-                const uint4 u = w[mt][i][sg];
-                w[mt][i][sg] = make_uint4((uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)u.x),
-                                          (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)u.y),
-                                          (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)u.z),
-                                          (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)u.w));
-            }
-        const uint4 *bw = lds + (kb * STEPS * 4 + q) * cs + bcol;
-#pragma unroll
         for (int s2 = 0; s2 < STEPS; ++s2) {
-            const uint4 b = bw[s2 * 4 * cs];
+            const int cq = (kb * STEPS + s2) * 4 + q;
+            const uint4 b = lds[cq * 4 + (bcol ^ swz4(cq))];
 #pragma unroll
             for (int mt = 0; mt < MTB; ++mt) acc[mt] = mfma(codes<FMT>(w[mt][i][s2 / SPS], s2 % SPS), b, acc[mt]);
             accs = mfma(ones, b, accs);
@@ -475,8 +487,7 @@ hipError_t launch_q1(const QmvArgs &a, hipStream_t st)
     const int passes = (a.S + kQ1Tpp - 1) / kQ1Tpp;
     const int64_t grid = (int64_t)(ngroups + 7) / 8 * 8 * passes;
     if (grid <= 0 || grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-    const int ntmax = a.S < kQ1Tpp ? a.S : kQ1Tpp;
-    const size_t stage = (size_t)a.nkb * MF<FMT>::STEPS * 4 * (2 * ntmax) * 16;
+    const size_t stage = (size_t)a.nkb * MF<FMT>::STEPS * 4 * 4 * 16;   // 4 column units per chunk
     const size_t red = (size_t)kQmvWaves * (MTB + 1) * kWave * 16;
     const size_t lds = stage > red ? stage : red;
     auto kern = k_qmv1<FMT, NKW, MTB>;
@@ -535,9 +546,8 @@ hipError_t launch_q(const QmvArgs &a, hipStream_t st)
 {
     const int rb = 16 * MT;
     const dim3 grid((unsigned)((a.O + rb - 1) / rb), (unsigned)((a.S + kQmvTpp - 1) / kQmvTpp));
-    // LDS: two round buffers for the widest pass, or the partial tiles
-    const int ntmax = a.S < kQmvTpp ? a.S : kQmvTpp;
-    const size_t stage = (size_t)2 * kQmvWaves * MF<FMT>::STEPS * 4 * (2 * ntmax) * 16;
+    // LDS: two round buffers, or the partial tiles
+    const size_t stage = (size_t)2 * kQmvWaves * MF<FMT>::STEPS * 4 * 16 * 16;
     const size_t red = (size_t)kQmvWaves * (MT + 1) * kWave * 16;
     const size_t lds = stage > red ? stage : red;
     auto kern = k_qmv<FMT, MT>;
@@ -577,8 +587,7 @@ __global__ __launch_bounds__(512) void k_qmvg(QmvArgs a, int passes, int ntiles)
     extern __shared__ uint4 lds[];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int col = lane & 15, q = lane >> 4, lrow = lane >> 2, lchunk = lane & 3;
-    const int src4 = 4 * (4 * col + q);
+    const int col = lane & 15, q = lane >> 4;
     const int xcd = blockIdx.x % 8, jb = blockIdx.x / 8;
     const int tile = (jb / passes) * 8 + xcd, pass = jb % passes;
     if (tile >= ntiles) return;                           // whole block, before any barrier
@@ -586,13 +595,11 @@ __global__ __launch_bounds__(512) void k_qmvg(QmvArgs a, int passes, int ntiles)
     const int t0 = pass * kQ1Tpp;
     const int nt = min(kQ1Tpp, a.S - t0);
     const int nkb = a.nkb, ng = a.ng, gs = a.gs;
-    const int cs = 2 * nt;
     const int kw0 = wave * NKW;
     const int rw = max(0, min(RW, (nkb - kw0) * (KB / RUN)));
-    // scales of the block's rows after the largest staged activation area
-    // (min(S, kQ1Tpp) rows)
-    const int ntmax = min(a.S, kQ1Tpp);
-    float *sl = reinterpret_cast<float *>(lds + (int64_t)nkb * STEPS * 4 * (2 * ntmax));
+    // scales of the block's rows after the staged activations (4 column
+    // units per chunk, at column ^ swz4(chunk))
+    float *sl = reinterpret_cast<float *>(lds + (int64_t)nkb * STEPS * 4 * 4);
 
     // the block's scales first: rows row0 .. row0 + 15 (those below O) are
     // the contiguous span scale[row0 * ng ..], 16-byte aligned (row0 * ng is a
@@ -627,8 +634,8 @@ __global__ __launch_bounds__(512) void k_qmvg(QmvArgs a, int passes, int ntiles)
         xrun_issue<RUN>(a.x + (int64_t)(t0 + t) * a.I, a.x, e0, a.I, xv[p]);
     }
     // then every weight load of this wave
-    const uint32_t coff = (uint32_t)min(16 * lchunk, (int)(a.rb - 16));   // short rows: see k_qmv
-    const uint32_t roff = (uint32_t)(min(row0 + lrow, a.O - 1) * a.rb) + coff;
+    const uint32_t coff = (uint32_t)min(16 * q, (int)(a.rb - 16));   // short rows: see k_qmv
+    const uint32_t roff = (uint32_t)(min(row0 + col, a.O - 1) * a.rb) + coff;
     const uint32_t last_seg = (uint32_t)(a.rb - 16) - coff;
     uint4 w[NKW][2];
 #pragma unroll
@@ -698,9 +705,9 @@ __global__ __launch_bounds__(512) void k_qmvg(QmvArgs a, int passes, int ntiles)
             hw[m] = hilo_pair(v[m], v[m + 4], 0.f);
             lw[m] = hilo_pair(v[m], v[m + 4], 1.f);
         }
-        uint4 *dst = lds + c * cs + 2 * t;
-        dst[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-        dst[1] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        uint4 *dst = lds + c * 4;
+        dst[(2 * t) ^ swz4(c)] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        dst[(2 * t + 1) ^ swz4(c)] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
     }
     __syncthreads();                                      // the scales are read by every wave
 
@@ -719,20 +726,12 @@ __global__ __launch_bounds__(512) void k_qmvg(QmvArgs a, int passes, int ntiles)
         if (kb >= nkb) break;                             // uniform
 #pragma unroll
         for (int sg = 0; sg < 2; ++sg) {
-            const uint4 u = w[i][sg];
-            w[i][sg] = make_uint4((uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)u.x),
-                                  (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)u.y),
-                                  (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)u.z),
-                                  (uint32_t)__builtin_amdgcn_ds_bpermute(src4, (int)u.w));
-        }
-        const uint4 *bw = lds + (kb * STEPS * 4 + q) * cs + bcol;
-#pragma unroll
-        for (int sg = 0; sg < 2; ++sg) {
             floatx4 ap = floatx4{0.f, 0.f, 0.f, 0.f}, sp = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int sub = 0; sub < SPS; ++sub) {
                 const int s2 = sg * SPS + sub;
-                const uint4 b0 = bw[s2 * 4 * cs];
+                const int cq = (kb * STEPS + s2) * 4 + q;
+                const uint4 b0 = lds[cq * 4 + (bcol ^ swz4(cq))];
                 const uint4 b = mine ? b0 : make_uint4(0u, 0u, 0u, 0u);
                 ap = mfma(codes<kI4>(w[i][sg], sub), b, ap);
                 sp = mfma(ones, b, sp);
@@ -787,8 +786,7 @@ hipError_t launch_qg(const QmvArgs &a, hipStream_t st)
     const int passes = (a.S + kQ1Tpp - 1) / kQ1Tpp;
     const int64_t grid = (int64_t)(ntiles + 7) / 8 * 8 * passes;
     if (grid <= 0 || grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-    const int ntmax = a.S < kQ1Tpp ? a.S : kQ1Tpp;
-    const size_t stage = (size_t)a.nkb * MF<kI4>::STEPS * 4 * (2 * ntmax) * 16 + (size_t)(a.ng + 15) * 16 * 4;
+    const size_t stage = (size_t)a.nkb * MF<kI4>::STEPS * 4 * 4 * 16 + (size_t)(a.ng + 15) * 16 * 4;
     const size_t red = (size_t)kQmvWaves * kWave * 16;     // the partial tiles, at the end
     const size_t lds = stage > red ? stage : red;
     if (lds > 160 * 1024) return hipErrorInvalidValue;
