@@ -65,6 +65,26 @@ def test_tiles_per_block_ragged(dev, orc, fmt, O):
         np.testing.assert_array_equal(got, ref.astype(np.float32), err_msg=f"fmt{fmt} O{O} S{S}")
 
 
+@pytest.mark.parametrize("O", [1, 17, 4100, 8200, 12290])
+def test_f32_matrix_cores_exact(dev, orc, O):
+    """fp32 rows on the fp32 matrix cores: integer weights in [-8, 8),
+    integer x in [-4, 4] and scales 2^-k give sums that fp32 holds exactly,
+    so the device equals the oracle bit for bit; 1 to 3 row tiles per block
+    with a ragged last one, widths from one 16-byte run to a ragged
+    per-wave part, and 16 / 17 rows (one full pass, then a second pass of
+    one row)."""
+    g = synth.rng(260, O)
+    for I in (4, 60, 1028, 6148):
+        W = g.integers(-8, 8, size=(O, I)).astype(np.float32).view(np.uint8)
+        sc = synth.exact_scales(g, O)
+        for S in (1, 3, 16, 17):
+            announce("qgemv f32 exact", O, I, S)
+            x = synth.exact_activations(g, S, I)
+            ref, _ = orc.qgemv(0, W, sc, x)
+            got = run_gpu(dev, 0, W, sc, x, O)
+            np.testing.assert_array_equal(got, ref.astype(np.float32), err_msg=f"O{O} I{I} S{S}")
+
+
 @pytest.mark.parametrize("fmt", [0, 1, 2, 3])
 @pytest.mark.parametrize("O,I", [(37, 40), (300, 1000), (257, 4096), (64, 8192 + 64), (40, 16384 + 40)])
 def test_exact_integer_bitwise(dev, orc, fmt, O, I):

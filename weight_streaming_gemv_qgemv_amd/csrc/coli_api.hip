@@ -1094,6 +1094,20 @@ extern "C" int coli_qgemv(int fmt, const void *W, const float *scale, const floa
     if (rc != COLI_OK) return rc;
     if (S == 0 || O == 0) return COLI_OK;
     const int64_t rb = coli_row_bytes(fmt, I);
+    if (fmt == COLI_F32 && qmv_f32_supported(I, W, x)) {
+        // fp32 matrix cores: whole 16-byte runs, aligned operands
+        QmvArgs q = {};
+        q.W = (const uint8_t *)W;
+        q.scale = scale;
+        q.x = x;
+        q.y = y;
+        q.S = S;
+        q.I = I;
+        q.O = O;
+        q.rb = rb;
+        StageTimer t(kStQgemv, (hipStream_t)stream);
+        return to_status(qmv_f32_launch(q, (hipStream_t)stream));
+    }
     if (qmv_supported(fmt, rb, I, O, W, x)) {
         // matrix cores: whole 16-byte row segments, aligned operands
         QmvArgs q = {};

@@ -24,6 +24,11 @@ struct QmvArgs {
 bool qmv_supported(int fmt, int64_t rb, int I, int O, const void *W, const float *x);
 hipError_t qmv_launch(QmvArgs a, int fmt, hipStream_t st);
 
+// fp32 rows (fmt f32) on the fp32 matrix cores: I a multiple of 4, W and x
+// 16-byte aligned (64-bit row offsets: any matrix size).
+bool qmv_f32_supported(int I, const void *W, const float *x);
+hipError_t qmv_f32_launch(QmvArgs a, hipStream_t st);
+
 // Grouped-scale int4 (scale [O, ceil(I / gs)]): gs 32, 64 or a multiple of
 // 128; 16-byte row segments, 16-byte aligned W, scale and x, I <= 12288.
 bool qmv_grouped_supported(int64_t rb, int I, int gs, const void *W, const float *scale, const float *x);

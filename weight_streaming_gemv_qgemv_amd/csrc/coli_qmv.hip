@@ -526,6 +526,123 @@ hipError_t launch_q1_nkw(const QmvArgs &a, int nkw, hipStream_t st)
     }
 }
 
+// ---------------------------------------------------------------- fp32 rows
+// fp32 weights on the fp32 matrix cores (v_mfma_f32_16x16x4_f32): the
+// products need neither codes nor a hi/lo split, and no activation staging.
+// A block of 8 waves owns MTB tiles of 16 rows for a pass of up to 16
+// activation rows (one MFMA column each); wave w takes the w-th eighth of the
+// row width in steps of 16 elements: lane (c, q) loads 16 bytes of weight
+// row c and 16 of activation row c at element 16 j + 4 q and feeds them to 4
+// consecutive MFMAs (k-slot q of product i is element 16 j + 4 q + i).  The
+// loads of the next 4 steps are in flight while the current 4 are
+// multiplied; the 8 waves' tiles are added in wave order through LDS.
+constexpr int kQfTpp = 16;   // activation rows per pass
+constexpr int kQfUnr = 4;    // steps per load batch
+
+template <int MTB>
+__global__ __launch_bounds__(512) void k_qmvf(QmvArgs a, int passes, int ntiles, int kw)
+{
+    __shared__ floatx4 red[kQmvWaves * MTB * kWave];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 15, q = lane >> 4;
+    const int xcd = blockIdx.x % 8, jb = blockIdx.x / 8;
+    const int tgroup = (jb / passes) * 8 + xcd, pass = jb % passes;
+    if (tgroup * MTB >= ntiles) return;                   // whole block, before any barrier
+    const int row0 = tgroup * MTB * 16;
+    const int t0 = pass * kQfTpp;
+    const int nt = min(kQfTpp, a.S - t0);
+
+    // wave mt < MTB finishes tile mt: its 4 scales per lane are requested first
+    float scp[4] = {1.f, 1.f, 1.f, 1.f};
+    if (wave < MTB && a.scale) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) scp[r] = a.scale[min(row0 + 16 * wave + 4 * q + r, a.O - 1)];
+    }
+    const float *wr[MTB];
+#pragma unroll
+    for (int mt = 0; mt < MTB; ++mt)
+        wr[mt] = reinterpret_cast<const float *>(a.W) + (int64_t)min(row0 + 16 * mt + col, a.O - 1) * a.I;
+    // dead columns repeat the last live activation row (never stored)
+    const float *xr = a.x + (int64_t)(t0 + min(col, nt - 1)) * a.I;
+    const int k0 = wave * kw, k1 = min(a.I, k0 + kw);      // this wave's elements
+    constexpr int BATCH = 16 * kQfUnr;
+
+    floatx4 acc[MTB];
+#pragma unroll
+    for (int mt = 0; mt < MTB; ++mt) acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    // batch at element e: lane (c, q) takes elements e + 16 u + 4 q .. + 3
+    // (I is a multiple of 4: a run is wholly inside the wave's part or not
+    // loaded at all, its values zero)
+    auto load = [&](int e, float4 (&wv)[kQfUnr][MTB], float4 (&xv)[kQfUnr]) {
+#pragma unroll
+        for (int u = 0; u < kQfUnr; ++u) {
+            const int k = e + 16 * u + 4 * q;
+            const bool in = k < k1;
+#pragma unroll
+            for (int mt = 0; mt < MTB; ++mt) wv[u][mt] = in ? gload4f(wr[mt] + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+            xv[u] = in ? gload4f(xr + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    };
+    auto product = [&](const float4 (&wv)[kQfUnr][MTB], const float4 (&xv)[kQfUnr]) {
+#pragma unroll
+        for (int u = 0; u < kQfUnr; ++u) {
+            const float xa[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int mt = 0; mt < MTB; ++mt) {
+                    const float wa[4] = {wv[u][mt].x, wv[u][mt].y, wv[u][mt].z, wv[u][mt].w};
+                    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(wa[i], xa[i], acc[mt], 0, 0, 0);
+                }
+        }
+    };
+    float4 wA[kQfUnr][MTB], xA[kQfUnr], wB[kQfUnr][MTB], xB[kQfUnr];
+    if (k0 < k1) load(k0, wA, xA);
+    for (int e = k0; e < k1; e += 2 * BATCH) {
+        if (e + BATCH < k1) load(e + BATCH, wB, xB);
+        product(wA, xA);
+        if (e + BATCH >= k1) break;
+        if (e + 2 * BATCH < k1) load(e + 2 * BATCH, wA, xA);
+        product(wB, xB);
+    }
+
+    // partial tiles of the 8 waves, added in wave order; wave mt < MTB adds
+    // tile mt
+#pragma unroll
+    for (int mt = 0; mt < MTB; ++mt) red[(wave * MTB + mt) * kWave + lane] = acc[mt];
+    __syncthreads();
+    if (wave >= MTB) return;
+    const int mt = wave;
+    floatx4 v = red[mt * kWave + lane];
+#pragma unroll
+    for (int ww = 1; ww < kQmvWaves; ++ww) v += red[(ww * MTB + mt) * kWave + lane];
+    // D[4 q + r][col]: weight row row0 + 16 mt + 4 q + r, activation row t0 + col
+    const int ob = row0 + 16 * mt + 4 * q;
+    if (col < nt) {
+        float *yp = a.y + (int64_t)(t0 + col) * a.O;
+        if (a.y_vec4 && ob + 3 < a.O) {
+            *reinterpret_cast<float4 *>(yp + ob) = make_float4(scp[0] * v[0], scp[1] * v[1], scp[2] * v[2], scp[3] * v[3]);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (ob + r < a.O) yp[ob + r] = scp[r] * v[r];
+        }
+    }
+}
+
+template <int MTB>
+hipError_t launch_qf(const QmvArgs &a, hipStream_t st)
+{
+    const int ntiles = (a.O + 15) / 16;
+    const int ngroups = (ntiles + MTB - 1) / MTB;
+    const int passes = (a.S + kQfTpp - 1) / kQfTpp;
+    const int64_t grid = (int64_t)(ngroups + 7) / 8 * 8 * passes;
+    if (grid <= 0 || grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const int kw = ((a.I + kQmvWaves - 1) / kQmvWaves + 15) / 16 * 16;
+    hipLaunchKernelGGL((k_qmvf<MTB>), dim3((unsigned)grid), dim3(64 * kQmvWaves), 0, st, a, passes, ntiles, kw);
+    return hipGetLastError();
+}
+
 // compute units of the current device (cached per device)
 int64_t qmv_cus()
 {
@@ -815,6 +932,26 @@ hipError_t launch_qg_nkw(const QmvArgs &a, int nkw, hipStream_t st)
 }
 
 }  // namespace
+
+bool qmv_f32_supported(int I, const void *W, const float *x)
+{
+    return I >= 4 && I % 4 == 0 && ((uintptr_t)W & 15u) == 0 && ((uintptr_t)x & 15u) == 0;
+}
+
+// fp32 rows: up to 4 activation rows one row tile per block (more blocks
+// per CU; 12288 x 6144: S = 1 58.4 us against 65.1 with 3 tiles); from 5 rows
+// on about one block per CU with at most 3 tiles, so fewer blocks re-read the
+// activations (S = 8: 69.9 against 74.5 us, S = 16: 75.3 against 90.3 us)
+hipError_t qmv_f32_launch(QmvArgs a, hipStream_t st)
+{
+    if (a.S <= 0 || a.O <= 0) return hipSuccess;
+    a.y_vec4 = a.O % 4 == 0 && ((uintptr_t)a.y & 15u) == 0;
+    const int64_t ntiles = (a.O + 15) / 16;
+    const int64_t mtb = a.S <= 4 ? 1 : (ntiles + qmv_cus() - 1) / qmv_cus();
+    if (mtb >= 3) return launch_qf<3>(a, st);
+    if (mtb == 2) return launch_qf<2>(a, st);
+    return launch_qf<1>(a, st);
+}
 
 bool qmv_supported(int fmt, int64_t rb, int I, int O, const void *W, const float *x)
 {
