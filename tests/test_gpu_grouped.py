@@ -53,10 +53,14 @@ def test_small_shapes(dev, orc, gs):
 @pytest.mark.parametrize("gs", GS + (384,))
 def test_exact_integer_bitwise(dev, orc, gs):
     """Integer x in [-4, 4] and power-of-two scales per group: every partial
-    sum is an exact fp32 value, so the device result equals the oracle's."""
+    sum is an exact fp32 value, so the device result equals the oracle's.
+    Up to 2 rows one pass of the two-row kernel; from 3 rows (gs 32: from 7)
+    the rounds kernel (passes of 8 rows; 9 rows: a second pass of one) while
+    the block's scales fit its LDS (gs 32 at I = 12288 takes two-row passes);
+    8200 rows take 32- or 48-row blocks with a ragged last one."""
     g = synth.rng(7200, gs)
-    for O, I in ((37, 1024 + 32), (300, 4096), (64, 12288)):
-        for S in (1, 2, 3):
+    for O, I in ((37, 1024 + 32), (300, 4096), (64, 12288), (8200, 1024 + 128)):
+        for S in (1, 2, 3, 8, 9):
             announce("grouped exact", gs, O, I, S)
             W = synth.weight_bytes(g, 2, O, I)
             ng = (I + gs - 1) // gs
@@ -91,7 +95,7 @@ def test_group_scale_is_applied_per_group(dev, orc):
 @pytest.mark.parametrize("gs", (32, 128))
 def test_full_size_12288x6144_sampled(dev, orc, gs):
     """The dense sweep's matrix in grouped form: O=12288, I=6144, S in
-    {1, 2, 4}; the oracle checks 1024 sampled output rows."""
+    {1, 2, 4, 8}; the oracle checks 1024 sampled output rows."""
     import torch
     from weight_streaming_gemv_qgemv_amd import binding as b
     O, I = 12288, 6144
@@ -101,7 +105,7 @@ def test_full_size_12288x6144_sampled(dev, orc, gs):
     Wd, scd = to_dev(W, dev), to_dev(sc, dev)
     rows = np.sort(g.choice(O, 1024, replace=False))
     rows[0], rows[-1] = 0, O - 1
-    for S in (1, 2, 4):
+    for S in (1, 2, 4, 8):
         announce("grouped 12288x6144", gs, S)
         x = synth.activations(g, S, I)
         y = torch.empty((S, O), dtype=torch.float32, device=dev)

@@ -91,9 +91,19 @@ __device__ __forceinline__ void xrun_elements(const float *xr, int e0, int I, fl
     for (int i = 0; i < RUN; ++i) v[i] = e0 + i < I ? xr[e0 + i] : 0.f;
 }
 
-template <int FMT, int MT>
+// GPS > 0: int4 rows with one scale per gs elements, GPS groups per 64-byte
+// segment (128 elements): 1 (gs a multiple of 128), 2 (gs 64) or 4 (gs 32).
+// Lane group q holds the segment's elements 32 q .. 32 q + 31, so group j is
+// lane groups q with q / (4 / GPS) = j: per step one product per group with
+// the activation operand zero in the other lane groups.  Each segment's
+// products and activation sums start from zero and are then scaled into the
+// running total, tot += scale[o, g] (products - OFF sums); the block's
+// scales are staged in LDS after the round buffers.
+template <int FMT, int MT, int GPS = 0>
 __global__ __launch_bounds__(512) void k_qmv(QmvArgs a)
 {
+    constexpr bool GS = GPS > 0;
+    static_assert(!GS || FMT == kI4, "group scales: int4 rows");
     using T = MF<FMT>;
     constexpr int STEPS = T::STEPS, KB = T::KB, SEGS = T::SEGS, BITS = T::BITS, SPS = T::SPS;
     constexpr int RB = 16 * MT;
@@ -119,6 +129,8 @@ __global__ __launch_bounds__(512) void k_qmv(QmvArgs a)
     const int nkb = a.nkb;
     const int rounds = (nkb + kQmvWaves - 1) / kQmvWaves;
     constexpr int units = kQmvWaves * STEPS * 4 * 16;   // units per round buffer
+    float *sl = reinterpret_cast<float *>(lds + 2 * units);   // GS: the block's scales
+    const int ngp = a.ng | 1;
 
     // a chunk past the end of a row shorter than 64 bytes is read at the
     // row's last chunk (it meets zero activations)
@@ -207,7 +219,7 @@ __global__ __launch_bounds__(512) void k_qmv(QmvArgs a)
             put(v);
         }
     };
-    auto compute = [&](uint4 (&w)[MT][SEGS], const uint4 *buf) {
+    auto compute = [&](uint4 (&w)[MT][SEGS], const uint4 *buf, int kb) {
         if constexpr (XPOSE) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
@@ -222,6 +234,44 @@ __global__ __launch_bounds__(512) void k_qmv(QmvArgs a)
         }
         // dead columns read the last live row's units
         const int bcol = (col >> 1) < nt ? col : 2 * (nt - 1) + (col & 1);
+        if constexpr (GS) {
+            constexpr int GPSX = GS ? GPS : 1;
+            const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+            for (int sg = 0; sg < SEGS; ++sg) {
+                floatx4 ap[GPSX][MT], sp[GPSX];
+#pragma unroll
+                for (int jg = 0; jg < GPSX; ++jg) {
+                    sp[jg] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) ap[jg][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+                }
+#pragma unroll
+                for (int sub = 0; sub < SPS; ++sub) {
+                    const int cq = (wave * STEPS + sg * SPS + sub) * 4 + q;
+                    const uint4 b = buf[cq * 16 + (bcol ^ swz16(cq))];
+#pragma unroll
+                    for (int jg = 0; jg < GPSX; ++jg) {
+                        const uint4 bj = (GPSX == 1 || q / (4 / GPSX) == jg) ? b : zero;
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt) ap[jg][mt] = mfma(codes<FMT>(w[mt][sg], sub), bj, ap[jg][mt]);
+                        sp[jg] = mfma(ones, bj, sp[jg]);
+                    }
+                }
+                // each group's scale (segments past the row end meet zero
+                // activations: their products and sums are zero)
+#pragma unroll
+                for (int jg = 0; jg < GPSX; ++jg) {
+                    const int g = min((kb * KB + sg * 128 + jg * (128 / GPSX)) / a.gs, a.ng - 1);
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            acc[mt][r] += sl[(16 * mt + 4 * q + r) * ngp + g] * (ap[jg][mt][r] - OFF * sp[jg][r]);
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int s = 0; s < STEPS; ++s) {
             const int cq = (wave * STEPS + s) * 4 + q;
@@ -238,7 +288,7 @@ __global__ __launch_bounds__(512) void k_qmv(QmvArgs a)
     // other buffer, barrier.
     // the epilogue wave's (wave mt < MT) scales, requested before anything else
     float scp[4] = {1.f, 1.f, 1.f, 1.f};
-    if (wave < MT && a.scale) {
+    if (!GS && wave < MT && a.scale) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) scp[r] = a.scale[min(row0 + 16 * wave + 4 * q + r, a.O - 1)];
     }
@@ -246,13 +296,24 @@ __global__ __launch_bounds__(512) void k_qmv(QmvArgs a)
     float4 xv[PASSES][RUN / 4];
     loadX(0, xv);
     loadW(0, wA);
+    if constexpr (GS) {
+        // the block's rows' scales (one contiguous span of ng per row) at
+        // sl[row * ngp + g]; an odd row stride puts the 4 rows a read meets
+        // (4 q + r, q = 0..3) in different banks
+        const int nsc = (min(row0 + RB, a.O) - row0) * a.ng;
+        const float *sb = a.scale + (int64_t)row0 * a.ng;
+        for (int e = tid; e < nsc; e += 512) {
+            const int rr = e / a.ng, g = e - rr * a.ng;
+            sl[rr * ngp + g] = sb[e];
+        }
+    }
     stageX(0, xv, lds);
     __syncthreads();
     for (int r = 0; r < rounds; r += 2) {
         loadX(r + 1 < rounds ? r + 1 : r, xv);
         loadW(r + 1 < rounds ? r + 1 : r, wB);
         __builtin_amdgcn_sched_barrier(0);
-        if (r * kQmvWaves + wave < nkb) compute(wA, lds);
+        if (r * kQmvWaves + wave < nkb) compute(wA, lds, r * kQmvWaves + wave);
         __builtin_amdgcn_sched_barrier(0);
         if (r + 1 >= rounds) break;
         stageX(r + 1, xv, lds + units);
@@ -260,7 +321,7 @@ __global__ __launch_bounds__(512) void k_qmv(QmvArgs a)
         loadX(r + 2 < rounds ? r + 2 : r + 1, xv);
         loadW(r + 2 < rounds ? r + 2 : r + 1, wA);
         __builtin_amdgcn_sched_barrier(0);
-        if ((r + 1) * kQmvWaves + wave < nkb) compute(wB, lds + units);
+        if ((r + 1) * kQmvWaves + wave < nkb) compute(wB, lds + units, (r + 1) * kQmvWaves + wave);
         __builtin_amdgcn_sched_barrier(0);
         if (r + 2 >= rounds) break;
         stageX(r + 2, xv, lds);
@@ -289,7 +350,7 @@ __global__ __launch_bounds__(512) void k_qmv(QmvArgs a)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const float vv = v[r] + __shfl_xor(v[r], 1, kWave);
-        res[r] = scp[r] * (vv - OFF * xs);
+        res[r] = GS ? vv : scp[r] * (vv - OFF * xs);   // GS: scaled segment by segment
     }
     const int tok = col >> 1;
     if ((col & 1) == 0 && tok < nt) {
@@ -658,16 +719,18 @@ int64_t qmv_cus()
     return cache[dev];
 }
 
-template <int FMT, int MT>
+template <int FMT, int MT, int GPS = 0>
 hipError_t launch_q(const QmvArgs &a, hipStream_t st)
 {
     const int rb = 16 * MT;
     const dim3 grid((unsigned)((a.O + rb - 1) / rb), (unsigned)((a.S + kQmvTpp - 1) / kQmvTpp));
-    // LDS: two round buffers, or the partial tiles
-    const size_t stage = (size_t)2 * kQmvWaves * MF<FMT>::STEPS * 4 * 16 * 16;
+    // LDS: two round buffers (GS: and the block's scales), or the partial tiles
+    const size_t stage = (size_t)2 * kQmvWaves * MF<FMT>::STEPS * 4 * 16 * 16 +
+                         (GPS > 0 ? (size_t)rb * (size_t)(a.ng | 1) * 4 : 0);
     const size_t red = (size_t)kQmvWaves * (MT + 1) * kWave * 16;
     const size_t lds = stage > red ? stage : red;
-    auto kern = k_qmv<FMT, MT>;
+    if (lds > 160 * 1024) return hipErrorInvalidValue;
+    auto kern = k_qmv<FMT, MT, GPS>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
@@ -933,6 +996,23 @@ hipError_t launch_qg_nkw(const QmvArgs &a, int nkw, hipStream_t st)
 
 }  // namespace
 
+// Row tiles per block of the rounds kernel: 64 or 48 rows once that still
+// gives at least 128 blocks, else 32 (each block stages every activation
+// row, so fewer rows per block cost activation traffic): of 64 and 48 the one
+// whose blocks fill the last round of CUs best, 64 on a tie (12288 rows: 256
+// blocks of 48 against 192 of 64 -- int8 8 rows 22.0 -> 20.0 us, int4 16.7
+// -> 16.3 us)
+int rounds_mt(int O)
+{
+    if ((int64_t)O < 64 * 128) return 2;
+    const int64_t cus = qmv_cus();
+    auto fill = [&](int rows) {
+        const int64_t blocks = (O + rows - 1) / rows, rounds = (blocks + cus - 1) / cus;
+        return (double)blocks / (double)(rounds * cus);
+    };
+    return fill(48) > fill(64) ? 3 : 4;
+}
+
 bool qmv_f32_supported(int I, const void *W, const float *x)
 {
     return I >= 4 && I % 4 == 0 && ((uintptr_t)W & 15u) == 0 && ((uintptr_t)x & 15u) == 0;
@@ -978,21 +1058,7 @@ hipError_t qmv_launch(QmvArgs a, int fmt, hipStream_t st)
         default: return hipErrorInvalidValue;
         }
     }
-    // 64 or 48 rows per block once that still gives at least 128 blocks, else
-    // 32 (each block stages every activation row, so fewer rows per block
-    // cost activation traffic): of 64 and 48 the one whose blocks fill the
-    // last round of CUs best, 64 on a tie (12288 rows: 256 blocks of 48
-    // against 192 of 64 -- int8 8 rows 22.0 -> 20.0 us, int4 16.7 -> 16.3 us)
-    const bool wide = (int64_t)a.O >= 64 * 128;
-    int mt = 2;
-    if (wide) {
-        const int64_t cus = qmv_cus();
-        auto fill = [&](int rows) {
-            const int64_t blocks = (a.O + rows - 1) / rows, rounds = (blocks + cus - 1) / cus;
-            return (double)blocks / (double)(rounds * cus);
-        };
-        mt = fill(48) > fill(64) ? 3 : 4;
-    }
+    const int mt = rounds_mt(a.O);
 #define COLI_Q_MT(F) return mt == 4 ? launch_q<F, 4>(a, st) : mt == 3 ? launch_q<F, 3>(a, st) : launch_q<F, 2>(a, st)
     switch (fmt) {
     case kI8: COLI_Q_MT(kI8);
@@ -1022,6 +1088,26 @@ hipError_t qmv_grouped_launch(QmvArgs a, hipStream_t st)
     a.nkb = (a.I + MF<kI4>::KB - 1) / MF<kI4>::KB;
     a.ng = (a.I + a.gs - 1) / a.gs;
     a.y_vec4 = a.O % 4 == 0 && ((uintptr_t)a.y & 15u) == 0;
+    // more rows than one pass of k_qmvg holds: the rounds kernel with group
+    // scales takes 8 rows per pass (12288 x 6144, gs 128: 4 rows 15.3 us
+    // against 21.7 us for two passes, 8 rows 16.0 against 38.9 us; gs 64:
+    // 18.1 / 19.5 against 23.7 / 43.1 us).  gs 32 costs it four products and
+    // four flushes per step and segment (4 rows: 36.2 against 24.3 us for two
+    // passes, 8 rows: 38.0 against 44.2 us), so gs 32 takes it from 7 rows on.
+    // Only when the block's scales fit LDS beside the two round buffers;
+    // else, for the widest rows at gs 32 / 64, passes of k_qmvg.
+    if (a.S > kQ1Tpp && (a.gs != 32 || a.S > 3 * kQ1Tpp)) {
+        int mt = rounds_mt(a.O);
+        if (a.gs == 32) mt = 2;                           // 48 rows: 4 x 3 group tiles spill
+        else if (a.gs == 64 && mt > 3) mt = 3;
+        const size_t need = (size_t)2 * kQmvWaves * MF<kI4>::STEPS * 4 * 16 * 16 + (size_t)16 * mt * (size_t)(a.ng | 1) * 4;
+        if (need <= 160 * 1024) {
+            if (a.gs == 32) return launch_q<kI4, 2, 4>(a, st);
+            if (a.gs == 64) return mt == 3 ? launch_q<kI4, 3, 2>(a, st) : launch_q<kI4, 2, 2>(a, st);
+            return mt == 4 ? launch_q<kI4, 4, 1>(a, st) : mt == 3 ? launch_q<kI4, 3, 1>(a, st)
+                                                            : launch_q<kI4, 2, 1>(a, st);
+        }
+    }
     const int nkw = (a.nkb + kQmvWaves - 1) / kQmvWaves;
     if (a.gs == 32) return launch_qg_nkw<4>(a, nkw, st);
     if (a.gs == 64) return launch_qg_nkw<2>(a, nkw, st);
