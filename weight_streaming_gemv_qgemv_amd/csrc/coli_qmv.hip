@@ -1,25 +1,28 @@
-// coli_qmv.hip -- the dense quantised matrix-vector product on the bf16
-// matrix cores, fp32-level accuracy:
+// coli_qmv.hip -- the dense quantised matrix-vector product on the matrix
+// cores, fp32-level accuracy:
 //   y[s, o] = scale[o] * sum_i v(o, i) x[s, i]
-// over int8 / int4 (nibble - 8) / int2 (crumb - 2) rows [glm.c@98759bf --
-// typedef QT, matmul_qt, matmul_q, matmul_i4, matmul_i2; metal@93cde63 --
-// mm_gemv].
+// over int8 / int4 (nibble - 8) / int2 (crumb - 2) rows on the bf16 matrix
+// cores, fp32 rows on the fp32 ones, and int4 rows with one scale per gs
+// elements [glm.c@98759bf -- typedef QT, matmul_qt, matmul_q, matmul_i4,
+// matmul_i2; metal@93cde63 -- mm_gemv; docs-quickstart -- qt_resolve_fmt].
 //
-// Two kernels.  k_qmv1 (one or two activation rows) issues every weight load
-// of the call up front; see its comment.  k_qmv (more rows): a block of 8
-// waves owns 16 MT consecutive output rows for one pass of up to 8
-// activation rows; wave w multiplies the rows' k-blocks w, w + 8, ... (a
-// K-slice) in rounds of 8 k-blocks, so one block's loads cover its rows'
-// whole width and there are enough blocks for the chip even for a few
-// thousand rows.  In both, each lane loads its matrix-core operand straight
-// from the row-major rows (lane 16 q + c: row c, bytes 16 q .. 16 q + 15 of
-// each 64-byte segment; measured faster than coalesced row loads transposed
-// with ds_bpermute, except for int8 rows in k_qmv), and the
-// activations are split into bf16 hi/lo in the kernel (column 2t: hi of row
-// t, column 2t+1: lo) straight from the fp32 input, so the call needs no
-// scratch memory.  sum(x), needed to remove OFF * sum(x) from the code
-// products, is one more MFMA per step against a tile of ones.  The 8 waves'
-// partial tiles are added in wave order through LDS.
+// k_qmv1 (one or two activation rows) issues every weight load of the call
+// up front; see its comment.  k_qmv (more rows): a block of 8 waves owns
+// 16 MT consecutive output rows for one pass of up to 8 activation rows;
+// wave w multiplies the rows' k-blocks w, w + 8, ... (a K-slice) in rounds
+// of 8 k-blocks, so one block's loads cover its rows' whole width and there
+// are enough blocks for the chip even for a few thousand rows; with GPS > 0
+// it applies group scales segment by segment.  k_qmvg: group scales for one
+// or two rows.  k_qmvf: fp32 rows.  In the integer kernels each lane loads
+// its matrix-core operand straight from the row-major rows (lane 16 q + c:
+// row c, bytes 16 q .. 16 q + 15 of each 64-byte segment; measured faster
+// than coalesced row loads transposed with ds_bpermute, except for int8
+// rows in k_qmv), and the activations are split into bf16 hi/lo in the
+// kernel (column 2t: hi of row t, column 2t+1: lo) straight from the fp32
+// input, so the call needs no scratch memory.  sum(x), needed to remove
+// OFF * sum(x) from the code products, is one more MFMA per step against a
+// tile of ones.  The 8 waves' partial tiles are added in wave order through
+// LDS.
 #include "coli_device.h"
 #include "coli_frag.h"
 #include "coli_qmv.h"
