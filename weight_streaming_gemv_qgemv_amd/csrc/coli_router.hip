@@ -50,7 +50,7 @@ __global__ __launch_bounds__(256) void k_router_partial(const float *__restrict_
                                                         int E, int D, int slice,
                                                         double *__restrict__ part)
 {
-    constexpr int kSteps = TSUB == 1 ? 6 : 2;   // 16-d steps per chunk
+    constexpr int kSteps = TSUB == 1 ? 6 : 1;   // 16-d steps per chunk
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int t0 = blockIdx.x * 16 * TSUB;
     const int e0 = blockIdx.y * 64 + wave * 16;
@@ -123,15 +123,33 @@ __global__ __launch_bounds__(256) void k_router_partial(const float *__restrict_
             }
         }
     };
+    constexpr int CH = 16 * kSteps;   // d per chunk
     float4 wa0[kSteps], wa1[kSteps];
     float4 xb0[kSteps][TSUB], xb1[kSteps][TSUB];
     load(dbeg, wa0, xb0);
-    for (int d0 = dbeg; d0 < dend; d0 += 32 * kSteps) {
-        load(d0 + 16 * kSteps, wa1, xb1);   // past dend: all zeros, no access
-        product(wa0, xb0);
-        if (d0 + 16 * kSteps >= dend) break;
-        load(d0 + 32 * kSteps, wa0, xb0);
-        product(wa1, xb1);
+    if constexpr (TSUB == 1) {
+        for (int d0 = dbeg; d0 < dend; d0 += 2 * CH) {
+            load(d0 + CH, wa1, xb1);   // past dend: all zeros, no access
+            product(wa0, xb0);
+            if (d0 + CH >= dend) break;
+            load(d0 + 2 * CH, wa0, xb0);
+            product(wa1, xb1);
+        }
+    } else {
+        // one 16-d step per chunk, two chunks ahead (the registers of a
+        // 32-d chunk kept two ahead would lower the occupancy)
+        float4 wa2[kSteps], xb2[kSteps][TSUB];
+        load(dbeg + CH, wa1, xb1);
+        for (int d0 = dbeg; d0 < dend; d0 += 3 * CH) {
+            load(d0 + 2 * CH, wa2, xb2);
+            product(wa0, xb0);
+            if (d0 + CH >= dend) break;
+            load(d0 + 3 * CH, wa0, xb0);
+            product(wa1, xb1);
+            if (d0 + 2 * CH >= dend) break;
+            load(d0 + 4 * CH, wa1, xb1);
+            product(wa2, xb2);
+        }
     }
     // D[i][j]: i = expert row 4*r + kg, j = token column `row` of sub-tile u
 #pragma unroll
