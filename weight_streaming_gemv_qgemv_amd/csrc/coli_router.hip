@@ -173,35 +173,47 @@ __device__ __forceinline__ uint32_t order_key(float f)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Wave-wide max / min of a 32-bit value on the DPP network (registers only):
+// Wave-wide max of a 64-bit value on the DPP network (registers only):
 // pairs within quads, half rows and rows, then rows 0-1 into 1 and 3, rows
-// 0-2 into 3; lane 63 ends with the whole wave's result.
-template <bool MAX>
-__device__ __forceinline__ uint32_t wave_ext_u32(uint32_t v)
+// 0-2 into 3; lane 63 ends with the whole wave's result.  Each step moves
+// both halves and keeps the larger (all values here are >= 0, so the 0 a
+// lane of a disabled row reads is never the larger).
+template <int CTRL, int RM>
+__device__ __forceinline__ uint64_t dpp_max64(uint64_t v)
 {
-    const int id = MAX ? 0 : -1;
-    auto f = [](uint32_t a, uint32_t b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
-    v = f(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
-    v = f(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
-    v = f(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
-    v = f(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x140, 0xF, 0xF, false));  // row_mirror
-    v = f(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x142, 0xA, 0xF, false));  // row_bcast:15
-    v = f(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x143, 0xC, 0xF, false));  // row_bcast:31
-    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, RM, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, RM, 0xF, false);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    return o > v ? o : v;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
+{
+    v = dpp_max64<0xB1, 0xF>(v);    // quad_perm 1,0,3,2
+    v = dpp_max64<0x4E, 0xF>(v);    // quad_perm 2,3,0,1
+    v = dpp_max64<0x141, 0xF>(v);   // row_half_mirror
+    v = dpp_max64<0x140, 0xF>(v);   // row_mirror
+    v = dpp_max64<0x142, 0xA>(v);   // row_bcast:15
+    v = dpp_max64<0x143, 0xC>(v);   // row_bcast:31
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+    return ((uint64_t)hi << 32) | lo;
 }
 
 // One token per block.  First the block sums each score's slices in slice
 // order and takes the sigmoid in fp64, rounded once (scores go to `sig` and
 // to LDS).  Then the first wave runs the greedy top-K over
 // choice = sig + bias:
-//  - lane l owns experts e = l + 64 j (j < ceil(E/64) <= 16), so e rises
-//    with j; a lane's candidate is its first maximal untaken choice
-//    (strict '>' on order keys while j rises);
-//  - the wave's largest key wins; when several lanes hold it, the lowest
-//    e = 64 j + l among them (a second reduction), so the pick is the
-//    sequential scan's first maximum;
-//  - the pick's owner clears it; lane 0 then runs the pages' tail (top-p,
-//    normalisation, routed_scale) sequentially in fp32.
+//  - expert e (held by lane e % 64, slot e / 64; PER >= ceil(E / 64) slots)
+//    gets the unique 64-bit value (order key of its choice, ~e): the largest
+//    value is the largest choice and, among equal choices, the lowest e --
+//    the sequential scan's first maximum;
+//  - each lane sorts its values once (Batcher's odd-even merge network), so
+//    its best untaken expert is always its list head;
+//  - per pick one wave-wide max of the heads names the expert; its lane
+//    drops its head; lane 0 then reads the picks' scores from LDS and runs
+//    the pages' tail (top-p, normalisation, routed_scale) sequentially in
+//    fp32.
+template <int PER>
 __global__ __launch_bounds__(256) void k_router_topk(const double *__restrict__ part, int splits,
                                                      const float *__restrict__ bias, int S,
                                                      int E, int K, int norm_topk,
@@ -217,13 +229,12 @@ __global__ __launch_bounds__(256) void k_router_topk(const double *__restrict__ 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int s0 = blockIdx.x;
     const int nt = 1;
-    const int per = (E + 63) / 64;
     // the selecting wave's biases, requested before anything else
-    float bz[16];
+    float bz[PER];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < PER; ++j) {
         const int e = lane + 64 * j;
-        bz[j] = (wave == 0 && j < per && e < E) ? bias[e] : 0.f;
+        bz[j] = (wave == 0 && e < E) ? bias[e] : 0.f;
     }
     {
         const int64_t n = (int64_t)S * E;
@@ -249,49 +260,41 @@ __global__ __launch_bounds__(256) void k_router_topk(const double *__restrict__ 
     __syncthreads();
     const int s = s0;
     if (wave != 0) return;   // whole waves leave; no block barrier below
-    const float *sg = sig_s;
-    float sv[16];
-    uint32_t key[16];
+    // (key, ~e); slots past E hold 0, below every real value (keys are > 0)
+    uint64_t ck[PER];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < PER; ++j) {
         const int e = lane + 64 * j;
-        const bool ok = j < per && e < E;
-        sv[j] = ok ? sg[e] : 0.f;
-        key[j] = ok ? order_key(sv[j] + bz[j]) : 0u;     // choice = sig + bias (fp32)
+        ck[j] = e < E ? ((uint64_t)order_key(sig_s[e] + bz[j]) << 32) | (uint32_t)~(uint32_t)e : 0ull;
     }
+    // descending sort, Batcher's odd-even merge network on PER values
+#pragma unroll
+    for (int p = 1; p < PER; p <<= 1)
+#pragma unroll
+        for (int k = p; k >= 1; k >>= 1)
+#pragma unroll
+            for (int j = k % p; j + k < PER; j += 2 * k)
+#pragma unroll
+                for (int i = 0; i < k; ++i)
+                    if ((i + j) / (2 * p) == (i + j + k) / (2 * p)) {
+                        const uint64_t a = ck[i + j], b = ck[i + j + k];
+                        ck[i + j] = a > b ? a : b;
+                        ck[i + j + k] = a > b ? b : a;
+                    }
     int *pick = pick_s;
     float *pw = pw_s;
     for (int kk = 0; kk < K; ++kk) {
-        uint32_t bk = 0;
-        int bj = 0;
+        const uint64_t m = wave_max_u64(ck[0]);
+        const int e = (int)~(uint32_t)m;   // K <= E: m is a real expert's value
+        if ((e & 63) == lane) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
-            if (key[j] > bk) { bk = key[j]; bj = j; }
-        const uint32_t m = wave_ext_u32<true>(bk);
-        int e = -1;
-        if (m != 0) {
-            const uint64_t tied = __ballot(bk == m);
-            if (__popcll(tied) == 1) {
-                const int wl = __ffsll((unsigned long long)tied) - 1;
-                e = 64 * __builtin_amdgcn_readlane(bj, wl) + wl;
-            } else {
-                e = (int)wave_ext_u32<false>(bk == m ? (uint32_t)(64 * bj + lane) : 0xFFFFFFFFu);
-            }
+            for (int j = 0; j + 1 < PER; ++j) ck[j] = ck[j + 1];
+            ck[PER - 1] = 0ull;
         }
-        float sbest = 0.f;
-        if (e >= 0 && (e & 63) == lane) {
-            const int j = e >> 6;
-#pragma unroll
-            for (int jj = 0; jj < 16; ++jj)
-                if (jj == j) { sbest = sv[jj]; key[jj] = 0u; }
-        }
-        if (e >= 0) sbest = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sbest), e & 63));
-        if (lane == 0) {
-            pick[kk] = e;
-            pw[kk] = sbest;
-        }
+        if (lane == 0) pick[kk] = e;
     }
     if (lane != 0) return;
+    for (int kk = 0; kk < K; ++kk) pw[kk] = sig_s[pick[kk]];
     int ke = K;
     if (topp > 0.f && topp < 1.f) {
         for (int a2 = 1; a2 < K; ++a2) {
@@ -354,9 +357,16 @@ hipError_t router_launch(const float *Wr, const float *bias, const float *x, int
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    if (E > kRouterMaxE) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_router_topk, dim3(S), dim3(256), 0, st, part, splits, bias, S,
-                       E, K, norm_topk, routed_scale, topp, sig, idx, w, keff);
+    if (E > kRouterMaxE || K > E || K > 64) return hipErrorInvalidValue;
+    // slots per lane: the sort network's size
+#define COLI_TOPK(P) hipLaunchKernelGGL(k_router_topk<P>, dim3(S), dim3(256), 0, st, part, splits, bias, S, \
+                                        E, K, norm_topk, routed_scale, topp, sig, idx, w, keff)
+    if (E <= 64) COLI_TOPK(1);
+    else if (E <= 128) COLI_TOPK(2);
+    else if (E <= 256) COLI_TOPK(4);
+    else if (E <= 512) COLI_TOPK(8);
+    else COLI_TOPK(16);
+#undef COLI_TOPK
     return hipGetLastError();
 }
 
