@@ -392,6 +392,15 @@ __device__ __forceinline__ float4 yload4(const uint16_t *y, int64_t i)
     return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
                        __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
 }
+// 8 bf16 (16 bytes) -> two float4
+__device__ __forceinline__ void yload8(const uint16_t *y, int64_t i, float4 &lo, float4 &hi)
+{
+    const uint4 u = *reinterpret_cast<const uint4 *>(y + i);
+    lo = make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
+    hi = make_float4(__uint_as_float(u.z << 16), __uint_as_float(u.z & 0xFFFF0000u),
+                     __uint_as_float(u.w << 16), __uint_as_float(u.w & 0xFFFF0000u));
+}
 __device__ __forceinline__ float yload1(const float *y, int64_t i) { return y[i]; }
 __device__ __forceinline__ float yload1(const uint16_t *y, int64_t i) { return __uint_as_float((uint32_t)y[i] << 16); }
 
@@ -408,6 +417,56 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(const YT *__restric
     // slots in runs of kCombineRun: the run's rows are all requested before
     // the first is added, the additions stay in slot order
     constexpr int kCombineRun = 8;
+    if constexpr (sizeof(YT) == 2) {
+        if (vec4 == 2) {   // bf16 rows, 8 elements (one 16-byte load per row) per thread
+            const int d = (blockIdx.y * kCombineThreads + threadIdx.x) * 8;
+            if (d >= D) return;
+            float4 a0 = make_float4(0.f, 0.f, 0.f, 0.f), a1 = a0;
+            auto fma4 = [](float wk, const float4 &v, float4 &acc) {
+                acc.x = fmaf(wk, v.x, acc.x);
+                acc.y = fmaf(wk, v.y, acc.y);
+                acc.z = fmaf(wk, v.z, acc.z);
+                acc.w = fmaf(wk, v.w, acc.w);
+            };
+            for (int k0 = 0; k0 < K; k0 += kCombineRun) {
+                int r[kCombineRun];
+                float wk[kCombineRun];
+                float4 v0[kCombineRun], v1[kCombineRun];
+#pragma unroll
+                for (int j = 0; j < kCombineRun; ++j) {
+                    r[j] = k0 + j < K ? pr[k0 + j] : -1;
+                    wk[j] = k0 + j < K ? ws[k0 + j] : 0.f;
+                }
+#pragma unroll
+                for (int j = 0; j < kCombineRun; ++j) {
+                    v0[j] = v1[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+                    if (r[j] >= 0) yload8(y, (int64_t)r[j] * D + d, v0[j], v1[j]);
+                }
+#pragma unroll
+                for (int j = 0; j < kCombineRun; ++j) {
+                    if (r[j] < 0) continue;
+                    fma4(wk[j], v0[j], a0);
+                    fma4(wk[j], v1[j], a1);
+                }
+            }
+            if (has_shared) {
+                float4 v0, v1;
+                yload8(y, (shared_row0 + s) * (int64_t)D + d, v0, v1);
+                a0.x += v0.x; a0.y += v0.y; a0.z += v0.z; a0.w += v0.w;
+                a1.x += v1.x; a1.y += v1.y; a1.z += v1.z; a1.w += v1.w;
+            }
+            if (resid) {
+                const float4 r0 = *reinterpret_cast<const float4 *>(resid + (int64_t)s * D + d);
+                const float4 r1 = *reinterpret_cast<const float4 *>(resid + (int64_t)s * D + d + 4);
+                a0 = make_float4(r0.x + a0.x, r0.y + a0.y, r0.z + a0.z, r0.w + a0.w);
+                a1 = make_float4(r1.x + a1.x, r1.y + a1.y, r1.z + a1.z, r1.w + a1.w);
+            }
+            float4 *o = reinterpret_cast<float4 *>(out + (int64_t)s * D + d);
+            o[0] = a0;
+            o[1] = a1;
+            return;
+        }
+    }
     if (vec4) {
         const int d = (blockIdx.y * kCombineThreads + threadIdx.x) * 4;
         if (d >= D) return;
@@ -474,7 +533,9 @@ hipError_t combine_launch(const float *y, int S, int D, int K, const int32_t *pa
                           const float *w, int has_shared, int64_t shared_row0, float *out,
                           int vec4, hipStream_t st, const float *resid, int y_bf16 = 0)
 {
-    const int per = vec4 ? 4 * kCombineThreads : kCombineThreads;
+    // bf16 rows: 8 elements per thread when whole 16-byte runs (vec4 = 2)
+    if (y_bf16 && vec4 && D % 8 == 0 && ((uintptr_t)y & 15u) == 0) vec4 = 2;
+    const int per = vec4 ? 4 * vec4 * kCombineThreads : kCombineThreads;
     const dim3 grid((unsigned)S, (unsigned)((D + per - 1) / per));
     if (y_bf16)
         hipLaunchKernelGGL(k_combine<uint16_t>, grid, dim3(kCombineThreads), 0, st,
