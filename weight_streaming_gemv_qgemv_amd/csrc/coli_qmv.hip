@@ -506,9 +506,10 @@ __global__ __launch_bounds__(512) void k_qmv1(QmvArgs a, int passes, int ntiles)
     }
 
     // partial tiles of the 8 waves, added in wave order; wave mt < MTB adds
-    // tile mt
-    __syncthreads();   // every wave is done with the staged activations
-    floatx4 *red = reinterpret_cast<floatx4 *>(lds);
+    // tile mt.  They go to LDS past the staged activations, so one barrier
+    // suffices (measured 0.1-0.4 us faster than reusing the staging area
+    // behind a second barrier at 12288 x 6144)
+    floatx4 *red = reinterpret_cast<floatx4 *>(lds + nkb * STEPS * 4 * 4);
 #pragma unroll
     for (int mt = 0; mt < MTB; ++mt) red[(wave * (MTB + 1) + mt) * kWave + lane] = acc[mt];
     red[(wave * (MTB + 1) + MTB) * kWave + lane] = accs;
@@ -553,7 +554,7 @@ hipError_t launch_q1(const QmvArgs &a, hipStream_t st)
     if (grid <= 0 || grid > 0x7FFFFFFF) return hipErrorInvalidValue;
     const size_t stage = (size_t)a.nkb * MF<FMT>::STEPS * 4 * 4 * 16;   // 4 column units per chunk
     const size_t red = (size_t)kQmvWaves * (MTB + 1) * kWave * 16;
-    const size_t lds = stage > red ? stage : red;
+    const size_t lds = stage + red;   // at most 96 + 32 KB (nkw <= 6)
     auto kern = k_qmv1<FMT, NKW, MTB>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
