@@ -102,6 +102,32 @@ __device__ __forceinline__ void xrun_elements(const float *xr, int e0, int I, fl
 // products and activation sums start from zero and are then scaled into the
 // running total, tot += scale[o, g] (products - OFF sums); the block's
 // scales are staged in LDS after the round buffers.
+// LDS of the rounds kernel: two round buffers, with group scales their
+// block's scales (16 MT rows of ng | 1 floats), then the 8 waves' partial
+// tiles -- past the rest when that keeps as many blocks on a CU (160 KB of
+// LDS), else over the round buffers behind one more barrier.  The byte
+// offset of the partial tiles (0: over the buffers) is shared by the kernel
+// and its launch.
+constexpr size_t kLdsMax = 160 * 1024;
+__host__ __device__ inline bool lds_apart(size_t stage, size_t red)
+{
+    const size_t both = stage > red ? stage : red;
+    return stage + red <= kLdsMax && kLdsMax / (stage + red) >= kLdsMax / both;
+}
+template <int FMT, int MT, int GPS>
+__host__ __device__ inline size_t qmv_stage_bytes(int ng)
+{
+    return (size_t)2 * kQmvWaves * MF<FMT>::STEPS * 4 * 16 * 16 + (GPS > 0 ? (size_t)16 * MT * (size_t)(ng | 1) * 4 : 0);
+}
+template <int MT>
+constexpr size_t qmv_red_bytes = (size_t)kQmvWaves * (MT + 1) * kWave * 16;
+template <int FMT, int MT, int GPS>
+__host__ __device__ inline size_t qmv_red_at(int ng)
+{
+    const size_t st = qmv_stage_bytes<FMT, MT, GPS>(ng);
+    return lds_apart(st, qmv_red_bytes<MT>) ? st : 0;
+}
+
 template <int FMT, int MT, int GPS = 0>
 __global__ __launch_bounds__(512) void k_qmv(QmvArgs a)
 {
@@ -114,8 +140,8 @@ __global__ __launch_bounds__(512) void k_qmv(QmvArgs a)
     constexpr uint32_t kbytes = KB * BITS / 8;
     constexpr int RUN = FMT == kI2 ? 16 : 8;          // elements per staging run
     // two round buffers of activation units -- per chunk 16 column units (hi
-    // and lo of each row) at column ^ swz16(chunk) -- reused at the end for
-    // the partial tiles
+    // and lo of each row) at column ^ swz16(chunk); the partial tiles at the
+    // end go past them or over them (qmv_red_at)
     extern __shared__ uint4 lds[];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -332,8 +358,9 @@ __global__ __launch_bounds__(512) void k_qmv(QmvArgs a)
     }
 
     // partial tiles of the 8 waves, added in wave order
-    __syncthreads();   // every wave is done with the round buffers
-    floatx4 *red = reinterpret_cast<floatx4 *>(lds);
+    const size_t red_at = qmv_red_at<FMT, MT, GPS>(a.ng);
+    if (red_at == 0) __syncthreads();   // every wave is done with the round buffers
+    floatx4 *red = reinterpret_cast<floatx4 *>(reinterpret_cast<char *>(lds) + red_at);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) red[(wave * (MT + 1) + mt) * kWave + lane] = acc[mt];
     red[(wave * (MT + 1) + MT) * kWave + lane] = accs;
@@ -728,12 +755,12 @@ hipError_t launch_q(const QmvArgs &a, hipStream_t st)
 {
     const int rb = 16 * MT;
     const dim3 grid((unsigned)((a.O + rb - 1) / rb), (unsigned)((a.S + kQmvTpp - 1) / kQmvTpp));
-    // LDS: two round buffers (GS: and the block's scales), or the partial tiles
-    const size_t stage = (size_t)2 * kQmvWaves * MF<FMT>::STEPS * 4 * 16 * 16 +
-                         (GPS > 0 ? (size_t)rb * (size_t)(a.ng | 1) * 4 : 0);
-    const size_t red = (size_t)kQmvWaves * (MT + 1) * kWave * 16;
-    const size_t lds = stage > red ? stage : red;
-    if (lds > 160 * 1024) return hipErrorInvalidValue;
+    // LDS: two round buffers (GS: and the block's scales), then or over
+    // them the partial tiles
+    const size_t stage = qmv_stage_bytes<FMT, MT, GPS>(a.ng), red = qmv_red_bytes<MT>;
+    const size_t red_at = qmv_red_at<FMT, MT, GPS>(a.ng);
+    const size_t lds = red_at ? red_at + red : (stage > red ? stage : red);
+    if (lds > kLdsMax) return hipErrorInvalidValue;
     auto kern = k_qmv<FMT, MT, GPS>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -757,6 +784,21 @@ hipError_t launch_q(const QmvArgs &a, hipStream_t st)
 // OFF * sum) for its column's group; the columns of one token are summed at
 // the end.  The block's scales (16 consecutive rows: one contiguous span of
 // 16 ng floats) are staged in LDS in row order.
+// LDS of k_qmvg: the staged activations, the block's scales (ng + 15 rows
+// of 16 floats), then the 8 waves' partial tiles -- past the rest when that
+// keeps as many blocks on a CU, else over the staging behind one more
+// barrier.
+__host__ __device__ inline size_t qmvg_stage_bytes(int nkb, int ng)
+{
+    return (size_t)nkb * MF<kI4>::STEPS * 4 * 4 * 16 + (size_t)(ng + 15) * 16 * 4;
+}
+constexpr size_t kQgRedBytes = (size_t)kQmvWaves * kWave * 16;
+__host__ __device__ inline size_t qmvg_red_at(int nkb, int ng)
+{
+    const size_t st = qmvg_stage_bytes(nkb, ng);
+    return lds_apart(st, kQgRedBytes) ? st : 0;
+}
+
 template <int GPS, int NKW>
 __global__ __launch_bounds__(512) void k_qmvg(QmvArgs a, int passes, int ntiles)
 {
@@ -933,8 +975,11 @@ __global__ __launch_bounds__(512) void k_qmvg(QmvArgs a, int passes, int ntiles)
     }
 
     // partial tiles of the 8 waves, added in wave order
-    __syncthreads();
-    floatx4 *red = reinterpret_cast<floatx4 *>(lds);
+    // (past the staged activations and scales when they fit, else over them
+    // behind one more barrier)
+    const size_t red_at = qmvg_red_at(nkb, ng);
+    if (red_at == 0) __syncthreads();
+    floatx4 *red = reinterpret_cast<floatx4 *>(reinterpret_cast<char *>(lds) + red_at);
     red[wave * kWave + lane] = acc;
     __syncthreads();
     if (wave != 0) return;
@@ -970,10 +1015,10 @@ hipError_t launch_qg(const QmvArgs &a, hipStream_t st)
     const int passes = (a.S + kQ1Tpp - 1) / kQ1Tpp;
     const int64_t grid = (int64_t)(ntiles + 7) / 8 * 8 * passes;
     if (grid <= 0 || grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-    const size_t stage = (size_t)a.nkb * MF<kI4>::STEPS * 4 * 4 * 16 + (size_t)(a.ng + 15) * 16 * 4;
-    const size_t red = (size_t)kQmvWaves * kWave * 16;     // the partial tiles, at the end
-    const size_t lds = stage > red ? stage : red;
-    if (lds > 160 * 1024) return hipErrorInvalidValue;
+    const size_t stage = qmvg_stage_bytes(a.nkb, a.ng), red = kQgRedBytes;
+    const size_t red_at = qmvg_red_at(a.nkb, a.ng);
+    const size_t lds = red_at ? red_at + red : (stage > red ? stage : red);
+    if (lds > kLdsMax) return hipErrorInvalidValue;
     if (16 * a.ng > 4 * 512 * ((GPS * NKW + 7) / 8)) return hipErrorInvalidValue;   // the scale span
     auto kern = k_qmvg<GPS, NKW>;
     if (lds > 64 * 1024) {
@@ -1105,7 +1150,7 @@ hipError_t qmv_grouped_launch(QmvArgs a, hipStream_t st)
         if (a.gs == 32) mt = 2;                           // 48 rows: 4 x 3 group tiles spill
         else if (a.gs == 64 && mt > 3) mt = 3;
         const size_t need = (size_t)2 * kQmvWaves * MF<kI4>::STEPS * 4 * 16 * 16 + (size_t)16 * mt * (size_t)(a.ng | 1) * 4;
-        if (need <= 160 * 1024) {
+        if (need <= kLdsMax) {
             if (a.gs == 32) return launch_q<kI4, 2, 4>(a, st);
             if (a.gs == 64) return mt == 3 ? launch_q<kI4, 3, 2>(a, st) : launch_q<kI4, 2, 2>(a, st);
             return mt == 4 ? launch_q<kI4, 4, 1>(a, st) : mt == 3 ? launch_q<kI4, 3, 1>(a, st)
