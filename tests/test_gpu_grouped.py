@@ -57,7 +57,10 @@ def test_exact_integer_bitwise(dev, orc, gs):
     Up to 2 rows one pass of the two-row kernel; from 3 rows (gs 32: from 7)
     the rounds kernel (passes of 8 rows; 9 rows: a second pass of one) while
     the block's scales fit its LDS (gs 32 at I = 12288 takes two-row passes);
-    8200 rows take 32- or 48-row blocks with a ragged last one."""
+    8200 rows take 32- or 48-row blocks with a ragged last one.  Both places
+    of the partial tiles are met: past the staging (two-row kernel at
+    I = 12288, rounds kernel with 32-row blocks at the narrow widths) and
+    over it (two-row kernel at the narrow widths, rounds kernel otherwise)."""
     g = synth.rng(7200, gs)
     for O, I in ((37, 1024 + 32), (300, 4096), (64, 12288), (8200, 1024 + 128)):
         for S in (1, 2, 3, 8, 9):
